@@ -1,0 +1,44 @@
+"""Comparison metrics, computed in fp64 on the CPU.
+
+The juejin post (§三, check [2]) compares a parallel output with the
+full-sequence reference by the maximum absolute error and the cosine
+similarity of the flattened tensors, and accepts bf16 results with
+max_abs_err within 1e-2 and cosine above 0.999; the fused-operator
+precision page (§3.1, §3.4) computes goldens in higher precision and uses the
+strict fp32 tier 1e-5.  The relative L2 error is added because with many
+visible keys the outputs are small and max_abs_err alone discriminates
+weakly.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import _f64
+
+
+def max_abs_err(a, b) -> float:
+    a, b = _f64(a), _f64(b)
+    if a.size == 0:
+        return 0.0
+    return float(np.max(np.abs(a - b)))
+
+
+def cosine(a, b) -> float:
+    a, b = _f64(a).ravel(), _f64(b).ravel()
+    na, nb = np.linalg.norm(a), np.linalg.norm(b)
+    if na == 0.0 and nb == 0.0:
+        return 1.0
+    if na == 0.0 or nb == 0.0:
+        return 0.0
+    return float(a @ b / (na * nb))
+
+
+def rel_l2(a, b) -> float:
+    a, b = _f64(a).ravel(), _f64(b).ravel()
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def compare(got, ref) -> dict:
+    return {"max_abs_err": max_abs_err(got, ref), "cos": cosine(got, ref),
+            "rel_l2": rel_l2(got, ref)}
