@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark: attention TFLOP/s of one rank's ring-attention share on one GPU.
+
+A step is one pass of the hot path over the long-context causal workload:
+rank 3 of a P=8 ring over a global sequence of L=131072 tokens, 64 heads of
+D=128 (hidden 8192), bf16 inputs with fp32 accumulation.  The rank's query
+shard (16384 tokens) visits the 8 K/V blocks in ring order 3,2,1,0,7,6,5,4:
+its own block is diagonal (element mask), blocks 2,1,0 are fully visible,
+blocks 7..4 are in the future and never read.  One step = one launch of the
+fused ring kernel (ra_ring_attn_fwd), inputs resident in HBM.
+
+Algorithmic work = 4*D FLOPs per visible (query, key) pair (2D for Q K^T,
+2D for P V), summed over heads and the share's rows; masked pairs, skipped
+blocks and softmax exponentials are not counted.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints ONE JSON line.  One GPU only: --gpus N > 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix-core peak (256 CU x 2.4 GHz x 4096 FLOP/clk)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "attention TFLOP/s per GPU (bf16, per-rank shard) + % of MFMA peak"
+
+
+def visible_pairs_causal_rank(rank: int, Sb: int, valid_len: int) -> int:
+    """Number of visible (query, key) pairs of a causal rank share per head:
+    query at global position p (< valid_len) sees keys 0..p."""
+    lo = rank * Sb
+    hi = min((rank + 1) * Sb, valid_len)
+    if hi <= lo:
+        return 0
+    # sum_{p=lo}^{hi-1} (p + 1)
+    return (lo + 1 + hi) * (hi - lo) // 2
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the side measurements (Ulysses layout, DiT shard)")
+    return ap.parse_args()
+
+
+def cpu_baseline(q, k, v, rank, Sb, H, D):
+    """The fp64 oracle, as it stands, on a bounded sample of the same share:
+    128 evenly spaced query rows of rank 3, all 64 heads, each over its whole
+    visible prefix.  Returns the oracle's algorithmic TFLOP/s on it."""
+    import numpy as np
+    import oracle
+    rows = np.unique(np.linspace(0, Sb - 1, 128).astype(np.int64))
+    kq = k[:, :(rank + 1) * Sb].cpu()
+    vq = v[:, :(rank + 1) * Sb].cpu()
+    qr = q[:, rank * Sb:(rank + 1) * Sb].cpu()
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    oracle.attention(qr, kq, vq, causal=True, q_pos0=rank * Sb, k_pos0=0, rows=rows)
+    dt = time.perf_counter() - t0
+    pairs = int(sum(rank * Sb + int(r) + 1 for r in rows)) * H
+    flops = 4.0 * D * pairs
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"rank {rank} share, {len(rows)} evenly spaced query rows x {H} heads, "
+                  f"each over its full causal prefix ({flops:.3e} algorithmic FLOPs, "
+                  f"{dt:.1f} s, numpy fp64)",
+        "seconds": dt,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's share of the ring on ONE GPU; multi-GPU runs "
+              "are not part of this build (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import ring_ulysses_sequence_amd as ra
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ra.lib()
+    w = W.LONG_CAUSAL
+    rank, Sb, H, D, P = 3, w.block_len, w.H, w.D, w.P
+    q, k, v = W.make_qkv(w, device="cuda")
+    kb = [k[:, j * Sb:(j + 1) * Sb] for j in range(P)]   # B = 1: contiguous blocks
+    vb = [v[:, j * Sb:(j + 1) * Sb] for j in range(P)]
+    q_r = q[:, rank * Sb:(rank + 1) * Sb]
+    o = torch.empty_like(q_r)
+    lse = torch.empty((1, Sb, H), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ra.ring_attn_fwd(q_r, kb, vb, rank, causal=True, valid_len=w.S, out=o,
+                         lse_out=lse, stream=stream)
+
+    pairs = visible_pairs_causal_rank(rank, Sb, w.S) * H * w.B
+    flops = 4.0 * D * pairs
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # per-launch HIP events on the launch stream (the roofline's duration)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step()
+        evs[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    launch_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_per_step = total_ms / args.steps
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+
+    extra = {}
+    if not args.no_extra:
+        extra = side_measurements(torch, ra, W, stream)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(q, k, v, rank, Sb, H, D)
+        extra["cpu_baseline_seconds"] = round(cpu.pop("seconds"), 2)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: N(0,1) q,k,v (seed 0, torch device generator) cast to bf16",
+        "config": {
+            "workload": "long-context causal ring share: L=131072, H=64, D=128 "
+                        "(hidden 8192), P=8, rank 3 (16384 query tokens over K/V "
+                        "blocks 3,2,1,0; 7..4 skipped), B=1",
+            "global_batch": 1, "seq_len": w.S, "heads": H, "head_dim": D, "ring_degree": P,
+            "rank": rank, "causal": True, "parallelism": "one rank's share on 1 GPU",
+            "algorithmic_flops_per_step": flops,
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma", "kernel": "ring_attn_bf16<128>",
+            "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "avg_launch_ms": round(avg_launch_ms, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+        "wall_s_timed_region": round(wall, 3),
+        "extra": extra,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def side_measurements(torch, ra, W, stream):
+    """Side numbers, not the step: the DiT-shard fused ring (rank 0) and the
+    Ulysses seq->head / head->seq layout of one tensor."""
+    out = {}
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    # DiT shard, rank 0 (non-causal, 4 blocks of 1024)
+    w = W.DIT_SHARD
+    q, k, v = W.make_qkv(w, device="cuda")
+    Sb = w.block_len
+    kb = [k[:, j * Sb:(j + 1) * Sb].contiguous() for j in range(w.P)]
+    vb = [v[:, j * Sb:(j + 1) * Sb].contiguous() for j in range(w.P)]
+    q0 = q[:, :Sb].contiguous()
+    o = torch.empty_like(q0)
+    for _ in range(3):
+        ra.ring_attn_fwd(q0, kb, vb, 0, out=o, want_lse=False, stream=stream)
+    a, b = ev(), ev()
+    n = 50
+    a.record(stream)
+    for _ in range(n):
+        ra.ring_attn_fwd(q0, kb, vb, 0, out=o, want_lse=False, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / n
+    fl = 4.0 * w.D * Sb * w.S * w.H * w.B
+    out["dit_shard_rank0"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+                              "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+    del q, k, v, kb, vb, q0, o
+    # Ulysses layout: one [8, 1, 2048, 32, 128] bf16 tensor each way
+    w = W.ULYSSES
+    x = W.random_tensor((w.P, w.B, w.S // w.P, w.H, w.D), device="cuda")
+    y = ra.seq2head(x, stream=stream)
+    z = ra.head2seq(y, stream=stream)
+    torch.cuda.synchronize()
+    for name, fn, src in (("seq2head", ra.seq2head, x), ("head2seq", ra.head2seq, y)):
+        dst = fn(src, stream=stream)
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(n):
+            fn(src, out=dst, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n
+        byts = 2.0 * src.numel() * src.element_size()
+        out[f"ulysses_{name}"] = {"ms": round(ms, 4), "GBps": round(byts / ms / 1e6, 1),
+                                  "frac_hbm": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3)}
+    del x, y, z
+    return out
+
+
+if __name__ == "__main__":
+    main()

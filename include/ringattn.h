@@ -1,0 +1,178 @@
+/*
+ * ringattn.h -- C ABI of the MI355X (gfx950) ring-order block attention and
+ * Ulysses layout library (libringattn.so).
+ *
+ * What it computes: exact scaled dot-product attention O = softmax(Q K^T *
+ * scale) V (scale = 1/sqrt(D) by default, D the head dimension) for ONE
+ * rank's share of a sequence-parallel job, evaluated the Ring-Attention way:
+ * the rank's query shard stays put while the P key/value blocks are visited
+ * in ring order and merged by the online-softmax recurrence, plus the Ulysses
+ * sequence-shard <-> head-shard transposes as local permutations.
+ *
+ * Pages cited (by title and section):
+ *   [RA]  "序列并行与 Ring Attention" (Sequence Parallelism and Ring Attention
+ *         tutorial, jefxiong.cn): §3.1 attention and the rank-local output,
+ *         §3.2 online softmax (m, l, u, alpha), §3.3 ring order, §3.4 causal
+ *         block classes on global positions, §3.5 Ulysses transpose.
+ *   [SPD] juejin post 7702110021828427786 (a sequence-parallel attention
+ *         library that never communicated): §三 the (B, S_local, H, D) call
+ *         shape, §四 the log-sum-exp combine and the is_causal precondition.
+ *   [UG]  "Finalize guidelines for Ulysses-based context-parallel attention"
+ *         (aitangshan.cn): §三-§七 divisibility and padding.
+ *
+ * Conventions for every entry point:
+ *   - Activations are [B, S, H, D] row-major, D innermost, contiguous
+ *     (the shards are made contiguous before the call, [SPD] §三).
+ *   - Device pointers are plain HIP device addresses owned by the caller;
+ *     the library never allocates, frees or keeps them.  `stream` is a
+ *     hipStream_t passed as void* (NULL = the null stream); work is enqueued
+ *     there and is asynchronous to the host.
+ *   - Validation happens on the host before anything is launched; on error
+ *     nothing is enqueued, a status != RA_OK is returned and
+ *     ra_last_error() (thread-local) describes it.  A launch failure returns
+ *     RA_ERR_HIP; faults inside a kernel surface at the caller's next
+ *     synchronisation.  Nothing aborts or throws across the ABI.
+ *   - Global positions: query row i of a call sits at q_pos0 + i, key row j
+ *     at k_pos0 + j.  Keys at positions >= valid_len are padding and masked
+ *     (valid_len < 0 means "no padding").  Causal attention lets query i see
+ *     key j only when pos(j) <= pos(i) ([RA] §3.4, §09: global, not local,
+ *     indices).  A query that sees no key gets O = 0, lse = -inf.
+ *   - Supported: D in {64, 128}; dtype bf16 (fp32 accumulation) or fp32.
+ */
+#ifndef RINGATTN_H
+#define RINGATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RA_OK = 0,
+  RA_ERR_NULL = 1,        /* a required pointer is NULL */
+  RA_ERR_SHAPE = 2,       /* sizes inconsistent (e.g. S not divisible by P) */
+  RA_ERR_DTYPE = 3,       /* unknown dtype / element size */
+  RA_ERR_RANGE = 4,       /* an index out of range (rank >= P, P > RA_MAX_P) */
+  RA_ERR_UNSUPPORTED = 5, /* valid but not implemented (e.g. D = 96) */
+  RA_ERR_HIP = 6          /* the HIP runtime refused a launch */
+} ra_status;
+
+typedef enum { RA_BF16 = 0, RA_FP32 = 1 } ra_dtype;
+
+/* Block classes of [RA] §3.4: a K/V block wholly in the future of the query
+ * block is skipped, one wholly in the past needs no mask, the overlapping
+ * (diagonal) one gets the element mask. */
+typedef enum { RA_SKIP = 0, RA_FULL = 1, RA_DIAG = 2 } ra_block_class;
+
+#define RA_MAX_P 64          /* largest ring degree one call accepts */
+#define RA_PAD_MULTIPLE 16   /* default per-rank padding granularity */
+
+/* ---------------------------------------------------------------------
+ * Host-only helpers (no GPU needed; exported for tests and schedule dumps)
+ * ------------------------------------------------------------------- */
+
+/* ABI version of this header (bumped on any signature change). */
+int ra_abi_version(void);
+
+/* Message of the last error on the calling thread ("" if none).  The
+ * pointer stays valid until the next ra_* call on this thread. */
+const char* ra_last_error(void);
+
+/* Padded global length: the smallest multiple of P * pad_multiple that is
+ * >= S ([UG] §六 padded_seq_len; its §七 test pads 3000 to 3008 for four
+ * ranks, which holds with pad_multiple = RA_PAD_MULTIPLE).  Returns -1 (and
+ * sets the error) if S < 0, P <= 0 or pad_multiple <= 0. */
+long long ra_padded_len(long long S, int P, int pad_multiple);
+
+/* Rank `rank`'s contiguous shard [*begin, *end) = [rank*S/P, (rank+1)*S/P)
+ * of a length-S sequence ([SPD] §三 shard-cover check).  RA_ERR_SHAPE if
+ * S % P != 0 (the message names the padded length), RA_ERR_RANGE if rank is
+ * outside [0, P). */
+ra_status ra_shard_range(long long S, int P, int rank, long long* begin,
+                         long long* end);
+
+/* Class of query positions [q0, q1) against key positions [k0, k1)
+ * ([RA] §3.4), written to *cls as an ra_block_class.  Non-causal blocks are
+ * FULL unless padding keys (>= valid_len) are involved. */
+ra_status ra_classify_block(long long q0, long long q1, long long k0,
+                            long long k1, int causal, long long valid_len,
+                            int* cls);
+
+/* The ring of rank `rank` among P ranks with blocks of block_len rows:
+ * src_out[t] = (rank - t) mod P for t = 0..P-1 ([RA] §3.3) and
+ * class_out[t] = the class of that block against the rank's query shard.
+ * Both arrays are caller-owned host arrays of P ints. */
+ra_status ra_ring_schedule(int P, int rank, long long block_len, int causal,
+                           long long valid_len, int* src_out, int* class_out);
+
+/* ---------------------------------------------------------------------
+ * Device entry points
+ * ------------------------------------------------------------------- */
+
+/* One round of the ring: attention of the query shard q [B,Sq,H,D] over ONE
+ * key/value block k, v [B,Sk,H,D] (both in dtype dt), at global positions
+ * q_pos0 / k_pos0 ([SPD] §四 local_attn_with_lse; [RA] §3.2 block step).
+ * Outputs (device, fp32, caller-owned):
+ *   o   [B,Sq,H,D]  this block's normalised partial output;
+ *   lse [B,Sq,H]    natural log-sum-exp of the visible scaled scores;
+ *   m_opt [B,Sq,H]  max of the visible scaled scores (may be NULL);
+ *   l_opt [B,Sq,H]  sum of exp(score - m) (may be NULL).
+ * scale <= 0 selects 1/sqrt(D).  Rows with no visible key: o = 0,
+ * lse = m = -inf, l = 0.  Errors: RA_ERR_NULL, RA_ERR_SHAPE (negative
+ * sizes), RA_ERR_UNSUPPORTED (D not 64/128), RA_ERR_DTYPE, RA_ERR_HIP. */
+ra_status ra_block_attn_fwd(const void* q, const void* k, const void* v,
+                            int B, int Sq, int Sk, int H, int D, ra_dtype dt,
+                            float scale, long long q_pos0, long long k_pos0,
+                            int causal, long long valid_len, float* o,
+                            float* lse, float* m_opt, float* l_opt,
+                            void* stream);
+
+/* Fold one round's partial into the running result ([SPD] §四 combine):
+ *   lse' = logaddexp(lse_acc, lse_blk)
+ *   o'   = o_acc * exp(lse_acc - lse') + o_blk * exp(lse_blk - lse')
+ * in place in o_acc [B,Sq,H,D] / lse_acc [B,Sq,H] (fp32).  Two empty
+ * partials (lse = -inf) merge to (0, -inf), never NaN.  If o_final_opt is
+ * not NULL, o' is also written there in final_dt ([B,Sq,H,D], bf16 by
+ * round-to-nearest-even, or fp32).  Errors: RA_ERR_NULL, RA_ERR_SHAPE,
+ * RA_ERR_DTYPE, RA_ERR_HIP. */
+ra_status ra_ring_merge(float* o_acc, float* lse_acc, const float* o_blk,
+                        const float* lse_blk, int B, int Sq, int H, int D,
+                        void* o_final_opt, ra_dtype final_dt, void* stream);
+
+/* The whole ring of rank `rank` in one launch ([RA] §3.2-§3.4): the query
+ * shard q_r [B,Sb,H,D] (global rows rank*Sb ..) against the P blocks
+ * k_blocks[j], v_blocks[j] (each [B,Sb,H,D], global rows j*Sb ..), visited
+ * in the order (rank - t) mod P, future blocks (causal) never read, the
+ * running (m, l, u) kept on chip across rounds.  k_blocks / v_blocks are
+ * HOST arrays of P device pointers.  Output o [B,Sb,H,D] in dt (bf16 by
+ * round-to-nearest-even), lse_opt [B,Sb,H] fp32 natural log-sum-exp (may
+ * be NULL).  valid_len: real global length (keys at or beyond it are padding;
+ * < 0 means P*Sb).  Errors: RA_ERR_NULL, RA_ERR_SHAPE, RA_ERR_RANGE
+ * (rank >= P, P > RA_MAX_P), RA_ERR_UNSUPPORTED, RA_ERR_DTYPE, RA_ERR_HIP. */
+ra_status ra_ring_attn_fwd(const void* q_r, const void* const* k_blocks,
+                           const void* const* v_blocks, int B, int Sb, int H,
+                           int D, int P, int rank, ra_dtype dt, float scale,
+                           int causal, long long valid_len, void* o,
+                           float* lse_opt, void* stream);
+
+/* Ulysses sequence-shard -> head-shard transpose ([RA] §3.5) of the P
+ * per-rank tensors stacked rank-major:
+ *   src [P, B, S/P, H, D]  ->  dst [P, B, S, H/P, D]
+ *   dst[r, b, j*S/P + s, h', d] = src[j, b, s, r*H/P + h', d]
+ * S is the GLOBAL length.  A pure bit copy of elem_bytes-sized elements
+ * (1, 2, 4 or 8), bit-exact for any payload (NaN, -0).  src and dst must not
+ * overlap.  Errors: RA_ERR_NULL, RA_ERR_SHAPE (S % P or H % P non-zero,
+ * [UG] §三), RA_ERR_DTYPE (elem_bytes), RA_ERR_HIP. */
+ra_status ra_seq2head(const void* src, void* dst, int P, int B, long long S,
+                      int H, int D, int elem_bytes, void* stream);
+
+/* The inverse: src [P, B, S, H/P, D] -> dst [P, B, S/P, H, D]
+ *   dst[j, b, s, r*H/P + h', d] = src[r, b, j*S/P + s, h', d]
+ * Same arguments and errors as ra_seq2head. */
+ra_status ra_head2seq(const void* src, void* dst, int P, int B, long long S,
+                      int H, int D, int elem_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RINGATTN_H */

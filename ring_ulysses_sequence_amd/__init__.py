@@ -1,0 +1,315 @@
+"""Python binding of libringattn.so (ring-order block attention and Ulysses
+transposes for MI355X / gfx950).
+
+Argument marshalling only: every step of the hot path runs in the library's
+HIP kernels.  Tensors are torch tensors on the GPU (PyTorch supplies device
+memory and the current stream); shapes follow the C ABI in
+include/ringattn.h:
+
+    block_attn_fwd(q, k, v, ...)   -> (o fp32, lse, m, l)     one ring round
+    ring_merge(o_acc, lse_acc, o_blk, lse_blk, ...)           LSE combine
+    ring_attn_fwd(q_r, k_blocks, v_blocks, rank, ...) -> (o, lse)
+    seq2head(x) / head2seq(x)                                 Ulysses layout
+    ring_schedule(P, rank, block_len, causal, valid_len)      host only
+    padded_len(S, P), shard_range(S, P, rank), classify_block(...)
+
+Errors: RA_ERR_SHAPE raises ValueError (as the Ulysses guideline's
+divisibility check does), every other status RuntimeError.  If the shared
+library has not been built the import succeeds but every call raises; there
+is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libringattn.so")
+
+RA_OK, RA_ERR_NULL, RA_ERR_SHAPE, RA_ERR_DTYPE, RA_ERR_RANGE, RA_ERR_UNSUPPORTED, RA_ERR_HIP = range(7)
+RA_BF16, RA_FP32 = 0, 1
+RA_SKIP, RA_FULL, RA_DIAG = 0, 1, 2
+RA_MAX_P = 64
+RA_PAD_MULTIPLE = 16
+
+# Every symbol include/ringattn.h declares.
+EXPORTED = (
+    "ra_abi_version", "ra_last_error", "ra_padded_len", "ra_shard_range",
+    "ra_classify_block", "ra_ring_schedule", "ra_block_attn_fwd",
+    "ra_ring_merge", "ra_ring_attn_fwd", "ra_seq2head", "ra_head2seq",
+)
+
+_lib = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LibraryMissing(
+            f"{LIB_PATH} is not built; run `python -m ring_ulysses_sequence_amd.build` "
+            "(hipcc for gfx950). There is no CPU fallback.")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_ll, c_int, c_vp, c_float = ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p, ctypes.c_float
+    c_fp = ctypes.POINTER(ctypes.c_float)
+    sig = {
+        "ra_abi_version": (c_int, []),
+        "ra_last_error": (ctypes.c_char_p, []),
+        "ra_padded_len": (c_ll, [c_ll, c_int, c_int]),
+        "ra_shard_range": (c_int, [c_ll, c_int, c_int, ctypes.POINTER(c_ll), ctypes.POINTER(c_ll)]),
+        "ra_classify_block": (c_int, [c_ll, c_ll, c_ll, c_ll, c_int, c_ll, ctypes.POINTER(c_int)]),
+        "ra_ring_schedule": (c_int, [c_int, c_int, c_ll, c_int, c_ll,
+                                     ctypes.POINTER(c_int), ctypes.POINTER(c_int)]),
+        "ra_block_attn_fwd": (c_int, [c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int,
+                                      c_int, c_float, c_ll, c_ll, c_int, c_ll,
+                                      c_vp, c_vp, c_vp, c_vp, c_vp]),
+        "ra_ring_merge": (c_int, [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
+                                  c_vp, c_int, c_vp]),
+        "ra_ring_attn_fwd": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp),
+                                     c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                     c_float, c_int, c_ll, c_vp, c_vp, c_vp]),
+        "ra_seq2head": (c_int, [c_vp, c_vp, c_int, c_int, c_ll, c_int, c_int, c_int, c_vp]),
+        "ra_head2seq": (c_int, [c_vp, c_vp, c_int, c_int, c_ll, c_int, c_int, c_int, c_vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def lib():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _load()
+
+
+def _check(status: int, what: str):
+    if status == RA_OK:
+        return
+    msg = _load().ra_last_error().decode(errors="replace")
+    if status == RA_ERR_SHAPE:
+        raise ValueError(f"{what}: {msg}")
+    raise RuntimeError(f"{what}: status {status}: {msg}")
+
+
+# --------------------------------------------------------------- host helpers
+def abi_version() -> int:
+    return _load().ra_abi_version()
+
+
+def padded_len(S: int, P: int, pad_multiple: int = RA_PAD_MULTIPLE) -> int:
+    r = _load().ra_padded_len(S, P, pad_multiple)
+    if r < 0:
+        raise ValueError(_load().ra_last_error().decode())
+    return r
+
+
+def shard_range(S: int, P: int, rank: int):
+    b, e = ctypes.c_longlong(), ctypes.c_longlong()
+    _check(_load().ra_shard_range(S, P, rank, ctypes.byref(b), ctypes.byref(e)), "shard_range")
+    return b.value, e.value
+
+
+def classify_block(q0: int, q1: int, k0: int, k1: int, causal: bool, valid_len: int = -1) -> int:
+    c = ctypes.c_int()
+    _check(_load().ra_classify_block(q0, q1, k0, k1, int(causal), valid_len, ctypes.byref(c)),
+           "classify_block")
+    return c.value
+
+
+def ring_schedule(P: int, rank: int, block_len: int, causal: bool, valid_len: int = -1):
+    """(sources, classes) of rank's ring; sources[t] = (rank - t) mod P."""
+    src = (ctypes.c_int * max(P, 1))()
+    cls = (ctypes.c_int * max(P, 1))()
+    _check(_load().ra_ring_schedule(P, rank, block_len, int(causal), valid_len, src, cls),
+           "ring_schedule")
+    return list(src)[:P], list(cls)[:P]
+
+
+# --------------------------------------------------------------- device calls
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return RA_BF16
+    if t.dtype == torch.float32:
+        return RA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def block_attn_fwd(q, k, v, *, scale: float = 0.0, q_pos0: int = 0, k_pos0: int = 0,
+                   causal: bool = False, valid_len: int = -1, want_ml: bool = True,
+                   out=None, stream=None):
+    """One ring round: (o fp32 [B,Sq,H,D], lse, m, l [B,Sq,H]) of q over one block."""
+    torch = _torch()
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if k.shape != (B, Sk, H, D) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    dt = _dtype_code(q)
+    if out is None:
+        o = torch.empty((B, Sq, H, D), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, Sq, H), dtype=torch.float32, device=q.device)
+        m = torch.empty_like(lse) if want_ml else None
+        l = torch.empty_like(lse) if want_ml else None
+    else:
+        o, lse, m, l = out
+    st = _load().ra_block_attn_fwd(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Sq, Sk, H, D, dt, float(scale),
+        q_pos0, k_pos0, int(causal), valid_len, _dev(o, "o"), _dev(lse, "lse"),
+        _dev(m, "m") if m is not None else None, _dev(l, "l") if l is not None else None,
+        _stream(stream))
+    _check(st, "ra_block_attn_fwd")
+    return o, lse, m, l
+
+
+def ring_merge(o_acc, lse_acc, o_blk, lse_blk, *, out_final=None, stream=None):
+    """In-place LSE combine of (o_blk, lse_blk) into (o_acc, lse_acc)."""
+    torch = _torch()
+    B, Sq, H, D = o_acc.shape
+    for t, n in ((o_acc, "o_acc"), (o_blk, "o_blk"), (lse_acc, "lse_acc"), (lse_blk, "lse_blk")):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{n} must be fp32")
+    if o_blk.shape != o_acc.shape or lse_acc.shape != (B, Sq, H) or lse_blk.shape != (B, Sq, H):
+        raise ValueError("merge operands have inconsistent shapes")
+    fdt = RA_FP32
+    fptr = None
+    if out_final is not None:
+        if out_final.shape != o_acc.shape:
+            raise ValueError("out_final shape mismatch")
+        fdt = _dtype_code(out_final)
+        fptr = _dev(out_final, "out_final")
+    st = _load().ra_ring_merge(_dev(o_acc, "o_acc"), _dev(lse_acc, "lse_acc"),
+                               _dev(o_blk, "o_blk"), _dev(lse_blk, "lse_blk"),
+                               B, Sq, H, D, fptr, fdt, _stream(stream))
+    _check(st, "ra_ring_merge")
+    return o_acc, lse_acc
+
+
+def ring_attn_fwd(q_r, k_blocks: Sequence, v_blocks: Sequence, rank: int, *,
+                  causal: bool = False, valid_len: int = -1, scale: float = 0.0,
+                  want_lse: bool = True, out=None, lse_out=None, stream=None):
+    """Rank ``rank``'s whole ring in one launch: (o [B,Sb,H,D] in q's dtype, lse)."""
+    torch = _torch()
+    B, Sb, H, D = q_r.shape
+    P = len(k_blocks)
+    if len(v_blocks) != P:
+        raise ValueError("k_blocks and v_blocks differ in length")
+    if P > RA_MAX_P:
+        raise RuntimeError(f"P={P} exceeds {RA_MAX_P}")
+    dt = _dtype_code(q_r)
+    kp = (ctypes.c_void_p * P)()
+    vp = (ctypes.c_void_p * P)()
+    for j in range(P):
+        for t, n in ((k_blocks[j], "k"), (v_blocks[j], "v")):
+            if t.shape != q_r.shape or t.dtype != q_r.dtype:
+                raise ValueError(f"{n}_blocks[{j}] must match q_r in shape and dtype")
+        kp[j] = k_blocks[j].data_ptr()
+        vp[j] = v_blocks[j].data_ptr()
+        _dev(k_blocks[j], f"k_blocks[{j}]"), _dev(v_blocks[j], f"v_blocks[{j}]")
+    o = torch.empty_like(q_r) if out is None else out
+    lse = lse_out
+    if lse is None and want_lse:
+        lse = torch.empty((B, Sb, H), dtype=torch.float32, device=q_r.device)
+    st = _load().ra_ring_attn_fwd(_dev(q_r, "q_r"), kp, vp, B, Sb, H, D, P, rank, dt,
+                                  float(scale), int(causal), valid_len, _dev(o, "o"),
+                                  _dev(lse, "lse") if lse is not None else None,
+                                  _stream(stream))
+    _check(st, "ra_ring_attn_fwd")
+    return o, lse
+
+
+def _perm(fn_name, x, out_shape, P, B, S, H, D, out, stream):
+    torch = _torch()
+    y = torch.empty(out_shape, dtype=x.dtype, device=x.device) if out is None else out
+    if y.shape != out_shape or y.dtype != x.dtype:
+        raise ValueError(f"out must be {out_shape} of {x.dtype}")
+    st = getattr(_load(), fn_name)(_dev(x, "src"), _dev(y, "dst"), P, B, S, H, D,
+                                   x.element_size(), _stream(stream))
+    _check(st, fn_name)
+    return y
+
+
+def seq2head(x, *, out=None, stream=None):
+    """[P, B, S/P, H, D] -> [P, B, S, H/P, D] (bit copy)."""
+    P, B, Sl, H, D = x.shape
+    if H % P:
+        raise ValueError(f"head count H={H} is not divisible by P={P}")
+    return _perm("ra_seq2head", x, (P, B, Sl * P, H // P, D), P, B, Sl * P, H, D, out, stream)
+
+
+def head2seq(x, *, out=None, stream=None):
+    """[P, B, S, H/P, D] -> [P, B, S/P, H, D] (bit copy)."""
+    P, B, S, Hl, D = x.shape
+    if S % P:
+        raise ValueError(f"sequence length {S} is not divisible by P={P}")
+    return _perm("ra_head2seq", x, (P, B, S // P, Hl * P, D), P, B, S, Hl * P, D, out, stream)
+
+
+def ring_attn_composable(q_r, k_blocks, v_blocks, rank: int, *, causal: bool = False,
+                         valid_len: int = -1, scale: float = 0.0, stream=None):
+    """The same ring as ``ring_attn_fwd`` done round by round: one
+    ``block_attn_fwd`` per visited block in ring order, folded in with
+    ``ring_merge``; the last merge writes the output in q's dtype.  With a
+    single visited block the fold is against an empty partial (a zero-key
+    block: o = 0, lse = -inf), so the conversion also runs in the merge."""
+    torch = _torch()
+    B, Sb, H, D = q_r.shape
+    P = len(k_blocks)
+    srcs, classes = ring_schedule(P, rank, Sb, causal, valid_len)
+    visit = [j for j, c in zip(srcs, classes) if c != RA_SKIP]
+    final = torch.empty_like(q_r)
+    kw = dict(scale=scale, q_pos0=rank * Sb, causal=causal, valid_len=valid_len,
+              stream=stream)
+    empty = q_r[:, :0]
+    first = visit[0] if visit else None
+    o_acc, lse_acc, _, _ = (
+        block_attn_fwd(q_r, k_blocks[first], v_blocks[first], k_pos0=first * Sb,
+                       want_ml=False, **kw) if first is not None
+        else block_attn_fwd(q_r, empty, empty, want_ml=False, **kw))
+    blk = (torch.empty_like(o_acc), torch.empty_like(lse_acc), None, None)
+    rest = visit[1:]
+    if not rest:
+        block_attn_fwd(q_r, empty, empty, out=blk, **kw)
+        ring_merge(o_acc, lse_acc, blk[0], blk[1], out_final=final, stream=stream)
+        return final, lse_acc
+    for n, j in enumerate(rest):
+        block_attn_fwd(q_r, k_blocks[j], v_blocks[j], k_pos0=j * Sb, out=blk, **kw)
+        ring_merge(o_acc, lse_acc, blk[0], blk[1],
+                   out_final=final if n == len(rest) - 1 else None, stream=stream)
+    return final, lse_acc
+
+
+__all__ = [
+    "lib", "abi_version", "padded_len", "shard_range", "classify_block", "ring_schedule",
+    "block_attn_fwd", "ring_merge", "ring_attn_fwd", "seq2head", "head2seq",
+    "ring_attn_composable", "EXPORTED", "LIB_PATH", "LibraryMissing",
+    "RA_BF16", "RA_FP32", "RA_SKIP", "RA_FULL", "RA_DIAG", "RA_MAX_P", "RA_PAD_MULTIPLE",
+]

@@ -1,0 +1,92 @@
+// Pairwise log-sum-exp merge of two partial attention results (the combine
+// of [SPD] §四, the composable form of one ring round):
+//   lse' = logaddexp(lse_acc, lse_blk)
+//   o'   = o_acc * exp(lse_acc - lse') + o_blk * exp(lse_blk - lse')
+// HBM-bound elementwise work: each row reads two D-vectors and two scalars
+// and writes one D-vector and one scalar (plus the optional final copy).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "ra_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.693147180559945309f;
+
+// One row is handled by D/4 consecutive lanes of ONE wavefront (D/4 divides
+// 64), so every lane of a row reads lse_acc before any lane writes it.
+__global__ __launch_bounds__(kThreads) void lse_merge(
+    float* __restrict__ o_acc, float* lse_acc, const float* __restrict__ o_blk,
+    const float* __restrict__ lse_blk, long long rows, int q4, void* o_final,
+    int final_bf16) {
+  const long long t = (long long)blockIdx.x * kThreads + threadIdx.x;
+  const long long row = t / q4;
+  if (row >= rows) return;
+  const int c = (int)(t - row * q4);
+  const float a = lse_acc[row];
+  const float b = lse_blk[row];
+  const float mx = fmaxf(a, b);
+  float wa = 0.0f, wb = 0.0f, lse = -INFINITY;
+  if (mx != -INFINITY) {
+    // logaddexp via the larger term: lse = mx + ln(2^((a-mx)log2e) + 2^((b-mx)log2e))
+    const float ea = __builtin_amdgcn_exp2f((a - mx) * kLog2e);
+    const float eb = __builtin_amdgcn_exp2f((b - mx) * kLog2e);
+    const float sum = ea + eb;
+    lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
+    const float inv = 1.0f / sum;
+    wa = ea * inv;
+    wb = eb * inv;
+  }
+  const float4 x = ((const float4*)o_acc)[t];
+  const float4 y = ((const float4*)o_blk)[t];
+  const float4 z = float4{fmaf(x.x, wa, y.x * wb), fmaf(x.y, wa, y.y * wb),
+                          fmaf(x.z, wa, y.z * wb), fmaf(x.w, wa, y.w * wb)};
+  ((float4*)o_acc)[t] = z;
+  if (c == 0) lse_acc[row] = lse;
+  if (o_final) {
+    if (final_bf16) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 r;
+      r[0] = (__bf16)z.x; r[1] = (__bf16)z.y; r[2] = (__bf16)z.z; r[3] = (__bf16)z.w;
+      ((bf16x4*)o_final)[t] = r;
+    } else {
+      ((float4*)o_final)[t] = z;
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" ra_status ra_ring_merge(float* o_acc, float* lse_acc, const float* o_blk,
+                                   const float* lse_blk, int B, int Sq, int H, int D,
+                                   void* o_final_opt, ra_dtype final_dt, void* stream) {
+  static const char* name = "ra_ring_merge";
+  ra::clear_error();
+  if (B < 0 || Sq < 0 || H < 0 || D <= 0)
+    return ra::fail(RA_ERR_SHAPE, "%s: need B, Sq, H >= 0 and D > 0", name);
+  if (D % 4 != 0 || 64 % (D / 4) != 0)
+    return ra::fail(RA_ERR_UNSUPPORTED, "%s: D=%d must be 4*2^k with D <= 256", name, D);
+  if (final_dt != RA_BF16 && final_dt != RA_FP32)
+    return ra::fail(RA_ERR_DTYPE, "%s: unknown final dtype %d", name, (int)final_dt);
+  const long long rows = (long long)B * Sq * H;
+  if (rows == 0) return RA_OK;
+  if (!o_acc || !lse_acc || !o_blk || !lse_blk)
+    return ra::fail(RA_ERR_NULL, "%s: NULL o/lse pointer", name);
+  if (((uintptr_t)o_acc | (uintptr_t)o_blk | (uintptr_t)o_final_opt) & 15)
+    return ra::fail(RA_ERR_SHAPE, "%s: o buffers must be 16-byte aligned", name);
+  const int q4 = D / 4;
+  const long long n = rows * q4;
+  const long long blocks = (n + kThreads - 1) / kThreads;
+  if (blocks > 0x7fffffffLL) return ra::fail(RA_ERR_UNSUPPORTED, "%s: too large", name);
+  hipLaunchKernelGGL(lse_merge, dim3((unsigned)blocks), dim3(kThreads), 0,
+                     (hipStream_t)stream, o_acc, lse_acc, o_blk, lse_blk, rows, q4,
+                     o_final_opt, final_dt == RA_BF16 ? 1 : 0);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess)
+    return ra::fail(RA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
+  return RA_OK;
+}

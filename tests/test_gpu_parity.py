@@ -1,0 +1,444 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances (written here, from the pages): bf16 inputs with fp32
+accumulation -- max_abs_err <= 1e-2 and cosine > 0.999 against the
+full-sequence reference (juejin post §二 table, §三 check [2]); fp32 --
+max_abs_err <= 1e-5 (fused-operator precision page §3.4, fp32 tier);
+layout permutations -- bit-exact (same page: integer / bitwise data exact).
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from oracle.attention import _f64
+
+pytestmark = pytest.mark.gpu
+
+ra = pytest.importorskip("ring_ulysses_sequence_amd")
+
+BF16_ATOL, BF16_COS, FP32_ATOL = 1e-2, 0.999, 1e-5
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (torch.cuda.is_available() is False)")
+    if not os.path.exists(ra.LIB_PATH):
+        pytest.fail("libringattn.so is not built")
+    ra.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def check_bf16(got, ref, what):
+    c = oracle.compare(got, ref)
+    say(what, {k: f"{v:.3e}" for k, v in c.items()})
+    assert np.all(np.isfinite(_f64(got)))
+    assert c["max_abs_err"] <= BF16_ATOL, (what, c)
+    assert c["cos"] > BF16_COS, (what, c)
+    return c
+
+
+def check_fp32(got, ref, what, atol=FP32_ATOL):
+    c = oracle.compare(got, ref)
+    say(what, {k: f"{v:.3e}" for k, v in c.items()})
+    assert c["max_abs_err"] <= atol, (what, c)
+    return c
+
+
+def blocks_of(x, P):
+    """P contiguous sequence blocks of a [B, S, H, D] tensor (the ring buffers)."""
+    Sb = x.shape[1] // P
+    return [x[:, j * Sb:(j + 1) * Sb].contiguous() for j in range(P)]
+
+
+def oracle_share(q, k, v, w, rank, rows=None, heads=None):
+    """Oracle attention of rank's share over the global K/V (per head to keep
+    host memory small).  Returns o [B, R, H', D], lse [B, R, H']."""
+    Sb = w.block_len
+    heads = range(w.H) if heads is None else heads
+    q_r = q[:, rank * Sb:(rank + 1) * Sb]
+    klim = (rank + 1) * Sb if w.causal else k.shape[1]
+    os_, ls_ = [], []
+    for h in heads:
+        o, lse, _, _ = oracle.attention(q_r[:, :, h:h + 1], k[:, :klim, h:h + 1],
+                                        v[:, :klim, h:h + 1], causal=w.causal,
+                                        q_pos0=rank * Sb, k_pos0=0, valid_len=w.S,
+                                        rows=rows)
+        os_.append(o)
+        ls_.append(lse)
+    return np.concatenate(os_, axis=2), np.concatenate(ls_, axis=2)
+
+
+def real_rows(w, rank):
+    """Rows of rank's share that are real tokens (pad queries are discarded)."""
+    Sb = w.block_len
+    n = max(0, min(Sb, w.S - rank * Sb))
+    return np.arange(n)
+
+
+# ------------------------------------------------------------ worked example
+def test_worked_example_through_abi():
+    """Tutorial §04 example: D zero-padded 2 -> 64 (scores unchanged), scale
+    1/sqrt(2) passed explicitly, two ranks with K/V blocks of two rows."""
+    import json
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "ring_tutorial_worked_example.json")))
+    def pad(x):
+        t = torch.zeros(1, 4, 1, 64, dtype=torch.float32)
+        t[0, :, 0, :2] = torch.tensor(x, dtype=torch.float32)
+        return t.cuda()
+    q, k, v = pad(g["q"]), pad(g["k"]), pad(g["v"])
+    kb, vb = blocks_of(k, 2), blocks_of(v, 2)
+    outs = []
+    for r in range(2):
+        say("worked example rank", r)
+        o, _ = ra.ring_attn_fwd(q[:, 2 * r:2 * r + 2].contiguous(), kb, vb, r,
+                                scale=1 / math.sqrt(2))
+        outs.append(o)
+    torch.cuda.synchronize()
+    o = torch.cat(outs, 1).cpu()
+    np.testing.assert_allclose(o[0, 0, 0, :2].numpy(), g["full_row0"], atol=2e-6)
+    assert torch.all(o[..., 2:] == 0)
+    full, _, _, _ = oracle.attention(q[..., :2].cpu(), k[..., :2].cpu(), v[..., :2].cpu())
+    check_fp32(o[..., :2], full, "worked example all rows")
+
+
+# ------------------------------------------------------------ C1 tiny fp32
+@pytest.mark.parametrize("path", ["fused", "composable"])
+def test_tiny_fp32_ring(path):
+    w = W.TINY_FP32
+    q, k, v = W.make_qkv(w)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    kb, vb = blocks_of(kg, w.P), blocks_of(vg, w.P)
+    for r in w.ranks:
+        say(w.name, path, "rank", r)
+        q_r = qg[:, r * w.block_len:(r + 1) * w.block_len].contiguous()
+        fn = ra.ring_attn_fwd if path == "fused" else ra.ring_attn_composable
+        o, lse = fn(q_r, kb, vb, r)
+        torch.cuda.synchronize()
+        ref_o, ref_lse = oracle_share(q, k, v, w, r)
+        check_fp32(o.cpu(), ref_o, f"{w.name} {path} r{r} O")
+        check_fp32(lse.cpu(), ref_lse, f"{w.name} {path} r{r} lse", atol=1e-5)
+        loc = oracle.local_only_attention(q_r.cpu(), kb[r].cpu(), vb[r].cpu(),
+                                          pos0=r * w.block_len)
+        assert oracle.max_abs_err(o.cpu(), loc) > 0
+
+
+# ------------------------------------------------------------ C2 DiT shard
+@pytest.fixture(scope="module")
+def dit():
+    w = W.DIT_SHARD
+    q, k, v = W.make_qkv(w)
+    return w, (q, k, v), (q.cuda(), k.cuda(), v.cuda())
+
+
+@pytest.mark.parametrize("rank", [0, 1, 2, 3])
+def test_dit_shard_fused(dit, rank):
+    w, (q, k, v), (qg, kg, vg) = dit
+    kb, vb = blocks_of(kg, w.P), blocks_of(vg, w.P)
+    q_r = qg[:, rank * w.block_len:(rank + 1) * w.block_len].contiguous()
+    say(w.name, "fused rank", rank)
+    o, lse = ra.ring_attn_fwd(q_r, kb, vb, rank)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = oracle_share(q, k, v, w, rank)
+    check_bf16(o.cpu(), ref_o, f"{w.name} r{rank} O")
+    assert oracle.max_abs_err(lse.cpu(), ref_lse) <= 1e-3
+    # communication really happened: differs from local-only attention
+    loc = oracle.local_only_attention(q_r.cpu(), kb[rank].cpu(), vb[rank].cpu())
+    assert oracle.max_abs_err(o.cpu(), loc) > 0
+    assert oracle.cosine(o.cpu(), loc) < BF16_COS
+
+
+def test_dit_shard_composable_matches(dit):
+    w, (q, k, v), (qg, kg, vg) = dit
+    kb, vb = blocks_of(kg, w.P), blocks_of(vg, w.P)
+    r = 2
+    q_r = qg[:, r * w.block_len:(r + 1) * w.block_len].contiguous()
+    say(w.name, "composable rank", r)
+    o_c, lse_c = ra.ring_attn_composable(q_r, kb, vb, r)
+    o_f, lse_f = ra.ring_attn_fwd(q_r, kb, vb, r)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = oracle_share(q, k, v, w, r)
+    check_bf16(o_c.cpu(), ref_o, f"{w.name} composable r{r}")
+    assert oracle.max_abs_err(lse_c.cpu(), ref_lse) <= 1e-3
+    assert oracle.max_abs_err(o_c.cpu(), o_f.cpu()) <= BF16_ATOL
+
+
+def test_dit_shard_deterministic(dit):
+    """No atomics on the path: two runs are bitwise identical."""
+    w, _, (qg, kg, vg) = dit
+    kb, vb = blocks_of(kg, w.P), blocks_of(vg, w.P)
+    q_r = qg[:, :w.block_len].contiguous()
+    say(w.name, "determinism")
+    a, la = ra.ring_attn_fwd(q_r, kb, vb, 0)
+    b, lb = ra.ring_attn_fwd(q_r, kb, vb, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(la, lb)
+
+
+def test_block_attn_partials_and_stats(dit):
+    """One round (block_attn_fwd): o, lse, m, l against the oracle, with
+    global positions; then merging all rounds gives the ring result."""
+    w, (q, k, v), (qg, kg, vg) = dit
+    r, Sb = 1, w.block_len
+    q_r = qg[:, r * Sb:(r + 1) * Sb].contiguous()
+    kb, vb = blocks_of(kg, w.P), blocks_of(vg, w.P)
+    j = 3
+    say(w.name, "block_attn_fwd block", j)
+    o, lse, m, l = ra.block_attn_fwd(q_r, kb[j], vb[j], q_pos0=r * Sb, k_pos0=j * Sb)
+    torch.cuda.synchronize()
+    ro, rl, rm, rll = oracle.attention(q[:, r * Sb:(r + 1) * Sb], k[:, j * Sb:(j + 1) * Sb],
+                                       v[:, j * Sb:(j + 1) * Sb])
+    check_bf16(o.cpu(), ro, "block_attn o")
+    assert oracle.max_abs_err(lse.cpu(), rl) <= 1e-3
+    assert oracle.max_abs_err(m.cpu(), rm) <= 1e-4 * max(1.0, float(np.abs(rm).max()))
+    np.testing.assert_allclose(l.cpu().numpy(), rll, rtol=2e-3)
+    np.testing.assert_allclose(lse.cpu().numpy(),
+                               m.cpu().numpy() + np.log(l.cpu().numpy()), atol=1e-5)
+
+
+# ------------------------------------------------------------ C3 Ulysses
+def test_ulysses_layout_and_attention():
+    w = W.ULYSSES
+    P, Sl, Hl = w.P, w.S // w.P, w.H // w.P
+    say(w.name, "generate")
+    q, k, v = W.make_qkv(w, device="cuda")
+    # the P per-rank sequence shards, stacked rank-major: [P, B, S/P, H, D]
+    stack = lambda x: x.view(w.B, P, Sl, w.H, w.D).transpose(0, 1).contiguous()
+    qs, ks, vs = stack(q), stack(k), stack(v)
+    say(w.name, "seq2head")
+    qh, kh, vh = ra.seq2head(qs), ra.seq2head(ks), ra.seq2head(vs)
+    torch.cuda.synchronize()
+    for src, dst in ((qs, qh), (ks, kh), (vs, vh)):
+        assert np.array_equal(dst.cpu().view(torch.int16).numpy(), oracle.seq2head(src.cpu()))
+    # local attention on the H/P heads of every rank: the stacked head
+    # shards [P, B, S, H/P, D] are one batch of P*B sequences, one ring
+    # block (P=1 in the attention call)
+    say(w.name, "attention on head shards")
+    flat = lambda x: x.view(P * w.B, w.S, Hl, w.D)
+    oh, _ = ra.ring_attn_fwd(flat(qh), [flat(kh)], [flat(vh)], 0)
+    oh = oh.view(P, w.B, w.S, Hl, w.D)
+    say(w.name, "head2seq")
+    os_ = ra.head2seq(oh)
+    torch.cuda.synchronize()
+    assert np.array_equal(os_.cpu().view(torch.int16).numpy(), oracle.head2seq(oh.cpu()))
+    assert torch.equal(ra.head2seq(qh).view(torch.int16), qs.view(torch.int16))
+    # sampled rows of the final sequence-sharded output vs the oracle
+    rows = np.unique(np.concatenate([np.arange(0, w.S, 61), [w.S - 1]]))
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    heads = [0, 5, 13, 31]
+    ref, _, _, _ = oracle.attention(qc[:, :, heads], kc[:, :, heads], vc[:, :, heads],
+                                    rows=rows)
+    got = os_.transpose(0, 1).reshape(w.B, w.S, w.H, w.D)[:, rows][:, :, heads].cpu()
+    check_bf16(got, ref, f"{w.name} O sampled rows")
+
+
+# ------------------------------------------------------------ C4 long causal
+def test_long_context_causal_rank3():
+    w = W.LONG_CAUSAL
+    r, Sb = 3, w.block_len
+    say(w.name, "generate on device")
+    q, k, v = W.make_qkv(w, device="cuda")
+    kb = [k[:, j * Sb:(j + 1) * Sb] for j in range(w.P)]   # B=1: contiguous views
+    vb = [v[:, j * Sb:(j + 1) * Sb] for j in range(w.P)]
+    q_r = q[:, r * Sb:(r + 1) * Sb]
+    say(w.name, "fused ring rank 3")
+    o, lse = ra.ring_attn_fwd(q_r, kb, vb, r, causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    # sampled rows: every 128th, both edges, and rows around the diagonal
+    # tile boundaries (query tile 128 rows, key tile 64 keys)
+    rows = np.unique(np.concatenate([
+        np.arange(0, Sb, 128), np.arange(0, 32), np.arange(Sb - 32, Sb),
+        np.arange(8192 - 3, 8192 + 3), np.arange(127, 130), np.arange(63, 66)]))
+    heads = list(range(0, w.H, 4))
+    say(w.name, "oracle on", len(rows), "rows x", len(heads), "heads")
+    kc = k[:, :(r + 1) * Sb].cpu()
+    vc = v[:, :(r + 1) * Sb].cpu()
+    ref_o, ref_lse = [], []
+    for h in heads:
+        o_h, l_h, _, _ = oracle.attention(q_r[:, :, h:h + 1].cpu(), kc[:, :, h:h + 1],
+                                          vc[:, :, h:h + 1], causal=True,
+                                          q_pos0=r * Sb, k_pos0=0, rows=rows)
+        ref_o.append(o_h)
+        ref_lse.append(l_h)
+    ref_o = np.concatenate(ref_o, 2)
+    ref_lse = np.concatenate(ref_lse, 2)
+    got = o[:, rows][:, :, heads].cpu()
+    check_bf16(got, ref_o, f"{w.name} sampled")
+    assert oracle.rel_l2(got, ref_o) < 2e-2
+    assert oracle.max_abs_err(lse[:, rows][:, :, heads].cpu(), ref_lse) <= 1e-3
+
+
+# ------------------------------------------------------------ C5 padded causal
+@pytest.fixture(scope="module")
+def padded():
+    w = W.PADDED_CAUSAL
+    q, k, v = W.make_qkv(w)
+    return w, (q, k, v), (q.cuda(), k.cuda(), v.cuda())
+
+
+@pytest.mark.parametrize("path", ["fused", "composable"])
+def test_padded_causal_all_ranks(padded, path):
+    w, (q, k, v), (qg, kg, vg) = padded
+    assert w.S_padded == 3008 and w.block_len == 752
+    kb, vb = blocks_of(kg, w.P), blocks_of(vg, w.P)
+    fn = ra.ring_attn_fwd if path == "fused" else ra.ring_attn_composable
+    for r in w.ranks:
+        q_r = qg[:, r * w.block_len:(r + 1) * w.block_len].contiguous()
+        say(w.name, path, "rank", r)
+        o, lse = fn(q_r, kb, vb, r, causal=True, valid_len=w.S)
+        torch.cuda.synchronize()
+        rows = real_rows(w, r)
+        ref_o, ref_lse = oracle_share(q, k, v, w, r, rows=rows)
+        check_bf16(o[:, rows].cpu(), ref_o, f"{w.name} {path} r{r}")
+        assert oracle.max_abs_err(lse[:, rows].cpu(), ref_lse) <= 2e-3
+
+
+def test_padded_skipped_blocks_never_read(padded):
+    """Poison the K/V of every block a causal rank skips with NaN: the output
+    stays bit-identical.  Poison a visited block: rows that see it change."""
+    w, _, (qg, kg, vg) = padded
+    kb, vb = blocks_of(kg, w.P), blocks_of(vg, w.P)
+    r = 1
+    q_r = qg[:, r * w.block_len:(r + 1) * w.block_len].contiguous()
+    say(w.name, "poison test")
+    base, _ = ra.ring_attn_fwd(q_r, kb, vb, r, causal=True, valid_len=w.S)
+    kp = [x.clone() for x in kb]
+    vp = [x.clone() for x in vb]
+    for j in (2, 3):
+        kp[j].fill_(float("nan"))
+        vp[j].fill_(float("nan"))
+    same, _ = ra.ring_attn_fwd(q_r, kp, vp, r, causal=True, valid_len=w.S)
+    vp[0].fill_(1e4)
+    diff, _ = ra.ring_attn_fwd(q_r, kp, vp, r, causal=True, valid_len=w.S)
+    torch.cuda.synchronize()
+    assert torch.equal(base.view(torch.int16), same.view(torch.int16))
+    assert (diff.float() - base.float()).abs().max().item() > 1.0
+
+
+# ------------------------------------------------------------ merge kernel
+def test_ring_merge_against_oracle():
+    g = torch.Generator().manual_seed(5)
+    B, Sq, H, D = 2, 37, 3, 64
+    o1 = torch.randn(B, Sq, H, D, generator=g)
+    o2 = torch.randn(B, Sq, H, D, generator=g)
+    l1 = torch.randn(B, Sq, H, generator=g) * 4
+    l2 = torch.randn(B, Sq, H, generator=g) * 4
+    l1[0, :5] = -math.inf                      # empty partials on either side
+    l2[0, 3:8] = -math.inf
+    o1[0, :5] = 0
+    o2[0, 3:8] = 0
+    ref_o, ref_l = oracle.lse_combine(o1, l1, o2, l2)
+    oa, la = o1.cuda(), l1.cuda()
+    fin = torch.empty(B, Sq, H, D, dtype=torch.bfloat16, device="cuda")
+    say("merge")
+    ra.ring_merge(oa, la, o2.cuda(), l2.cuda(), out_final=fin)
+    torch.cuda.synchronize()
+    assert torch.isfinite(oa).all()
+    check_fp32(oa.cpu(), ref_o, "merge o", atol=2e-6)
+    lg = la.cpu().numpy()
+    assert np.array_equal(np.isneginf(lg), np.isneginf(ref_l))
+    fin_ref = torch.from_numpy(ref_o).float().to(torch.bfloat16)
+    assert torch.equal(fin.cpu().view(torch.int16), fin_ref.view(torch.int16)) or \
+        (fin.cpu().float() - fin_ref.float()).abs().max().item() <= 2 ** -7
+    m = np.isfinite(ref_l)
+    np.testing.assert_allclose(lg[m], ref_l[m], atol=2e-6)
+
+
+# ------------------------------------------------------------ edge cases
+def test_edge_cases_fp32():
+    g = torch.Generator().manual_seed(9)
+    mk = lambda *s: torch.randn(*s, generator=g)
+    # one query, one key; ragged tiles; non-default scale
+    for (B, Sq, Sk, H, D) in [(1, 1, 1, 1, 64), (2, 130, 67, 3, 64), (1, 33, 200, 2, 128)]:
+        q, k, v = mk(B, Sq, H, D), mk(B, Sk, H, D), mk(B, Sk, H, D)
+        for causal, qp, kp in [(False, 0, 0), (True, 100, 0), (True, 0, 0)]:
+            say("edge", (B, Sq, Sk, H, D), causal, qp, kp)
+            o, lse, m, l = ra.block_attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=0.3,
+                                             q_pos0=qp, k_pos0=kp, causal=causal)
+            torch.cuda.synchronize()
+            ro, rl, rm, rl2 = oracle.attention(q, k, v, scale=0.3, q_pos0=qp, k_pos0=kp,
+                                               causal=causal)
+            check_fp32(o.cpu(), ro, "edge o")
+            lg = lse.cpu().numpy()
+            assert np.array_equal(np.isneginf(lg), np.isneginf(rl))   # unseen rows
+            fin = np.isfinite(rl)
+            np.testing.assert_allclose(lg[fin], rl[fin], atol=1e-5)
+            assert np.all(o.cpu().numpy()[~fin] == 0)
+
+
+def test_edge_empty_inputs():
+    say("edge empty")
+    z = torch.zeros(1, 0, 2, 64, device="cuda", dtype=torch.bfloat16)
+    q = torch.randn(1, 5, 2, 64, device="cuda").to(torch.bfloat16)
+    o, lse, m, l = ra.block_attn_fwd(q, z, z)              # no keys at all
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse)) and torch.all(l == 0)
+    o, lse, _, _ = ra.block_attn_fwd(z, q, q)              # no queries
+    assert o.numel() == 0
+    e = torch.zeros(2, 0, 0, 4, 64, dtype=torch.bfloat16, device="cuda")
+    assert ra.seq2head(e).shape == (2, 0, 0, 2, 64)
+    with pytest.raises(ValueError):
+        ra.seq2head(torch.zeros(3, 1, 2, 4, 8, dtype=torch.bfloat16, device="cuda"))
+
+
+def test_stability_large_scores():
+    """Tutorial §09: large scores stay finite.  K' = K + w adds q_i.w to every
+    score of row i (a per-row shift of ~1e3, which a naive exp overflows);
+    the GPU result matches the oracle on the same shifted inputs."""
+    g = torch.Generator().manual_seed(4)
+    B, S, H, D = 1, 256, 2, 64
+    q, k, v = (torch.randn(B, S, H, D, generator=g) for _ in range(3))
+    wv = torch.zeros(D)
+    wv[0] = 8000.0
+    k2 = k + wv
+    say("stability")
+    o, lse = ra.ring_attn_fwd(q.cuda(), [k2.cuda()], [v.cuda()], 0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    ref, _, _, _ = oracle.attention(q, k2, v)
+    s = oracle.scores(q, k2, 1 / math.sqrt(D))
+    assert np.abs(s).max() > 1000          # the shift really is large
+    # fp32 scores of magnitude ~1e3 carry ~1e-4 absolute rounding, which the
+    # exponent turns into relative weight errors of that size
+    check_fp32(o.cpu(), ref, "stability", atol=2e-3)
+
+
+# ------------------------------------------------------------ permutations
+@pytest.mark.parametrize("P,B,S,H,D,dtype", [
+    (8, 1, 16384, 32, 128, torch.int16),      # the Ulysses workload's shape
+    (4, 2, 64, 8, 3, torch.int16),            # run of 6 bytes: element path
+    (2, 3, 10, 4, 5, torch.int8),
+    (4, 1, 32, 4, 16, torch.int32),
+    (3, 1, 12, 3, 2, torch.int64),
+])
+def test_permutations_bit_exact(P, B, S, H, D, dtype):
+    say("permute", (P, B, S, H, D, dtype))
+    if dtype == torch.int16:
+        x = W.random_bits16((P, B, S // P, H, D), seed=P + S)
+    else:
+        info = torch.iinfo(dtype)
+        x = torch.randint(info.min, info.max, (P, B, S // P, H, D),
+                          generator=torch.Generator().manual_seed(3), dtype=dtype)
+    xg = x.cuda()
+    hx = ra.seq2head(xg)
+    back = ra.head2seq(hx)
+    torch.cuda.synchronize()
+    assert np.array_equal(hx.cpu().numpy(), oracle.seq2head(x.numpy()))
+    assert torch.equal(back.cpu(), x)
+    if P * B * S * H * D <= 4096:
+        assert np.array_equal(hx.cpu().numpy(), oracle.seq2head_loops(x.numpy()))

@@ -1,0 +1,146 @@
+"""The C ABI on the host: the library loads, exports every declared symbol,
+and its host-side logic (padding, shard cover, ring order, block classes)
+agrees with the oracle's brute force.  No GPU and no compute calls."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import schedule as sch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ringattn.h")
+
+ra = pytest.importorskip("ring_ulysses_sequence_amd")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ra.LIB_PATH):
+        pytest.fail("libringattn.so is not built (run __graft_entry__.build())")
+    return ra.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert set(declared) == set(ra.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    # the symbols are plain C (unmangled) exports of the shared object
+    out = os.popen(f"nm -D --defined-only {ra.LIB_PATH}").read()
+    for name in declared:
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_abi_version(lib):
+    assert ra.abi_version() == 1
+
+
+def test_padded_len_matches_oracle(lib):
+    for S in [0, 1, 15, 16, 3000, 3008, 4096, 131072, 131073]:
+        for P in [1, 2, 3, 4, 8]:
+            for m in [1, 16]:
+                assert ra.padded_len(S, P, m) == sch.padded_len(S, P, m)
+    assert ra.padded_len(3000, 4) == 3008
+    with pytest.raises(ValueError):
+        ra.padded_len(-1, 4)
+    with pytest.raises(ValueError):
+        ra.padded_len(10, 0)
+
+
+def test_shard_range_matches_oracle_and_errors(lib):
+    for S, P in [(3008, 4), (131072, 8), (64, 2), (12, 3)]:
+        for r in range(P):
+            assert ra.shard_range(S, P, r) == sch.shard_range(r, P, S)
+    with pytest.raises(ValueError, match="3008"):
+        ra.shard_range(3002, 4, 0)       # message names the padded length
+    with pytest.raises(RuntimeError):
+        ra.shard_range(64, 2, 2)          # rank out of range
+
+
+def test_ring_schedule_matches_oracle(lib):
+    for P in range(1, 9):
+        for r in range(P):
+            for causal in (False, True):
+                for bl, vl in [(5, 5 * P), (16, 16 * P - 7), (752, 3000)]:
+                    if vl <= 0:
+                        continue
+                    got = ra.ring_schedule(P, r, bl, causal, vl)
+                    exp = sch.ring_schedule(P, r, bl, causal, vl)
+                    assert got == (list(exp[0]), list(exp[1])), (P, r, causal, bl, vl)
+    assert ra.ring_schedule(8, 3, 16384, True) == (
+        [3, 2, 1, 0, 7, 6, 5, 4], [ra.RA_DIAG, ra.RA_FULL, ra.RA_FULL, ra.RA_FULL,
+                                   ra.RA_SKIP, ra.RA_SKIP, ra.RA_SKIP, ra.RA_SKIP])
+    with pytest.raises(RuntimeError):
+        ra.ring_schedule(4, 4, 16, True)
+
+
+def test_classify_block_matches_brute_force(lib):
+    rng = np.random.default_rng(11)
+    for _ in range(3000):
+        q0, k0 = (int(x) for x in rng.integers(0, 50, 2))
+        q1 = q0 + int(rng.integers(0, 14))
+        k1 = k0 + int(rng.integers(0, 14))
+        vl = int(rng.integers(0, 70))
+        causal = bool(rng.integers(0, 2))
+        assert ra.classify_block(q0, q1, k0, k1, causal, vl) == \
+            sch.classify_block(q0, q1, k0, k1, causal, vl), (q0, q1, k0, k1, causal, vl)
+    # negative valid_len means no padding
+    assert ra.classify_block(0, 4, 0, 4, False, -1) == ra.RA_FULL
+
+
+def test_device_entry_points_validate_before_launch(lib):
+    """Validation errors come back synchronously without touching a GPU
+    (null pointers, bad sizes, unsupported head dimension, bad rank)."""
+    import ctypes
+    null = None
+    # unsupported head dimension
+    st = lib.ra_block_attn_fwd(null, null, null, 1, 4, 4, 1, 96, ra.RA_BF16, 0.0, 0, 0,
+                               0, -1, null, null, null, null, null)
+    assert st == 5 and b"96" in lib.ra_last_error()
+    # null pointers with non-empty sizes
+    st = lib.ra_block_attn_fwd(null, null, null, 1, 4, 4, 1, 64, ra.RA_BF16, 0.0, 0, 0,
+                               0, -1, null, null, null, null, null)
+    assert st == 1
+    # empty problem: nothing to do, OK without pointers
+    st = lib.ra_block_attn_fwd(null, null, null, 0, 4, 4, 1, 64, ra.RA_BF16, 0.0, 0, 0,
+                               0, -1, null, null, null, null, null)
+    assert st == 0
+    # ring: rank >= P and P > RA_MAX_P
+    arr = (ctypes.c_void_p * 2)()
+    st = lib.ra_ring_attn_fwd(null, arr, arr, 1, 16, 1, 64, 2, 2, ra.RA_BF16, 0.0, 0,
+                              -1, null, null, null)
+    assert st == 4
+    st = lib.ra_ring_attn_fwd(null, arr, arr, 1, 16, 1, 64, 65, 0, ra.RA_BF16, 0.0, 0,
+                              -1, null, null, null)
+    assert st == 4
+    # permutations: S not divisible by P names the padded length; H % P
+    st = lib.ra_seq2head(ctypes.c_void_p(16), ctypes.c_void_p(1 << 40), 4, 1, 3002, 8, 64, 2, null)
+    assert st == 2 and b"3008" in lib.ra_last_error()
+    st = lib.ra_seq2head(ctypes.c_void_p(16), ctypes.c_void_p(1 << 40), 4, 1, 3008, 6, 64, 2, null)
+    assert st == 2
+    st = lib.ra_head2seq(ctypes.c_void_p(16), ctypes.c_void_p(1 << 40), 4, 1, 3008, 8, 64, 3, null)
+    assert st == 3
+    # merge: unsupported D, unknown dtype
+    st = lib.ra_ring_merge(null, null, null, null, 1, 4, 1, 12, null, ra.RA_FP32, null)
+    assert st == 5
+    st = lib.ra_ring_merge(null, null, null, null, 1, 4, 1, 64, null, 7, null)
+    assert st == 3
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    """The binding never falls back to a CPU computation."""
+    import torch
+    q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        ra.block_attn_fwd(q, q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        ra.seq2head(torch.zeros(2, 1, 4, 2, 8, dtype=torch.bfloat16))
