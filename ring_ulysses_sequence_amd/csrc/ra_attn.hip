@@ -149,29 +149,75 @@ __device__ __forceinline__ float online_update(float (&s)[NS], RowState& st, flo
 // ---------------------------------------------------------------------------
 // bf16 kernel
 // ---------------------------------------------------------------------------
+// K and V tiles (64 keys x D, row-major as in HBM) are copied HBM -> LDS by
+// the buffer unit itself (buffer_load ... lds: each lane's 16 bytes land at
+// LDS base + 16*lane), so staging costs no registers and no VALU work, and
+// rows past the end of a block come back as zeros from the buffer range
+// check.  The copy picks, for every LDS position, the global 16-byte chunk
+// that belongs there under an XOR swizzle that keeps the matrix-core operand
+// reads free of bank conflicts:
+//   K: chunk c of key row r is stored at chunk c ^ (r & 15)       (D = 128)
+//                                          c ^ ((r >> 1) & 7)     (D = 64)
+//   V: chunk c of key row r is stored at chunk c ^ ((r & 3) << 2) (D = 128)
+//                                          c ^ (((r >> 1) & 1) << 2) (D = 64)
+// K feeds S^T = K Q^T as the A operand with ds_read_b128.  V feeds
+// O^T += V^T P^T as the A operand through ds_read_b64_tr_b16: inside each
+// 16-lane group, lane j receives element j%4 of the 64-bit rows supplied by
+// lanes j/4, j/4+4, j/4+8, j/4+12; supplier r = 4e + q points at
+// V[key_e][d0 + 4q .. d0 + 4q + 3], so lane j gets V[key_0..3][d0 + j].
 template <int D>
 struct Bf16Cfg {
-  static constexpr int BC = 64;                 // keys per tile
-  static constexpr int KS = D * 2 + 16;         // K row stride in LDS (bytes)
-  static constexpr int VS = BC * 2 + 16;        // V^T row stride in LDS (bytes)
-  static constexpr int K_BYTES = BC * KS;
-  static constexpr int V_BYTES = D * VS;
-  static constexpr int BUF = K_BYTES + V_BYTES;
-  static constexpr int K_UNITS = BC * D / 8 / kThreads;     // 16B per unit
-  static constexpr int V_ITEMS = (BC / 4) * (D / 8);        // 4 keys x 8 d
-  static constexpr int V_PER_T = (V_ITEMS + kThreads - 1) / kThreads;
-  static constexpr int NC = D / 16;                         // k-steps of QK^T
-  static constexpr int NDT = D / 32;                        // d tiles of O^T
+  static constexpr int BC = 64;                   // keys per tile
+  static constexpr int ROWB = D * 2;              // bytes per key row in LDS
+  static constexpr int TILE = BC * ROWB;          // one K or V tile
+  static constexpr int STAGE = 2 * TILE;          // K tile + V tile
+  static constexpr int CHUNKS = D / 8;            // 16-byte chunks per row
+  static constexpr int DMA = TILE / 1024 / kWaves;  // 1 KiB copies per wave per tile
+  static constexpr int NC = D / 16;               // k-steps of S^T = K Q^T
+  static constexpr int NDT = D / 32;              // 32-row d tiles of O^T
 };
 
-// Position of key `g*4` (a group of 4 keys) inside the permuted V^T row:
-// within each 16-key group the four 4-key groups are stored in the order
-// 0, 2, 1, 3, so that lane half h reads its 8 keys {4h..4h+3, 8+4h..8+4h+3}
-// as one 16-byte load.
-__device__ __forceinline__ int vt_key_slot(int g) {
-  const int G = g >> 2, gg = g & 3;
-  const int pg = (gg == 1) ? 2 : (gg == 2 ? 1 : gg);
-  return G * 16 + pg * 4;
+template <int D>
+__device__ __forceinline__ int swz_k(int r, int c) {
+  return D == 128 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r, int c) {
+  return D == 128 ? (c ^ ((r & 3) << 2)) : (c ^ (((r >> 1) & 1) << 2));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access
+constexpr float kRescaleSlack = 8.0f;   // lazy rescale threshold (base-2 units)
+
+// Copy K/V tile `ti` of ring block `bi` (rows kt0 .. kt0+63 of batch b,
+// head h) HBM -> LDS stage `dst` with the buffer unit: each wave copies its
+// C::DMA KiB of K and of V; rows past the block end read as zeros.
+template <int D>
+__device__ __forceinline__ void issue_tile(const AttnArgs& a, int bi, int ti, int b, int h,
+                                           int HD2, int wave, const int* voff,
+                                           const int* voffv, char* dst_stage) {
+  using C = Bf16Cfg<D>;
+  const KVBlock& kb = a.blk[bi];
+  const int kt0 = ti * C::BC;
+  const int rows = min(C::BC, kb.len - kt0);
+  const long long off = (((long long)b * kb.len + kt0) * a.H + h) * (D * 2);
+  const int nrec = (rows - 1) * HD2 + D * 2;
+  __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)kb.k + off), 0, nrec, kRsrcWord3);
+  __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)kb.v + off), 0, nrec, kRsrcWord3);
+#pragma unroll
+  for (int i = 0; i < C::DMA; ++i) {
+    char* dst = dst_stage + (wave * C::DMA + i) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_ptr)dst, 16, voff[i], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_ptr)(dst + C::TILE), 16, voffv[i], 0, 0, 0);
+  }
 }
 
 template <int D>
@@ -179,7 +225,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void ring_attn_bf16(const AttnArgs a) {
   using C = Bf16Cfg<D>;
   constexpr int BC = C::BC;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -189,108 +235,71 @@ void ring_attn_bf16(const AttnArgs a) {
 
   int b, h, qt;
   tile_coords(a, b, h, qt);
-  const int row0 = qt * kBR;                       // first local row of the WG
+  const int row0 = qt * kBR;
   const int rows_here = min(kBR, a.Sq - row0);
   const long long q_lo = a.q_pos0 + row0;
   const long long q_hi = q_lo + rows_here - 1;
-  const int wrow0 = row0 + wave * 32;              // first row of this wave
-  const int wrows = min(32, a.Sq - wrow0);         // may be <= 0
+  const int wrow0 = row0 + wave * 32;
+  const int wrows = min(32, a.Sq - wrow0);
   const long long wq_lo = a.q_pos0 + wrow0;
   const long long wq_hi = wq_lo + wrows - 1;
-  const long long HD = (long long)a.H * D;         // row stride (elements)
+  const long long HD = (long long)a.H * D;
+  const int HD2 = a.H * D * 2;  // bytes between consecutive key rows
 
-  // Q fragment (B operand of S^T = K Q^T): query row wrow0+col,
-  // features 16c + 8*half .. +7.
+  // Q fragment (B operand of S^T = K Q^T): query wrow0 + col, features
+  // 16c + 8*half .. +7.
   bf16x8 qf[C::NC];
   {
     const int r = wrow0 + col;
     const __bf16* qp = (const __bf16*)a.q + ((long long)b * a.Sq + r) * HD + (long long)h * D;
 #pragma unroll
-    for (int c = 0; c < C::NC; ++c) {
-      if (r < a.Sq) qf[c] = *(const bf16x8*)(qp + 16 * c + 8 * half);
-      else qf[c] = bf16x8{};
+    for (int c = 0; c < C::NC; ++c)
+      qf[c] = r < a.Sq ? *(const bf16x8*)(qp + 16 * c + 8 * half) : bf16x8{};
+  }
+
+  // per-lane constant parts of the copy sources and the LDS read addresses
+  int voff[C::DMA];   // byte offset (within a tile's rows) of this lane's chunk
+  int voffv[C::DMA];
+#pragma unroll
+  for (int i = 0; i < C::DMA; ++i) {
+    const int p = (wave * C::DMA + i) * 64 + lane;  // physical 16B chunk in the tile
+    const int r = p / C::CHUNKS, pc = p % C::CHUNKS;
+    voff[i] = r * HD2 + swz_k<D>(r, pc) * 16;
+    voffv[i] = r * HD2 + swz_v<D>(r, pc) * 16;
+  }
+  int kaddr[C::NC];   // K operand: row col, logical chunk 2c + half
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) kaddr[c] = col * C::ROWB + swz_k<D>(col, 2 * c + half) * 16;
+  int vaddr[C::NDT];  // V operand: supplier row 4*half + e, d0 = 32dt + 16*(group&1) + 4q
+  {
+    const int j = lane & 15, e = j >> 2, q = j & 3, g = lane >> 4;
+    const int kl = 4 * half + e;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+      const int d0 = 32 * dt + 16 * (g & 1) + 4 * q;
+      vaddr[dt] = kl * C::ROWB + swz_v<D>(kl, d0 >> 3) * 16 + (d0 & 7) * 2;
     }
   }
 
   f32x16 oacc[C::NDT];
 #pragma unroll
   for (int i = 0; i < C::NDT; ++i) oacc[i] = f32x16{};
-  RowState st{-INFINITY, 0.0f};
+  float m_ref = -INFINITY;   // reference max (base 2) of this lane's query
+  float m_true = -INFINITY;  // exact running max (base 2)
+  float l_run = 0.0f;        // this lane's half of sum 2^(s - m_ref)
 
   // ---- tile cursor over (block, tile) in ring order ----
   int cb = 0, ct = 0, cn = 0;
   while (cb < a.nblk && (cn = tiles_of<BC>(a, cb, q_hi)) == 0) ++cb;
   bool have = cb < a.nblk;
 
-  uint4 kreg[C::K_UNITS];
-  uint4 vreg[C::V_PER_T][4];
-
-  auto fetch = [&](int bi, int ti) {
-    const KVBlock& kb = a.blk[bi];
-    const int kt0 = ti * BC;
-    const __bf16* kp = (const __bf16*)kb.k + ((long long)b * kb.len + kt0) * HD + (long long)h * D;
-    const __bf16* vp = (const __bf16*)kb.v + ((long long)b * kb.len + kt0) * HD + (long long)h * D;
-    const int rows = min(BC, kb.len - kt0);
-#pragma unroll
-    for (int u = 0; u < C::K_UNITS; ++u) {
-      const int unit = tid + u * kThreads;
-      const int r = unit / (D / 8), c = unit % (D / 8);
-      kreg[u] = r < rows ? *(const uint4*)(kp + r * HD + 8 * c) : uint4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < C::V_PER_T; ++u) {
-      const int item = tid + u * kThreads;
-      const int g = item % (BC / 4), c = item / (BC / 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e;
-        vreg[u][e] = (item < C::V_ITEMS && r < rows)
-                         ? *(const uint4*)(vp + r * HD + 8 * c) : uint4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_lds = [&](int buf) {
-    char* kl = smem + buf * C::BUF;
-    char* vl = kl + C::K_BYTES;
-#pragma unroll
-    for (int u = 0; u < C::K_UNITS; ++u) {
-      const int unit = tid + u * kThreads;
-      const int r = unit / (D / 8), c = unit % (D / 8);
-      *(uint4*)(kl + r * C::KS + 16 * c) = kreg[u];
-    }
-#pragma unroll
-    for (int u = 0; u < C::V_PER_T; ++u) {
-      const int item = tid + u * kThreads;
-      if (item < C::V_ITEMS) {
-        const int g = item % (BC / 4), c = item / (BC / 4);
-        const int slot = vt_key_slot(g);
-        const unsigned* w0 = (const unsigned*)&vreg[u][0];
-        const unsigned* w1 = (const unsigned*)&vreg[u][1];
-        const unsigned* w2 = (const unsigned*)&vreg[u][2];
-        const unsigned* w3 = (const unsigned*)&vreg[u][3];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          const int sh = (e & 1) * 16;
-          const unsigned lo = ((w0[w] >> sh) & 0xffffu) | (((w1[w] >> sh) & 0xffffu) << 16);
-          const unsigned hi = ((w2[w] >> sh) & 0xffffu) | (((w3[w] >> sh) & 0xffffu) << 16);
-          *(uint2*)(vl + (8 * c + e) * C::VS + slot * 2) = uint2{lo, hi};
-        }
-      }
-    }
-  };
-
   const float c_scale = a.scale_log2;
-  int buf = 0;
-  if (have) {
-    fetch(cb, ct);
-    store_lds(0);
-  }
+  int stage = 0;
+  if (have) issue_tile<D>(a, cb, ct, b, h, HD2, wave, voff, voffv, smem);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   while (have) {
-    // advance the cursor: next tile of this block, or the first tile of the
-    // next visited block in ring order
     int nb = cb, nt = ct + 1, nn = cn;
     if (nt >= nn) {
       nt = 0;
@@ -298,76 +307,116 @@ void ring_attn_bf16(const AttnArgs a) {
       while (nb < a.nblk && (nn = tiles_of<BC>(a, nb, q_hi)) == 0) ++nb;
     }
     const bool has_next = nb < a.nblk;
-    if (has_next) fetch(nb, nt);
+    if (has_next)
+      issue_tile<D>(a, nb, nt, b, h, HD2, wave, voff, voffv, smem + (stage ^ 1) * C::STAGE);
 
-    // ---- compute on the current tile ----
     const KVBlock& kb = a.blk[cb];
     const int kt0 = ct * BC;
     const long long kp0 = kb.k_pos0 + kt0;
     const bool wave_live = wrows > 0 && !(a.causal && kp0 > wq_hi);
     if (wave_live) {
-      const char* kl = smem + buf * C::BUF;
-      const char* vl = kl + C::K_BYTES;
-      float s[BC / 2];  // 2 S^T tiles x 16 values
+      const int sb = stage * C::STAGE;
+      float s[BC / 2];
 #pragma unroll
       for (int kt = 0; kt < BC / 32; ++kt) {
         f32x16 acc = f32x16{};
 #pragma unroll
         for (int c = 0; c < C::NC; ++c) {
-          const bf16x8 kf = *(const bf16x8*)(kl + (32 * kt + col) * C::KS + (16 * c + 8 * half) * 2);
+          const bf16x8 kf = *(const bf16x8*)(smem + sb + kt * 32 * C::ROWB + kaddr[c]);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], acc, 0, 0, 0);
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[kt * 16 + v] = acc[v];
       }
-      const bool need_mask =
-          kt0 + BC > kb.len ||
-          (kb.cls == RA_DIAG &&
-           (kp0 + BC - 1 >= a.valid_len || (a.causal && kp0 + BC - 1 > wq_lo)));
+      // element mask on diagonal / ragged / padded tiles, in 32-bit
+      // positions relative to the tile: key j of the tile is masked for the
+      // lane's query when j > (query - first key) or j >= klim
+      long long lim_ll = kb.len - kt0;
+      if (a.valid_len - kp0 < lim_ll) lim_ll = a.valid_len - kp0;
+      const bool need_mask = lim_ll < BC || (a.causal && kp0 + BC - 1 > wq_lo);
       if (need_mask) {
-        const long long qpos = wq_lo + col;
+        const int klim = (int)max(0LL, lim_ll);  // <= BC here or the causal test fired
+        int t = min(klim, BC) - 1 - 4 * half;    // masked if jconst > t
+        if (a.causal) {
+          long long rel = wq_lo + col - kp0 - 4 * half;
+          if (rel < -1) rel = -1;
+          if (rel < t) t = (int)rel;
+        }
 #pragma unroll
         for (int kt = 0; kt < BC / 32; ++kt)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int j = 32 * kt + 8 * (v >> 2) + 4 * half + (v & 3);
-            const long long kpos = kp0 + j;
-            const bool masked = kt0 + j >= kb.len || kpos >= a.valid_len ||
-                                (a.causal && kpos > qpos);
-            if (masked) s[kt * 16 + v] = -INFINITY;
+            const int jc = 32 * kt + 8 * (v >> 2) + (v & 3);
+            if (jc > t) s[kt * 16 + v] = -INFINITY;
           }
       }
-      const float alpha = online_update<BC / 2>(s, st, c_scale);
+      // online softmax ([RA] §3.2) with a lazily moved reference max: the
+      // accumulators are rescaled only when the row max passes the
+      // reference by more than kRescaleSlack, so p = 2^(s - m_ref) <= 2^8;
+      // u / l is unchanged because u and l share the reference.
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < C::NDT; ++i)
+      for (int i = 0; i < BC / 2; ++i) mx = fmaxf(mx, s[i]);
+      mx = pair_max(mx) * c_scale;
+      m_true = fmaxf(m_true, mx);
+      const bool need = mx > m_ref + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? mx : m_ref;
+        const float alpha = fast_exp2(m_ref - m_new);
+        l_run *= alpha;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
-      // P^T in bf16: for key group G (16 keys), the lane's 8 values
+        for (int i = 0; i < C::NDT; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
+        m_ref = m_new;
+      }
+      const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
+#pragma unroll
+      for (int i = 0; i < BC / 2; ++i) s[i] = fast_exp2(fmaf(s[i], c_scale, -m_use));
       bf16x8 pb[BC / 16];
 #pragma unroll
       for (int G = 0; G < BC / 16; ++G)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[G][e] = (__bf16)s[(G >> 1) * 16 + (G & 1) * 8 + e];
+      // the denominator sums the SAME bf16-rounded weights that enter P V, so
+      // u / l stays an exact convex combination of V rows whatever the
+      // rounding (one v_dot2 against (1, 1) per pair of weights)
+      float lsum0 = 0.0f, lsum1 = 0.0f;
+#pragma unroll
+      for (int G = 0; G < BC / 16; ++G)
+#pragma unroll
+        for (int e = 0; e < 8; e += 4) {
+          const bf16x2 p0 = {pb[G][e], pb[G][e + 1]}, p1 = {pb[G][e + 2], pb[G][e + 3]};
+          lsum0 = __builtin_amdgcn_fdot2_f32_bf16(p0, kOnes2, lsum0, false);
+          lsum1 = __builtin_amdgcn_fdot2_f32_bf16(p1, kOnes2, lsum1, false);
+        }
+      l_run += lsum0 + lsum1;
+      char* vl = smem + sb + C::TILE;
 #pragma unroll
       for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
         for (int G = 0; G < BC / 16; ++G) {
-          const bf16x8 vf = *(const bf16x8*)(vl + (32 * dt + col) * C::VS + (16 * G + 8 * half) * 2);
+          char* p0 = vl + G * 16 * C::ROWB + vaddr[dt];
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p0);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p0 + 8 * C::ROWB));
+          bf16x8 vf;
+          __builtin_memcpy(&vf, &lo, 8);
+          __builtin_memcpy((char*)&vf + 8, &hi, 8);
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[G], oacc[dt], 0, 0, 0);
         }
     }
 
-    if (has_next) store_lds(buf ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile landed
+    __syncthreads();                // everyone's copies landed, everyone done reading
     cb = nb;
     ct = nt;
     cn = nn;
     have = has_next;
-    buf ^= 1;
+    stage ^= 1;
   }
 
   // ---- epilogue: o = u / l, lse = m + ln l ([RA] §3.2; [SPD] §四) ----
-  const float l_tot = pair_sum(st.l);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const int r = wrow0 + col;
   if (wrows > 0 && r < a.Sq) {
@@ -391,9 +440,9 @@ void ring_attn_bf16(const AttnArgs a) {
     if (half == 0) {
       const long long so = ((long long)b * a.Sq + r) * a.H + h;
       const bool seen = l_tot > 0.0f;
-      if (a.lse) a.lse[so] = seen ? (st.m + fast_log2(l_tot)) * kLn2 : -INFINITY;
-      if (a.m_out) a.m_out[so] = seen ? st.m * kLn2 : -INFINITY;
-      if (a.l_out) a.l_out[so] = l_tot;
+      if (a.lse) a.lse[so] = seen ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
+      if (a.m_out) a.m_out[so] = seen ? m_true * kLn2 : -INFINITY;
+      if (a.l_out) a.l_out[so] = seen ? l_tot * fast_exp2(m_ref - m_true) : 0.0f;
     }
   }
 }

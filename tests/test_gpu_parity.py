@@ -23,6 +23,11 @@ pytestmark = pytest.mark.gpu
 ra = pytest.importorskip("ring_ulysses_sequence_amd")
 
 BF16_ATOL, BF16_COS, FP32_ATOL = 1e-2, 0.999, 1e-5
+# lse of a bf16 call: P is rounded to bf16 (relative error <= 2^-8) before it
+# enters P V, and the denominator sums those same rounded weights so that O
+# stays an exact convex combination of V rows; the log-sum-exp therefore
+# carries up to ln(1 + 2^-8) = 3.9e-3 of that rounding (plus fp32 noise).
+LSE_BF16_ATOL = 4e-3
 
 
 def say(*a):
@@ -154,7 +159,7 @@ def test_dit_shard_fused(dit, rank):
     torch.cuda.synchronize()
     ref_o, ref_lse = oracle_share(q, k, v, w, rank)
     check_bf16(o.cpu(), ref_o, f"{w.name} r{rank} O")
-    assert oracle.max_abs_err(lse.cpu(), ref_lse) <= 1e-3
+    assert oracle.max_abs_err(lse.cpu(), ref_lse) <= LSE_BF16_ATOL
     # communication really happened: differs from local-only attention
     loc = oracle.local_only_attention(q_r.cpu(), kb[rank].cpu(), vb[rank].cpu())
     assert oracle.max_abs_err(o.cpu(), loc) > 0
@@ -172,7 +177,7 @@ def test_dit_shard_composable_matches(dit):
     torch.cuda.synchronize()
     ref_o, ref_lse = oracle_share(q, k, v, w, r)
     check_bf16(o_c.cpu(), ref_o, f"{w.name} composable r{r}")
-    assert oracle.max_abs_err(lse_c.cpu(), ref_lse) <= 1e-3
+    assert oracle.max_abs_err(lse_c.cpu(), ref_lse) <= LSE_BF16_ATOL
     assert oracle.max_abs_err(o_c.cpu(), o_f.cpu()) <= BF16_ATOL
 
 
@@ -203,9 +208,10 @@ def test_block_attn_partials_and_stats(dit):
     ro, rl, rm, rll = oracle.attention(q[:, r * Sb:(r + 1) * Sb], k[:, j * Sb:(j + 1) * Sb],
                                        v[:, j * Sb:(j + 1) * Sb])
     check_bf16(o.cpu(), ro, "block_attn o")
-    assert oracle.max_abs_err(lse.cpu(), rl) <= 1e-3
+    assert oracle.max_abs_err(lse.cpu(), rl) <= LSE_BF16_ATOL
     assert oracle.max_abs_err(m.cpu(), rm) <= 1e-4 * max(1.0, float(np.abs(rm).max()))
-    np.testing.assert_allclose(l.cpu().numpy(), rll, rtol=2e-3)
+    # l sums bf16-rounded weights: relative error up to 2^-8
+    np.testing.assert_allclose(l.cpu().numpy(), rll, rtol=4e-3)
     np.testing.assert_allclose(lse.cpu().numpy(),
                                m.cpu().numpy() + np.log(l.cpu().numpy()), atol=1e-5)
 
@@ -280,7 +286,7 @@ def test_long_context_causal_rank3():
     got = o[:, rows][:, :, heads].cpu()
     check_bf16(got, ref_o, f"{w.name} sampled")
     assert oracle.rel_l2(got, ref_o) < 2e-2
-    assert oracle.max_abs_err(lse[:, rows][:, :, heads].cpu(), ref_lse) <= 1e-3
+    assert oracle.max_abs_err(lse[:, rows][:, :, heads].cpu(), ref_lse) <= LSE_BF16_ATOL
 
 
 # ------------------------------------------------------------ C5 padded causal
@@ -305,7 +311,7 @@ def test_padded_causal_all_ranks(padded, path):
         rows = real_rows(w, r)
         ref_o, ref_lse = oracle_share(q, k, v, w, r, rows=rows)
         check_bf16(o[:, rows].cpu(), ref_o, f"{w.name} {path} r{r}")
-        assert oracle.max_abs_err(lse[:, rows].cpu(), ref_lse) <= 2e-3
+        assert oracle.max_abs_err(lse[:, rows].cpu(), ref_lse) <= LSE_BF16_ATOL
 
 
 def test_padded_skipped_blocks_never_read(padded):
