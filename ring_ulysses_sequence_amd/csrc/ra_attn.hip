@@ -156,25 +156,39 @@ __device__ __forceinline__ float online_update(float (&s)[NS], RowState& st, flo
 // check.  The copy picks, for every LDS position, the global 16-byte chunk
 // that belongs there under an XOR swizzle that keeps the matrix-core operand
 // reads free of bank conflicts:
-//   K: chunk c of key row r is stored at chunk c ^ (r & 15)       (D = 128)
-//                                          c ^ ((r >> 1) & 7)     (D = 64)
-//   V: chunk c of key row r is stored at chunk c ^ ((r & 3) << 2) (D = 128)
+//   K: chunk c of key row r is stored at chunk c ^ (r & 15)          (D = 128)
+//                                          c ^ ((r >> 1) & 7)        (D = 64)
+//   V: chunk c of key row r is stored at chunk c ^ ((r & 3) << 2)    (D = 128)
 //                                          c ^ (((r >> 1) & 1) << 2) (D = 64)
 // K feeds S^T = K Q^T as the A operand with ds_read_b128.  V feeds
 // O^T += V^T P^T as the A operand through ds_read_b64_tr_b16: inside each
 // 16-lane group, lane j receives element j%4 of the 64-bit rows supplied by
 // lanes j/4, j/4+4, j/4+8, j/4+12; supplier r = 4e + q points at
 // V[key_e][d0 + 4q .. d0 + 4q + 3], so lane j gets V[key_0..3][d0 + j].
+//
+// Software pipeline (per wave, iteration n over the visited tiles):
+//   LDS holds K(n+1) and V(n) (copied during iteration n-1);
+//   copy K(n+2) and V(n+1) into the buffers freed by iteration n-1;
+//   mask / row max / rescale of tile n's scores (already in registers);
+//   S^T(n+1) = K(n+1) Q^T on the matrix cores, interleaved instruction by
+//   instruction with the exponentials of tile n on the vector ALUs;
+//   O^T += V(n)^T P(n)^T;
+//   wait for this wave's copies, barrier.
+// K therefore runs one tile ahead of V, and the two buffers of each stay
+// enough.  The loop is unrolled by two so buffer parities are constants.
 template <int D>
 struct Bf16Cfg {
   static constexpr int BC = 64;                   // keys per tile
   static constexpr int ROWB = D * 2;              // bytes per key row in LDS
   static constexpr int TILE = BC * ROWB;          // one K or V tile
-  static constexpr int STAGE = 2 * TILE;          // K tile + V tile
+  static constexpr int KB = 0;                    // K buffers at KB + p*TILE
+  static constexpr int VB = 2 * TILE;             // V buffers at VB + p*TILE
+  static constexpr int LDS = 4 * TILE;
   static constexpr int CHUNKS = D / 8;            // 16-byte chunks per row
   static constexpr int DMA = TILE / 1024 / kWaves;  // 1 KiB copies per wave per tile
   static constexpr int NC = D / 16;               // k-steps of S^T = K Q^T
   static constexpr int NDT = D / 32;              // 32-row d tiles of O^T
+  static constexpr int NS = BC / 2;               // scores per lane per tile
 };
 
 template <int D>
@@ -188,44 +202,272 @@ __device__ __forceinline__ int swz_v(int r, int c) {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
+__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access
 constexpr float kRescaleSlack = 8.0f;   // lazy rescale threshold (base-2 units)
 
-// Copy K/V tile `ti` of ring block `bi` (rows kt0 .. kt0+63 of batch b,
-// head h) HBM -> LDS stage `dst` with the buffer unit: each wave copies its
-// C::DMA KiB of K and of V; rows past the block end read as zeros.
+// Position in the visited-tile sequence: tile t (of n) of visited block blk.
+struct Cursor {
+  int blk, t, n;
+};
+
+__device__ __forceinline__ Cursor cursor_first(const AttnArgs& a, long long q_hi) {
+  Cursor c{0, 0, 0};
+  while (c.blk < a.nblk && (c.n = tiles_of<64>(a, c.blk, q_hi)) == 0) ++c.blk;
+  return c;
+}
+__device__ __forceinline__ Cursor cursor_next(const AttnArgs& a, long long q_hi, Cursor c) {
+  if (c.blk >= a.nblk) return c;
+  if (++c.t < c.n) return c;
+  c.t = 0;
+  ++c.blk;
+  while (c.blk < a.nblk && (c.n = tiles_of<64>(a, c.blk, q_hi)) == 0) ++c.blk;
+  return c;
+}
+
+// Everything a wave keeps in registers across tiles.
 template <int D>
-__device__ __forceinline__ void issue_tile(const AttnArgs& a, int bi, int ti, int b, int h,
-                                           int HD2, int wave, const int* voff,
-                                           const int* voffv, char* dst_stage) {
+struct WaveState {
   using C = Bf16Cfg<D>;
-  const KVBlock& kb = a.blk[bi];
+  bf16x8 qf[C::NC];        // Q fragment (B operand of S^T)
+  f32x16 oacc[C::NDT];     // O^T accumulators (unnormalised u)
+  float m_ref;             // reference max (base 2), -inf before any key
+  float m_true;            // exact running max (base 2)
+  float l_run;             // this lane's half of sum of bf16(2^(s - m_ref))
+  int kaddr[C::NC];        // LDS byte offsets of the K operand reads
+  int vaddr[C::NDT];       // LDS byte offsets of the V operand reads
+  int voffk[C::DMA];       // copy source offsets (K) within a tile
+  int voffv[C::DMA];       // copy source offsets (V) within a tile
+};
+
+// Copy one K or V tile (rows kt0 .. kt0+63 of batch b, head h of `src`, a
+// visited block of `len` rows) into LDS at `dst`; each wave copies C::DMA KiB.
+template <int D>
+__device__ __forceinline__ void copy_tile(const void* src, int len, int ti, int b, int h,
+                                          int H, int HD2, int wave, const int* voff,
+                                          char* dst) {
+  using C = Bf16Cfg<D>;
   const int kt0 = ti * C::BC;
-  const int rows = min(C::BC, kb.len - kt0);
-  const long long off = (((long long)b * kb.len + kt0) * a.H + h) * (D * 2);
+  const int rows = min(C::BC, len - kt0);
+  const long long off = (((long long)b * len + kt0) * H + h) * (D * 2);
   const int nrec = (rows - 1) * HD2 + D * 2;
-  __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)kb.k + off), 0, nrec, kRsrcWord3);
-  __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)kb.v + off), 0, nrec, kRsrcWord3);
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)src + off), 0, nrec, kRsrcWord3);
 #pragma unroll
-  for (int i = 0; i < C::DMA; ++i) {
-    char* dst = dst_stage + (wave * C::DMA + i) * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_ptr)dst, 16, voff[i], 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_ptr)(dst + C::TILE), 16, voffv[i], 0, 0, 0);
+  for (int i = 0; i < C::DMA; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (lds_void_ptr)(dst + (wave * C::DMA + i) * 1024), 16, voff[i], 0, 0, 0);
+}
+
+// S^T of one 64-key tile: the K tile at LDS byte offset kb times Q^T.
+template <int D>
+__device__ __forceinline__ void scores_tile(char* smem, int kb, const WaveState<D>& w,
+                                            f32x16 (&acc)[2]) {
+  using C = Bf16Cfg<D>;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    acc[kt] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) {
+      const bf16x8 kf = *(const bf16x8*)(smem + kb + kt * 32 * C::ROWB + w.kaddr[c]);
+      acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, w.qf[c], acc[kt], 0, 0, 0);
+    }
   }
+}
+
+// Exponentials of one tile against the reference max, their bf16 copy P^T
+// and the denominator over the same rounded weights ([RA] §3.2).
+template <int NS>
+__device__ __forceinline__ void exp_tile(float (&s)[NS], float m_use, float c_scale,
+                                         bf16x8 (&pb)[NS / 8], float& l_run) {
+#pragma unroll
+  for (int i = 0; i < NS; ++i) s[i] = fast_exp2(fmaf(s[i], c_scale, -m_use));
+#pragma unroll
+  for (int G = 0; G < NS / 8; ++G)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[G][e] = (__bf16)s[(G >> 1) * 16 + (G & 1) * 8 + e];
+  float l0 = 0.0f, l1 = 0.0f;
+#pragma unroll
+  for (int G = 0; G < NS / 8; ++G)
+#pragma unroll
+    for (int e = 0; e < 8; e += 4) {
+      const bf16x2 p0 = {pb[G][e], pb[G][e + 1]}, p1 = {pb[G][e + 2], pb[G][e + 3]};
+      l0 = __builtin_amdgcn_fdot2_f32_bf16(p0, kOnes2, l0, false);
+      l1 = __builtin_amdgcn_fdot2_f32_bf16(p1, kOnes2, l1, false);
+    }
+  l_run += l0 + l1;
+}
+
+// One pipeline step.  PAR = n & 1: K(n+1) sits in K buffer PAR^1, V(n) in
+// V buffer PAR; the copies go to K buffer PAR and V buffer PAR^1.
+template <int D, int PAR>
+__device__ __forceinline__ void pipeline_step(
+    const AttnArgs& a, char* smem, WaveState<D>& w, float (&s_cur)[Bf16Cfg<D>::NS],
+    float (&s_nxt)[Bf16Cfg<D>::NS], Cursor& t0, Cursor& t1, Cursor& t2, long long q_hi,
+    long long wq_lo, long long wq_hi, int wrows, int col, int half, int b, int h,
+    int HD2, int wave) {
+  using C = Bf16Cfg<D>;
+  constexpr int BC = C::BC;
+  const float c_scale = a.scale_log2;
+  // copies for the tiles two (K) and one (V) ahead
+  if (t1.blk < a.nblk) {
+    const KVBlock& kb1 = a.blk[t1.blk];
+    copy_tile<D>(kb1.v, kb1.len, t1.t, b, h, a.H, HD2, wave, w.voffv,
+                 smem + C::VB + (PAR ^ 1) * C::TILE);
+  }
+  if (t2.blk < a.nblk) {
+    const KVBlock& kb2 = a.blk[t2.blk];
+    copy_tile<D>(kb2.k, kb2.len, t2.t, b, h, a.H, HD2, wave, w.voffk,
+                 smem + C::KB + PAR * C::TILE);
+  }
+  // tile n: classification, mask, row max, lazy rescale
+  const KVBlock& kb0 = a.blk[t0.blk];
+  const int kt0 = t0.t * BC;
+  const long long kp0 = kb0.k_pos0 + kt0;
+  const bool live0 = wrows > 0 && !(a.causal && kp0 > wq_hi);
+  bool live1 = false;
+  if (t1.blk < a.nblk) {
+    const long long kp1 = a.blk[t1.blk].k_pos0 + (long long)t1.t * BC;
+    live1 = wrows > 0 && !(a.causal && kp1 > wq_hi);
+  }
+  float m_use = 0.0f;
+  if (live0) {
+    long long lim_ll = kb0.len - kt0;
+    if (a.valid_len - kp0 < lim_ll) lim_ll = a.valid_len - kp0;
+    if (lim_ll < BC || (a.causal && kp0 + BC - 1 > wq_lo)) {
+      // key j of the tile is masked for this lane's query when
+      // j > (query - first key) or j >= klim (32-bit, tile relative)
+      const int klim = (int)max(0LL, lim_ll);
+      int t = min(klim, BC) - 1 - 4 * half;
+      if (a.causal) {
+        // wave-uniform offset of the first query from the first key, clamped
+        // on the scalar unit so the per-lane part stays 32-bit
+        const long long d = wq_lo - kp0;
+        const int dc = (int)(d < -2 * BC ? -2 * BC : (d > 2 * BC ? 2 * BC : d));
+        const int rel = max(-1, dc + col - 4 * half);
+        t = min(t, rel);
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (32 * kt + 8 * (v >> 2) + (v & 3) > t) s_cur[kt * 16 + v] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < C::NS; ++i) mx = fmaxf(mx, s_cur[i]);
+    mx = pair_max(mx) * c_scale;
+    w.m_true = fmaxf(w.m_true, mx);
+    const bool need = mx > w.m_ref + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      // move the reference: u and l are rescaled together, so u / l keeps
+      // the value of [RA] §3.2's recurrence while p = 2^(s - m_ref) <= 2^8
+      const float m_new = need ? mx : w.m_ref;
+      const float alpha = fast_exp2(w.m_ref - m_new);
+      w.l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < C::NDT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) w.oacc[i][v] *= alpha;
+      w.m_ref = m_new;
+    }
+    m_use = w.m_ref == -INFINITY ? 0.0f : w.m_ref;
+  }
+  // S^T(n+1) on the matrix cores alongside the exponentials of tile n
+  constexpr int kbuf_next = C::KB + (PAR ^ 1) * C::TILE;
+  f32x16 acc[2];
+  bf16x8 pb[C::NS / 8];
+  if (live0 && live1) {
+    // Explicit interleave: step i issues the K read of step i+2, the
+    // matrix-core op of step i and 16/NC exponentials (with their bf16
+    // conversion and denominator update); sched_barrier keeps the steps in
+    // this order so the vector work of tile n fills the matrix-core
+    // latency of tile n+1.
+    constexpr int NSTEP = 2 * C::NC;
+    constexpr int PER = C::NS / NSTEP;  // scores per step (2 for D=128)
+    bf16x8 kf[3];
+    // step i works on score tile kt = i % 2 with k-step c = i / 2, so
+    // consecutive matrix-core ops never depend on each other
+    auto kread = [&](int i) -> bf16x8 {
+      return *(const bf16x8*)(smem + kbuf_next + (i % 2) * 32 * C::ROWB + w.kaddr[i / 2]);
+    };
+    kf[0] = kread(0);
+    kf[1] = kread(1);
+    float lp[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+      if (i + 2 < NSTEP) kf[(i + 2) % 3] = kread(i + 2);
+      const int kt = i % 2, c = i / 2;
+      acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], w.qf[c],
+                                                        c == 0 ? f32x16{} : acc[kt], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < PER; j += 2) {
+        const int v = i * PER + j;  // score index, even
+        const float e0 = fast_exp2(fmaf(s_cur[v], c_scale, -m_use));
+        const float e1 = fast_exp2(fmaf(s_cur[v + 1], c_scale, -m_use));
+        const int G = 2 * (v >> 4) + ((v & 15) >> 3), e = v & 7;
+        pb[G][e] = (__bf16)e0;
+        pb[G][e + 1] = (__bf16)e1;
+        const bf16x2 pr = {pb[G][e], pb[G][e + 1]};
+        lp[(v >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, lp[(v >> 1) & 1], false);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    w.l_run += lp[0] + lp[1];
+  } else {
+    if (live1) scores_tile<D>(smem, kbuf_next, w, acc);
+    if (live0) exp_tile<C::NS>(s_cur, m_use, c_scale, pb, w.l_run);
+  }
+  if (live1) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s_nxt[kt * 16 + v] = acc[kt][v];
+  }
+  // O^T += V(n)^T P(n)^T: fragment j = (G = j / NDT, dt = j % NDT) is read
+  // two ops ahead, and consecutive ops accumulate into different d tiles
+  if (live0) {
+    char* vl = smem + C::VB + PAR * C::TILE;
+    constexpr int NJ = (BC / 16) * C::NDT;
+    auto vread = [&](int j) -> bf16x8 {
+      char* p0 = vl + (j / C::NDT) * 16 * C::ROWB + w.vaddr[j % C::NDT];
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p0);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p0 + 8 * C::ROWB));
+      bf16x8 vf;
+      __builtin_memcpy(&vf, &lo, 8);
+      __builtin_memcpy((char*)&vf + 8, &hi, 8);
+      return vf;
+    };
+    bf16x8 vf[3];
+    vf[0] = vread(0);
+    vf[1] = vread(1);
+    // this phase is matrix-core bound: give it issue priority over the
+    // other wave on the SIMD, whose exponentials fill the gaps
+    __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if (j + 2 < NJ) vf[(j + 2) % 3] = vread(j + 2);
+      const int G = j / C::NDT, dt = j % C::NDT;
+      w.oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j % 3], pb[G], w.oacc[dt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's copies landed
+  __syncthreads();                // everyone's copies landed, everyone done reading
+  t0 = t1;
+  t1 = t2;
+  t2 = cursor_next(a, q_hi, t2);
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ring_attn_bf16(const AttnArgs a) {
   using C = Bf16Cfg<D>;
-  constexpr int BC = C::BC;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -246,177 +488,77 @@ void ring_attn_bf16(const AttnArgs a) {
   const long long HD = (long long)a.H * D;
   const int HD2 = a.H * D * 2;  // bytes between consecutive key rows
 
-  // Q fragment (B operand of S^T = K Q^T): query wrow0 + col, features
-  // 16c + 8*half .. +7.
-  bf16x8 qf[C::NC];
+  WaveState<D> w;
   {
     const int r = wrow0 + col;
     const __bf16* qp = (const __bf16*)a.q + ((long long)b * a.Sq + r) * HD + (long long)h * D;
 #pragma unroll
     for (int c = 0; c < C::NC; ++c)
-      qf[c] = r < a.Sq ? *(const bf16x8*)(qp + 16 * c + 8 * half) : bf16x8{};
+      w.qf[c] = r < a.Sq ? *(const bf16x8*)(qp + 16 * c + 8 * half) : bf16x8{};
   }
-
-  // per-lane constant parts of the copy sources and the LDS read addresses
-  int voff[C::DMA];   // byte offset (within a tile's rows) of this lane's chunk
-  int voffv[C::DMA];
 #pragma unroll
   for (int i = 0; i < C::DMA; ++i) {
     const int p = (wave * C::DMA + i) * 64 + lane;  // physical 16B chunk in the tile
     const int r = p / C::CHUNKS, pc = p % C::CHUNKS;
-    voff[i] = r * HD2 + swz_k<D>(r, pc) * 16;
-    voffv[i] = r * HD2 + swz_v<D>(r, pc) * 16;
+    w.voffk[i] = r * HD2 + swz_k<D>(r, pc) * 16;
+    w.voffv[i] = r * HD2 + swz_v<D>(r, pc) * 16;
   }
-  int kaddr[C::NC];   // K operand: row col, logical chunk 2c + half
 #pragma unroll
-  for (int c = 0; c < C::NC; ++c) kaddr[c] = col * C::ROWB + swz_k<D>(col, 2 * c + half) * 16;
-  int vaddr[C::NDT];  // V operand: supplier row 4*half + e, d0 = 32dt + 16*(group&1) + 4q
+  for (int c = 0; c < C::NC; ++c) w.kaddr[c] = col * C::ROWB + swz_k<D>(col, 2 * c + half) * 16;
   {
     const int j = lane & 15, e = j >> 2, q = j & 3, g = lane >> 4;
-    const int kl = 4 * half + e;
+    const int kl = 4 * half + e;  // supplier row within a 16-key group
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) {
       const int d0 = 32 * dt + 16 * (g & 1) + 4 * q;
-      vaddr[dt] = kl * C::ROWB + swz_v<D>(kl, d0 >> 3) * 16 + (d0 & 7) * 2;
+      w.vaddr[dt] = kl * C::ROWB + swz_v<D>(kl, d0 >> 3) * 16 + (d0 & 7) * 2;
     }
   }
-
-  f32x16 oacc[C::NDT];
 #pragma unroll
-  for (int i = 0; i < C::NDT; ++i) oacc[i] = f32x16{};
-  float m_ref = -INFINITY;   // reference max (base 2) of this lane's query
-  float m_true = -INFINITY;  // exact running max (base 2)
-  float l_run = 0.0f;        // this lane's half of sum 2^(s - m_ref)
+  for (int i = 0; i < C::NDT; ++i) w.oacc[i] = f32x16{};
+  w.m_ref = -INFINITY;
+  w.m_true = -INFINITY;
+  w.l_run = 0.0f;
 
-  // ---- tile cursor over (block, tile) in ring order ----
-  int cb = 0, ct = 0, cn = 0;
-  while (cb < a.nblk && (cn = tiles_of<BC>(a, cb, q_hi)) == 0) ++cb;
-  bool have = cb < a.nblk;
-
-  const float c_scale = a.scale_log2;
-  int stage = 0;
-  if (have) issue_tile<D>(a, cb, ct, b, h, HD2, wave, voff, voffv, smem);
+  // prologue: K(0), V(0), K(1) into K0, V0, K1; scores of tile 0
+  Cursor t0 = cursor_first(a, q_hi);
+  Cursor t1 = cursor_next(a, q_hi, t0);
+  Cursor t2 = cursor_next(a, q_hi, t1);
+  float sA[C::NS], sB[C::NS];
+  if (t0.blk < a.nblk) {
+    const KVBlock& kb = a.blk[t0.blk];
+    copy_tile<D>(kb.k, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffk, smem + C::KB);
+    copy_tile<D>(kb.v, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffv, smem + C::VB);
+  }
+  if (t1.blk < a.nblk) {
+    const KVBlock& kb = a.blk[t1.blk];
+    copy_tile<D>(kb.k, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffk, smem + C::KB + C::TILE);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-
-  while (have) {
-    int nb = cb, nt = ct + 1, nn = cn;
-    if (nt >= nn) {
-      nt = 0;
-      ++nb;
-      while (nb < a.nblk && (nn = tiles_of<BC>(a, nb, q_hi)) == 0) ++nb;
+  if (t0.blk < a.nblk) {
+    const long long kp0 = a.blk[t0.blk].k_pos0 + (long long)t0.t * C::BC;
+    if (wrows > 0 && !(a.causal && kp0 > wq_hi)) {
+      f32x16 acc[2];
+      scores_tile<D>(smem, C::KB, w, acc);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sA[kt * 16 + v] = acc[kt][v];
     }
-    const bool has_next = nb < a.nblk;
-    if (has_next)
-      issue_tile<D>(a, nb, nt, b, h, HD2, wave, voff, voffv, smem + (stage ^ 1) * C::STAGE);
+  }
+  __syncthreads();  // K buffer 0 is free for K(2)
 
-    const KVBlock& kb = a.blk[cb];
-    const int kt0 = ct * BC;
-    const long long kp0 = kb.k_pos0 + kt0;
-    const bool wave_live = wrows > 0 && !(a.causal && kp0 > wq_hi);
-    if (wave_live) {
-      const int sb = stage * C::STAGE;
-      float s[BC / 2];
-#pragma unroll
-      for (int kt = 0; kt < BC / 32; ++kt) {
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int c = 0; c < C::NC; ++c) {
-          const bf16x8 kf = *(const bf16x8*)(smem + sb + kt * 32 * C::ROWB + kaddr[c]);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[kt * 16 + v] = acc[v];
-      }
-      // element mask on diagonal / ragged / padded tiles, in 32-bit
-      // positions relative to the tile: key j of the tile is masked for the
-      // lane's query when j > (query - first key) or j >= klim
-      long long lim_ll = kb.len - kt0;
-      if (a.valid_len - kp0 < lim_ll) lim_ll = a.valid_len - kp0;
-      const bool need_mask = lim_ll < BC || (a.causal && kp0 + BC - 1 > wq_lo);
-      if (need_mask) {
-        const int klim = (int)max(0LL, lim_ll);  // <= BC here or the causal test fired
-        int t = min(klim, BC) - 1 - 4 * half;    // masked if jconst > t
-        if (a.causal) {
-          long long rel = wq_lo + col - kp0 - 4 * half;
-          if (rel < -1) rel = -1;
-          if (rel < t) t = (int)rel;
-        }
-#pragma unroll
-        for (int kt = 0; kt < BC / 32; ++kt)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int jc = 32 * kt + 8 * (v >> 2) + (v & 3);
-            if (jc > t) s[kt * 16 + v] = -INFINITY;
-          }
-      }
-      // online softmax ([RA] §3.2) with a lazily moved reference max: the
-      // accumulators are rescaled only when the row max passes the
-      // reference by more than kRescaleSlack, so p = 2^(s - m_ref) <= 2^8;
-      // u / l is unchanged because u and l share the reference.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < BC / 2; ++i) mx = fmaxf(mx, s[i]);
-      mx = pair_max(mx) * c_scale;
-      m_true = fmaxf(m_true, mx);
-      const bool need = mx > m_ref + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float m_new = need ? mx : m_ref;
-        const float alpha = fast_exp2(m_ref - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < C::NDT; ++i)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
-        m_ref = m_new;
-      }
-      const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
-#pragma unroll
-      for (int i = 0; i < BC / 2; ++i) s[i] = fast_exp2(fmaf(s[i], c_scale, -m_use));
-      bf16x8 pb[BC / 16];
-#pragma unroll
-      for (int G = 0; G < BC / 16; ++G)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[G][e] = (__bf16)s[(G >> 1) * 16 + (G & 1) * 8 + e];
-      // the denominator sums the SAME bf16-rounded weights that enter P V, so
-      // u / l stays an exact convex combination of V rows whatever the
-      // rounding (one v_dot2 against (1, 1) per pair of weights)
-      float lsum0 = 0.0f, lsum1 = 0.0f;
-#pragma unroll
-      for (int G = 0; G < BC / 16; ++G)
-#pragma unroll
-        for (int e = 0; e < 8; e += 4) {
-          const bf16x2 p0 = {pb[G][e], pb[G][e + 1]}, p1 = {pb[G][e + 2], pb[G][e + 3]};
-          lsum0 = __builtin_amdgcn_fdot2_f32_bf16(p0, kOnes2, lsum0, false);
-          lsum1 = __builtin_amdgcn_fdot2_f32_bf16(p1, kOnes2, lsum1, false);
-        }
-      l_run += lsum0 + lsum1;
-      char* vl = smem + sb + C::TILE;
-#pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-        for (int G = 0; G < BC / 16; ++G) {
-          char* p0 = vl + G * 16 * C::ROWB + vaddr[dt];
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p0);
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p0 + 8 * C::ROWB));
-          bf16x8 vf;
-          __builtin_memcpy(&vf, &lo, 8);
-          __builtin_memcpy((char*)&vf + 8, &hi, 8);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[G], oacc[dt], 0, 0, 0);
-        }
-    }
-
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile landed
-    __syncthreads();                // everyone's copies landed, everyone done reading
-    cb = nb;
-    ct = nt;
-    cn = nn;
-    have = has_next;
-    stage ^= 1;
+  while (t0.blk < a.nblk) {
+    pipeline_step<D, 0>(a, smem, w, sA, sB, t0, t1, t2, q_hi, wq_lo, wq_hi, wrows, col, half,
+                        b, h, HD2, wave);
+    if (t0.blk >= a.nblk) break;
+    pipeline_step<D, 1>(a, smem, w, sB, sA, t0, t1, t2, q_hi, wq_lo, wq_hi, wrows, col, half,
+                        b, h, HD2, wave);
   }
 
   // ---- epilogue: o = u / l, lse = m + ln l ([RA] §3.2; [SPD] §四) ----
-  const float l_tot = pair_sum(l_run);
+  const float l_tot = pair_sum(w.l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const int r = wrow0 + col;
   if (wrows > 0 && r < a.Sq) {
@@ -426,8 +568,8 @@ void ring_attn_bf16(const AttnArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * dt + 8 * g + 4 * half;
-        const float x0 = oacc[dt][4 * g + 0] * inv, x1 = oacc[dt][4 * g + 1] * inv;
-        const float x2 = oacc[dt][4 * g + 2] * inv, x3 = oacc[dt][4 * g + 3] * inv;
+        const float x0 = w.oacc[dt][4 * g + 0] * inv, x1 = w.oacc[dt][4 * g + 1] * inv;
+        const float x2 = w.oacc[dt][4 * g + 2] * inv, x3 = w.oacc[dt][4 * g + 3] * inv;
         if (a.o_fp32) {
           *(float4*)((float*)a.o + ro + d) = float4{x0, x1, x2, x3};
         } else {
@@ -440,9 +582,9 @@ void ring_attn_bf16(const AttnArgs a) {
     if (half == 0) {
       const long long so = ((long long)b * a.Sq + r) * a.H + h;
       const bool seen = l_tot > 0.0f;
-      if (a.lse) a.lse[so] = seen ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
-      if (a.m_out) a.m_out[so] = seen ? m_true * kLn2 : -INFINITY;
-      if (a.l_out) a.l_out[so] = seen ? l_tot * fast_exp2(m_ref - m_true) : 0.0f;
+      if (a.lse) a.lse[so] = seen ? (w.m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
+      if (a.m_out) a.m_out[so] = seen ? w.m_true * kLn2 : -INFINITY;
+      if (a.l_out) a.l_out[so] = seen ? l_tot * fast_exp2(w.m_ref - w.m_true) : 0.0f;
     }
   }
 }
