@@ -66,12 +66,28 @@ typedef enum { RA_SKIP = 0, RA_FULL = 1, RA_DIAG = 2 } ra_block_class;
 #define RA_MAX_P 64          /* largest ring degree one call accepts */
 #define RA_PAD_MULTIPLE 16   /* default per-rank padding granularity */
 
+/* Process-wide options (ra_set_option). */
+typedef enum { RA_OPT_ATTN_KERNEL = 0, RA_OPT_COUNT = 1 } ra_option;
+/* Values of RA_OPT_ATTN_KERNEL: which bf16 attention kernel the device
+ * entry points launch.  AUTO picks the faster one measured for the shape
+ * (currently the 128-row kernel everywhere).  Both compute the same
+ * function; the choice only changes tiling and scheduling. */
+#define RA_KERNEL_AUTO 0
+#define RA_KERNEL_BR128 1  /* 4 waves x 32 query rows, software-pipelined */
+#define RA_KERNEL_BR256 2  /* 8 waves x 32 query rows, two groups in ping-pong */
+
 /* ---------------------------------------------------------------------
  * Host-only helpers (no GPU needed; exported for tests and schedule dumps)
  * ------------------------------------------------------------------- */
 
 /* ABI version of this header (bumped on any signature change). */
 int ra_abi_version(void);
+
+/* Set a process-wide option (ra_option) to `value`; takes effect for
+ * launches made after the call (all threads).  RA_ERR_RANGE for an unknown
+ * option or value.  ra_get_option returns the current value. */
+ra_status ra_set_option(int option, int value);
+int ra_get_option(int option);
 
 /* Message of the last error on the calling thread ("" if none).  The
  * pointer stays valid until the next ra_* call on this thread. */

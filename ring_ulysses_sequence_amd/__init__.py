@@ -32,10 +32,12 @@ RA_BF16, RA_FP32 = 0, 1
 RA_SKIP, RA_FULL, RA_DIAG = 0, 1, 2
 RA_MAX_P = 64
 RA_PAD_MULTIPLE = 16
+RA_OPT_ATTN_KERNEL = 0
+RA_KERNEL_AUTO, RA_KERNEL_BR128, RA_KERNEL_BR256 = 0, 1, 2
 
 # Every symbol include/ringattn.h declares.
 EXPORTED = (
-    "ra_abi_version", "ra_last_error", "ra_padded_len", "ra_shard_range",
+    "ra_abi_version", "ra_set_option", "ra_get_option", "ra_last_error", "ra_padded_len", "ra_shard_range",
     "ra_classify_block", "ra_ring_schedule", "ra_block_attn_fwd",
     "ra_ring_merge", "ra_ring_attn_fwd", "ra_seq2head", "ra_head2seq",
 )
@@ -60,6 +62,8 @@ def _load():
     c_fp = ctypes.POINTER(ctypes.c_float)
     sig = {
         "ra_abi_version": (c_int, []),
+        "ra_set_option": (c_int, [c_int, c_int]),
+        "ra_get_option": (c_int, [c_int]),
         "ra_last_error": (ctypes.c_char_p, []),
         "ra_padded_len": (c_ll, [c_ll, c_int, c_int]),
         "ra_shard_range": (c_int, [c_ll, c_int, c_int, ctypes.POINTER(c_ll), ctypes.POINTER(c_ll)]),
@@ -102,6 +106,15 @@ def _check(status: int, what: str):
 # --------------------------------------------------------------- host helpers
 def abi_version() -> int:
     return _load().ra_abi_version()
+
+
+def set_attn_kernel(choice: int) -> None:
+    """Force the bf16 attention kernel (RA_KERNEL_AUTO / _BR128 / _BR256)."""
+    _check(_load().ra_set_option(RA_OPT_ATTN_KERNEL, choice), "set_attn_kernel")
+
+
+def get_attn_kernel() -> int:
+    return _load().ra_get_option(RA_OPT_ATTN_KERNEL)
 
 
 def padded_len(S: int, P: int, pad_multiple: int = RA_PAD_MULTIPLE) -> int:
@@ -308,8 +321,9 @@ def ring_attn_composable(q_r, k_blocks, v_blocks, rank: int, *, causal: bool = F
 
 
 __all__ = [
-    "lib", "abi_version", "padded_len", "shard_range", "classify_block", "ring_schedule",
+    "lib", "abi_version", "set_attn_kernel", "get_attn_kernel", "padded_len", "shard_range", "classify_block", "ring_schedule",
     "block_attn_fwd", "ring_merge", "ring_attn_fwd", "seq2head", "head2seq",
     "ring_attn_composable", "EXPORTED", "LIB_PATH", "LibraryMissing",
     "RA_BF16", "RA_FP32", "RA_SKIP", "RA_FULL", "RA_DIAG", "RA_MAX_P", "RA_PAD_MULTIPLE",
+    "RA_KERNEL_AUTO", "RA_KERNEL_BR128", "RA_KERNEL_BR256",
 ]

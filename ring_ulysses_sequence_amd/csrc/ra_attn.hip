@@ -365,8 +365,10 @@ __device__ __forceinline__ void pipeline_step(
     if (__builtin_amdgcn_ballot_w64(need)) {
       // move the reference: u and l are rescaled together, so u / l keeps
       // the value of [RA] §3.2's recurrence while p = 2^(s - m_ref) <= 2^8
+      // lanes that keep their reference use alpha = 1 (a lane still at
+      // -inf must not form 2^(-inf - -inf))
       const float m_new = need ? mx : w.m_ref;
-      const float alpha = fast_exp2(w.m_ref - m_new);
+      const float alpha = need ? fast_exp2(w.m_ref - mx) : 1.0f;
       w.l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < C::NDT; ++i)
@@ -590,6 +592,329 @@ void ring_attn_bf16(const AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 kernel, 8-wave ping-pong variant (256 query rows per workgroup)
+// ---------------------------------------------------------------------------
+// Waves 0-3 (group 0) and 4-7 (group 1) each hold one wave per SIMD.  Time
+// is cut into slots separated by workgroup barriers; group 1 runs one slot
+// behind group 0, and every wave alternates
+//   matrix phase:  S^T(n+1) = K(n+1) Q^T and O^T += V(n)^T P(n)^T  (32 ops)
+//   vector phase:  mask, row max, lazy rescale, exponentials of tile n+1
+// so in every slot one wave of each SIMD keeps the matrix core busy while
+// the other does the softmax.  K/V tiles live in a ring of four LDS stages;
+// tile m is copied (buffer_load ... lds) in slot 2m-4, read by group 0 in
+// slots 2m (K) and 2m+2 (V), by group 1 one slot later, and its stage is
+// reused by tile m+4 from slot 2m+4 on.
+template <int D>
+struct PPCfg {
+  static constexpr int NW = 8;                    // waves per workgroup
+  static constexpr int BR = 32 * NW;              // query rows per workgroup
+  static constexpr int BC = 64;                   // keys per tile
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILE = BC * ROWB;
+  static constexpr int STAGE = 2 * TILE;          // K tile + V tile
+  static constexpr int NBUF = 4;                  // stages in the ring
+  static constexpr int LDS = NBUF * STAGE;
+  static constexpr int CHUNKS = D / 8;
+  static constexpr int DMA = TILE / 1024 / NW;    // 1 KiB copies per wave per tensor
+  static constexpr int NC = D / 16;
+  static constexpr int NDT = D / 32;
+  static constexpr int NS = BC / 2;
+};
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maxima so they are not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Does tile c hold any key this wave's queries may see?
+__device__ __forceinline__ bool pp_live(const AttnArgs& a, const Cursor& c, int wrows,
+                                        long long wq_hi) {
+  if (c.blk >= a.nblk || wrows <= 0) return false;
+  const long long kp = a.blk[c.blk].k_pos0 + (long long)c.t * 64;
+  return !(a.causal && kp > wq_hi);
+}
+
+template <int D>
+__device__ __forceinline__ void pp_copy(const void* src, int len, int ti, int b, int h, int H,
+                                        int HD2, int wave, const int* voff, char* dst) {
+  using C = PPCfg<D>;
+  const int kt0 = ti * C::BC;
+  const int rows = min(C::BC, len - kt0);
+  const long long off = (((long long)b * len + kt0) * H + h) * (D * 2);
+  const int nrec = (rows - 1) * HD2 + D * 2;
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)src + off), 0, nrec, kRsrcWord3);
+#pragma unroll
+  for (int i = 0; i < C::DMA; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (lds_void_ptr)(dst + (wave * C::DMA + i) * 1024), 16, voff[i], 0, 0, 0);
+}
+
+// Copy K and V of tile c (ordinal m) into ring stage m % NBUF.
+template <int D>
+__device__ __forceinline__ void pp_copy_tile(const AttnArgs& a, const Cursor& c, int m, char* smem,
+                                             int b, int h, int HD2, int wave, const int* voffk,
+                                             const int* voffv) {
+  using C = PPCfg<D>;
+  const KVBlock& kb = a.blk[c.blk];
+  char* st = smem + (m & (C::NBUF - 1)) * C::STAGE;
+  pp_copy<D>(kb.k, kb.len, c.t, b, h, a.H, HD2, wave, voffk, st);
+  pp_copy<D>(kb.v, kb.len, c.t, b, h, a.H, HD2, wave, voffv, st + C::TILE);
+}
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void ring_attn_bf16_pp(const AttnArgs a) {
+  using C = PPCfg<D>;
+  constexpr int BC = C::BC;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int grp = wave >> 2;
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  int b, h, qt;
+  tile_coords(a, b, h, qt);
+  const int row0 = qt * C::BR;
+  const int rows_here = min(C::BR, a.Sq - row0);
+  const long long q_lo = a.q_pos0 + row0;
+  const long long q_hi = q_lo + rows_here - 1;
+  const int wrow0 = row0 + wave * 32;
+  const int wrows = min(32, a.Sq - wrow0);
+  const long long wq_lo = a.q_pos0 + wrow0;
+  const long long wq_hi = wq_lo + wrows - 1;
+  const long long HD = (long long)a.H * D;
+  const int HD2 = a.H * D * 2;
+  const float c_scale = a.scale_log2;
+
+  bf16x8 qf[C::NC];
+  {
+    const int r = wrow0 + col;
+    const __bf16* qp = (const __bf16*)a.q + ((long long)b * a.Sq + r) * HD + (long long)h * D;
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c)
+      qf[c] = r < a.Sq ? *(const bf16x8*)(qp + 16 * c + 8 * half) : bf16x8{};
+  }
+  int voffk[C::DMA], voffv[C::DMA];
+#pragma unroll
+  for (int i = 0; i < C::DMA; ++i) {
+    const int p = (wave * C::DMA + i) * 64 + lane;
+    const int r = p / C::CHUNKS, pc = p % C::CHUNKS;
+    voffk[i] = r * HD2 + swz_k<D>(r, pc) * 16;
+    voffv[i] = r * HD2 + swz_v<D>(r, pc) * 16;
+  }
+  int kaddr[C::NC];
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) kaddr[c] = col * C::ROWB + swz_k<D>(col, 2 * c + half) * 16;
+  int vaddr[C::NDT];
+  {
+    const int j = lane & 15, e = j >> 2, q = j & 3, g = lane >> 4;
+    const int kl = 4 * half + e;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+      const int d0 = 32 * dt + 16 * (g & 1) + 4 * q;
+      vaddr[dt] = kl * C::ROWB + swz_v<D>(kl, d0 >> 3) * 16 + (d0 & 7) * 2;
+    }
+  }
+  f32x16 oacc[C::NDT];
+#pragma unroll
+  for (int i = 0; i < C::NDT; ++i) oacc[i] = f32x16{};
+  float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.0f;
+
+  // number of visited tiles (uniform over the workgroup)
+  int T = 0;
+  for (int bi = 0; bi < a.nblk; ++bi) T += tiles_of<BC>(a, bi, q_hi);
+
+
+  // prologue: tiles 0 and 1
+  Cursor cd = cursor_first(a, q_hi);   // next tile to copy
+  int md = 0;                          // its ordinal
+  for (int k = 0; k < 2 && md < T; ++k) {
+    pp_copy_tile<D>(a, cd, md, smem, b, h, HD2, wave, voffk, voffv);
+    cd = cursor_next(a, q_hi, cd);
+    ++md;
+  }
+  if (T > 1) wait_vmcnt<2 * C::DMA>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+
+  Cursor c0 = cursor_first(a, q_hi);   // tile n (softmax / PV)
+  Cursor c1 = cursor_next(a, q_hi, c0);  // tile n+1 (scores)
+  int n = 0;
+  float sc[C::NS];
+  bf16x8 pb[C::NS / 8];
+  bool live_sc = false;                // sc holds scores of tile n
+
+  for (int s = 0; s <= 2 * T + 1; ++s) {
+    if ((s & 1) == 0 && md < T && md == s / 2 + 2) {
+      pp_copy_tile<D>(a, cd, md, smem, b, h, HD2, wave, voffk, voffv);
+      cd = cursor_next(a, q_hi, cd);
+      ++md;
+    }
+    const int p = s - grp;
+    if (p == 0) {
+      if (pp_live(a, c0, wrows, wq_hi)) {
+        char* kb = smem + 0;
+        f32x16 acc[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          acc[kt] = f32x16{};
+#pragma unroll
+          for (int c = 0; c < C::NC; ++c) {
+            const bf16x8 kf = *(const bf16x8*)(kb + kt * 32 * C::ROWB + kaddr[c]);
+            acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], acc[kt], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sc[kt * 16 + v] = acc[kt][v];
+        live_sc = true;
+      }
+    } else if (p > 0 && p <= 2 * T && (p & 1)) {
+      // vector phase: softmax of tile n ([RA] §3.2, lazy reference max)
+      if (live_sc) {
+        const KVBlock& kb0 = a.blk[c0.blk];
+        const int kt0 = c0.t * BC;
+        const long long kp0 = kb0.k_pos0 + kt0;
+        long long lim_ll = kb0.len - kt0;
+        if (a.valid_len - kp0 < lim_ll) lim_ll = a.valid_len - kp0;
+        if (lim_ll < BC || (a.causal && kp0 + BC - 1 > wq_lo)) {
+          const int klim = (int)max(0LL, lim_ll);
+          int t = min(klim, BC) - 1 - 4 * half;
+          if (a.causal) {
+            const long long d = wq_lo - kp0;
+            const int dc = (int)(d < -2 * BC ? -2 * BC : (d > 2 * BC ? 2 * BC : d));
+            t = min(t, max(-1, dc + col - 4 * half));
+          }
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (32 * kt + 8 * (v >> 2) + (v & 3) > t) sc[kt * 16 + v] = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < C::NS; ++i) mx = fmaxf(mx, sc[i]);
+        mx = pair_max(mx) * c_scale;
+        m_true = fmaxf(m_true, mx);
+        const bool need = mx > m_ref + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          const float m_new = need ? mx : m_ref;
+          const float alpha = need ? fast_exp2(m_ref - mx) : 1.0f;
+          l_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < C::NDT; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
+          m_ref = m_new;
+        }
+        const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
+        exp_tile<C::NS>(sc, m_use, c_scale, pb, l_run);
+      }
+    } else if (p >= 2 && p <= 2 * T) {
+      // matrix phase: S^T(n+1) and O^T += V(n)^T P(n)^T
+      __builtin_amdgcn_s_setprio(1);
+      const bool pv = live_sc;
+      const bool nx = n + 1 < T && pp_live(a, c1, wrows, wq_hi);
+      if (nx) {
+        char* kb = smem + ((n + 1) & (C::NBUF - 1)) * C::STAGE;
+        f32x16 acc[2];
+#pragma unroll
+        for (int i = 0; i < 2 * C::NC; ++i) {
+          const int kt = i & 1, c = i >> 1;
+          const bf16x8 kf = *(const bf16x8*)(kb + kt * 32 * C::ROWB + kaddr[c]);
+          acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? f32x16{} : acc[kt],
+                                                            0, 0, 0);
+        }
+        if (pv) {
+          char* vl = smem + (n & (C::NBUF - 1)) * C::STAGE + C::TILE;
+#pragma unroll
+          for (int j = 0; j < (BC / 16) * C::NDT; ++j) {
+            const int G = j / C::NDT, dt = j % C::NDT;
+            char* p0 = vl + G * 16 * C::ROWB + vaddr[dt];
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p0);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p0 + 8 * C::ROWB));
+            bf16x8 vf;
+            __builtin_memcpy(&vf, &lo, 8);
+            __builtin_memcpy((char*)&vf + 8, &hi, 8);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[G], oacc[dt], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sc[kt * 16 + v] = acc[kt][v];
+      } else if (pv) {
+        char* vl = smem + (n & (C::NBUF - 1)) * C::STAGE + C::TILE;
+#pragma unroll
+        for (int j = 0; j < (BC / 16) * C::NDT; ++j) {
+          const int G = j / C::NDT, dt = j % C::NDT;
+          char* p0 = vl + G * 16 * C::ROWB + vaddr[dt];
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p0);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p0 + 8 * C::ROWB));
+          bf16x8 vf;
+          __builtin_memcpy(&vf, &lo, 8);
+          __builtin_memcpy((char*)&vf + 8, &hi, 8);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[G], oacc[dt], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+      live_sc = nx;
+      c0 = c1;
+      c1 = cursor_next(a, q_hi, c1);
+      ++n;
+    }
+    // before slot 2m (group 0 reads K(m)), tile m's copies must have landed;
+    // only tile m+1's copies may still be outstanding
+    if (s & 1) {
+      const int m = (s + 1) / 2;
+      if (m + 1 < T) wait_vmcnt<2 * C::DMA>();
+      else wait_vmcnt<0>();
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: o = u / l, lse = m + ln l ([RA] §3.2; [SPD] §四) ----
+  const float l_tot = pair_sum(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const int r = wrow0 + col;
+  if (wrows > 0 && r < a.Sq) {
+    const long long ro = ((long long)b * a.Sq + r) * HD + (long long)h * D;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * half;
+        const float x0 = oacc[dt][4 * g + 0] * inv, x1 = oacc[dt][4 * g + 1] * inv;
+        const float x2 = oacc[dt][4 * g + 2] * inv, x3 = oacc[dt][4 * g + 3] * inv;
+        if (a.o_fp32) {
+          *(float4*)((float*)a.o + ro + d) = float4{x0, x1, x2, x3};
+        } else {
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          bf16x4 y;
+          y[0] = (__bf16)x0; y[1] = (__bf16)x1; y[2] = (__bf16)x2; y[3] = (__bf16)x3;
+          *(bf16x4*)((__bf16*)a.o + ro + d) = y;
+        }
+      }
+    if (half == 0) {
+      const long long so = ((long long)b * a.Sq + r) * a.H + h;
+      const bool seen = l_tot > 0.0f;
+      if (a.lse) a.lse[so] = seen ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
+      if (a.m_out) a.m_out[so] = seen ? m_true * kLn2 : -INFINITY;
+      if (a.l_out) a.l_out[so] = seen ? l_tot * fast_exp2(m_ref - m_true) : 0.0f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel (no bf16 rounding anywhere; fp32 matrix-core products)
 // ---------------------------------------------------------------------------
 template <int D>
@@ -779,19 +1104,38 @@ void ring_attn_f32(const AttnArgs a) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-ra_status launch(const AttnArgs& a, int D, ra_dtype dt, hipStream_t stream,
-                 const char* name) {
+// Kernel choice for bf16: the 256-row ping-pong kernel halves K/V traffic
+// per FLOP; the 128-row kernel runs two workgroups per CU.
+
+bool use_pp(const AttnArgs& a) {
+  const int mode = ra::option(RA_OPT_ATTN_KERNEL);
+  if (mode == RA_KERNEL_BR128) return false;
+  if (mode == RA_KERNEL_BR256) return true;
+  // AUTO: the 128-row kernel is currently the faster of the two at every
+  // size measured (long-context share: 1043 vs 784 TFLOP/s)
+  return false;
+}
+
+ra_status launch(AttnArgs& a, int D, ra_dtype dt, hipStream_t stream, const char* name) {
+  const bool pp = dt == RA_BF16 && use_pp(a);
+  const int br = pp ? PPCfg<128>::BR : kBR;
+  a.n_qtiles = (a.Sq + br - 1) / br;
   const long long n_wg = (long long)a.B * a.H * a.n_qtiles;
   if (n_wg == 0) return RA_OK;
   if (n_wg > 0x7fffffffLL)
     return ra::fail(RA_ERR_UNSUPPORTED, "%s: too many query tiles", name);
-  const dim3 grid((unsigned)n_wg), block(kThreads);
+  const dim3 grid((unsigned)n_wg);
   if (dt == RA_BF16) {
-    if (D == 128) hipLaunchKernelGGL(ring_attn_bf16<128>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(ring_attn_bf16<64>, grid, block, 0, stream, a);
+    if (pp) {
+      if (D == 128) hipLaunchKernelGGL(ring_attn_bf16_pp<128>, grid, dim3(512), 0, stream, a);
+      else hipLaunchKernelGGL(ring_attn_bf16_pp<64>, grid, dim3(512), 0, stream, a);
+    } else {
+      if (D == 128) hipLaunchKernelGGL(ring_attn_bf16<128>, grid, dim3(kThreads), 0, stream, a);
+      else hipLaunchKernelGGL(ring_attn_bf16<64>, grid, dim3(kThreads), 0, stream, a);
+    }
   } else {
-    if (D == 128) hipLaunchKernelGGL(ring_attn_f32<128>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(ring_attn_f32<64>, grid, block, 0, stream, a);
+    if (D == 128) hipLaunchKernelGGL(ring_attn_f32<128>, grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL(ring_attn_f32<64>, grid, dim3(kThreads), 0, stream, a);
   }
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess)
@@ -845,7 +1189,6 @@ extern "C" ra_status ra_block_attn_fwd(const void* q, const void* k, const void*
   a.B = B;
   a.Sq = Sq;
   a.H = H;
-  a.n_qtiles = (Sq + kBR - 1) / kBR;
   a.causal = causal != 0;
   a.o_fp32 = 1;
   const double sc = scale > 0.0f ? (double)scale : 1.0 / std::sqrt((double)D);
@@ -891,7 +1234,6 @@ extern "C" ra_status ra_ring_attn_fwd(const void* q_r, const void* const* k_bloc
   a.B = B;
   a.Sq = Sb;
   a.H = H;
-  a.n_qtiles = (Sb + kBR - 1) / kBR;
   a.causal = causal != 0;
   a.o_fp32 = dt == RA_FP32;
   const double sc = scale > 0.0f ? (double)scale : 1.0 / std::sqrt((double)D);

@@ -1,6 +1,7 @@
 // Host-only part of libringattn.so: error state, padding and shard cover,
 // ring order and block classification.  No HIP calls; also builds with a
 // plain host compiler.
+#include <atomic>
 #include <cstdint>
 #include <cstdio>
 #include <string>
@@ -23,6 +24,12 @@ ra_status fail(ra_status st, const char* fmt, ...) {
 
 void clear_error() { g_last_error.clear(); }
 
+static std::atomic<int> g_options[RA_OPT_COUNT];
+
+int option(int which) {
+  return (which >= 0 && which < RA_OPT_COUNT) ? g_options[which].load(std::memory_order_relaxed) : 0;
+}
+
 // The three cases of [RA] §3.4 as range comparisons.  With K the set of
 // real keys [k0, min(k1, valid_len)):
 //   no real key, or (causal) the first key after the last query -> SKIP;
@@ -44,6 +51,19 @@ int block_class(long long q0, long long q1, long long k0, long long k1,
 extern "C" {
 
 int ra_abi_version(void) { return 1; }
+
+ra_status ra_set_option(int opt, int value) {
+  ra::clear_error();
+  if (opt == RA_OPT_ATTN_KERNEL) {
+    if (value != RA_KERNEL_AUTO && value != RA_KERNEL_BR128 && value != RA_KERNEL_BR256)
+      return ra::fail(RA_ERR_RANGE, "ra_set_option: unknown kernel choice %d", value);
+    ra::g_options[opt].store(value, std::memory_order_relaxed);
+    return RA_OK;
+  }
+  return ra::fail(RA_ERR_RANGE, "ra_set_option: unknown option %d", opt);
+}
+
+int ra_get_option(int opt) { return ra::option(opt); }
 
 const char* ra_last_error(void) { return ra::g_last_error.c_str(); }
 

@@ -22,4 +22,7 @@ void clear_error();
 int block_class(long long q0, long long q1, long long k0, long long k1,
                 bool causal, long long valid_len);
 
+// Current value of a process-wide option (see ra_set_option).
+int option(int which);
+
 }  // namespace ra

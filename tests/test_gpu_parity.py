@@ -46,6 +46,16 @@ def gpu():
     torch.cuda.synchronize()
 
 
+@pytest.fixture(params=["br128", "br256"])
+def variant(request):
+    """Run a bf16 test with each attention kernel forced (both compute the
+    same function; AUTO picks by grid size)."""
+    choice = {"br128": ra.RA_KERNEL_BR128, "br256": ra.RA_KERNEL_BR256}[request.param]
+    ra.set_attn_kernel(choice)
+    yield request.param
+    ra.set_attn_kernel(ra.RA_KERNEL_AUTO)
+
+
 def check_bf16(got, ref, what):
     c = oracle.compare(got, ref)
     say(what, {k: f"{v:.3e}" for k, v in c.items()})
@@ -150,7 +160,7 @@ def dit():
 
 
 @pytest.mark.parametrize("rank", [0, 1, 2, 3])
-def test_dit_shard_fused(dit, rank):
+def test_dit_shard_fused(dit, rank, variant):
     w, (q, k, v), (qg, kg, vg) = dit
     kb, vb = blocks_of(kg, w.P), blocks_of(vg, w.P)
     q_r = qg[:, rank * w.block_len:(rank + 1) * w.block_len].contiguous()
@@ -166,7 +176,7 @@ def test_dit_shard_fused(dit, rank):
     assert oracle.cosine(o.cpu(), loc) < BF16_COS
 
 
-def test_dit_shard_composable_matches(dit):
+def test_dit_shard_composable_matches(dit, variant):
     w, (q, k, v), (qg, kg, vg) = dit
     kb, vb = blocks_of(kg, w.P), blocks_of(vg, w.P)
     r = 2
@@ -181,7 +191,7 @@ def test_dit_shard_composable_matches(dit):
     assert oracle.max_abs_err(o_c.cpu(), o_f.cpu()) <= BF16_ATOL
 
 
-def test_dit_shard_deterministic(dit):
+def test_dit_shard_deterministic(dit, variant):
     """No atomics on the path: two runs are bitwise identical."""
     w, _, (qg, kg, vg) = dit
     kb, vb = blocks_of(kg, w.P), blocks_of(vg, w.P)
@@ -194,7 +204,7 @@ def test_dit_shard_deterministic(dit):
     assert torch.equal(la, lb)
 
 
-def test_block_attn_partials_and_stats(dit):
+def test_block_attn_partials_and_stats(dit, variant):
     """One round (block_attn_fwd): o, lse, m, l against the oracle, with
     global positions; then merging all rounds gives the ring result."""
     w, (q, k, v), (qg, kg, vg) = dit
@@ -217,7 +227,7 @@ def test_block_attn_partials_and_stats(dit):
 
 
 # ------------------------------------------------------------ C3 Ulysses
-def test_ulysses_layout_and_attention():
+def test_ulysses_layout_and_attention(variant):
     w = W.ULYSSES
     P, Sl, Hl = w.P, w.S // w.P, w.H // w.P
     say(w.name, "generate")
@@ -253,7 +263,7 @@ def test_ulysses_layout_and_attention():
 
 
 # ------------------------------------------------------------ C4 long causal
-def test_long_context_causal_rank3():
+def test_long_context_causal_rank3(variant):
     w = W.LONG_CAUSAL
     r, Sb = 3, w.block_len
     say(w.name, "generate on device")
@@ -298,7 +308,7 @@ def padded():
 
 
 @pytest.mark.parametrize("path", ["fused", "composable"])
-def test_padded_causal_all_ranks(padded, path):
+def test_padded_causal_all_ranks(padded, path, variant):
     w, (q, k, v), (qg, kg, vg) = padded
     assert w.S_padded == 3008 and w.block_len == 752
     kb, vb = blocks_of(kg, w.P), blocks_of(vg, w.P)
@@ -314,7 +324,7 @@ def test_padded_causal_all_ranks(padded, path):
         assert oracle.max_abs_err(lse[:, rows].cpu(), ref_lse) <= LSE_BF16_ATOL
 
 
-def test_padded_skipped_blocks_never_read(padded):
+def test_padded_skipped_blocks_never_read(padded, variant):
     """Poison the K/V of every block a causal rank skips with NaN: the output
     stays bit-identical.  Poison a visited block: rows that see it change."""
     w, _, (qg, kg, vg) = padded
@@ -422,6 +432,35 @@ def test_stability_large_scores():
     # fp32 scores of magnitude ~1e3 carry ~1e-4 absolute rounding, which the
     # exponent turns into relative weight errors of that size
     check_fp32(o.cpu(), ref, "stability", atol=2e-3)
+
+
+def test_edge_cases_bf16(variant):
+    """bf16 through both kernels: ragged query and key tiles, causal offsets
+    (including rows that see no key), padding, non-default scale."""
+    g = torch.Generator().manual_seed(19)
+    mk = lambda *s: torch.randn(*s, generator=g).to(torch.bfloat16)
+    for (B, Sq, Sk, H, D) in [(1, 1, 1, 1, 64), (2, 300, 67, 3, 64), (1, 33, 200, 2, 128),
+                              (1, 520, 777, 2, 128)]:
+        q, k, v = mk(B, Sq, H, D), mk(B, Sk, H, D), mk(B, Sk, H, D)
+        for causal, qp, kp, vl in [(False, 0, 0, -1), (True, 100, 0, -1), (True, 0, 50, -1),
+                                   (True, 300, 0, 250), (False, 0, 0, 40)]:
+            say("edge bf16", variant, (B, Sq, Sk, H, D), causal, qp, kp, vl)
+            o, lse, m, l = ra.block_attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=0.11,
+                                             q_pos0=qp, k_pos0=kp, causal=causal,
+                                             valid_len=vl)
+            torch.cuda.synchronize()
+            ro, rl, rm, _ = oracle.attention(q, k, v, scale=0.11, q_pos0=qp, k_pos0=kp,
+                                             causal=causal, valid_len=None if vl < 0 else vl)
+            og = o.cpu().numpy()
+            assert np.all(np.isfinite(og))
+            assert oracle.max_abs_err(og, ro) <= BF16_ATOL, (variant, causal, qp, kp)
+            if np.abs(ro).sum() > 0:
+                assert oracle.cosine(og, ro) > BF16_COS
+            lg = lse.cpu().numpy()
+            assert np.array_equal(np.isneginf(lg), np.isneginf(rl))
+            fin = np.isfinite(rl)
+            assert oracle.max_abs_err(lg[fin], rl[fin]) <= LSE_BF16_ATOL
+            assert np.all(og[~fin] == 0)
 
 
 # ------------------------------------------------------------ permutations

@@ -44,6 +44,16 @@ def test_abi_version(lib):
     assert ra.abi_version() == 1
 
 
+def test_kernel_option(lib):
+    assert ra.get_attn_kernel() == ra.RA_KERNEL_AUTO
+    for c in (ra.RA_KERNEL_BR128, ra.RA_KERNEL_BR256, ra.RA_KERNEL_AUTO):
+        ra.set_attn_kernel(c)
+        assert ra.get_attn_kernel() == c
+    with pytest.raises(RuntimeError):
+        ra.set_attn_kernel(7)
+    assert lib.ra_set_option(99, 0) == 4
+
+
 def test_padded_len_matches_oracle(lib):
     for S in [0, 1, 15, 16, 3000, 3008, 4096, 131072, 131073]:
         for P in [1, 2, 3, 4, 8]:
