@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the side measurements (Ulysses layout, DiT shard)")
+    ap.add_argument("--attn-kernel", choices=["auto", "br128", "br256"], default="auto",
+                    help="force the bf16 attention kernel (both compute the same result)")
     return ap.parse_args()
 
 
@@ -101,6 +103,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     ra.lib()
+    ra.set_attn_kernel({"auto": ra.RA_KERNEL_AUTO, "br128": ra.RA_KERNEL_BR128,
+                        "br256": ra.RA_KERNEL_BR256}[args.attn_kernel])
     w = W.LONG_CAUSAL
     rank, Sb, H, D, P = 3, w.block_len, w.H, w.D, w.P
     q, k, v = W.make_qkv(w, device="cuda")
@@ -171,6 +175,7 @@ def main():
                         "blocks 3,2,1,0; 7..4 skipped), B=1",
             "global_batch": 1, "seq_len": w.S, "heads": H, "head_dim": D, "ring_degree": P,
             "rank": rank, "causal": True, "parallelism": "one rank's share on 1 GPU",
+            "attn_kernel": args.attn_kernel,
             "algorithmic_flops_per_step": flops,
         },
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

@@ -167,23 +167,25 @@ __device__ __forceinline__ float online_update(float (&s)[NS], RowState& st, flo
 // V[key_e][d0 + 4q .. d0 + 4q + 3], so lane j gets V[key_0..3][d0 + j].
 //
 // Software pipeline (per wave, iteration n over the visited tiles):
-//   LDS holds K(n+1) and V(n) (copied during iteration n-1);
-//   copy K(n+2) and V(n+1) into the buffers freed by iteration n-1;
+//   LDS holds K(n+1), V(n) and V(n+1) (copied during iterations n-2, n-1);
+//   copy K(n+2) and V(n+2) into the buffers freed by iteration n-1;
 //   mask / row max / rescale of tile n's scores (already in registers);
 //   S^T(n+1) = K(n+1) Q^T on the matrix cores, interleaved instruction by
 //   instruction with the exponentials of tile n on the vector ALUs;
 //   O^T += V(n)^T P(n)^T;
-//   wait for this wave's copies, barrier.
-// K therefore runs one tile ahead of V, and the two buffers of each stay
-// enough.  The loop is unrolled by two so buffer parities are constants.
+//   wait for this wave's K copy (the V copy may stay in flight), barrier.
+// Two K buffers and three V buffers (80 KiB at D = 128, so two workgroups
+// still share a CU).  Operand reads run four matrix ops ahead of their use.
+// The loop is unrolled by two so the K parity and the score registers are
+// constants; the V buffer index cycles mod 3 at run time.
 template <int D>
 struct Bf16Cfg {
   static constexpr int BC = 64;                   // keys per tile
   static constexpr int ROWB = D * 2;              // bytes per key row in LDS
   static constexpr int TILE = BC * ROWB;          // one K or V tile
-  static constexpr int KB = 0;                    // K buffers at KB + p*TILE
-  static constexpr int VB = 2 * TILE;             // V buffers at VB + p*TILE
-  static constexpr int LDS = 4 * TILE;
+  static constexpr int KB = 0;                    // 2 K buffers at KB + p*TILE
+  static constexpr int VB = 2 * TILE;             // 3 V buffers at VB + p*TILE
+  static constexpr int LDS = 5 * TILE;
   static constexpr int CHUNKS = D / 8;            // 16-byte chunks per row
   static constexpr int DMA = TILE / 1024 / kWaves;  // 1 KiB copies per wave per tile
   static constexpr int NC = D / 16;               // k-steps of S^T = K Q^T
@@ -208,6 +210,15 @@ __device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access
 constexpr float kRescaleSlack = 8.0f;   // lazy rescale threshold (base-2 units)
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maxima so they are not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 // Position in the visited-tile sequence: tile t (of n) of visited block blk.
 struct Cursor {
@@ -280,18 +291,19 @@ __device__ __forceinline__ void scores_tile(char* smem, int kb, const WaveState<
 
 // Exponentials of one tile against the reference max, their bf16 copy P^T
 // and the denominator over the same rounded weights ([RA] §3.2).
-template <int NS>
-__device__ __forceinline__ void exp_tile(float (&s)[NS], float m_use, float c_scale,
-                                         bf16x8 (&pb)[NS / 8], float& l_run) {
+__device__ __forceinline__ void exp_tile(f32x16 (&s)[2], float m_use, float c_scale,
+                                         bf16x8 (&pb)[4], float& l_run) {
 #pragma unroll
-  for (int i = 0; i < NS; ++i) s[i] = fast_exp2(fmaf(s[i], c_scale, -m_use));
+  for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-  for (int G = 0; G < NS / 8; ++G)
+    for (int v = 0; v < 16; ++v) s[kt][v] = fast_exp2(fmaf(s[kt][v], c_scale, -m_use));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pb[G][e] = (__bf16)s[(G >> 1) * 16 + (G & 1) * 8 + e];
+  for (int G = 0; G < 4; ++G)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[G][e] = (__bf16)s[G >> 1][(G & 1) * 8 + e];
   float l0 = 0.0f, l1 = 0.0f;
 #pragma unroll
-  for (int G = 0; G < NS / 8; ++G)
+  for (int G = 0; G < 4; ++G)
 #pragma unroll
     for (int e = 0; e < 8; e += 4) {
       const bf16x2 p0 = {pb[G][e], pb[G][e + 1]}, p1 = {pb[G][e + 2], pb[G][e + 3]};
@@ -305,23 +317,22 @@ __device__ __forceinline__ void exp_tile(float (&s)[NS], float m_use, float c_sc
 // V buffer PAR; the copies go to K buffer PAR and V buffer PAR^1.
 template <int D, int PAR>
 __device__ __forceinline__ void pipeline_step(
-    const AttnArgs& a, char* smem, WaveState<D>& w, float (&s_cur)[Bf16Cfg<D>::NS],
-    float (&s_nxt)[Bf16Cfg<D>::NS], Cursor& t0, Cursor& t1, Cursor& t2, long long q_hi,
-    long long wq_lo, long long wq_hi, int wrows, int col, int half, int b, int h,
-    int HD2, int wave) {
+    const AttnArgs& a, char* smem, WaveState<D>& w, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+    Cursor& t0, Cursor& t1, Cursor& t2, int& vb,
+    long long q_hi, long long wq_lo, long long wq_hi, int wrows, int col, int half, int b,
+    int h, int HD2, int wave) {
   using C = Bf16Cfg<D>;
   constexpr int BC = C::BC;
   const float c_scale = a.scale_log2;
-  // copies for the tiles two (K) and one (V) ahead
-  if (t1.blk < a.nblk) {
-    const KVBlock& kb1 = a.blk[t1.blk];
-    copy_tile<D>(kb1.v, kb1.len, t1.t, b, h, a.H, HD2, wave, w.voffv,
-                 smem + C::VB + (PAR ^ 1) * C::TILE);
-  }
-  if (t2.blk < a.nblk) {
+  // copies of tile n+2: K first, so that waiting for it leaves V in flight
+  const int vb2 = vb == 0 ? 2 : vb - 1;  // (vb + 2) % 3
+  const bool copy2 = t2.blk < a.nblk;
+  if (copy2) {
     const KVBlock& kb2 = a.blk[t2.blk];
     copy_tile<D>(kb2.k, kb2.len, t2.t, b, h, a.H, HD2, wave, w.voffk,
                  smem + C::KB + PAR * C::TILE);
+    copy_tile<D>(kb2.v, kb2.len, t2.t, b, h, a.H, HD2, wave, w.voffv,
+                 smem + C::VB + vb2 * C::TILE);
   }
   // tile n: classification, mask, row max, lazy rescale
   const KVBlock& kb0 = a.blk[t0.blk];
@@ -354,11 +365,11 @@ __device__ __forceinline__ void pipeline_step(
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          if (32 * kt + 8 * (v >> 2) + (v & 3) > t) s_cur[kt * 16 + v] = -INFINITY;
+          if (32 * kt + 8 * (v >> 2) + (v & 3) > t) s_cur[kt][v] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < C::NS; ++i) mx = fmaxf(mx, s_cur[i]);
+    for (int i = 0; i < C::NS; ++i) mx = fmaxf(mx, s_cur[i >> 4][i & 15]);
     mx = pair_max(mx) * c_scale;
     w.m_true = fmaxf(w.m_true, mx);
     const bool need = mx > w.m_ref + kRescaleSlack;
@@ -380,7 +391,6 @@ __device__ __forceinline__ void pipeline_step(
   }
   // S^T(n+1) on the matrix cores alongside the exponentials of tile n
   constexpr int kbuf_next = C::KB + (PAR ^ 1) * C::TILE;
-  f32x16 acc[2];
   bf16x8 pb[C::NS / 8];
   if (live0 && live1) {
     // Explicit interleave: step i issues the K read of step i+2, the
@@ -390,26 +400,27 @@ __device__ __forceinline__ void pipeline_step(
     // latency of tile n+1.
     constexpr int NSTEP = 2 * C::NC;
     constexpr int PER = C::NS / NSTEP;  // scores per step (2 for D=128)
-    bf16x8 kf[3];
+    constexpr int PF = NSTEP >= 8 ? 4 : 2;  // operand read lead (matrix ops)
+    bf16x8 kf[PF + 1];
     // step i works on score tile kt = i % 2 with k-step c = i / 2, so
     // consecutive matrix-core ops never depend on each other
     auto kread = [&](int i) -> bf16x8 {
       return *(const bf16x8*)(smem + kbuf_next + (i % 2) * 32 * C::ROWB + w.kaddr[i / 2]);
     };
-    kf[0] = kread(0);
-    kf[1] = kread(1);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) kf[i] = kread(i);
     float lp[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) {
-      if (i + 2 < NSTEP) kf[(i + 2) % 3] = kread(i + 2);
+      if (i + PF < NSTEP) kf[(i + PF) % (PF + 1)] = kread(i + PF);
       const int kt = i % 2, c = i / 2;
-      acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], w.qf[c],
-                                                        c == 0 ? f32x16{} : acc[kt], 0, 0, 0);
+      s_nxt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % (PF + 1)], w.qf[c],
+                                                          c == 0 ? f32x16{} : s_nxt[kt], 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < PER; j += 2) {
         const int v = i * PER + j;  // score index, even
-        const float e0 = fast_exp2(fmaf(s_cur[v], c_scale, -m_use));
-        const float e1 = fast_exp2(fmaf(s_cur[v + 1], c_scale, -m_use));
+        const float e0 = fast_exp2(fmaf(s_cur[v >> 4][v & 15], c_scale, -m_use));
+        const float e1 = fast_exp2(fmaf(s_cur[v >> 4][(v & 15) + 1], c_scale, -m_use));
         const int G = 2 * (v >> 4) + ((v & 15) >> 3), e = v & 7;
         pb[G][e] = (__bf16)e0;
         pb[G][e + 1] = (__bf16)e1;
@@ -420,20 +431,15 @@ __device__ __forceinline__ void pipeline_step(
     }
     w.l_run += lp[0] + lp[1];
   } else {
-    if (live1) scores_tile<D>(smem, kbuf_next, w, acc);
-    if (live0) exp_tile<C::NS>(s_cur, m_use, c_scale, pb, w.l_run);
-  }
-  if (live1) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s_nxt[kt * 16 + v] = acc[kt][v];
+    if (live1) scores_tile<D>(smem, kbuf_next, w, s_nxt);
+    if (live0) exp_tile(s_cur, m_use, c_scale, pb, w.l_run);
   }
   // O^T += V(n)^T P(n)^T: fragment j = (G = j / NDT, dt = j % NDT) is read
   // two ops ahead, and consecutive ops accumulate into different d tiles
   if (live0) {
-    char* vl = smem + C::VB + PAR * C::TILE;
+    char* vl = smem + C::VB + vb * C::TILE;
     constexpr int NJ = (BC / 16) * C::NDT;
+    constexpr int PF = NJ >= 8 ? 4 : 2;
     auto vread = [&](int j) -> bf16x8 {
       char* p0 = vl + (j / C::NDT) * 16 * C::ROWB + w.vaddr[j % C::NDT];
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p0);
@@ -443,26 +449,30 @@ __device__ __forceinline__ void pipeline_step(
       __builtin_memcpy((char*)&vf + 8, &hi, 8);
       return vf;
     };
-    bf16x8 vf[3];
-    vf[0] = vread(0);
-    vf[1] = vread(1);
+    bf16x8 vf[PF + 1];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) vf[j] = vread(j);
     // this phase is matrix-core bound: give it issue priority over the
     // other wave on the SIMD, whose exponentials fill the gaps
     __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      if (j + 2 < NJ) vf[(j + 2) % 3] = vread(j + 2);
+      if (j + PF < NJ) vf[(j + PF) % (PF + 1)] = vread(j + PF);
       const int G = j / C::NDT, dt = j % C::NDT;
-      w.oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j % 3], pb[G], w.oacc[dt], 0, 0, 0);
+      w.oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j % (PF + 1)], pb[G], w.oacc[dt],
+                                                           0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's copies landed
-  __syncthreads();                // everyone's copies landed, everyone done reading
+  // this wave's K(n+2) copy (and everything older) landed; V(n+2) may fly
+  if (copy2) wait_vmcnt<C::DMA>();
+  else wait_vmcnt<0>();
+  __syncthreads();  // everyone's copies landed, everyone done reading
   t0 = t1;
   t1 = t2;
   t2 = cursor_next(a, q_hi, t2);
+  vb = vb == 2 ? 0 : vb + 1;
 }
 
 template <int D>
@@ -526,7 +536,7 @@ void ring_attn_bf16(const AttnArgs a) {
   Cursor t0 = cursor_first(a, q_hi);
   Cursor t1 = cursor_next(a, q_hi, t0);
   Cursor t2 = cursor_next(a, q_hi, t1);
-  float sA[C::NS], sB[C::NS];
+  f32x16 sA[2], sB[2];
   if (t0.blk < a.nblk) {
     const KVBlock& kb = a.blk[t0.blk];
     copy_tile<D>(kb.k, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffk, smem + C::KB);
@@ -535,28 +545,23 @@ void ring_attn_bf16(const AttnArgs a) {
   if (t1.blk < a.nblk) {
     const KVBlock& kb = a.blk[t1.blk];
     copy_tile<D>(kb.k, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffk, smem + C::KB + C::TILE);
+    copy_tile<D>(kb.v, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffv, smem + C::VB + C::TILE);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (t0.blk < a.nblk) {
     const long long kp0 = a.blk[t0.blk].k_pos0 + (long long)t0.t * C::BC;
-    if (wrows > 0 && !(a.causal && kp0 > wq_hi)) {
-      f32x16 acc[2];
-      scores_tile<D>(smem, C::KB, w, acc);
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sA[kt * 16 + v] = acc[kt][v];
-    }
+    if (wrows > 0 && !(a.causal && kp0 > wq_hi)) scores_tile<D>(smem, C::KB, w, sA);
   }
   __syncthreads();  // K buffer 0 is free for K(2)
 
+  int vb = 0;  // V buffer of tile n
   while (t0.blk < a.nblk) {
-    pipeline_step<D, 0>(a, smem, w, sA, sB, t0, t1, t2, q_hi, wq_lo, wq_hi, wrows, col, half,
-                        b, h, HD2, wave);
+    pipeline_step<D, 0>(a, smem, w, sA, sB, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows, col,
+                        half, b, h, HD2, wave);
     if (t0.blk >= a.nblk) break;
-    pipeline_step<D, 1>(a, smem, w, sB, sA, t0, t1, t2, q_hi, wq_lo, wq_hi, wrows, col, half,
-                        b, h, HD2, wave);
+    pipeline_step<D, 1>(a, smem, w, sB, sA, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows, col,
+                        half, b, h, HD2, wave);
   }
 
   // ---- epilogue: o = u / l, lse = m + ln l ([RA] §3.2; [SPD] §四) ----
@@ -620,15 +625,6 @@ struct PPCfg {
   static constexpr int NDT = D / 32;
   static constexpr int NS = BC / 2;
 };
-
-// Wait until at most N vector-memory operations of this wave are in flight
-// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
-// left at their maxima so they are not waited on).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 // Does tile c hold any key this wave's queries may see?
 __device__ __forceinline__ bool pp_live(const AttnArgs& a, const Cursor& c, int wrows,
@@ -748,7 +744,7 @@ void ring_attn_bf16_pp(const AttnArgs a) {
   Cursor c0 = cursor_first(a, q_hi);   // tile n (softmax / PV)
   Cursor c1 = cursor_next(a, q_hi, c0);  // tile n+1 (scores)
   int n = 0;
-  float sc[C::NS];
+  f32x16 sc[2];
   bf16x8 pb[C::NS / 8];
   bool live_sc = false;                // sc holds scores of tile n
 
@@ -772,10 +768,8 @@ void ring_attn_bf16_pp(const AttnArgs a) {
             acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], acc[kt], 0, 0, 0);
           }
         }
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) sc[kt * 16 + v] = acc[kt][v];
+        sc[0] = acc[0];
+        sc[1] = acc[1];
         live_sc = true;
       }
     } else if (p > 0 && p <= 2 * T && (p & 1)) {
@@ -798,11 +792,11 @@ void ring_attn_bf16_pp(const AttnArgs a) {
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-              if (32 * kt + 8 * (v >> 2) + (v & 3) > t) sc[kt * 16 + v] = -INFINITY;
+              if (32 * kt + 8 * (v >> 2) + (v & 3) > t) sc[kt][v] = -INFINITY;
         }
         float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < C::NS; ++i) mx = fmaxf(mx, sc[i]);
+        for (int i = 0; i < C::NS; ++i) mx = fmaxf(mx, sc[i >> 4][i & 15]);
         mx = pair_max(mx) * c_scale;
         m_true = fmaxf(m_true, mx);
         const bool need = mx > m_ref + kRescaleSlack;
@@ -817,15 +811,56 @@ void ring_attn_bf16_pp(const AttnArgs a) {
           m_ref = m_new;
         }
         const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
-        exp_tile<C::NS>(sc, m_use, c_scale, pb, l_run);
+        exp_tile(sc, m_use, c_scale, pb, l_run);
       }
     } else if (p >= 2 && p <= 2 * T) {
       // matrix phase: S^T(n+1) and O^T += V(n)^T P(n)^T
       __builtin_amdgcn_s_setprio(1);
       const bool pv = live_sc;
       const bool nx = n + 1 < T && pp_live(a, c1, wrows, wq_hi);
-      if (nx) {
-        char* kb = smem + ((n + 1) & (C::NBUF - 1)) * C::STAGE;
+      char* kb = smem + ((n + 1) & (C::NBUF - 1)) * C::STAGE;
+      char* vl = smem + (n & (C::NBUF - 1)) * C::STAGE + C::TILE;
+      if (nx && pv) {
+        // one sequence of matrix-core ops: steps 0..2NC-1 build S^T(n+1)
+        // (alternating score tiles), the rest accumulate O^T (alternating
+        // d tiles); operands are read from LDS PF steps ahead
+        constexpr int NK = 2 * C::NC, NSTEP = NK + (BC / 16) * C::NDT, PF = 4;
+        f32x16 acc[2];
+        bf16x8 fr[PF + 1];
+#pragma unroll
+        for (int i = 0; i < NSTEP + PF; ++i) {
+          if (i < NSTEP) {
+            const int f = i;
+            if (f < NK) {
+              fr[f % (PF + 1)] =
+                  *(const bf16x8*)(kb + (f & 1) * 32 * C::ROWB + kaddr[f >> 1]);
+            } else {
+              const int j = f - NK;
+              char* p0 = vl + (j / C::NDT) * 16 * C::ROWB + vaddr[j % C::NDT];
+              const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p0);
+              const s16x4 hi =
+                  __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p0 + 8 * C::ROWB));
+              __builtin_memcpy(&fr[f % (PF + 1)], &lo, 8);
+              __builtin_memcpy((char*)&fr[f % (PF + 1)] + 8, &hi, 8);
+            }
+          }
+          const int st = i - PF;  // matrix step issued in this iteration
+          if (st >= 0) {
+            if (st < NK) {
+              const int kt = st & 1, c = st >> 1;
+              acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  fr[st % (PF + 1)], qf[c], c == 0 ? f32x16{} : acc[kt], 0, 0, 0);
+            } else {
+              const int j = st - NK, G = j / C::NDT, dt = j % C::NDT;
+              oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[st % (PF + 1)], pb[G],
+                                                                 oacc[dt], 0, 0, 0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        sc[0] = acc[0];
+        sc[1] = acc[1];
+      } else if (nx) {
         f32x16 acc[2];
 #pragma unroll
         for (int i = 0; i < 2 * C::NC; ++i) {
@@ -834,26 +869,9 @@ void ring_attn_bf16_pp(const AttnArgs a) {
           acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? f32x16{} : acc[kt],
                                                             0, 0, 0);
         }
-        if (pv) {
-          char* vl = smem + (n & (C::NBUF - 1)) * C::STAGE + C::TILE;
-#pragma unroll
-          for (int j = 0; j < (BC / 16) * C::NDT; ++j) {
-            const int G = j / C::NDT, dt = j % C::NDT;
-            char* p0 = vl + G * 16 * C::ROWB + vaddr[dt];
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p0);
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p0 + 8 * C::ROWB));
-            bf16x8 vf;
-            __builtin_memcpy(&vf, &lo, 8);
-            __builtin_memcpy((char*)&vf + 8, &hi, 8);
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[G], oacc[dt], 0, 0, 0);
-          }
-        }
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) sc[kt * 16 + v] = acc[kt][v];
+        sc[0] = acc[0];
+        sc[1] = acc[1];
       } else if (pv) {
-        char* vl = smem + (n & (C::NBUF - 1)) * C::STAGE + C::TILE;
 #pragma unroll
         for (int j = 0; j < (BC / 16) * C::NDT; ++j) {
           const int G = j / C::NDT, dt = j % C::NDT;
