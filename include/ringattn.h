@@ -71,10 +71,11 @@ typedef enum { RA_OPT_ATTN_KERNEL = 0, RA_OPT_COUNT = 1 } ra_option;
 /* Values of RA_OPT_ATTN_KERNEL: which bf16 attention kernel the device
  * entry points launch.  AUTO picks the faster one measured for the shape
  * (currently the 128-row kernel everywhere).  Both compute the same
- * function; the choice only changes tiling and scheduling. */
+ * function with the same per-wave pipeline; the choice only changes how
+ * many query rows share one workgroup's K/V tiles. */
 #define RA_KERNEL_AUTO 0
-#define RA_KERNEL_BR128 1  /* 4 waves x 32 query rows, software-pipelined */
-#define RA_KERNEL_BR256 2  /* 8 waves x 32 query rows, two groups in ping-pong */
+#define RA_KERNEL_BR128 1  /* 4 waves x 32 query rows per workgroup */
+#define RA_KERNEL_BR256 2  /* 8 waves x 32 query rows per workgroup */
 
 /* ---------------------------------------------------------------------
  * Host-only helpers (no GPU needed; exported for tests and schedule dumps)

@@ -178,8 +178,10 @@ __device__ __forceinline__ float online_update(float (&s)[NS], RowState& st, flo
 // still share a CU).  Operand reads run four matrix ops ahead of their use.
 // The loop is unrolled by two so the K parity and the score registers are
 // constants; the V buffer index cycles mod 3 at run time.
-template <int D>
+template <int D, int NW>
 struct Bf16Cfg {
+  static constexpr int THREADS = 64 * NW;         // NW waves per workgroup
+  static constexpr int BR = 32 * NW;              // query rows per workgroup
   static constexpr int BC = 64;                   // keys per tile
   static constexpr int ROWB = D * 2;              // bytes per key row in LDS
   static constexpr int TILE = BC * ROWB;          // one K or V tile
@@ -187,7 +189,7 @@ struct Bf16Cfg {
   static constexpr int VB = 2 * TILE;             // 3 V buffers at VB + p*TILE
   static constexpr int LDS = 5 * TILE;
   static constexpr int CHUNKS = D / 8;            // 16-byte chunks per row
-  static constexpr int DMA = TILE / 1024 / kWaves;  // 1 KiB copies per wave per tile
+  static constexpr int DMA = TILE / 1024 / NW;     // 1 KiB copies per wave per tile
   static constexpr int NC = D / 16;               // k-steps of S^T = K Q^T
   static constexpr int NDT = D / 32;              // 32-row d tiles of O^T
   static constexpr int NS = BC / 2;               // scores per lane per tile
@@ -240,9 +242,9 @@ __device__ __forceinline__ Cursor cursor_next(const AttnArgs& a, long long q_hi,
 }
 
 // Everything a wave keeps in registers across tiles.
-template <int D>
+template <int D, int NW>
 struct WaveState {
-  using C = Bf16Cfg<D>;
+  using C = Bf16Cfg<D, NW>;
   bf16x8 qf[C::NC];        // Q fragment (B operand of S^T)
   f32x16 oacc[C::NDT];     // O^T accumulators (unnormalised u)
   float m_ref;             // reference max (base 2), -inf before any key
@@ -256,11 +258,11 @@ struct WaveState {
 
 // Copy one K or V tile (rows kt0 .. kt0+63 of batch b, head h of `src`, a
 // visited block of `len` rows) into LDS at `dst`; each wave copies C::DMA KiB.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void copy_tile(const void* src, int len, int ti, int b, int h,
                                           int H, int HD2, int wave, const int* voff,
                                           char* dst) {
-  using C = Bf16Cfg<D>;
+  using C = Bf16Cfg<D, NW>;
   const int kt0 = ti * C::BC;
   const int rows = min(C::BC, len - kt0);
   const long long off = (((long long)b * len + kt0) * H + h) * (D * 2);
@@ -274,10 +276,10 @@ __device__ __forceinline__ void copy_tile(const void* src, int len, int ti, int 
 }
 
 // S^T of one 64-key tile: the K tile at LDS byte offset kb times Q^T.
-template <int D>
-__device__ __forceinline__ void scores_tile(char* smem, int kb, const WaveState<D>& w,
+template <int D, int NW>
+__device__ __forceinline__ void scores_tile(char* smem, int kb, const WaveState<D, NW>& w,
                                             f32x16 (&acc)[2]) {
-  using C = Bf16Cfg<D>;
+  using C = Bf16Cfg<D, NW>;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     acc[kt] = f32x16{};
@@ -315,13 +317,13 @@ __device__ __forceinline__ void exp_tile(f32x16 (&s)[2], float m_use, float c_sc
 
 // One pipeline step.  PAR = n & 1: K(n+1) sits in K buffer PAR^1, V(n) in
 // V buffer PAR; the copies go to K buffer PAR and V buffer PAR^1.
-template <int D, int PAR>
+template <int D, int NW, int PAR>
 __device__ __forceinline__ void pipeline_step(
-    const AttnArgs& a, char* smem, WaveState<D>& w, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+    const AttnArgs& a, char* smem, WaveState<D, NW>& w, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
     Cursor& t0, Cursor& t1, Cursor& t2, int& vb,
     long long q_hi, long long wq_lo, long long wq_hi, int wrows, int col, int half, int b,
     int h, int HD2, int wave) {
-  using C = Bf16Cfg<D>;
+  using C = Bf16Cfg<D, NW>;
   constexpr int BC = C::BC;
   const float c_scale = a.scale_log2;
   // copies of tile n+2: K first, so that waiting for it leaves V in flight
@@ -329,9 +331,9 @@ __device__ __forceinline__ void pipeline_step(
   const bool copy2 = t2.blk < a.nblk;
   if (copy2) {
     const KVBlock& kb2 = a.blk[t2.blk];
-    copy_tile<D>(kb2.k, kb2.len, t2.t, b, h, a.H, HD2, wave, w.voffk,
+    copy_tile<D, NW>(kb2.k, kb2.len, t2.t, b, h, a.H, HD2, wave, w.voffk,
                  smem + C::KB + PAR * C::TILE);
-    copy_tile<D>(kb2.v, kb2.len, t2.t, b, h, a.H, HD2, wave, w.voffv,
+    copy_tile<D, NW>(kb2.v, kb2.len, t2.t, b, h, a.H, HD2, wave, w.voffv,
                  smem + C::VB + vb2 * C::TILE);
   }
   // tile n: classification, mask, row max, lazy rescale
@@ -431,7 +433,7 @@ __device__ __forceinline__ void pipeline_step(
     }
     w.l_run += lp[0] + lp[1];
   } else {
-    if (live1) scores_tile<D>(smem, kbuf_next, w, s_nxt);
+    if (live1) scores_tile<D, NW>(smem, kbuf_next, w, s_nxt);
     if (live0) exp_tile(s_cur, m_use, c_scale, pb, w.l_run);
   }
   // O^T += V(n)^T P(n)^T: fragment j = (G = j / NDT, dt = j % NDT) is read
@@ -475,10 +477,10 @@ __device__ __forceinline__ void pipeline_step(
   vb = vb == 2 ? 0 : vb + 1;
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ring_attn_bf16(const AttnArgs a) {
-  using C = Bf16Cfg<D>;
+  using C = Bf16Cfg<D, NW>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
   const int tid = threadIdx.x;
@@ -489,8 +491,8 @@ void ring_attn_bf16(const AttnArgs a) {
 
   int b, h, qt;
   tile_coords(a, b, h, qt);
-  const int row0 = qt * kBR;
-  const int rows_here = min(kBR, a.Sq - row0);
+  const int row0 = qt * C::BR;
+  const int rows_here = min(C::BR, a.Sq - row0);
   const long long q_lo = a.q_pos0 + row0;
   const long long q_hi = q_lo + rows_here - 1;
   const int wrow0 = row0 + wave * 32;
@@ -500,7 +502,7 @@ void ring_attn_bf16(const AttnArgs a) {
   const long long HD = (long long)a.H * D;
   const int HD2 = a.H * D * 2;  // bytes between consecutive key rows
 
-  WaveState<D> w;
+  WaveState<D, NW> w;
   {
     const int r = wrow0 + col;
     const __bf16* qp = (const __bf16*)a.q + ((long long)b * a.Sq + r) * HD + (long long)h * D;
@@ -539,28 +541,28 @@ void ring_attn_bf16(const AttnArgs a) {
   f32x16 sA[2], sB[2];
   if (t0.blk < a.nblk) {
     const KVBlock& kb = a.blk[t0.blk];
-    copy_tile<D>(kb.k, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffk, smem + C::KB);
-    copy_tile<D>(kb.v, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffv, smem + C::VB);
+    copy_tile<D, NW>(kb.k, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffk, smem + C::KB);
+    copy_tile<D, NW>(kb.v, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffv, smem + C::VB);
   }
   if (t1.blk < a.nblk) {
     const KVBlock& kb = a.blk[t1.blk];
-    copy_tile<D>(kb.k, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffk, smem + C::KB + C::TILE);
-    copy_tile<D>(kb.v, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffv, smem + C::VB + C::TILE);
+    copy_tile<D, NW>(kb.k, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffk, smem + C::KB + C::TILE);
+    copy_tile<D, NW>(kb.v, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffv, smem + C::VB + C::TILE);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (t0.blk < a.nblk) {
     const long long kp0 = a.blk[t0.blk].k_pos0 + (long long)t0.t * C::BC;
-    if (wrows > 0 && !(a.causal && kp0 > wq_hi)) scores_tile<D>(smem, C::KB, w, sA);
+    if (wrows > 0 && !(a.causal && kp0 > wq_hi)) scores_tile<D, NW>(smem, C::KB, w, sA);
   }
   __syncthreads();  // K buffer 0 is free for K(2)
 
   int vb = 0;  // V buffer of tile n
   while (t0.blk < a.nblk) {
-    pipeline_step<D, 0>(a, smem, w, sA, sB, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows, col,
+    pipeline_step<D, NW, 0>(a, smem, w, sA, sB, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows, col,
                         half, b, h, HD2, wave);
     if (t0.blk >= a.nblk) break;
-    pipeline_step<D, 1>(a, smem, w, sB, sA, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows, col,
+    pipeline_step<D, NW, 1>(a, smem, w, sB, sA, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows, col,
                         half, b, h, HD2, wave);
   }
 
@@ -592,342 +594,6 @@ void ring_attn_bf16(const AttnArgs a) {
       if (a.lse) a.lse[so] = seen ? (w.m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
       if (a.m_out) a.m_out[so] = seen ? w.m_true * kLn2 : -INFINITY;
       if (a.l_out) a.l_out[so] = seen ? l_tot * fast_exp2(w.m_ref - w.m_true) : 0.0f;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// bf16 kernel, 8-wave ping-pong variant (256 query rows per workgroup)
-// ---------------------------------------------------------------------------
-// Waves 0-3 (group 0) and 4-7 (group 1) each hold one wave per SIMD.  Time
-// is cut into slots separated by workgroup barriers; group 1 runs one slot
-// behind group 0, and every wave alternates
-//   matrix phase:  S^T(n+1) = K(n+1) Q^T and O^T += V(n)^T P(n)^T  (32 ops)
-//   vector phase:  mask, row max, lazy rescale, exponentials of tile n+1
-// so in every slot one wave of each SIMD keeps the matrix core busy while
-// the other does the softmax.  K/V tiles live in a ring of four LDS stages;
-// tile m is copied (buffer_load ... lds) in slot 2m-4, read by group 0 in
-// slots 2m (K) and 2m+2 (V), by group 1 one slot later, and its stage is
-// reused by tile m+4 from slot 2m+4 on.
-template <int D>
-struct PPCfg {
-  static constexpr int NW = 8;                    // waves per workgroup
-  static constexpr int BR = 32 * NW;              // query rows per workgroup
-  static constexpr int BC = 64;                   // keys per tile
-  static constexpr int ROWB = D * 2;
-  static constexpr int TILE = BC * ROWB;
-  static constexpr int STAGE = 2 * TILE;          // K tile + V tile
-  static constexpr int NBUF = 4;                  // stages in the ring
-  static constexpr int LDS = NBUF * STAGE;
-  static constexpr int CHUNKS = D / 8;
-  static constexpr int DMA = TILE / 1024 / NW;    // 1 KiB copies per wave per tensor
-  static constexpr int NC = D / 16;
-  static constexpr int NDT = D / 32;
-  static constexpr int NS = BC / 2;
-};
-
-// Does tile c hold any key this wave's queries may see?
-__device__ __forceinline__ bool pp_live(const AttnArgs& a, const Cursor& c, int wrows,
-                                        long long wq_hi) {
-  if (c.blk >= a.nblk || wrows <= 0) return false;
-  const long long kp = a.blk[c.blk].k_pos0 + (long long)c.t * 64;
-  return !(a.causal && kp > wq_hi);
-}
-
-template <int D>
-__device__ __forceinline__ void pp_copy(const void* src, int len, int ti, int b, int h, int H,
-                                        int HD2, int wave, const int* voff, char* dst) {
-  using C = PPCfg<D>;
-  const int kt0 = ti * C::BC;
-  const int rows = min(C::BC, len - kt0);
-  const long long off = (((long long)b * len + kt0) * H + h) * (D * 2);
-  const int nrec = (rows - 1) * HD2 + D * 2;
-  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)src + off), 0, nrec, kRsrcWord3);
-#pragma unroll
-  for (int i = 0; i < C::DMA; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (lds_void_ptr)(dst + (wave * C::DMA + i) * 1024), 16, voff[i], 0, 0, 0);
-}
-
-// Copy K and V of tile c (ordinal m) into ring stage m % NBUF.
-template <int D>
-__device__ __forceinline__ void pp_copy_tile(const AttnArgs& a, const Cursor& c, int m, char* smem,
-                                             int b, int h, int HD2, int wave, const int* voffk,
-                                             const int* voffv) {
-  using C = PPCfg<D>;
-  const KVBlock& kb = a.blk[c.blk];
-  char* st = smem + (m & (C::NBUF - 1)) * C::STAGE;
-  pp_copy<D>(kb.k, kb.len, c.t, b, h, a.H, HD2, wave, voffk, st);
-  pp_copy<D>(kb.v, kb.len, c.t, b, h, a.H, HD2, wave, voffv, st + C::TILE);
-}
-
-template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void ring_attn_bf16_pp(const AttnArgs a) {
-  using C = PPCfg<D>;
-  constexpr int BC = C::BC;
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int grp = wave >> 2;
-  const int lane = tid & 63;
-  const int col = lane & 31;
-  const int half = lane >> 5;
-
-  int b, h, qt;
-  tile_coords(a, b, h, qt);
-  const int row0 = qt * C::BR;
-  const int rows_here = min(C::BR, a.Sq - row0);
-  const long long q_lo = a.q_pos0 + row0;
-  const long long q_hi = q_lo + rows_here - 1;
-  const int wrow0 = row0 + wave * 32;
-  const int wrows = min(32, a.Sq - wrow0);
-  const long long wq_lo = a.q_pos0 + wrow0;
-  const long long wq_hi = wq_lo + wrows - 1;
-  const long long HD = (long long)a.H * D;
-  const int HD2 = a.H * D * 2;
-  const float c_scale = a.scale_log2;
-
-  bf16x8 qf[C::NC];
-  {
-    const int r = wrow0 + col;
-    const __bf16* qp = (const __bf16*)a.q + ((long long)b * a.Sq + r) * HD + (long long)h * D;
-#pragma unroll
-    for (int c = 0; c < C::NC; ++c)
-      qf[c] = r < a.Sq ? *(const bf16x8*)(qp + 16 * c + 8 * half) : bf16x8{};
-  }
-  int voffk[C::DMA], voffv[C::DMA];
-#pragma unroll
-  for (int i = 0; i < C::DMA; ++i) {
-    const int p = (wave * C::DMA + i) * 64 + lane;
-    const int r = p / C::CHUNKS, pc = p % C::CHUNKS;
-    voffk[i] = r * HD2 + swz_k<D>(r, pc) * 16;
-    voffv[i] = r * HD2 + swz_v<D>(r, pc) * 16;
-  }
-  int kaddr[C::NC];
-#pragma unroll
-  for (int c = 0; c < C::NC; ++c) kaddr[c] = col * C::ROWB + swz_k<D>(col, 2 * c + half) * 16;
-  int vaddr[C::NDT];
-  {
-    const int j = lane & 15, e = j >> 2, q = j & 3, g = lane >> 4;
-    const int kl = 4 * half + e;
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) {
-      const int d0 = 32 * dt + 16 * (g & 1) + 4 * q;
-      vaddr[dt] = kl * C::ROWB + swz_v<D>(kl, d0 >> 3) * 16 + (d0 & 7) * 2;
-    }
-  }
-  f32x16 oacc[C::NDT];
-#pragma unroll
-  for (int i = 0; i < C::NDT; ++i) oacc[i] = f32x16{};
-  float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.0f;
-
-  // number of visited tiles (uniform over the workgroup)
-  int T = 0;
-  for (int bi = 0; bi < a.nblk; ++bi) T += tiles_of<BC>(a, bi, q_hi);
-
-
-  // prologue: tiles 0 and 1
-  Cursor cd = cursor_first(a, q_hi);   // next tile to copy
-  int md = 0;                          // its ordinal
-  for (int k = 0; k < 2 && md < T; ++k) {
-    pp_copy_tile<D>(a, cd, md, smem, b, h, HD2, wave, voffk, voffv);
-    cd = cursor_next(a, q_hi, cd);
-    ++md;
-  }
-  if (T > 1) wait_vmcnt<2 * C::DMA>();
-  else wait_vmcnt<0>();
-  __syncthreads();
-
-  Cursor c0 = cursor_first(a, q_hi);   // tile n (softmax / PV)
-  Cursor c1 = cursor_next(a, q_hi, c0);  // tile n+1 (scores)
-  int n = 0;
-  f32x16 sc[2];
-  bf16x8 pb[C::NS / 8];
-  bool live_sc = false;                // sc holds scores of tile n
-
-  for (int s = 0; s <= 2 * T + 1; ++s) {
-    if ((s & 1) == 0 && md < T && md == s / 2 + 2) {
-      pp_copy_tile<D>(a, cd, md, smem, b, h, HD2, wave, voffk, voffv);
-      cd = cursor_next(a, q_hi, cd);
-      ++md;
-    }
-    const int p = s - grp;
-    if (p == 0) {
-      if (pp_live(a, c0, wrows, wq_hi)) {
-        char* kb = smem + 0;
-        f32x16 acc[2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          acc[kt] = f32x16{};
-#pragma unroll
-          for (int c = 0; c < C::NC; ++c) {
-            const bf16x8 kf = *(const bf16x8*)(kb + kt * 32 * C::ROWB + kaddr[c]);
-            acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], acc[kt], 0, 0, 0);
-          }
-        }
-        sc[0] = acc[0];
-        sc[1] = acc[1];
-        live_sc = true;
-      }
-    } else if (p > 0 && p <= 2 * T && (p & 1)) {
-      // vector phase: softmax of tile n ([RA] §3.2, lazy reference max)
-      if (live_sc) {
-        const KVBlock& kb0 = a.blk[c0.blk];
-        const int kt0 = c0.t * BC;
-        const long long kp0 = kb0.k_pos0 + kt0;
-        long long lim_ll = kb0.len - kt0;
-        if (a.valid_len - kp0 < lim_ll) lim_ll = a.valid_len - kp0;
-        if (lim_ll < BC || (a.causal && kp0 + BC - 1 > wq_lo)) {
-          const int klim = (int)max(0LL, lim_ll);
-          int t = min(klim, BC) - 1 - 4 * half;
-          if (a.causal) {
-            const long long d = wq_lo - kp0;
-            const int dc = (int)(d < -2 * BC ? -2 * BC : (d > 2 * BC ? 2 * BC : d));
-            t = min(t, max(-1, dc + col - 4 * half));
-          }
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-              if (32 * kt + 8 * (v >> 2) + (v & 3) > t) sc[kt][v] = -INFINITY;
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < C::NS; ++i) mx = fmaxf(mx, sc[i >> 4][i & 15]);
-        mx = pair_max(mx) * c_scale;
-        m_true = fmaxf(m_true, mx);
-        const bool need = mx > m_ref + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-          const float m_new = need ? mx : m_ref;
-          const float alpha = need ? fast_exp2(m_ref - mx) : 1.0f;
-          l_run *= alpha;
-#pragma unroll
-          for (int i = 0; i < C::NDT; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
-          m_ref = m_new;
-        }
-        const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
-        exp_tile(sc, m_use, c_scale, pb, l_run);
-      }
-    } else if (p >= 2 && p <= 2 * T) {
-      // matrix phase: S^T(n+1) and O^T += V(n)^T P(n)^T
-      __builtin_amdgcn_s_setprio(1);
-      const bool pv = live_sc;
-      const bool nx = n + 1 < T && pp_live(a, c1, wrows, wq_hi);
-      char* kb = smem + ((n + 1) & (C::NBUF - 1)) * C::STAGE;
-      char* vl = smem + (n & (C::NBUF - 1)) * C::STAGE + C::TILE;
-      if (nx && pv) {
-        // one sequence of matrix-core ops: steps 0..2NC-1 build S^T(n+1)
-        // (alternating score tiles), the rest accumulate O^T (alternating
-        // d tiles); operands are read from LDS PF steps ahead
-        constexpr int NK = 2 * C::NC, NSTEP = NK + (BC / 16) * C::NDT, PF = 4;
-        f32x16 acc[2];
-        bf16x8 fr[PF + 1];
-#pragma unroll
-        for (int i = 0; i < NSTEP + PF; ++i) {
-          if (i < NSTEP) {
-            const int f = i;
-            if (f < NK) {
-              fr[f % (PF + 1)] =
-                  *(const bf16x8*)(kb + (f & 1) * 32 * C::ROWB + kaddr[f >> 1]);
-            } else {
-              const int j = f - NK;
-              char* p0 = vl + (j / C::NDT) * 16 * C::ROWB + vaddr[j % C::NDT];
-              const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p0);
-              const s16x4 hi =
-                  __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p0 + 8 * C::ROWB));
-              __builtin_memcpy(&fr[f % (PF + 1)], &lo, 8);
-              __builtin_memcpy((char*)&fr[f % (PF + 1)] + 8, &hi, 8);
-            }
-          }
-          const int st = i - PF;  // matrix step issued in this iteration
-          if (st >= 0) {
-            if (st < NK) {
-              const int kt = st & 1, c = st >> 1;
-              acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  fr[st % (PF + 1)], qf[c], c == 0 ? f32x16{} : acc[kt], 0, 0, 0);
-            } else {
-              const int j = st - NK, G = j / C::NDT, dt = j % C::NDT;
-              oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[st % (PF + 1)], pb[G],
-                                                                 oacc[dt], 0, 0, 0);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        sc[0] = acc[0];
-        sc[1] = acc[1];
-      } else if (nx) {
-        f32x16 acc[2];
-#pragma unroll
-        for (int i = 0; i < 2 * C::NC; ++i) {
-          const int kt = i & 1, c = i >> 1;
-          const bf16x8 kf = *(const bf16x8*)(kb + kt * 32 * C::ROWB + kaddr[c]);
-          acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? f32x16{} : acc[kt],
-                                                            0, 0, 0);
-        }
-        sc[0] = acc[0];
-        sc[1] = acc[1];
-      } else if (pv) {
-#pragma unroll
-        for (int j = 0; j < (BC / 16) * C::NDT; ++j) {
-          const int G = j / C::NDT, dt = j % C::NDT;
-          char* p0 = vl + G * 16 * C::ROWB + vaddr[dt];
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p0);
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p0 + 8 * C::ROWB));
-          bf16x8 vf;
-          __builtin_memcpy(&vf, &lo, 8);
-          __builtin_memcpy((char*)&vf + 8, &hi, 8);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[G], oacc[dt], 0, 0, 0);
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
-      live_sc = nx;
-      c0 = c1;
-      c1 = cursor_next(a, q_hi, c1);
-      ++n;
-    }
-    // before slot 2m (group 0 reads K(m)), tile m's copies must have landed;
-    // only tile m+1's copies may still be outstanding
-    if (s & 1) {
-      const int m = (s + 1) / 2;
-      if (m + 1 < T) wait_vmcnt<2 * C::DMA>();
-      else wait_vmcnt<0>();
-    }
-    __syncthreads();
-  }
-
-  // ---- epilogue: o = u / l, lse = m + ln l ([RA] §3.2; [SPD] §四) ----
-  const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const int r = wrow0 + col;
-  if (wrows > 0 && r < a.Sq) {
-    const long long ro = ((long long)b * a.Sq + r) * HD + (long long)h * D;
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * half;
-        const float x0 = oacc[dt][4 * g + 0] * inv, x1 = oacc[dt][4 * g + 1] * inv;
-        const float x2 = oacc[dt][4 * g + 2] * inv, x3 = oacc[dt][4 * g + 3] * inv;
-        if (a.o_fp32) {
-          *(float4*)((float*)a.o + ro + d) = float4{x0, x1, x2, x3};
-        } else {
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          bf16x4 y;
-          y[0] = (__bf16)x0; y[1] = (__bf16)x1; y[2] = (__bf16)x2; y[3] = (__bf16)x3;
-          *(bf16x4*)((__bf16*)a.o + ro + d) = y;
-        }
-      }
-    if (half == 0) {
-      const long long so = ((long long)b * a.Sq + r) * a.H + h;
-      const bool seen = l_tot > 0.0f;
-      if (a.lse) a.lse[so] = seen ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
-      if (a.m_out) a.m_out[so] = seen ? m_true * kLn2 : -INFINITY;
-      if (a.l_out) a.l_out[so] = seen ? l_tot * fast_exp2(m_ref - m_true) : 0.0f;
     }
   }
 }
@@ -1125,18 +791,24 @@ void ring_attn_f32(const AttnArgs a) {
 // Kernel choice for bf16: the 256-row ping-pong kernel halves K/V traffic
 // per FLOP; the 128-row kernel runs two workgroups per CU.
 
-bool use_pp(const AttnArgs& a) {
+int bf16_waves(const AttnArgs& a) {
   const int mode = ra::option(RA_OPT_ATTN_KERNEL);
-  if (mode == RA_KERNEL_BR128) return false;
-  if (mode == RA_KERNEL_BR256) return true;
-  // AUTO: the 128-row kernel is currently the faster of the two at every
-  // size measured (long-context share: 1043 vs 784 TFLOP/s)
-  return false;
+  if (mode == RA_KERNEL_BR128) return 4;
+  if (mode == RA_KERNEL_BR256) return 8;
+  // AUTO: the 128-row kernel measured faster on every shape tried (the
+  // 256-row one halves the K/V re-reads but keeps its eight waves in step)
+  return 4;
+}
+
+template <int NW>
+void launch_bf16(const AttnArgs& a, int D, dim3 grid, hipStream_t stream) {
+  if (D == 128) hipLaunchKernelGGL((ring_attn_bf16<128, NW>), grid, dim3(64 * NW), 0, stream, a);
+  else hipLaunchKernelGGL((ring_attn_bf16<64, NW>), grid, dim3(64 * NW), 0, stream, a);
 }
 
 ra_status launch(AttnArgs& a, int D, ra_dtype dt, hipStream_t stream, const char* name) {
-  const bool pp = dt == RA_BF16 && use_pp(a);
-  const int br = pp ? PPCfg<128>::BR : kBR;
+  const int nw = dt == RA_BF16 ? bf16_waves(a) : kWaves;
+  const int br = 32 * nw;
   a.n_qtiles = (a.Sq + br - 1) / br;
   const long long n_wg = (long long)a.B * a.H * a.n_qtiles;
   if (n_wg == 0) return RA_OK;
@@ -1144,13 +816,8 @@ ra_status launch(AttnArgs& a, int D, ra_dtype dt, hipStream_t stream, const char
     return ra::fail(RA_ERR_UNSUPPORTED, "%s: too many query tiles", name);
   const dim3 grid((unsigned)n_wg);
   if (dt == RA_BF16) {
-    if (pp) {
-      if (D == 128) hipLaunchKernelGGL(ring_attn_bf16_pp<128>, grid, dim3(512), 0, stream, a);
-      else hipLaunchKernelGGL(ring_attn_bf16_pp<64>, grid, dim3(512), 0, stream, a);
-    } else {
-      if (D == 128) hipLaunchKernelGGL(ring_attn_bf16<128>, grid, dim3(kThreads), 0, stream, a);
-      else hipLaunchKernelGGL(ring_attn_bf16<64>, grid, dim3(kThreads), 0, stream, a);
-    }
+    if (nw == 8) launch_bf16<8>(a, D, grid, stream);
+    else launch_bf16<4>(a, D, grid, stream);
   } else {
     if (D == 128) hipLaunchKernelGGL(ring_attn_f32<128>, grid, dim3(kThreads), 0, stream, a);
     else hipLaunchKernelGGL(ring_attn_f32<64>, grid, dim3(kThreads), 0, stream, a);
