@@ -28,6 +28,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "ra_internal.h"
 
@@ -205,8 +206,17 @@ __device__ __forceinline__ int swz_v(int r, int c) {
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 __device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -220,6 +230,43 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// ds_read_b64_tr_b16 as inline assembly.  The compiler's own form of this
+// read makes it wait for every LDS-DMA copy in flight (it cannot tell which
+// LDS bytes they write), which would stall each P V phase on the copies
+// issued at the start of the same iteration.  Here the read is invisible to
+// the compiler's wait insertion, so its result must be claimed with
+// claim_lds<N> before use; the copies it must not overtake are ordered by
+// the explicit waits and barriers of the pipeline.
+__device__ __forceinline__ s16x4 lds_read_tr16(unsigned addr_lds) {
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr_lds));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ s16x4 lds_read_tr16(unsigned addr_lds) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr_lds), "n"(OFF));
+  return r;
+}
+// Wait until at most N LDS (or scalar-memory) operations of this wave are
+// outstanding, and make `x` depend on the wait so that no use of it is
+// scheduled before.  LDS operations complete in issue order, so with N =
+// the number of LDS reads issued after the one that produced x, x is ready.
+template <int N, typename T>
+__device__ __forceinline__ void claim_lds(T& x) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "n"(N));
+}
+// Workgroup barrier for the copy pipeline.  The caller has already waited
+// (vmcnt) for the copies that must be visible after it; unlike
+// __syncthreads, this does not also wait for the copies that may stay in
+// flight.  All of this wave's LDS reads have returned (lgkmcnt(0)), so the
+// buffers they read may be overwritten once every wave has arrived.
+__device__ __forceinline__ void pipeline_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Position in the visited-tile sequence: tile t (of n) of visited block blk.
@@ -439,38 +486,44 @@ __device__ __forceinline__ void pipeline_step(
   // O^T += V(n)^T P(n)^T: fragment j = (G = j / NDT, dt = j % NDT) is read
   // two ops ahead, and consecutive ops accumulate into different d tiles
   if (live0) {
-    char* vl = smem + C::VB + vb * C::TILE;
     constexpr int NJ = (BC / 16) * C::NDT;
     constexpr int PF = NJ >= 8 ? 4 : 2;
-    auto vread = [&](int j) -> bf16x8 {
-      char* p0 = vl + (j / C::NDT) * 16 * C::ROWB + w.vaddr[j % C::NDT];
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p0);
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p0 + 8 * C::ROWB));
-      bf16x8 vf;
-      __builtin_memcpy(&vf, &lo, 8);
-      __builtin_memcpy((char*)&vf + 8, &hi, 8);
-      return vf;
-    };
-    bf16x8 vf[PF + 1];
+    unsigned vbase[C::NDT];
+    const unsigned vl = (unsigned)(size_t)(lds_void_ptr)(smem + C::VB + vb * C::TILE);
 #pragma unroll
-    for (int j = 0; j < PF; ++j) vf[j] = vread(j);
+    for (int dt = 0; dt < C::NDT; ++dt) vbase[dt] = vl + w.vaddr[dt];
+    // two 64-bit transposed reads per fragment: keys 16G .. 16G+7 and
+    // 16G+8 .. 16G+15 of the fragment's d tile
+    s16x8 vr[PF + 1];
+    auto vread = [&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int off = (j / C::NDT) * 16 * C::ROWB;
+      const s16x4 lo = lds_read_tr16<off>(vbase[j % C::NDT]);
+      const s16x4 hi = lds_read_tr16<off + 8 * C::ROWB>(vbase[j % C::NDT]);
+      vr[j % (PF + 1)] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    static_for<0, PF>([&](auto jc) { vread(jc); });
     // this phase is matrix-core bound: give it issue priority over the
     // other wave on the SIMD, whose exponentials fill the gaps
     __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      if (j + PF < NJ) vf[(j + PF) % (PF + 1)] = vread(j + PF);
-      const int G = j / C::NDT, dt = j % C::NDT;
-      w.oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j % (PF + 1)], pb[G], w.oacc[dt],
-                                                           0, 0, 0);
+    static_for<0, NJ>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j + PF < NJ) vread(std::integral_constant<int, j + PF>{});
+      // reads issued after fragment j's: those of fragments j+1 .. j+PF
+      constexpr int later = 2 * ((j + PF < NJ ? j + PF : NJ - 1) - j);
+      claim_lds<later>(vr[j % (PF + 1)]);
+      bf16x8 vf;
+      __builtin_memcpy(&vf, &vr[j % (PF + 1)], 16);
+      constexpr int G = j / C::NDT, dt = j % C::NDT;
+      w.oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[G], w.oacc[dt], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     __builtin_amdgcn_s_setprio(0);
   }
   // this wave's K(n+2) copy (and everything older) landed; V(n+2) may fly
   if (copy2) wait_vmcnt<C::DMA>();
   else wait_vmcnt<0>();
-  __syncthreads();  // everyone's copies landed, everyone done reading
+  pipeline_barrier();  // everyone's copies landed, everyone done reading
   t0 = t1;
   t1 = t2;
   t2 = cursor_next(a, q_hi, t2);
@@ -594,6 +647,563 @@ void ring_attn_bf16(const AttnArgs a) {
       if (a.lse) a.lse[so] = seen ? (w.m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
       if (a.m_out) a.m_out[so] = seen ? w.m_true * kLn2 : -INFINITY;
       if (a.l_out) a.l_out[so] = seen ? l_tot * fast_exp2(w.m_ref - w.m_true) : 0.0f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernel, 64 query rows per wave
+// ---------------------------------------------------------------------------
+// Same arithmetic as ring_attn_bf16, but each wave owns 64 query rows (two
+// 32-row column blocks cb = 0, 1) and runs alone on its SIMD with the whole
+// register file (512 registers; the O^T accumulators live in AGPRs).  Every
+// K or V fragment read from LDS then feeds two matrix ops instead of one,
+// which halves LDS read traffic per FLOP, and a workgroup of four waves
+// covers 256 query rows, which halves the HBM/L2 -> LDS copies per FLOP.
+//
+// K/V move through LDS in stages of 64 keys; the wave computes in sub-tiles
+// of 32 keys.  Sub-step j (two per stage) runs
+//   phase B: S^T(j+1) = K(j+1) Q^T on the matrix cores, interleaved with
+//            the exponentials of tile j and their bf16 copy P(j);
+//   phase C: O^T += V(j)^T P(j)^T, interleaved with the denominator of P(j),
+//            the mask and row max of S(j+1), the choice of its reference max
+//            and the scaled, shifted scores of S(j+1).
+// A rescale of O and l forced by a new reference max (rare, see the lazy
+// reference above) is applied at the start of the next sub-step, after the
+// P V products of the old reference were issued.
+//
+// Stage pipeline (n = stage of the iteration): LDS holds K(n), K(n+1), V(n);
+// the iteration issues the copies of K(n+3) and V(n+2) and, before its
+// closing barrier, waits for those of K(n+2) and V(n+1), issued one
+// iteration earlier: every copy has two iterations to land.  Four K and
+// three V buffers (112 KiB at D = 128).
+template <int D>
+struct W64Cfg {
+  static constexpr int NW = 4;                    // waves per workgroup
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int WR = 64;                   // query rows per wave
+  static constexpr int BR = NW * WR;              // query rows per workgroup
+  static constexpr int BC = 64;                   // keys per LDS stage
+  static constexpr int ROWB = D * 2;              // bytes per key row in LDS
+  static constexpr int TILE = BC * ROWB;          // one K or V stage
+  static constexpr int NKB = 4, NVB = 3;          // stage buffers
+  static constexpr int KB = 0, VB = NKB * TILE;
+  static constexpr int LDS = (NKB + NVB) * TILE;
+  static constexpr int CHUNKS = D / 8;
+  static constexpr int DMA = TILE / 1024 / NW;    // 1 KiB copies per wave per stage
+  static constexpr int NC = D / 16;               // k-steps of S^T
+  static constexpr int NDT = D / 32;              // 32-row d tiles of O^T
+};
+
+// A 64-key stage of the visited sequence with everything the loop needs
+// about it.  The kernel arguments (the block table) are read only when the
+// sequence enters a new block; inside a block a stage advances by pointer
+// arithmetic.  Positions are 32-bit here (the host routes longer sequences
+// to the other kernels).
+struct Stage {
+  int blk;           // visited block, a.nblk once past the end
+  int t, n;          // stage t of the n this workgroup visits in the block
+  int kp;            // global position of the stage's first key
+  int rows;          // rows of the block from that key on (>= 64: a full stage)
+  const char* k;     // K of this (batch, head) from that key on
+  const char* v;     // V likewise
+};
+
+__device__ __forceinline__ Stage stage_enter(const AttnArgs& a, int blk, long long q_hi, int b,
+                                             int h, int D2, int HD2) {
+  Stage s;
+  s.blk = blk;
+  s.t = 0;
+  s.n = 0;
+  while (s.blk < a.nblk && (s.n = tiles_of<64>(a, s.blk, q_hi)) == 0) ++s.blk;
+  s.kp = 0;
+  s.rows = 0;
+  s.k = s.v = nullptr;
+  if (s.blk < a.nblk) {
+    const KVBlock& kb = a.blk[s.blk];
+    const long long off = (long long)b * kb.len * HD2 + (long long)h * D2;
+    s.kp = (int)kb.k_pos0;
+    s.rows = kb.len;
+    s.k = (const char*)kb.k + off;
+    s.v = (const char*)kb.v + off;
+  }
+  return s;
+}
+
+__device__ __forceinline__ Stage stage_next(const AttnArgs& a, Stage s, long long q_hi, int b,
+                                            int h, int D2, int HD2) {
+  if (s.blk >= a.nblk) return s;
+  if (++s.t < s.n) {
+    s.kp += 64;
+    s.rows -= 64;
+    s.k += 64LL * HD2;
+    s.v += 64LL * HD2;
+    return s;
+  }
+  return stage_enter(a, s.blk + 1, q_hi, b, h, D2, HD2);
+}
+
+// Copy one stage (64 key rows of K or V from src) into LDS at dst; each wave
+// copies its share.  Rows past the block's end come back as zeros from the
+// buffer range check.  lds_wave is this wave's first 1 KiB slot (uniform).
+template <int D>
+__device__ __forceinline__ void copy_stage(const char* src, int rows, int HD2, const int* voff,
+                                           unsigned dst) {
+  using C = W64Cfg<D>;
+  const int nrec = (min(rows, C::BC) - 1) * HD2 + D * 2;
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, nrec, kRsrcWord3);
+#pragma unroll
+  for (int i = 0; i < C::DMA; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(size_t)(dst + i * 1024), 16,
+                                             voff[i], 0, 0, 0);
+}
+
+// One 32-key sub-tile as this wave sees it.
+struct Sub {
+  bool mask;       // some (row, key) pair of it must be masked (all, if dead)
+  int kp;          // global position of its first key
+  int klim;        // keys [0, klim) exist, are not padding and may be visible
+};
+
+__device__ __forceinline__ Sub sub_info(const Stage& st, int sub, bool causal, int valid_len,
+                                        int wq_lo, int wq_hi, bool wave_live) {
+  Sub s{true, 0, 0};  // dead: every pair masked
+  if (!wave_live || st.n == 0) return s;
+  s.kp = st.kp + 32 * sub;
+  int lim = min(st.rows - 32 * sub, valid_len - s.kp);
+  lim = min(lim, 32);
+  const bool live = lim > 0 && !(causal && s.kp > wq_hi);
+  s.klim = live ? lim : 0;
+  s.mask = !live || lim < 32 || (causal && s.kp + 31 > wq_lo);
+  return s;
+}
+
+template <int D>
+struct W64State {
+  using C = W64Cfg<D>;
+  bf16x8 qf[2][C::NC];     // Q^T fragments of the two column blocks
+  f32x16 oacc[2][C::NDT];  // O^T accumulators (unnormalised u)
+  float m_ref[2];          // reference max (base 2), -inf before any key
+  float m_true[2];         // exact running max (base 2)
+  float m_use[2];          // shift applied to the scores in flight
+  float alpha[2];          // pending rescale factor of O and l
+  float l_run[2];          // this lane's half of sum of bf16(2^(s - m_ref))
+  int kaddr[C::NC];
+  int vaddr[C::NDT];
+  int voffk[C::DMA];
+  int voffv[C::DMA];
+};
+
+// Mask of S^T for column block cb of a sub-tile: key j (0..31) of lane
+// (col, half) at register v is 8*(v/4) + v%4 + 4*half; it is masked when
+// j >= klim or, causal, when its position exceeds the query's.
+__device__ __forceinline__ void mask_sub(f32x16& s, const Sub& st, bool causal, int wq_lo,
+                                         int cb, int col, int half) {
+  int t = st.klim - 1 - 4 * half;
+  if (causal) {
+    const int dc = min(64, max(-64, wq_lo + 32 * cb - st.kp));
+    t = min(t, max(-1, dc + col - 4 * half));
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    if (8 * (v >> 2) + (v & 3) > t) s[v] = -INFINITY;
+}
+
+// max(a, b, c) in one instruction.  Written as assembly because the
+// compiler's fmaxf first quiets signalling NaNs (an extra v_max per operand)
+// for values it cannot prove canonical, such as matrix-core results.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// S^T = K Q^T products with the accumulator in VGPRs, written as assembly.
+// The compiler would put every matrix-core accumulator of this kernel in
+// AGPRs (it needs more than 256 registers), and the scores would then have
+// to be copied out before any vector instruction could read them.  As the
+// compiler does not see these as matrix ops, the reader of a result must
+// first let the matrix pipe drain (mfma_results_ready); dependent products
+// on the same accumulator need no wait.
+__device__ __forceinline__ void mfma_v_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// 16 wait states: more than an 8-pass matrix op needs before a vector
+// instruction may read its result.
+__device__ __forceinline__ void mfma_results_ready() {
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+__device__ __forceinline__ float max16(const f32x16& s) {
+  float a = fmaxf(fmaxf(s[0], s[1]), s[2]), b = fmaxf(fmaxf(s[3], s[4]), s[5]);
+  float c = fmaxf(fmaxf(s[6], s[7]), s[8]), d = fmaxf(fmaxf(s[9], s[10]), s[11]);
+  float e = fmaxf(fmaxf(s[12], s[13]), s[14]);
+  return fmaxf(fmaxf(fmaxf(a, b), fmaxf(c, d)), fmaxf(e, s[15]));
+}
+
+// Row max of the (masked) scores of the next sub-tile and the choice of
+// its reference ([RA] §3.2 with the lazy reference): sets m_use and, when
+// the reference moves, alpha and the returned flag.
+template <int D>
+__device__ __forceinline__ bool decide(W64State<D>& w, const float (&mlane)[2], float c_scale) {
+  float mx[2];
+  bool need[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    mx[cb] = pair_max(mlane[cb]) * c_scale;
+    w.m_true[cb] = fmaxf(w.m_true[cb], mx[cb]);
+    need[cb] = mx[cb] > w.m_ref[cb] + kRescaleSlack;
+  }
+  const bool any = __builtin_amdgcn_ballot_w64(need[0] || need[1]) != 0;
+  if (any) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      w.alpha[cb] = need[cb] ? fast_exp2(w.m_ref[cb] - mx[cb]) : 1.0f;
+      w.m_ref[cb] = need[cb] ? mx[cb] : w.m_ref[cb];
+    }
+  }
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) w.m_use[cb] = w.m_ref[cb] == -INFINITY ? 0.0f : w.m_ref[cb];
+  return any;
+}
+
+// acc *= alpha for an accumulator held in AGPRs.  The product is formed in
+// inline assembly on each AGPR in place, so the accumulator never has to
+// leave the AGPR file (vector ALU instructions cannot name AGPRs).
+__device__ __forceinline__ void scale_agpr(f32x16& acc, float alpha) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float x = acc[v], t;
+    asm volatile(
+        "v_accvgpr_read_b32 %1, %0\n\t"
+        "v_mul_f32 %1, %1, %2\n\t"
+        "v_accvgpr_write_b32 %0, %1"
+        : "+a"(x), "=&v"(t)
+        : "v"(alpha));
+    acc[v] = x;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void apply_rescale(W64State<D>& w) {
+  using C = W64Cfg<D>;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    w.l_run[cb] *= w.alpha[cb];
+#pragma unroll
+    for (int i = 0; i < C::NDT; ++i) scale_agpr(w.oacc[cb][i], w.alpha[cb]);
+  }
+}
+
+// S^T of one sub-tile (no interleave): K rows at LDS offset kofs; results
+// readable after mfma_results_ready().
+template <int D>
+__device__ __forceinline__ void scores_sub(char* smem, int kofs, const W64State<D>& w,
+                                           f32x16 (&s)[2]) {
+  using C = W64Cfg<D>;
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) {
+    const bf16x8 kf = *(const bf16x8*)(smem + kofs + w.kaddr[c]);
+    if (c == 0) {
+      mfma_v_first(s[0], kf, w.qf[0][c]);
+      mfma_v_first(s[1], kf, w.qf[1][c]);
+    } else {
+      mfma_v_acc(s[0], kf, w.qf[0][c]);
+      mfma_v_acc(s[1], kf, w.qf[1][c]);
+    }
+  }
+}
+
+// One sub-step.  s_cur holds the raw scores of sub-tile j (cur, masked,
+// reference already chosen), s_nxt receives S^T of sub-tile j+1 (nxt) from
+// the K rows at LDS offset kofs; P(j) V(j) uses the V rows at LDS offset
+// vofs (32 keys).  The code has no branch on liveness: a sub-tile that is
+// dead for this wave is masked entirely (its scores become -inf, its
+// weights 0), which keeps the O^T accumulators in one register class across
+// the loop.  The V rows of cur always belong to a copied stage (zero-filled
+// past a block's end), so 0 * V stays 0; the K rows of a dead nxt may be
+// stale, but are always rows of a copied stage, and the mask replaces every
+// score they produce.
+template <int D>
+__device__ __forceinline__ void w64_substep(const AttnArgs& a, char* smem, W64State<D>& w,
+                                            f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+                                            const Sub& nxt, int kofs, unsigned vofs,
+                                            bool& pending, int wq_lo, int col, int half) {
+  using C = W64Cfg<D>;
+  const float c_scale = a.scale_log2;
+  if (pending) {  // the reference moved when cur's reference was chosen
+    apply_rescale(w);
+    pending = false;
+  }
+  // ---- phase B: S^T(nxt) alongside the weights P(cur) ----
+  bf16x8 pb[2][2];
+  {
+    constexpr int NSTEP = 2 * C::NC;     // matrix ops (k-step c, block cb)
+    constexpr int PF = 3;                // K fragment lead (fragments)
+    bf16x8 kf[PF + 1];
+    auto kread = [&](int c) -> bf16x8 { return *(const bf16x8*)(smem + kofs + w.kaddr[c]); };
+#pragma unroll
+    for (int c = 0; c < PF; ++c) kf[c] = kread(c);
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+      const int c = i >> 1, cb = i & 1;
+      if (cb == 0 && c + PF < C::NC) kf[(c + PF) % (PF + 1)] = kread(c + PF);
+      if (c == 0) mfma_v_first(s_nxt[cb], kf[c % (PF + 1)], w.qf[cb][c]);
+      else mfma_v_acc(s_nxt[cb], kf[c % (PF + 1)], w.qf[cb][c]);
+      // 32 / NSTEP weights of cur per op (score x: block x / 16, register
+      // x % 16): p = 2^(s * scale - m_use), rounded to bf16
+      constexpr int PER = 32 / NSTEP;
+#pragma unroll
+      for (int x = i * PER; x < (i + 1) * PER; x += 2) {
+        const int eb = x >> 4, v = x & 15;
+        const float e0 = fast_exp2(fmaf(s_cur[eb][v], c_scale, -w.m_use[eb]));
+        const float e1 = fast_exp2(fmaf(s_cur[eb][v + 1], c_scale, -w.m_use[eb]));
+        pb[eb][v >> 3][v & 7] = (__bf16)e0;
+        pb[eb][v >> 3][(v & 7) + 1] = (__bf16)e1;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // keep the weights here, under the matrix ops, rather than let the
+    // compiler sink them to their first use in phase C
+    asm volatile("" ::"v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[1][0]), "v"(pb[1][1]));
+  }
+  mfma_results_ready();
+  if (nxt.mask) {  // diagonal, ragged or dead sub-tile
+    mask_sub(s_nxt[0], nxt, a.causal, wq_lo, 0, col, half);
+    mask_sub(s_nxt[1], nxt, a.causal, wq_lo, 1, col, half);
+  }
+  // ---- phase C: O^T += V(cur)^T P(cur)^T alongside the max of nxt (first
+  // half of the ops) and the denominator of P(cur) (second half) ----
+  {
+    constexpr int NF = 2 * C::NDT;       // V fragments (G, dt) of the sub-tile
+    constexpr int NJ = 2 * NF;           // matrix ops (fragment, block cb)
+    constexpr int PF = 2;                // V fragment lead (fragments)
+    s16x8 vr[PF + 1];
+    auto vread = [&](auto fc) {
+      constexpr int f = decltype(fc)::value;
+      constexpr int off = (f / C::NDT) * 16 * C::ROWB;
+      const unsigned base = vofs + w.vaddr[f % C::NDT];
+      const s16x4 lo = lds_read_tr16<off>(base);
+      const s16x4 hi = lds_read_tr16<off + 8 * C::ROWB>(base);
+      vr[f % (PF + 1)] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    static_for<0, PF>([&](auto fc) { vread(fc); });
+    float lp[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+    float mxp[2] = {-INFINITY, -INFINITY};  // this lane's max of nxt per block
+    auto pv_op = [&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int f = j / 2, cb = j % 2;
+      if constexpr (cb == 0) {
+        if constexpr (f + PF < NF) vread(std::integral_constant<int, f + PF>{});
+        constexpr int later = 2 * ((f + PF < NF ? f + PF : NF - 1) - f);
+        claim_lds<later>(vr[f % (PF + 1)]);
+      }
+      bf16x8 vf;
+      __builtin_memcpy(&vf, &vr[f % (PF + 1)], 16);
+      constexpr int G = f / C::NDT, dt = f % C::NDT;
+      w.oacc[cb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[cb][G], w.oacc[cb][dt],
+                                                               0, 0, 0);
+    };
+    constexpr int NH = NJ / 2;
+    static_for<0, NH>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      pv_op(jc);
+      // 32 / NH scores of nxt into its row max (score x: block x / 16)
+      static_for<0, 32 / NH / 2>([&](auto yc) {
+        constexpr int x = j * 32 / NH + 2 * decltype(yc)::value;
+        constexpr int mb = x >> 4, q = x & 15;
+        mxp[mb] = vmax3(mxp[mb], s_nxt[mb][q], s_nxt[mb][q + 1]);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    pending = decide(w, mxp, c_scale);
+    static_for<NH, NJ>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      pv_op(jc);
+      // 16 / NH bf16 pairs of P(cur) into the denominator (pair x: block
+      // x / 8, fragment (x / 4) % 2, elements 2 (x % 4), +1)
+      static_for<(j - NH) * 16 / NH, (j - NH + 1) * 16 / NH>([&](auto xc) {
+        constexpr int x = decltype(xc)::value;
+        constexpr int eb = x >> 3, G2 = (x >> 2) & 1, e = 2 * (x & 3);
+        const bf16x2 pr = {pb[eb][G2][e], pb[eb][G2][e + 1]};
+        lp[eb][x & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, lp[eb][x & 1], false);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // keep the denominator updates under the matrix ops as well
+    asm volatile("" ::"v"(lp[0][0]), "v"(lp[0][1]), "v"(lp[1][0]), "v"(lp[1][1]));
+    w.l_run[0] += lp[0][0] + lp[0][1];
+    w.l_run[1] += lp[1][0] + lp[1][1];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ring_attn_bf16_w64(const AttnArgs a) {
+  using C = W64Cfg<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  int b, h, qt;
+  tile_coords(a, b, h, qt);
+  const int row0 = qt * C::BR;
+  const int rows_here = min(C::BR, a.Sq - row0);
+  const long long q_hi = a.q_pos0 + row0 + rows_here - 1;
+  const int wrow0 = row0 + wave * C::WR;
+  const int wrows = min(C::WR, a.Sq - wrow0);
+  const bool wave_live = wrows > 0;
+  const int wq_lo = (int)a.q_pos0 + wrow0;
+  const int wq_hi = wq_lo + wrows - 1;
+  const int valid_len = a.valid_len > 0x7fffffffLL ? 0x7fffffff : (int)a.valid_len;
+  const bool causal = a.causal != 0;
+  const long long HD = (long long)a.H * D;
+  const int D2 = D * 2;
+  const int HD2 = a.H * D2;
+
+  W64State<D> w;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int r = wrow0 + 32 * cb + col;
+    const __bf16* qp = (const __bf16*)a.q + ((long long)b * a.Sq + r) * HD + (long long)h * D;
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c)
+      w.qf[cb][c] = r < a.Sq ? *(const bf16x8*)(qp + 16 * c + 8 * half) : bf16x8{};
+  }
+#pragma unroll
+  for (int i = 0; i < C::DMA; ++i) {
+    const int p = (wave * C::DMA + i) * 64 + lane;
+    const int r = p / C::CHUNKS, pc = p % C::CHUNKS;
+    w.voffk[i] = r * HD2 + swz_k<D>(r, pc) * 16;
+    w.voffv[i] = r * HD2 + swz_v<D>(r, pc) * 16;
+  }
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) w.kaddr[c] = col * C::ROWB + swz_k<D>(col, 2 * c + half) * 16;
+  {
+    const int j = lane & 15, e = j >> 2, q = j & 3, g = lane >> 4;
+    const int kl = 4 * half + e;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+      const int d0 = 32 * dt + 16 * (g & 1) + 4 * q;
+      w.vaddr[dt] = kl * C::ROWB + swz_v<D>(kl, d0 >> 3) * 16 + (d0 & 7) * 2;
+    }
+  }
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+    for (int i = 0; i < C::NDT; ++i) w.oacc[cb][i] = f32x16{};
+    w.m_ref[cb] = -INFINITY;
+    w.m_true[cb] = -INFINITY;
+    w.m_use[cb] = 0.0f;
+    w.alpha[cb] = 1.0f;
+    w.l_run[cb] = 0.0f;
+  }
+  const unsigned smem_lds = (unsigned)(size_t)(lds_void_ptr)smem;
+  // this wave's 1 KiB copy slots within a stage buffer
+  const unsigned kdst0 = smem_lds + C::KB + wave * C::DMA * 1024;
+  const unsigned vdst0 = smem_lds + C::VB + wave * C::DMA * 1024;
+
+  // prologue: stages 0..2 of K, 0..1 of V; scores of sub-tile 0
+  Stage t0 = stage_enter(a, 0, q_hi, b, h, D2, HD2);
+  Stage t1 = stage_next(a, t0, q_hi, b, h, D2, HD2);
+  Stage t2 = stage_next(a, t1, q_hi, b, h, D2, HD2);
+  Stage t3 = stage_next(a, t2, q_hi, b, h, D2, HD2);
+  if (t0.blk < a.nblk) {
+    copy_stage<D>(t0.k, t0.rows, HD2, w.voffk, kdst0);
+    copy_stage<D>(t0.v, t0.rows, HD2, w.voffv, vdst0);
+  }
+  if (t1.blk < a.nblk) {
+    copy_stage<D>(t1.k, t1.rows, HD2, w.voffk, kdst0 + C::TILE);
+    copy_stage<D>(t1.v, t1.rows, HD2, w.voffv, vdst0 + C::TILE);
+  }
+  if (t2.blk < a.nblk) copy_stage<D>(t2.k, t2.rows, HD2, w.voffk, kdst0 + 2 * C::TILE);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 sA[2], sB[2];
+  bool pending = false;
+  if (t0.blk < a.nblk) {
+    const Sub s0 = sub_info(t0, 0, causal, valid_len, wq_lo, wq_hi, wave_live);
+    scores_sub<D>(smem, C::KB, w, sA);
+    mfma_results_ready();
+    if (s0.mask) {
+      mask_sub(sA[0], s0, causal, wq_lo, 0, col, half);
+      mask_sub(sA[1], s0, causal, wq_lo, 1, col, half);
+    }
+    const float ml[2] = {max16(sA[0]), max16(sA[1])};
+    decide(w, ml, a.scale_log2);  // nothing accumulated yet: no rescale
+  }
+
+  int kb0 = 0, vb0 = 0;  // K / V buffer of stage n
+  while (t0.blk < a.nblk) {
+    // copies of K(n+3) and V(n+2) into the buffers stage n-1 released
+    const bool ck = t3.blk < a.nblk, cv = t2.blk < a.nblk;
+    if (cv) {
+      const int vbuf = vb0 == 0 ? 2 : vb0 - 1;  // (n + 2) % 3
+      copy_stage<D>(t2.v, t2.rows, HD2, w.voffv, vdst0 + vbuf * C::TILE);
+    }
+    if (ck) copy_stage<D>(t3.k, t3.rows, HD2, w.voffk, kdst0 + ((kb0 + 3) & 3) * C::TILE);
+    const Sub s01 = sub_info(t0, 1, causal, valid_len, wq_lo, wq_hi, wave_live);
+    const Sub s10 = sub_info(t1, 0, causal, valid_len, wq_lo, wq_hi, wave_live);
+    const int k_n = C::KB + kb0 * C::TILE;
+    // past the last stage nxt is dead: point it at rows that were copied
+    const int k_n1 = t1.blk < a.nblk ? C::KB + ((kb0 + 1) & 3) * C::TILE : k_n;
+    const unsigned v_n = smem_lds + C::VB + vb0 * C::TILE;
+    // sub-step 2n: S(stage n, sub 1), P V of (stage n, sub 0)
+    w64_substep<D>(a, smem, w, sA, sB, s01, k_n + 32 * C::ROWB, v_n, pending, wq_lo, col, half);
+    // sub-step 2n+1: S(stage n+1, sub 0), P V of (stage n, sub 1)
+    w64_substep<D>(a, smem, w, sB, sA, s10, k_n1, v_n + 2 * 16 * C::ROWB, pending, wq_lo, col,
+                   half);
+    // this wave's copies of K(n+2) and V(n+1) landed; K(n+3), V(n+2) may fly
+    if (ck) wait_vmcnt<2 * C::DMA>();
+    else if (cv) wait_vmcnt<C::DMA>();
+    else wait_vmcnt<0>();
+    pipeline_barrier();
+    t0 = t1;
+    t1 = t2;
+    t2 = t3;
+    t3 = stage_next(a, t3, q_hi, b, h, D2, HD2);
+    kb0 = (kb0 + 1) & 3;
+    vb0 = vb0 == 2 ? 0 : vb0 + 1;
+  }
+  if (pending) apply_rescale(w);
+
+  // ---- epilogue: o = u / l, lse = m + ln l ([RA] §3.2; [SPD] §四) ----
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const float l_tot = pair_sum(w.l_run[cb]);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const int r = wrow0 + 32 * cb + col;
+    if (r >= a.Sq) continue;
+    const long long ro = ((long long)b * a.Sq + r) * HD + (long long)h * D;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * half;
+        const float x0 = w.oacc[cb][dt][4 * g + 0] * inv, x1 = w.oacc[cb][dt][4 * g + 1] * inv;
+        const float x2 = w.oacc[cb][dt][4 * g + 2] * inv, x3 = w.oacc[cb][dt][4 * g + 3] * inv;
+        if (a.o_fp32) {
+          *(float4*)((float*)a.o + ro + d) = float4{x0, x1, x2, x3};
+        } else {
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          bf16x4 y;
+          y[0] = (__bf16)x0; y[1] = (__bf16)x1; y[2] = (__bf16)x2; y[3] = (__bf16)x3;
+          *(bf16x4*)((__bf16*)a.o + ro + d) = y;
+        }
+      }
+    if (half == 0) {
+      const long long so = ((long long)b * a.Sq + r) * a.H + h;
+      const bool seen = l_tot > 0.0f;
+      if (a.lse) a.lse[so] = seen ? (w.m_ref[cb] + fast_log2(l_tot)) * kLn2 : -INFINITY;
+      if (a.m_out) a.m_out[so] = seen ? w.m_true[cb] * kLn2 : -INFINITY;
+      if (a.l_out) a.l_out[so] = seen ? l_tot * fast_exp2(w.m_ref[cb] - w.m_true[cb]) : 0.0f;
     }
   }
 }
@@ -788,16 +1398,26 @@ void ring_attn_f32(const AttnArgs a) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-// Kernel choice for bf16: the 256-row ping-pong kernel halves K/V traffic
-// per FLOP; the 128-row kernel runs two workgroups per CU.
+// Kernel choice for bf16 (RA_OPT_ATTN_KERNEL): 4 or 8 waves of 32 rows
+// (two waves per SIMD), or 4 waves of 64 rows (one wave per SIMD).
+enum Bf16Kernel { K_BR128, K_BR256, K_W64 };
 
-int bf16_waves(const AttnArgs& a) {
+// The 64-row kernel keeps positions in 32 bits: usable when every query
+// and key position (plus a tile of slack) stays below 2^31.
+bool positions_fit_32(const AttnArgs& a) {
+  const long long lim = 0x7fffffffLL - 256;
+  if (a.q_pos0 + a.Sq > lim) return false;
+  for (int i = 0; i < a.nblk; ++i)
+    if (a.blk[i].k_pos0 + a.blk[i].len > lim) return false;
+  return true;
+}
+
+Bf16Kernel bf16_kernel(const AttnArgs& a) {
   const int mode = ra::option(RA_OPT_ATTN_KERNEL);
-  if (mode == RA_KERNEL_BR128) return 4;
-  if (mode == RA_KERNEL_BR256) return 8;
-  // AUTO: the 128-row kernel measured faster on every shape tried (the
-  // 256-row one halves the K/V re-reads but keeps its eight waves in step)
-  return 4;
+  if (mode == RA_KERNEL_BR128) return K_BR128;
+  if (mode == RA_KERNEL_BR256) return K_BR256;
+  if (mode == RA_KERNEL_W64) return positions_fit_32(a) ? K_W64 : K_BR128;
+  return K_BR128;
 }
 
 template <int NW>
@@ -807,8 +1427,8 @@ void launch_bf16(const AttnArgs& a, int D, dim3 grid, hipStream_t stream) {
 }
 
 ra_status launch(AttnArgs& a, int D, ra_dtype dt, hipStream_t stream, const char* name) {
-  const int nw = dt == RA_BF16 ? bf16_waves(a) : kWaves;
-  const int br = 32 * nw;
+  const Bf16Kernel kk = dt == RA_BF16 ? bf16_kernel(a) : K_BR128;
+  const int br = dt != RA_BF16 ? kBR : kk == K_W64 ? 256 : kk == K_BR256 ? 256 : 128;
   a.n_qtiles = (a.Sq + br - 1) / br;
   const long long n_wg = (long long)a.B * a.H * a.n_qtiles;
   if (n_wg == 0) return RA_OK;
@@ -816,8 +1436,14 @@ ra_status launch(AttnArgs& a, int D, ra_dtype dt, hipStream_t stream, const char
     return ra::fail(RA_ERR_UNSUPPORTED, "%s: too many query tiles", name);
   const dim3 grid((unsigned)n_wg);
   if (dt == RA_BF16) {
-    if (nw == 8) launch_bf16<8>(a, D, grid, stream);
-    else launch_bf16<4>(a, D, grid, stream);
+    if (kk == K_W64) {
+      if (D == 128) hipLaunchKernelGGL(ring_attn_bf16_w64<128>, grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL(ring_attn_bf16_w64<64>, grid, dim3(256), 0, stream, a);
+    } else if (kk == K_BR256) {
+      launch_bf16<8>(a, D, grid, stream);
+    } else {
+      launch_bf16<4>(a, D, grid, stream);
+    }
   } else {
     if (D == 128) hipLaunchKernelGGL(ring_attn_f32<128>, grid, dim3(kThreads), 0, stream, a);
     else hipLaunchKernelGGL(ring_attn_f32<64>, grid, dim3(kThreads), 0, stream, a);

@@ -46,11 +46,12 @@ def gpu():
     torch.cuda.synchronize()
 
 
-@pytest.fixture(params=["br128", "br256"])
+@pytest.fixture(params=["br128", "br256", "w64"])
 def variant(request):
-    """Run a bf16 test with each attention kernel forced (both compute the
-    same function; AUTO picks by grid size)."""
-    choice = {"br128": ra.RA_KERNEL_BR128, "br256": ra.RA_KERNEL_BR256}[request.param]
+    """Run a bf16 test with each attention kernel forced (all compute the
+    same function with different tilings)."""
+    choice = {"br128": ra.RA_KERNEL_BR128, "br256": ra.RA_KERNEL_BR256,
+              "w64": ra.RA_KERNEL_W64}[request.param]
     ra.set_attn_kernel(choice)
     yield request.param
     ra.set_attn_kernel(ra.RA_KERNEL_AUTO)
