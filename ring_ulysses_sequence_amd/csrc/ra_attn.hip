@@ -693,6 +693,8 @@ struct W64Cfg {
   static constexpr int DMA = TILE / 1024 / NW;    // 1 KiB copies per wave per stage
   static constexpr int NC = D / 16;               // k-steps of S^T
   static constexpr int NDT = D / 32;              // 32-row d tiles of O^T
+  static constexpr int KPF = 4;                   // K fragment lead (fragments)
+  static constexpr int VPF = 3;                   // V fragment lead (fragments)
 };
 
 // A 64-key stage of the visited sequence with everything the loop needs
@@ -756,6 +758,36 @@ __device__ __forceinline__ void copy_stage(const char* src, int rows, int HD2, c
   for (int i = 0; i < C::DMA; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(size_t)(dst + i * 1024), 16,
                                              voff[i], 0, 0, 0);
+}
+
+// A stage copy to be issued during a sub-step, one 1 KiB instruction at a
+// time between matrix ops, so that the wave's vector-memory issue hides
+// under them (issued back to back, the copies stall a wave that has no
+// other to cover for it).
+struct StageCopy {
+  __amdgpu_buffer_rsrc_t rs;
+  const int* voff;
+  unsigned dst;    // this wave's first 1 KiB slot
+  bool on;
+};
+
+template <int D>
+__device__ __forceinline__ StageCopy stage_copy(const char* src, int rows, int HD2,
+                                                const int* voff, unsigned dst, bool on) {
+  using C = W64Cfg<D>;
+  StageCopy c;
+  const int nrec = (min(rows, C::BC) - 1) * HD2 + D * 2;
+  c.rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, nrec, kRsrcWord3);
+  c.voff = voff;
+  c.dst = dst;
+  c.on = on;
+  return c;
+}
+
+__device__ __forceinline__ void stage_copy_part(const StageCopy& c, int i) {
+  if (c.on)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, (lds_void_ptr)(size_t)(c.dst + i * 1024), 16,
+                                             c.voff[i], 0, 0, 0);
 }
 
 // One 32-key sub-tile as this wave sees it.
@@ -927,26 +959,40 @@ __device__ __forceinline__ void scores_sub(char* smem, int kofs, const W64State<
 // past a block's end), so 0 * V stays 0; the K rows of a dead nxt may be
 // stale, but are always rows of a copied stage, and the mask replaces every
 // score they produce.
+//
+// Operand reads run ahead across phase boundaries: the first K fragments of
+// a sub-step are read (into kf) during the previous sub-step's last matrix
+// ops, the first V fragments of phase C during phase B's last ones.
 template <int D>
 __device__ __forceinline__ void w64_substep(const AttnArgs& a, char* smem, W64State<D>& w,
                                             f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
-                                            const Sub& nxt, int kofs, unsigned vofs,
-                                            bool& pending, int wq_lo, int col, int half) {
+                                            bf16x8 (&kf)[W64Cfg<D>::KPF + 1], const Sub& nxt,
+                                            int kofs, int kofs_next, unsigned vofs,
+                                            const StageCopy& cp, bool& pending, int wq_lo,
+                                            int col, int half) {
   using C = W64Cfg<D>;
+  constexpr int NF = 2 * C::NDT;         // V fragments (G, dt) of the sub-tile
+  constexpr int VPF = C::VPF;
   const float c_scale = a.scale_log2;
   if (pending) {  // the reference moved when cur's reference was chosen
     apply_rescale(w);
     pending = false;
   }
+  s16x8 vr[VPF + 1];
+  auto vread = [&](auto fc) {
+    constexpr int f = decltype(fc)::value;
+    constexpr int off = (f / C::NDT) * 16 * C::ROWB;
+    const unsigned base = vofs + w.vaddr[f % C::NDT];
+    const s16x4 lo = lds_read_tr16<off>(base);
+    const s16x4 hi = lds_read_tr16<off + 8 * C::ROWB>(base);
+    vr[f % (VPF + 1)] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
   // ---- phase B: S^T(nxt) alongside the weights P(cur) ----
   bf16x8 pb[2][2];
   {
     constexpr int NSTEP = 2 * C::NC;     // matrix ops (k-step c, block cb)
-    constexpr int PF = 3;                // K fragment lead (fragments)
-    bf16x8 kf[PF + 1];
+    constexpr int PF = C::KPF;
     auto kread = [&](int c) -> bf16x8 { return *(const bf16x8*)(smem + kofs + w.kaddr[c]); };
-#pragma unroll
-    for (int c = 0; c < PF; ++c) kf[c] = kread(c);
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) {
       const int c = i >> 1, cb = i & 1;
@@ -964,6 +1010,8 @@ __device__ __forceinline__ void w64_substep(const AttnArgs& a, char* smem, W64St
         pb[eb][v >> 3][v & 7] = (__bf16)e0;
         pb[eb][v >> 3][(v & 7) + 1] = (__bf16)e1;
       }
+      // the last K fragment is in registers: start phase C's V reads
+      if (i == NSTEP - 2) static_for<0, VPF>([&](auto fc) { vread(fc); });
       __builtin_amdgcn_sched_barrier(0);
     }
     // keep the weights here, under the matrix ops, rather than let the
@@ -978,19 +1026,8 @@ __device__ __forceinline__ void w64_substep(const AttnArgs& a, char* smem, W64St
   // ---- phase C: O^T += V(cur)^T P(cur)^T alongside the max of nxt (first
   // half of the ops) and the denominator of P(cur) (second half) ----
   {
-    constexpr int NF = 2 * C::NDT;       // V fragments (G, dt) of the sub-tile
     constexpr int NJ = 2 * NF;           // matrix ops (fragment, block cb)
-    constexpr int PF = 2;                // V fragment lead (fragments)
-    s16x8 vr[PF + 1];
-    auto vread = [&](auto fc) {
-      constexpr int f = decltype(fc)::value;
-      constexpr int off = (f / C::NDT) * 16 * C::ROWB;
-      const unsigned base = vofs + w.vaddr[f % C::NDT];
-      const s16x4 lo = lds_read_tr16<off>(base);
-      const s16x4 hi = lds_read_tr16<off + 8 * C::ROWB>(base);
-      vr[f % (PF + 1)] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    static_for<0, PF>([&](auto fc) { vread(fc); });
+    constexpr int PF = VPF;
     float lp[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
     float mxp[2] = {-INFINITY, -INFINITY};  // this lane's max of nxt per block
     auto pv_op = [&](auto jc) {
@@ -1011,6 +1048,7 @@ __device__ __forceinline__ void w64_substep(const AttnArgs& a, char* smem, W64St
     static_for<0, NH>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       pv_op(jc);
+      if constexpr ((j & 1) && (j >> 1) < C::DMA) stage_copy_part(cp, j >> 1);
       // 32 / NH scores of nxt into its row max (score x: block x / 16)
       static_for<0, 32 / NH / 2>([&](auto yc) {
         constexpr int x = j * 32 / NH + 2 * decltype(yc)::value;
@@ -1031,6 +1069,12 @@ __device__ __forceinline__ void w64_substep(const AttnArgs& a, char* smem, W64St
         const bf16x2 pr = {pb[eb][G2][e], pb[eb][G2][e + 1]};
         lp[eb][x & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, lp[eb][x & 1], false);
       });
+      // every V read is claimed: start the next sub-step's K reads
+      if constexpr (j == NJ - 2) {
+#pragma unroll
+        for (int c = 0; c < C::KPF; ++c)
+          kf[c] = *(const bf16x8*)(smem + kofs_next + w.kaddr[c]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
     // keep the denominator updates under the matrix ops as well
@@ -1140,15 +1184,20 @@ void ring_attn_bf16_w64(const AttnArgs a) {
     decide(w, ml, a.scale_log2);  // nothing accumulated yet: no rescale
   }
 
+  // K fragments of the first sub-step (stage 0, sub-tile 1)
+  bf16x8 kf[C::KPF + 1];
+#pragma unroll
+  for (int c = 0; c < C::KPF; ++c) kf[c] = *(const bf16x8*)(smem + C::KB + 32 * C::ROWB + w.kaddr[c]);
   int kb0 = 0, vb0 = 0;  // K / V buffer of stage n
   while (t0.blk < a.nblk) {
-    // copies of K(n+3) and V(n+2) into the buffers stage n-1 released
+    // copies of V(n+2) and K(n+3) into the buffers stage n-1 released,
+    // issued piecewise during the two sub-steps
     const bool ck = t3.blk < a.nblk, cv = t2.blk < a.nblk;
-    if (cv) {
-      const int vbuf = vb0 == 0 ? 2 : vb0 - 1;  // (n + 2) % 3
-      copy_stage<D>(t2.v, t2.rows, HD2, w.voffv, vdst0 + vbuf * C::TILE);
-    }
-    if (ck) copy_stage<D>(t3.k, t3.rows, HD2, w.voffk, kdst0 + ((kb0 + 3) & 3) * C::TILE);
+    const int vbuf = vb0 == 0 ? 2 : vb0 - 1;  // (n + 2) % 3
+    const StageCopy cpv =
+        stage_copy<D>(t2.v, t2.rows, HD2, w.voffv, vdst0 + vbuf * C::TILE, cv);
+    const StageCopy cpk =
+        stage_copy<D>(t3.k, t3.rows, HD2, w.voffk, kdst0 + ((kb0 + 3) & 3) * C::TILE, ck);
     const Sub s01 = sub_info(t0, 1, causal, valid_len, wq_lo, wq_hi, wave_live);
     const Sub s10 = sub_info(t1, 0, causal, valid_len, wq_lo, wq_hi, wave_live);
     const int k_n = C::KB + kb0 * C::TILE;
@@ -1156,15 +1205,20 @@ void ring_attn_bf16_w64(const AttnArgs a) {
     const int k_n1 = t1.blk < a.nblk ? C::KB + ((kb0 + 1) & 3) * C::TILE : k_n;
     const unsigned v_n = smem_lds + C::VB + vb0 * C::TILE;
     // sub-step 2n: S(stage n, sub 1), P V of (stage n, sub 0)
-    w64_substep<D>(a, smem, w, sA, sB, s01, k_n + 32 * C::ROWB, v_n, pending, wq_lo, col, half);
-    // sub-step 2n+1: S(stage n+1, sub 0), P V of (stage n, sub 1)
-    w64_substep<D>(a, smem, w, sB, sA, s10, k_n1, v_n + 2 * 16 * C::ROWB, pending, wq_lo, col,
-                   half);
+    w64_substep<D>(a, smem, w, sA, sB, kf, s01, k_n + 32 * C::ROWB, k_n1, v_n, cpv, pending,
+                   wq_lo, col, half);
+    // sub-step 2n+1: S(stage n+1, sub 0), P V of (stage n, sub 1); its
+    // K(n+1) stays resident across the barrier, so the next sub-step's
+    // (stage n+1, sub-tile 1) K reads may start before it
+    w64_substep<D>(a, smem, w, sB, sA, kf, s10, k_n1, k_n1 + 32 * C::ROWB,
+                   v_n + 2 * 16 * C::ROWB, cpk, pending, wq_lo, col, half);
     // this wave's copies of K(n+2) and V(n+1) landed; K(n+3), V(n+2) may fly
     if (ck) wait_vmcnt<2 * C::DMA>();
     else if (cv) wait_vmcnt<C::DMA>();
     else wait_vmcnt<0>();
-    pipeline_barrier();
+    // every LDS read of K(n) and V(n) has been consumed by a matrix op; the
+    // K(n+1) reads still in flight target a buffer no copy overwrites next
+    asm volatile("s_barrier" ::: "memory");
     t0 = t1;
     t1 = t2;
     t2 = t3;
