@@ -58,13 +58,36 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(q, k, v, rank, Sb, H, D):
+KERNEL_NAMES = {"auto": "ring_attn_bf16<128,4>", "br128": "ring_attn_bf16<128,4>",
+                "br256": "ring_attn_bf16<128,8>", "w64": "ring_attn_bf16_w64<128>"}
+ATTN_SOURCE = os.path.join(ROOT, "ring_ulysses_sequence_amd", "csrc", "ra_attn.hip")
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` on this workload, from the committed
+    rocprofv3 counter summary under profiles/ -- only if the summary was taken
+    on the attention source as it is now (its sha256 matches); else None."""
+    import glob
+    import hashlib
+    sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.txt"))):
+        for line in open(path, encoding="utf-8"):
+            if not line.startswith("traffic_per_launch:"):
+                continue
+            kv = dict(item.split("=", 1) for item in line.split(":", 1)[1].split())
+            if kv.get("kernel") == kernel and kv.get("source_sha256") == sha:
+                return int(kv["bytes"]), os.path.relpath(path, ROOT)
+    return None, None
+
+
+def cpu_baseline(q, k, v, rank, Sb, H, D, n_rows=512):
     """The fp64 oracle, as it stands, on a bounded sample of the same share:
-    128 evenly spaced query rows of rank 3, all 64 heads, each over its whole
-    visible prefix.  Returns the oracle's algorithmic TFLOP/s on it."""
+    n_rows evenly spaced query rows of rank 3, all 64 heads, each over its
+    whole visible prefix (about 15 s of host time).  Returns the oracle's
+    algorithmic TFLOP/s on it."""
     import numpy as np
     import oracle
-    rows = np.unique(np.linspace(0, Sb - 1, 128).astype(np.int64))
+    rows = np.unique(np.linspace(0, Sb - 1, n_rows).astype(np.int64))
     kq = k[:, :(rank + 1) * Sb].cpu()
     vq = v[:, :(rank + 1) * Sb].cpu()
     qr = q[:, rank * Sb:(rank + 1) * Sb].cpu()
@@ -147,6 +170,11 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
 
+    kernel = KERNEL_NAMES[args.attn_kernel]
+    traffic, traffic_src = measured_traffic(kernel)
+    # Q, the four visited K and V blocks, O (bf16) and lse (fp32)
+    algo_bytes = (q_r.numel() * 2 + 4 * 2 * kb[0].numel() * 2 + o.numel() * 2
+                  + lse.numel() * 4)
     extra = {}
     if not args.no_extra:
         extra = side_measurements(torch, ra, W, stream)
@@ -180,11 +208,15 @@ def main():
         },
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
-            "bound": "mfma", "kernel": "ring_attn_bf16<128>",
+            "bound": "mfma", "kernel": kernel,
             "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "avg_launch_ms": round(avg_launch_ms, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_unit": "bytes per launch (HBM/fabric, rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                            "copy-kernel calibrated)",
+            "traffic_source": traffic_src,
+            "algorithmic_bytes": algo_bytes,
         },
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall, 3),
