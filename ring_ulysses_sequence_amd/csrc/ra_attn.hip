@@ -988,35 +988,55 @@ __device__ __forceinline__ void w64_substep(const AttnArgs& a, char* smem, W64St
     vr[f % (VPF + 1)] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   // ---- phase B: S^T(nxt) alongside the weights P(cur) ----
+  // The weights go through three stages one matrix op apart, so that no
+  // vector instruction waits on the one just before it: pair x (scores 2x,
+  // 2x+1: block x / 8, registers 2 (x % 8), +1) is scaled and shifted
+  // (t = s * scale - m_use) at op x / PPS, exponentiated at the next op and
+  // rounded to bf16 at the one after; the last pairs finish under the first
+  // ops of phase C.
+  constexpr int NSTEP = 2 * C::NC;       // phase B matrix ops (k-step c, block cb)
+  constexpr int PPS = 16 / NSTEP;        // weight pairs per op
   bf16x8 pb[2][2];
+  float tq[3][PPS][2], eq[3][PPS][2];
+  auto w_stage = [&](auto ic) {  // the weight stages that belong to op i
+    constexpr int i = decltype(ic)::value;
+    static_for<0, PPS>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      // (each stage's results are pinned to its op: left alone, the
+      // compiler sinks the whole chain to the first use in phase C)
+      if constexpr (i >= 2 && i - 2 < NSTEP) {  // round to bf16
+        constexpr int x = (i - 2) * PPS + u, eb = x >> 3, v = 2 * (x & 7);
+        pb[eb][v >> 3][v & 7] = (__bf16)eq[(i - 2) % 3][u][0];
+        pb[eb][v >> 3][(v & 7) + 1] = (__bf16)eq[(i - 2) % 3][u][1];
+        asm volatile("" ::"v"(pb[eb][v >> 3]));
+      }
+      if constexpr (i >= 1 && i - 1 < NSTEP) {  // exponentiate
+        eq[(i - 1) % 3][u][0] = fast_exp2(tq[(i - 1) % 3][u][0]);
+        eq[(i - 1) % 3][u][1] = fast_exp2(tq[(i - 1) % 3][u][1]);
+        asm volatile("" ::"v"(eq[(i - 1) % 3][u][0]), "v"(eq[(i - 1) % 3][u][1]));
+      }
+      if constexpr (i < NSTEP) {  // scale and shift
+        constexpr int x = i * PPS + u, eb = x >> 3, v = 2 * (x & 7);
+        tq[i % 3][u][0] = fmaf(s_cur[eb][v], c_scale, -w.m_use[eb]);
+        tq[i % 3][u][1] = fmaf(s_cur[eb][v + 1], c_scale, -w.m_use[eb]);
+        asm volatile("" ::"v"(tq[i % 3][u][0]), "v"(tq[i % 3][u][1]));
+      }
+    });
+  };
   {
-    constexpr int NSTEP = 2 * C::NC;     // matrix ops (k-step c, block cb)
     constexpr int PF = C::KPF;
     auto kread = [&](int c) -> bf16x8 { return *(const bf16x8*)(smem + kofs + w.kaddr[c]); };
-#pragma unroll
-    for (int i = 0; i < NSTEP; ++i) {
-      const int c = i >> 1, cb = i & 1;
-      if (cb == 0 && c + PF < C::NC) kf[(c + PF) % (PF + 1)] = kread(c + PF);
-      if (c == 0) mfma_v_first(s_nxt[cb], kf[c % (PF + 1)], w.qf[cb][c]);
+    static_for<0, NSTEP>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int c = i >> 1, cb = i & 1;
+      if constexpr (cb == 0 && c + PF < C::NC) kf[(c + PF) % (PF + 1)] = kread(c + PF);
+      if constexpr (c == 0) mfma_v_first(s_nxt[cb], kf[c % (PF + 1)], w.qf[cb][c]);
       else mfma_v_acc(s_nxt[cb], kf[c % (PF + 1)], w.qf[cb][c]);
-      // 32 / NSTEP weights of cur per op (score x: block x / 16, register
-      // x % 16): p = 2^(s * scale - m_use), rounded to bf16
-      constexpr int PER = 32 / NSTEP;
-#pragma unroll
-      for (int x = i * PER; x < (i + 1) * PER; x += 2) {
-        const int eb = x >> 4, v = x & 15;
-        const float e0 = fast_exp2(fmaf(s_cur[eb][v], c_scale, -w.m_use[eb]));
-        const float e1 = fast_exp2(fmaf(s_cur[eb][v + 1], c_scale, -w.m_use[eb]));
-        pb[eb][v >> 3][v & 7] = (__bf16)e0;
-        pb[eb][v >> 3][(v & 7) + 1] = (__bf16)e1;
-      }
+      w_stage(ic);
       // the last K fragment is in registers: start phase C's V reads
-      if (i == NSTEP - 2) static_for<0, VPF>([&](auto fc) { vread(fc); });
+      if constexpr (i == NSTEP - 2) static_for<0, VPF>([&](auto fc) { vread(fc); });
       __builtin_amdgcn_sched_barrier(0);
-    }
-    // keep the weights here, under the matrix ops, rather than let the
-    // compiler sink them to their first use in phase C
-    asm volatile("" ::"v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[1][0]), "v"(pb[1][1]));
+    });
   }
   mfma_results_ready();
   if (nxt.mask) {  // diagonal, ragged or dead sub-tile
@@ -1048,6 +1068,10 @@ __device__ __forceinline__ void w64_substep(const AttnArgs& a, char* smem, W64St
     static_for<0, NH>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       pv_op(jc);
+      // the last weight pairs of cur: needed from op 2 NDT + 1 on
+      if constexpr (j < 2) w_stage(std::integral_constant<int, NSTEP + j>{});
+      if constexpr (j == 1)
+        asm volatile("" ::"v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[1][0]), "v"(pb[1][1]));
       if constexpr ((j & 1) && (j >> 1) < C::DMA) stage_copy_part(cp, j >> 1);
       // 32 / NH scores of nxt into its row max (score x: block x / 16)
       static_for<0, 32 / NH / 2>([&](auto yc) {
@@ -1263,6 +1287,461 @@ void ring_attn_bf16_w64(const AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 kernel, producer / consumer waves
+// ---------------------------------------------------------------------------
+// Eight waves per workgroup = four (producer, consumer) pairs, each pair
+// owning 64 query rows, the pair's two waves sharing one SIMD.  The producer
+// holds Q and computes S^T = K Q^T, the mask, the row max, the reference
+// choice and the weights P = 2^(s - m) (bf16), which it hands to its
+// consumer through LDS; the consumer holds O^T and computes O^T += V^T P^T.
+// The softmax's vector work of one wave thus runs beside the other wave's
+// matrix ops on the same SIMD, while each K or V fragment read from LDS
+// still feeds two matrix ops (64 rows), as in the 64-row kernel.
+//
+// Steps run over 32-key sub-tiles t = 0, 1, ...: at step t the producer
+// chooses the reference of t (its rescale factor into alpha slot t % 3),
+// computes P(t) (into P buffer t % 2) and S^T(t+1); the consumer applies
+// alpha(t-1) to O and adds P(t-1) V(t-1).  A barrier ends each step.
+// K and V move through LDS in 64-key stages; at step 2n the producers copy
+// K(n+2) and the consumers V(n+1), each waited for at the end of step 2n+2:
+// three K and three V stage buffers.
+template <int D>
+struct WsCfg {
+  static constexpr int NP = 4;                    // pairs
+  static constexpr int THREADS = 128 * NP;        // 8 waves
+  static constexpr int WR = 64;                   // query rows per pair
+  static constexpr int BR = NP * WR;              // query rows per workgroup
+  static constexpr int BC = 64;                   // keys per LDS stage
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILE = BC * ROWB;
+  static constexpr int NKB = 3, NVB = 3;
+  static constexpr int KB = 0, VB = NKB * TILE;
+  static constexpr int PBUF = 4 * 1024;           // one pair's P of a sub-tile
+  static constexpr int PB = VB + NVB * TILE;      // 2 x NP P buffers
+  static constexpr int ASLOT = 64 * 8;            // one pair's alpha (2 floats / lane)
+  static constexpr int AB = PB + 2 * NP * PBUF;   // 3 x NP alpha slots
+  static constexpr int LDS = AB + 3 * NP * ASLOT;
+  static constexpr int CHUNKS = D / 8;
+  static constexpr int DMA = TILE / 1024 / NP;    // 1 KiB copies per wave per stage
+  static constexpr int NC = D / 16;
+  static constexpr int NDT = D / 32;
+  static constexpr int VPF = 3;                   // V fragment lead (fragments)
+};
+static_assert(W64Cfg<128>::DMA == WsCfg<128>::DMA && W64Cfg<64>::DMA == WsCfg<64>::DMA,
+              "copy_stage is shared with the 64-row kernel");
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ s16x8 lds_read_b128_asm(unsigned addr_lds) {
+  s16x8 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr_lds));
+  return r;
+}
+__device__ __forceinline__ f32x2 lds_read_b64_asm(unsigned addr_lds) {
+  f32x2 r;
+  asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(addr_lds));
+  return r;
+}
+
+template <int D>
+struct WsProducer {
+  using C = WsCfg<D>;
+  bf16x8 qf[2][C::NC];
+  float m_ref[2], m_true[2], m_use[2], l_run[2];
+  int kaddr[C::NC];
+  int voff[C::DMA];
+};
+
+template <int D>
+struct WsConsumer {
+  using C = WsCfg<D>;
+  f32x16 oacc[2][C::NDT];
+  int vaddr[C::NDT];
+  int voff[C::DMA];
+};
+
+// Producer step t.  cur = sub-tile t (masked raw scores in s_cur), nxt =
+// t+1.  The matrix ops of S^T(nxt) (if has_nxt, from the K rows at kofs)
+// carry the vector work of cur: during the first quarter of them the row
+// max of cur and the choice of its reference ([RA] §3.2 with the lazy
+// reference; rescale factor alpha(t) into al_dst, l scaled with it), during
+// the rest the weights P(cur) = bf16(2^(s * scale - m)), handed to the
+// consumer at p_dst and summed into l.  The weights go through three stages
+// one step apart (scale and shift, exponential, bf16 and sum), so that no
+// instruction waits on the one just before it; every stage's results are
+// pinned to their op, as the compiler would otherwise sink the chain.
+template <int D>
+__device__ __forceinline__ void ws_produce(const AttnArgs& a, char* smem, WsProducer<D>& w,
+                                           const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+                                           const Sub& nxt, bool has_nxt, int kofs, char* p_dst,
+                                           char* al_dst, int wq_lo, int lane, int col,
+                                           int half) {
+  using C = WsCfg<D>;
+  constexpr int NSTEP = 2 * C::NC;    // matrix ops (k-step c, block cb)
+  constexpr int NMAX = NSTEP / 4;     // ops carrying the row max
+  constexpr int NT = 18;              // weight pipeline times (16 pairs + 2)
+  const float c_scale = a.scale_log2;
+  bf16x8 pb[2][2];
+  float lp[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+  float tq[16][2], eq[16][2];
+  float mq[2][2] = {{-INFINITY, -INFINITY}, {-INFINITY, -INFINITY}};
+  // row max: 32 scores of this lane, 32 / NMAX per op, two chains per block
+  auto max_part = [&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    static_for<0, 16 / NMAX>([&](auto yc) {
+      constexpr int x = (i * 16 / NMAX + decltype(yc)::value) * 2;  // score index, even
+      constexpr int mb = x >> 4, q = x & 15;
+      mq[mb][(q >> 1) & 1] = vmax3(mq[mb][(q >> 1) & 1], s_cur[mb][q], s_cur[mb][q + 1]);
+    });
+  };
+  auto decide_cur = [&]() {
+    float alpha[2] = {1.0f, 1.0f}, mx[2];
+    bool need[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      mx[cb] = pair_max(fmaxf(mq[cb][0], mq[cb][1])) * c_scale;
+      w.m_true[cb] = fmaxf(w.m_true[cb], mx[cb]);
+      need[cb] = mx[cb] > w.m_ref[cb] + kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(need[0] || need[1])) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        alpha[cb] = need[cb] ? fast_exp2(w.m_ref[cb] - mx[cb]) : 1.0f;
+        w.m_ref[cb] = need[cb] ? mx[cb] : w.m_ref[cb];
+        w.l_run[cb] *= alpha[cb];
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) w.m_use[cb] = w.m_ref[cb] == -INFINITY ? 0.0f : w.m_ref[cb];
+    *(f32x2*)(al_dst + lane * 8) = f32x2{alpha[0], alpha[1]};
+  };
+  // weight pipeline time k: bf16 + sum of pair k-2, exponential of pair
+  // k-1, scale and shift of pair k (pair x: block x / 8, registers 2 (x % 8), +1)
+  auto w_time = [&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k >= 2 && k - 2 < 16) {
+      constexpr int x = k - 2, eb = x >> 3, v = 2 * (x & 7);
+      pb[eb][v >> 3][v & 7] = (__bf16)eq[x][0];
+      pb[eb][v >> 3][(v & 7) + 1] = (__bf16)eq[x][1];
+      const bf16x2 pr = {pb[eb][v >> 3][v & 7], pb[eb][v >> 3][(v & 7) + 1]};
+      lp[eb][x & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, lp[eb][x & 1], false);
+      asm volatile("" ::"v"(pb[eb][v >> 3]), "v"(lp[eb][x & 1]));
+      // a complete fragment (cb, G) goes to the consumer right away, at
+      // p_dst + (2 cb + G) KiB + 16 lane, the layout it reads back
+      if constexpr ((x & 3) == 3)
+        *(bf16x8*)(p_dst + (2 * eb + (v >> 3)) * 1024 + lane * 16) = pb[eb][v >> 3];
+    }
+    if constexpr (k >= 1 && k - 1 < 16) {
+      constexpr int x = k - 1;
+      eq[x][0] = fast_exp2(tq[x][0]);
+      eq[x][1] = fast_exp2(tq[x][1]);
+      asm volatile("" ::"v"(eq[x][0]), "v"(eq[x][1]));
+    }
+    if constexpr (k < 16) {
+      constexpr int x = k, eb = x >> 3, v = 2 * (x & 7);
+      tq[x][0] = fmaf(s_cur[eb][v], c_scale, -w.m_use[eb]);
+      tq[x][1] = fmaf(s_cur[eb][v + 1], c_scale, -w.m_use[eb]);
+      asm volatile("" ::"v"(tq[x][0]), "v"(tq[x][1]));
+    }
+  };
+  // the pipeline times carried by op i (i >= NMAX)
+  auto w_part = [&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    constexpr int E = NSTEP - NMAX;
+    static_for<(i - NMAX) * NT / E, (i - NMAX + 1) * NT / E>([&](auto kc) { w_time(kc); });
+  };
+  if (has_nxt) {
+    constexpr int PF = 3;
+    bf16x8 kf[PF + 1];
+    auto kread = [&](int c) -> bf16x8 { return *(const bf16x8*)(smem + kofs + w.kaddr[c]); };
+#pragma unroll
+    for (int c = 0; c < PF; ++c) kf[c] = kread(c);
+    static_for<0, NSTEP>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int c = i >> 1, cb = i & 1;
+      if constexpr (cb == 0 && c + PF < C::NC) kf[(c + PF) % (PF + 1)] = kread(c + PF);
+      s_nxt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c % (PF + 1)], w.qf[cb][c],
+                                                          c == 0 ? f32x16{} : s_nxt[cb], 0, 0, 0);
+      if constexpr (i < NMAX) max_part(ic);
+      if constexpr (i == NMAX - 1) decide_cur();
+      if constexpr (i >= NMAX) w_part(ic);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  } else {
+    static_for<0, NMAX>([&](auto ic) { max_part(ic); });
+    decide_cur();
+    static_for<0, NT>([&](auto kc) { w_time(kc); });
+  }
+  w.l_run[0] += lp[0][0] + lp[0][1];
+  w.l_run[1] += lp[1][0] + lp[1][1];
+  if (has_nxt && nxt.mask) {
+    mask_sub(s_nxt[0], nxt, a.causal, wq_lo, 0, col, half);
+    mask_sub(s_nxt[1], nxt, a.causal, wq_lo, 1, col, half);
+  }
+}
+
+// Consumer step: O^T *= alpha (when any row's reference moved), then
+// O^T += V^T P^T with P from the LDS buffer at p_src and V rows at vofs.
+template <int D>
+__device__ __forceinline__ void ws_consume(WsConsumer<D>& w, unsigned vofs, unsigned p_src,
+                                           unsigned al_src, int lane) {
+  using C = WsCfg<D>;
+  constexpr int NF = 2 * C::NDT;
+  constexpr int NJ = 2 * NF;
+  constexpr int PF = C::VPF;
+  const f32x2 al = lds_read_b64_asm(al_src + lane * 8);
+  s16x8 pr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pr[i] = lds_read_b128_asm(p_src + i * 1024 + lane * 16);
+  s16x8 vr[PF + 1];
+  auto vread = [&](auto fc) {
+    constexpr int f = decltype(fc)::value;
+    constexpr int off = (f / C::NDT) * 16 * C::ROWB;
+    const unsigned base = vofs + w.vaddr[f % C::NDT];
+    const s16x4 lo = lds_read_tr16<off>(base);
+    const s16x4 hi = lds_read_tr16<off + 8 * C::ROWB>(base);
+    vr[f % (PF + 1)] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  static_for<0, PF>([&](auto fc) { vread(fc); });
+  f32x2 alc = al;
+  claim_lds<4 + 2 * PF>(alc);
+  if (__builtin_amdgcn_ballot_w64(alc[0] != 1.0f || alc[1] != 1.0f)) {
+#pragma unroll
+    for (int i = 0; i < C::NDT; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        w.oacc[0][i][v] *= alc[0];
+        w.oacc[1][i][v] *= alc[1];
+      }
+  }
+  claim_lds<3 + 2 * PF>(pr[0]);
+  claim_lds<2 + 2 * PF>(pr[1]);
+  claim_lds<1 + 2 * PF>(pr[2]);
+  claim_lds<2 * PF>(pr[3]);
+  bf16x8 pb[2][2];
+  __builtin_memcpy(&pb[0][0], &pr[0], 16);
+  __builtin_memcpy(&pb[0][1], &pr[1], 16);
+  __builtin_memcpy(&pb[1][0], &pr[2], 16);
+  __builtin_memcpy(&pb[1][1], &pr[3], 16);
+  static_for<0, NJ>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int f = j / 2, cb = j % 2;
+    if constexpr (cb == 0) {
+      if constexpr (f + PF < NF) vread(std::integral_constant<int, f + PF>{});
+      constexpr int later = 2 * ((f + PF < NF ? f + PF : NF - 1) - f);
+      claim_lds<later>(vr[f % (PF + 1)]);
+    }
+    bf16x8 vf;
+    __builtin_memcpy(&vf, &vr[f % (PF + 1)], 16);
+    constexpr int G = f / C::NDT, dt = f % C::NDT;
+    w.oacc[cb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[cb][G], w.oacc[cb][dt],
+                                                             0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void ring_attn_bf16_ws(const AttnArgs a) {
+  using C = WsCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const bool producer = wave < C::NP;
+  const int pair = wave & (C::NP - 1);
+
+  int b, h, qt;
+  tile_coords(a, b, h, qt);
+  const int row0 = qt * C::BR;
+  const int rows_here = min(C::BR, a.Sq - row0);
+  const long long q_hi = a.q_pos0 + row0 + rows_here - 1;
+  const int wrow0 = row0 + pair * C::WR;
+  const int wrows = min(C::WR, a.Sq - wrow0);
+  const bool wave_live = wrows > 0;
+  const int wq_lo = (int)a.q_pos0 + wrow0;
+  const int wq_hi = wq_lo + wrows - 1;
+  const int valid_len = a.valid_len > 0x7fffffffLL ? 0x7fffffff : (int)a.valid_len;
+  const bool causal = a.causal != 0;
+  const long long HD = (long long)a.H * D;
+  const int D2 = D * 2;
+  const int HD2 = a.H * D2;
+  const unsigned smem_lds = (unsigned)(size_t)(lds_void_ptr)smem;
+  // copy slots: producers copy K stages, consumers V stages
+  int voff[C::DMA];
+#pragma unroll
+  for (int i = 0; i < C::DMA; ++i) {
+    const int p = (pair * C::DMA + i) * 64 + lane;
+    const int r = p / C::CHUNKS, pc = p % C::CHUNKS;
+    voff[i] = r * HD2 + (producer ? swz_k<D>(r, pc) : swz_v<D>(r, pc)) * 16;
+  }
+  const unsigned cdst0 = smem_lds + (producer ? C::KB : C::VB) + pair * C::DMA * 1024;
+  char* const p_base = smem + C::PB + pair * C::PBUF;
+  char* const a_base = smem + C::AB + pair * C::ASLOT;
+
+  Stage c0 = stage_enter(a, 0, q_hi, b, h, D2, HD2);    // stage n
+  Stage c1 = stage_next(a, c0, q_hi, b, h, D2, HD2);    // n + 1
+  Stage c2 = stage_next(a, c1, q_hi, b, h, D2, HD2);    // n + 2
+  // prologue copies: K(0), K(1) by the producers, V(0) by the consumers
+  if (producer) {
+    if (c0.blk < a.nblk) copy_stage<D>(c0.k, c0.rows, HD2, voff, cdst0);
+    if (c1.blk < a.nblk) copy_stage<D>(c1.k, c1.rows, HD2, voff, cdst0 + C::TILE);
+  } else {
+    if (c0.blk < a.nblk) copy_stage<D>(c0.v, c0.rows, HD2, voff, cdst0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  if (producer) {
+    WsProducer<D> w;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int r = wrow0 + 32 * cb + col;
+      const __bf16* qp = (const __bf16*)a.q + ((long long)b * a.Sq + r) * HD + (long long)h * D;
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c)
+        w.qf[cb][c] = r < a.Sq ? *(const bf16x8*)(qp + 16 * c + 8 * half) : bf16x8{};
+      w.m_ref[cb] = -INFINITY;
+      w.m_true[cb] = -INFINITY;
+      w.m_use[cb] = 0.0f;
+      w.l_run[cb] = 0.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) w.kaddr[c] = col * C::ROWB + swz_k<D>(col, 2 * c + half) * 16;
+    f32x16 sA[2], sB[2];
+    if (c0.blk < a.nblk) {  // S^T of sub-tile 0, its reference
+      const Sub s0 = sub_info(c0, 0, causal, valid_len, wq_lo, wq_hi, wave_live);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) sA[cb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) {
+        const bf16x8 kf = *(const bf16x8*)(smem + C::KB + w.kaddr[c]);
+        sA[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, w.qf[0][c], sA[0], 0, 0, 0);
+        sA[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, w.qf[1][c], sA[1], 0, 0, 0);
+      }
+      if (s0.mask) {
+        mask_sub(sA[0], s0, causal, wq_lo, 0, col, half);
+        mask_sub(sA[1], s0, causal, wq_lo, 1, col, half);
+      }
+    }
+    int kb0 = 0;  // K buffer of stage n
+    for (int n = 0;; ++n) {
+      // even step 2n: P(2n), S(2n+1); copy K(n+2)
+      const bool live = c0.blk < a.nblk;
+      const bool ck = c2.blk < a.nblk;
+      if (ck) copy_stage<D>(c2.k, c2.rows, HD2, voff, cdst0 + ((kb0 + 2) % 3) * C::TILE);
+      if (live) {
+        const Sub s01 = sub_info(c0, 1, causal, valid_len, wq_lo, wq_hi, wave_live);
+        ws_produce<D>(a, smem, w, sA, sB, s01, true, C::KB + kb0 * C::TILE + 32 * C::ROWB,
+                      p_base, a_base + ((2 * n) % 3) * C::NP * C::ASLOT, wq_lo, lane, col, half);
+      }
+      if (ck) wait_vmcnt<C::DMA>();
+      else wait_vmcnt<0>();
+      pipeline_barrier();
+      if (!live) break;
+      // odd step 2n+1: P(2n+1), S(2n+2)
+      {
+        const bool has = c1.blk < a.nblk;
+        const Sub s10 = sub_info(c1, 0, causal, valid_len, wq_lo, wq_hi, wave_live);
+        ws_produce<D>(a, smem, w, sB, sA, s10, has, C::KB + ((kb0 + 1) % 3) * C::TILE,
+                      p_base + C::NP * C::PBUF, a_base + ((2 * n + 1) % 3) * C::NP * C::ASLOT,
+                      wq_lo, lane, col, half);
+      }
+      pipeline_barrier();
+      c0 = c1;
+      c1 = c2;
+      c2 = stage_next(a, c2, q_hi, b, h, D2, HD2);
+      kb0 = kb0 == 2 ? 0 : kb0 + 1;
+    }
+    // hand l to the consumer; write lse (and m, l) of the rows
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float l_tot = pair_sum(w.l_run[cb]);
+      if (half == 0) *(float*)(a_base + col * 8 + cb * 4) = l_tot;
+      const int r = wrow0 + 32 * cb + col;
+      if (half == 0 && r < a.Sq) {
+        const long long so = ((long long)b * a.Sq + r) * a.H + h;
+        const bool seen = l_tot > 0.0f;
+        if (a.lse) a.lse[so] = seen ? (w.m_ref[cb] + fast_log2(l_tot)) * kLn2 : -INFINITY;
+        if (a.m_out) a.m_out[so] = seen ? w.m_true[cb] * kLn2 : -INFINITY;
+        if (a.l_out) a.l_out[so] = seen ? l_tot * fast_exp2(w.m_ref[cb] - w.m_true[cb]) : 0.0f;
+      }
+    }
+    __syncthreads();
+  } else {
+    WsConsumer<D> w;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < C::NDT; ++i) w.oacc[cb][i] = f32x16{};
+    {
+      const int j = lane & 15, e = j >> 2, q = j & 3, g = lane >> 4;
+      const int kl = 4 * half + e;
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) {
+        const int d0 = 32 * dt + 16 * (g & 1) + 4 * q;
+        w.vaddr[dt] = kl * C::ROWB + swz_v<D>(kl, d0 >> 3) * 16 + (d0 & 7) * 2;
+      }
+    }
+    const unsigned p0 = (unsigned)(size_t)(lds_void_ptr)p_base;
+    const unsigned al0 = (unsigned)(size_t)(lds_void_ptr)a_base;
+    int vbp = 2;  // V buffer of stage n - 1
+    for (int n = 0;; ++n) {
+      // even step 2n: P(2n-1) V(2n-1); copy V(n+1)
+      const bool live = c0.blk < a.nblk;
+      const bool cv = c1.blk < a.nblk;
+      const int vb0 = vbp == 2 ? 0 : vbp + 1;
+      if (cv) copy_stage<D>(c1.v, c1.rows, HD2, voff, cdst0 + ((vb0 + 1) % 3) * C::TILE);
+      if (n > 0)
+        ws_consume<D>(w, smem_lds + C::VB + vbp * C::TILE + 32 * C::ROWB,
+                      p0 + C::NP * C::PBUF, al0 + ((2 * n - 1) % 3) * C::NP * C::ASLOT, lane);
+      if (cv) wait_vmcnt<C::DMA>();
+      else wait_vmcnt<0>();
+      pipeline_barrier();
+      if (!live) break;
+      // odd step 2n+1: P(2n) V(2n)
+      ws_consume<D>(w, smem_lds + C::VB + vb0 * C::TILE, p0,
+                    al0 + ((2 * n) % 3) * C::NP * C::ASLOT, lane);
+      pipeline_barrier();
+      c0 = c1;
+      c1 = c2;
+      c2 = stage_next(a, c2, q_hi, b, h, D2, HD2);
+      vbp = vb0;
+    }
+    __syncthreads();  // the producer's l
+    float l_tot[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) l_tot[cb] = *(const float*)(a_base + col * 8 + cb * 4);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float inv = l_tot[cb] > 0.0f ? 1.0f / l_tot[cb] : 0.0f;
+      const int r = wrow0 + 32 * cb + col;
+      if (r >= a.Sq) continue;
+      const long long ro = ((long long)b * a.Sq + r) * HD + (long long)h * D;
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * dt + 8 * g + 4 * half;
+          const float x0 = w.oacc[cb][dt][4 * g + 0] * inv, x1 = w.oacc[cb][dt][4 * g + 1] * inv;
+          const float x2 = w.oacc[cb][dt][4 * g + 2] * inv, x3 = w.oacc[cb][dt][4 * g + 3] * inv;
+          if (a.o_fp32) {
+            *(float4*)((float*)a.o + ro + d) = float4{x0, x1, x2, x3};
+          } else {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            bf16x4 y;
+            y[0] = (__bf16)x0; y[1] = (__bf16)x1; y[2] = (__bf16)x2; y[3] = (__bf16)x3;
+            *(bf16x4*)((__bf16*)a.o + ro + d) = y;
+          }
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel (no bf16 rounding anywhere; fp32 matrix-core products)
 // ---------------------------------------------------------------------------
 template <int D>
@@ -1453,8 +1932,9 @@ void ring_attn_f32(const AttnArgs a) {
 // host side
 // ---------------------------------------------------------------------------
 // Kernel choice for bf16 (RA_OPT_ATTN_KERNEL): 4 or 8 waves of 32 rows
-// (two waves per SIMD), or 4 waves of 64 rows (one wave per SIMD).
-enum Bf16Kernel { K_BR128, K_BR256, K_W64 };
+// (two waves per SIMD), 4 waves of 64 rows (one wave per SIMD), or 4
+// producer / consumer pairs of 64 rows (two waves per SIMD).
+enum Bf16Kernel { K_BR128, K_BR256, K_W64, K_WS };
 
 // The 64-row kernel keeps positions in 32 bits: usable when every query
 // and key position (plus a tile of slack) stays below 2^31.
@@ -1471,6 +1951,7 @@ Bf16Kernel bf16_kernel(const AttnArgs& a) {
   if (mode == RA_KERNEL_BR128) return K_BR128;
   if (mode == RA_KERNEL_BR256) return K_BR256;
   if (mode == RA_KERNEL_W64) return positions_fit_32(a) ? K_W64 : K_BR128;
+  if (mode == RA_KERNEL_WS) return positions_fit_32(a) ? K_WS : K_BR128;
   return K_BR128;
 }
 
@@ -1482,7 +1963,7 @@ void launch_bf16(const AttnArgs& a, int D, dim3 grid, hipStream_t stream) {
 
 ra_status launch(AttnArgs& a, int D, ra_dtype dt, hipStream_t stream, const char* name) {
   const Bf16Kernel kk = dt == RA_BF16 ? bf16_kernel(a) : K_BR128;
-  const int br = dt != RA_BF16 ? kBR : kk == K_W64 ? 256 : kk == K_BR256 ? 256 : 128;
+  const int br = dt != RA_BF16 ? kBR : kk == K_BR128 ? 128 : 256;
   a.n_qtiles = (a.Sq + br - 1) / br;
   const long long n_wg = (long long)a.B * a.H * a.n_qtiles;
   if (n_wg == 0) return RA_OK;
@@ -1493,6 +1974,9 @@ ra_status launch(AttnArgs& a, int D, ra_dtype dt, hipStream_t stream, const char
     if (kk == K_W64) {
       if (D == 128) hipLaunchKernelGGL(ring_attn_bf16_w64<128>, grid, dim3(256), 0, stream, a);
       else hipLaunchKernelGGL(ring_attn_bf16_w64<64>, grid, dim3(256), 0, stream, a);
+    } else if (kk == K_WS) {
+      if (D == 128) hipLaunchKernelGGL(ring_attn_bf16_ws<128>, grid, dim3(512), 0, stream, a);
+      else hipLaunchKernelGGL(ring_attn_bf16_ws<64>, grid, dim3(512), 0, stream, a);
     } else if (kk == K_BR256) {
       launch_bf16<8>(a, D, grid, stream);
     } else {
