@@ -1347,7 +1347,7 @@ template <int D>
 struct WsProducer {
   using C = WsCfg<D>;
   bf16x8 qf[2][C::NC];
-  float m_ref[2], m_true[2], m_use[2], l_run[2];
+  float m_ref[2], m_true[2], m_use[2];
   int kaddr[C::NC];
   int voff[C::DMA];
 };
@@ -1356,6 +1356,7 @@ template <int D>
 struct WsConsumer {
   using C = WsCfg<D>;
   f32x16 oacc[2][C::NDT];
+  float l_run[2];          // this lane's half of sum of the bf16 weights
   int vaddr[C::NDT];
   int voff[C::DMA];
 };
@@ -1364,9 +1365,9 @@ struct WsConsumer {
 // t+1.  The matrix ops of S^T(nxt) (if has_nxt, from the K rows at kofs)
 // carry the vector work of cur: during the first quarter of them the row
 // max of cur and the choice of its reference ([RA] §3.2 with the lazy
-// reference; rescale factor alpha(t) into al_dst, l scaled with it), during
-// the rest the weights P(cur) = bf16(2^(s * scale - m)), handed to the
-// consumer at p_dst and summed into l.  The weights go through three stages
+// reference; rescale factor alpha(t) into al_dst), during the rest the
+// weights P(cur) = bf16(2^(s * scale - m)), handed to the consumer at p_dst
+// (which sums them into the denominator).  The weights go through three stages
 // one step apart (scale and shift, exponential, bf16 and sum), so that no
 // instruction waits on the one just before it; every stage's results are
 // pinned to their op, as the compiler would otherwise sink the chain.
@@ -1382,7 +1383,6 @@ __device__ __forceinline__ void ws_produce(const AttnArgs& a, char* smem, WsProd
   constexpr int NT = 18;              // weight pipeline times (16 pairs + 2)
   const float c_scale = a.scale_log2;
   bf16x8 pb[2][2];
-  float lp[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
   float tq[16][2], eq[16][2];
   float mq[2][2] = {{-INFINITY, -INFINITY}, {-INFINITY, -INFINITY}};
   // row max: 32 scores of this lane, 32 / NMAX per op, two chains per block
@@ -1408,24 +1408,21 @@ __device__ __forceinline__ void ws_produce(const AttnArgs& a, char* smem, WsProd
       for (int cb = 0; cb < 2; ++cb) {
         alpha[cb] = need[cb] ? fast_exp2(w.m_ref[cb] - mx[cb]) : 1.0f;
         w.m_ref[cb] = need[cb] ? mx[cb] : w.m_ref[cb];
-        w.l_run[cb] *= alpha[cb];
       }
     }
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) w.m_use[cb] = w.m_ref[cb] == -INFINITY ? 0.0f : w.m_ref[cb];
     *(f32x2*)(al_dst + lane * 8) = f32x2{alpha[0], alpha[1]};
   };
-  // weight pipeline time k: bf16 + sum of pair k-2, exponential of pair
-  // k-1, scale and shift of pair k (pair x: block x / 8, registers 2 (x % 8), +1)
+  // weight pipeline time k: bf16 of pair k-2, exponential of pair k-1,
+  // scale and shift of pair k (pair x: block x / 8, registers 2 (x % 8), +1)
   auto w_time = [&](auto kc) {
     constexpr int k = decltype(kc)::value;
     if constexpr (k >= 2 && k - 2 < 16) {
       constexpr int x = k - 2, eb = x >> 3, v = 2 * (x & 7);
       pb[eb][v >> 3][v & 7] = (__bf16)eq[x][0];
       pb[eb][v >> 3][(v & 7) + 1] = (__bf16)eq[x][1];
-      const bf16x2 pr = {pb[eb][v >> 3][v & 7], pb[eb][v >> 3][(v & 7) + 1]};
-      lp[eb][x & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, lp[eb][x & 1], false);
-      asm volatile("" ::"v"(pb[eb][v >> 3]), "v"(lp[eb][x & 1]));
+      asm volatile("" ::"v"(pb[eb][v >> 3]));
       // a complete fragment (cb, G) goes to the consumer right away, at
       // p_dst + (2 cb + G) KiB + 16 lane, the layout it reads back
       if constexpr ((x & 3) == 3)
@@ -1472,8 +1469,6 @@ __device__ __forceinline__ void ws_produce(const AttnArgs& a, char* smem, WsProd
     decide_cur();
     static_for<0, NT>([&](auto kc) { w_time(kc); });
   }
-  w.l_run[0] += lp[0][0] + lp[0][1];
-  w.l_run[1] += lp[1][0] + lp[1][1];
   if (has_nxt && nxt.mask) {
     mask_sub(s_nxt[0], nxt, a.causal, wq_lo, 0, col, half);
     mask_sub(s_nxt[1], nxt, a.causal, wq_lo, 1, col, half);
@@ -1506,6 +1501,8 @@ __device__ __forceinline__ void ws_consume(WsConsumer<D>& w, unsigned vofs, unsi
   f32x2 alc = al;
   claim_lds<4 + 2 * PF>(alc);
   if (__builtin_amdgcn_ballot_w64(alc[0] != 1.0f || alc[1] != 1.0f)) {
+    w.l_run[0] *= alc[0];
+    w.l_run[1] *= alc[1];
 #pragma unroll
     for (int i = 0; i < C::NDT; ++i)
 #pragma unroll
@@ -1523,9 +1520,18 @@ __device__ __forceinline__ void ws_consume(WsConsumer<D>& w, unsigned vofs, unsi
   __builtin_memcpy(&pb[0][1], &pr[1], 16);
   __builtin_memcpy(&pb[1][0], &pr[2], 16);
   __builtin_memcpy(&pb[1][1], &pr[3], 16);
+  float lp[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
   static_for<0, NJ>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     constexpr int f = j / 2, cb = j % 2;
+    // the denominator of P: 16 / NJ bf16 pairs per op (pair x: block x / 8,
+    // fragment (x / 4) % 2, elements 2 (x % 4), +1)
+    static_for<j * 16 / NJ, (j + 1) * 16 / NJ>([&](auto xc) {
+      constexpr int x = decltype(xc)::value;
+      constexpr int eb = x >> 3, G2 = (x >> 2) & 1, e = 2 * (x & 3);
+      const bf16x2 pq = {pb[eb][G2][e], pb[eb][G2][e + 1]};
+      lp[eb][x & 1] = __builtin_amdgcn_fdot2_f32_bf16(pq, kOnes2, lp[eb][x & 1], false);
+    });
     if constexpr (cb == 0) {
       if constexpr (f + PF < NF) vread(std::integral_constant<int, f + PF>{});
       constexpr int later = 2 * ((f + PF < NF ? f + PF : NF - 1) - f);
@@ -1538,6 +1544,8 @@ __device__ __forceinline__ void ws_consume(WsConsumer<D>& w, unsigned vofs, unsi
                                                              0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   });
+  w.l_run[0] += lp[0][0] + lp[0][1];
+  w.l_run[1] += lp[1][0] + lp[1][1];
 }
 
 template <int D>
@@ -1607,7 +1615,6 @@ void ring_attn_bf16_ws(const AttnArgs a) {
       w.m_ref[cb] = -INFINITY;
       w.m_true[cb] = -INFINITY;
       w.m_use[cb] = 0.0f;
-      w.l_run[cb] = 0.0f;
     }
 #pragma unroll
     for (int c = 0; c < C::NC; ++c) w.kaddr[c] = col * C::ROWB + swz_k<D>(col, 2 * c + half) * 16;
@@ -1656,27 +1663,20 @@ void ring_attn_bf16_ws(const AttnArgs a) {
       c2 = stage_next(a, c2, q_hi, b, h, D2, HD2);
       kb0 = kb0 == 2 ? 0 : kb0 + 1;
     }
-    // hand l to the consumer; write lse (and m, l) of the rows
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const float l_tot = pair_sum(w.l_run[cb]);
-      if (half == 0) *(float*)(a_base + col * 8 + cb * 4) = l_tot;
-      const int r = wrow0 + 32 * cb + col;
-      if (half == 0 && r < a.Sq) {
-        const long long so = ((long long)b * a.Sq + r) * a.H + h;
-        const bool seen = l_tot > 0.0f;
-        if (a.lse) a.lse[so] = seen ? (w.m_ref[cb] + fast_log2(l_tot)) * kLn2 : -INFINITY;
-        if (a.m_out) a.m_out[so] = seen ? w.m_true[cb] * kLn2 : -INFINITY;
-        if (a.l_out) a.l_out[so] = seen ? l_tot * fast_exp2(w.m_ref[cb] - w.m_true[cb]) : 0.0f;
-      }
+    // hand the reference and the exact max of every row to the consumer
+    if (half == 0) {
+      *(f32x2*)(a_base + col * 8) = f32x2{w.m_ref[0], w.m_ref[1]};
+      *(f32x2*)(a_base + 256 + col * 8) = f32x2{w.m_true[0], w.m_true[1]};
     }
     __syncthreads();
   } else {
     WsConsumer<D> w;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
       for (int i = 0; i < C::NDT; ++i) w.oacc[cb][i] = f32x16{};
+      w.l_run[cb] = 0.0f;
+    }
     {
       const int j = lane & 15, e = j >> 2, q = j & 3, g = lane >> 4;
       const int kl = 4 * half + e;
@@ -1711,14 +1711,22 @@ void ring_attn_bf16_ws(const AttnArgs a) {
       c2 = stage_next(a, c2, q_hi, b, h, D2, HD2);
       vbp = vb0;
     }
-    __syncthreads();  // the producer's l
-    float l_tot[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) l_tot[cb] = *(const float*)(a_base + col * 8 + cb * 4);
+    __syncthreads();  // the producer's reference and max
+    const f32x2 m_ref = *(const f32x2*)(a_base + col * 8);
+    const f32x2 m_true = *(const f32x2*)(a_base + 256 + col * 8);
+    // ---- epilogue: o = u / l, lse = m + ln l ([RA] §3.2; [SPD] §四) ----
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const float inv = l_tot[cb] > 0.0f ? 1.0f / l_tot[cb] : 0.0f;
+      const float l_tot = pair_sum(w.l_run[cb]);
+      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
       const int r = wrow0 + 32 * cb + col;
+      if (half == 0 && r < a.Sq) {
+        const long long so = ((long long)b * a.Sq + r) * a.H + h;
+        const bool seen = l_tot > 0.0f;
+        if (a.lse) a.lse[so] = seen ? (m_ref[cb] + fast_log2(l_tot)) * kLn2 : -INFINITY;
+        if (a.m_out) a.m_out[so] = seen ? m_true[cb] * kLn2 : -INFINITY;
+        if (a.l_out) a.l_out[so] = seen ? l_tot * fast_exp2(m_ref[cb] - m_true[cb]) : 0.0f;
+      }
       if (r >= a.Sq) continue;
       const long long ro = ((long long)b * a.Sq + r) * HD + (long long)h * D;
 #pragma unroll
