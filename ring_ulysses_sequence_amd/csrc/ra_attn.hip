@@ -103,18 +103,33 @@ __device__ __forceinline__ int tiles_of(const AttnArgs& a, int b, long long q_hi
 
 // Workgroup -> (batch, head, query tile).  Workgroups are dispatched
 // round-robin over the 8 XCDs; the remap gives every XCD a contiguous range
-// of tiles so the workgroups resident on one XCD share the same heads' K/V in
-// that XCD's L2.  Within a head, later query tiles (more causal work) go
-// first.
+// of work, so the workgroups resident on one XCD share K/V in that XCD's L2.
+// Within the range, work goes in groups of kHeadGroup heads: the group's
+// query tiles are taken kTileRun at a time from each of its heads in turn,
+// later tiles (more causal work) first.  The workgroups resident together
+// then cover a few heads with neighbouring query tiles, which walk the same
+// K/V tiles at nearly the same time (measured: ~4 % over whole heads in
+// turn on the long-context share).  Shapes that do not divide evenly take
+// the heads one after another.
+constexpr int kHeadGroup = 4, kTileRun = 8;
+
 __device__ __forceinline__ void tile_coords(const AttnArgs& a, int& b, int& h, int& qt) {
   const int n = gridDim.x;
   int id = blockIdx.x;
   if ((n & 7) == 0) id = (id & 7) * (n >> 3) + (id >> 3);
-  qt = id % a.n_qtiles;
-  const int bh = id / a.n_qtiles;
+  const int Q = a.n_qtiles, BH = a.B * a.H;
+  int bh;
+  if (Q % kTileRun == 0 && BH % kHeadGroup == 0) {
+    const int g = id / (kHeadGroup * Q), r = id % (kHeadGroup * Q);
+    const int run = r / (kHeadGroup * kTileRun);
+    bh = g * kHeadGroup + (r / kTileRun) % kHeadGroup;
+    qt = Q - 1 - (run * kTileRun + r % kTileRun);
+  } else {
+    bh = id / Q;
+    qt = Q - 1 - id % Q;
+  }
   h = bh % a.H;
   b = bh / a.H;
-  qt = a.n_qtiles - 1 - qt;
 }
 
 // Shared per-row bookkeeping of the online softmax for one lane (one query
