@@ -53,14 +53,14 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the side measurements (Ulysses layout, DiT shard)")
-    ap.add_argument("--attn-kernel", choices=["auto", "br128", "br256", "w64", "ws"], default="auto",
-                    help="force the bf16 attention kernel (both compute the same result)")
+    ap.add_argument("--attn-kernel", choices=["auto", "br128", "br256", "w64", "ws", "pp"], default="auto",
+                    help="force the bf16 attention kernel (all compute the same result)")
     return ap.parse_args()
 
 
 KERNEL_NAMES = {"auto": "ring_attn_bf16<128,4>", "br128": "ring_attn_bf16<128,4>",
                 "br256": "ring_attn_bf16<128,8>", "w64": "ring_attn_bf16_w64<128>",
-                "ws": "ring_attn_bf16_ws<128>"}
+                "ws": "ring_attn_bf16_ws<128>", "pp": "ring_attn_bf16_pp<128>"}
 ATTN_SOURCE = os.path.join(ROOT, "ring_ulysses_sequence_amd", "csrc", "ra_attn.hip")
 
 
@@ -129,7 +129,7 @@ def main():
     ra.lib()
     ra.set_attn_kernel({"auto": ra.RA_KERNEL_AUTO, "br128": ra.RA_KERNEL_BR128,
                         "br256": ra.RA_KERNEL_BR256, "w64": ra.RA_KERNEL_W64,
-                        "ws": ra.RA_KERNEL_WS}[args.attn_kernel])
+                        "ws": ra.RA_KERNEL_WS, "pp": ra.RA_KERNEL_PP}[args.attn_kernel])
     w = W.LONG_CAUSAL
     rank, Sb, H, D, P = 3, w.block_len, w.H, w.D, w.P
     q, k, v = W.make_qkv(w, device="cuda")

@@ -78,6 +78,7 @@ typedef enum { RA_OPT_ATTN_KERNEL = 0, RA_OPT_COUNT = 1 } ra_option;
 #define RA_KERNEL_BR256 2  /* 8 waves x 32 query rows per workgroup */
 #define RA_KERNEL_W64 3    /* 4 waves x 64 query rows, one wave per SIMD */
 #define RA_KERNEL_WS 4     /* 4 producer/consumer wave pairs x 64 query rows */
+#define RA_KERNEL_PP 5     /* 8 waves x 32 query rows in two groups half a step apart */
 
 /* ---------------------------------------------------------------------
  * Host-only helpers (no GPU needed; exported for tests and schedule dumps)

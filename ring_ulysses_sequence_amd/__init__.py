@@ -33,7 +33,8 @@ RA_SKIP, RA_FULL, RA_DIAG = 0, 1, 2
 RA_MAX_P = 64
 RA_PAD_MULTIPLE = 16
 RA_OPT_ATTN_KERNEL = 0
-RA_KERNEL_AUTO, RA_KERNEL_BR128, RA_KERNEL_BR256, RA_KERNEL_W64, RA_KERNEL_WS = 0, 1, 2, 3, 4
+RA_KERNEL_AUTO, RA_KERNEL_BR128, RA_KERNEL_BR256, RA_KERNEL_W64, RA_KERNEL_WS, RA_KERNEL_PP = (
+    0, 1, 2, 3, 4, 5)
 
 # Every symbol include/ringattn.h declares.
 EXPORTED = (
@@ -109,7 +110,7 @@ def abi_version() -> int:
 
 
 def set_attn_kernel(choice: int) -> None:
-    """Force the bf16 attention kernel (RA_KERNEL_AUTO / _BR128 / _BR256 / _W64 / _WS)."""
+    """Force the bf16 attention kernel (RA_KERNEL_AUTO / _BR128 / _BR256 / _W64 / _WS / _PP)."""
     _check(_load().ra_set_option(RA_OPT_ATTN_KERNEL, choice), "set_attn_kernel")
 
 
@@ -326,4 +327,5 @@ __all__ = [
     "ring_attn_composable", "EXPORTED", "LIB_PATH", "LibraryMissing",
     "RA_BF16", "RA_FP32", "RA_SKIP", "RA_FULL", "RA_DIAG", "RA_MAX_P", "RA_PAD_MULTIPLE",
     "RA_KERNEL_AUTO", "RA_KERNEL_BR128", "RA_KERNEL_BR256", "RA_KERNEL_W64", "RA_KERNEL_WS",
+    "RA_KERNEL_PP",
 ]

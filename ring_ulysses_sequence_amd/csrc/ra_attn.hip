@@ -377,27 +377,18 @@ __device__ __forceinline__ void exp_tile(f32x16 (&s)[2], float m_use, float c_sc
   l_run += l0 + l1;
 }
 
-// One pipeline step.  PAR = n & 1: K(n+1) sits in K buffer PAR^1, V(n) in
-// V buffer PAR; the copies go to K buffer PAR and V buffer PAR^1.
+// Front half of pipeline step n: classification of tiles n and n+1, mask,
+// row max and lazy rescale of tile n, then S^T(n+1) = K(n+1) Q^T on the
+// matrix cores alongside the exponentials of tile n (P(n) into pb).  K(n+1)
+// sits in K buffer PAR^1.  Returns whether tile n is live for this wave.
 template <int D, int NW, int PAR>
-__device__ __forceinline__ void pipeline_step(
+__device__ __forceinline__ bool step_front(
     const AttnArgs& a, char* smem, WaveState<D, NW>& w, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
-    Cursor& t0, Cursor& t1, Cursor& t2, int& vb,
-    long long q_hi, long long wq_lo, long long wq_hi, int wrows, int col, int half, int b,
-    int h, int HD2, int wave) {
+    const Cursor& t0, const Cursor& t1, long long wq_lo, long long wq_hi, int wrows, int col,
+    int half, bf16x8 (&pb)[Bf16Cfg<D, NW>::NS / 8]) {
   using C = Bf16Cfg<D, NW>;
   constexpr int BC = C::BC;
   const float c_scale = a.scale_log2;
-  // copies of tile n+2: K first, so that waiting for it leaves V in flight
-  const int vb2 = vb == 0 ? 2 : vb - 1;  // (vb + 2) % 3
-  const bool copy2 = t2.blk < a.nblk;
-  if (copy2) {
-    const KVBlock& kb2 = a.blk[t2.blk];
-    copy_tile<D, NW>(kb2.k, kb2.len, t2.t, b, h, a.H, HD2, wave, w.voffk,
-                 smem + C::KB + PAR * C::TILE);
-    copy_tile<D, NW>(kb2.v, kb2.len, t2.t, b, h, a.H, HD2, wave, w.voffv,
-                 smem + C::VB + vb2 * C::TILE);
-  }
   // tile n: classification, mask, row max, lazy rescale
   const KVBlock& kb0 = a.blk[t0.blk];
   const int kt0 = t0.t * BC;
@@ -455,7 +446,6 @@ __device__ __forceinline__ void pipeline_step(
   }
   // S^T(n+1) on the matrix cores alongside the exponentials of tile n
   constexpr int kbuf_next = C::KB + (PAR ^ 1) * C::TILE;
-  bf16x8 pb[C::NS / 8];
   if (live0 && live1) {
     // Explicit interleave: step i issues the K read of step i+2, the
     // matrix-core op of step i and 16/NC exponentials (with their bf16
@@ -474,32 +464,59 @@ __device__ __forceinline__ void pipeline_step(
 #pragma unroll
     for (int i = 0; i < PF; ++i) kf[i] = kread(i);
     float lp[2] = {0.0f, 0.0f};
+    float xs[3][PER];
 #pragma unroll
-    for (int i = 0; i < NSTEP; ++i) {
-      if (i + PF < NSTEP) kf[(i + PF) % (PF + 1)] = kread(i + PF);
-      const int kt = i % 2, c = i / 2;
-      s_nxt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % (PF + 1)], w.qf[c],
-                                                          c == 0 ? f32x16{} : s_nxt[kt], 0, 0, 0);
-#pragma unroll
-      for (int j = 0; j < PER; j += 2) {
-        const int v = i * PER + j;  // score index, even
-        const float e0 = fast_exp2(fmaf(s_cur[v >> 4][v & 15], c_scale, -m_use));
-        const float e1 = fast_exp2(fmaf(s_cur[v >> 4][(v & 15) + 1], c_scale, -m_use));
-        const int G = 2 * (v >> 4) + ((v & 15) >> 3), e = v & 7;
-        pb[G][e] = (__bf16)e0;
-        pb[G][e + 1] = (__bf16)e1;
-        const bf16x2 pr = {pb[G][e], pb[G][e + 1]};
-        lp[(v >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, lp[(v >> 1) & 1], false);
+    for (int t = 0; t < NSTEP + 2; ++t) {
+      // slot t: matrix op t - 2 (slots 0, 1 run ahead of the first), shift of
+      // group t, exponential of group t - 1, bf16 copy and sum of group t - 2
+      const int i = t - 2;
+      if (i >= 0) {
+        if (i + PF < NSTEP) kf[(i + PF) % (PF + 1)] = kread(i + PF);
+        const int kt = i % 2, c = i / 2;
+        s_nxt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % (PF + 1)], w.qf[c],
+                                                            c == 0 ? f32x16{} : s_nxt[kt], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      if (t < NSTEP) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int v = t * PER + j;
+          xs[t % 3][j] = fmaf(s_cur[v >> 4][v & 15], c_scale, -m_use);
+        }
+      }
+      if (t >= 1 && t - 1 < NSTEP) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) xs[(t - 1) % 3][j] = fast_exp2(xs[(t - 1) % 3][j]);
+      }
+      if (i >= 0) {
+#pragma unroll
+        for (int j = 0; j < PER; j += 2) {
+          const int v = i * PER + j;
+          const int G = 2 * (v >> 4) + ((v & 15) >> 3), e = v & 7;
+          pb[G][e] = (__bf16)xs[i % 3][j];
+          pb[G][e + 1] = (__bf16)xs[i % 3][j + 1];
+          const bf16x2 pr = {pb[G][e], pb[G][e + 1]};
+          lp[(v >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, lp[(v >> 1) & 1], false);
+        }
+      }
+      if (i >= 0) __builtin_amdgcn_sched_barrier(0);
     }
     w.l_run += lp[0] + lp[1];
   } else {
     if (live1) scores_tile<D, NW>(smem, kbuf_next, w, s_nxt);
     if (live0) exp_tile(s_cur, m_use, c_scale, pb, w.l_run);
   }
+  return live0;
+}
+
+// Back half of pipeline step n: O^T += V(n)^T P(n)^T from V buffer vb.
+template <int D, int NW>
+__device__ __forceinline__ void step_back(char* smem, WaveState<D, NW>& w,
+                                          const bf16x8 (&pb)[Bf16Cfg<D, NW>::NS / 8], int vb,
+                                          bool live0) {
+  using C = Bf16Cfg<D, NW>;
+  constexpr int BC = C::BC;
   // O^T += V(n)^T P(n)^T: fragment j = (G = j / NDT, dt = j % NDT) is read
-  // two ops ahead, and consecutive ops accumulate into different d tiles
+  // PF ops ahead, and consecutive ops accumulate into different d tiles
   if (live0) {
     constexpr int NJ = (BC / 16) * C::NDT;
     constexpr int PF = NJ >= 8 ? 4 : 2;
@@ -535,6 +552,31 @@ __device__ __forceinline__ void pipeline_step(
     });
     __builtin_amdgcn_s_setprio(0);
   }
+}
+
+// One pipeline step.  PAR = n & 1: K(n+1) sits in K buffer PAR^1, V(n) in
+// V buffer PAR; the copies go to K buffer PAR and V buffer PAR^1.
+template <int D, int NW, int PAR>
+__device__ __forceinline__ void pipeline_step(
+    const AttnArgs& a, char* smem, WaveState<D, NW>& w, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+    Cursor& t0, Cursor& t1, Cursor& t2, int& vb,
+    long long q_hi, long long wq_lo, long long wq_hi, int wrows, int col, int half, int b,
+    int h, int HD2, int wave) {
+  using C = Bf16Cfg<D, NW>;
+  // copies of tile n+2: K first, so that waiting for it leaves V in flight
+  const int vb2 = vb == 0 ? 2 : vb - 1;  // (vb + 2) % 3
+  const bool copy2 = t2.blk < a.nblk;
+  if (copy2) {
+    const KVBlock& kb2 = a.blk[t2.blk];
+    copy_tile<D, NW>(kb2.k, kb2.len, t2.t, b, h, a.H, HD2, wave, w.voffk,
+                 smem + C::KB + PAR * C::TILE);
+    copy_tile<D, NW>(kb2.v, kb2.len, t2.t, b, h, a.H, HD2, wave, w.voffv,
+                 smem + C::VB + vb2 * C::TILE);
+  }
+  bf16x8 pb[C::NS / 8];
+  const bool live0 = step_front<D, NW, PAR>(a, smem, w, s_cur, s_nxt, t0, t1, wq_lo, wq_hi,
+                                            wrows, col, half, pb);
+  step_back<D, NW>(smem, w, pb, vb, live0);
   // this wave's K(n+2) copy (and everything older) landed; V(n+2) may fly
   if (copy2) wait_vmcnt<C::DMA>();
   else wait_vmcnt<0>();
@@ -545,11 +587,54 @@ __device__ __forceinline__ void pipeline_step(
   vb = vb == 2 ? 0 : vb + 1;
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void ring_attn_bf16(const AttnArgs a) {
+// One step of the ping-pong form (8 waves, 256 query rows).  Group 0 (waves
+// 0-3) copies the K tiles and runs one half step ahead of group 1 (waves
+// 4-7), which copies the V tiles: between two barriers, the wave of one
+// group computes a front half (scores and exponentials, vector heavy) while
+// its partner wave on the same SIMD computes a back half (P V, matrix bound).
+// Buffer lifetimes: K(n+2) goes into K(n)'s buffer, issued by group 0 after
+// group 1's last read of K(n) (its front half n-1); V(n+2) goes into
+// V(n-1)'s buffer, issued by group 1 after its own back half n-1.  Group 0
+// waits for its K(n+2) before the barrier that closes its back half n;
+// group 1 waits for V(n+1) before the barrier that closes its back half n.
+template <int D, int PAR>
+__device__ __forceinline__ void pp_step(
+    const AttnArgs& a, char* smem, WaveState<D, 8>& w, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+    Cursor& t0, Cursor& t1, Cursor& t2, int& vb, long long q_hi, long long wq_lo,
+    long long wq_hi, int wrows, int col, int half, int b, int h, int HD2, int gw, int grp,
+    const int* voffg) {
+  using C = Bf16Cfg<D, 8>;
+  const int vb2 = vb == 0 ? 2 : vb - 1;  // (vb + 2) % 3
+  const bool copy2 = t2.blk < a.nblk;
+  if (copy2) {
+    const KVBlock& kb2 = a.blk[t2.blk];
+    if (grp == 0)
+      copy_tile<D, 4>(kb2.k, kb2.len, t2.t, b, h, a.H, HD2, gw, voffg,
+                      smem + C::KB + PAR * C::TILE);
+    else
+      copy_tile<D, 4>(kb2.v, kb2.len, t2.t, b, h, a.H, HD2, gw, voffg,
+                      smem + C::VB + vb2 * C::TILE);
+  }
+  bf16x8 pb[C::NS / 8];
+  const bool live0 = step_front<D, 8, PAR>(a, smem, w, s_cur, s_nxt, t0, t1, wq_lo, wq_hi,
+                                           wrows, col, half, pb);
+  pipeline_barrier();
+  step_back<D, 8>(smem, w, pb, vb, live0);
+  if (grp == 0 || !copy2) wait_vmcnt<0>();
+  else wait_vmcnt<Bf16Cfg<D, 4>::DMA>();
+  pipeline_barrier();
+  t0 = t1;
+  t1 = t2;
+  t2 = cursor_next(a, q_hi, t2);
+  vb = vb == 2 ? 0 : vb + 1;
+}
+
+// Kernel body shared by the 32-row-per-wave kernels; PP selects the
+// ping-pong form (NW = 8 only).
+template <int D, int NW, bool PP>
+__device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   using C = Bf16Cfg<D, NW>;
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+  static_assert(!PP || NW == 8, "the ping-pong form pairs waves w and w+4 on one SIMD");
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -602,20 +687,48 @@ void ring_attn_bf16(const AttnArgs a) {
   w.m_true = -INFINITY;
   w.l_run = 0.0f;
 
+  // ping-pong form: group 0 (waves 0-3) copies K, group 1 copies V; gw is
+  // the wave's index in its group and voffg its copy offsets
+  const int grp = wave >> 2, gw = wave & 3;
+  int voffg[PP ? Bf16Cfg<D, 4>::DMA : 1];
+  if constexpr (PP) {
+#pragma unroll
+    for (int i = 0; i < Bf16Cfg<D, 4>::DMA; ++i) {
+      const int p = (gw * Bf16Cfg<D, 4>::DMA + i) * 64 + lane;
+      const int r = p / C::CHUNKS, pc = p % C::CHUNKS;
+      voffg[i] = r * HD2 + (grp == 0 ? swz_k<D>(r, pc) : swz_v<D>(r, pc)) * 16;
+    }
+  }
+
   // prologue: K(0), V(0), K(1) into K0, V0, K1; scores of tile 0
   Cursor t0 = cursor_first(a, q_hi);
   Cursor t1 = cursor_next(a, q_hi, t0);
   Cursor t2 = cursor_next(a, q_hi, t1);
   f32x16 sA[2], sB[2];
-  if (t0.blk < a.nblk) {
-    const KVBlock& kb = a.blk[t0.blk];
-    copy_tile<D, NW>(kb.k, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffk, smem + C::KB);
-    copy_tile<D, NW>(kb.v, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffv, smem + C::VB);
-  }
-  if (t1.blk < a.nblk) {
-    const KVBlock& kb = a.blk[t1.blk];
-    copy_tile<D, NW>(kb.k, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffk, smem + C::KB + C::TILE);
-    copy_tile<D, NW>(kb.v, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffv, smem + C::VB + C::TILE);
+  if constexpr (PP) {
+    if (t0.blk < a.nblk) {
+      const KVBlock& kb = a.blk[t0.blk];
+      copy_tile<D, 4>(grp == 0 ? kb.k : kb.v, kb.len, t0.t, b, h, a.H, HD2, gw, voffg,
+                      smem + (grp == 0 ? C::KB : C::VB));
+    }
+    if (t1.blk < a.nblk) {
+      const KVBlock& kb = a.blk[t1.blk];
+      copy_tile<D, 4>(grp == 0 ? kb.k : kb.v, kb.len, t1.t, b, h, a.H, HD2, gw, voffg,
+                      smem + (grp == 0 ? C::KB : C::VB) + C::TILE);
+    }
+  } else {
+    if (t0.blk < a.nblk) {
+      const KVBlock& kb = a.blk[t0.blk];
+      copy_tile<D, NW>(kb.k, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffk, smem + C::KB);
+      copy_tile<D, NW>(kb.v, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffv, smem + C::VB);
+    }
+    if (t1.blk < a.nblk) {
+      const KVBlock& kb = a.blk[t1.blk];
+      copy_tile<D, NW>(kb.k, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffk,
+                       smem + C::KB + C::TILE);
+      copy_tile<D, NW>(kb.v, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffv,
+                       smem + C::VB + C::TILE);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -626,12 +739,27 @@ void ring_attn_bf16(const AttnArgs a) {
   __syncthreads();  // K buffer 0 is free for K(2)
 
   int vb = 0;  // V buffer of tile n
-  while (t0.blk < a.nblk) {
-    pipeline_step<D, NW, 0>(a, smem, w, sA, sB, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows, col,
-                        half, b, h, HD2, wave);
-    if (t0.blk >= a.nblk) break;
-    pipeline_step<D, NW, 1>(a, smem, w, sB, sA, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows, col,
-                        half, b, h, HD2, wave);
+  if constexpr (PP) {
+    // group 1 starts one half step behind: its first barrier is group 0's
+    // after front half 0; group 0 closes with the barrier of group 1's last
+    // back half, so both groups pass the same number of barriers
+    if (grp == 1) pipeline_barrier();
+    while (t0.blk < a.nblk) {
+      pp_step<D, 0>(a, smem, w, sA, sB, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows, col, half, b,
+                    h, HD2, gw, grp, voffg);
+      if (t0.blk >= a.nblk) break;
+      pp_step<D, 1>(a, smem, w, sB, sA, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows, col, half, b,
+                    h, HD2, gw, grp, voffg);
+    }
+    if (grp == 0) pipeline_barrier();
+  } else {
+    while (t0.blk < a.nblk) {
+      pipeline_step<D, NW, 0>(a, smem, w, sA, sB, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows,
+                              col, half, b, h, HD2, wave);
+      if (t0.blk >= a.nblk) break;
+      pipeline_step<D, NW, 1>(a, smem, w, sB, sA, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows,
+                              col, half, b, h, HD2, wave);
+    }
   }
 
   // ---- epilogue: o = u / l, lse = m + ln l ([RA] §3.2; [SPD] §四) ----
@@ -664,6 +792,21 @@ void ring_attn_bf16(const AttnArgs a) {
       if (a.l_out) a.l_out[so] = seen ? l_tot * fast_exp2(w.m_ref - w.m_true) : 0.0f;
     }
   }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void ring_attn_bf16(const AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[Bf16Cfg<D, NW>::LDS];
+  attn_bf16_body<D, NW, false>(a, smem);
+}
+
+// Ping-pong form: 8 waves x 32 query rows, one workgroup per CU.
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void ring_attn_bf16_pp(const AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[Bf16Cfg<D, 8>::LDS];
+  attn_bf16_body<D, 8, true>(a, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1955,9 +2098,10 @@ void ring_attn_f32(const AttnArgs a) {
 // host side
 // ---------------------------------------------------------------------------
 // Kernel choice for bf16 (RA_OPT_ATTN_KERNEL): 4 or 8 waves of 32 rows
-// (two waves per SIMD), 4 waves of 64 rows (one wave per SIMD), or 4
-// producer / consumer pairs of 64 rows (two waves per SIMD).
-enum Bf16Kernel { K_BR128, K_BR256, K_W64, K_WS };
+// (two waves per SIMD), 4 waves of 64 rows (one wave per SIMD), 4
+// producer / consumer pairs of 64 rows (two waves per SIMD), or the
+// ping-pong form of 8 waves of 32 rows.
+enum Bf16Kernel { K_BR128, K_BR256, K_W64, K_WS, K_PP };
 
 // The 64-row kernel keeps positions in 32 bits: usable when every query
 // and key position (plus a tile of slack) stays below 2^31.
@@ -1975,6 +2119,7 @@ Bf16Kernel bf16_kernel(const AttnArgs& a) {
   if (mode == RA_KERNEL_BR256) return K_BR256;
   if (mode == RA_KERNEL_W64) return positions_fit_32(a) ? K_W64 : K_BR128;
   if (mode == RA_KERNEL_WS) return positions_fit_32(a) ? K_WS : K_BR128;
+  if (mode == RA_KERNEL_PP) return K_PP;
   return K_BR128;
 }
 
@@ -2000,6 +2145,9 @@ ra_status launch(AttnArgs& a, int D, ra_dtype dt, hipStream_t stream, const char
     } else if (kk == K_WS) {
       if (D == 128) hipLaunchKernelGGL(ring_attn_bf16_ws<128>, grid, dim3(512), 0, stream, a);
       else hipLaunchKernelGGL(ring_attn_bf16_ws<64>, grid, dim3(512), 0, stream, a);
+    } else if (kk == K_PP) {
+      if (D == 128) hipLaunchKernelGGL(ring_attn_bf16_pp<128>, grid, dim3(512), 0, stream, a);
+      else hipLaunchKernelGGL(ring_attn_bf16_pp<64>, grid, dim3(512), 0, stream, a);
     } else if (kk == K_BR256) {
       launch_bf16<8>(a, D, grid, stream);
     } else {

@@ -56,7 +56,7 @@ ra_status ra_set_option(int opt, int value) {
   ra::clear_error();
   if (opt == RA_OPT_ATTN_KERNEL) {
     if (value != RA_KERNEL_AUTO && value != RA_KERNEL_BR128 && value != RA_KERNEL_BR256 &&
-        value != RA_KERNEL_W64 && value != RA_KERNEL_WS)
+        value != RA_KERNEL_W64 && value != RA_KERNEL_WS && value != RA_KERNEL_PP)
       return ra::fail(RA_ERR_RANGE, "ra_set_option: unknown kernel choice %d", value);
     ra::g_options[opt].store(value, std::memory_order_relaxed);
     return RA_OK;

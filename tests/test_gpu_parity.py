@@ -46,12 +46,13 @@ def gpu():
     torch.cuda.synchronize()
 
 
-@pytest.fixture(params=["br128", "br256", "w64", "ws"])
+@pytest.fixture(params=["br128", "br256", "w64", "ws", "pp"])
 def variant(request):
     """Run a bf16 test with each attention kernel forced (all compute the
     same function with different tilings)."""
     choice = {"br128": ra.RA_KERNEL_BR128, "br256": ra.RA_KERNEL_BR256,
-              "w64": ra.RA_KERNEL_W64, "ws": ra.RA_KERNEL_WS}[request.param]
+              "w64": ra.RA_KERNEL_W64, "ws": ra.RA_KERNEL_WS,
+              "pp": ra.RA_KERNEL_PP}[request.param]
     ra.set_attn_kernel(choice)
     yield request.param
     ra.set_attn_kernel(ra.RA_KERNEL_AUTO)

@@ -47,6 +47,7 @@ def test_abi_version(lib):
 def test_kernel_option(lib):
     assert ra.get_attn_kernel() == ra.RA_KERNEL_AUTO
     for c in (ra.RA_KERNEL_BR128, ra.RA_KERNEL_BR256, ra.RA_KERNEL_W64, ra.RA_KERNEL_WS,
+              ra.RA_KERNEL_PP,
               ra.RA_KERNEL_AUTO):
         ra.set_attn_kernel(c)
         assert ra.get_attn_kernel() == c
