@@ -587,54 +587,53 @@ __device__ __forceinline__ void pipeline_step(
   vb = vb == 2 ? 0 : vb + 1;
 }
 
-// One step of the ping-pong form (8 waves, 256 query rows).  Group 0 (waves
-// 0-3) copies the K tiles and runs one half step ahead of group 1 (waves
-// 4-7), which copies the V tiles: between two barriers, the wave of one
-// group computes a front half (scores and exponentials, vector heavy) while
-// its partner wave on the same SIMD computes a back half (P V, matrix bound).
-// Buffer lifetimes: K(n+2) goes into K(n)'s buffer, issued by group 0 after
-// group 1's last read of K(n) (its front half n-1); V(n+2) goes into
-// V(n-1)'s buffer, issued by group 1 after its own back half n-1.  Group 0
-// waits for its K(n+2) before the barrier that closes its back half n;
-// group 1 waits for V(n+1) before the barrier that closes its back half n.
+// One step of the staggered form (8 waves, 256 query rows, one barrier per
+// step).  Both groups run front(n) then back(n), but group 0 (waves 0-3)
+// passes its barrier after back(n) and group 1 (waves 4-7) after front(n).
+// Between two barriers the group-0 wave thus computes front(n), back(n)
+// while its partner on the same SIMD computes back(n-1), front(n): one is
+// in its vector-heavy half while the other is in its matrix-bound half.
+// Group 0 copies whole tiles: K(n+2) into K(n)'s buffer and V(n+2) into
+// V(n-2)'s (four V buffers, as group 1 reads V(n-1) during step n), and
+// waits for its K(n+2) before its barrier.
 template <int D, int PAR>
 __device__ __forceinline__ void pp_step(
     const AttnArgs& a, char* smem, WaveState<D, 8>& w, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
     Cursor& t0, Cursor& t1, Cursor& t2, int& vb, long long q_hi, long long wq_lo,
     long long wq_hi, int wrows, int col, int half, int b, int h, int HD2, int gw, int grp,
-    const int* voffg) {
+    const int* voffk4, const int* voffv4) {
   using C = Bf16Cfg<D, 8>;
-  const int vb2 = vb == 0 ? 2 : vb - 1;  // (vb + 2) % 3
-  const bool copy2 = t2.blk < a.nblk;
+  const bool copy2 = grp == 0 && t2.blk < a.nblk;
   if (copy2) {
     const KVBlock& kb2 = a.blk[t2.blk];
-    if (grp == 0)
-      copy_tile<D, 4>(kb2.k, kb2.len, t2.t, b, h, a.H, HD2, gw, voffg,
-                      smem + C::KB + PAR * C::TILE);
-    else
-      copy_tile<D, 4>(kb2.v, kb2.len, t2.t, b, h, a.H, HD2, gw, voffg,
-                      smem + C::VB + vb2 * C::TILE);
+    copy_tile<D, 4>(kb2.k, kb2.len, t2.t, b, h, a.H, HD2, gw, voffk4,
+                    smem + C::KB + PAR * C::TILE);
+    copy_tile<D, 4>(kb2.v, kb2.len, t2.t, b, h, a.H, HD2, gw, voffv4,
+                    smem + C::VB + ((vb + 2) & 3) * C::TILE);
   }
   bf16x8 pb[C::NS / 8];
   const bool live0 = step_front<D, 8, PAR>(a, smem, w, s_cur, s_nxt, t0, t1, wq_lo, wq_hi,
                                            wrows, col, half, pb);
-  pipeline_barrier();
+  if (grp == 1) pipeline_barrier();
   step_back<D, 8>(smem, w, pb, vb, live0);
-  if (grp == 0 || !copy2) wait_vmcnt<0>();
-  else wait_vmcnt<Bf16Cfg<D, 4>::DMA>();
-  pipeline_barrier();
+  if (grp == 0) {
+    // this wave's K(n+2) copy (and everything older) landed; V(n+2) may fly
+    if (copy2) wait_vmcnt<Bf16Cfg<D, 4>::DMA>();
+    else wait_vmcnt<0>();
+    pipeline_barrier();
+  }
   t0 = t1;
   t1 = t2;
   t2 = cursor_next(a, q_hi, t2);
-  vb = vb == 2 ? 0 : vb + 1;
+  vb = (vb + 1) & 3;
 }
 
 // Kernel body shared by the 32-row-per-wave kernels; PP selects the
-// ping-pong form (NW = 8 only).
+// staggered form (NW = 8 only).
 template <int D, int NW, bool PP>
 __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   using C = Bf16Cfg<D, NW>;
-  static_assert(!PP || NW == 8, "the ping-pong form pairs waves w and w+4 on one SIMD");
+  static_assert(!PP || NW == 8, "the staggered form pairs waves w and w+4 on one SIMD");
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -687,16 +686,17 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   w.m_true = -INFINITY;
   w.l_run = 0.0f;
 
-  // ping-pong form: group 0 (waves 0-3) copies K, group 1 copies V; gw is
-  // the wave's index in its group and voffg its copy offsets
+  // staggered form: group of the wave, its index in the group and, for
+  // group 0, the copy offsets of whole tiles over four waves
   const int grp = wave >> 2, gw = wave & 3;
-  int voffg[PP ? Bf16Cfg<D, 4>::DMA : 1];
+  int voffk4[PP ? Bf16Cfg<D, 4>::DMA : 1], voffv4[PP ? Bf16Cfg<D, 4>::DMA : 1];
   if constexpr (PP) {
 #pragma unroll
     for (int i = 0; i < Bf16Cfg<D, 4>::DMA; ++i) {
       const int p = (gw * Bf16Cfg<D, 4>::DMA + i) * 64 + lane;
       const int r = p / C::CHUNKS, pc = p % C::CHUNKS;
-      voffg[i] = r * HD2 + (grp == 0 ? swz_k<D>(r, pc) : swz_v<D>(r, pc)) * 16;
+      voffk4[i] = r * HD2 + swz_k<D>(r, pc) * 16;
+      voffv4[i] = r * HD2 + swz_v<D>(r, pc) * 16;
     }
   }
 
@@ -705,30 +705,15 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   Cursor t1 = cursor_next(a, q_hi, t0);
   Cursor t2 = cursor_next(a, q_hi, t1);
   f32x16 sA[2], sB[2];
-  if constexpr (PP) {
-    if (t0.blk < a.nblk) {
-      const KVBlock& kb = a.blk[t0.blk];
-      copy_tile<D, 4>(grp == 0 ? kb.k : kb.v, kb.len, t0.t, b, h, a.H, HD2, gw, voffg,
-                      smem + (grp == 0 ? C::KB : C::VB));
-    }
-    if (t1.blk < a.nblk) {
-      const KVBlock& kb = a.blk[t1.blk];
-      copy_tile<D, 4>(grp == 0 ? kb.k : kb.v, kb.len, t1.t, b, h, a.H, HD2, gw, voffg,
-                      smem + (grp == 0 ? C::KB : C::VB) + C::TILE);
-    }
-  } else {
-    if (t0.blk < a.nblk) {
-      const KVBlock& kb = a.blk[t0.blk];
-      copy_tile<D, NW>(kb.k, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffk, smem + C::KB);
-      copy_tile<D, NW>(kb.v, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffv, smem + C::VB);
-    }
-    if (t1.blk < a.nblk) {
-      const KVBlock& kb = a.blk[t1.blk];
-      copy_tile<D, NW>(kb.k, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffk,
-                       smem + C::KB + C::TILE);
-      copy_tile<D, NW>(kb.v, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffv,
-                       smem + C::VB + C::TILE);
-    }
+  if (t0.blk < a.nblk) {
+    const KVBlock& kb = a.blk[t0.blk];
+    copy_tile<D, NW>(kb.k, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffk, smem + C::KB);
+    copy_tile<D, NW>(kb.v, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffv, smem + C::VB);
+  }
+  if (t1.blk < a.nblk) {
+    const KVBlock& kb = a.blk[t1.blk];
+    copy_tile<D, NW>(kb.k, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffk, smem + C::KB + C::TILE);
+    copy_tile<D, NW>(kb.v, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffv, smem + C::VB + C::TILE);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -740,18 +725,13 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
 
   int vb = 0;  // V buffer of tile n
   if constexpr (PP) {
-    // group 1 starts one half step behind: its first barrier is group 0's
-    // after front half 0; group 0 closes with the barrier of group 1's last
-    // back half, so both groups pass the same number of barriers
-    if (grp == 1) pipeline_barrier();
     while (t0.blk < a.nblk) {
       pp_step<D, 0>(a, smem, w, sA, sB, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows, col, half, b,
-                    h, HD2, gw, grp, voffg);
+                    h, HD2, gw, grp, voffk4, voffv4);
       if (t0.blk >= a.nblk) break;
       pp_step<D, 1>(a, smem, w, sB, sA, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows, col, half, b,
-                    h, HD2, gw, grp, voffg);
+                    h, HD2, gw, grp, voffk4, voffv4);
     }
-    if (grp == 0) pipeline_barrier();
   } else {
     while (t0.blk < a.nblk) {
       pipeline_step<D, NW, 0>(a, smem, w, sA, sB, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows,
@@ -801,11 +781,12 @@ void ring_attn_bf16(const AttnArgs a) {
   attn_bf16_body<D, NW, false>(a, smem);
 }
 
-// Ping-pong form: 8 waves x 32 query rows, one workgroup per CU.
+// Staggered form: 8 waves x 32 query rows, one workgroup per CU, two K and
+// four V buffers.
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ring_attn_bf16_pp(const AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[Bf16Cfg<D, 8>::LDS];
+  __shared__ __attribute__((aligned(1024))) char smem[Bf16Cfg<D, 8>::LDS + Bf16Cfg<D, 8>::TILE];
   attn_bf16_body<D, 8, true>(a, smem);
 }
 
