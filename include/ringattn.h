@@ -69,10 +69,11 @@ typedef enum { RA_SKIP = 0, RA_FULL = 1, RA_DIAG = 2 } ra_block_class;
 /* Process-wide options (ra_set_option). */
 typedef enum { RA_OPT_ATTN_KERNEL = 0, RA_OPT_COUNT = 1 } ra_option;
 /* Values of RA_OPT_ATTN_KERNEL: which bf16 attention kernel the device
- * entry points launch.  AUTO picks the faster one measured for the shape
- * (currently the 128-row kernel everywhere).  Both compute the same
- * function with the same per-wave pipeline; the choice only changes how
- * many query rows share one workgroup's K/V tiles. */
+ * entry points launch.  AUTO picks the fastest one measured for the shape
+ * (currently the 128-row kernel everywhere).  All compute the same
+ * function to the same tolerance; they differ in how many query rows a
+ * wave and a workgroup own and in how the waves of a SIMD share the work.
+ * Any value other than these is rejected by ra_set_option. */
 #define RA_KERNEL_AUTO 0
 #define RA_KERNEL_BR128 1  /* 4 waves x 32 query rows per workgroup */
 #define RA_KERNEL_BR256 2  /* 8 waves x 32 query rows per workgroup */
