@@ -125,6 +125,29 @@ ra_status ra_classify_block(long long q0, long long q1, long long k0,
 ra_status ra_ring_schedule(int P, int rank, long long block_len, int causal,
                            long long valid_len, int* src_out, int* class_out);
 
+/* Zigzag (load-balanced causal) sharding ([RA] §3.4: with contiguous shards
+ * a causal ring gives rank r about r+1/2 blocks of work; holding an early
+ * and a late part of the sequence on every rank balances it).  Reading
+ * adopted: the padded sequence is cut into 2P chunks of chunk_len rows and
+ * rank r holds chunk r followed by chunk 2P-1-r.  Every rank then has
+ * chunk_len * (2P * chunk_len + 1) visible (query, key) pairs per head when
+ * causal.
+ *
+ * ra_zigzag_padded_len: the smallest multiple of 2P * 64 that is >= S (the
+ * kernels need chunks of a multiple of 64 rows); -1 and the error set if
+ * S < 0 or P <= 0.
+ *
+ * ra_zigzag_schedule: src_out[t] = (rank - t) mod P for t = 0..P-1 (the ring
+ * order of [RA] §3.3 over the ranks' shares) and class_out[2t + h] = the
+ * class of chunk (h == 0 ? src : 2P-1-src) against the positions from the
+ * rank's first to its last query (SKIP: after every query; FULL: before
+ * every query and all real).  src_out holds P ints, class_out 2P ints,
+ * both caller-owned host arrays.  Errors: RA_ERR_NULL, RA_ERR_SHAPE,
+ * RA_ERR_RANGE (rank outside [0, P)). */
+long long ra_zigzag_padded_len(long long S, int P);
+ra_status ra_zigzag_schedule(int P, int rank, long long chunk_len, int causal,
+                             long long valid_len, int* src_out, int* class_out);
+
 /* ---------------------------------------------------------------------
  * Device entry points
  * ------------------------------------------------------------------- */
@@ -174,6 +197,24 @@ ra_status ra_ring_attn_fwd(const void* q_r, const void* const* k_blocks,
                            int D, int P, int rank, ra_dtype dt, float scale,
                            int causal, long long valid_len, void* o,
                            float* lse_opt, void* stream);
+
+/* The whole ring of rank `rank` over zigzag shares in one launch ([RA]
+ * §3.2-§3.4 with the sharding of ra_zigzag_schedule).  q_r [B,Sr,H,D] is
+ * the rank's share: rows [0, Sr/2) are chunk rank (global rows
+ * rank*Sr/2 ..), rows [Sr/2, Sr) chunk 2P-1-rank.  k_shares[j], v_shares[j]
+ * ([B,Sr,H,D] each, HOST arrays of P device pointers) are rank j's shares
+ * laid out the same way.  Shares are visited in the order (rank - t) mod P;
+ * chunks in the future of every query of the share (causal) are never
+ * read.  Output o [B,Sr,H,D] in dt for the rank's rows in share order,
+ * lse_opt [B,Sr,H] fp32 natural log-sum-exp (may be NULL).  valid_len: real
+ * global length (< 0 means P*Sr).  Sr must be a multiple of 128
+ * (RA_ERR_SHAPE otherwise; pad to ra_zigzag_padded_len).  P at most
+ * RA_MAX_P/2 (RA_ERR_RANGE).  Other errors as ra_ring_attn_fwd. */
+ra_status ra_zigzag_attn_fwd(const void* q_r, const void* const* k_shares,
+                             const void* const* v_shares, int B, int Sr, int H,
+                             int D, int P, int rank, ra_dtype dt, float scale,
+                             int causal, long long valid_len, void* o,
+                             float* lse_opt, void* stream);
 
 /* Ulysses sequence-shard -> head-shard transpose ([RA] §3.5) of the P
  * per-rank tensors stacked rank-major:

@@ -12,7 +12,8 @@ Sources (the pages this follows, cited by title and section):
   tutorial, jefxiong.cn) -- §3.1 scaled dot-product attention and the rank-local
   output, §3.2 the online-softmax recurrence over (m, l, u), §3.3 the ring order
   (source (r - t) mod P at round t), §3.4 causal block classes on global
-  positions, §3.5 the Ulysses seq-shard <-> head-shard transpose, §04 the
+  positions and the zigzag load-balancing idea, §3.5 the Ulysses seq-shard <->
+  head-shard transpose, §04 the
   4 x 2 worked example, §09 the stability and global-index checks.
 * juejin post 7702110021828427786 (a sequence-parallel attention library that
   never communicated) -- §三 the shard-cover and did-it-communicate checks,
@@ -27,15 +28,18 @@ Sources (the pages this follows, cited by title and section):
 Parity status of each function is listed in its module docstring.
 """
 from .attention import attention, local_only_attention, scores
-from .online import ring_attention_rank, lse_combine, composable_ring_rank, chunked_attention
+from .online import (ring_attention_rank, lse_combine, composable_ring_rank, chunked_attention,
+                     zigzag_ring_rank)
 from .schedule import (SKIP, FULL, DIAG, padded_len, seq_divisible, shard_range, ring_sources,
-                       classify_block, ring_schedule, visible_mask)
+                       classify_block, ring_schedule, visible_mask, zigzag_chunks,
+                       zigzag_positions, zigzag_schedule, visible_pairs)
 from .permute import seq2head, head2seq, seq2head_loops, head2seq_loops
 from .compare import max_abs_err, cosine, rel_l2, compare
 
 __all__ = [
     "attention", "local_only_attention", "scores",
     "ring_attention_rank", "lse_combine", "composable_ring_rank", "chunked_attention",
+    "zigzag_ring_rank", "zigzag_chunks", "zigzag_positions", "zigzag_schedule", "visible_pairs",
     "SKIP", "FULL", "DIAG", "padded_len", "seq_divisible", "shard_range", "ring_sources",
     "classify_block", "ring_schedule", "visible_mask",
     "seq2head", "head2seq", "seq2head_loops", "head2seq_loops",

@@ -20,7 +20,12 @@ extended so that two empty partials (lse = -inf) merge to (0, -inf).
 ``composable_ring_rank`` is the same ring done the post's way: per-round
 partial attention (o, lse) of one block, folded in with ``lse_combine``.
 
-Parity: pinned -- both agree with the plain definition in ``attention`` to
+``zigzag_ring_rank`` runs the same recurrence over zigzag shares (tutorial
+§3.4's load balancing; see ``schedule.zigzag_positions``): the rank's
+queries sit at two ranges of global positions and round t brings the two
+chunks of rank (r - t) mod P's share, each at its own positions.
+
+Parity: pinned -- all three agree with the plain definition in ``attention`` to
 <= 1e-12 for 1, 2, 4, 8 and 16 chunks and block sizes 1, 2, 4 (the post
 reports ~1e-16 for its pure-Python check, the tutorial max_abs_diff = 0 for its
 worked example), survive a +1000 shift of all scores (tutorial §09), and the
@@ -31,7 +36,7 @@ from __future__ import annotations
 import numpy as np
 
 from .attention import _f64, attention
-from .schedule import SKIP, ring_sources, visible_mask
+from .schedule import SKIP, ring_sources, visible_mask, zigzag_chunks, zigzag_positions
 
 
 def ring_attention_rank(q_r, k_blocks, v_blocks, rank, *, scale=None,
@@ -157,3 +162,52 @@ def chunked_attention(q, k, v, n_chunks, *, scale=None, causal=False):
 
 __all__ = ["ring_attention_rank", "lse_combine", "composable_ring_rank",
            "chunked_attention", "SKIP"]
+
+
+def zigzag_ring_rank(q_share, k_shares, v_shares, rank, *, scale=None,
+                     causal=True, valid_len=None):
+    """Rank ``rank``'s output over zigzag shares by the (m, l, u) recurrence.
+
+    q_share and every share: [B, 2c, H, D], chunk r then chunk 2P-1-r of the
+    sequence (r the owner).  Round t visits share (rank - t) mod P, first
+    chunk then second chunk, each at its global positions; a chunk with no
+    visible pair for any query of the share is skipped.  Returns (o, lse).
+    """
+    P = len(k_shares)
+    q = _f64(q_share)
+    B, Sr, H, D = q.shape
+    c = Sr // 2
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    if valid_len is None:
+        valid_len = P * Sr
+    q_pos = zigzag_positions(P, rank, c)
+    m = np.full((B, Sr, H), -np.inf)
+    l = np.zeros((B, Sr, H))
+    u = np.zeros((B, Sr, H, D))
+    for j in ring_sources(P, rank):
+        kj = _f64(k_shares[j])
+        vj = _f64(v_shares[j])
+        for half, kc in enumerate(zigzag_chunks(P, j)):
+            k_pos = kc * c + np.arange(c)
+            vis = visible_mask(q_pos, k_pos, causal, valid_len)
+            if not vis.any():
+                continue
+            kk = kj[:, half * c:(half + 1) * c]
+            vv = vj[:, half * c:(half + 1) * c]
+            for b in range(B):
+                for h in range(H):
+                    s = scale * (q[b, :, h, :] @ kk[b, :, h, :].T)
+                    s = np.where(vis, s, -np.inf)
+                    m_old = m[b, :, h]
+                    m_new = np.maximum(m_old, s.max(axis=1))
+                    m_ref = np.where(np.isfinite(m_new), m_new, 0.0)
+                    alpha = np.where(np.isfinite(m_old), np.exp(m_old - m_ref), 0.0)
+                    p = np.where(vis, np.exp(s - m_ref[:, None]), 0.0)
+                    l[b, :, h] = alpha * l[b, :, h] + p.sum(axis=1)
+                    u[b, :, h, :] = alpha[:, None] * u[b, :, h, :] + p @ vv[b, :, h, :]
+                    m[b, :, h] = m_new
+    seen = l > 0
+    o = np.where(seen[..., None], u / np.where(seen, l, 1.0)[..., None], 0.0)
+    lse = np.where(seen, m + np.log(np.where(seen, l, 1.0)), -np.inf)
+    return o, lse

@@ -7,7 +7,10 @@ and by the per-rank figures of the budget script in the Ring Attention
 tutorial §04 (16384 local tokens, 8 rounds at L=131072, P=8);
 ``classify_block`` by brute force over ``visible_mask``; ``ring_sources`` by
 the rule of the tutorial §3.3 and by the visited-block count of the causal
-ring.
+ring.  The zigzag helpers (tutorial §3.4's load-balanced sharding, read as:
+2P chunks, rank r holding chunks r and 2P-1-r) are pinned by the cover of
+the sequence, by the closed-form visible-pair count c (2P c + 1) per rank,
+and by brute-force classes over ``visible_mask``.
 """
 from __future__ import annotations
 
@@ -105,3 +108,46 @@ def ring_schedule(P: int, rank: int, block_len: int, causal: bool,
     cls = [classify_block(q0, q1, j * block_len, (j + 1) * block_len, causal,
                           valid_len) for j in srcs]
     return srcs, cls
+
+
+# ---------------------------------------------------------------- zigzag
+# Tutorial §3.4: with contiguous shards the causal ring gives rank r the
+# work of r + 1/2 blocks; implementations rebalance it by letting every rank
+# hold both early and late positions.  Reading adopted (the page names the
+# idea only): cut the sequence into 2P equal chunks; rank r holds chunk r
+# followed by chunk 2P-1-r.
+
+def zigzag_chunks(P: int, rank: int):
+    """The two chunk indices of rank ``rank``'s share, in share order."""
+    return rank, 2 * P - 1 - rank
+
+
+def zigzag_positions(P: int, rank: int, chunk_len: int) -> np.ndarray:
+    """Global positions of the rows of rank ``rank``'s share, in share order."""
+    a, b = zigzag_chunks(P, rank)
+    return np.concatenate([a * chunk_len + np.arange(chunk_len),
+                           b * chunk_len + np.arange(chunk_len)])
+
+
+def zigzag_schedule(P: int, rank: int, chunk_len: int, causal: bool,
+                    valid_len: int):
+    """(sources, classes): round t visits the share of rank (rank - t) mod P
+    (tutorial §3.3); classes[t] = (class of its first chunk, class of its
+    second chunk) against the rank's query positions, by brute force."""
+    q_pos = zigzag_positions(P, rank, chunk_len)
+    srcs = ring_sources(P, rank)
+    cls = []
+    for j in srcs:
+        pair = []
+        for kc in zigzag_chunks(P, j):
+            m = visible_mask(q_pos, kc * chunk_len + np.arange(chunk_len), causal,
+                             valid_len)
+            pair.append(SKIP if not m.any() else (FULL if m.all() else DIAG))
+        cls.append(tuple(pair))
+    return srcs, cls
+
+
+def visible_pairs(q_pos, P: int, S: int, causal: bool, valid_len: int) -> int:
+    """Number of visible (query, key) pairs of the given query positions over
+    keys 0 .. S-1 (brute force)."""
+    return int(visible_mask(q_pos, np.arange(S), causal, valid_len).sum())

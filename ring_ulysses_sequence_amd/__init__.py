@@ -41,6 +41,7 @@ EXPORTED = (
     "ra_abi_version", "ra_set_option", "ra_get_option", "ra_last_error", "ra_padded_len", "ra_shard_range",
     "ra_classify_block", "ra_ring_schedule", "ra_block_attn_fwd",
     "ra_ring_merge", "ra_ring_attn_fwd", "ra_seq2head", "ra_head2seq",
+    "ra_zigzag_padded_len", "ra_zigzag_schedule", "ra_zigzag_attn_fwd",
 )
 
 _lib = None
@@ -79,6 +80,12 @@ def _load():
         "ra_ring_attn_fwd": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp),
                                      c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                      c_float, c_int, c_ll, c_vp, c_vp, c_vp]),
+        "ra_zigzag_padded_len": (c_ll, [c_ll, c_int]),
+        "ra_zigzag_schedule": (c_int, [c_int, c_int, c_ll, c_int, c_ll,
+                                       ctypes.POINTER(c_int), ctypes.POINTER(c_int)]),
+        "ra_zigzag_attn_fwd": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp),
+                                       c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                       c_float, c_int, c_ll, c_vp, c_vp, c_vp]),
         "ra_seq2head": (c_int, [c_vp, c_vp, c_int, c_int, c_ll, c_int, c_int, c_int, c_vp]),
         "ra_head2seq": (c_int, [c_vp, c_vp, c_int, c_int, c_ll, c_int, c_int, c_int, c_vp]),
     }
@@ -145,6 +152,24 @@ def ring_schedule(P: int, rank: int, block_len: int, causal: bool, valid_len: in
     _check(_load().ra_ring_schedule(P, rank, block_len, int(causal), valid_len, src, cls),
            "ring_schedule")
     return list(src)[:P], list(cls)[:P]
+
+
+def zigzag_padded_len(S: int, P: int) -> int:
+    """Smallest multiple of 2P*64 >= S (zigzag chunks of a multiple of 64 rows)."""
+    r = _load().ra_zigzag_padded_len(S, P)
+    if r < 0:
+        raise ValueError(_load().ra_last_error().decode())
+    return r
+
+
+def zigzag_schedule(P: int, rank: int, chunk_len: int, causal: bool, valid_len: int = -1):
+    """(sources, classes) of rank's zigzag ring: sources[t] = (rank - t) mod P,
+    classes[t] = (class of chunk sources[t], class of chunk 2P-1-sources[t])."""
+    src = (ctypes.c_int * max(P, 1))()
+    cls = (ctypes.c_int * max(2 * P, 2))()
+    _check(_load().ra_zigzag_schedule(P, rank, chunk_len, int(causal), valid_len, src, cls),
+           "zigzag_schedule")
+    return list(src)[:P], [(cls[2 * t], cls[2 * t + 1]) for t in range(P)]
 
 
 # --------------------------------------------------------------- device calls
@@ -260,6 +285,41 @@ def ring_attn_fwd(q_r, k_blocks: Sequence, v_blocks: Sequence, rank: int, *,
     return o, lse
 
 
+def zigzag_attn_fwd(q_r, k_shares: Sequence, v_shares: Sequence, rank: int, *,
+                    causal: bool = True, valid_len: int = -1, scale: float = 0.0,
+                    want_lse: bool = True, out=None, lse_out=None, stream=None):
+    """Rank ``rank``'s whole ring over zigzag shares in one launch.  q_r and
+    every share are [B, Sr, H, D]: chunk r then chunk 2P-1-r of the sequence.
+    Returns (o [B,Sr,H,D] in q's dtype, lse [B,Sr,H] fp32)."""
+    torch = _torch()
+    B, Sr, H, D = q_r.shape
+    P = len(k_shares)
+    if len(v_shares) != P:
+        raise ValueError("k_shares and v_shares differ in length")
+    if 2 * P > RA_MAX_P:
+        raise RuntimeError(f"P={P} exceeds {RA_MAX_P // 2}")
+    dt = _dtype_code(q_r)
+    kp = (ctypes.c_void_p * max(P, 1))()
+    vp = (ctypes.c_void_p * max(P, 1))()
+    for j in range(P):
+        for t, n in ((k_shares[j], "k"), (v_shares[j], "v")):
+            if t.shape != q_r.shape or t.dtype != q_r.dtype:
+                raise ValueError(f"{n}_shares[{j}] must match q_r in shape and dtype")
+        kp[j] = k_shares[j].data_ptr()
+        vp[j] = v_shares[j].data_ptr()
+        _dev(k_shares[j], f"k_shares[{j}]"), _dev(v_shares[j], f"v_shares[{j}]")
+    o = torch.empty_like(q_r) if out is None else out
+    lse = lse_out
+    if lse is None and want_lse:
+        lse = torch.empty((B, Sr, H), dtype=torch.float32, device=q_r.device)
+    st = _load().ra_zigzag_attn_fwd(_dev(q_r, "q_r"), kp, vp, B, Sr, H, D, P, rank, dt,
+                                    float(scale), int(causal), valid_len, _dev(o, "o"),
+                                    _dev(lse, "lse") if lse is not None else None,
+                                    _stream(stream))
+    _check(st, "ra_zigzag_attn_fwd")
+    return o, lse
+
+
 def _perm(fn_name, x, out_shape, P, B, S, H, D, out, stream):
     torch = _torch()
     y = torch.empty(out_shape, dtype=x.dtype, device=x.device) if out is None else out
@@ -324,6 +384,7 @@ def ring_attn_composable(q_r, k_blocks, v_blocks, rank: int, *, causal: bool = F
 __all__ = [
     "lib", "abi_version", "set_attn_kernel", "get_attn_kernel", "padded_len", "shard_range", "classify_block", "ring_schedule",
     "block_attn_fwd", "ring_merge", "ring_attn_fwd", "seq2head", "head2seq",
+    "zigzag_padded_len", "zigzag_schedule", "zigzag_attn_fwd",
     "ring_attn_composable", "EXPORTED", "LIB_PATH", "LibraryMissing",
     "RA_BF16", "RA_FP32", "RA_SKIP", "RA_FULL", "RA_DIAG", "RA_MAX_P", "RA_PAD_MULTIPLE",
     "RA_KERNEL_AUTO", "RA_KERNEL_BR128", "RA_KERNEL_BR256", "RA_KERNEL_W64", "RA_KERNEL_WS",

@@ -55,7 +55,14 @@ struct AttnArgs {
   float* lse;          // [B, Sq, H] or null
   float* m_out;        // [B, Sq, H] or null
   float* l_out;        // [B, Sq, H] or null
+  // global position of query row r: q_pos0 + r for r < q_split, else
+  // q_pos1 + (r - q_split) (two segments for the zigzag share; q_split is a
+  // multiple of 64 and q_pos1 >= q_pos0 + q_split, so positions increase
+  // with the row)
   long long q_pos0;
+  long long q_pos1;
+  int q_split;
+  int kv_rows_b;       // rows between consecutive batches in every K/V buffer
   long long valid_len; // keys at global positions >= valid_len are padding
   int B, Sq, H;
   int n_qtiles;
@@ -67,6 +74,10 @@ struct AttnArgs {
 };
 
 constexpr float kLn2 = 0.693147180559945309f;
+
+__host__ __device__ __forceinline__ long long qpos(const AttnArgs& a, int row) {
+  return row < a.q_split ? a.q_pos0 + row : a.q_pos1 + (row - a.q_split);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -319,15 +330,16 @@ struct WaveState {
 };
 
 // Copy one K or V tile (rows kt0 .. kt0+63 of batch b, head h of `src`, a
-// visited block of `len` rows) into LDS at `dst`; each wave copies C::DMA KiB.
+// visited block of `len` rows whose batches lie rows_b rows apart) into LDS
+// at `dst`; each wave copies C::DMA KiB.
 template <int D, int NW>
-__device__ __forceinline__ void copy_tile(const void* src, int len, int ti, int b, int h,
-                                          int H, int HD2, int wave, const int* voff,
+__device__ __forceinline__ void copy_tile(const void* src, int len, int rows_b, int ti, int b,
+                                          int h, int H, int HD2, int wave, const int* voff,
                                           char* dst) {
   using C = Bf16Cfg<D, NW>;
   const int kt0 = ti * C::BC;
   const int rows = min(C::BC, len - kt0);
-  const long long off = (((long long)b * len + kt0) * H + h) * (D * 2);
+  const long long off = (((long long)b * rows_b + kt0) * H + h) * (D * 2);
   const int nrec = (rows - 1) * HD2 + D * 2;
   __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const char*)src + off), 0, nrec, kRsrcWord3);
@@ -568,9 +580,9 @@ __device__ __forceinline__ void pipeline_step(
   const bool copy2 = t2.blk < a.nblk;
   if (copy2) {
     const KVBlock& kb2 = a.blk[t2.blk];
-    copy_tile<D, NW>(kb2.k, kb2.len, t2.t, b, h, a.H, HD2, wave, w.voffk,
+    copy_tile<D, NW>(kb2.k, kb2.len, a.kv_rows_b, t2.t, b, h, a.H, HD2, wave, w.voffk,
                  smem + C::KB + PAR * C::TILE);
-    copy_tile<D, NW>(kb2.v, kb2.len, t2.t, b, h, a.H, HD2, wave, w.voffv,
+    copy_tile<D, NW>(kb2.v, kb2.len, a.kv_rows_b, t2.t, b, h, a.H, HD2, wave, w.voffv,
                  smem + C::VB + vb2 * C::TILE);
   }
   bf16x8 pb[C::NS / 8];
@@ -606,9 +618,9 @@ __device__ __forceinline__ void pp_step(
   const bool copy2 = grp == 0 && t2.blk < a.nblk;
   if (copy2) {
     const KVBlock& kb2 = a.blk[t2.blk];
-    copy_tile<D, 4>(kb2.k, kb2.len, t2.t, b, h, a.H, HD2, gw, voffk4,
+    copy_tile<D, 4>(kb2.k, kb2.len, a.kv_rows_b, t2.t, b, h, a.H, HD2, gw, voffk4,
                     smem + C::KB + PAR * C::TILE);
-    copy_tile<D, 4>(kb2.v, kb2.len, t2.t, b, h, a.H, HD2, gw, voffv4,
+    copy_tile<D, 4>(kb2.v, kb2.len, a.kv_rows_b, t2.t, b, h, a.H, HD2, gw, voffv4,
                     smem + C::VB + ((vb + 2) & 3) * C::TILE);
   }
   bf16x8 pb[C::NS / 8];
@@ -645,11 +657,10 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   tile_coords(a, b, h, qt);
   const int row0 = qt * C::BR;
   const int rows_here = min(C::BR, a.Sq - row0);
-  const long long q_lo = a.q_pos0 + row0;
-  const long long q_hi = q_lo + rows_here - 1;
+  const long long q_hi = qpos(a, row0 + rows_here - 1);
   const int wrow0 = row0 + wave * 32;
   const int wrows = min(32, a.Sq - wrow0);
-  const long long wq_lo = a.q_pos0 + wrow0;
+  const long long wq_lo = qpos(a, wrow0);
   const long long wq_hi = wq_lo + wrows - 1;
   const long long HD = (long long)a.H * D;
   const int HD2 = a.H * D * 2;  // bytes between consecutive key rows
@@ -707,13 +718,17 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   f32x16 sA[2], sB[2];
   if (t0.blk < a.nblk) {
     const KVBlock& kb = a.blk[t0.blk];
-    copy_tile<D, NW>(kb.k, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffk, smem + C::KB);
-    copy_tile<D, NW>(kb.v, kb.len, t0.t, b, h, a.H, HD2, wave, w.voffv, smem + C::VB);
+    copy_tile<D, NW>(kb.k, kb.len, a.kv_rows_b, t0.t, b, h, a.H, HD2, wave, w.voffk,
+                     smem + C::KB);
+    copy_tile<D, NW>(kb.v, kb.len, a.kv_rows_b, t0.t, b, h, a.H, HD2, wave, w.voffv,
+                     smem + C::VB);
   }
   if (t1.blk < a.nblk) {
     const KVBlock& kb = a.blk[t1.blk];
-    copy_tile<D, NW>(kb.k, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffk, smem + C::KB + C::TILE);
-    copy_tile<D, NW>(kb.v, kb.len, t1.t, b, h, a.H, HD2, wave, w.voffv, smem + C::VB + C::TILE);
+    copy_tile<D, NW>(kb.k, kb.len, a.kv_rows_b, t1.t, b, h, a.H, HD2, wave, w.voffk,
+                     smem + C::KB + C::TILE);
+    copy_tile<D, NW>(kb.v, kb.len, a.kv_rows_b, t1.t, b, h, a.H, HD2, wave, w.voffv,
+                     smem + C::VB + C::TILE);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -862,7 +877,7 @@ __device__ __forceinline__ Stage stage_enter(const AttnArgs& a, int blk, long lo
   s.k = s.v = nullptr;
   if (s.blk < a.nblk) {
     const KVBlock& kb = a.blk[s.blk];
-    const long long off = (long long)b * kb.len * HD2 + (long long)h * D2;
+    const long long off = (long long)b * a.kv_rows_b * HD2 + (long long)h * D2;
     s.kp = (int)kb.k_pos0;
     s.rows = kb.len;
     s.k = (const char*)kb.k + off;
@@ -1263,11 +1278,11 @@ void ring_attn_bf16_w64(const AttnArgs a) {
   tile_coords(a, b, h, qt);
   const int row0 = qt * C::BR;
   const int rows_here = min(C::BR, a.Sq - row0);
-  const long long q_hi = a.q_pos0 + row0 + rows_here - 1;
+  const long long q_hi = qpos(a, row0 + rows_here - 1);
   const int wrow0 = row0 + wave * C::WR;
   const int wrows = min(C::WR, a.Sq - wrow0);
   const bool wave_live = wrows > 0;
-  const int wq_lo = (int)a.q_pos0 + wrow0;
+  const int wq_lo = (int)qpos(a, wrow0);
   const int wq_hi = wq_lo + wrows - 1;
   const int valid_len = a.valid_len > 0x7fffffffLL ? 0x7fffffff : (int)a.valid_len;
   const bool causal = a.causal != 0;
@@ -1705,11 +1720,11 @@ void ring_attn_bf16_ws(const AttnArgs a) {
   tile_coords(a, b, h, qt);
   const int row0 = qt * C::BR;
   const int rows_here = min(C::BR, a.Sq - row0);
-  const long long q_hi = a.q_pos0 + row0 + rows_here - 1;
+  const long long q_hi = qpos(a, row0 + rows_here - 1);
   const int wrow0 = row0 + pair * C::WR;
   const int wrows = min(C::WR, a.Sq - wrow0);
   const bool wave_live = wrows > 0;
-  const int wq_lo = (int)a.q_pos0 + wrow0;
+  const int wq_lo = (int)qpos(a, wrow0);
   const int wq_hi = wq_lo + wrows - 1;
   const int valid_len = a.valid_len > 0x7fffffffLL ? 0x7fffffff : (int)a.valid_len;
   const bool causal = a.causal != 0;
@@ -1920,11 +1935,10 @@ void ring_attn_f32(const AttnArgs a) {
   tile_coords(a, b, h, qt);
   const int row0 = qt * kBR;
   const int rows_here = min(kBR, a.Sq - row0);
-  const long long q_lo = a.q_pos0 + row0;
-  const long long q_hi = q_lo + rows_here - 1;
+  const long long q_hi = qpos(a, row0 + rows_here - 1);
   const int wrow0 = row0 + wave * 32;
   const int wrows = min(32, a.Sq - wrow0);
-  const long long wq_lo = a.q_pos0 + wrow0;
+  const long long wq_lo = qpos(a, wrow0);
   const long long wq_hi = wq_lo + wrows - 1;
   const long long HD = (long long)a.H * D;
 
@@ -1952,8 +1966,8 @@ void ring_attn_f32(const AttnArgs a) {
   auto fetch = [&](int bi, int ti) {
     const KVBlock& kb = a.blk[bi];
     const int kt0 = ti * BC;
-    const float* kp = (const float*)kb.k + ((long long)b * kb.len + kt0) * HD + (long long)h * D;
-    const float* vp = (const float*)kb.v + ((long long)b * kb.len + kt0) * HD + (long long)h * D;
+    const float* kp = (const float*)kb.k + ((long long)b * a.kv_rows_b + kt0) * HD + (long long)h * D;
+    const float* vp = (const float*)kb.v + ((long long)b * a.kv_rows_b + kt0) * HD + (long long)h * D;
     const int rows = min(BC, kb.len - kt0);
 #pragma unroll
     for (int u = 0; u < C::UNITS; ++u) {
@@ -2088,7 +2102,7 @@ enum Bf16Kernel { K_BR128, K_BR256, K_W64, K_WS, K_PP };
 // and key position (plus a tile of slack) stays below 2^31.
 bool positions_fit_32(const AttnArgs& a) {
   const long long lim = 0x7fffffffLL - 256;
-  if (a.q_pos0 + a.Sq > lim) return false;
+  if (qpos(a, a.Sq - 1) + 1 > lim) return false;
   for (int i = 0; i < a.nblk; ++i)
     if (a.blk[i].k_pos0 + a.blk[i].len > lim) return false;
   return true;
@@ -2186,6 +2200,9 @@ extern "C" ra_status ra_block_attn_fwd(const void* q, const void* k, const void*
   a.m_out = m_opt;
   a.l_out = l_opt;
   a.q_pos0 = q_pos0;
+  a.q_pos1 = q_pos0 + Sq;
+  a.q_split = Sq;
+  a.kv_rows_b = Sk;
   a.valid_len = valid_len;
   a.B = B;
   a.Sq = Sq;
@@ -2231,6 +2248,9 @@ extern "C" ra_status ra_ring_attn_fwd(const void* q_r, const void* const* k_bloc
   a.o = o;
   a.lse = lse_opt;
   a.q_pos0 = (long long)rank * Sb;
+  a.q_pos1 = a.q_pos0 + Sb;
+  a.q_split = Sb;
+  a.kv_rows_b = Sb;
   a.valid_len = valid_len;
   a.B = B;
   a.Sq = Sb;
@@ -2253,6 +2273,73 @@ extern "C" ra_status ra_ring_attn_fwd(const void* q_r, const void* const* k_bloc
     if (!aligned16(k_blocks[j]) || !aligned16(v_blocks[j]))
       return ra::fail(RA_ERR_SHAPE, "%s: block %d not 16-byte aligned", name, j);
     a.blk[a.nblk++] = KVBlock{k_blocks[j], v_blocks[j], (long long)j * Sb, Sb, cls[t]};
+  }
+  return launch(a, D, dt, (hipStream_t)stream, name);
+}
+
+extern "C" ra_status ra_zigzag_attn_fwd(const void* q_r, const void* const* k_shares,
+                                        const void* const* v_shares, int B, int Sr, int H,
+                                        int D, int P, int rank, ra_dtype dt, float scale,
+                                        int causal, long long valid_len, void* o,
+                                        float* lse_opt, void* stream) {
+  static const char* name = "ra_zigzag_attn_fwd";
+  ra::clear_error();
+  ra_status st = check_common(name, B, Sr, H, D, dt);
+  if (st != RA_OK) return st;
+  if (P <= 0) return ra::fail(RA_ERR_SHAPE, "%s: P must be positive (got %d)", name, P);
+  if (2 * P > RA_MAX_P)
+    return ra::fail(RA_ERR_RANGE, "%s: P=%d exceeds RA_MAX_P/2=%d", name, P, RA_MAX_P / 2);
+  if (rank < 0 || rank >= P)
+    return ra::fail(RA_ERR_RANGE, "%s: rank %d outside [0, %d)", name, rank, P);
+  if (Sr % 128 != 0)
+    return ra::fail(RA_ERR_SHAPE, "%s: rows per rank (%d) must be two chunks of a multiple "
+                    "of 64 rows; pad the sequence to ra_zigzag_padded_len(S, P)", name, Sr);
+  const long long n_out = (long long)B * Sr * H;
+  if (n_out == 0) return RA_OK;
+  if (!q_r || !o || !k_shares || !v_shares)
+    return ra::fail(RA_ERR_NULL, "%s: NULL q/o/share table", name);
+  if (!aligned16(q_r) || !aligned16(o))
+    return ra::fail(RA_ERR_SHAPE, "%s: q and o must be 16-byte aligned", name);
+  const int c = Sr / 2;  // chunk length
+  const long long S = (long long)P * Sr;
+  if (valid_len < 0 || valid_len > S) valid_len = S;
+  AttnArgs a{};
+  a.q = q_r;
+  a.o = o;
+  a.lse = lse_opt;
+  // the share is chunk rank (rows [0, c)) then chunk 2P-1-rank (rows [c, 2c))
+  a.q_pos0 = (long long)rank * c;
+  a.q_pos1 = (long long)(2 * P - 1 - rank) * c;
+  a.q_split = c;
+  a.kv_rows_b = Sr;
+  a.valid_len = valid_len;
+  a.B = B;
+  a.Sq = Sr;
+  a.H = H;
+  a.causal = causal != 0;
+  a.o_fp32 = dt == RA_FP32;
+  const double sc = scale > 0.0f ? (double)scale : 1.0 / std::sqrt((double)D);
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  // round t visits the share of rank (rank - t) mod P, as in the plain ring;
+  // each share is two chunks, classified against the whole query share
+  int src[RA_MAX_P], cls[2 * RA_MAX_P];
+  st = ra_zigzag_schedule(P, rank, c, causal, valid_len, src, cls);
+  if (st != RA_OK) return st;
+  a.nblk = 0;
+  const size_t row_bytes = (size_t)H * D * (dt == RA_BF16 ? 2 : 4);
+  for (int t = 0; t < P; ++t) {
+    const int j = src[t];
+    for (int half = 0; half < 2; ++half) {
+      if (cls[2 * t + half] == RA_SKIP) continue;
+      if (!k_shares[j] || !v_shares[j])
+        return ra::fail(RA_ERR_NULL, "%s: NULL pointer for visited share %d", name, j);
+      if (!aligned16(k_shares[j]) || !aligned16(v_shares[j]))
+        return ra::fail(RA_ERR_SHAPE, "%s: share %d not 16-byte aligned", name, j);
+      const int chunk = half == 0 ? j : 2 * P - 1 - j;
+      const size_t off = (size_t)half * c * row_bytes;
+      a.blk[a.nblk++] = KVBlock{(const char*)k_shares[j] + off, (const char*)v_shares[j] + off,
+                                (long long)chunk * c, c, cls[2 * t + half]};
+    }
   }
   return launch(a, D, dt, (hipStream_t)stream, name);
 }

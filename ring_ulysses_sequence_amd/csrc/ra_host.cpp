@@ -129,4 +129,44 @@ ra_status ra_ring_schedule(int P, int rank, long long block_len, int causal,
   return RA_OK;
 }
 
+long long ra_zigzag_padded_len(long long S, int P) {
+  ra::clear_error();
+  if (S < 0 || P <= 0) {
+    ra::fail(RA_ERR_SHAPE, "ra_zigzag_padded_len: need S >= 0 and P > 0 (got S=%lld P=%d)",
+             S, P);
+    return -1;
+  }
+  const long long unit = 2LL * P * 64;  // 2P chunks of a multiple of 64 rows
+  return (S + unit - 1) / unit * unit;
+}
+
+ra_status ra_zigzag_schedule(int P, int rank, long long chunk_len, int causal,
+                             long long valid_len, int* src_out, int* class_out) {
+  ra::clear_error();
+  if (!src_out || !class_out)
+    return ra::fail(RA_ERR_NULL, "ra_zigzag_schedule: NULL output array");
+  if (P <= 0 || chunk_len < 0)
+    return ra::fail(RA_ERR_SHAPE, "ra_zigzag_schedule: need P > 0 and chunk_len >= 0");
+  if (rank < 0 || rank >= P)
+    return ra::fail(RA_ERR_RANGE, "ra_zigzag_schedule: rank %d outside [0, %d)", rank, P);
+  if (valid_len < 0) valid_len = 2LL * P * chunk_len;
+  // the query share: chunk rank and chunk 2P-1-rank, positions increasing;
+  // a key chunk is classified against [first query, last query] (SKIP only
+  // if it is in the future of both query chunks, FULL only if it is in the
+  // past of both), which is what the kernel needs: within a DIAG chunk each
+  // wave still decides per tile on its own rows
+  const long long q0 = rank * chunk_len;
+  const long long q1 = (2LL * P - 1 - rank) * chunk_len + chunk_len;
+  for (int t = 0; t < P; ++t) {
+    const int j = ((rank - t) % P + P) % P;  // [RA] §3.3
+    src_out[t] = j;
+    for (int half = 0; half < 2; ++half) {
+      const long long kc = half == 0 ? j : 2LL * P - 1 - j;
+      class_out[2 * t + half] = ra::block_class(q0, q1, kc * chunk_len, (kc + 1) * chunk_len,
+                                                causal != 0, valid_len);
+    }
+  }
+  return RA_OK;
+}
+
 }  // extern "C"

@@ -348,6 +348,101 @@ def test_padded_skipped_blocks_never_read(padded, variant):
     assert (diff.float() - base.float()).abs().max().item() > 1.0
 
 
+# ------------------------------------------------------------ zigzag shares
+def zigzag_shares(x, P):
+    """The P zigzag shares of a [B, S, H, D] tensor (rows at the positions the
+    oracle assigns to each rank), each contiguous [B, 2c, H, D]."""
+    c = x.shape[1] // (2 * P)
+    return [x[:, torch.as_tensor(oracle.zigzag_positions(P, r, c), device=x.device)].contiguous()
+            for r in range(P)]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_zigzag_all_ranks(variant, causal):
+    """Zigzag shares (chunks r and 2P-1-r), B = 2: every rank's output and
+    lse against the oracle's recurrence over the same shares."""
+    B, S, H, D, P = 2, 2048, 4, 128, 4
+    q, k, v = (W.random_tensor((B, S, H, D), seed=s_, device="cuda") for s_ in (11, 12, 13))
+    qs, ks, vs = zigzag_shares(q, P), zigzag_shares(k, P), zigzag_shares(v, P)
+    kc, vc = [x.cpu() for x in ks], [x.cpu() for x in vs]
+    for r in range(P):
+        o, lse = ra.zigzag_attn_fwd(qs[r], ks, vs, r, causal=causal)
+        torch.cuda.synchronize()
+        ref_o, ref_lse = oracle.zigzag_ring_rank(qs[r].cpu(), kc, vc, r, causal=causal)
+        check_bf16(o.cpu(), ref_o, f"zigzag causal={causal} r{r}")
+        assert oracle.max_abs_err(lse.cpu(), ref_lse) <= LSE_BF16_ATOL
+
+
+def test_zigzag_padded_all_ranks(variant):
+    """S = 3000 padded to 3072 (chunks of 384), one K row per (b, h) x8:
+    real rows of every rank against the plain definition at their global
+    positions (pad queries discarded)."""
+    w = W.PADDED_ZIGZAG
+    assert w.S_padded == 3072
+    q, k, v = W.make_qkv(w)
+    qs, ks, vs = (zigzag_shares(x.cuda(), w.P) for x in (q, k, v))
+    c = w.S_padded // (2 * w.P)
+    full, full_lse, _, _ = oracle.attention(q, k, v, causal=True, valid_len=w.S)
+    for r in w.ranks:
+        say(w.name, "rank", r)
+        o, lse = ra.zigzag_attn_fwd(qs[r], ks, vs, r, causal=True, valid_len=w.S)
+        torch.cuda.synchronize()
+        pos = oracle.zigzag_positions(w.P, r, c)
+        real = np.flatnonzero(pos < w.S)
+        check_bf16(o.cpu()[:, real], full[:, pos[real]], f"{w.name} r{r}")
+        assert oracle.max_abs_err(lse.cpu()[:, real], full_lse[:, pos[real]]) <= LSE_BF16_ATOL
+
+
+def test_zigzag_fp32():
+    """fp32 inputs through the fp32 kernel: every rank to 1e-5."""
+    B, S, H, D, P = 1, 1024, 2, 64, 2
+    q, k, v = (W.random_tensor((B, S, H, D), dtype=torch.float32, seed=s_, device="cuda")
+               for s_ in (21, 22, 23))
+    qs, ks, vs = zigzag_shares(q, P), zigzag_shares(k, P), zigzag_shares(v, P)
+    kc, vc = [x.cpu() for x in ks], [x.cpu() for x in vs]
+    for r in range(P):
+        o, lse = ra.zigzag_attn_fwd(qs[r], ks, vs, r, causal=True)
+        torch.cuda.synchronize()
+        ref_o, ref_lse = oracle.zigzag_ring_rank(qs[r].cpu(), kc, vc, r, causal=True)
+        check_fp32(o.cpu(), ref_o, f"zigzag fp32 r{r}")
+        assert oracle.max_abs_err(lse.cpu(), ref_lse) <= 1e-4
+
+
+def test_zigzag_long_context_ranks_0_and_7():
+    """L = 131072, H = 64, P = 8 zigzag shares (chunks of 8192 rows), ranks 0
+    and 7, in the launch configuration the bench times: sampled rows of both
+    chunks against the plain definition at their global positions."""
+    w = W.LONG_ZIGZAG
+    P, c = w.P, w.S_padded // (2 * w.P)
+    say(w.name, "generate on device")
+    q, k, v = W.make_qkv(w, device="cuda")
+    ks, vs = zigzag_shares(k, P), zigzag_shares(v, P)
+    heads = list(range(0, w.H, 8))
+    for r in w.ranks:
+        q_r = zigzag_shares(q, P)[r]
+        say(w.name, "rank", r)
+        o, lse = ra.zigzag_attn_fwd(q_r, ks, vs, r, causal=True)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o.float()).all()
+        for half, chunk in enumerate(oracle.zigzag_chunks(P, r)):
+            rows = np.unique(np.concatenate([np.arange(0, c, 512), np.arange(0, 4),
+                                             np.arange(c - 4, c), np.arange(126, 130)]))
+            q_c = q[:, chunk * c:(chunk + 1) * c]
+            klim = (chunk + 1) * c
+            kc, vc = k[:, :klim].cpu(), v[:, :klim].cpu()
+            ref_o, ref_l = [], []
+            for h in heads:
+                o_h, l_h, _, _ = oracle.attention(q_c[:, :, h:h + 1].cpu(), kc[:, :, h:h + 1],
+                                                  vc[:, :, h:h + 1], causal=True,
+                                                  q_pos0=chunk * c, k_pos0=0, rows=rows)
+                ref_o.append(o_h)
+                ref_l.append(l_h)
+            got = o[:, half * c + rows][:, :, heads].cpu()
+            check_bf16(got, np.concatenate(ref_o, 2), f"{w.name} r{r} chunk {chunk}")
+            assert oracle.max_abs_err(lse[:, half * c + rows][:, :, heads].cpu(),
+                                      np.concatenate(ref_l, 2)) <= LSE_BF16_ATOL
+
+
 # ------------------------------------------------------------ merge kernel
 def test_ring_merge_against_oracle():
     g = torch.Generator().manual_seed(5)

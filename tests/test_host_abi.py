@@ -95,6 +95,34 @@ def test_ring_schedule_matches_oracle(lib):
         ra.ring_schedule(4, 4, 16, True)
 
 
+def test_zigzag_schedule_matches_oracle(lib):
+    """The library's zigzag ring (sources and chunk classes) equals the
+    oracle's brute force over the share's positions, causal or not, with
+    and without padding."""
+    for P in (1, 2, 3, 4, 8):
+        for c in (1, 3, 64):
+            S = 2 * P * c
+            for causal in (False, True):
+                for valid in (S, S - 1, S - c - 1, c):
+                    if valid <= 0:
+                        continue
+                    for r in range(P):
+                        got = ra.zigzag_schedule(P, r, c, causal, valid)
+                        want = sch.zigzag_schedule(P, r, c, causal, valid)
+                        assert got[0] == want[0]
+                        assert got[1] == [tuple(x) for x in want[1]], (P, c, causal, valid, r)
+
+
+def test_zigzag_padded_len(lib):
+    """Multiples of 2P * 64: the long-context share needs no padding, 3000
+    tokens on four ranks pad to 3072; bad arguments are refused."""
+    assert ra.zigzag_padded_len(131072, 8) == 131072
+    assert ra.zigzag_padded_len(3000, 4) == 3072
+    assert ra.zigzag_padded_len(0, 4) == 0
+    with pytest.raises(ValueError):
+        ra.zigzag_padded_len(10, 0)
+
+
 def test_classify_block_matches_brute_force(lib):
     rng = np.random.default_rng(11)
     for _ in range(3000):
@@ -141,6 +169,20 @@ def test_device_entry_points_validate_before_launch(lib):
     assert st == 2
     st = lib.ra_head2seq(ctypes.c_void_p(16), ctypes.c_void_p(1 << 40), 4, 1, 3008, 8, 64, 3, null)
     assert st == 3
+    # zigzag: rows per rank not two chunks of a multiple of 64; rank >= P;
+    # P above RA_MAX_P / 2
+    st = lib.ra_zigzag_attn_fwd(null, arr, arr, 1, 96, 1, 64, 2, 0, ra.RA_BF16, 0.0, 1,
+                                -1, null, null, null)
+    assert st == 2 and b"ra_zigzag_padded_len" in lib.ra_last_error()
+    st = lib.ra_zigzag_attn_fwd(null, arr, arr, 1, 128, 1, 64, 2, 2, ra.RA_BF16, 0.0, 1,
+                                -1, null, null, null)
+    assert st == 4
+    st = lib.ra_zigzag_attn_fwd(null, arr, arr, 1, 128, 1, 64, 33, 0, ra.RA_BF16, 0.0, 1,
+                                -1, null, null, null)
+    assert st == 4
+    st = lib.ra_zigzag_attn_fwd(null, arr, arr, 1, 128, 1, 64, 2, 0, ra.RA_BF16, 0.0, 1,
+                                -1, null, null, null)
+    assert st == 1
     # merge: unsupported D, unknown dtype
     st = lib.ra_ring_merge(null, null, null, null, 1, 4, 1, 12, null, ra.RA_FP32, null)
     assert st == 5

@@ -421,3 +421,96 @@ def test_seq2head_gives_each_rank_whole_sequence_of_its_heads():
         np.testing.assert_array_equal(hx[r], glob[:, :, r * Hl:(r + 1) * Hl])
     with pytest.raises(ValueError):
         oracle.seq2head(np.zeros((3, 1, 2, 4, 1), np.int16))
+
+
+# ---------------------------------------------------------------- zigzag
+@pytest.mark.parametrize("P", [2, 3, 4])
+def test_zigzag_shares_cover_the_sequence(P):
+    """Every position is held by exactly one rank; each share is two chunks
+    in increasing order, the second in the mirror image of the first."""
+    c = 5
+    pos = np.concatenate([sch.zigzag_positions(P, r, c) for r in range(P)])
+    assert sorted(pos.tolist()) == list(range(2 * P * c))
+    for r in range(P):
+        p = sch.zigzag_positions(P, r, c)
+        assert np.all(np.diff(p) > 0)
+        assert p[0] == r * c and p[-1] == (2 * P - r) * c - 1
+
+
+@pytest.mark.parametrize("P", [2, 4, 8])
+def test_zigzag_balances_causal_work(P):
+    """Closed form: every zigzag rank sees c (2P c + 1) pairs per head, while
+    contiguous rank r sees (2r + 1) C^2 / 2 + C/2 with C = 2c (imbalanced)."""
+    c = 6
+    S = 2 * P * c
+    zig = [sch.visible_pairs(sch.zigzag_positions(P, r, c), P, S, True, S) for r in range(P)]
+    assert zig == [c * (2 * P * c + 1)] * P
+    C = 2 * c
+    cont = [sch.visible_pairs(np.arange(r * C, (r + 1) * C), P, S, True, S) for r in range(P)]
+    assert cont == [r * C * C + C * (C + 1) // 2 for r in range(P)]
+    assert sum(zig) == sum(cont) == S * (S + 1) // 2
+
+
+def test_zigzag_schedule_classes():
+    """Round order (r - t) mod P; a chunk is skipped iff it lies after the
+    rank's last query (chunk index > 2P-1-r), the rank's own chunks are
+    diagonal, chunks between the two query chunks are mixed (DIAG), chunks
+    before the first are FULL."""
+    P, c = 4, 3
+    for r in range(P):
+        srcs, cls = sch.zigzag_schedule(P, r, c, True, 2 * P * c)
+        assert srcs == [(r - t) % P for t in range(P)]
+        for j, pair in zip(srcs, cls):
+            for kc, k in zip(sch.zigzag_chunks(P, j), pair):
+                if kc > 2 * P - 1 - r:
+                    want = sch.SKIP
+                elif kc < r:
+                    want = sch.FULL
+                else:
+                    want = sch.DIAG
+                assert k == want, (r, j, kc)
+    # non-causal: everything FULL, padding makes the last chunk DIAG or SKIP
+    srcs, cls = sch.zigzag_schedule(P, 1, c, False, 2 * P * c)
+    assert all(p == (sch.FULL, sch.FULL) for p in cls)
+    srcs, cls = sch.zigzag_schedule(P, 0, c, False, 2 * P * c - 1)
+    assert dict(zip(srcs, cls))[0] == (sch.FULL, sch.DIAG)
+
+
+@pytest.mark.parametrize("P,causal,pad", [(2, True, 0), (3, True, 2), (4, False, 0), (4, True, 5)])
+def test_zigzag_ring_equals_definition(P, causal, pad):
+    """The recurrence over zigzag shares reproduces the plain definition at
+    the share's global positions (to fp64 rounding), with and without padding."""
+    B, H, D, c = 2, 2, 8, 6
+    S = 2 * P * c
+    valid = S - pad
+    g = torch.Generator().manual_seed(7)
+    q = torch.randn(B, S, H, D, generator=g, dtype=torch.float64).numpy()
+    k = torch.randn(B, S, H, D, generator=g, dtype=torch.float64).numpy()
+    v = torch.randn(B, S, H, D, generator=g, dtype=torch.float64).numpy()
+    full, lse_full, _, _ = oracle.attention(q, k, v, causal=causal, valid_len=valid)
+    shares = [sch.zigzag_positions(P, r, c) for r in range(P)]
+    ks = [k[:, p] for p in shares]
+    vs = [v[:, p] for p in shares]
+    for r in range(P):
+        o, lse = oracle.zigzag_ring_rank(q[:, shares[r]], ks, vs, r, causal=causal,
+                                         valid_len=valid)
+        real = shares[r] < valid
+        np.testing.assert_allclose(o[:, real], full[:, shares[r][real]], atol=1e-12, rtol=0)
+        np.testing.assert_allclose(lse[:, real], lse_full[:, shares[r][real]], atol=1e-12, rtol=0)
+
+
+def test_zigzag_wrong_chunk_order_is_caught():
+    """Swapping the two chunks of the key shares (positions taken in the
+    wrong order) changes the causal result: the positions really matter."""
+    P, B, H, D, c = 2, 1, 1, 8, 4
+    S = 2 * P * c
+    g = torch.Generator().manual_seed(3)
+    q, k, v = (torch.randn(B, S, H, D, generator=g, dtype=torch.float64).numpy() for _ in range(3))
+    shares = [sch.zigzag_positions(P, r, c) for r in range(P)]
+    ks = [k[:, p] for p in shares]
+    vs = [v[:, p] for p in shares]
+    good, _ = oracle.zigzag_ring_rank(q[:, shares[1]], ks, vs, 1)
+    ks_bad = [np.concatenate([x[:, c:], x[:, :c]], axis=1) for x in ks]
+    vs_bad = [np.concatenate([x[:, c:], x[:, :c]], axis=1) for x in vs]
+    bad, _ = oracle.zigzag_ring_rank(q[:, shares[1]], ks_bad, vs_bad, 1)
+    assert np.max(np.abs(good - bad)) > 1e-3

@@ -52,6 +52,8 @@ class Workload:
     outlier_k_scale: Optional[float] = None
     seed: int = 0
     note: str = ""
+    # zigzag sharding: 2P chunks, rank r holds chunks r and 2P-1-r
+    zigzag: bool = False
 
     pad_multiple: int = 16
 
@@ -92,8 +94,20 @@ PADDED_CAUSAL = Workload(
     causal=True, ranks=(0, 1, 2, 3), outlier_k_scale=8.0,
     note="S=3000 padded to 3008, one K row per (b,h) scaled x8")
 
+# Zigzag (load-balanced) sharding of the same shapes: chunks of a multiple
+# of 64 rows, so the padding unit is P * 128.
+LONG_ZIGZAG = Workload(
+    name="long_context_causal_zigzag", dtype="bf16", B=1, S=131072, H=64,
+    D=128, P=8, causal=True, ranks=(0, 7), zigzag=True, pad_multiple=128,
+    note="L=131072, P=8, zigzag shares (chunks r and 15-r of 8192 rows)")
+PADDED_ZIGZAG = Workload(
+    name="padded_causal_zigzag", dtype="bf16", B=2, S=3000, H=16, D=64, P=4,
+    causal=True, ranks=(0, 1, 2, 3), outlier_k_scale=8.0, zigzag=True,
+    pad_multiple=128, note="S=3000 padded to 3072, zigzag chunks of 384")
+
 CONFIGS = (TINY_FP32, DIT_SHARD, ULYSSES, LONG_CAUSAL, PADDED_CAUSAL)
-BY_NAME = {c.name: c for c in CONFIGS}
+ZIGZAG_CONFIGS = (LONG_ZIGZAG, PADDED_ZIGZAG)
+BY_NAME = {c.name: c for c in CONFIGS + ZIGZAG_CONFIGS}
 
 
 def outlier_token(b: int, h: int, block_len: int) -> int:
