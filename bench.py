@@ -180,6 +180,7 @@ def main():
     extra = {}
     if not args.no_extra:
         extra = side_measurements(torch, ra, W, stream)
+        extra.update(zigzag_measurements(torch, ra, W, stream, q, k, v))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -273,6 +274,59 @@ def side_measurements(torch, ra, W, stream):
         out[f"ulysses_{name}"] = {"ms": round(ms, 4), "GBps": round(byts / ms / 1e6, 1),
                                   "frac_hbm": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3)}
     del x, y, z
+    return out
+
+
+def zigzag_measurements(torch, ra, W, stream, q, k, v):
+    """Load balance of the causal ring on the same long-context tensors: the
+    zigzag shares of ranks 0 and 7 (chunks r and 15-r of 8192 rows, equal
+    work) against the slowest contiguous rank (7, 7.5 blocks of work).  The
+    ring job takes as long as its slowest rank."""
+    w = W.LONG_ZIGZAG
+    P, c, H, D = w.P, w.S // (2 * w.P), w.H, w.D
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def share(x, r):
+        a, b = r, 2 * P - 1 - r
+        return torch.cat([x[:, a * c:(a + 1) * c], x[:, b * c:(b + 1) * c]], dim=1).contiguous()
+
+    ks = [share(k, r) for r in range(P)]
+    vs = [share(v, r) for r in range(P)]
+
+    def timed(fn, n=3):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    out = {}
+    zz_flops = 4.0 * D * H * c * (2 * P * c + 1)
+    for r in w.ranks:
+        q_r = share(q, r)
+        o = torch.empty_like(q_r)
+        ms = timed(lambda: ra.zigzag_attn_fwd(q_r, ks, vs, r, causal=True, out=o,
+                                              want_lse=False, stream=stream))
+        out[f"zigzag_long_rank{r}"] = {"ms": round(ms, 3), "flops": zz_flops,
+                                       "tflops": round(zz_flops / ms / 1e9, 2)}
+        del q_r, o
+    del ks, vs
+    Sb = w.S // P
+    kb = [k[:, j * Sb:(j + 1) * Sb] for j in range(P)]
+    vb = [v[:, j * Sb:(j + 1) * Sb] for j in range(P)]
+    q7 = q[:, 7 * Sb:8 * Sb]
+    o = torch.empty_like(q7)
+    ms = timed(lambda: ra.ring_attn_fwd(q7, kb, vb, 7, causal=True, out=o, want_lse=False,
+                                        stream=stream))
+    fl7 = 4.0 * D * H * visible_pairs_causal_rank(7, Sb, w.S)
+    out["contiguous_long_rank7"] = {"ms": round(ms, 3), "flops": fl7,
+                                    "tflops": round(fl7 / ms / 1e9, 2)}
+    slow_zz = max(out[f"zigzag_long_rank{r}"]["ms"] for r in w.ranks)
+    out["zigzag_job_speedup_vs_contiguous"] = round(ms / slow_zz, 3)
     return out
 
 
