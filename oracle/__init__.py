@@ -13,7 +13,7 @@ Sources (the pages this follows, cited by title and section):
   output, §3.2 the online-softmax recurrence over (m, l, u), §3.3 the ring order
   (source (r - t) mod P at round t), §3.4 causal block classes on global
   positions and the zigzag load-balancing idea, §3.5 the Ulysses seq-shard <->
-  head-shard transpose, §04 the
+  head-shard transpose, §6.2 the ring backward, §6.6 the fp64 gradient oracle, §04 the
   4 x 2 worked example, §09 the stability and global-index checks.
 * juejin post 7702110021828427786 (a sequence-parallel attention library that
   never communicated) -- §三 the shard-cover and did-it-communicate checks,
@@ -34,12 +34,14 @@ from .schedule import (SKIP, FULL, DIAG, padded_len, seq_divisible, shard_range,
                        classify_block, ring_schedule, visible_mask, zigzag_chunks,
                        zigzag_positions, zigzag_schedule, visible_pairs)
 from .permute import seq2head, head2seq, seq2head_loops, head2seq_loops
+from .grad import attention_grad, ring_attention_bwd_rank
 from .compare import max_abs_err, cosine, rel_l2, compare
 
 __all__ = [
     "attention", "local_only_attention", "scores",
     "ring_attention_rank", "lse_combine", "composable_ring_rank", "chunked_attention",
     "zigzag_ring_rank", "zigzag_chunks", "zigzag_positions", "zigzag_schedule", "visible_pairs",
+    "attention_grad", "ring_attention_bwd_rank",
     "SKIP", "FULL", "DIAG", "padded_len", "seq_divisible", "shard_range", "ring_sources",
     "classify_block", "ring_schedule", "visible_mask",
     "seq2head", "head2seq", "seq2head_loops", "head2seq_loops",

@@ -514,3 +514,118 @@ def test_zigzag_wrong_chunk_order_is_caught():
     vs_bad = [np.concatenate([x[:, c:], x[:, :c]], axis=1) for x in vs]
     bad, _ = oracle.zigzag_ring_rank(q[:, shares[1]], ks_bad, vs_bad, 1)
     assert np.max(np.abs(good - bad)) > 1e-3
+
+
+# ---------------------------------------------------------------- backward
+def _loss(q, k, v, do, **kw):
+    o, _, _, _ = oracle.attention(q, k, v, **kw)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("causal,valid", [(False, None), (True, None), (True, 4), (False, 3)])
+def test_grad_matches_finite_differences(causal, valid):
+    """Central differences of L = sum(dO * O) in every element of q, k, v
+    (brute force, independent of the closed form)."""
+    rng = np.random.default_rng(5)
+    B, S, H, D = 1, 5, 2, 3
+    q, k, v, do = (rng.standard_normal((B, S, H, D)) for _ in range(4))
+    kw = dict(causal=causal, valid_len=valid, q_pos0=0, k_pos0=0)
+    dq, dk, dv = oracle.attention_grad(q, k, v, do, **kw)
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            lp = _loss(q, k, v, do, **kw)
+            x[idx] = old - eps
+            lm = _loss(q, k, v, do, **kw)
+            x[idx] = old
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g, num, atol=1e-8, rtol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grad_matches_torch_autograd_fp64(causal):
+    """Library special case: torch's fp64 autograd through
+    scaled_dot_product_attention ([B, H, S, D] layout)."""
+    g = torch.Generator().manual_seed(9)
+    B, S, H, D = 2, 7, 3, 8
+    q, k, v, do = (torch.randn(B, S, H, D, generator=g, dtype=torch.float64) for _ in range(4))
+    qt, kt, vt = (x.transpose(1, 2).clone().requires_grad_(True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=causal)
+    (o * do.transpose(1, 2)).sum().backward()
+    dq, dk, dv = oracle.attention_grad(q, k, v, do, causal=causal)
+    for mine, ref in ((dq, qt.grad), (dk, kt.grad), (dv, vt.grad)):
+        np.testing.assert_allclose(mine, ref.transpose(1, 2).numpy(), atol=1e-12, rtol=0)
+
+
+def test_grad_invariants():
+    """sum_j dK_j = 0 (each dS row sums to zero) and sum_j dV_j = sum_i dO_i
+    (each P row sums to one); a uniform shift of every key leaves all three
+    gradients unchanged."""
+    rng = np.random.default_rng(2)
+    B, S, H, D = 2, 9, 2, 4
+    q, k, v, do = (rng.standard_normal((B, S, H, D)) for _ in range(4))
+    for causal in (False, True):
+        dq, dk, dv = oracle.attention_grad(q, k, v, do, causal=causal)
+        np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-12)
+        np.testing.assert_allclose(dv.sum(axis=1), do.sum(axis=1), atol=1e-12)
+        w = rng.standard_normal((1, 1, H, D)) * 5
+        dq2, dk2, dv2 = oracle.attention_grad(q, k + w, v, do, causal=causal)
+        np.testing.assert_allclose(dq2, dq, atol=1e-10)
+        np.testing.assert_allclose(dk2, dk, atol=1e-10)
+        np.testing.assert_allclose(dv2, dv, atol=1e-10)
+
+
+@pytest.mark.parametrize("P,causal,pad", [(2, True, 0), (4, True, 3), (3, False, 0), (4, False, 2)])
+def test_ring_backward_sums_to_full_gradient(P, causal, pad):
+    """Tutorial §6.2: every rank's dQ equals the full-sequence dQ of its rows,
+    and each block's dK / dV parts summed over all ranks (returned to the
+    owner) equal the full-sequence dK / dV of that block."""
+    rng = np.random.default_rng(11)
+    B, H, D, Sb = 2, 2, 4, 5
+    S = P * Sb
+    valid = S - pad
+    q, k, v, do = (rng.standard_normal((B, S, H, D)) for _ in range(4))
+    dq, dk, dv = oracle.attention_grad(q, k, v, do, causal=causal, valid_len=valid)
+    kb = [k[:, j * Sb:(j + 1) * Sb] for j in range(P)]
+    vb = [v[:, j * Sb:(j + 1) * Sb] for j in range(P)]
+    dk_sum = [np.zeros_like(x) for x in kb]
+    dv_sum = [np.zeros_like(x) for x in vb]
+    for r in range(P):
+        sl = slice(r * Sb, (r + 1) * Sb)
+        dq_r, dkp, dvp = oracle.ring_attention_bwd_rank(q[:, sl], kb, vb, do[:, sl], r,
+                                                        causal=causal, valid_len=valid)
+        np.testing.assert_allclose(dq_r, dq[:, sl], atol=1e-12)
+        for j in range(P):
+            dk_sum[j] += dkp[j]
+            dv_sum[j] += dvp[j]
+    np.testing.assert_allclose(np.concatenate(dk_sum, 1), dk, atol=1e-12)
+    np.testing.assert_allclose(np.concatenate(dv_sum, 1), dv, atol=1e-12)
+
+
+def test_ring_backward_planted_mistakes_fail():
+    """Tutorial §6.6: forward right but backward wrong points at dK/dV not
+    returned to the owner.  Parts added to the receiving rank's own block,
+    or probabilities normalised per block instead of by the global lse,
+    both miss the full gradient by far more than rounding."""
+    rng = np.random.default_rng(4)
+    P, B, H, D, Sb = 3, 1, 1, 4, 4
+    S = P * Sb
+    q, k, v, do = (rng.standard_normal((B, S, H, D)) for _ in range(4))
+    dq, dk, dv = oracle.attention_grad(q, k, v, do, causal=True)
+    kb = [k[:, j * Sb:(j + 1) * Sb] for j in range(P)]
+    vb = [v[:, j * Sb:(j + 1) * Sb] for j in range(P)]
+    wrong_owner = [np.zeros_like(x) for x in kb]
+    local_dq = []
+    for r in range(P):
+        sl = slice(r * Sb, (r + 1) * Sb)
+        _, dkp, _ = oracle.ring_attention_bwd_rank(q[:, sl], kb, vb, do[:, sl], r, causal=True)
+        for j in range(P):
+            wrong_owner[r] += dkp[j]
+        dq_bad, _, _ = oracle.ring_attention_bwd_rank(q[:, sl], kb, vb, do[:, sl], r, causal=True,
+                                                      lse_block_local=True)
+        local_dq.append(dq_bad)
+    assert np.max(np.abs(np.concatenate(wrong_owner, 1) - dk)) > 1e-2
+    assert np.max(np.abs(np.concatenate(local_dq, 1) - dq)) > 1e-2
