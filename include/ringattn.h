@@ -216,6 +216,33 @@ ra_status ra_zigzag_attn_fwd(const void* q_r, const void* const* k_shares,
                              int causal, long long valid_len, void* o,
                              float* lse_opt, void* stream);
 
+/* Backward of rank `rank`'s ring ([RA] §3.3 closing paragraph, §6.2): the
+ * gradients of the loss with respect to the rank's queries and to the K/V
+ * blocks it visits, given the upstream gradient dO.  Inputs (device, bf16,
+ * [B,Sb,H,D] contiguous): q_r, o_r (the forward's output), do_r; lse_r
+ * [B,Sb,H] fp32 natural log-sum-exp of the forward (ra_ring_attn_fwd's
+ * lse).  k_blocks / v_blocks as in ra_ring_attn_fwd.  With P_j =
+ * exp(scale * Q_r K_j^T - lse_r) over the visible pairs of block j (the
+ * forward's probabilities, recomputed) and D = rowsum(dO * O):
+ *   dq_r          += scale * sum_j (P_j * (dO V_j^T - D)) K_j
+ *   dk_blocks[j]  += scale * (P_j * (dO V_j^T - D))^T Q_r
+ *   dv_blocks[j]  += P_j^T dO
+ * All three are fp32 [B,Sb,H,D] device buffers, ACCUMULATED into (the
+ * caller zeroes them; summing dk/dv over all ranks' calls gives the owners'
+ * gradients, as the ring returns them).  dk_blocks / dv_blocks are HOST
+ * arrays of P device pointers; entries of blocks the rank skips (causal
+ * future) may be NULL and are not touched.  delta_ws: fp32 [B,Sb,H] scratch
+ * the call overwrites (D).  Two launches on `stream` (dq, then dk/dv).
+ * Only bf16 inputs (RA_ERR_UNSUPPORTED for fp32).  Errors as
+ * ra_ring_attn_fwd. */
+ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_blocks,
+                           const void* const* v_blocks, const void* o_r,
+                           const void* do_r, const float* lse_r, int B, int Sb,
+                           int H, int D, int P, int rank, ra_dtype dt, float scale,
+                           int causal, long long valid_len, float* dq_r,
+                           float* const* dk_blocks, float* const* dv_blocks,
+                           float* delta_ws, void* stream);
+
 /* Ulysses sequence-shard -> head-shard transpose ([RA] §3.5) of the P
  * per-rank tensors stacked rank-major:
  *   src [P, B, S/P, H, D]  ->  dst [P, B, S, H/P, D]

@@ -41,7 +41,7 @@ EXPORTED = (
     "ra_abi_version", "ra_set_option", "ra_get_option", "ra_last_error", "ra_padded_len", "ra_shard_range",
     "ra_classify_block", "ra_ring_schedule", "ra_block_attn_fwd",
     "ra_ring_merge", "ra_ring_attn_fwd", "ra_seq2head", "ra_head2seq",
-    "ra_zigzag_padded_len", "ra_zigzag_schedule", "ra_zigzag_attn_fwd",
+    "ra_zigzag_padded_len", "ra_zigzag_schedule", "ra_zigzag_attn_fwd", "ra_ring_attn_bwd",
 )
 
 _lib = None
@@ -86,6 +86,10 @@ def _load():
         "ra_zigzag_attn_fwd": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp),
                                        c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                        c_float, c_int, c_ll, c_vp, c_vp, c_vp]),
+        "ra_ring_attn_bwd": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp, c_vp,
+                                     c_vp, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                     c_float, c_int, c_ll, c_vp, ctypes.POINTER(c_vp),
+                                     ctypes.POINTER(c_vp), c_vp, c_vp]),
         "ra_seq2head": (c_int, [c_vp, c_vp, c_int, c_int, c_ll, c_int, c_int, c_int, c_vp]),
         "ra_head2seq": (c_int, [c_vp, c_vp, c_int, c_int, c_ll, c_int, c_int, c_int, c_vp]),
     }
@@ -320,6 +324,54 @@ def zigzag_attn_fwd(q_r, k_shares: Sequence, v_shares: Sequence, rank: int, *,
     return o, lse
 
 
+def ring_attn_bwd(q_r, k_blocks: Sequence, v_blocks: Sequence, o_r, do_r, lse_r, rank: int, *,
+                  causal: bool = False, valid_len: int = -1, scale: float = 0.0,
+                  dq=None, dk_blocks=None, dv_blocks=None, stream=None):
+    """Backward of rank ``rank``'s ring: accumulates into (dq [B,Sb,H,D],
+    dk_blocks[j], dv_blocks[j]) (fp32, zero-initialised when not given) the
+    gradients of the rank's queries and of the blocks it visits.  Returns
+    (dq, dk_blocks, dv_blocks)."""
+    torch = _torch()
+    B, Sb, H, D = q_r.shape
+    P = len(k_blocks)
+    if len(v_blocks) != P:
+        raise ValueError("k_blocks and v_blocks differ in length")
+    if P > RA_MAX_P:
+        raise RuntimeError(f"P={P} exceeds {RA_MAX_P}")
+    dt = _dtype_code(q_r)
+    for t, n in ((o_r, "o_r"), (do_r, "do_r")):
+        if t.shape != q_r.shape or t.dtype != q_r.dtype:
+            raise ValueError(f"{n} must match q_r in shape and dtype")
+    if lse_r.shape != (B, Sb, H) or lse_r.dtype != torch.float32:
+        raise ValueError("lse_r must be fp32 [B, Sb, H]")
+    f32 = dict(dtype=torch.float32, device=q_r.device)
+    dq = torch.zeros(q_r.shape, **f32) if dq is None else dq
+    dk_blocks = [torch.zeros(q_r.shape, **f32) for _ in range(P)] if dk_blocks is None else dk_blocks
+    dv_blocks = [torch.zeros(q_r.shape, **f32) for _ in range(P)] if dv_blocks is None else dv_blocks
+    kp = (ctypes.c_void_p * max(P, 1))()
+    vp = (ctypes.c_void_p * max(P, 1))()
+    dkp = (ctypes.c_void_p * max(P, 1))()
+    dvp = (ctypes.c_void_p * max(P, 1))()
+    for j in range(P):
+        for t, n in ((k_blocks[j], "k"), (v_blocks[j], "v")):
+            if t.shape != q_r.shape or t.dtype != q_r.dtype:
+                raise ValueError(f"{n}_blocks[{j}] must match q_r in shape and dtype")
+        for t, n in ((dk_blocks[j], "dk"), (dv_blocks[j], "dv")):
+            if t.shape != q_r.shape or t.dtype != torch.float32:
+                raise ValueError(f"{n}_blocks[{j}] must be fp32 of q_r's shape")
+        kp[j], vp[j] = _dev(k_blocks[j], "k").value, _dev(v_blocks[j], "v").value
+        dkp[j], dvp[j] = _dev(dk_blocks[j], "dk").value, _dev(dv_blocks[j], "dv").value
+    if dq.shape != q_r.shape or dq.dtype != torch.float32:
+        raise ValueError("dq must be fp32 of q_r's shape")
+    delta = torch.empty((B, Sb, H), **f32)
+    st = _load().ra_ring_attn_bwd(_dev(q_r, "q_r"), kp, vp, _dev(o_r, "o_r"), _dev(do_r, "do_r"),
+                                  _dev(lse_r, "lse_r"), B, Sb, H, D, P, rank, dt, float(scale),
+                                  int(causal), valid_len, _dev(dq, "dq"), dkp, dvp,
+                                  _dev(delta, "delta"), _stream(stream))
+    _check(st, "ra_ring_attn_bwd")
+    return dq, dk_blocks, dv_blocks
+
+
 def _perm(fn_name, x, out_shape, P, B, S, H, D, out, stream):
     torch = _torch()
     y = torch.empty(out_shape, dtype=x.dtype, device=x.device) if out is None else out
@@ -384,7 +436,7 @@ def ring_attn_composable(q_r, k_blocks, v_blocks, rank: int, *, causal: bool = F
 __all__ = [
     "lib", "abi_version", "set_attn_kernel", "get_attn_kernel", "padded_len", "shard_range", "classify_block", "ring_schedule",
     "block_attn_fwd", "ring_merge", "ring_attn_fwd", "seq2head", "head2seq",
-    "zigzag_padded_len", "zigzag_schedule", "zigzag_attn_fwd",
+    "zigzag_padded_len", "zigzag_schedule", "zigzag_attn_fwd", "ring_attn_bwd",
     "ring_attn_composable", "EXPORTED", "LIB_PATH", "LibraryMissing",
     "RA_BF16", "RA_FP32", "RA_SKIP", "RA_FULL", "RA_DIAG", "RA_MAX_P", "RA_PAD_MULTIPLE",
     "RA_KERNEL_AUTO", "RA_KERNEL_BR128", "RA_KERNEL_BR256", "RA_KERNEL_W64", "RA_KERNEL_WS",

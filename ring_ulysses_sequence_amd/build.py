@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libringattn.so")
 
-SOURCES = ["ra_host.cpp", "ra_attn.hip", "ra_merge.hip", "ra_permute.hip"]
+SOURCES = ["ra_host.cpp", "ra_attn.hip", "ra_attn_bwd.hip", "ra_merge.hip", "ra_permute.hip"]
 ARCH = "gfx950"
 
 

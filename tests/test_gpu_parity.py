@@ -443,6 +443,71 @@ def test_zigzag_long_context_ranks_0_and_7():
                                       np.concatenate(ref_l, 2)) <= LSE_BF16_ATOL
 
 
+# ------------------------------------------------------------ ring backward
+# Gradient tolerances (bf16 operands, fp32 accumulation): P and dS are
+# rounded to bf16 (relative 2^-9) before their matrix products, as O's P is
+# in the forward; against the fp64 oracle fed the same saved O and lse we
+# require cos > 0.999, rel-L2 < 1e-2 and max_abs_err <= 1e-2 * max|ref|
+# (the forward's absolute 1e-2 bound, scaled to the gradient's magnitude,
+# which grows with the number of rows a block is summed over).
+def check_grad(got, ref, what):
+    c = oracle.compare(got, ref)
+    scale = max(1.0, float(np.max(np.abs(ref))))
+    say(what, {k: f"{v:.3e}" for k, v in c.items()}, f"max|ref| {scale:.3e}")
+    assert np.all(np.isfinite(_f64(got)))
+    assert c["cos"] > 0.999, (what, c)
+    assert c["rel_l2"] < 1e-2, (what, c)
+    assert c["max_abs_err"] <= 1e-2 * scale, (what, c)
+
+
+@pytest.mark.parametrize("D,causal,pad", [(128, True, 0), (128, False, 0), (64, True, 37)])
+def test_ring_backward_all_ranks(D, causal, pad):
+    """Every rank's backward (dq, and its dk/dv parts of the blocks it
+    visits) against the oracle's ring backward fed the same saved O and
+    lse; then the parts summed over all ranks (accumulated into the same
+    buffers, as the ring returns them to the owners) against the
+    full-sequence gradients of the plain definition."""
+    B, S, H, P = 2, 1024, 3, 4
+    Sb = S // P
+    valid = S - pad
+    q, k, v, do = (W.random_tensor((B, S, H, D), seed=s_, device="cuda") for s_ in (31, 32, 33, 34))
+    if pad:
+        for x in (q, k, v, do):
+            x[:, valid:] = 0
+    kb, vb = blocks_of(k, P), blocks_of(v, P)
+    kc, vc = [x.cpu() for x in kb], [x.cpu() for x in vb]
+    dk_all = [torch.zeros((B, Sb, H, D), dtype=torch.float32, device="cuda") for _ in range(P)]
+    dv_all = [torch.zeros((B, Sb, H, D), dtype=torch.float32, device="cuda") for _ in range(P)]
+    dq_all = []
+    for r in range(P):
+        sl = slice(r * Sb, (r + 1) * Sb)
+        q_r, do_r = q[:, sl].contiguous(), do[:, sl].contiguous()
+        o_r, lse_r = ra.ring_attn_fwd(q_r, kb, vb, r, causal=causal, valid_len=valid)
+        say("ring bwd", D, causal, pad, "rank", r)
+        dq, dk, dv = ra.ring_attn_bwd(q_r, kb, vb, o_r, do_r, lse_r, r, causal=causal,
+                                      valid_len=valid)
+        ra.ring_attn_bwd(q_r, kb, vb, o_r, do_r, lse_r, r, causal=causal, valid_len=valid,
+                         dq=torch.zeros_like(dq), dk_blocks=dk_all, dv_blocks=dv_all)
+        torch.cuda.synchronize()
+        rq, rk, rv = oracle.ring_attention_bwd_rank(q_r.cpu(), kc, vc, do_r.cpu(), r,
+                                                    o_r=o_r.cpu(), lse_r=lse_r.cpu(),
+                                                    causal=causal, valid_len=valid)
+        check_grad(dq.cpu(), rq, f"dq r{r}")
+        for j in range(P):
+            if np.any(rk[j]):
+                check_grad(dk[j].cpu(), rk[j], f"dk r{r} block {j}")
+                check_grad(dv[j].cpu(), rv[j], f"dv r{r} block {j}")
+            else:
+                assert not dk[j].any() and not dv[j].any()
+        dq_all.append(dq.cpu())
+    fq, fk, fv = oracle.attention_grad(q.cpu(), k.cpu(), v.cpu(), do.cpu(), causal=causal,
+                                       valid_len=valid)
+    real = np.arange(valid)
+    check_grad(torch.cat(dq_all, 1)[:, real], fq[:, real], "dq all ranks vs full")
+    check_grad(torch.cat([x.cpu() for x in dk_all], 1)[:, real], fk[:, real], "dk owners vs full")
+    check_grad(torch.cat([x.cpu() for x in dv_all], 1)[:, real], fv[:, real], "dv owners vs full")
+
+
 # ------------------------------------------------------------ merge kernel
 def test_ring_merge_against_oracle():
     g = torch.Generator().manual_seed(5)

@@ -183,6 +183,19 @@ def test_device_entry_points_validate_before_launch(lib):
     st = lib.ra_zigzag_attn_fwd(null, arr, arr, 1, 128, 1, 64, 2, 0, ra.RA_BF16, 0.0, 1,
                                 -1, null, null, null)
     assert st == 1
+    # ring backward: fp32 inputs unsupported, D, rank, NULL buffers
+    st = lib.ra_ring_attn_bwd(null, arr, arr, null, null, null, 1, 16, 1, 64, 2, 0, ra.RA_FP32,
+                              0.0, 0, -1, null, arr, arr, null, null)
+    assert st == 5 and b"bf16" in lib.ra_last_error()
+    st = lib.ra_ring_attn_bwd(null, arr, arr, null, null, null, 1, 16, 1, 80, 2, 0, ra.RA_BF16,
+                              0.0, 0, -1, null, arr, arr, null, null)
+    assert st == 5
+    st = lib.ra_ring_attn_bwd(null, arr, arr, null, null, null, 1, 16, 1, 64, 2, 3, ra.RA_BF16,
+                              0.0, 0, -1, null, arr, arr, null, null)
+    assert st == 4
+    st = lib.ra_ring_attn_bwd(null, arr, arr, null, null, null, 1, 16, 1, 64, 2, 0, ra.RA_BF16,
+                              0.0, 0, -1, null, arr, arr, null, null)
+    assert st == 1
     # merge: unsupported D, unknown dtype
     st = lib.ra_ring_merge(null, null, null, null, 1, 4, 1, 12, null, ra.RA_FP32, null)
     assert st == 5
