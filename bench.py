@@ -181,6 +181,7 @@ def main():
     if not args.no_extra:
         extra = side_measurements(torch, ra, W, stream)
         extra.update(zigzag_measurements(torch, ra, W, stream, q, k, v))
+        extra.update(backward_measurement(torch, ra, W, stream, q_r, kb, vb, o, lse, flops))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -275,6 +276,41 @@ def side_measurements(torch, ra, W, stream):
                                   "frac_hbm": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3)}
     del x, y, z
     return out
+
+
+def backward_measurement(torch, ra, W, stream, q_r, kb, vb, o, lse, fwd_flops):
+    """The ring backward of the same rank-3 share (dq and the dk/dv parts of
+    the four visited blocks, accumulated into preallocated fp32 buffers).
+    Algorithmic FLOPs: 2.5x the forward's (five products of 2*D per visible
+    pair: the recomputed scores, dP, dV, dK, dQ)."""
+    do = W.random_tensor(q_r.shape, seed=41, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dq = torch.zeros(q_r.shape, **f32)
+    # blocks 4..7 are skipped (causal future) and their buffers never
+    # touched, so block 0's buffers stand in for them
+    dk = [torch.zeros(q_r.shape, **f32) for _ in range(4)]
+    dv = [torch.zeros(q_r.shape, **f32) for _ in range(4)]
+    dk += [dk[0]] * (len(kb) - 4)
+    dv += [dv[0]] * (len(kb) - 4)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def run():
+        ra.ring_attn_bwd(q_r, kb, vb, o, do, lse, 3, causal=True, dq=dq, dk_blocks=dk,
+                         dv_blocks=dv, stream=stream)
+    run()
+    torch.cuda.synchronize()
+    n = 3
+    a, b = ev(), ev()
+    a.record(stream)
+    for _ in range(n):
+        run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / n
+    fl = 2.5 * fwd_flops
+    return {"backward_long_rank3": {"ms": round(ms, 3), "flops": fl,
+                                    "tflops": round(fl / ms / 1e9, 2),
+                                    "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}}
 
 
 def zigzag_measurements(torch, ra, W, stream, q, k, v):

@@ -34,14 +34,14 @@ from .schedule import (SKIP, FULL, DIAG, padded_len, seq_divisible, shard_range,
                        classify_block, ring_schedule, visible_mask, zigzag_chunks,
                        zigzag_positions, zigzag_schedule, visible_pairs)
 from .permute import seq2head, head2seq, seq2head_loops, head2seq_loops
-from .grad import attention_grad, ring_attention_bwd_rank
+from .grad import attention_grad, attention_grad_sampled, ring_attention_bwd_rank
 from .compare import max_abs_err, cosine, rel_l2, compare
 
 __all__ = [
     "attention", "local_only_attention", "scores",
     "ring_attention_rank", "lse_combine", "composable_ring_rank", "chunked_attention",
     "zigzag_ring_rank", "zigzag_chunks", "zigzag_positions", "zigzag_schedule", "visible_pairs",
-    "attention_grad", "ring_attention_bwd_rank",
+    "attention_grad", "attention_grad_sampled", "ring_attention_bwd_rank",
     "SKIP", "FULL", "DIAG", "padded_len", "seq_divisible", "shard_range", "ring_sources",
     "classify_block", "ring_schedule", "visible_mask",
     "seq2head", "head2seq", "seq2head_loops", "head2seq_loops",

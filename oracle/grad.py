@@ -29,7 +29,8 @@ sum_j dV_j = sum_i dO_i (rows with a visible key); ``ring_attention_bwd_rank``
 by the ring decomposition (the owners' sums over all ranks equal the
 full-sequence gradients to fp64 rounding) and by two planted mistakes (parts
 returned to the wrong owner; probabilities from a block-local instead of the
-global log-sum-exp) that must fail (tests/test_oracle_pins.py).
+global log-sum-exp) that must fail; ``attention_grad_sampled`` by equality
+with the selected rows of ``attention_grad`` (tests/test_oracle_pins.py).
 """
 from __future__ import annotations
 
@@ -127,3 +128,46 @@ def ring_attention_bwd_rank(q_r, k_blocks, v_blocks, do_r, rank, *, o_r=None, ls
                 dk_parts[j][b, :, h] += scale * (ds.T @ q[b, :, h])
                 dv_parts[j][b, :, h] += p.T @ do[b, :, h]
     return dq, dk_parts, dv_parts
+
+
+def attention_grad_sampled(q, k, v, do, o, lse, *, q_rows, k_rows, scale=None, causal=False,
+                           q_pos0=0, k_pos0=0, valid_len=None):
+    """Selected rows of (dq, dk, dv) from the saved forward statistics.
+
+    Same gradients as ``attention_grad`` (P = exp(s - lse) over the visible
+    pairs, D = rowsum(dO * O)), evaluated only for the query rows ``q_rows``
+    (dq: each needs its scores against every key) and the key rows
+    ``k_rows`` (dk, dv: each needs its scores against every query), so that
+    a long share can be checked on a sample.  Returns (dq [B, |q_rows|, H, D],
+    dk [B, |k_rows|, H, D], dv [B, |k_rows|, H, D]).
+    """
+    q, k, v, do, o, lse = (_f64(x) for x in (q, k, v, do, o, lse))
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    if valid_len is None:
+        valid_len = np.iinfo(np.int64).max
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.asarray(k_rows, dtype=np.int64)
+    dsum = (do * o).sum(axis=3)                                   # [B, Sq, H]
+    lse_ref = np.where(np.isfinite(lse), lse, np.inf)            # no key seen: P = 0
+    dq = np.zeros((B, len(q_rows), H, D))
+    dk = np.zeros((B, len(k_rows), H, D))
+    dv = np.zeros((B, len(k_rows), H, D))
+    vis_q = visible_mask(q_pos0 + q_rows, k_pos0 + np.arange(Sk), causal, valid_len)
+    vis_k = visible_mask(q_pos0 + np.arange(Sq), k_pos0 + k_rows, causal, valid_len)
+    for b in range(B):
+        for h in range(H):
+            # rows: scores of the sampled queries against all keys
+            s = scale * (q[b, q_rows, h] @ k[b, :, h].T)
+            p = np.where(vis_q, np.exp(s - lse_ref[b, q_rows, h][:, None]), 0.0)
+            ds = p * (do[b, q_rows, h] @ v[b, :, h].T - dsum[b, q_rows, h][:, None])
+            dq[b, :, h] = scale * (ds @ k[b, :, h])
+            # columns: scores of all queries against the sampled keys
+            s = scale * (q[b, :, h] @ k[b, k_rows, h].T)
+            p = np.where(vis_k, np.exp(s - lse_ref[b, :, h][:, None]), 0.0)
+            ds = p * (do[b, :, h] @ v[b, k_rows, h].T - dsum[b, :, h][:, None])
+            dk[b, :, h] = scale * (ds.T @ q[b, :, h])
+            dv[b, :, h] = p.T @ do[b, :, h]
+    return dq, dk, dv

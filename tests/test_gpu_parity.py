@@ -508,6 +508,43 @@ def test_ring_backward_all_ranks(D, causal, pad):
     check_grad(torch.cat([x.cpu() for x in dv_all], 1)[:, real], fv[:, real], "dv owners vs full")
 
 
+def test_ring_backward_long_context_rank3():
+    """L = 131072, H = 64, P = 8, rank 3 (the bench share): dq on sampled
+    rows and dk / dv on sampled keys of the diagonal and the first block,
+    against the oracle evaluated from the same saved O and lse."""
+    w = W.LONG_CAUSAL
+    r, Sb = 3, w.block_len
+    say(w.name, "backward: generate on device")
+    q, k, v = W.make_qkv(w, device="cuda")
+    kb = [k[:, j * Sb:(j + 1) * Sb] for j in range(w.P)]
+    vb = [v[:, j * Sb:(j + 1) * Sb] for j in range(w.P)]
+    q_r = q[:, r * Sb:(r + 1) * Sb]
+    do_r = W.random_tensor(q_r.shape, seed=41, device="cuda")
+    o_r, lse_r = ra.ring_attn_fwd(q_r, kb, vb, r, causal=True)
+    say(w.name, "backward rank 3")
+    dq, dk, dv = ra.ring_attn_bwd(q_r, kb, vb, o_r, do_r, lse_r, r, causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq).all()
+    for j in range(r + 1, w.P):
+        assert not dk[j].any() and not dv[j].any()
+    q_rows = np.unique(np.concatenate([np.arange(0, Sb, 1024), [1, 63, 64, 127, Sb - 1]]))
+    k_local = np.array([0, 1, 63, 64, 5000, Sb - 2, Sb - 1])
+    heads = [0, 21, 42, 63]
+    kc = k[:, :(r + 1) * Sb].cpu()
+    vc = v[:, :(r + 1) * Sb].cpu()
+    qc, dc, oc, lc = q_r.cpu(), do_r.cpu(), o_r.cpu(), lse_r.cpu()
+    for j in (0, r):
+        for h in heads:
+            hs = slice(h, h + 1)
+            sq, sk, sv = oracle.attention_grad_sampled(
+                qc[:, :, hs], kc[:, :, hs], vc[:, :, hs], dc[:, :, hs], oc[:, :, hs], lc[:, :, hs],
+                q_rows=q_rows, k_rows=j * Sb + k_local, causal=True, q_pos0=r * Sb, k_pos0=0)
+            check_grad(dk[j][:, k_local, hs].cpu(), sk, f"dk block {j} head {h}")
+            check_grad(dv[j][:, k_local, hs].cpu(), sv, f"dv block {j} head {h}")
+            if j == r:
+                check_grad(dq[:, q_rows, hs].cpu(), sq, f"dq head {h}")
+
+
 # ------------------------------------------------------------ merge kernel
 def test_ring_merge_against_oracle():
     g = torch.Generator().manual_seed(5)

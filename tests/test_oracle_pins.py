@@ -629,3 +629,22 @@ def test_ring_backward_planted_mistakes_fail():
         local_dq.append(dq_bad)
     assert np.max(np.abs(np.concatenate(wrong_owner, 1) - dk)) > 1e-2
     assert np.max(np.abs(np.concatenate(local_dq, 1) - dq)) > 1e-2
+
+
+@pytest.mark.parametrize("causal,valid,q_pos0", [(True, None, 0), (False, 11, 0), (True, None, 4)])
+def test_grad_sampled_equals_full_rows(causal, valid, q_pos0):
+    """The sampled gradient (from saved o and lse) equals the selected rows
+    of the full closed form, with a query shard offset from the keys."""
+    rng = np.random.default_rng(8)
+    B, Sq, Sk, H, D = 2, 6, 13, 2, 5
+    q = rng.standard_normal((B, Sq, H, D))
+    k, v = (rng.standard_normal((B, Sk, H, D)) for _ in range(2))
+    do = rng.standard_normal((B, Sq, H, D))
+    kw = dict(causal=causal, valid_len=valid, q_pos0=q_pos0, k_pos0=0)
+    o, lse, _, _ = oracle.attention(q, k, v, **kw)
+    dq, dk, dv = oracle.attention_grad(q, k, v, do, **kw)
+    qr, kr = np.array([0, 3, 5]), np.array([1, 2, 7, 12])
+    sq, sk, sv = oracle.attention_grad_sampled(q, k, v, do, o, lse, q_rows=qr, k_rows=kr, **kw)
+    np.testing.assert_allclose(sq, dq[:, qr], atol=1e-12)
+    np.testing.assert_allclose(sk, dk[:, kr], atol=1e-12)
+    np.testing.assert_allclose(sv, dv[:, kr], atol=1e-12)
