@@ -172,7 +172,7 @@ struct TileAddr {
 // dQ (and D = rowsum(dO * O)): one workgroup per (batch, head, 128 rows)
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ring_attn_bwd_dq(const BwdArgs a) {
   constexpr int NC = D / 16, NDT = D / 32, ROWB = D * 2;
   using TS = TileStage<D>;
@@ -243,88 +243,93 @@ void ring_attn_bwd_dq(const BwdArgs a) {
   int cb = 0, ct = 0, cn = 0;
   while (cb < a.nblk && (cn = ntiles(cb)) == 0) ++cb;
 
-  TS sk, sv;
-  auto stage = [&](int bi, int ti) {
-    const BwdBlock& kb = a.blk[bi];
-    const long long off = (((long long)b * a.kv_rows_b + (long long)ti * kTile) * a.H + h) * D * 2;
-    const int rows = min(kTile, kb.len - ti * kTile);
-    sk.load((const char*)kb.k + off, rows, row_stride);
-    sv.load((const char*)kb.v + off, rows, row_stride);
+  // one staging register set, used for the next tile's K, then its V
+  TS st;
+  auto src_of = [&](int bi, int ti, const void* base) -> const char* {
+    return (const char*)base +
+           (((long long)b * a.kv_rows_b + (long long)ti * kTile) * a.H + h) * D * 2;
   };
   int buf = 0;
   if (cb < a.nblk) {
-    stage(cb, 0);
-    sk.store(smem[0]);
-    sv.store(smem[0] + TS::BYTES);
+    const int rows = min(kTile, a.blk[cb].len);
+    st.load(src_of(cb, 0, a.blk[cb].k), rows, row_stride);
+    st.store(smem[0]);
+    st.load(src_of(cb, 0, a.blk[cb].v), rows, row_stride);
+    st.store(smem[0] + TS::BYTES);
   }
   __syncthreads();
   const float c_scale = a.scale_log2;
   while (cb < a.nblk) {
-    // next tile's position and its loads (in flight during this tile)
+    // next tile's position; its K loads fly during the first half of this
+    // tile, its V loads during the second (the other buffer was last read
+    // in the previous iteration, before its closing barrier)
     int nb = cb, nt = ct + 1, nn = cn;
     if (nt >= nn) {
       nt = 0;
       ++nb;
       while (nb < a.nblk && (nn = ntiles(nb)) == 0) ++nb;
     }
-    if (nb < a.nblk) stage(nb, nt);
+    const bool more = nb < a.nblk;
+    const int nrows = more ? min(kTile, a.blk[nb].len - nt * kTile) : 0;
+    if (more) st.load(src_of(nb, nt, a.blk[nb].k), nrows, row_stride);
 
     const BwdBlock& kb = a.blk[cb];
     const long long kp0 = kb.k_pos0 + (long long)ct * kTile;
     const char* kt = smem[buf];
     const char* vt = smem[buf] + TS::BYTES;
-    if (wrows > 0 && !(a.causal && kp0 > wq_hi)) {
-      f32x16 s[2], dp[2];
+    const bool live = wrows > 0 && !(a.causal && kp0 > wq_hi);
+    // mask: key j of the tile (j = 32t + 8(v/4) + 4half + v%4) is hidden
+    // for this lane's query when j >= the keys left in the block or at or
+    // beyond valid_len, or (causal) when it lies after the query
+    long long lim_ll = kb.len - (long long)ct * kTile;
+    if (a.valid_len - kp0 < lim_ll) lim_ll = a.valid_len - kp0;
+    const bool need = lim_ll < kTile || (a.causal && kp0 + kTile - 1 > wq_lo);
+    long long lim = lim_ll;
+    if (a.causal) {
+      const long long rel = wq_lo + col - kp0 + 1;  // keys 0 .. rel-1 visible
+      if (rel < lim) lim = rel;
+    }
+    // as a 32-bit bound relative to this lane's first key of each group
+    const int lim_h = (int)(lim < 0 ? 0 : (lim > kTile ? kTile : lim)) - 4 * half;
+    // one 32-key half of the tile at a time (keeps two waves per SIMD)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        s[t] = f32x16{};
-        dp[t] = f32x16{};
+    for (int t = 0; t < 2; ++t) {
+      if (live) {
+        f32x16 sc = f32x16{}, dpt = f32x16{};
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.row(kt, t, c), qf[c], s[t], 0, 0, 0);
-          dp[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.row(vt, t, c), df[c], dp[t], 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.row(kt, t, c), qf[c], sc, 0, 0, 0);
+          dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.row(vt, t, c), df[c], dpt, 0, 0, 0);
+          // keep the operand reads next to their products (bounded live range)
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      // mask: key j of the tile (j = 32t + 8(v/4) + 4half + v%4) is hidden
-      // for this lane's query when j >= the keys left in the block or at or
-      // beyond valid_len, or (causal) when it lies after the query
-      long long lim_ll = kb.len - (long long)ct * kTile;
-      if (a.valid_len - kp0 < lim_ll) lim_ll = a.valid_len - kp0;
-      const bool need = lim_ll < kTile || (a.causal && kp0 + kTile - 1 > wq_lo);
-      if (need) {
-        long long lim = lim_ll;
-        if (a.causal) {
-          const long long rel = wq_lo + col - kp0 + 1;  // keys 0 .. rel-1 visible
-          if (rel < lim) lim = rel;
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
+        if (need) {
 #pragma unroll
           for (int v = 0; v < 16; ++v)
-            if (32 * t + 8 * (v >> 2) + 4 * half + (v & 3) >= lim) s[t][v] = -INFINITY;
-      }
-      // dS^T = P^T (dP^T - D), packed as the B operand of K^T dS^T
-      bf16x8 dsb[4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
+            if (32 * t + 8 * (v >> 2) + (v & 3) >= lim_h) sc[v] = -INFINITY;
+        }
+        // dS^T = P^T (dP^T - D), packed as the B operand of K^T dS^T
+        bf16x8 dsb[2];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f(s[t][v] * c_scale - lse2);
-          dsb[2 * t + (v >> 3)][v & 7] = (__bf16)(p * (dp[t][v] - dsum));
+          const float p = __builtin_amdgcn_exp2f(sc[v] * c_scale - lse2);
+          dsb[v >> 3][v & 7] = (__bf16)(p * (dpt[v] - dsum));
         }
 #pragma unroll
-      for (int G = 0; G < 4; ++G)
+        for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.tr(kt, G, dt), dsb[G], acc[dt],
-                                                            0, 0, 0);
+          for (int dt = 0; dt < NDT; ++dt) {
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.tr(kt, 2 * t + g, dt), dsb[g],
+                                                              acc[dt], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
+      if (t == 0 && more) {
+        st.store(smem[buf ^ 1]);
+        st.load(src_of(nb, nt, a.blk[nb].v), nrows, row_stride);
+      }
     }
-    // the other buffer was last read in the previous iteration, before its
-    // closing barrier
-    if (nb < a.nblk) {
-      sk.store(smem[buf ^ 1]);
-      sv.store(smem[buf ^ 1] + TS::BYTES);
-    }
+    if (more) st.store(smem[buf ^ 1] + TS::BYTES);
     __syncthreads();
     buf ^= 1;
     cb = nb;
@@ -406,13 +411,13 @@ void ring_attn_bwd_dkv(const BwdArgs a) {
   if (a.causal && k_lo > a.q_pos0) t0 = (int)min((long long)a.Sq, (k_lo - a.q_pos0) / kTile);
   const int n_t = (a.Sq + kTile - 1) / kTile;
 
-  TS sq, sd;
+  // one staging register set, used for the next tile's Q, then its dO
+  TS st;
   float stat = 0.0f;  // one lse2 (threads 0-63) or D (64-127) value
-  auto stage = [&](int ti) {
-    const long long off = (((long long)b * a.Sq + (long long)ti * kTile) * a.H + h) * D * 2;
-    const int rows = min(kTile, a.Sq - ti * kTile);
-    sq.load((const char*)a.q + off, rows, row_stride);
-    sd.load((const char*)a.dout + off, rows, row_stride);
+  auto src_of = [&](int ti, const void* base) -> const char* {
+    return (const char*)base + (((long long)b * a.Sq + (long long)ti * kTile) * a.H + h) * D * 2;
+  };
+  auto load_stat = [&](int ti) {
     if (tid < 2 * kTile) {
       const int rr = ti * kTile + (tid & (kTile - 1));
       const long long so = ((long long)b * a.Sq + rr) * a.H + h;
@@ -425,44 +430,57 @@ void ring_attn_bwd_dkv(const BwdArgs a) {
       }
     }
   };
-  auto put = [&](char* dst) {
-    sq.store(dst);
-    sd.store(dst + TS::BYTES);
+  auto put_stat = [&](char* dst) {
     if (tid < 2 * kTile) ((float*)(dst + 2 * TS::BYTES))[tid] = stat;
   };
   int buf = 0;
   if (t0 < n_t) {
-    stage(t0);
-    put(smem[0]);
+    const int rows = min(kTile, a.Sq - t0 * kTile);
+    st.load(src_of(t0, a.q), rows, row_stride);
+    st.store(smem[0]);
+    st.load(src_of(t0, a.dout), rows, row_stride);
+    st.store(smem[0] + TS::BYTES);
+    load_stat(t0);
+    put_stat(smem[0]);
   }
   __syncthreads();
   const float c_scale = a.scale_log2;
   for (int ti = t0; ti < n_t; ++ti) {
-    if (ti + 1 < n_t) stage(ti + 1);
+    // next tile: its Q loads fly during the first half of this tile, its dO
+    // loads during the second (the other buffer was last read in the
+    // previous iteration, before its closing barrier)
+    const bool more = ti + 1 < n_t;
+    const int nrows = more ? min(kTile, a.Sq - (ti + 1) * kTile) : 0;
+    if (more) {
+      st.load(src_of(ti + 1, a.q), nrows, row_stride);
+      load_stat(ti + 1);
+    }
     const char* qt = smem[buf];
     const char* dt_ = smem[buf] + TS::BYTES;
     const float* ls = (const float*)(smem[buf] + 2 * TS::BYTES);
     const float* ds_ = ls + kTile;
     const long long qp0 = a.q_pos0 + (long long)ti * kTile;
     const long long qp_hi = qp0 + min(kTile, a.Sq - ti * kTile) - 1;
-    if (!(a.causal && kw_lo > qp_hi) && kw_lo < a.valid_len) {
-      f32x16 s[2], dp[2];
+    const bool live = !(a.causal && kw_lo > qp_hi) && kw_lo < a.valid_len;
+    // element (query m = 32t + 8g + 4half + i of the tile, this lane's key)
+    // is hidden when the key is padding or (causal) after the query, i.e.
+    // m < rel with rel = key - first query of the tile (32-bit, clamped)
+    const bool need = kw_hi >= a.valid_len || (a.causal && kw_hi > qp0);
+    int rel = 0;
+    if (kpos >= a.valid_len) rel = kTile;
+    else if (a.causal) rel = (int)max(0LL, min((long long)kTile, kpos - qp0));
+    const int rel_h = rel - 4 * half;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        s[t] = f32x16{};
-        dp[t] = f32x16{};
+    for (int t = 0; t < 2; ++t) {
+      if (live) {
+        f32x16 sc = f32x16{}, dpt = f32x16{};
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.row(qt, t, c), kf[c], s[t], 0, 0, 0);
-          dp[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.row(dt_, t, c), vf[c], dp[t], 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.row(qt, t, c), kf[c], sc, 0, 0, 0);
+          dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.row(dt_, t, c), vf[c], dpt, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      // element (query m = 32t + 8(v/4) + 4half + v%4, this lane's key):
-      // hidden when the key is padding or (causal) after the query
-      const bool need = kw_hi >= a.valid_len || (a.causal && kw_hi > qp0);
-      bf16x8 pb[4], sb[4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
+        bf16x8 pb[2], sb[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int m0 = 32 * t + 8 * g + 4 * half;
@@ -473,23 +491,33 @@ void ring_attn_bwd_dkv(const BwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int v = 4 * g + i;
-            float x = s[t][v] * c_scale - lv[i];
-            if (need && (kpos >= a.valid_len || (a.causal && kpos > qp0 + m0 + i))) x = -INFINITY;
+            float x = sc[v] * c_scale - lv[i];
+            if (need && 32 * t + 8 * g + i < rel_h) x = -INFINITY;
             const float p = __builtin_amdgcn_exp2f(x);
-            const int G = 2 * t + (v >> 3), e = v & 7;
-            pb[G][e] = (__bf16)p;
-            sb[G][e] = (__bf16)(p * (dp[t][v] - dv4[i]));
+            pb[v >> 3][v & 7] = (__bf16)p;
+            sb[v >> 3][v & 7] = (__bf16)(p * (dpt[v] - dv4[i]));
           }
         }
 #pragma unroll
-      for (int G = 0; G < 4; ++G)
+        for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int d = 0; d < NDT; ++d) {
-          dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.tr(dt_, G, d), pb[G], dv[d], 0, 0, 0);
-          dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.tr(qt, G, d), sb[G], dk[d], 0, 0, 0);
-        }
+          for (int d = 0; d < NDT; ++d) {
+            dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.tr(dt_, 2 * t + g, d), pb[g], dv[d],
+                                                            0, 0, 0);
+            dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.tr(qt, 2 * t + g, d), sb[g], dk[d],
+                                                            0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
+      if (t == 0 && more) {
+        st.store(smem[buf ^ 1]);
+        st.load(src_of(ti + 1, a.dout), nrows, row_stride);
+      }
     }
-    if (ti + 1 < n_t) put(smem[buf ^ 1]);
+    if (more) {
+      st.store(smem[buf ^ 1] + TS::BYTES);
+      put_stat(smem[buf ^ 1]);
+    }
     __syncthreads();
     buf ^= 1;
   }
