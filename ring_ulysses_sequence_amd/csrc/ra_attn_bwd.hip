@@ -23,10 +23,11 @@
 //     K/V rows in LDS, then dQ^T += K^T dS^T with K^T read transposed
 //     (ds_read_b64_tr_b16) and dS^T from registers -- the forward's P V step
 //     with V replaced by K.  It also writes D_r for the second kernel.
-//   ring_attn_bwd_dkv<D>: one workgroup per 128 keys of one visited block
-//     (4 waves x 32 keys).  Each lane holds one key column: S = Q K^T and
-//     dP = dO V^T from Q/dO rows in LDS, then dV^T += dO^T P and
-//     dK^T += Q^T dS with dO^T and Q^T read transposed.
+//   ring_attn_bwd_dkv<D, PART>: one workgroup per 128 keys of one visited
+//     block (4 waves x 32 keys).  Each lane holds one key column: S = Q K^T
+//     (and, for dK, dP = dO V^T) from Q/dO rows in LDS, then dV^T += dO^T P
+//     (PART 0) or dK^T += Q^T dS (PART 1) with dO^T / Q^T read transposed.
+//     Two launches rather than one so that each fits two waves per SIMD.
 // Tiles (64 rows) are staged through registers: the next tile's global
 // loads are issued before the current tile is computed and written to the
 // other LDS buffer after it, one barrier per tile.
@@ -358,8 +359,10 @@ void ring_attn_bwd_dq(const BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per (visited block, batch, head, 128 keys)
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// PART 0 accumulates dV (needs S only), PART 1 dK (needs S and dP): split so
+// that each fits two waves per SIMD; the scores are recomputed in both.
+template <int D, int PART>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ring_attn_bwd_dkv(const BwdArgs a) {
   constexpr int NC = D / 16, NDT = D / 32;
   using TS = TileStage<D>;
@@ -386,7 +389,8 @@ void ring_attn_bwd_dkv(const BwdArgs a) {
   const long long kpos = kb.k_pos0 + kr;
   const long long kw_lo = kb.k_pos0 + kt * kRows + wave * 32;
   const long long kw_hi = kw_lo + 31;
-  bf16x8 kf[NC], vf[NC];
+  constexpr bool DK = PART == 1;
+  bf16x8 kf[NC], vf[DK ? NC : 1];
   {
     const long long off = ((long long)b * a.kv_rows_b + kr) * HD + (long long)h * D;
     const __bf16* kp = (const __bf16*)kb.k + off;
@@ -395,14 +399,14 @@ void ring_attn_bwd_dkv(const BwdArgs a) {
     for (int c = 0; c < NC; ++c) {
       const int d = 16 * c + 8 * half;
       kf[c] = key_ok ? *(const bf16x8*)(kp + d) : bf16x8{};
-      vf[c] = key_ok ? *(const bf16x8*)(vp + d) : bf16x8{};
+      if constexpr (DK) vf[c] = key_ok ? *(const bf16x8*)(vp + d) : bf16x8{};
     }
   }
   TileAddr<D> ad;
   ad.init(lane);
-  f32x16 dk[NDT], dv[NDT];
+  f32x16 acc[NDT];  // dK^T (PART 1) or dV^T (PART 0)
 #pragma unroll
-  for (int i = 0; i < NDT; ++i) dk[i] = dv[i] = f32x16{};
+  for (int i = 0; i < NDT; ++i) acc[i] = f32x16{};
 
   // query tiles that can see a key of this workgroup (causal: from the one
   // holding position k_lo on)
@@ -477,7 +481,8 @@ void ring_attn_bwd_dkv(const BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.row(qt, t, c), kf[c], sc, 0, 0, 0);
-          dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.row(dt_, t, c), vf[c], dpt, 0, 0, 0);
+          if constexpr (DK)
+            dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.row(dt_, t, c), vf[c], dpt, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
         bf16x8 pb[2], sb[2];
@@ -494,18 +499,21 @@ void ring_attn_bwd_dkv(const BwdArgs a) {
             float x = sc[v] * c_scale - lv[i];
             if (need && 32 * t + 8 * g + i < rel_h) x = -INFINITY;
             const float p = __builtin_amdgcn_exp2f(x);
-            pb[v >> 3][v & 7] = (__bf16)p;
-            sb[v >> 3][v & 7] = (__bf16)(p * (dpt[v] - dv4[i]));
+            if constexpr (DK) sb[v >> 3][v & 7] = (__bf16)(p * (dpt[v] - dv4[i]));
+            else pb[v >> 3][v & 7] = (__bf16)p;
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
           for (int d = 0; d < NDT; ++d) {
-            dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.tr(dt_, 2 * t + g, d), pb[g], dv[d],
-                                                            0, 0, 0);
-            dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.tr(qt, 2 * t + g, d), sb[g], dk[d],
-                                                            0, 0, 0);
+            if constexpr (DK)
+              acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.tr(qt, 2 * t + g, d), sb[g],
+                                                               acc[d], 0, 0, 0);
+            else
+              acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.tr(dt_, 2 * t + g, d), pb[g],
+                                                               acc[d], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
           }
       }
@@ -524,25 +532,19 @@ void ring_attn_bwd_dkv(const BwdArgs a) {
 
   if (key_ok) {
     const long long off = ((long long)b * a.kv_rows_b + kr) * HD + (long long)h * D;
-    float* dkp = kb.dk + off;
-    float* dvp = kb.dv + off;
+    float* dst = (DK ? kb.dk : kb.dv) + off;
+    const float f = DK ? a.scale : 1.0f;
 #pragma unroll
     for (int d = 0; d < NDT; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int f = 32 * d + 8 * g + 4 * half;
-        float4 x = *(float4*)(dkp + f);
-        x.x += a.scale * dk[d][4 * g + 0];
-        x.y += a.scale * dk[d][4 * g + 1];
-        x.z += a.scale * dk[d][4 * g + 2];
-        x.w += a.scale * dk[d][4 * g + 3];
-        *(float4*)(dkp + f) = x;
-        float4 y = *(float4*)(dvp + f);
-        y.x += dv[d][4 * g + 0];
-        y.y += dv[d][4 * g + 1];
-        y.z += dv[d][4 * g + 2];
-        y.w += dv[d][4 * g + 3];
-        *(float4*)(dvp + f) = y;
+        float4* p = (float4*)(dst + 32 * d + 8 * g + 4 * half);
+        float4 x = *p;
+        x.x += f * acc[d][4 * g + 0];
+        x.y += f * acc[d][4 * g + 1];
+        x.z += f * acc[d][4 * g + 2];
+        x.w += f * acc[d][4 * g + 3];
+        *p = x;
       }
   }
 }
@@ -621,8 +623,14 @@ extern "C" ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_bloc
   if (D == 128) hipLaunchKernelGGL(ring_attn_bwd_dq<128>, dim3((unsigned)n_dq), dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL(ring_attn_bwd_dq<64>, dim3((unsigned)n_dq), dim3(kThreads), 0, s, a);
   if (n_dkv > 0) {
-    if (D == 128) hipLaunchKernelGGL(ring_attn_bwd_dkv<128>, dim3((unsigned)n_dkv), dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL(ring_attn_bwd_dkv<64>, dim3((unsigned)n_dkv), dim3(kThreads), 0, s, a);
+    const dim3 g((unsigned)n_dkv);
+    if (D == 128) {
+      hipLaunchKernelGGL((ring_attn_bwd_dkv<128, 0>), g, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((ring_attn_bwd_dkv<128, 1>), g, dim3(kThreads), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((ring_attn_bwd_dkv<64, 0>), g, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((ring_attn_bwd_dkv<64, 1>), g, dim3(kThreads), 0, s, a);
+    }
   }
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess)
