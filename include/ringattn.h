@@ -198,6 +198,18 @@ ra_status ra_ring_attn_fwd(const void* q_r, const void* const* k_blocks,
                            int causal, long long valid_len, void* o,
                            float* lse_opt, void* stream);
 
+/* Grouped-query form of ra_ring_attn_fwd ([RA] §3.5 and §6 name GQA, where
+ * fewer K/V heads than query heads serve groups of query heads): q_r is
+ * [B,Sb,H,D], every k_blocks[j] / v_blocks[j] is [B,Sb,H_kv,D], and query
+ * head h attends with K/V head h / (H / H_kv).  H_kv = H is the plain ring,
+ * H_kv = 1 multi-query attention.  RA_ERR_SHAPE unless H_kv > 0 divides H;
+ * everything else as ra_ring_attn_fwd. */
+ra_status ra_ring_attn_fwd_gqa(const void* q_r, const void* const* k_blocks,
+                               const void* const* v_blocks, int B, int Sb, int H,
+                               int H_kv, int D, int P, int rank, ra_dtype dt,
+                               float scale, int causal, long long valid_len,
+                               void* o, float* lse_opt, void* stream);
+
 /* The whole ring of rank `rank` over zigzag shares in one launch ([RA]
  * §3.2-§3.4 with the sharding of ra_zigzag_schedule).  q_r [B,Sr,H,D] is
  * the rank's share: rows [0, Sr/2) are chunk rank (global rows

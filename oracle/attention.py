@@ -24,7 +24,10 @@ Parity: pinned -- by the tutorial's printed 4 x 2 worked example (§04),
 by torch's fp64 CPU scaled_dot_product_attention on full non-causal inputs,
 by the prefix-mean closed form with equal keys (causal, global positions),
 by constant-V and +1000-shift invariances, and by a pure-Python brute force
-on tiny inputs (tests/test_oracle_pins.py).
+on tiny inputs (tests/test_oracle_pins.py).  ``gqa_expand`` (the K/V head a
+query head reads under grouped-query attention) is pinned by the identity at
+H_kv = H, by a per-head loop over the head map, and by the multi-query
+invariances (tests/test_oracle_pins.py).
 """
 from __future__ import annotations
 
@@ -113,3 +116,15 @@ def local_only_attention(q_r, k_r, v_r, *, scale=None, causal=False,
     o, _, _, _ = attention(q_r, k_r, v_r, scale=scale, causal=causal,
                            q_pos0=pos0, k_pos0=pos0, valid_len=valid_len)
     return o
+
+
+def gqa_expand(x, H):
+    """K or V [B, S, H_kv, D] seen by H query heads: query head h reads K/V
+    head h // (H / H_kv) (grouped-query attention, named by the Ring
+    Attention tutorial §3.5 and §6 as the case with fewer K/V heads than
+    query heads).  Returns [B, S, H, D]; H_kv = H is the identity."""
+    x = _f64(x)
+    Hkv = x.shape[2]
+    if Hkv <= 0 or H % Hkv:
+        raise ValueError(f"{H} query heads are not a multiple of {Hkv} K/V heads")
+    return x[:, :, np.arange(H) // (H // Hkv)]

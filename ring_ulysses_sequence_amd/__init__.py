@@ -42,6 +42,7 @@ EXPORTED = (
     "ra_classify_block", "ra_ring_schedule", "ra_block_attn_fwd",
     "ra_ring_merge", "ra_ring_attn_fwd", "ra_seq2head", "ra_head2seq",
     "ra_zigzag_padded_len", "ra_zigzag_schedule", "ra_zigzag_attn_fwd", "ra_ring_attn_bwd",
+    "ra_ring_attn_fwd_gqa",
 )
 
 _lib = None
@@ -86,6 +87,9 @@ def _load():
         "ra_zigzag_attn_fwd": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp),
                                        c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                        c_float, c_int, c_ll, c_vp, c_vp, c_vp]),
+        "ra_ring_attn_fwd_gqa": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp),
+                                         c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                         c_float, c_int, c_ll, c_vp, c_vp, c_vp]),
         "ra_ring_attn_bwd": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp, c_vp,
                                      c_vp, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                      c_float, c_int, c_ll, c_vp, ctypes.POINTER(c_vp),
@@ -259,7 +263,9 @@ def ring_merge(o_acc, lse_acc, o_blk, lse_blk, *, out_final=None, stream=None):
 def ring_attn_fwd(q_r, k_blocks: Sequence, v_blocks: Sequence, rank: int, *,
                   causal: bool = False, valid_len: int = -1, scale: float = 0.0,
                   want_lse: bool = True, out=None, lse_out=None, stream=None):
-    """Rank ``rank``'s whole ring in one launch: (o [B,Sb,H,D] in q's dtype, lse)."""
+    """Rank ``rank``'s whole ring in one launch: (o [B,Sb,H,D] in q's dtype, lse).
+    K/V blocks with fewer heads than q_r (a divisor of H) select the grouped-query
+    form: query head h reads K/V head h / (H / H_kv)."""
     torch = _torch()
     B, Sb, H, D = q_r.shape
     P = len(k_blocks)
@@ -268,12 +274,14 @@ def ring_attn_fwd(q_r, k_blocks: Sequence, v_blocks: Sequence, rank: int, *,
     if P > RA_MAX_P:
         raise RuntimeError(f"P={P} exceeds {RA_MAX_P}")
     dt = _dtype_code(q_r)
-    kp = (ctypes.c_void_p * P)()
-    vp = (ctypes.c_void_p * P)()
+    Hkv = k_blocks[0].shape[2] if P else H
+    kv_shape = (B, Sb, Hkv, D)
+    kp = (ctypes.c_void_p * max(P, 1))()
+    vp = (ctypes.c_void_p * max(P, 1))()
     for j in range(P):
         for t, n in ((k_blocks[j], "k"), (v_blocks[j], "v")):
-            if t.shape != q_r.shape or t.dtype != q_r.dtype:
-                raise ValueError(f"{n}_blocks[{j}] must match q_r in shape and dtype")
+            if tuple(t.shape) != kv_shape or t.dtype != q_r.dtype:
+                raise ValueError(f"{n}_blocks[{j}] must be {kv_shape} of q_r's dtype")
         kp[j] = k_blocks[j].data_ptr()
         vp[j] = v_blocks[j].data_ptr()
         _dev(k_blocks[j], f"k_blocks[{j}]"), _dev(v_blocks[j], f"v_blocks[{j}]")
@@ -281,11 +289,15 @@ def ring_attn_fwd(q_r, k_blocks: Sequence, v_blocks: Sequence, rank: int, *,
     lse = lse_out
     if lse is None and want_lse:
         lse = torch.empty((B, Sb, H), dtype=torch.float32, device=q_r.device)
-    st = _load().ra_ring_attn_fwd(_dev(q_r, "q_r"), kp, vp, B, Sb, H, D, P, rank, dt,
-                                  float(scale), int(causal), valid_len, _dev(o, "o"),
-                                  _dev(lse, "lse") if lse is not None else None,
-                                  _stream(stream))
-    _check(st, "ra_ring_attn_fwd")
+    args = (float(scale), int(causal), valid_len, _dev(o, "o"),
+            _dev(lse, "lse") if lse is not None else None, _stream(stream))
+    if Hkv == H:
+        st = _load().ra_ring_attn_fwd(_dev(q_r, "q_r"), kp, vp, B, Sb, H, D, P, rank, dt, *args)
+        _check(st, "ra_ring_attn_fwd")
+    else:
+        st = _load().ra_ring_attn_fwd_gqa(_dev(q_r, "q_r"), kp, vp, B, Sb, H, Hkv, D, P, rank,
+                                          dt, *args)
+        _check(st, "ra_ring_attn_fwd_gqa")
     return o, lse
 
 

@@ -63,6 +63,8 @@ struct AttnArgs {
   long long q_pos1;
   int q_split;
   int kv_rows_b;       // rows between consecutive batches in every K/V buffer
+  int Hkv;             // K/V heads (H % Hkv == 0): query head h reads K/V head
+                       // h / (H / Hkv)
   long long valid_len; // keys at global positions >= valid_len are padding
   int B, Sq, H;
   int n_qtiles;
@@ -580,9 +582,9 @@ __device__ __forceinline__ void pipeline_step(
   const bool copy2 = t2.blk < a.nblk;
   if (copy2) {
     const KVBlock& kb2 = a.blk[t2.blk];
-    copy_tile<D, NW>(kb2.k, kb2.len, a.kv_rows_b, t2.t, b, h, a.H, HD2, wave, w.voffk,
+    copy_tile<D, NW>(kb2.k, kb2.len, a.kv_rows_b, t2.t, b, h, a.Hkv, HD2, wave, w.voffk,
                  smem + C::KB + PAR * C::TILE);
-    copy_tile<D, NW>(kb2.v, kb2.len, a.kv_rows_b, t2.t, b, h, a.H, HD2, wave, w.voffv,
+    copy_tile<D, NW>(kb2.v, kb2.len, a.kv_rows_b, t2.t, b, h, a.Hkv, HD2, wave, w.voffv,
                  smem + C::VB + vb2 * C::TILE);
   }
   bf16x8 pb[C::NS / 8];
@@ -618,9 +620,9 @@ __device__ __forceinline__ void pp_step(
   const bool copy2 = grp == 0 && t2.blk < a.nblk;
   if (copy2) {
     const KVBlock& kb2 = a.blk[t2.blk];
-    copy_tile<D, 4>(kb2.k, kb2.len, a.kv_rows_b, t2.t, b, h, a.H, HD2, gw, voffk4,
+    copy_tile<D, 4>(kb2.k, kb2.len, a.kv_rows_b, t2.t, b, h, a.Hkv, HD2, gw, voffk4,
                     smem + C::KB + PAR * C::TILE);
-    copy_tile<D, 4>(kb2.v, kb2.len, a.kv_rows_b, t2.t, b, h, a.H, HD2, gw, voffv4,
+    copy_tile<D, 4>(kb2.v, kb2.len, a.kv_rows_b, t2.t, b, h, a.Hkv, HD2, gw, voffv4,
                     smem + C::VB + ((vb + 2) & 3) * C::TILE);
   }
   bf16x8 pb[C::NS / 8];
@@ -663,7 +665,8 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   const long long wq_lo = qpos(a, wrow0);
   const long long wq_hi = wq_lo + wrows - 1;
   const long long HD = (long long)a.H * D;
-  const int HD2 = a.H * D * 2;  // bytes between consecutive key rows
+  const int HD2 = a.Hkv * D * 2;  // bytes between consecutive key rows
+  const int hk = h / (a.H / a.Hkv);  // K/V head of this query head
 
   WaveState<D, NW> w;
   {
@@ -718,16 +721,16 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   f32x16 sA[2], sB[2];
   if (t0.blk < a.nblk) {
     const KVBlock& kb = a.blk[t0.blk];
-    copy_tile<D, NW>(kb.k, kb.len, a.kv_rows_b, t0.t, b, h, a.H, HD2, wave, w.voffk,
+    copy_tile<D, NW>(kb.k, kb.len, a.kv_rows_b, t0.t, b, hk, a.Hkv, HD2, wave, w.voffk,
                      smem + C::KB);
-    copy_tile<D, NW>(kb.v, kb.len, a.kv_rows_b, t0.t, b, h, a.H, HD2, wave, w.voffv,
+    copy_tile<D, NW>(kb.v, kb.len, a.kv_rows_b, t0.t, b, hk, a.Hkv, HD2, wave, w.voffv,
                      smem + C::VB);
   }
   if (t1.blk < a.nblk) {
     const KVBlock& kb = a.blk[t1.blk];
-    copy_tile<D, NW>(kb.k, kb.len, a.kv_rows_b, t1.t, b, h, a.H, HD2, wave, w.voffk,
+    copy_tile<D, NW>(kb.k, kb.len, a.kv_rows_b, t1.t, b, hk, a.Hkv, HD2, wave, w.voffk,
                      smem + C::KB + C::TILE);
-    copy_tile<D, NW>(kb.v, kb.len, a.kv_rows_b, t1.t, b, h, a.H, HD2, wave, w.voffv,
+    copy_tile<D, NW>(kb.v, kb.len, a.kv_rows_b, t1.t, b, hk, a.Hkv, HD2, wave, w.voffv,
                      smem + C::VB + C::TILE);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -742,18 +745,18 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   if constexpr (PP) {
     while (t0.blk < a.nblk) {
       pp_step<D, 0>(a, smem, w, sA, sB, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows, col, half, b,
-                    h, HD2, gw, grp, voffk4, voffv4);
+                    hk, HD2, gw, grp, voffk4, voffv4);
       if (t0.blk >= a.nblk) break;
       pp_step<D, 1>(a, smem, w, sB, sA, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows, col, half, b,
-                    h, HD2, gw, grp, voffk4, voffv4);
+                    hk, HD2, gw, grp, voffk4, voffv4);
     }
   } else {
     while (t0.blk < a.nblk) {
       pipeline_step<D, NW, 0>(a, smem, w, sA, sB, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows,
-                              col, half, b, h, HD2, wave);
+                              col, half, b, hk, HD2, wave);
       if (t0.blk >= a.nblk) break;
       pipeline_step<D, NW, 1>(a, smem, w, sB, sA, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows,
-                              col, half, b, h, HD2, wave);
+                              col, half, b, hk, HD2, wave);
     }
   }
 
@@ -1288,7 +1291,8 @@ void ring_attn_bf16_w64(const AttnArgs a) {
   const bool causal = a.causal != 0;
   const long long HD = (long long)a.H * D;
   const int D2 = D * 2;
-  const int HD2 = a.H * D2;
+  const int HD2 = a.Hkv * D2;
+  const int hk = h / (a.H / a.Hkv);  // K/V head of this query head
 
   W64State<D> w;
 #pragma unroll
@@ -1333,10 +1337,10 @@ void ring_attn_bf16_w64(const AttnArgs a) {
   const unsigned vdst0 = smem_lds + C::VB + wave * C::DMA * 1024;
 
   // prologue: stages 0..2 of K, 0..1 of V; scores of sub-tile 0
-  Stage t0 = stage_enter(a, 0, q_hi, b, h, D2, HD2);
-  Stage t1 = stage_next(a, t0, q_hi, b, h, D2, HD2);
-  Stage t2 = stage_next(a, t1, q_hi, b, h, D2, HD2);
-  Stage t3 = stage_next(a, t2, q_hi, b, h, D2, HD2);
+  Stage t0 = stage_enter(a, 0, q_hi, b, hk, D2, HD2);
+  Stage t1 = stage_next(a, t0, q_hi, b, hk, D2, HD2);
+  Stage t2 = stage_next(a, t1, q_hi, b, hk, D2, HD2);
+  Stage t3 = stage_next(a, t2, q_hi, b, hk, D2, HD2);
   if (t0.blk < a.nblk) {
     copy_stage<D>(t0.k, t0.rows, HD2, w.voffk, kdst0);
     copy_stage<D>(t0.v, t0.rows, HD2, w.voffv, vdst0);
@@ -1400,7 +1404,7 @@ void ring_attn_bf16_w64(const AttnArgs a) {
     t0 = t1;
     t1 = t2;
     t2 = t3;
-    t3 = stage_next(a, t3, q_hi, b, h, D2, HD2);
+    t3 = stage_next(a, t3, q_hi, b, hk, D2, HD2);
     kb0 = (kb0 + 1) & 3;
     vb0 = vb0 == 2 ? 0 : vb0 + 1;
   }
@@ -1730,7 +1734,8 @@ void ring_attn_bf16_ws(const AttnArgs a) {
   const bool causal = a.causal != 0;
   const long long HD = (long long)a.H * D;
   const int D2 = D * 2;
-  const int HD2 = a.H * D2;
+  const int HD2 = a.Hkv * D2;
+  const int hk = h / (a.H / a.Hkv);  // K/V head of this query head
   const unsigned smem_lds = (unsigned)(size_t)(lds_void_ptr)smem;
   // copy slots: producers copy K stages, consumers V stages
   int voff[C::DMA];
@@ -1744,9 +1749,9 @@ void ring_attn_bf16_ws(const AttnArgs a) {
   char* const p_base = smem + C::PB + pair * C::PBUF;
   char* const a_base = smem + C::AB + pair * C::ASLOT;
 
-  Stage c0 = stage_enter(a, 0, q_hi, b, h, D2, HD2);    // stage n
-  Stage c1 = stage_next(a, c0, q_hi, b, h, D2, HD2);    // n + 1
-  Stage c2 = stage_next(a, c1, q_hi, b, h, D2, HD2);    // n + 2
+  Stage c0 = stage_enter(a, 0, q_hi, b, hk, D2, HD2);    // stage n
+  Stage c1 = stage_next(a, c0, q_hi, b, hk, D2, HD2);    // n + 1
+  Stage c2 = stage_next(a, c1, q_hi, b, hk, D2, HD2);    // n + 2
   // prologue copies: K(0), K(1) by the producers, V(0) by the consumers
   if (producer) {
     if (c0.blk < a.nblk) copy_stage<D>(c0.k, c0.rows, HD2, voff, cdst0);
@@ -1814,7 +1819,7 @@ void ring_attn_bf16_ws(const AttnArgs a) {
       pipeline_barrier();
       c0 = c1;
       c1 = c2;
-      c2 = stage_next(a, c2, q_hi, b, h, D2, HD2);
+      c2 = stage_next(a, c2, q_hi, b, hk, D2, HD2);
       kb0 = kb0 == 2 ? 0 : kb0 + 1;
     }
     // hand the reference and the exact max of every row to the consumer
@@ -1862,7 +1867,7 @@ void ring_attn_bf16_ws(const AttnArgs a) {
       pipeline_barrier();
       c0 = c1;
       c1 = c2;
-      c2 = stage_next(a, c2, q_hi, b, h, D2, HD2);
+      c2 = stage_next(a, c2, q_hi, b, hk, D2, HD2);
       vbp = vb0;
     }
     __syncthreads();  // the producer's reference and max
@@ -1941,6 +1946,8 @@ void ring_attn_f32(const AttnArgs a) {
   const long long wq_lo = qpos(a, wrow0);
   const long long wq_hi = wq_lo + wrows - 1;
   const long long HD = (long long)a.H * D;
+  const long long HDkv = (long long)a.Hkv * D;
+  const int hk = h / (a.H / a.Hkv);  // K/V head of this query head
 
   // Q fragment: feature index of (step c4, element e) for this half is
   // 8*c4 + 4*half + e (the same map is used for K).
@@ -1966,15 +1973,15 @@ void ring_attn_f32(const AttnArgs a) {
   auto fetch = [&](int bi, int ti) {
     const KVBlock& kb = a.blk[bi];
     const int kt0 = ti * BC;
-    const float* kp = (const float*)kb.k + ((long long)b * a.kv_rows_b + kt0) * HD + (long long)h * D;
-    const float* vp = (const float*)kb.v + ((long long)b * a.kv_rows_b + kt0) * HD + (long long)h * D;
+    const float* kp = (const float*)kb.k + ((long long)b * a.kv_rows_b + kt0) * HDkv + (long long)hk * D;
+    const float* vp = (const float*)kb.v + ((long long)b * a.kv_rows_b + kt0) * HDkv + (long long)hk * D;
     const int rows = min(BC, kb.len - kt0);
 #pragma unroll
     for (int u = 0; u < C::UNITS; ++u) {
       const int unit = tid + u * kThreads;
       const int r = unit / (D / 4), c = unit % (D / 4);
-      kreg[u] = r < rows ? *(const float4*)(kp + r * HD + 4 * c) : float4{0, 0, 0, 0};
-      vreg[u] = r < rows ? *(const float4*)(vp + r * HD + 4 * c) : float4{0, 0, 0, 0};
+      kreg[u] = r < rows ? *(const float4*)(kp + r * HDkv + 4 * c) : float4{0, 0, 0, 0};
+      vreg[u] = r < rows ? *(const float4*)(vp + r * HDkv + 4 * c) : float4{0, 0, 0, 0};
     }
   };
   auto store_lds = [&](int buf) {
@@ -2203,6 +2210,7 @@ extern "C" ra_status ra_block_attn_fwd(const void* q, const void* k, const void*
   a.q_pos1 = q_pos0 + Sq;
   a.q_split = Sq;
   a.kv_rows_b = Sk;
+  a.Hkv = H;
   a.valid_len = valid_len;
   a.B = B;
   a.Sq = Sq;
@@ -2221,15 +2229,18 @@ extern "C" ra_status ra_block_attn_fwd(const void* q, const void* k, const void*
   return launch(a, D, dt, (hipStream_t)stream, name);
 }
 
-extern "C" ra_status ra_ring_attn_fwd(const void* q_r, const void* const* k_blocks,
-                                      const void* const* v_blocks, int B, int Sb,
-                                      int H, int D, int P, int rank, ra_dtype dt,
-                                      float scale, int causal, long long valid_len,
-                                      void* o, float* lse_opt, void* stream) {
-  static const char* name = "ra_ring_attn_fwd";
+namespace {
+// The whole ring of one rank (shared by the MHA and GQA entry points).
+ra_status ring_fwd(const char* name, const void* q_r, const void* const* k_blocks,
+                   const void* const* v_blocks, int B, int Sb, int H, int Hkv, int D, int P,
+                   int rank, ra_dtype dt, float scale, int causal, long long valid_len, void* o,
+                   float* lse_opt, void* stream) {
   ra::clear_error();
   ra_status st = check_common(name, B, Sb, H, D, dt);
   if (st != RA_OK) return st;
+  if (Hkv <= 0 || H % Hkv != 0)
+    return ra::fail(RA_ERR_SHAPE, "%s: %d query heads are not a multiple of %d K/V heads",
+                    name, H, Hkv);
   if (P <= 0) return ra::fail(RA_ERR_SHAPE, "%s: P must be positive (got %d)", name, P);
   if (P > RA_MAX_P)
     return ra::fail(RA_ERR_RANGE, "%s: P=%d exceeds RA_MAX_P=%d", name, P, RA_MAX_P);
@@ -2251,6 +2262,7 @@ extern "C" ra_status ra_ring_attn_fwd(const void* q_r, const void* const* k_bloc
   a.q_pos1 = a.q_pos0 + Sb;
   a.q_split = Sb;
   a.kv_rows_b = Sb;
+  a.Hkv = Hkv;
   a.valid_len = valid_len;
   a.B = B;
   a.Sq = Sb;
@@ -2275,6 +2287,25 @@ extern "C" ra_status ra_ring_attn_fwd(const void* q_r, const void* const* k_bloc
     a.blk[a.nblk++] = KVBlock{k_blocks[j], v_blocks[j], (long long)j * Sb, Sb, cls[t]};
   }
   return launch(a, D, dt, (hipStream_t)stream, name);
+}
+}  // namespace
+
+extern "C" ra_status ra_ring_attn_fwd(const void* q_r, const void* const* k_blocks,
+                                      const void* const* v_blocks, int B, int Sb,
+                                      int H, int D, int P, int rank, ra_dtype dt,
+                                      float scale, int causal, long long valid_len,
+                                      void* o, float* lse_opt, void* stream) {
+  return ring_fwd("ra_ring_attn_fwd", q_r, k_blocks, v_blocks, B, Sb, H, H, D, P, rank, dt,
+                  scale, causal, valid_len, o, lse_opt, stream);
+}
+
+extern "C" ra_status ra_ring_attn_fwd_gqa(const void* q_r, const void* const* k_blocks,
+                                          const void* const* v_blocks, int B, int Sb, int H,
+                                          int H_kv, int D, int P, int rank, ra_dtype dt,
+                                          float scale, int causal, long long valid_len,
+                                          void* o, float* lse_opt, void* stream) {
+  return ring_fwd("ra_ring_attn_fwd_gqa", q_r, k_blocks, v_blocks, B, Sb, H, H_kv, D, P, rank,
+                  dt, scale, causal, valid_len, o, lse_opt, stream);
 }
 
 extern "C" ra_status ra_zigzag_attn_fwd(const void* q_r, const void* const* k_shares,
@@ -2312,6 +2343,7 @@ extern "C" ra_status ra_zigzag_attn_fwd(const void* q_r, const void* const* k_sh
   a.q_pos1 = (long long)(2 * P - 1 - rank) * c;
   a.q_split = c;
   a.kv_rows_b = Sr;
+  a.Hkv = H;
   a.valid_len = valid_len;
   a.B = B;
   a.Sq = Sr;

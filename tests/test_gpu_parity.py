@@ -443,6 +443,50 @@ def test_zigzag_long_context_ranks_0_and_7():
                                       np.concatenate(ref_l, 2)) <= LSE_BF16_ATOL
 
 
+# ------------------------------------------------------------ grouped-query attention
+@pytest.mark.parametrize("Hkv", [1, 2, 8])
+def test_gqa_ring_all_ranks(variant, Hkv):
+    """K/V with H_kv of H = 8 heads (multi-query, grouped, plain), B = 2,
+    causal: every rank against the plain definition with query head h
+    reading K/V head h / (H / H_kv)."""
+    B, S, H, D, P = 2, 2048, 8, 128, 4
+    Sb = S // P
+    q = W.random_tensor((B, S, H, D), seed=51, device="cuda")
+    k = W.random_tensor((B, S, Hkv, D), seed=52, device="cuda")
+    v = W.random_tensor((B, S, Hkv, D), seed=53, device="cuda")
+    kb, vb = blocks_of(k, P), blocks_of(v, P)
+    ke, ve = oracle.gqa_expand(k.cpu(), H), oracle.gqa_expand(v.cpu(), H)
+    for r in range(P):
+        q_r = q[:, r * Sb:(r + 1) * Sb].contiguous()
+        o, lse = ra.ring_attn_fwd(q_r, kb, vb, r, causal=True)
+        torch.cuda.synchronize()
+        ref_o, ref_lse, _, _ = oracle.attention(q_r.cpu(), ke[:, :(r + 1) * Sb], ve[:, :(r + 1) * Sb],
+                                                causal=True, q_pos0=r * Sb, k_pos0=0)
+        check_bf16(o.cpu(), ref_o, f"gqa Hkv={Hkv} r{r}")
+        assert oracle.max_abs_err(lse.cpu(), ref_lse) <= LSE_BF16_ATOL
+
+
+def test_gqa_fp32_and_bad_heads():
+    """The fp32 kernel reads the grouped K/V heads too; a K/V head count that
+    does not divide H is refused (ValueError) before any launch."""
+    B, S, H, D, P, Hkv = 1, 512, 4, 64, 2, 2
+    Sb = S // P
+    q = W.random_tensor((B, S, H, D), dtype=torch.float32, seed=61, device="cuda")
+    k = W.random_tensor((B, S, Hkv, D), dtype=torch.float32, seed=62, device="cuda")
+    v = W.random_tensor((B, S, Hkv, D), dtype=torch.float32, seed=63, device="cuda")
+    kb, vb = blocks_of(k, P), blocks_of(v, P)
+    ke, ve = oracle.gqa_expand(k.cpu(), H), oracle.gqa_expand(v.cpu(), H)
+    for r in range(P):
+        q_r = q[:, r * Sb:(r + 1) * Sb].contiguous()
+        o, _ = ra.ring_attn_fwd(q_r, kb, vb, r, causal=False)
+        torch.cuda.synchronize()
+        ref_o, _, _, _ = oracle.attention(q_r.cpu(), ke, ve, causal=False, q_pos0=r * Sb)
+        check_fp32(o.cpu(), ref_o, f"gqa fp32 r{r}")
+    k3 = [x[:, :, :1].repeat(1, 1, 3, 1).contiguous() for x in kb]
+    with pytest.raises(ValueError):
+        ra.ring_attn_fwd(q[:, :Sb].contiguous(), k3, k3, 0)
+
+
 # ------------------------------------------------------------ ring backward
 # Gradient tolerances (bf16 operands, fp32 accumulation): P and dS are
 # rounded to bf16 (relative 2^-9) before their matrix products, as O's P is

@@ -183,6 +183,13 @@ def test_device_entry_points_validate_before_launch(lib):
     st = lib.ra_zigzag_attn_fwd(null, arr, arr, 1, 128, 1, 64, 2, 0, ra.RA_BF16, 0.0, 1,
                                 -1, null, null, null)
     assert st == 1
+    # grouped-query ring: K/V heads must divide H
+    st = lib.ra_ring_attn_fwd_gqa(null, arr, arr, 1, 16, 6, 4, 64, 2, 0, ra.RA_BF16, 0.0, 0,
+                                  -1, null, null, null)
+    assert st == 2 and b"K/V heads" in lib.ra_last_error()
+    st = lib.ra_ring_attn_fwd_gqa(null, arr, arr, 1, 16, 6, 0, 64, 2, 0, ra.RA_BF16, 0.0, 0,
+                                  -1, null, null, null)
+    assert st == 2
     # ring backward: fp32 inputs unsupported, D, rank, NULL buffers
     st = lib.ra_ring_attn_bwd(null, arr, arr, null, null, null, 1, 16, 1, 64, 2, 0, ra.RA_FP32,
                               0.0, 0, -1, null, arr, arr, null, null)

@@ -648,3 +648,31 @@ def test_grad_sampled_equals_full_rows(causal, valid, q_pos0):
     np.testing.assert_allclose(sq, dq[:, qr], atol=1e-12)
     np.testing.assert_allclose(sk, dk[:, kr], atol=1e-12)
     np.testing.assert_allclose(sv, dv[:, kr], atol=1e-12)
+
+
+# ---------------------------------------------------------------- grouped-query attention
+def test_gqa_expand_pins():
+    """H_kv = H is the identity; the head map h -> h // (H / H_kv) checked by a
+    per-head loop; with one K/V head (multi-query), equal query heads give
+    equal outputs and permuting query heads permutes the outputs."""
+    rng = np.random.default_rng(12)
+    B, S, H, D = 1, 6, 6, 4
+    k = rng.standard_normal((B, S, H, D))
+    np.testing.assert_array_equal(oracle.gqa_expand(k, H), k)
+    for Hkv in (1, 2, 3):
+        kk = rng.standard_normal((B, S, Hkv, D))
+        e = oracle.gqa_expand(kk, H)
+        for h in range(H):
+            np.testing.assert_array_equal(e[:, :, h], kk[:, :, (h * Hkv) // H])
+    with pytest.raises(ValueError):
+        oracle.gqa_expand(rng.standard_normal((B, S, 4, D)), H)
+    q = np.repeat(rng.standard_normal((B, S, 1, D)), H, axis=2)
+    k1, v1 = rng.standard_normal((B, S, 1, D)), rng.standard_normal((B, S, 1, D))
+    o, _, _, _ = oracle.attention(q, oracle.gqa_expand(k1, H), oracle.gqa_expand(v1, H), causal=True)
+    for h in range(1, H):
+        np.testing.assert_allclose(o[:, :, h], o[:, :, 0], atol=1e-14)
+    q = rng.standard_normal((B, S, H, D))
+    perm = rng.permutation(H)
+    o, _, _, _ = oracle.attention(q, oracle.gqa_expand(k1, H), oracle.gqa_expand(v1, H))
+    op, _, _, _ = oracle.attention(q[:, :, perm], oracle.gqa_expand(k1, H), oracle.gqa_expand(v1, H))
+    np.testing.assert_allclose(op, o[:, :, perm], atol=1e-14)
