@@ -210,6 +210,24 @@ ra_status ra_ring_attn_fwd_gqa(const void* q_r, const void* const* k_blocks,
                                float scale, int causal, long long valid_len,
                                void* o, float* lse_opt, void* stream);
 
+/* Packed variable-length form of ra_ring_attn_fwd ([RA] §6: a packed
+ * sequence carries its sample boundaries and a sample never attends to
+ * another).  B = 1; the P*Sb global positions hold n_seqs samples, sample i
+ * at [cu_seqlens[i], cu_seqlens[i+1]) (a HOST array of n_seqs + 1
+ * increasing int64 values from 0; positions past cu_seqlens[n_seqs] are
+ * padding).  Query at position p attends to the keys of its own sample
+ * (causal: at or before p).  q_r [1,Sb,H,D], blocks [1,Sb,H,D] as in
+ * ra_ring_attn_fwd; rows of the share outside every sample are left
+ * untouched in o and lse_opt.  One launch per sample that meets the rank's
+ * rows, each over the parts of the visited blocks inside the sample, in
+ * ring order.  RA_ERR_SHAPE for boundaries that do not increase from 0 or
+ * end past P*Sb; otherwise as ra_ring_attn_fwd. */
+ra_status ra_ring_attn_fwd_varlen(const void* q_r, const void* const* k_blocks,
+                                  const void* const* v_blocks, int Sb, int H, int D,
+                                  int P, int rank, ra_dtype dt, float scale, int causal,
+                                  const long long* cu_seqlens, int n_seqs, void* o,
+                                  float* lse_opt, void* stream);
+
 /* The whole ring of rank `rank` over zigzag shares in one launch ([RA]
  * §3.2-§3.4 with the sharding of ra_zigzag_schedule).  q_r [B,Sr,H,D] is
  * the rank's share: rows [0, Sr/2) are chunk rank (global rows

@@ -27,7 +27,7 @@ Sources (the pages this follows, cited by title and section):
 
 Parity status of each function is listed in its module docstring.
 """
-from .attention import attention, local_only_attention, scores, gqa_expand
+from .attention import attention, local_only_attention, scores, gqa_expand, packed_attention
 from .online import (ring_attention_rank, lse_combine, composable_ring_rank, chunked_attention,
                      zigzag_ring_rank)
 from .schedule import (SKIP, FULL, DIAG, padded_len, seq_divisible, shard_range, ring_sources,
@@ -38,7 +38,7 @@ from .grad import attention_grad, attention_grad_sampled, ring_attention_bwd_ran
 from .compare import max_abs_err, cosine, rel_l2, compare
 
 __all__ = [
-    "attention", "local_only_attention", "scores", "gqa_expand",
+    "attention", "local_only_attention", "scores", "gqa_expand", "packed_attention",
     "ring_attention_rank", "lse_combine", "composable_ring_rank", "chunked_attention",
     "zigzag_ring_rank", "zigzag_chunks", "zigzag_positions", "zigzag_schedule", "visible_pairs",
     "attention_grad", "attention_grad_sampled", "ring_attention_bwd_rank",

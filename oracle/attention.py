@@ -27,7 +27,9 @@ by constant-V and +1000-shift invariances, and by a pure-Python brute force
 on tiny inputs (tests/test_oracle_pins.py).  ``gqa_expand`` (the K/V head a
 query head reads under grouped-query attention) is pinned by the identity at
 H_kv = H, by a per-head loop over the head map, and by the multi-query
-invariances (tests/test_oracle_pins.py).
+invariances; ``packed_attention`` by a brute force with an explicit
+same-sample mask and by the single-sample special case
+(tests/test_oracle_pins.py).
 """
 from __future__ import annotations
 
@@ -128,3 +130,33 @@ def gqa_expand(x, H):
     if Hkv <= 0 or H % Hkv:
         raise ValueError(f"{H} query heads are not a multiple of {Hkv} K/V heads")
     return x[:, :, np.arange(H) // (H // Hkv)]
+
+
+def packed_attention(q, k, v, cu_seqlens, *, scale=None, causal=True, q_pos0=0, rows=None):
+    """Attention over a packed sequence (B = 1): sample i holds global
+    positions [cu_seqlens[i], cu_seqlens[i+1]) and a query attends only to
+    keys of its own sample (the Ring Attention tutorial §6: packed sequences
+    carry their boundaries and blocks never attend across samples).
+
+    q: [1, Sq, H, D] at global positions q_pos0 + row; k, v: [1, S, H, D]
+    from position 0.  Computed sample by sample with ``attention``: each
+    sample is an independent sequence at its own global positions.  Rows
+    outside every sample get o = 0, lse = -inf.  Returns (o, lse).
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    _, Sq, H, D = q.shape
+    rows = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.zeros((1, len(rows), H, v.shape[-1]))
+    lse = np.full((1, len(rows), H), -np.inf)
+    pos = q_pos0 + rows
+    for s0, s1 in zip(cu_seqlens[:-1], cu_seqlens[1:]):
+        sel = np.flatnonzero((pos >= s0) & (pos < s1))
+        if len(sel) == 0:
+            continue
+        oi, li, _, _ = attention(q, k[:, s0:s1], v[:, s0:s1], scale=scale, causal=causal,
+                                 q_pos0=q_pos0, k_pos0=s0, rows=rows[sel])
+        o[:, sel] = oi
+        lse[:, sel] = li
+    return o, lse

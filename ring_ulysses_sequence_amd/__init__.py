@@ -42,7 +42,7 @@ EXPORTED = (
     "ra_classify_block", "ra_ring_schedule", "ra_block_attn_fwd",
     "ra_ring_merge", "ra_ring_attn_fwd", "ra_seq2head", "ra_head2seq",
     "ra_zigzag_padded_len", "ra_zigzag_schedule", "ra_zigzag_attn_fwd", "ra_ring_attn_bwd",
-    "ra_ring_attn_fwd_gqa",
+    "ra_ring_attn_fwd_gqa", "ra_ring_attn_fwd_varlen",
 )
 
 _lib = None
@@ -90,6 +90,10 @@ def _load():
         "ra_ring_attn_fwd_gqa": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp),
                                          c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                          c_float, c_int, c_ll, c_vp, c_vp, c_vp]),
+        "ra_ring_attn_fwd_varlen": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp),
+                                            c_int, c_int, c_int, c_int, c_int, c_int, c_float,
+                                            c_int, ctypes.POINTER(c_ll), c_int, c_vp, c_vp,
+                                            c_vp]),
         "ra_ring_attn_bwd": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp, c_vp,
                                      c_vp, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                      c_float, c_int, c_ll, c_vp, ctypes.POINTER(c_vp),
@@ -301,6 +305,46 @@ def ring_attn_fwd(q_r, k_blocks: Sequence, v_blocks: Sequence, rank: int, *,
     return o, lse
 
 
+def ring_attn_fwd_varlen(q_r, k_blocks: Sequence, v_blocks: Sequence, rank: int,
+                         cu_seqlens: Sequence, *, causal: bool = True, scale: float = 0.0,
+                         want_lse: bool = True, out=None, lse_out=None, stream=None):
+    """Rank ``rank``'s ring over a packed sequence (B = 1): sample i holds
+    global positions [cu_seqlens[i], cu_seqlens[i+1]) and attends only within
+    itself.  Returns (o, lse); rows outside every sample are left as allocated
+    (zero-filled here when the outputs are not given)."""
+    torch = _torch()
+    B, Sb, H, D = q_r.shape
+    if B != 1:
+        raise ValueError("packed sequences need B = 1")
+    P = len(k_blocks)
+    if len(v_blocks) != P:
+        raise ValueError("k_blocks and v_blocks differ in length")
+    if P > RA_MAX_P:
+        raise RuntimeError(f"P={P} exceeds {RA_MAX_P}")
+    dt = _dtype_code(q_r)
+    kp = (ctypes.c_void_p * max(P, 1))()
+    vp = (ctypes.c_void_p * max(P, 1))()
+    for j in range(P):
+        for t, n in ((k_blocks[j], "k"), (v_blocks[j], "v")):
+            if t.shape != q_r.shape or t.dtype != q_r.dtype:
+                raise ValueError(f"{n}_blocks[{j}] must match q_r in shape and dtype")
+        kp[j] = k_blocks[j].data_ptr()
+        vp[j] = v_blocks[j].data_ptr()
+        _dev(k_blocks[j], f"k_blocks[{j}]"), _dev(v_blocks[j], f"v_blocks[{j}]")
+    o = torch.zeros_like(q_r) if out is None else out
+    lse = lse_out
+    if lse is None and want_lse:
+        lse = torch.full((B, Sb, H), float("-inf"), dtype=torch.float32, device=q_r.device)
+    n = len(cu_seqlens) - 1
+    cu = (ctypes.c_longlong * max(n + 1, 1))(*[int(x) for x in cu_seqlens])
+    st = _load().ra_ring_attn_fwd_varlen(_dev(q_r, "q_r"), kp, vp, Sb, H, D, P, rank, dt,
+                                         float(scale), int(causal), cu, max(n, 0), _dev(o, "o"),
+                                         _dev(lse, "lse") if lse is not None else None,
+                                         _stream(stream))
+    _check(st, "ra_ring_attn_fwd_varlen")
+    return o, lse
+
+
 def zigzag_attn_fwd(q_r, k_shares: Sequence, v_shares: Sequence, rank: int, *,
                     causal: bool = True, valid_len: int = -1, scale: float = 0.0,
                     want_lse: bool = True, out=None, lse_out=None, stream=None):
@@ -449,6 +493,7 @@ __all__ = [
     "lib", "abi_version", "set_attn_kernel", "get_attn_kernel", "padded_len", "shard_range", "classify_block", "ring_schedule",
     "block_attn_fwd", "ring_merge", "ring_attn_fwd", "seq2head", "head2seq",
     "zigzag_padded_len", "zigzag_schedule", "zigzag_attn_fwd", "ring_attn_bwd",
+    "ring_attn_fwd_varlen",
     "ring_attn_composable", "EXPORTED", "LIB_PATH", "LibraryMissing",
     "RA_BF16", "RA_FP32", "RA_SKIP", "RA_FULL", "RA_DIAG", "RA_MAX_P", "RA_PAD_MULTIPLE",
     "RA_KERNEL_AUTO", "RA_KERNEL_BR128", "RA_KERNEL_BR256", "RA_KERNEL_W64", "RA_KERNEL_WS",

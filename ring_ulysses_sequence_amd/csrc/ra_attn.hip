@@ -2290,6 +2290,87 @@ ra_status ring_fwd(const char* name, const void* q_r, const void* const* k_block
 }
 }  // namespace
 
+extern "C" ra_status ra_ring_attn_fwd_varlen(const void* q_r, const void* const* k_blocks,
+                                             const void* const* v_blocks, int Sb, int H, int D,
+                                             int P, int rank, ra_dtype dt, float scale,
+                                             int causal, const long long* cu_seqlens,
+                                             int n_seqs, void* o, float* lse_opt,
+                                             void* stream) {
+  static const char* name = "ra_ring_attn_fwd_varlen";
+  ra::clear_error();
+  ra_status st = check_common(name, 1, Sb, H, D, dt);
+  if (st != RA_OK) return st;
+  if (P <= 0) return ra::fail(RA_ERR_SHAPE, "%s: P must be positive (got %d)", name, P);
+  if (P > RA_MAX_P)
+    return ra::fail(RA_ERR_RANGE, "%s: P=%d exceeds RA_MAX_P=%d", name, P, RA_MAX_P);
+  if (rank < 0 || rank >= P)
+    return ra::fail(RA_ERR_RANGE, "%s: rank %d outside [0, %d)", name, rank, P);
+  if (n_seqs < 0 || (n_seqs > 0 && !cu_seqlens))
+    return ra::fail(RA_ERR_NULL, "%s: NULL or negative sample table", name);
+  const long long S = (long long)P * Sb;
+  for (int i = 0; i < n_seqs; ++i)
+    if (cu_seqlens[i] > cu_seqlens[i + 1] || cu_seqlens[i] < 0)
+      return ra::fail(RA_ERR_SHAPE, "%s: sample boundaries must increase from 0", name);
+  if (n_seqs > 0 && (cu_seqlens[0] != 0 || cu_seqlens[n_seqs] > S))
+    return ra::fail(RA_ERR_SHAPE, "%s: samples must start at 0 and end within P*Sb = %lld",
+                    name, S);
+  if ((long long)Sb * H == 0) return RA_OK;
+  if (!q_r || !o || !k_blocks || !v_blocks)
+    return ra::fail(RA_ERR_NULL, "%s: NULL q/o/block table", name);
+  if (!aligned16(q_r) || !aligned16(o))
+    return ra::fail(RA_ERR_SHAPE, "%s: q and o must be 16-byte aligned", name);
+  const size_t row_bytes = (size_t)H * D * (dt == RA_BF16 ? 2 : 4);
+  const double sc = scale > 0.0f ? (double)scale : 1.0 / std::sqrt((double)D);
+  const long long q0 = (long long)rank * Sb, q1 = q0 + Sb;
+  int src[RA_MAX_P], cls[RA_MAX_P];
+  st = ra_ring_schedule(P, rank, Sb, causal, S, src, cls);
+  if (st != RA_OK) return st;
+  // one launch per sample that meets the rank's rows: its rows of the share
+  // against the parts of the visited blocks that lie inside the sample, in
+  // ring order (a packed sequence never attends across samples)
+  for (int i = 0; i < n_seqs; ++i) {
+    const long long s0 = cu_seqlens[i], s1 = cu_seqlens[i + 1];
+    const long long r0 = s0 > q0 ? s0 : q0, r1 = s1 < q1 ? s1 : q1;
+    if (r1 <= r0) continue;
+    AttnArgs a{};
+    a.q = (const char*)q_r + (size_t)(r0 - q0) * row_bytes;
+    a.o = (char*)o + (size_t)(r0 - q0) * row_bytes;
+    a.lse = lse_opt ? lse_opt + (r0 - q0) * H : nullptr;
+    a.q_pos0 = r0;
+    a.q_pos1 = r1;
+    a.q_split = (int)(r1 - r0);
+    a.kv_rows_b = Sb;  // B = 1: never used for a stride
+    a.Hkv = H;
+    a.valid_len = s1;  // keys past the sample's end are not real for it
+    a.B = 1;
+    a.Sq = (int)(r1 - r0);
+    a.H = H;
+    a.causal = causal != 0;
+    a.o_fp32 = dt == RA_FP32;
+    a.scale_log2 = (float)(sc * 1.4426950408889634);
+    a.nblk = 0;
+    for (int t = 0; t < P; ++t) {
+      if (cls[t] == RA_SKIP) continue;
+      const int j = src[t];
+      const long long b0 = (long long)j * Sb, b1 = b0 + Sb;
+      const long long k0 = b0 > s0 ? b0 : s0, k1 = b1 < s1 ? b1 : s1;
+      if (k1 <= k0) continue;
+      const int c = ra::block_class(r0, r1, k0, k1, causal != 0, s1);
+      if (c == RA_SKIP) continue;
+      if (!k_blocks[j] || !v_blocks[j])
+        return ra::fail(RA_ERR_NULL, "%s: NULL pointer for visited block %d", name, j);
+      if (!aligned16(k_blocks[j]) || !aligned16(v_blocks[j]))
+        return ra::fail(RA_ERR_SHAPE, "%s: block %d not 16-byte aligned", name, j);
+      const size_t off = (size_t)(k0 - b0) * row_bytes;
+      a.blk[a.nblk++] = KVBlock{(const char*)k_blocks[j] + off, (const char*)v_blocks[j] + off,
+                                k0, (int)(k1 - k0), c};
+    }
+    st = launch(a, D, dt, (hipStream_t)stream, name);
+    if (st != RA_OK) return st;
+  }
+  return RA_OK;
+}
+
 extern "C" ra_status ra_ring_attn_fwd(const void* q_r, const void* const* k_blocks,
                                       const void* const* v_blocks, int B, int Sb,
                                       int H, int D, int P, int rank, ra_dtype dt,

@@ -487,6 +487,56 @@ def test_gqa_fp32_and_bad_heads():
         ra.ring_attn_fwd(q[:, :Sb].contiguous(), k3, k3, 0)
 
 
+# ------------------------------------------------------------ packed samples
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_all_ranks(variant, causal):
+    """Packed samples (boundaries across the rank shares, a tail outside
+    every sample): every rank against the oracle's same-sample attention;
+    rows outside every sample are left untouched."""
+    S, H, D, P = 2048, 4, 128, 4
+    Sb = S // P
+    cu = [0, 300, 1000, 1148, 1900]
+    q, k, v = (W.random_tensor((1, S, H, D), seed=s_, device="cuda") for s_ in (71, 72, 73))
+    kb, vb = blocks_of(k, P), blocks_of(v, P)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    for r in range(P):
+        q_r = q[:, r * Sb:(r + 1) * Sb].contiguous()
+        o, lse = ra.ring_attn_fwd_varlen(q_r, kb, vb, r, cu, causal=causal)
+        torch.cuda.synchronize()
+        ref_o, ref_lse = oracle.packed_attention(qc[:, r * Sb:(r + 1) * Sb], kc, vc, cu,
+                                                 causal=causal, q_pos0=r * Sb)
+        inside = np.flatnonzero(r * Sb + np.arange(Sb) < cu[-1])
+        outside = np.flatnonzero(r * Sb + np.arange(Sb) >= cu[-1])
+        if len(inside):
+            check_bf16(o.cpu()[:, inside], ref_o[:, inside], f"varlen causal={causal} r{r}")
+            assert oracle.max_abs_err(lse.cpu()[:, inside], ref_lse[:, inside]) <= LSE_BF16_ATOL
+        if len(outside):
+            assert not o[:, outside].any()
+            assert torch.isneginf(lse[:, outside]).all()
+
+
+def test_varlen_fp32_and_bad_tables():
+    """fp32 through the fp32 kernel to 1e-5; boundaries that do not start at
+    0, decrease or run past the sequence are refused before any launch."""
+    S, H, D, P = 1024, 2, 64, 2
+    Sb = S // P
+    cu = [0, 100, 611, 1024]
+    q, k, v = (W.random_tensor((1, S, H, D), dtype=torch.float32, seed=s_, device="cuda")
+               for s_ in (81, 82, 83))
+    kb, vb = blocks_of(k, P), blocks_of(v, P)
+    for r in range(P):
+        q_r = q[:, r * Sb:(r + 1) * Sb].contiguous()
+        o, _ = ra.ring_attn_fwd_varlen(q_r, kb, vb, r, cu, causal=True)
+        torch.cuda.synchronize()
+        ref_o, _ = oracle.packed_attention(q.cpu()[:, r * Sb:(r + 1) * Sb], k.cpu(), v.cpu(), cu,
+                                           causal=True, q_pos0=r * Sb)
+        check_fp32(o.cpu(), ref_o, f"varlen fp32 r{r}")
+    q0 = q[:, :Sb].contiguous()
+    for bad in ([5, 600, 1024], [0, 600, 500, 1024], [0, 600, 1100]):
+        with pytest.raises(ValueError):
+            ra.ring_attn_fwd_varlen(q0, kb, vb, 0, bad)
+
+
 # ------------------------------------------------------------ ring backward
 # Gradient tolerances (bf16 operands, fp32 accumulation): P and dS are
 # rounded to bf16 (relative 2^-9) before their matrix products, as O's P is

@@ -676,3 +676,38 @@ def test_gqa_expand_pins():
     o, _, _, _ = oracle.attention(q, oracle.gqa_expand(k1, H), oracle.gqa_expand(v1, H))
     op, _, _, _ = oracle.attention(q[:, :, perm], oracle.gqa_expand(k1, H), oracle.gqa_expand(v1, H))
     np.testing.assert_allclose(op, o[:, :, perm], atol=1e-14)
+
+
+# ---------------------------------------------------------------- packed samples
+@pytest.mark.parametrize("causal", [True, False])
+def test_packed_attention_brute_force(causal):
+    """Packed samples against a pure-Python brute force with an explicit
+    same-sample mask (query rows offset from the keys); one sample covering
+    everything is plain attention; rows outside every sample are empty."""
+    rng = np.random.default_rng(21)
+    S, H, D = 13, 2, 3
+    cu = [0, 4, 5, 11]          # positions 11, 12: outside every sample
+    q = rng.standard_normal((1, S, H, D))
+    k = rng.standard_normal((1, S, H, D))
+    v = rng.standard_normal((1, S, H, D))
+    seg = np.full(S, -1)
+    for i, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        seg[a:b] = i
+    o, lse = oracle.packed_attention(q[:, 3:], k, v, cu, causal=causal, q_pos0=3)
+    for r in range(S - 3):
+        p = r + 3
+        for h in range(H):
+            js = [j for j in range(S) if seg[j] == seg[p] and seg[p] >= 0 and (not causal or j <= p)]
+            if not js:
+                assert np.all(o[0, r, h] == 0) and lse[0, r, h] == -np.inf
+                continue
+            s = [q[0, p, h] @ k[0, j, h] / math.sqrt(D) for j in js]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            want = sum(wi * v[0, j, h] for wi, j in zip(w, js)) / sum(w)
+            np.testing.assert_allclose(o[0, r, h], want, atol=1e-13)
+            assert abs(lse[0, r, h] - (m + math.log(sum(w)))) < 1e-13
+    one, one_lse = oracle.packed_attention(q, k, v, [0, S], causal=causal)
+    full, full_lse, _, _ = oracle.attention(q, k, v, causal=causal)
+    np.testing.assert_allclose(one, full, atol=1e-14)
+    np.testing.assert_allclose(one_lse, full_lse, atol=1e-14)
