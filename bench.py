@@ -182,6 +182,7 @@ def main():
         extra = side_measurements(torch, ra, W, stream)
         extra.update(zigzag_measurements(torch, ra, W, stream, q, k, v))
         extra.update(backward_measurement(torch, ra, W, stream, q_r, kb, vb, o, lse, flops))
+        extra.update(gqa_varlen_measurements(torch, ra, stream, q_r, k, v, kb, vb))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -311,6 +312,63 @@ def backward_measurement(torch, ra, W, stream, q_r, kb, vb, o, lse, fwd_flops):
     return {"backward_long_rank3": {"ms": round(ms, 3), "flops": fl,
                                     "tflops": round(fl / ms / 1e9, 2),
                                     "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}}
+
+
+def packed_sample_bounds(S: int, n: int, seed: int):
+    """Boundaries of n packed samples covering [0, S): lengths drawn from a
+    seeded uniform split (the synthetic stand-in for a mixed-length batch)."""
+    import numpy as np
+    g = np.random.default_rng(seed)
+    cuts = np.sort(g.choice(np.arange(1, S), size=n - 1, replace=False))
+    return [0] + [int(x) for x in cuts] + [S]
+
+
+def gqa_varlen_measurements(torch, ra, stream, q_r, k, v, kb, vb):
+    """The same rank-3 share with grouped-query K/V (8 K/V heads for the 64
+    query heads: the first head of each group of 8) and as a packed sequence
+    of 16 samples (causal within each sample), each with its own algorithmic
+    FLOPs (4*D per visible pair)."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    B, Sb, H, D = q_r.shape
+    P, rank = len(kb), 3
+
+    def timed(fn, n=3):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    out = {}
+    Hkv = 8
+    kg = k[:, :, ::H // Hkv].contiguous()
+    vg = v[:, :, ::H // Hkv].contiguous()
+    kgb = [kg[:, j * Sb:(j + 1) * Sb] for j in range(P)]
+    vgb = [vg[:, j * Sb:(j + 1) * Sb] for j in range(P)]
+    o = torch.empty_like(q_r)
+    ms = timed(lambda: ra.ring_attn_fwd(q_r, kgb, vgb, rank, causal=True, out=o, want_lse=False,
+                                        stream=stream))
+    fl = 4.0 * D * H * visible_pairs_causal_rank(rank, Sb, P * Sb)
+    out["gqa_long_rank3_hkv8"] = {"ms": round(ms, 3), "tflops": round(fl / ms / 1e9, 2),
+                                  "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+    del kg, vg, kgb, vgb
+    cu = packed_sample_bounds(P * Sb, 16, seed=5)
+    q0, q1 = rank * Sb, (rank + 1) * Sb
+    pairs = 0
+    for s0, s1 in zip(cu[:-1], cu[1:]):
+        a, b = max(s0, q0), min(s1, q1)
+        if b > a:  # query p sees keys s0 .. p of its sample
+            pairs += (a - s0 + 1 + b - s0) * (b - a) // 2
+    fl = 4.0 * D * H * pairs
+    ms = timed(lambda: ra.ring_attn_fwd_varlen(q_r, kb, vb, rank, cu, causal=True, out=o,
+                                               want_lse=False, stream=stream))
+    out["varlen_long_rank3_16_samples"] = {"ms": round(ms, 3), "tflops": round(fl / ms / 1e9, 2),
+                                           "flops": fl, "samples": cu}
+    return out
 
 
 def zigzag_measurements(torch, ra, W, stream, q, k, v):
