@@ -261,8 +261,9 @@ ra_status ra_zigzag_attn_fwd(const void* q_r, const void* const* k_shares,
  * caller zeroes them; summing dk/dv over all ranks' calls gives the owners'
  * gradients, as the ring returns them).  dk_blocks / dv_blocks are HOST
  * arrays of P device pointers; entries of blocks the rank skips (causal
- * future) may be NULL and are not touched.  delta_ws: fp32 [B,Sb,H] scratch
- * the call overwrites (D).  Two launches on `stream` (dq, then dk/dv).
+ * future) may be NULL and are not touched.  stats_ws: fp32 scratch of
+ * 2*B*Sb*H floats the call overwrites (per-row base-2 lse and D, [2,B,H,Sb]).
+ * Three launches on `stream` (dq, then dv, then dk).
  * Only bf16 inputs (RA_ERR_UNSUPPORTED for fp32).  Errors as
  * ra_ring_attn_fwd. */
 ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_blocks,
@@ -271,7 +272,7 @@ ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_blocks,
                            int H, int D, int P, int rank, ra_dtype dt, float scale,
                            int causal, long long valid_len, float* dq_r,
                            float* const* dk_blocks, float* const* dv_blocks,
-                           float* delta_ws, void* stream);
+                           float* stats_ws, void* stream);
 
 /* Ulysses sequence-shard -> head-shard transpose ([RA] §3.5) of the P
  * per-rank tensors stacked rank-major:

@@ -419,11 +419,11 @@ def ring_attn_bwd(q_r, k_blocks: Sequence, v_blocks: Sequence, o_r, do_r, lse_r,
         dkp[j], dvp[j] = _dev(dk_blocks[j], "dk").value, _dev(dv_blocks[j], "dv").value
     if dq.shape != q_r.shape or dq.dtype != torch.float32:
         raise ValueError("dq must be fp32 of q_r's shape")
-    delta = torch.empty((B, Sb, H), **f32)
+    stats = torch.empty((2, B, H, Sb), **f32)
     st = _load().ra_ring_attn_bwd(_dev(q_r, "q_r"), kp, vp, _dev(o_r, "o_r"), _dev(do_r, "do_r"),
                                   _dev(lse_r, "lse_r"), B, Sb, H, D, P, rank, dt, float(scale),
                                   int(causal), valid_len, _dev(dq, "dq"), dkp, dvp,
-                                  _dev(delta, "delta"), _stream(stream))
+                                  _dev(stats, "stats"), _stream(stream))
     _check(st, "ra_ring_attn_bwd")
     return dq, dk_blocks, dv_blocks
 

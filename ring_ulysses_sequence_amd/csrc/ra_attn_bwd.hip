@@ -22,35 +22,43 @@
 //     Each lane holds one query column: S^T = K Q^T and dP^T = V dO^T from
 //     K/V rows in LDS, then dQ^T += K^T dS^T with K^T read transposed
 //     (ds_read_b64_tr_b16) and dS^T from registers -- the forward's P V step
-//     with V replaced by K.  It also writes D_r for the second kernel.
+//     with V replaced by K.  It also writes the per-row statistics the second
+//     kernel reads: the base-2 lse and D_r.
 //   ring_attn_bwd_dkv<D, PART>: one workgroup per 128 keys of one visited
 //     block (4 waves x 32 keys).  Each lane holds one key column: S = Q K^T
 //     (and, for dK, dP = dO V^T) from Q/dO rows in LDS, then dV^T += dO^T P
 //     (PART 0) or dK^T += Q^T dS (PART 1) with dO^T / Q^T read transposed.
 //     Two launches rather than one so that each fits two waves per SIMD.
-// Tiles (64 rows) are staged through registers: the next tile's global
-// loads are issued before the current tile is computed and written to the
-// other LDS buffer after it, one barrier per tile.
+// Tiles of 64 rows are copied HBM -> LDS by the buffer unit (buffer_load ...
+// lds), double-buffered: the copy of tile n+1 is issued when tile n starts
+// and has the whole of tile n's compute to land; one wait and one barrier
+// per tile.  Rows are stored with an XOR swizzle of their 16-byte chunks
+// (chunk c of row r at c ^ (r & 15) for D = 128, c ^ ((r >> 1) & 7) for
+// D = 64) so that both the row reads (ds_read_b128) and the transposed reads
+// are free of bank conflicts; the copy picks for every LDS position the
+// global chunk that belongs there.  Operand reads run kPF matrix-op pairs
+// ahead of their use.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 
+#include "ra_cdna4.h"
 #include "ra_internal.h"
 
 namespace {
 
+using namespace ra_cdna4;
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;  // query rows (dq) or keys (dkv) per workgroup
-constexpr int kTile = 64;           // rows per staged tile
+constexpr int kTile = 64;           // rows per copied tile
+constexpr int kPF = 2;              // operand reads in flight ahead of use (pairs)
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdBlock {
@@ -69,7 +77,8 @@ struct BwdArgs {
   const void* dout;   // [B, Sq, H, D] bf16
   const float* lse;   // [B, Sq, H] natural log-sum-exp of the forward
   float* dq;          // [B, Sq, H, D] fp32, accumulated (+=)
-  float* delta;       // [B, Sq, H] fp32: rowsum(dO * O), written by the dq kernel
+  float* stats;       // [2, B, H, Sq] fp32: base-2 lse, then rowsum(dO * O);
+                      // written by the dq kernel, read by the dk/dv kernel
   long long q_pos0;   // global position of query row 0
   long long valid_len;
   int B, Sq, H;
@@ -83,9 +92,17 @@ struct BwdArgs {
 };
 
 template <int D>
+struct Cfg {
+  static constexpr int ROWB = D * 2;                   // bytes per row in LDS
+  static constexpr int TILE = kTile * ROWB;            // one copied tile
+  static constexpr int CHUNKS = D / 8;                 // 16-byte chunks per row
+  static constexpr int DMA = TILE / 1024 / kWaves;     // 1 KiB copies per wave per tile
+  static constexpr int NC = D / 16;                    // k-steps of the score products
+  static constexpr int NDT = D / 32;                   // 32-feature tiles of the gradients
+};
+
+template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
-  // 16-byte chunk c of row r: XOR swizzle that spreads a column of rows over
-  // the LDS banks (the forward's K layout)
   return D == 128 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
 }
 
@@ -95,9 +112,8 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ s16x4 read_tr(const char* smem, unsigned off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(smem + off));
-}
+__device__ __forceinline__ bf16x8 as_bf16(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ __forceinline__ f32x4 as_f32(u32x4 x) { return __builtin_bit_cast(f32x4, x); }
 
 __device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
   const s16x4 x[2] = {lo, hi};
@@ -106,79 +122,162 @@ __device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
   return r;
 }
 
-// A 64-row tile of a [B, rows_b, H, D] bf16 tensor staged through registers
-// into LDS (swizzled rows of D*2 bytes).  Each thread moves UNITS chunks of
-// 16 bytes; rows at or beyond `rows` read as zeros.
+// Copy one 64-row tile (rows at or beyond `rows` read as zeros) whose row 0
+// starts at `src`, rows HD2 bytes apart, into LDS: this wave's Cfg::DMA KiB
+// land at byte address dst, dst + 1024, ..; voff[i] is the source offset of
+// this lane's chunk (row * HD2 + swizzled chunk * 16).
 template <int D>
-struct TileStage {
-  static constexpr int ROWB = D * 2;
-  static constexpr int BYTES = kTile * ROWB;
-  static constexpr int CHUNKS = D / 8;
-  static constexpr int UNITS = BYTES / 16 / kThreads;
-  u32x4 r[UNITS];
-  __device__ __forceinline__ void load(const char* base, int rows, long long row_stride) {
+__device__ __forceinline__ void copy_tile(const char* src, int rows, int HD2, const int* voff,
+                                          unsigned dst) {
+  using C = Cfg<D>;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)src, 0, (rows - 1) * HD2 + C::ROWB, kRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < UNITS; ++i) {
-      const int p = i * kThreads + (int)threadIdx.x;
-      const int row = p / CHUNKS, c = p % CHUNKS;
-      r[i] = row < rows ? *(const u32x4*)(base + row * row_stride + c * 16) : u32x4{0, 0, 0, 0};
-    }
-  }
-  __device__ __forceinline__ void store(char* lds) const {
-#pragma unroll
-    for (int i = 0; i < UNITS; ++i) {
-      const int p = i * kThreads + (int)threadIdx.x;
-      const int row = p / CHUNKS, c = p % CHUNKS;
-      *(u32x4*)(lds + row * ROWB + swz<D>(row, c) * 16) = r[i];
-    }
-  }
-};
+  for (int i = 0; i < C::DMA; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(size_t)(dst + i * 1024), 16,
+                                             voff[i], 0, 0, 0);
+}
 
-// Per-lane LDS byte offsets of the operand reads inside one staged tile:
-//   row_off[c]: A/B fragment of row `col`, features 16c + 8*half .. +7
-//   tr_lo[dt], tr_hi[dt]: transposed reads of rows 4*half + e (+8 for hi) at
+// Per-lane LDS byte addresses of the operand reads in the current buffer:
+//   row[c]: A fragment of row `col`, features 16c + 8*half .. +7
+//   lo[dt], hi[dt]: transposed reads of rows 4*half + e (+8 for hi) at
 //   features 32*dt + 16*(g & 1) + 4*q (ds_read_b64_tr_b16: lane j of each
 //   16-lane group receives element j%4 of the rows supplied by lanes j/4 +
 //   4e, so lane l ends with features 32*dt + l%32 of 4 consecutive rows)
+// Rows 32t + col (row reads) and 16G + .. (transposed reads) keep the same
+// swizzle, so those tiles are reached through the immediate offset.
 template <int D>
-struct TileAddr {
-  static constexpr int ROWB = D * 2;
-  static constexpr int NC = D / 16;
-  static constexpr int NDT = D / 32;
-  int row_off[NC];
-  unsigned tr_lo[NDT], tr_hi[NDT];
-  __device__ __forceinline__ void init(int lane) {
+struct LaneAddr {
+  using C = Cfg<D>;
+  unsigned row[C::NC], lo[C::NDT], hi[C::NDT];
+  __device__ __forceinline__ void init(unsigned base, int lane) {
     const int col = lane & 31, half = lane >> 5;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) row_off[c] = col * ROWB + swz<D>(col, 2 * c + half) * 16;
+    for (int c = 0; c < C::NC; ++c) row[c] = base + col * C::ROWB + swz<D>(col, 2 * c + half) * 16;
     const int j = lane & 15, e = j >> 2, q = j & 3, g = lane >> 4;
     const int kl = 4 * half + e;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+    for (int dt = 0; dt < C::NDT; ++dt) {
       const int d0 = 32 * dt + 16 * (g & 1) + 4 * q;
-      tr_lo[dt] = kl * ROWB + swz<D>(kl, d0 >> 3) * 16 + (d0 & 7) * 2;
-      tr_hi[dt] = (kl + 8) * ROWB + swz<D>(kl + 8, d0 >> 3) * 16 + (d0 & 7) * 2;
+      lo[dt] = base + kl * C::ROWB + swz<D>(kl, d0 >> 3) * 16 + (d0 & 7) * 2;
+      hi[dt] = base + (kl + 8) * C::ROWB + swz<D>(kl + 8, d0 >> 3) * 16 + (d0 & 7) * 2;
     }
   }
-  // transposed A fragment of feature tile dt over rows 16G .. 16G+15
-  __device__ __forceinline__ bf16x8 tr(const char* tile, int G, int dt) const {
-    return join(read_tr(tile, tr_lo[dt] + 16 * G * ROWB), read_tr(tile, tr_hi[dt] + 16 * G * ROWB));
-  }
-  __device__ __forceinline__ bf16x8 row(const char* tile, int rt, int c) const {
-    return *(const bf16x8*)(tile + rt * 32 * ROWB + row_off[c]);
+  __device__ __forceinline__ void shift(int delta) {
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) row[c] += delta;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+      lo[dt] += delta;
+      hi[dt] += delta;
+    }
   }
 };
 
+// Transposed read of rows 16G + .. (G = 2T + g, g a constant after unrolling)
+// at tile offset OFF.
+template <int D, int OFF>
+__device__ __forceinline__ s16x4 read_tr_g(int g, unsigned addr) {
+  constexpr int G1 = 16 * Cfg<D>::ROWB;
+  return g ? lds_read_tr16<OFF + G1>(addr) : lds_read_tr16<OFF>(addr);
+}
+
+// Source offsets of this lane's copy chunks within a tile.
+template <int D>
+__device__ __forceinline__ void copy_offsets(int wave, int lane, int HD2, int* voff) {
+  using C = Cfg<D>;
+#pragma unroll
+  for (int i = 0; i < C::DMA; ++i) {
+    const int p = (wave * C::DMA + i) * 64 + lane;  // physical chunk in the tile
+    const int r = p / C::CHUNKS, pc = p % C::CHUNKS;
+    voff[i] = r * HD2 + swz<D>(r, pc) * 16;
+  }
+}
+
 // ---------------------------------------------------------------------------
-// dQ (and D = rowsum(dO * O)): one workgroup per (batch, head, 128 rows)
+// dQ (and the row statistics): one workgroup per (batch, head, 128 rows)
 // ---------------------------------------------------------------------------
+template <int D>
+struct DqLane {
+  using C = Cfg<D>;
+  bf16x8 qf[C::NC], df[C::NC];  // this lane's query row of Q and dO (B operands)
+  f32x16 acc[C::NDT];           // dQ^T
+  LaneAddr<D> ad;
+};
+
+// Rows 32T .. 32T+31 of the K/V tiles in the current buffer (K at 0, V at
+// TILE): S^T, dP^T, the mask, dS^T and dQ^T += K^T dS^T.
+template <int D, int T>
+__device__ __forceinline__ void dq_half(DqLane<D>& w, float dsum, float lse2, float c_scale,
+                                        bool need, int lim_h) {
+  using C = Cfg<D>;
+  constexpr int RO = T * 32 * C::ROWB;
+  constexpr int NB = kPF + 1;
+  f32x16 sc = f32x16{}, dpt = f32x16{};
+  {
+    u32x4 ka[NB], va[NB];
+#pragma unroll
+    for (int c = 0; c < kPF; ++c) {
+      ka[c] = lds_read_b128<RO>(w.ad.row[c]);
+      va[c] = lds_read_b128<C::TILE + RO>(w.ad.row[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) {
+      if (c + kPF < C::NC) {
+        ka[(c + kPF) % NB] = lds_read_b128<RO>(w.ad.row[c + kPF]);
+        va[(c + kPF) % NB] = lds_read_b128<C::TILE + RO>(w.ad.row[c + kPF]);
+      }
+      const int n = 2 * min(kPF, C::NC - 1 - c);
+      claim_lds_n(n, ka[c % NB]);
+      claim_lds_n(n, va[c % NB]);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(ka[c % NB]), w.qf[c], sc, 0, 0, 0);
+      dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(va[c % NB]), w.df[c], dpt, 0, 0, 0);
+    }
+  }
+  // the first K^T reads of the dQ product fly during the exponentials
+  constexpr int NJ = 2 * C::NDT;  // (g, dt) pairs, g major
+  s16x4 lo[NB], hi[NB];
+#pragma unroll
+  for (int j = 0; j < kPF; ++j) {
+    lo[j] = read_tr_g<D, 32 * T * C::ROWB>(j / C::NDT, w.ad.lo[j % C::NDT]);
+    hi[j] = read_tr_g<D, 32 * T * C::ROWB>(j / C::NDT, w.ad.hi[j % C::NDT]);
+  }
+  // key j of the tile (j = 32T + 8(v/4) + 4half + v%4) is hidden for this
+  // lane's query when j >= lim_h + 4half
+  if (need) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (32 * T + 8 * (v >> 2) + (v & 3) >= lim_h) sc[v] = -INFINITY;
+  }
+  // dS^T = P^T (dP^T - D), packed as the B operand of K^T dS^T
+  bf16x8 dsb[2];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const float p = __builtin_amdgcn_exp2f(sc[v] * c_scale - lse2);
+    dsb[v >> 3][v & 7] = (__bf16)(p * (dpt[v] - dsum));
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    if (j + kPF < NJ) {
+      const int jn = j + kPF;
+      lo[jn % NB] = read_tr_g<D, 32 * T * C::ROWB>(jn / C::NDT, w.ad.lo[jn % C::NDT]);
+      hi[jn % NB] = read_tr_g<D, 32 * T * C::ROWB>(jn / C::NDT, w.ad.hi[jn % C::NDT]);
+    }
+    const int n = 2 * min(kPF, NJ - 1 - j);
+    claim_lds_n(n, lo[j % NB]);
+    claim_lds_n(n, hi[j % NB]);
+    const int dt = j % C::NDT;
+    w.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(lo[j % NB], hi[j % NB]),
+                                                        dsb[j / C::NDT], w.acc[dt], 0, 0, 0);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ring_attn_bwd_dq(const BwdArgs a) {
-  constexpr int NC = D / 16, NDT = D / 32, ROWB = D * 2;
-  using TS = TileStage<D>;
+  using C = Cfg<D>;
   // two buffers, each a K tile then a V tile
-  __shared__ __attribute__((aligned(16))) char smem[2][2 * TS::BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[2][2 * C::TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
@@ -191,12 +290,12 @@ void ring_attn_bwd_dq(const BwdArgs a) {
   const int wrows = min(32, a.Sq - wrow0);
   const long long wq_lo = a.q_pos0 + wrow0, wq_hi = wq_lo + wrows - 1;
   const long long HD = (long long)a.H * D;
-  const long long row_stride = HD * 2;  // bytes between K/V rows
+  const int HD2 = (int)(HD * 2);  // bytes between K/V rows
 
-  // this lane's query row: Q and dO fragments (B operands), D and lse
+  // this lane's query row: Q and dO fragments, D and the base-2 lse
+  DqLane<D> w;
   const int r = wrow0 + col;
   const bool row_ok = r < a.Sq;
-  bf16x8 qf[NC], df[NC];
   float dsum = 0.0f;
   {
     const long long off = ((long long)b * a.Sq + r) * HD + (long long)h * D;
@@ -204,31 +303,35 @@ void ring_attn_bwd_dq(const BwdArgs a) {
     const __bf16* dp = (const __bf16*)a.dout + off;
     const __bf16* op = (const __bf16*)a.o + off;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    for (int c = 0; c < C::NC; ++c) {
       const int d = 16 * c + 8 * half;
-      qf[c] = row_ok ? *(const bf16x8*)(qp + d) : bf16x8{};
-      df[c] = row_ok ? *(const bf16x8*)(dp + d) : bf16x8{};
+      w.qf[c] = row_ok ? *(const bf16x8*)(qp + d) : bf16x8{};
+      w.df[c] = row_ok ? *(const bf16x8*)(dp + d) : bf16x8{};
       const bf16x8 of = row_ok ? *(const bf16x8*)(op + d) : bf16x8{};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dsum += (float)df[c][e] * (float)of[e];
+      for (int e = 0; e < 8; ++e) dsum += (float)w.df[c][e] * (float)of[e];
     }
   }
   dsum = pair_sum(dsum);
-  const long long so = ((long long)b * a.Sq + r) * a.H + h;
-  if (row_ok && half == 0) a.delta[so] = dsum;
-  // base-2 lse; a row that saw no key in the forward gets +inf, so every
-  // probability of it is 0 (its scores are all masked anyway)
+  // a row that saw no key in the forward gets +inf, so every probability of
+  // it is 0 (its scores are all masked anyway)
   float lse2 = INFINITY;
   if (row_ok) {
-    const float l = a.lse[so];
+    const float l = a.lse[((long long)b * a.Sq + r) * a.H + h];
     lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    if (half == 0) {
+      const long long so = ((long long)b * a.H + h) * a.Sq + r;
+      a.stats[so] = lse2;
+      a.stats[(long long)a.B * a.H * a.Sq + so] = dsum;
+    }
   }
-
-  TileAddr<D> ad;
-  ad.init(lane);
-  f32x16 acc[NDT];
 #pragma unroll
-  for (int i = 0; i < NDT; ++i) acc[i] = f32x16{};
+  for (int i = 0; i < C::NDT; ++i) w.acc[i] = f32x16{};
+  const unsigned base = lds_addr(smem);
+  w.ad.init(base, lane);
+  int voff[C::DMA];
+  copy_offsets<D>(wave, lane, HD2, voff);
+  const unsigned dst0 = base + wave * C::DMA * 1024;
 
   // visited tiles: all blocks in order, tiles up to the last one with a
   // key visible to the workgroup's last query
@@ -241,47 +344,37 @@ void ring_attn_bwd_dq(const BwdArgs a) {
     const long long last = (lim - kb.k_pos0) / kTile + 1;
     return last < n ? (int)last : n;
   };
+  auto copy_kv = [&](int bi, int ti, unsigned dst) {
+    const BwdBlock& kb = a.blk[bi];
+    const long long off = (((long long)b * a.kv_rows_b + (long long)ti * kTile) * a.H + h) * D * 2;
+    const int rows = min(kTile, kb.len - ti * kTile);
+    copy_tile<D>((const char*)kb.k + off, rows, HD2, voff, dst);
+    copy_tile<D>((const char*)kb.v + off, rows, HD2, voff, dst + C::TILE);
+  };
   int cb = 0, ct = 0, cn = 0;
   while (cb < a.nblk && (cn = ntiles(cb)) == 0) ++cb;
-
-  // one staging register set, used for the next tile's K, then its V
-  TS st;
-  auto src_of = [&](int bi, int ti, const void* base) -> const char* {
-    return (const char*)base +
-           (((long long)b * a.kv_rows_b + (long long)ti * kTile) * a.H + h) * D * 2;
-  };
+  if (cb < a.nblk) copy_kv(cb, 0, dst0);
+  wait_vmcnt<0>();
+  pipeline_barrier();
   int buf = 0;
-  if (cb < a.nblk) {
-    const int rows = min(kTile, a.blk[cb].len);
-    st.load(src_of(cb, 0, a.blk[cb].k), rows, row_stride);
-    st.store(smem[0]);
-    st.load(src_of(cb, 0, a.blk[cb].v), rows, row_stride);
-    st.store(smem[0] + TS::BYTES);
-  }
-  __syncthreads();
   const float c_scale = a.scale_log2;
   while (cb < a.nblk) {
-    // next tile's position; its K loads fly during the first half of this
-    // tile, its V loads during the second (the other buffer was last read
-    // in the previous iteration, before its closing barrier)
+    // the next tile's copy goes to the other buffer, last read in the
+    // previous iteration (before its closing barrier)
     int nb = cb, nt = ct + 1, nn = cn;
     if (nt >= nn) {
       nt = 0;
       ++nb;
       while (nb < a.nblk && (nn = ntiles(nb)) == 0) ++nb;
     }
-    const bool more = nb < a.nblk;
-    const int nrows = more ? min(kTile, a.blk[nb].len - nt * kTile) : 0;
-    if (more) st.load(src_of(nb, nt, a.blk[nb].k), nrows, row_stride);
+    if (nb < a.nblk) copy_kv(nb, nt, dst0 + (buf ^ 1) * 2 * C::TILE);
 
     const BwdBlock& kb = a.blk[cb];
     const long long kp0 = kb.k_pos0 + (long long)ct * kTile;
-    const char* kt = smem[buf];
-    const char* vt = smem[buf] + TS::BYTES;
     const bool live = wrows > 0 && !(a.causal && kp0 > wq_hi);
-    // mask: key j of the tile (j = 32t + 8(v/4) + 4half + v%4) is hidden
-    // for this lane's query when j >= the keys left in the block or at or
-    // beyond valid_len, or (causal) when it lies after the query
+    // mask: key j of the tile is hidden for this lane's query when j >= the
+    // keys left in the block or at or beyond valid_len, or (causal) when it
+    // lies after the query
     long long lim_ll = kb.len - (long long)ct * kTile;
     if (a.valid_len - kp0 < lim_ll) lim_ll = a.valid_len - kp0;
     const bool need = lim_ll < kTile || (a.causal && kp0 + kTile - 1 > wq_lo);
@@ -292,46 +385,13 @@ void ring_attn_bwd_dq(const BwdArgs a) {
     }
     // as a 32-bit bound relative to this lane's first key of each group
     const int lim_h = (int)(lim < 0 ? 0 : (lim > kTile ? kTile : lim)) - 4 * half;
-    // one 32-key half of the tile at a time (keeps two waves per SIMD)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (live) {
-        f32x16 sc = f32x16{}, dpt = f32x16{};
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.row(kt, t, c), qf[c], sc, 0, 0, 0);
-          dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.row(vt, t, c), df[c], dpt, 0, 0, 0);
-          // keep the operand reads next to their products (bounded live range)
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (need) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (32 * t + 8 * (v >> 2) + (v & 3) >= lim_h) sc[v] = -INFINITY;
-        }
-        // dS^T = P^T (dP^T - D), packed as the B operand of K^T dS^T
-        bf16x8 dsb[2];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f(sc[v] * c_scale - lse2);
-          dsb[v >> 3][v & 7] = (__bf16)(p * (dpt[v] - dsum));
-        }
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.tr(kt, 2 * t + g, dt), dsb[g],
-                                                              acc[dt], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-      }
-      if (t == 0 && more) {
-        st.store(smem[buf ^ 1]);
-        st.load(src_of(nb, nt, a.blk[nb].v), nrows, row_stride);
-      }
+    if (live) {
+      dq_half<D, 0>(w, dsum, lse2, c_scale, need, lim_h);
+      dq_half<D, 1>(w, dsum, lse2, c_scale, need, lim_h);
     }
-    if (more) st.store(smem[buf ^ 1] + TS::BYTES);
-    __syncthreads();
+    wait_vmcnt<0>();
+    pipeline_barrier();
+    w.ad.shift(buf ? -2 * C::TILE : 2 * C::TILE);
     buf ^= 1;
     cb = nb;
     ct = nt;
@@ -342,15 +402,15 @@ void ring_attn_bwd_dq(const BwdArgs a) {
   if (row_ok) {
     float* dqp = a.dq + ((long long)b * a.Sq + r) * HD + (long long)h * D;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         float4* p = (float4*)(dqp + 32 * dt + 8 * g + 4 * half);
         float4 x = *p;
-        x.x += a.scale * acc[dt][4 * g + 0];
-        x.y += a.scale * acc[dt][4 * g + 1];
-        x.z += a.scale * acc[dt][4 * g + 2];
-        x.w += a.scale * acc[dt][4 * g + 3];
+        x.x += a.scale * w.acc[dt][4 * g + 0];
+        x.y += a.scale * w.acc[dt][4 * g + 1];
+        x.z += a.scale * w.acc[dt][4 * g + 2];
+        x.w += a.scale * w.acc[dt][4 * g + 3];
         *p = x;
       }
   }
@@ -362,13 +422,116 @@ void ring_attn_bwd_dq(const BwdArgs a) {
 // PART 0 accumulates dV (needs S only), PART 1 dK (needs S and dP): split so
 // that each fits two waves per SIMD; the scores are recomputed in both.
 template <int D, int PART>
+struct DkvLane {
+  using C = Cfg<D>;
+  bf16x8 kf[C::NC], vf[PART == 1 ? C::NC : 1];  // this lane's key row of K, V
+  f32x16 acc[C::NDT];                           // dK^T (PART 1) or dV^T (PART 0)
+  LaneAddr<D> ad;
+  unsigned sa;  // LDS address of this lane's statistics (rows 4*half ..)
+};
+
+// Query rows 32T .. 32T+31 of the tiles in the current buffer (Q at 0, dO at
+// TILE, base-2 lse at 2*TILE, D at 2*TILE + 256).
+template <int D, int PART, int T>
+__device__ __forceinline__ void dkv_half(DkvLane<D, PART>& w, float c_scale, bool need,
+                                         int rel_h) {
+  using C = Cfg<D>;
+  constexpr bool DK = PART == 1;
+  constexpr int RO = T * 32 * C::ROWB;
+  constexpr int NB = kPF + 1;
+  constexpr int NR = DK ? 2 : 1;  // row reads per k-step
+  f32x16 sc = f32x16{}, dpt = f32x16{};
+  {
+    u32x4 qa[NB], da[DK ? NB : 1];
+#pragma unroll
+    for (int c = 0; c < kPF; ++c) {
+      qa[c] = lds_read_b128<RO>(w.ad.row[c]);
+      if constexpr (DK) da[c] = lds_read_b128<C::TILE + RO>(w.ad.row[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) {
+      if (c + kPF < C::NC) {
+        qa[(c + kPF) % NB] = lds_read_b128<RO>(w.ad.row[c + kPF]);
+        if constexpr (DK) da[(c + kPF) % NB] = lds_read_b128<C::TILE + RO>(w.ad.row[c + kPF]);
+      }
+      const int n = NR * min(kPF, C::NC - 1 - c);
+      claim_lds_n(n, qa[c % NB]);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(qa[c % NB]), w.kf[c], sc, 0, 0, 0);
+      if constexpr (DK) {
+        claim_lds_n(n, da[c % NB]);
+        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(da[c % NB]), w.vf[c], dpt, 0, 0, 0);
+      }
+    }
+  }
+  // statistics of the 16 query rows of this lane, then the first reads of
+  // the gradient product, all in flight during the wait for the scores
+  u32x4 ls[4], ds[DK ? 4 : 1];
+  constexpr int SO = 2 * C::TILE + 128 * T;
+  ls[0] = lds_read_b128<SO + 0>(w.sa);
+  ls[1] = lds_read_b128<SO + 32>(w.sa);
+  ls[2] = lds_read_b128<SO + 64>(w.sa);
+  ls[3] = lds_read_b128<SO + 96>(w.sa);
+  if constexpr (DK) {
+    ds[0] = lds_read_b128<SO + 256>(w.sa);
+    ds[1] = lds_read_b128<SO + 256 + 32>(w.sa);
+    ds[2] = lds_read_b128<SO + 256 + 64>(w.sa);
+    ds[3] = lds_read_b128<SO + 256 + 96>(w.sa);
+  }
+  constexpr int NJ = 2 * C::NDT;
+  constexpr int TO = (DK ? 0 : C::TILE) + 32 * T * C::ROWB;  // Q^T (dK) or dO^T (dV)
+  s16x4 lo[NB], hi[NB];
+#pragma unroll
+  for (int j = 0; j < kPF; ++j) {
+    lo[j] = read_tr_g<D, TO>(j / C::NDT, w.ad.lo[j % C::NDT]);
+    hi[j] = read_tr_g<D, TO>(j / C::NDT, w.ad.hi[j % C::NDT]);
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    claim_lds<2 * kPF>(ls[g]);
+    if constexpr (DK) claim_lds<2 * kPF>(ds[g]);
+  }
+  // element (query m = 32T + 8g + 4half + i, this lane's key) is hidden when
+  // m < rel_h + 4half
+  bf16x8 pb[2];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 l4 = as_f32(ls[g]);
+    const f32x4 d4 = as_f32(ds[DK ? g : 0]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = 4 * g + i;
+      float x = sc[v] * c_scale - l4[i];
+      if (need && 32 * T + 8 * g + i < rel_h) x = -INFINITY;
+      const float p = __builtin_amdgcn_exp2f(x);
+      if constexpr (DK) pb[v >> 3][v & 7] = (__bf16)(p * (dpt[v] - d4[i]));
+      else pb[v >> 3][v & 7] = (__bf16)p;
+    }
+  }
+  // dK^T += Q^T dS (PART 1) or dV^T += dO^T P (PART 0)
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    if (j + kPF < NJ) {
+      const int jn = j + kPF;
+      lo[jn % NB] = read_tr_g<D, TO>(jn / C::NDT, w.ad.lo[jn % C::NDT]);
+      hi[jn % NB] = read_tr_g<D, TO>(jn / C::NDT, w.ad.hi[jn % C::NDT]);
+    }
+    const int n = 2 * min(kPF, NJ - 1 - j);
+    claim_lds_n(n, lo[j % NB]);
+    claim_lds_n(n, hi[j % NB]);
+    const int d = j % C::NDT;
+    w.acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(lo[j % NB], hi[j % NB]),
+                                                       pb[j / C::NDT], w.acc[d], 0, 0, 0);
+  }
+}
+
+template <int D, int PART>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ring_attn_bwd_dkv(const BwdArgs a) {
-  constexpr int NC = D / 16, NDT = D / 32;
-  using TS = TileStage<D>;
-  // two buffers, each: Q tile, dO tile, lse2 (64 floats), D (64 floats)
-  constexpr int BUF = 2 * TS::BYTES + 2 * kTile * 4;
-  __shared__ __attribute__((aligned(16))) char smem[2][BUF];
+  using C = Cfg<D>;
+  constexpr bool DK = PART == 1;
+  // two buffers, each: Q tile, dO tile, base-2 lse (64 floats), D (64 floats)
+  constexpr int BUF = 2 * C::TILE + 2 * kTile * 4;
+  __shared__ __attribute__((aligned(1024))) char smem[2][BUF];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
@@ -381,7 +544,7 @@ void ring_attn_bwd_dkv(const BwdArgs a) {
   const int bi = id / a.B;
   const BwdBlock& kb = a.blk[bi];
   const long long HD = (long long)a.H * D;
-  const long long row_stride = HD * 2;
+  const int HD2 = (int)(HD * 2);
 
   // this lane's key row of the block: K and V fragments (B operands)
   const int kr = kt * kRows + wave * 32 + col;
@@ -389,24 +552,25 @@ void ring_attn_bwd_dkv(const BwdArgs a) {
   const long long kpos = kb.k_pos0 + kr;
   const long long kw_lo = kb.k_pos0 + kt * kRows + wave * 32;
   const long long kw_hi = kw_lo + 31;
-  constexpr bool DK = PART == 1;
-  bf16x8 kf[NC], vf[DK ? NC : 1];
+  DkvLane<D, PART> w;
   {
     const long long off = ((long long)b * a.kv_rows_b + kr) * HD + (long long)h * D;
     const __bf16* kp = (const __bf16*)kb.k + off;
     const __bf16* vp = (const __bf16*)kb.v + off;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    for (int c = 0; c < C::NC; ++c) {
       const int d = 16 * c + 8 * half;
-      kf[c] = key_ok ? *(const bf16x8*)(kp + d) : bf16x8{};
-      if constexpr (DK) vf[c] = key_ok ? *(const bf16x8*)(vp + d) : bf16x8{};
+      w.kf[c] = key_ok ? *(const bf16x8*)(kp + d) : bf16x8{};
+      if constexpr (DK) w.vf[c] = key_ok ? *(const bf16x8*)(vp + d) : bf16x8{};
     }
   }
-  TileAddr<D> ad;
-  ad.init(lane);
-  f32x16 acc[NDT];  // dK^T (PART 1) or dV^T (PART 0)
 #pragma unroll
-  for (int i = 0; i < NDT; ++i) acc[i] = f32x16{};
+  for (int i = 0; i < C::NDT; ++i) w.acc[i] = f32x16{};
+  const unsigned base = lds_addr(smem);
+  w.ad.init(base, lane);
+  w.sa = base + 16 * half;
+  int voff[C::DMA];
+  copy_offsets<D>(wave, lane, HD2, voff);
 
   // query tiles that can see a key of this workgroup (causal: from the one
   // holding position k_lo on)
@@ -415,118 +579,52 @@ void ring_attn_bwd_dkv(const BwdArgs a) {
   if (a.causal && k_lo > a.q_pos0) t0 = (int)min((long long)a.Sq, (k_lo - a.q_pos0) / kTile);
   const int n_t = (a.Sq + kTile - 1) / kTile;
 
-  // one staging register set, used for the next tile's Q, then its dO
-  TS st;
-  float stat = 0.0f;  // one lse2 (threads 0-63) or D (64-127) value
-  auto src_of = [&](int ti, const void* base) -> const char* {
-    return (const char*)base + (((long long)b * a.Sq + (long long)ti * kTile) * a.H + h) * D * 2;
-  };
-  auto load_stat = [&](int ti) {
-    if (tid < 2 * kTile) {
-      const int rr = ti * kTile + (tid & (kTile - 1));
-      const long long so = ((long long)b * a.Sq + rr) * a.H + h;
-      if (tid < kTile) {
-        // base-2 lse; +inf for rows past the end or rows that saw no key
-        const float l = rr < a.Sq ? a.lse[so] : -INFINITY;
-        stat = l == -INFINITY ? INFINITY : l * kLog2e;
-      } else {
-        stat = rr < a.Sq ? a.delta[so] : 0.0f;
-      }
+  // Q and dO tiles by all waves; the statistics (64 floats each) by wave 0
+  // (lse) and wave 1 (D)
+  const long long stat0 = ((long long)b * a.H + h) * a.Sq;
+  auto copy_q = [&](int ti, unsigned buf_base) {
+    const long long off = (((long long)b * a.Sq + (long long)ti * kTile) * a.H + h) * D * 2;
+    const int rows = min(kTile, a.Sq - ti * kTile);
+    copy_tile<D>((const char*)a.q + off, rows, HD2, voff, buf_base + wave * C::DMA * 1024);
+    copy_tile<D>((const char*)a.dout + off, rows, HD2, voff,
+                 buf_base + C::TILE + wave * C::DMA * 1024);
+    if (wave < (DK ? 2 : 1)) {
+      const float* src = a.stats + (wave ? (long long)a.B * a.H * a.Sq : 0) + stat0 + ti * kTile;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, rows * 4, kRsrcWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void_ptr)(size_t)(buf_base + 2 * C::TILE + wave * 256), 4, lane * 4, 0, 0, 0);
     }
   };
-  auto put_stat = [&](char* dst) {
-    if (tid < 2 * kTile) ((float*)(dst + 2 * TS::BYTES))[tid] = stat;
-  };
+  if (t0 < n_t) copy_q(t0, base);
+  wait_vmcnt<0>();
+  pipeline_barrier();
   int buf = 0;
-  if (t0 < n_t) {
-    const int rows = min(kTile, a.Sq - t0 * kTile);
-    st.load(src_of(t0, a.q), rows, row_stride);
-    st.store(smem[0]);
-    st.load(src_of(t0, a.dout), rows, row_stride);
-    st.store(smem[0] + TS::BYTES);
-    load_stat(t0);
-    put_stat(smem[0]);
-  }
-  __syncthreads();
   const float c_scale = a.scale_log2;
   for (int ti = t0; ti < n_t; ++ti) {
-    // next tile: its Q loads fly during the first half of this tile, its dO
-    // loads during the second (the other buffer was last read in the
-    // previous iteration, before its closing barrier)
-    const bool more = ti + 1 < n_t;
-    const int nrows = more ? min(kTile, a.Sq - (ti + 1) * kTile) : 0;
-    if (more) {
-      st.load(src_of(ti + 1, a.q), nrows, row_stride);
-      load_stat(ti + 1);
-    }
-    const char* qt = smem[buf];
-    const char* dt_ = smem[buf] + TS::BYTES;
-    const float* ls = (const float*)(smem[buf] + 2 * TS::BYTES);
-    const float* ds_ = ls + kTile;
+    // the next tile's copy goes to the other buffer, last read in the
+    // previous iteration (before its closing barrier)
+    if (ti + 1 < n_t) copy_q(ti + 1, base + (buf ^ 1) * BUF);
     const long long qp0 = a.q_pos0 + (long long)ti * kTile;
     const long long qp_hi = qp0 + min(kTile, a.Sq - ti * kTile) - 1;
     const bool live = !(a.causal && kw_lo > qp_hi) && kw_lo < a.valid_len;
-    // element (query m = 32t + 8g + 4half + i of the tile, this lane's key)
-    // is hidden when the key is padding or (causal) after the query, i.e.
-    // m < rel with rel = key - first query of the tile (32-bit, clamped)
+    // element (query m of the tile, this lane's key) is hidden when the key
+    // is padding or (causal) after the query, i.e. m < rel with rel = key -
+    // first query of the tile (32-bit, clamped)
     const bool need = kw_hi >= a.valid_len || (a.causal && kw_hi > qp0);
     int rel = 0;
     if (kpos >= a.valid_len) rel = kTile;
     else if (a.causal) rel = (int)max(0LL, min((long long)kTile, kpos - qp0));
     const int rel_h = rel - 4 * half;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (live) {
-        f32x16 sc = f32x16{}, dpt = f32x16{};
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.row(qt, t, c), kf[c], sc, 0, 0, 0);
-          if constexpr (DK)
-            dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.row(dt_, t, c), vf[c], dpt, 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        bf16x8 pb[2], sb[2];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int m0 = 32 * t + 8 * g + 4 * half;
-          const float4 l4 = *(const float4*)(ls + m0);
-          const float4 d4 = *(const float4*)(ds_ + m0);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int v = 4 * g + i;
-            float x = sc[v] * c_scale - lv[i];
-            if (need && 32 * t + 8 * g + i < rel_h) x = -INFINITY;
-            const float p = __builtin_amdgcn_exp2f(x);
-            if constexpr (DK) sb[v >> 3][v & 7] = (__bf16)(p * (dpt[v] - dv4[i]));
-            else pb[v >> 3][v & 7] = (__bf16)p;
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-          for (int d = 0; d < NDT; ++d) {
-            if constexpr (DK)
-              acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.tr(qt, 2 * t + g, d), sb[g],
-                                                               acc[d], 0, 0, 0);
-            else
-              acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.tr(dt_, 2 * t + g, d), pb[g],
-                                                               acc[d], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-      }
-      if (t == 0 && more) {
-        st.store(smem[buf ^ 1]);
-        st.load(src_of(ti + 1, a.dout), nrows, row_stride);
-      }
+    if (live) {
+      dkv_half<D, PART, 0>(w, c_scale, need, rel_h);
+      dkv_half<D, PART, 1>(w, c_scale, need, rel_h);
     }
-    if (more) {
-      st.store(smem[buf ^ 1] + TS::BYTES);
-      put_stat(smem[buf ^ 1]);
-    }
-    __syncthreads();
+    wait_vmcnt<0>();
+    pipeline_barrier();
+    const int delta = buf ? -BUF : BUF;
+    w.ad.shift(delta);
+    w.sa += delta;
     buf ^= 1;
   }
 
@@ -535,15 +633,15 @@ void ring_attn_bwd_dkv(const BwdArgs a) {
     float* dst = (DK ? kb.dk : kb.dv) + off;
     const float f = DK ? a.scale : 1.0f;
 #pragma unroll
-    for (int d = 0; d < NDT; ++d)
+    for (int d = 0; d < C::NDT; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         float4* p = (float4*)(dst + 32 * d + 8 * g + 4 * half);
         float4 x = *p;
-        x.x += f * acc[d][4 * g + 0];
-        x.y += f * acc[d][4 * g + 1];
-        x.z += f * acc[d][4 * g + 2];
-        x.w += f * acc[d][4 * g + 3];
+        x.x += f * w.acc[d][4 * g + 0];
+        x.y += f * w.acc[d][4 * g + 1];
+        x.z += f * w.acc[d][4 * g + 2];
+        x.w += f * w.acc[d][4 * g + 3];
         *p = x;
       }
   }
@@ -559,7 +657,7 @@ extern "C" ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_bloc
                                       int H, int D, int P, int rank, ra_dtype dt, float scale,
                                       int causal, long long valid_len, float* dq_r,
                                       float* const* dk_blocks, float* const* dv_blocks,
-                                      float* delta_ws, void* stream) {
+                                      float* stats_ws, void* stream) {
   static const char* name = "ra_ring_attn_bwd";
   ra::clear_error();
   if (B < 0 || Sb < 0 || H < 0)
@@ -572,7 +670,7 @@ extern "C" ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_bloc
   if (P > RA_MAX_P) return ra::fail(RA_ERR_RANGE, "%s: P=%d exceeds RA_MAX_P=%d", name, P, RA_MAX_P);
   if (rank < 0 || rank >= P) return ra::fail(RA_ERR_RANGE, "%s: rank %d outside [0, %d)", name, rank, P);
   if ((long long)B * Sb * H == 0) return RA_OK;
-  if (!q_r || !o_r || !do_r || !lse_r || !dq_r || !delta_ws || !k_blocks || !v_blocks ||
+  if (!q_r || !o_r || !do_r || !lse_r || !dq_r || !stats_ws || !k_blocks || !v_blocks ||
       !dk_blocks || !dv_blocks)
     return ra::fail(RA_ERR_NULL, "%s: NULL argument", name);
   if (!aligned16(q_r) || !aligned16(o_r) || !aligned16(do_r) || !aligned16(dq_r))
@@ -585,7 +683,7 @@ extern "C" ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_bloc
   a.dout = do_r;
   a.lse = lse_r;
   a.dq = dq_r;
-  a.delta = delta_ws;
+  a.stats = stats_ws;
   a.q_pos0 = (long long)rank * Sb;
   a.valid_len = valid_len;
   a.B = B;
@@ -619,7 +717,7 @@ extern "C" ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_bloc
   const long long n_dkv = (long long)a.nblk * B * H * a.n_ktiles;
   if (n_dq > 0x7fffffffLL || n_dkv > 0x7fffffffLL)
     return ra::fail(RA_ERR_UNSUPPORTED, "%s: grid too large", name);
-  // dq first: it writes D = rowsum(dO * O), which the dk/dv kernel reads
+  // dq first: it writes the row statistics that the dk/dv kernels read
   if (D == 128) hipLaunchKernelGGL(ring_attn_bwd_dq<128>, dim3((unsigned)n_dq), dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL(ring_attn_bwd_dq<64>, dim3((unsigned)n_dq), dim3(kThreads), 0, s, a);
   if (n_dkv > 0) {
