@@ -246,6 +246,32 @@ ra_status ra_zigzag_attn_fwd(const void* q_r, const void* const* k_shares,
                              int causal, long long valid_len, void* o,
                              float* lse_opt, void* stream);
 
+/* Backward of one round ([RA] §3.3 closing paragraph, §6.2): the gradient
+ * terms of one K/V block for one query shard, the unit the ring backward
+ * repeats as each block arrives.  q, o (the forward's final output), dout
+ * [B,Sq,H,D] and k, v [B,Sk,H,D]: device, bf16, contiguous; lse [B,Sq,H]
+ * fp32, the natural log-sum-exp of the WHOLE forward (over every block the
+ * rows attend to, as ra_ring_attn_fwd returns it), so that
+ * P = exp(scale * Q K^T - lse) are this block's true probabilities
+ * (masked pairs 0).  Global positions q_pos0 / k_pos0, causal and
+ * valid_len (< 0: no padding) as in ra_block_attn_fwd.  With
+ * D = rowsum(dO * O), accumulates (+=, the caller zeroes):
+ *   dq [B,Sq,H,D] fp32 += scale * (P * (dO V^T - D)) K
+ *   dk [B,Sk,H,D] fp32 += scale * (P * (dO V^T - D))^T Q
+ *   dv [B,Sk,H,D] fp32 += P^T dO
+ * A block with no visible pair (SKIP) returns at once without touching
+ * anything.  stats_ws: fp32 scratch of 2*B*Sq*H floats the call
+ * overwrites.  Three launches on `stream`.  Only bf16 inputs
+ * (RA_ERR_UNSUPPORTED for fp32); D 64 or 128; tensors 16-byte aligned
+ * (RA_ERR_SHAPE); NULL pointers with non-empty sizes RA_ERR_NULL. */
+ra_status ra_block_attn_bwd(const void* q, const void* k, const void* v,
+                            const void* o, const void* dout, const float* lse,
+                            int B, int Sq, int Sk, int H, int D, ra_dtype dt,
+                            float scale, long long q_pos0, long long k_pos0,
+                            int causal, long long valid_len, float* dq,
+                            float* dk, float* dv, float* stats_ws,
+                            void* stream);
+
 /* Backward of rank `rank`'s ring ([RA] §3.3 closing paragraph, §6.2): the
  * gradients of the loss with respect to the rank's queries and to the K/V
  * blocks it visits, given the upstream gradient dO.  Inputs (device, bf16,

@@ -42,7 +42,7 @@ EXPORTED = (
     "ra_classify_block", "ra_ring_schedule", "ra_block_attn_fwd",
     "ra_ring_merge", "ra_ring_attn_fwd", "ra_seq2head", "ra_head2seq",
     "ra_zigzag_padded_len", "ra_zigzag_schedule", "ra_zigzag_attn_fwd", "ra_ring_attn_bwd",
-    "ra_ring_attn_fwd_gqa", "ra_ring_attn_fwd_varlen",
+    "ra_ring_attn_fwd_gqa", "ra_ring_attn_fwd_varlen", "ra_block_attn_bwd",
 )
 
 _lib = None
@@ -98,6 +98,9 @@ def _load():
                                      c_vp, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                      c_float, c_int, c_ll, c_vp, ctypes.POINTER(c_vp),
                                      ctypes.POINTER(c_vp), c_vp, c_vp]),
+        "ra_block_attn_bwd": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int,
+                                      c_int, c_int, c_int, c_float, c_ll, c_ll, c_int, c_ll,
+                                      c_vp, c_vp, c_vp, c_vp, c_vp]),
         "ra_seq2head": (c_int, [c_vp, c_vp, c_int, c_int, c_ll, c_int, c_int, c_int, c_vp]),
         "ra_head2seq": (c_int, [c_vp, c_vp, c_int, c_int, c_ll, c_int, c_int, c_int, c_vp]),
     }
@@ -380,6 +383,41 @@ def zigzag_attn_fwd(q_r, k_shares: Sequence, v_shares: Sequence, rank: int, *,
     return o, lse
 
 
+def block_attn_bwd(q, k, v, o, do, lse, *, scale: float = 0.0, q_pos0: int = 0,
+                   k_pos0: int = 0, causal: bool = False, valid_len: int = -1,
+                   dq=None, dk=None, dv=None, stream=None):
+    """Backward of one round: accumulates this K/V block's gradient terms
+    into (dq [B,Sq,H,D], dk, dv [B,Sk,H,D]) (fp32, zero-initialised when not
+    given), with ``lse`` the natural log-sum-exp of the whole forward.
+    Returns (dq, dk, dv)."""
+    torch = _torch()
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if k.shape != (B, Sk, H, D) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == do.dtype):
+        raise TypeError("q, k, v, o, do must share a dtype")
+    if o.shape != q.shape or do.shape != q.shape:
+        raise ValueError("o and do must match q in shape")
+    if lse.shape != (B, Sq, H) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 [B, Sq, H]")
+    dt = _dtype_code(q)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.zeros(q.shape, **f32) if dq is None else dq
+    dk = torch.zeros(k.shape, **f32) if dk is None else dk
+    dv = torch.zeros(k.shape, **f32) if dv is None else dv
+    for t, n, shp in ((dq, "dq", q.shape), (dk, "dk", k.shape), (dv, "dv", k.shape)):
+        if t.shape != shp or t.dtype != torch.float32:
+            raise ValueError(f"{n} must be fp32 of shape {tuple(shp)}")
+    stats = torch.empty((2, B, H, Sq), **f32)
+    st = _load().ra_block_attn_bwd(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(do, "do"), _dev(lse, "lse"),
+        B, Sq, Sk, H, D, dt, float(scale), q_pos0, k_pos0, int(causal), valid_len,
+        _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), _dev(stats, "stats"), _stream(stream))
+    _check(st, "ra_block_attn_bwd")
+    return dq, dk, dv
+
+
 def ring_attn_bwd(q_r, k_blocks: Sequence, v_blocks: Sequence, o_r, do_r, lse_r, rank: int, *,
                   causal: bool = False, valid_len: int = -1, scale: float = 0.0,
                   dq=None, dk_blocks=None, dv_blocks=None, stream=None):
@@ -494,7 +532,7 @@ __all__ = [
     "block_attn_fwd", "ring_merge", "ring_attn_fwd", "seq2head", "head2seq",
     "zigzag_padded_len", "zigzag_schedule", "zigzag_attn_fwd", "ring_attn_bwd",
     "ring_attn_fwd_varlen",
-    "ring_attn_composable", "EXPORTED", "LIB_PATH", "LibraryMissing",
+    "ring_attn_composable", "block_attn_bwd", "EXPORTED", "LIB_PATH", "LibraryMissing",
     "RA_BF16", "RA_FP32", "RA_SKIP", "RA_FULL", "RA_DIAG", "RA_MAX_P", "RA_PAD_MULTIPLE",
     "RA_KERNEL_AUTO", "RA_KERNEL_BR128", "RA_KERNEL_BR256", "RA_KERNEL_W64", "RA_KERNEL_WS",
     "RA_KERNEL_PP",

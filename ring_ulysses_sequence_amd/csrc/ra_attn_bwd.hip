@@ -40,6 +40,7 @@
 // ahead of their use.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdint>
 
@@ -649,7 +650,91 @@ void ring_attn_bwd_dkv(const BwdArgs a) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// Checks shared by both entry points (errors before any launch).
+ra_status check_common(const char* name, int B, int Sq, int H, int D, ra_dtype dt) {
+  if (B < 0 || Sq < 0 || H < 0)
+    return ra::fail(RA_ERR_SHAPE, "%s: negative size (B=%d Sq=%d H=%d)", name, B, Sq, H);
+  if (dt != RA_BF16 && dt != RA_FP32) return ra::fail(RA_ERR_DTYPE, "%s: unknown dtype %d", name, (int)dt);
+  if (dt != RA_BF16) return ra::fail(RA_ERR_UNSUPPORTED, "%s: only bf16 inputs are supported", name);
+  if (D != 64 && D != 128)
+    return ra::fail(RA_ERR_UNSUPPORTED, "%s: head dimension %d not supported (64 or 128)", name, D);
+  return RA_OK;
+}
+
+void set_scale(BwdArgs& a, float scale, int D) {
+  const double sc = scale > 0.0f ? (double)scale : 1.0 / std::sqrt((double)D);
+  a.scale = (float)sc;
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+}
+
+// The three launches over a.nblk visited blocks of block_len rows each.
+ra_status launch_bwd(const char* name, BwdArgs& a, int D, int block_len, hipStream_t s) {
+  const long long n_dq = (long long)a.B * a.H * ((a.Sq + kRows - 1) / kRows);
+  a.n_ktiles = (block_len + kRows - 1) / kRows;
+  const long long n_dkv = (long long)a.nblk * a.B * a.H * a.n_ktiles;
+  if (n_dq > 0x7fffffffLL || n_dkv > 0x7fffffffLL)
+    return ra::fail(RA_ERR_UNSUPPORTED, "%s: grid too large", name);
+  // dq first: it writes the row statistics that the dk/dv kernels read
+  if (D == 128) hipLaunchKernelGGL(ring_attn_bwd_dq<128>, dim3((unsigned)n_dq), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(ring_attn_bwd_dq<64>, dim3((unsigned)n_dq), dim3(kThreads), 0, s, a);
+  if (n_dkv > 0) {
+    const dim3 g((unsigned)n_dkv);
+    if (D == 128) {
+      hipLaunchKernelGGL((ring_attn_bwd_dkv<128, 0>), g, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((ring_attn_bwd_dkv<128, 1>), g, dim3(kThreads), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((ring_attn_bwd_dkv<64, 0>), g, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((ring_attn_bwd_dkv<64, 1>), g, dim3(kThreads), 0, s, a);
+    }
+  }
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess)
+    return ra::fail(RA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
+  return RA_OK;
+}
+
 }  // namespace
+
+extern "C" ra_status ra_block_attn_bwd(const void* q, const void* k, const void* v,
+                                       const void* o, const void* dout, const float* lse,
+                                       int B, int Sq, int Sk, int H, int D, ra_dtype dt,
+                                       float scale, long long q_pos0, long long k_pos0,
+                                       int causal, long long valid_len, float* dq, float* dk,
+                                       float* dv, float* stats_ws, void* stream) {
+  static const char* name = "ra_block_attn_bwd";
+  ra::clear_error();
+  ra_status st = check_common(name, B, Sq, H, D, dt);
+  if (st != RA_OK) return st;
+  if (Sk < 0) return ra::fail(RA_ERR_SHAPE, "%s: negative size (Sk=%d)", name, Sk);
+  if ((long long)B * Sq * H == 0 || Sk == 0) return RA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !stats_ws)
+    return ra::fail(RA_ERR_NULL, "%s: NULL argument", name);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return ra::fail(RA_ERR_SHAPE, "%s: tensors must be 16-byte aligned", name);
+  if (valid_len < 0) valid_len = LLONG_MAX;
+  BwdArgs a{};
+  a.q = q;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.stats = stats_ws;
+  a.q_pos0 = q_pos0;
+  a.valid_len = valid_len;
+  a.B = B;
+  a.Sq = Sq;
+  a.H = H;
+  a.kv_rows_b = Sk;
+  a.causal = causal != 0;
+  set_scale(a, scale, D);
+  // a block with no visible pair ([RA] §3.4 SKIP) is neither read nor written
+  a.nblk = 0;
+  if (ra::block_class(q_pos0, q_pos0 + Sq, k_pos0, k_pos0 + Sk, causal != 0, valid_len) != RA_SKIP)
+    a.blk[a.nblk++] = BwdBlock{k, v, dk, dv, k_pos0, Sk, 0};
+  if (a.nblk == 0) return RA_OK;
+  return launch_bwd(name, a, D, Sk, (hipStream_t)stream);
+}
 
 extern "C" ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_blocks,
                                       const void* const* v_blocks, const void* o_r,
@@ -660,12 +745,8 @@ extern "C" ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_bloc
                                       float* stats_ws, void* stream) {
   static const char* name = "ra_ring_attn_bwd";
   ra::clear_error();
-  if (B < 0 || Sb < 0 || H < 0)
-    return ra::fail(RA_ERR_SHAPE, "%s: negative size (B=%d Sb=%d H=%d)", name, B, Sb, H);
-  if (dt != RA_BF16 && dt != RA_FP32) return ra::fail(RA_ERR_DTYPE, "%s: unknown dtype %d", name, (int)dt);
-  if (dt != RA_BF16) return ra::fail(RA_ERR_UNSUPPORTED, "%s: only bf16 inputs are supported", name);
-  if (D != 64 && D != 128)
-    return ra::fail(RA_ERR_UNSUPPORTED, "%s: head dimension %d not supported (64 or 128)", name, D);
+  ra_status st = check_common(name, B, Sb, H, D, dt);
+  if (st != RA_OK) return st;
   if (P <= 0) return ra::fail(RA_ERR_SHAPE, "%s: P must be positive (got %d)", name, P);
   if (P > RA_MAX_P) return ra::fail(RA_ERR_RANGE, "%s: P=%d exceeds RA_MAX_P=%d", name, P, RA_MAX_P);
   if (rank < 0 || rank >= P) return ra::fail(RA_ERR_RANGE, "%s: rank %d outside [0, %d)", name, rank, P);
@@ -691,13 +772,11 @@ extern "C" ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_bloc
   a.H = H;
   a.kv_rows_b = Sb;
   a.causal = causal != 0;
-  const double sc = scale > 0.0f ? (double)scale : 1.0 / std::sqrt((double)D);
-  a.scale = (float)sc;
-  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  set_scale(a, scale, D);
   // the ring schedule of [RA] §3.3 with the classes of §3.4; SKIP blocks
   // are neither read nor written
   int src[RA_MAX_P], cls[RA_MAX_P];
-  ra_status st = ra_ring_schedule(P, rank, Sb, causal, valid_len, src, cls);
+  st = ra_ring_schedule(P, rank, Sb, causal, valid_len, src, cls);
   if (st != RA_OK) return st;
   a.nblk = 0;
   for (int t = 0; t < P; ++t) {
@@ -711,27 +790,5 @@ extern "C" ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_bloc
     a.blk[a.nblk++] = BwdBlock{k_blocks[j], v_blocks[j], dk_blocks[j], dv_blocks[j],
                                (long long)j * Sb, Sb, 0};
   }
-  hipStream_t s = (hipStream_t)stream;
-  const long long n_dq = (long long)B * H * ((Sb + kRows - 1) / kRows);
-  a.n_ktiles = (Sb + kRows - 1) / kRows;
-  const long long n_dkv = (long long)a.nblk * B * H * a.n_ktiles;
-  if (n_dq > 0x7fffffffLL || n_dkv > 0x7fffffffLL)
-    return ra::fail(RA_ERR_UNSUPPORTED, "%s: grid too large", name);
-  // dq first: it writes the row statistics that the dk/dv kernels read
-  if (D == 128) hipLaunchKernelGGL(ring_attn_bwd_dq<128>, dim3((unsigned)n_dq), dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(ring_attn_bwd_dq<64>, dim3((unsigned)n_dq), dim3(kThreads), 0, s, a);
-  if (n_dkv > 0) {
-    const dim3 g((unsigned)n_dkv);
-    if (D == 128) {
-      hipLaunchKernelGGL((ring_attn_bwd_dkv<128, 0>), g, dim3(kThreads), 0, s, a);
-      hipLaunchKernelGGL((ring_attn_bwd_dkv<128, 1>), g, dim3(kThreads), 0, s, a);
-    } else {
-      hipLaunchKernelGGL((ring_attn_bwd_dkv<64, 0>), g, dim3(kThreads), 0, s, a);
-      hipLaunchKernelGGL((ring_attn_bwd_dkv<64, 1>), g, dim3(kThreads), 0, s, a);
-    }
-  }
-  const hipError_t err = hipGetLastError();
-  if (err != hipSuccess)
-    return ra::fail(RA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
-  return RA_OK;
+  return launch_bwd(name, a, D, Sb, (hipStream_t)stream);
 }

@@ -602,6 +602,52 @@ def test_ring_backward_all_ranks(D, causal, pad):
     check_grad(torch.cat([x.cpu() for x in dv_all], 1)[:, real], fv[:, real], "dv owners vs full")
 
 
+@pytest.mark.parametrize("D,causal", [(128, True), (64, False)])
+def test_block_backward_rounds(D, causal):
+    """ra_block_attn_bwd one round at a time: a query shard of 200 rows
+    (global rows 300..499) against four K/V blocks of uneven, ragged
+    lengths (130, 170, 220, 180 keys; real length 610, the rest padding).
+    Each block's dq, dk and dv terms against the oracle's gradients of that
+    block from the same saved O and lse; the rounds' dq summed against the
+    plain definition.  Causal: the last block lies after every query (SKIP)
+    and must leave the buffers untouched."""
+    B, H, Sq, q0, valid = 2, 3, 200, 300, 610
+    bounds = [0, 130, 300, 520, 700]
+    S = bounds[-1]
+    qf, k, v, dof = (W.random_tensor((B, S, H, D), seed=s_) for s_ in (51, 52, 53, 54))
+    q = qf[:, q0:q0 + Sq].contiguous()
+    do = dof[:, q0:q0 + Sq].contiguous()
+    of, lsef, _, _ = oracle.attention(q, k, v, causal=causal, q_pos0=q0, valid_len=valid)
+    o = torch.from_numpy(of).to(torch.bfloat16)
+    lse = torch.from_numpy(lsef).to(torch.float32)
+    qg, dog, og, lg = (x.cuda() for x in (q, do, o, lse))
+    dq_sum = torch.zeros((B, Sq, H, D), dtype=torch.float32, device="cuda")
+    for a_, b_ in zip(bounds[:-1], bounds[1:]):
+        kb, vb = k[:, a_:b_].contiguous(), v[:, a_:b_].contiguous()
+        say("block bwd", D, causal, "keys", a_, b_)
+        sentinel = 7.0
+        dq = torch.full((B, Sq, H, D), sentinel, dtype=torch.float32, device="cuda")
+        dk = torch.full(kb.shape, sentinel, dtype=torch.float32, device="cuda")
+        dv = torch.full(kb.shape, sentinel, dtype=torch.float32, device="cuda")
+        ra.block_attn_bwd(qg, kb.cuda(), vb.cuda(), og, dog, lg, q_pos0=q0, k_pos0=a_,
+                          causal=causal, valid_len=valid, dq=dq, dk=dk, dv=dv)
+        ra.block_attn_bwd(qg, kb.cuda(), vb.cuda(), og, dog, lg, q_pos0=q0, k_pos0=a_,
+                          causal=causal, valid_len=valid, dq=dq_sum)
+        torch.cuda.synchronize()
+        if causal and a_ > q0 + Sq - 1:
+            for t in (dq, dk, dv):
+                assert bool((t == sentinel).all())
+            continue
+        rq, rk, rv = oracle.attention_grad_sampled(q, kb, vb, do, o, lse, q_rows=np.arange(Sq),
+                                                   k_rows=np.arange(b_ - a_), causal=causal,
+                                                   q_pos0=q0, k_pos0=a_, valid_len=valid)
+        check_grad(dq.cpu() - sentinel, rq, f"dq keys {a_}..{b_}")
+        check_grad(dk.cpu() - sentinel, rk, f"dk keys {a_}..{b_}")
+        check_grad(dv.cpu() - sentinel, rv, f"dv keys {a_}..{b_}")
+    fq, _, _ = oracle.attention_grad(q, k, v, do, causal=causal, q_pos0=q0, valid_len=valid)
+    check_grad(dq_sum.cpu(), fq, "dq summed over the rounds vs the plain definition")
+
+
 def test_ring_backward_long_context_rank3():
     """L = 131072, H = 64, P = 8, rank 3 (the bench share): dq on sampled
     rows and dk / dv on sampled keys of the diagonal and the first block,
