@@ -210,6 +210,35 @@ ra_status ra_ring_attn_fwd_gqa(const void* q_r, const void* const* k_blocks,
                                float scale, int causal, long long valid_len,
                                void* o, float* lse_opt, void* stream);
 
+/* Split form of ra_ring_attn_fwd / _gqa for shares too small to fill the
+ * chip (few heads or few rows: B*H*ceil(Sb/128) workgroups against the
+ * device's slots): the visited blocks, in ring order, are cut into nsplit
+ * consecutive groups and ONE launch computes every (group, query tile)
+ * pair, each group into its own fp32 partial -- the per-round results of
+ * [RA] §3.3 grouped -- which a second launch merges with the log-sum-exp
+ * combine of [SPD] §四 (n-way).  Same result as the single pass up to fp32
+ * rounding.  nsplit >= 1 (RA_ERR_RANGE otherwise); it is clamped to the
+ * number of visited blocks, and 1 (or fp32 inputs) runs the single pass.
+ * Workspace, caller-owned, device fp32: o_part [nsplit,B,Sb,H,D] and
+ * lse_part [nsplit,B,Sb,H] (16-byte aligned; overwritten).  H_kv as in
+ * ra_ring_attn_fwd_gqa (H_kv = H for the plain ring).  Two launches on
+ * `stream`.  Errors as ra_ring_attn_fwd_gqa, RA_ERR_NULL for a missing
+ * workspace when a split happens. */
+ra_status ra_ring_attn_fwd_split(const void* q_r, const void* const* k_blocks,
+                                 const void* const* v_blocks, int B, int Sb, int H,
+                                 int H_kv, int D, int P, int rank, ra_dtype dt,
+                                 float scale, int causal, long long valid_len,
+                                 int nsplit, float* o_part, float* lse_part,
+                                 void* o, float* lse_opt, void* stream);
+
+/* Host-only: the number of slices ra_ring_attn_fwd_split should use for
+ * this share (1 = the single pass already fills the chip): enough for about
+ * two rounds of the device's 512 workgroup slots (two 128-row workgroups per
+ * compute unit on 256 compute units), at most one per visited block.
+ * Returns -1 (message in ra_last_error) for bad sizes or rank. */
+int ra_ring_split_hint(int B, int Sb, int H, int P, int rank, int causal,
+                       long long valid_len);
+
 /* Packed variable-length form of ra_ring_attn_fwd ([RA] §6: a packed
  * sequence carries its sample boundaries and a sample never attends to
  * another).  B = 1; the P*Sb global positions hold n_seqs samples, sample i

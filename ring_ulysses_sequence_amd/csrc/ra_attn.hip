@@ -71,6 +71,9 @@ struct AttnArgs {
   int causal;
   int o_fp32;
   float scale_log2;    // scale * log2(e): scores live in the base-2 domain
+  int nsplit;          // > 1: the visited blocks are split into nsplit groups,
+                       // one per slice of the grid; slice s writes its fp32
+                       // partial (o, lse) at o + s*B*Sq*H*D, lse + s*B*Sq*H
   int nblk;
   KVBlock blk[RA_MAX_P];
 };
@@ -126,9 +129,8 @@ __device__ __forceinline__ int tiles_of(const AttnArgs& a, int b, long long q_hi
 // the heads one after another.
 constexpr int kHeadGroup = 4, kTileRun = 8;
 
-__device__ __forceinline__ void tile_coords(const AttnArgs& a, int& b, int& h, int& qt) {
-  const int n = gridDim.x;
-  int id = blockIdx.x;
+__device__ __forceinline__ void tile_coords(const AttnArgs& a, int id, int n, int& b, int& h,
+                                            int& qt) {
   if ((n & 7) == 0) id = (id & 7) * (n >> 3) + (id >> 3);
   const int Q = a.n_qtiles, BH = a.B * a.H;
   int bh;
@@ -143,6 +145,9 @@ __device__ __forceinline__ void tile_coords(const AttnArgs& a, int& b, int& h, i
   }
   h = bh % a.H;
   b = bh / a.H;
+}
+__device__ __forceinline__ void tile_coords(const AttnArgs& a, int& b, int& h, int& qt) {
+  tile_coords(a, (int)blockIdx.x, (int)gridDim.x, b, h, qt);
 }
 
 // Shared per-row bookkeeping of the online softmax for one lane (one query
@@ -302,17 +307,27 @@ struct Cursor {
   int blk, t, n;
 };
 
-__device__ __forceinline__ Cursor cursor_first(const AttnArgs& a, long long q_hi) {
-  Cursor c{0, 0, 0};
-  while (c.blk < a.nblk && (c.n = tiles_of<64>(a, c.blk, q_hi)) == 0) ++c.blk;
+// The blocks a workgroup visits: [lo, hi) of a.blk (all of them unless the
+// blocks are split over grid slices), up to the workgroup's last query q_hi.
+// A cursor past the range reads blk = a.nblk.
+struct Span {
+  long long q_hi;
+  int lo, hi;
+};
+
+__device__ __forceinline__ Cursor cursor_first(const AttnArgs& a, const Span& sp) {
+  Cursor c{sp.lo, 0, 0};
+  while (c.blk < sp.hi && (c.n = tiles_of<64>(a, c.blk, sp.q_hi)) == 0) ++c.blk;
+  if (c.blk >= sp.hi) c.blk = a.nblk;
   return c;
 }
-__device__ __forceinline__ Cursor cursor_next(const AttnArgs& a, long long q_hi, Cursor c) {
+__device__ __forceinline__ Cursor cursor_next(const AttnArgs& a, const Span& sp, Cursor c) {
   if (c.blk >= a.nblk) return c;
   if (++c.t < c.n) return c;
   c.t = 0;
   ++c.blk;
-  while (c.blk < a.nblk && (c.n = tiles_of<64>(a, c.blk, q_hi)) == 0) ++c.blk;
+  while (c.blk < sp.hi && (c.n = tiles_of<64>(a, c.blk, sp.q_hi)) == 0) ++c.blk;
+  if (c.blk >= sp.hi) c.blk = a.nblk;
   return c;
 }
 
@@ -574,7 +589,7 @@ template <int D, int NW, int PAR>
 __device__ __forceinline__ void pipeline_step(
     const AttnArgs& a, char* smem, WaveState<D, NW>& w, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
     Cursor& t0, Cursor& t1, Cursor& t2, int& vb,
-    long long q_hi, long long wq_lo, long long wq_hi, int wrows, int col, int half, int b,
+    const Span& sp, long long wq_lo, long long wq_hi, int wrows, int col, int half, int b,
     int h, int HD2, int wave) {
   using C = Bf16Cfg<D, NW>;
   // copies of tile n+2: K first, so that waiting for it leaves V in flight
@@ -597,7 +612,7 @@ __device__ __forceinline__ void pipeline_step(
   pipeline_barrier();  // everyone's copies landed, everyone done reading
   t0 = t1;
   t1 = t2;
-  t2 = cursor_next(a, q_hi, t2);
+  t2 = cursor_next(a, sp, t2);
   vb = vb == 2 ? 0 : vb + 1;
 }
 
@@ -613,7 +628,7 @@ __device__ __forceinline__ void pipeline_step(
 template <int D, int PAR>
 __device__ __forceinline__ void pp_step(
     const AttnArgs& a, char* smem, WaveState<D, 8>& w, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
-    Cursor& t0, Cursor& t1, Cursor& t2, int& vb, long long q_hi, long long wq_lo,
+    Cursor& t0, Cursor& t1, Cursor& t2, int& vb, const Span& sp, long long wq_lo,
     long long wq_hi, int wrows, int col, int half, int b, int h, int HD2, int gw, int grp,
     const int* voffk4, const int* voffv4) {
   using C = Bf16Cfg<D, 8>;
@@ -638,7 +653,7 @@ __device__ __forceinline__ void pp_step(
   }
   t0 = t1;
   t1 = t2;
-  t2 = cursor_next(a, q_hi, t2);
+  t2 = cursor_next(a, sp, t2);
   vb = (vb + 1) & 3;
 }
 
@@ -655,11 +670,19 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  int b, h, qt;
-  tile_coords(a, b, h, qt);
+  // grid slice (split of the visited blocks), then (batch, head, query tile)
+  const int ns = a.nsplit > 1 ? a.nsplit : 1;
+  int b, h, qt, split = 0;
+  if (ns > 1) {
+    const int per = (int)gridDim.x / ns;
+    split = (int)blockIdx.x / per;
+    tile_coords(a, (int)blockIdx.x - split * per, per, b, h, qt);
+  } else {
+    tile_coords(a, b, h, qt);
+  }
   const int row0 = qt * C::BR;
   const int rows_here = min(C::BR, a.Sq - row0);
-  const long long q_hi = qpos(a, row0 + rows_here - 1);
+  const Span sp{qpos(a, row0 + rows_here - 1), split * a.nblk / ns, (split + 1) * a.nblk / ns};
   const int wrow0 = row0 + wave * 32;
   const int wrows = min(32, a.Sq - wrow0);
   const long long wq_lo = qpos(a, wrow0);
@@ -715,9 +738,9 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   }
 
   // prologue: K(0), V(0), K(1) into K0, V0, K1; scores of tile 0
-  Cursor t0 = cursor_first(a, q_hi);
-  Cursor t1 = cursor_next(a, q_hi, t0);
-  Cursor t2 = cursor_next(a, q_hi, t1);
+  Cursor t0 = cursor_first(a, sp);
+  Cursor t1 = cursor_next(a, sp, t0);
+  Cursor t2 = cursor_next(a, sp, t1);
   f32x16 sA[2], sB[2];
   if (t0.blk < a.nblk) {
     const KVBlock& kb = a.blk[t0.blk];
@@ -744,18 +767,18 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   int vb = 0;  // V buffer of tile n
   if constexpr (PP) {
     while (t0.blk < a.nblk) {
-      pp_step<D, 0>(a, smem, w, sA, sB, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows, col, half, b,
+      pp_step<D, 0>(a, smem, w, sA, sB, t0, t1, t2, vb, sp, wq_lo, wq_hi, wrows, col, half, b,
                     hk, HD2, gw, grp, voffk4, voffv4);
       if (t0.blk >= a.nblk) break;
-      pp_step<D, 1>(a, smem, w, sB, sA, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows, col, half, b,
+      pp_step<D, 1>(a, smem, w, sB, sA, t0, t1, t2, vb, sp, wq_lo, wq_hi, wrows, col, half, b,
                     hk, HD2, gw, grp, voffk4, voffv4);
     }
   } else {
     while (t0.blk < a.nblk) {
-      pipeline_step<D, NW, 0>(a, smem, w, sA, sB, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows,
+      pipeline_step<D, NW, 0>(a, smem, w, sA, sB, t0, t1, t2, vb, sp, wq_lo, wq_hi, wrows,
                               col, half, b, hk, HD2, wave);
       if (t0.blk >= a.nblk) break;
-      pipeline_step<D, NW, 1>(a, smem, w, sB, sA, t0, t1, t2, vb, q_hi, wq_lo, wq_hi, wrows,
+      pipeline_step<D, NW, 1>(a, smem, w, sB, sA, t0, t1, t2, vb, sp, wq_lo, wq_hi, wrows,
                               col, half, b, hk, HD2, wave);
     }
   }
@@ -765,7 +788,9 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const int r = wrow0 + col;
   if (wrows > 0 && r < a.Sq) {
-    const long long ro = ((long long)b * a.Sq + r) * HD + (long long)h * D;
+    // output row (b, r, h); a split slice writes its own partial plane
+    const long long so = (long long)split * a.B * a.Sq * a.H + ((long long)b * a.Sq + r) * a.H + h;
+    const long long ro = so * D;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
@@ -783,7 +808,6 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
         }
       }
     if (half == 0) {
-      const long long so = ((long long)b * a.Sq + r) * a.H + h;
       const bool seen = l_tot > 0.0f;
       if (a.lse) a.lse[so] = seen ? (w.m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
       if (a.m_out) a.m_out[so] = seen ? w.m_true * kLn2 : -INFINITY;
@@ -2132,10 +2156,12 @@ void launch_bf16(const AttnArgs& a, int D, dim3 grid, hipStream_t stream) {
 }
 
 ra_status launch(AttnArgs& a, int D, ra_dtype dt, hipStream_t stream, const char* name) {
-  const Bf16Kernel kk = dt == RA_BF16 ? bf16_kernel(a) : K_BR128;
+  Bf16Kernel kk = dt == RA_BF16 ? bf16_kernel(a) : K_BR128;
+  // a split ring needs the kernels built on attn_bf16_body
+  if (a.nsplit > 1 && (kk == K_W64 || kk == K_WS)) kk = K_BR128;
   const int br = dt != RA_BF16 ? kBR : kk == K_BR128 ? 128 : 256;
   a.n_qtiles = (a.Sq + br - 1) / br;
-  const long long n_wg = (long long)a.B * a.H * a.n_qtiles;
+  const long long n_wg = (long long)a.B * a.H * a.n_qtiles * (a.nsplit > 1 ? a.nsplit : 1);
   if (n_wg == 0) return RA_OK;
   if (n_wg > 0x7fffffffLL)
     return ra::fail(RA_ERR_UNSUPPORTED, "%s: too many query tiles", name);
@@ -2234,7 +2260,8 @@ namespace {
 ra_status ring_fwd(const char* name, const void* q_r, const void* const* k_blocks,
                    const void* const* v_blocks, int B, int Sb, int H, int Hkv, int D, int P,
                    int rank, ra_dtype dt, float scale, int causal, long long valid_len, void* o,
-                   float* lse_opt, void* stream) {
+                   float* lse_opt, void* stream, int nsplit = 1, float* o_part = nullptr,
+                   float* lse_part = nullptr) {
   ra::clear_error();
   ra_status st = check_common(name, B, Sb, H, D, dt);
   if (st != RA_OK) return st;
@@ -2285,6 +2312,22 @@ ra_status ring_fwd(const char* name, const void* q_r, const void* const* k_block
     if (!aligned16(k_blocks[j]) || !aligned16(v_blocks[j]))
       return ra::fail(RA_ERR_SHAPE, "%s: block %d not 16-byte aligned", name, j);
     a.blk[a.nblk++] = KVBlock{k_blocks[j], v_blocks[j], (long long)j * Sb, Sb, cls[t]};
+  }
+  // split ring: slice s of the grid visits blocks [s*nblk/ns, (s+1)*nblk/ns)
+  // of the ring order into its own fp32 partial; the partials are then
+  // merged as the rounds' results are ([SPD] §四 combine, n-way)
+  const int ns = dt == RA_BF16 ? (nsplit < a.nblk ? nsplit : a.nblk) : 1;
+  if (ns > 1) {
+    if (!o_part || !lse_part) return ra::fail(RA_ERR_NULL, "%s: NULL split workspace", name);
+    if (!aligned16(o_part))
+      return ra::fail(RA_ERR_SHAPE, "%s: o_part must be 16-byte aligned", name);
+    a.nsplit = ns;
+    a.o = o_part;
+    a.lse = lse_part;
+    a.o_fp32 = 1;
+    st = launch(a, D, dt, (hipStream_t)stream, name);
+    if (st != RA_OK) return st;
+    return ra::merge_splits(name, o_part, lse_part, ns, n_out, D, o, dt, lse_opt, stream);
   }
   return launch(a, D, dt, (hipStream_t)stream, name);
 }
@@ -2387,6 +2430,21 @@ extern "C" ra_status ra_ring_attn_fwd_gqa(const void* q_r, const void* const* k_
                                           void* o, float* lse_opt, void* stream) {
   return ring_fwd("ra_ring_attn_fwd_gqa", q_r, k_blocks, v_blocks, B, Sb, H, H_kv, D, P, rank,
                   dt, scale, causal, valid_len, o, lse_opt, stream);
+}
+
+extern "C" ra_status ra_ring_attn_fwd_split(const void* q_r, const void* const* k_blocks,
+                                            const void* const* v_blocks, int B, int Sb, int H,
+                                            int Hkv, int D, int P, int rank, ra_dtype dt,
+                                            float scale, int causal, long long valid_len,
+                                            int nsplit, float* o_part, float* lse_part, void* o,
+                                            float* lse_opt, void* stream) {
+  if (nsplit < 1) {
+    ra::clear_error();
+    return ra::fail(RA_ERR_RANGE, "ra_ring_attn_fwd_split: nsplit must be >= 1 (got %d)",
+                    nsplit);
+  }
+  return ring_fwd("ra_ring_attn_fwd_split", q_r, k_blocks, v_blocks, B, Sb, H, Hkv, D, P, rank,
+                  dt, scale, causal, valid_len, o, lse_opt, stream, nsplit, o_part, lse_part);
 }
 
 extern "C" ra_status ra_zigzag_attn_fwd(const void* q_r, const void* const* k_shares,

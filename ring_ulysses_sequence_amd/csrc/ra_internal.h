@@ -22,6 +22,16 @@ void clear_error();
 int block_class(long long q0, long long q1, long long k0, long long k1,
                 bool causal, long long valid_len);
 
+// Launch the n-way merge of split-ring partials (o_part [nsplit, rows, D]
+// fp32, lse_part [nsplit, rows]) into o (rows x D in dt) and lse_opt.
+ra_status merge_splits(const char* name, const float* o_part, const float* lse_part, int nsplit,
+                       long long rows, int D, void* o, ra_dtype dt, float* lse_opt,
+                       void* stream);
+
+// Slices worth splitting a ring's visited blocks into (1: none), from the
+// grid of 128-row workgroups against the chip's workgroup slots.
+int split_hint(long long base_workgroups, int visited);
+
 // Current value of a process-wide option (see ra_set_option).
 int option(int which);
 

@@ -59,6 +59,52 @@ __global__ __launch_bounds__(kThreads) void lse_merge(
   }
 }
 
+// n-way form for a ring whose visited blocks were split over grid slices:
+// slice s left its normalised partial in o_part[s] [rows, D] and its natural
+// log-sum-exp in lse_part[s] [rows]; with L = log sum_s exp(lse_s),
+//   o = sum_s exp(lse_s - L) o_s,   lse = L
+// (slices that saw no key carry lse_s = -inf and weigh 0; a row no slice saw
+// ends as (0, -inf)).  One row per D/4 consecutive lanes, as above.
+__global__ __launch_bounds__(kThreads) void split_merge(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part, int nsplit,
+    long long rows, int q4, void* o, int out_bf16, float* lse_out) {
+  const long long t = (long long)blockIdx.x * kThreads + threadIdx.x;
+  const long long row = t / q4;
+  if (row >= rows) return;
+  const int c = (int)(t - row * q4);
+  float mx = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, lse_part[s * rows + row]);
+  float4 acc = float4{0.0f, 0.0f, 0.0f, 0.0f};
+  float lse = -INFINITY;
+  if (mx != -INFINITY) {
+    float sum = 0.0f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float w = __builtin_amdgcn_exp2f((lse_part[s * rows + row] - mx) * kLog2e);
+      const float4 x = ((const float4*)o_part)[s * rows * q4 + t];
+      acc.x = fmaf(w, x.x, acc.x);
+      acc.y = fmaf(w, x.y, acc.y);
+      acc.z = fmaf(w, x.z, acc.z);
+      acc.w = fmaf(w, x.w, acc.w);
+      sum += w;
+    }
+    const float inv = 1.0f / sum;
+    acc.x *= inv;
+    acc.y *= inv;
+    acc.z *= inv;
+    acc.w *= inv;
+    lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
+  }
+  if (out_bf16) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 r;
+    r[0] = (__bf16)acc.x; r[1] = (__bf16)acc.y; r[2] = (__bf16)acc.z; r[3] = (__bf16)acc.w;
+    ((bf16x4*)o)[t] = r;
+  } else {
+    ((float4*)o)[t] = acc;
+  }
+  if (lse_out && c == 0) lse_out[row] = lse;
+}
+
 }  // namespace
 
 extern "C" ra_status ra_ring_merge(float* o_acc, float* lse_acc, const float* o_blk,
@@ -90,3 +136,24 @@ extern "C" ra_status ra_ring_merge(float* o_acc, float* lse_acc, const float* o_
     return ra::fail(RA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
   return RA_OK;
 }
+
+namespace ra {
+
+ra_status merge_splits(const char* name, const float* o_part, const float* lse_part, int nsplit,
+                       long long rows, int D, void* o, ra_dtype dt, float* lse_opt,
+                       void* stream) {
+  const int q4 = D / 4;
+  const long long n = rows * q4;
+  const long long blocks = (n + kThreads - 1) / kThreads;
+  if (blocks > 0x7fffffffLL) return ra::fail(RA_ERR_UNSUPPORTED, "%s: too large", name);
+  if (blocks == 0) return RA_OK;
+  hipLaunchKernelGGL(split_merge, dim3((unsigned)blocks), dim3(kThreads), 0,
+                     (hipStream_t)stream, o_part, lse_part, nsplit, rows, q4, o,
+                     dt == RA_BF16 ? 1 : 0, lse_opt);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess)
+    return ra::fail(RA_ERR_HIP, "%s: merge launch failed: %s", name, hipGetErrorString(err));
+  return RA_OK;
+}
+
+}  // namespace ra

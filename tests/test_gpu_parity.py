@@ -228,6 +228,64 @@ def test_block_attn_partials_and_stats(dit, variant):
                                m.cpu().numpy() + np.log(l.cpu().numpy()), atol=1e-5)
 
 
+# ------------------------------------------------------------ split ring
+@pytest.mark.parametrize("causal,D,pad,Hkv", [(False, 128, 0, 4), (True, 128, 0, 4),
+                                              (True, 64, 37, 4), (True, 128, 0, 2)])
+def test_split_ring_all_ranks(causal, D, pad, Hkv):
+    """The split ring (visited blocks cut into slices computed in one launch,
+    fp32 partials merged by log-sum-exp) for every slice count from 1 to one
+    past the number of visited blocks (clamped), on every rank, against the
+    oracle, and with the single pass to within the bf16 budget.  A grid of
+    16 workgroups, so the library's hint asks for one slice per block."""
+    B, S, H, P = 1, 2048, 4, 4
+    Sb, valid = S // P, S - pad
+    q, k, v = (W.random_tensor((B, S, h_, D), seed=s_) for s_, h_ in ((61, H), (62, Hkv), (63, Hkv)))
+    if pad:
+        for x in (q, k, v):
+            x[:, valid:] = 0
+    kb, vb = blocks_of(k.cuda(), P), blocks_of(v.cuda(), P)
+    kk = k.repeat_interleave(H // Hkv, dim=2)
+    vv = v.repeat_interleave(H // Hkv, dim=2)
+    for r in range(P):
+        q_r = q[:, r * Sb:(r + 1) * Sb].contiguous().cuda()
+        src, cls = ra.ring_schedule(P, r, Sb, causal, valid)
+        nvis = sum(c != ra.RA_SKIP for c in cls)
+        assert ra.ring_split_hint(B, Sb, H, P, r, causal, valid) == max(1, nvis)
+        ref_o, ref_lse, _, _ = oracle.attention(q[:, r * Sb:(r + 1) * Sb], kk, vv, causal=causal,
+                                                q_pos0=r * Sb, valid_len=valid)
+        rows = np.arange(max(0, min(Sb, valid - r * Sb)))
+        o1, l1 = ra.ring_attn_fwd(q_r, kb, vb, r, causal=causal, valid_len=valid, split=1)
+        for ns in range(1, nvis + 2):
+            say("split ring", causal, D, pad, Hkv, "rank", r, "slices", ns)
+            o, lse = ra.ring_attn_fwd(q_r, kb, vb, r, causal=causal, valid_len=valid, split=ns)
+            torch.cuda.synchronize()
+            check_bf16(o.cpu()[:, rows], ref_o[:, rows], f"split {ns} r{r} O")
+            assert oracle.max_abs_err(lse.cpu()[:, rows], ref_lse[:, rows]) <= LSE_BF16_ATOL
+            # against the single pass: each slice rounds its weights to bf16
+            # against its own reference max, so the two agree to the bf16
+            # budget, not bit for bit
+            assert float((o.float() - o1.float()).abs().max()) <= 4e-3
+            assert float((lse - l1).abs().max()) <= LSE_BF16_ATOL
+
+
+def test_split_ring_errors():
+    """nsplit < 1 is refused; a split without workspace is refused."""
+    import ctypes
+    q = torch.zeros((1, 128, 1, 64), dtype=torch.bfloat16, device="cuda")
+    kb = [q, q]
+    with pytest.raises(ValueError):
+        ra.ring_attn_fwd(q, kb, kb, 0, split=0)
+    arr = (ctypes.c_void_p * 2)(q.data_ptr(), q.data_ptr())
+    o = torch.empty_like(q)
+    lib = ra.lib()
+    st = lib.ra_ring_attn_fwd_split(q.data_ptr(), arr, arr, 1, 128, 1, 1, 64, 2, 0, ra.RA_BF16,
+                                    0.0, 0, -1, 0, None, None, o.data_ptr(), None, None)
+    assert st == ra.RA_ERR_RANGE
+    st = lib.ra_ring_attn_fwd_split(q.data_ptr(), arr, arr, 1, 128, 1, 1, 64, 2, 0, ra.RA_BF16,
+                                    0.0, 0, -1, 2, None, None, o.data_ptr(), None, None)
+    assert st == ra.RA_ERR_NULL and b"workspace" in lib.ra_last_error()
+
+
 # ------------------------------------------------------------ C3 Ulysses
 def test_ulysses_layout_and_attention(variant):
     w = W.ULYSSES

@@ -123,6 +123,22 @@ def test_zigzag_padded_len(lib):
         ra.zigzag_padded_len(10, 0)
 
 
+def test_split_hint(lib):
+    """One slice per visited block while the grid of 128-row workgroups is
+    under the chip's 512 slots, none once it fills them; -1 on bad sizes."""
+    # DiT shard: 24 heads x 8 row tiles = 192 workgroups, 4 blocks visited
+    assert ra.ring_split_hint(1, 1024, 24, 4, 0) == 4
+    # causal rank 1 visits 2 blocks; rank 0 only its own
+    assert ra.ring_split_hint(1, 1024, 24, 4, 1, causal=True) == 2
+    assert ra.ring_split_hint(1, 1024, 24, 4, 0, causal=True) == 1
+    # the long-context share fills the chip
+    assert ra.ring_split_hint(1, 16384, 64, 8, 3, causal=True) == 1
+    # 300 workgroups: ceil(1024 / 300) = 4 slices at most
+    assert ra.ring_split_hint(1, 128 * 75, 4, 8, 0) == 4
+    with pytest.raises(ValueError):
+        ra.ring_split_hint(1, 16, 1, 0, 0)
+
+
 def test_classify_block_matches_brute_force(lib):
     rng = np.random.default_rng(11)
     for _ in range(3000):
