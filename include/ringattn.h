@@ -232,10 +232,12 @@ ra_status ra_ring_attn_fwd_split(const void* q_r, const void* const* k_blocks,
                                  void* o, float* lse_opt, void* stream);
 
 /* Host-only: the number of slices ra_ring_attn_fwd_split should use for
- * this share (1 = the single pass already fills the chip): enough for about
- * two rounds of the device's 512 workgroup slots (two 128-row workgroups per
- * compute unit on 256 compute units), at most one per visited block.
- * Returns -1 (message in ra_last_error) for bad sizes or rank. */
+ * this share (1 = the single pass; always 1 once B*H*ceil(Sb/128) fills the
+ * device's 512 workgroup slots, two 128-row workgroups per compute unit on
+ * 256 compute units).  Among the slice counts that divide the visited blocks
+ * evenly it takes the one with the fewest (rounds of the slots x blocks per
+ * slice), counting 0.15 block per slice for the merge.  Returns -1 (message
+ * in ra_last_error) for bad sizes or rank. */
 int ra_ring_split_hint(int B, int Sb, int H, int P, int rank, int causal,
                        long long valid_len);
 

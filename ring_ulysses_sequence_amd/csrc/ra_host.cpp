@@ -52,9 +52,21 @@ constexpr long long kWorkgroupSlots = 512;
 
 int split_hint(long long base_workgroups, int visited) {
   if (visited <= 1 || base_workgroups <= 0 || base_workgroups >= kWorkgroupSlots) return 1;
-  // enough slices for about two rounds of slots, at most one per block
-  const long long n = (2 * kWorkgroupSlots + base_workgroups - 1) / base_workgroups;
-  return (int)(n < visited ? n : visited);
+  // slice counts that divide the visited blocks evenly, scored by rounds of
+  // the slots times blocks per slice, plus 0.15 block per slice for the
+  // merge's extra pass over a partial (units of 1/20 block)
+  int best = 1;
+  long long best_cost = -1;
+  for (int ns = 1; ns <= visited; ++ns) {
+    if (visited % ns) continue;
+    const long long rounds = (base_workgroups * ns + kWorkgroupSlots - 1) / kWorkgroupSlots;
+    const long long cost = 20 * rounds * (visited / ns) + 3 * ns;
+    if (best_cost < 0 || cost < best_cost) {
+      best = ns;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 }  // namespace ra

@@ -64,7 +64,9 @@ __global__ __launch_bounds__(kThreads) void lse_merge(
 // log-sum-exp in lse_part[s] [rows]; with L = log sum_s exp(lse_s),
 //   o = sum_s exp(lse_s - L) o_s,   lse = L
 // (slices that saw no key carry lse_s = -inf and weigh 0; a row no slice saw
-// ends as (0, -inf)).  One row per D/4 consecutive lanes, as above.
+// ends as (0, -inf)).  One row per D/4 consecutive lanes, as above.  NS is
+// the slice count (all loads issued before any use), 0 for a run-time count.
+template <int NS>
 __global__ __launch_bounds__(kThreads) void split_merge(
     const float* __restrict__ o_part, const float* __restrict__ lse_part, int nsplit,
     long long rows, int q4, void* o, int out_bf16, float* lse_out) {
@@ -72,15 +74,28 @@ __global__ __launch_bounds__(kThreads) void split_merge(
   const long long row = t / q4;
   if (row >= rows) return;
   const int c = (int)(t - row * q4);
+  const int ns = NS > 0 ? NS : nsplit;
+  constexpr int CAP = NS > 0 ? NS : 1;
+  float ls[CAP];
+  float4 xs[CAP];
+  if constexpr (NS > 0) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      ls[s] = lse_part[s * rows + row];
+      xs[s] = ((const float4*)o_part)[s * rows * q4 + t];
+    }
+  }
   float mx = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, lse_part[s * rows + row]);
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, NS > 0 ? ls[s] : lse_part[s * rows + row]);
   float4 acc = float4{0.0f, 0.0f, 0.0f, 0.0f};
   float lse = -INFINITY;
   if (mx != -INFINITY) {
     float sum = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float w = __builtin_amdgcn_exp2f((lse_part[s * rows + row] - mx) * kLog2e);
-      const float4 x = ((const float4*)o_part)[s * rows * q4 + t];
+#pragma unroll
+    for (int s = 0; s < ns; ++s) {
+      const float l = NS > 0 ? ls[s] : lse_part[s * rows + row];
+      const float4 x = NS > 0 ? xs[s] : ((const float4*)o_part)[s * rows * q4 + t];
+      const float w = __builtin_amdgcn_exp2f((l - mx) * kLog2e);
       acc.x = fmaf(w, x.x, acc.x);
       acc.y = fmaf(w, x.y, acc.y);
       acc.z = fmaf(w, x.z, acc.z);
@@ -147,9 +162,17 @@ ra_status merge_splits(const char* name, const float* o_part, const float* lse_p
   const long long blocks = (n + kThreads - 1) / kThreads;
   if (blocks > 0x7fffffffLL) return ra::fail(RA_ERR_UNSUPPORTED, "%s: too large", name);
   if (blocks == 0) return RA_OK;
-  hipLaunchKernelGGL(split_merge, dim3((unsigned)blocks), dim3(kThreads), 0,
-                     (hipStream_t)stream, o_part, lse_part, nsplit, rows, q4, o,
-                     dt == RA_BF16 ? 1 : 0, lse_opt);
+  const dim3 g((unsigned)blocks), t(kThreads);
+  hipStream_t s = (hipStream_t)stream;
+  const int bf = dt == RA_BF16 ? 1 : 0;
+  switch (nsplit) {
+    case 2: hipLaunchKernelGGL(split_merge<2>, g, t, 0, s, o_part, lse_part, 2, rows, q4, o, bf, lse_opt); break;
+    case 3: hipLaunchKernelGGL(split_merge<3>, g, t, 0, s, o_part, lse_part, 3, rows, q4, o, bf, lse_opt); break;
+    case 4: hipLaunchKernelGGL(split_merge<4>, g, t, 0, s, o_part, lse_part, 4, rows, q4, o, bf, lse_opt); break;
+    default:
+      hipLaunchKernelGGL(split_merge<0>, g, t, 0, s, o_part, lse_part, nsplit, rows, q4, o, bf,
+                         lse_opt);
+  }
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess)
     return ra::fail(RA_ERR_HIP, "%s: merge launch failed: %s", name, hipGetErrorString(err));

@@ -229,15 +229,17 @@ def test_block_attn_partials_and_stats(dit, variant):
 
 
 # ------------------------------------------------------------ split ring
-@pytest.mark.parametrize("causal,D,pad,Hkv", [(False, 128, 0, 4), (True, 128, 0, 4),
-                                              (True, 64, 37, 4), (True, 128, 0, 2)])
-def test_split_ring_all_ranks(causal, D, pad, Hkv):
+@pytest.mark.parametrize("causal,D,pad,Hkv,P", [(False, 128, 0, 4, 4), (True, 128, 0, 4, 4),
+                                                (True, 64, 37, 4, 4), (True, 128, 0, 2, 4),
+                                                (False, 64, 0, 4, 8)])
+def test_split_ring_all_ranks(causal, D, pad, Hkv, P):
     """The split ring (visited blocks cut into slices computed in one launch,
     fp32 partials merged by log-sum-exp) for every slice count from 1 to one
     past the number of visited blocks (clamped), on every rank, against the
-    oracle, and with the single pass to within the bf16 budget.  A grid of
-    16 workgroups, so the library's hint asks for one slice per block."""
-    B, S, H, P = 1, 2048, 4, 4
+    oracle, and with the single pass to within the bf16 budget.  Grids of
+    16 or 8 workgroups, so the library's hint asks for one slice per block
+    (up to 8 slices on 8 ranks)."""
+    B, S, H = 1, 2048, 4
     Sb, valid = S // P, S - pad
     q, k, v = (W.random_tensor((B, S, h_, D), seed=s_) for s_, h_ in ((61, H), (62, Hkv), (63, Hkv)))
     if pad:

@@ -124,17 +124,27 @@ def test_zigzag_padded_len(lib):
 
 
 def test_split_hint(lib):
-    """One slice per visited block while the grid of 128-row workgroups is
-    under the chip's 512 slots, none once it fills them; -1 on bad sizes."""
-    # DiT shard: 24 heads x 8 row tiles = 192 workgroups, 4 blocks visited
-    assert ra.ring_split_hint(1, 1024, 24, 4, 0) == 4
+    """Slices only while the grid of 128-row workgroups is under the chip's
+    512 slots, a divisor of the visited blocks that minimises rounds x
+    blocks per slice (+0.15 block per slice for the merge); -1 on bad
+    sizes."""
+    def model(base, vis):
+        if vis <= 1 or base >= 512:
+            return 1
+        cost = {ns: 20 * -(-base * ns // 512) * (vis // ns) + 3 * ns
+                for ns in range(1, vis + 1) if vis % ns == 0}
+        return min(cost, key=lambda ns: (cost[ns], ns))
+    # DiT shard: 24 heads x 8 row tiles = 192 workgroups, 4 blocks visited:
+    # two slices (one round of 384) beat four (two rounds of 768)
+    assert ra.ring_split_hint(1, 1024, 24, 4, 0) == 2 == model(192, 4)
     # causal rank 1 visits 2 blocks; rank 0 only its own
     assert ra.ring_split_hint(1, 1024, 24, 4, 1, causal=True) == 2
     assert ra.ring_split_hint(1, 1024, 24, 4, 0, causal=True) == 1
     # the long-context share fills the chip
     assert ra.ring_split_hint(1, 16384, 64, 8, 3, causal=True) == 1
-    # 300 workgroups: ceil(1024 / 300) = 4 slices at most
-    assert ra.ring_split_hint(1, 128 * 75, 4, 8, 0) == 4
+    for B, Sb, H, P in [(1, 128 * 75, 4, 8), (2, 512, 4, 4), (1, 2048, 2, 6), (1, 640, 9, 3)]:
+        base = B * H * -(-Sb // 128)
+        assert ra.ring_split_hint(B, Sb, H, P, 0) == model(base, P), (B, Sb, H, P)
     with pytest.raises(ValueError):
         ra.ring_split_hint(1, 16, 1, 0, 0)
 
