@@ -47,7 +47,8 @@ __device__ __forceinline__ long long h2s_src_run(long long dst_run, int P, int B
   return (r * B + b) * S + j * Sl + s;
 }
 
-// Vector path: runs are a whole number of 16-byte units.
+// Vector path for any run of a whole number of 16-byte units (64-bit
+// index arithmetic per unit).
 template <bool kSeq2Head>
 __global__ __launch_bounds__(kThreads) void permute_vec16(
     const u32x4* __restrict__ src, u32x4* __restrict__ dst, long long n_units,
@@ -71,6 +72,56 @@ __global__ __launch_bounds__(kThreads) void permute_vec16(
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u)
     if (idx[u] < n_units) __builtin_nontemporal_store(buf[u], &dst[idx[u]]);
+}
+
+// 32-bit forms of the run maps, for tensors of fewer than 2^31 units.
+__device__ __forceinline__ unsigned s2h_src_run32(unsigned dst_run, unsigned P, unsigned B,
+                                                  unsigned S, unsigned Sl) {
+  const unsigned t = dst_run % S, rb = dst_run / S;
+  const unsigned b = rb % B, r = rb / B;
+  const unsigned j = t / Sl, s = t % Sl;
+  return ((j * B + b) * Sl + s) * P + r;
+}
+__device__ __forceinline__ unsigned h2s_src_run32(unsigned dst_run, unsigned P, unsigned B,
+                                                  unsigned S, unsigned Sl) {
+  const unsigned r = dst_run % P, row = dst_run / P;
+  const unsigned s = row % Sl, jb = row / Sl;
+  const unsigned b = jb % B, j = jb / B;
+  return (r * B + b) * S + j * Sl + s;
+}
+
+// Vector path by 1 KiB pieces: each wave moves kPieces pieces of 64
+// consecutive destination units (one unit per lane), all loads before the
+// stores.  Runs are a multiple of 64 units (a piece lies in one run) or
+// divide 64 (a piece covers 64 / units_per_run whole runs), so the index
+// arithmetic is a handful of 32-bit divisions per piece, not per unit.
+// Loads are ordinary (a source just written by its producer is often still
+// in the last-level cache); stores are non-temporal (the destination is not
+// read again by this kernel).
+constexpr int kPieces = 4;
+template <bool kSeq2Head>
+__global__ __launch_bounds__(kThreads) void permute_pieces(
+    const u32x4* __restrict__ src, u32x4* __restrict__ dst, unsigned n_units,
+    unsigned units_per_run, unsigned P, unsigned B, unsigned S, unsigned Sl) {
+  const unsigned lane = threadIdx.x & 63;
+  const unsigned piece0 = (blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * kPieces;
+  u32x4 buf[kPieces];
+  unsigned di[kPieces];
+#pragma unroll
+  for (int u = 0; u < kPieces; ++u) {
+    const unsigned du = (piece0 + u) * 64 + lane;
+    di[u] = du;
+    if (du < n_units) {
+      const unsigned run = du / units_per_run;
+      const unsigned c = du - run * units_per_run;
+      const unsigned sr = kSeq2Head ? s2h_src_run32(run, P, B, S, Sl)
+                                    : h2s_src_run32(run, P, B, S, Sl);
+      buf[u] = src[(size_t)sr * units_per_run + c];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kPieces; ++u)
+    if (di[u] < n_units) __builtin_nontemporal_store(buf[u], &dst[di[u]]);
 }
 
 // Element path: any run length, element of T (1, 2, 4 or 8 bytes).
@@ -134,7 +185,16 @@ ra_status permute(const char* name, const void* src, void* dst, int P, int B,
   hipError_t err;
   const bool vec = run_bytes % 16 == 0 && ((uintptr_t)src % 16) == 0 &&
                    ((uintptr_t)dst % 16) == 0;
-  if (vec) {
+  const long long upr16 = run_bytes / 16;
+  if (vec && (upr16 % 64 == 0 || 64 % upr16 == 0) && n_runs * upr16 < (1LL << 31)) {
+    const long long n_units = n_runs * upr16;
+    const long long per_block = (long long)kThreads * kPieces;
+    const long long blocks = (n_units + per_block - 1) / per_block;
+    hipLaunchKernelGGL((permute_pieces<kSeq2Head>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, (const u32x4*)src, (u32x4*)dst, (unsigned)n_units,
+                       (unsigned)upr16, (unsigned)P, (unsigned)B, (unsigned)S, (unsigned)Sl);
+    err = hipGetLastError();
+  } else if (vec) {
     const int units_per_run = (int)(run_bytes / 16);
     const long long n_units = n_runs * units_per_run;
     const long long per_block = (long long)kThreads * kUnroll;

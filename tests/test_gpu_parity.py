@@ -864,7 +864,10 @@ def test_edge_cases_bf16(variant):
 
 # ------------------------------------------------------------ permutations
 @pytest.mark.parametrize("P,B,S,H,D,dtype", [
-    (8, 1, 16384, 32, 128, torch.int16),      # the Ulysses workload's shape
+    (8, 1, 16384, 32, 128, torch.int16),      # the Ulysses workload's shape (1 KiB runs)
+    (2, 1, 64, 16, 128, torch.int16),         # 2 KiB runs: two pieces per run
+    (4, 2, 256, 4, 128, torch.int16),         # 256-byte runs: four runs per piece
+    (2, 1, 8, 2, 24, torch.int16),            # 48-byte runs: 16-byte path per unit
     (4, 2, 64, 8, 3, torch.int16),            # run of 6 bytes: element path
     (2, 3, 10, 4, 5, torch.int8),
     (4, 1, 32, 4, 16, torch.int32),
