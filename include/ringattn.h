@@ -292,7 +292,7 @@ ra_status ra_zigzag_attn_fwd(const void* q_r, const void* const* k_shares,
  *   dv [B,Sk,H,D] fp32 += P^T dO
  * A block with no visible pair (SKIP) returns at once without touching
  * anything.  stats_ws: fp32 scratch of 2*B*Sq*H floats the call
- * overwrites.  Three launches on `stream`.  Only bf16 inputs
+ * overwrites.  Two launches on `stream`.  Only bf16 inputs
  * (RA_ERR_UNSUPPORTED for fp32); D 64 or 128; tensors 16-byte aligned
  * (RA_ERR_SHAPE); NULL pointers with non-empty sizes RA_ERR_NULL. */
 ra_status ra_block_attn_bwd(const void* q, const void* k, const void* v,
@@ -320,7 +320,7 @@ ra_status ra_block_attn_bwd(const void* q, const void* k, const void* v,
  * arrays of P device pointers; entries of blocks the rank skips (causal
  * future) may be NULL and are not touched.  stats_ws: fp32 scratch of
  * 2*B*Sb*H floats the call overwrites (per-row base-2 lse and D, [2,B,H,Sb]).
- * Three launches on `stream` (dq, then dv, then dk).
+ * Two launches on `stream` (dq and the row statistics, then dk/dv).
  * Only bf16 inputs (RA_ERR_UNSUPPORTED for fp32).  Errors as
  * ra_ring_attn_fwd. */
 ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_blocks,

@@ -18,17 +18,19 @@
 // kernels: A[m][k] lane holds m = col, k = 8*half ..; B[k][n] lane holds
 // n = col, k = 8*half ..; C[m][n] lane holds n = col, m = 8*(v/4) + 4*half +
 // v%4):
-//   ring_attn_bwd_dq<D>:  one workgroup per 128 query rows (4 waves x 32).
+//   ring_attn_bwd_dq<D>: one workgroup per 128 query rows (4 waves x 32).
 //     Each lane holds one query column: S^T = K Q^T and dP^T = V dO^T from
 //     K/V rows in LDS, then dQ^T += K^T dS^T with K^T read transposed
 //     (ds_read_b64_tr_b16) and dS^T from registers -- the forward's P V step
 //     with V replaced by K.  It also writes the per-row statistics the second
 //     kernel reads: the base-2 lse and D_r.
-//   ring_attn_bwd_dkv<D, PART>: one workgroup per 128 keys of one visited
-//     block (4 waves x 32 keys).  Each lane holds one key column: S = Q K^T
-//     (and, for dK, dP = dO V^T) from Q/dO rows in LDS, then dV^T += dO^T P
-//     (PART 0) or dK^T += Q^T dS (PART 1) with dO^T / Q^T read transposed.
-//     Two launches rather than one so that each fits two waves per SIMD.
+//   ring_attn_bwd_dkv_pair<D>: one workgroup per 128 keys of one visited
+//     block, 8 waves: each lane holds one key column, and the two waves of a
+//     SIMD split the work on their 32 keys -- one computes S = Q K^T, P and
+//     dV^T += dO^T P, the other dP = dO V^T, dS = P (dP - D) with its
+//     partner's P (handed over in LDS) and dK^T += Q^T dS, with dO^T / Q^T
+//     read transposed.  (One wave doing both would not fit in 256 registers;
+//     two separate launches would compute S and P twice.)
 // Tiles of 64 rows are copied HBM -> LDS by the buffer unit (buffer_load ...
 // lds), double-buffered: the copy of tile n+1 is issued when tile n starts
 // and has the whole of tile n's compute to land; one wait and one barrier
@@ -124,17 +126,19 @@ __device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
 }
 
 // Copy one 64-row tile (rows at or beyond `rows` read as zeros) whose row 0
-// starts at `src`, rows HD2 bytes apart, into LDS: this wave's Cfg::DMA KiB
-// land at byte address dst, dst + 1024, ..; voff[i] is the source offset of
-// this lane's chunk (row * HD2 + swizzled chunk * 16).
-template <int D>
+// starts at `src`, rows HD2 bytes apart, into LDS, shared by NWV waves: this
+// wave's TILE / 1024 / NWV KiB land at byte address dst, dst + 1024, ..;
+// voff[i] is the source offset of this lane's chunk (row * HD2 + swizzled
+// chunk * 16).
+template <int D, int NWV = kWaves>
 __device__ __forceinline__ void copy_tile(const char* src, int rows, int HD2, const int* voff,
                                           unsigned dst) {
   using C = Cfg<D>;
+  constexpr int DMA = C::TILE / 1024 / NWV;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)src, 0, (rows - 1) * HD2 + C::ROWB, kRsrcWord3);
 #pragma unroll
-  for (int i = 0; i < C::DMA; ++i)
+  for (int i = 0; i < DMA; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(size_t)(dst + i * 1024), 16,
                                              voff[i], 0, 0, 0);
 }
@@ -183,13 +187,15 @@ __device__ __forceinline__ s16x4 read_tr_g(int g, unsigned addr) {
   return g ? lds_read_tr16<OFF + G1>(addr) : lds_read_tr16<OFF>(addr);
 }
 
-// Source offsets of this lane's copy chunks within a tile.
-template <int D>
+// Source offsets of this lane's copy chunks within a tile copied by NWV
+// waves.
+template <int D, int NWV = kWaves>
 __device__ __forceinline__ void copy_offsets(int wave, int lane, int HD2, int* voff) {
   using C = Cfg<D>;
+  constexpr int DMA = C::TILE / 1024 / NWV;
 #pragma unroll
-  for (int i = 0; i < C::DMA; ++i) {
-    const int p = (wave * C::DMA + i) * 64 + lane;  // physical chunk in the tile
+  for (int i = 0; i < DMA; ++i) {
+    const int p = (wave * DMA + i) * 64 + lane;  // physical chunk in the tile
     const int r = p / C::CHUNKS, pc = p % C::CHUNKS;
     voff[i] = r * HD2 + swz<D>(r, pc) * 16;
   }
@@ -418,124 +424,133 @@ void ring_attn_bwd_dq(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per (visited block, batch, head, 128 keys)
+// dK and dV together: one workgroup of 8 waves per (visited block, batch,
+// head, 128 keys).  Waves g and g + 4 run on one SIMD and share the 32 keys
+// of group g:
+//   role 0 (wave g):     S = Q K^T, P = exp(S - lse) (masked), P to LDS,
+//                        dV^T += dO^T P
+//   role 1 (wave g + 4): dP = dO V^T; after the barrier, dS = P (dP - D)
+//                        with its partner's P, dK^T += Q^T dS
+// so the scores and exponentials are computed once per key, not once per
+// gradient.  Both roles share the Q / dO tiles in LDS; each half tile (32
+// query rows) has one barrier for the P hand-over, each tile one more for
+// its copies.
 // ---------------------------------------------------------------------------
-// PART 0 accumulates dV (needs S only), PART 1 dK (needs S and dP): split so
-// that each fits two waves per SIMD; the scores are recomputed in both.
-template <int D, int PART>
-struct DkvLane {
-  using C = Cfg<D>;
-  bf16x8 kf[C::NC], vf[PART == 1 ? C::NC : 1];  // this lane's key row of K, V
-  f32x16 acc[C::NDT];                           // dK^T (PART 1) or dV^T (PART 0)
-  LaneAddr<D> ad;
-  unsigned sa;  // LDS address of this lane's statistics (rows 4*half ..)
+constexpr int kPairThreads = 512;
+constexpr int kXSlot = 32 * 32 * 2;  // P of one key group for one half tile
+
+template <int D>
+struct PairCfg {
+  static constexpr int BUF = 2 * Cfg<D>::TILE + 2 * kTile * 4;  // Q, dO, lse2, D
+  static constexpr int XB = 2 * BUF;                            // P exchange
+  static constexpr int LDS = XB + 2 * 4 * kXSlot;               // two half parities
+  static constexpr int DMA = Cfg<D>::TILE / 1024 / 8;
 };
 
-// Query rows 32T .. 32T+31 of the tiles in the current buffer (Q at 0, dO at
-// TILE, base-2 lse at 2*TILE, D at 2*TILE + 256).
-template <int D, int PART, int T>
-__device__ __forceinline__ void dkv_half(DkvLane<D, PART>& w, float c_scale, bool need,
-                                         int rel_h) {
+template <int D, int ROLE>
+struct PairLane {
   using C = Cfg<D>;
-  constexpr bool DK = PART == 1;
-  constexpr int RO = T * 32 * C::ROWB;
+  bf16x8 f[C::NC];     // K (role 0) or V (role 1) row of this lane's key
+  f32x16 acc[C::NDT];  // dV^T (role 0) or dK^T (role 1)
+  LaneAddr<D> ad;
+  unsigned sa;         // this lane's statistics in the current buffer
+  unsigned xa;         // this lane's slot in the P exchange (parity 0)
+};
+
+template <int D, int ROLE, int T>
+__device__ __forceinline__ void pair_half(PairLane<D, ROLE>& w, bool live, bool need, int rel_h,
+                                          float c_scale) {
+  using C = Cfg<D>;
   constexpr int NB = kPF + 1;
-  constexpr int NR = DK ? 2 : 1;  // row reads per k-step
-  f32x16 sc = f32x16{}, dpt = f32x16{};
-  {
-    u32x4 qa[NB], da[DK ? NB : 1];
+  constexpr int RO = T * 32 * C::ROWB;
+  constexpr int AO = (ROLE == 0 ? 0 : C::TILE) + RO;                    // Q or dO rows
+  constexpr int TO = (ROLE == 0 ? C::TILE : 0) + RO;                    // dO^T or Q^T
+  constexpr int SO = 2 * C::TILE + (ROLE == 0 ? 0 : 4 * kTile) + 128 * T;  // lse2 or D
+  constexpr int XO = T * 4 * kXSlot;
+  constexpr int NJ = 2 * C::NDT;
+  f32x16 sc = f32x16{};
+  u32x4 st[4];
+  s16x4 lo[NB], hi[NB];
+  bf16x8 pb[2];
+  if (live) {
+    u32x4 ra[NB];
 #pragma unroll
-    for (int c = 0; c < kPF; ++c) {
-      qa[c] = lds_read_b128<RO>(w.ad.row[c]);
-      if constexpr (DK) da[c] = lds_read_b128<C::TILE + RO>(w.ad.row[c]);
-    }
+    for (int c = 0; c < kPF; ++c) ra[c] = lds_read_b128<AO>(w.ad.row[c]);
 #pragma unroll
     for (int c = 0; c < C::NC; ++c) {
-      if (c + kPF < C::NC) {
-        qa[(c + kPF) % NB] = lds_read_b128<RO>(w.ad.row[c + kPF]);
-        if constexpr (DK) da[(c + kPF) % NB] = lds_read_b128<C::TILE + RO>(w.ad.row[c + kPF]);
+      if (c + kPF < C::NC) ra[(c + kPF) % NB] = lds_read_b128<AO>(w.ad.row[c + kPF]);
+      claim_lds_n(min(kPF, C::NC - 1 - c), ra[c % NB]);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(ra[c % NB]), w.f[c], sc, 0, 0, 0);
+    }
+    st[0] = lds_read_b128<SO + 0>(w.sa);
+    st[1] = lds_read_b128<SO + 32>(w.sa);
+    st[2] = lds_read_b128<SO + 64>(w.sa);
+    st[3] = lds_read_b128<SO + 96>(w.sa);
+#pragma unroll
+    for (int j = 0; j < kPF; ++j) {
+      lo[j] = read_tr_g<D, TO>(j / C::NDT, w.ad.lo[j % C::NDT]);
+      hi[j] = read_tr_g<D, TO>(j / C::NDT, w.ad.hi[j % C::NDT]);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) claim_lds<2 * kPF>(st[g]);
+    if constexpr (ROLE == 0) {
+      // P of (query m = 32T + 8g + 4half + i, this lane's key), hidden when
+      // m < rel_h + 4half; handed to the partner in the lane's own slot
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l4 = as_f32(st[g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int v = 4 * g + i;
+          float x = sc[v] * c_scale - l4[i];
+          if (need && 32 * T + 8 * g + i < rel_h) x = -INFINITY;
+          pb[v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(x);
+        }
       }
-      const int n = NR * min(kPF, C::NC - 1 - c);
-      claim_lds_n(n, qa[c % NB]);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(qa[c % NB]), w.kf[c], sc, 0, 0, 0);
-      if constexpr (DK) {
-        claim_lds_n(n, da[c % NB]);
-        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(da[c % NB]), w.vf[c], dpt, 0, 0, 0);
+      lds_write_b128<XO>(w.xa, __builtin_bit_cast(u32x4, pb[0]));
+      lds_write_b128<XO + 1024>(w.xa, __builtin_bit_cast(u32x4, pb[1]));
+    }
+  }
+  pipeline_barrier();  // P of this half is in LDS for role 1
+  if (live) {
+    if constexpr (ROLE == 1) {
+      u32x4 x0 = lds_read_b128<XO>(w.xa), x1 = lds_read_b128<XO + 1024>(w.xa);
+      claim_lds<0>(x0);
+      claim_lds<0>(x1);
+      const bf16x8 p0 = as_bf16(x0), p1 = as_bf16(x1);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 d4 = as_f32(st[g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int v = 4 * g + i;
+          const float p = (float)(v < 8 ? p0[v] : p1[v - 8]);
+          pb[v >> 3][v & 7] = (__bf16)(p * (sc[v] - d4[i]));
+        }
       }
     }
-  }
-  // statistics of the 16 query rows of this lane, then the first reads of
-  // the gradient product, all in flight during the wait for the scores
-  u32x4 ls[4], ds[DK ? 4 : 1];
-  constexpr int SO = 2 * C::TILE + 128 * T;
-  ls[0] = lds_read_b128<SO + 0>(w.sa);
-  ls[1] = lds_read_b128<SO + 32>(w.sa);
-  ls[2] = lds_read_b128<SO + 64>(w.sa);
-  ls[3] = lds_read_b128<SO + 96>(w.sa);
-  if constexpr (DK) {
-    ds[0] = lds_read_b128<SO + 256>(w.sa);
-    ds[1] = lds_read_b128<SO + 256 + 32>(w.sa);
-    ds[2] = lds_read_b128<SO + 256 + 64>(w.sa);
-    ds[3] = lds_read_b128<SO + 256 + 96>(w.sa);
-  }
-  constexpr int NJ = 2 * C::NDT;
-  constexpr int TO = (DK ? 0 : C::TILE) + 32 * T * C::ROWB;  // Q^T (dK) or dO^T (dV)
-  s16x4 lo[NB], hi[NB];
 #pragma unroll
-  for (int j = 0; j < kPF; ++j) {
-    lo[j] = read_tr_g<D, TO>(j / C::NDT, w.ad.lo[j % C::NDT]);
-    hi[j] = read_tr_g<D, TO>(j / C::NDT, w.ad.hi[j % C::NDT]);
-  }
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    claim_lds<2 * kPF>(ls[g]);
-    if constexpr (DK) claim_lds<2 * kPF>(ds[g]);
-  }
-  // element (query m = 32T + 8g + 4half + i, this lane's key) is hidden when
-  // m < rel_h + 4half
-  bf16x8 pb[2];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const f32x4 l4 = as_f32(ls[g]);
-    const f32x4 d4 = as_f32(ds[DK ? g : 0]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v = 4 * g + i;
-      float x = sc[v] * c_scale - l4[i];
-      if (need && 32 * T + 8 * g + i < rel_h) x = -INFINITY;
-      const float p = __builtin_amdgcn_exp2f(x);
-      if constexpr (DK) pb[v >> 3][v & 7] = (__bf16)(p * (dpt[v] - d4[i]));
-      else pb[v >> 3][v & 7] = (__bf16)p;
+    for (int j = 0; j < NJ; ++j) {
+      if (j + kPF < NJ) {
+        const int jn = j + kPF;
+        lo[jn % NB] = read_tr_g<D, TO>(jn / C::NDT, w.ad.lo[jn % C::NDT]);
+        hi[jn % NB] = read_tr_g<D, TO>(jn / C::NDT, w.ad.hi[jn % C::NDT]);
+      }
+      const int n = 2 * min(kPF, NJ - 1 - j);
+      claim_lds_n(n, lo[j % NB]);
+      claim_lds_n(n, hi[j % NB]);
+      const int d = j % C::NDT;
+      w.acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(lo[j % NB], hi[j % NB]),
+                                                         pb[j / C::NDT], w.acc[d], 0, 0, 0);
     }
-  }
-  // dK^T += Q^T dS (PART 1) or dV^T += dO^T P (PART 0)
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    if (j + kPF < NJ) {
-      const int jn = j + kPF;
-      lo[jn % NB] = read_tr_g<D, TO>(jn / C::NDT, w.ad.lo[jn % C::NDT]);
-      hi[jn % NB] = read_tr_g<D, TO>(jn / C::NDT, w.ad.hi[jn % C::NDT]);
-    }
-    const int n = 2 * min(kPF, NJ - 1 - j);
-    claim_lds_n(n, lo[j % NB]);
-    claim_lds_n(n, hi[j % NB]);
-    const int d = j % C::NDT;
-    w.acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(lo[j % NB], hi[j % NB]),
-                                                       pb[j / C::NDT], w.acc[d], 0, 0, 0);
   }
 }
 
-template <int D, int PART>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void ring_attn_bwd_dkv(const BwdArgs a) {
+template <int D, int ROLE>
+__device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave, int lane) {
   using C = Cfg<D>;
-  constexpr bool DK = PART == 1;
-  // two buffers, each: Q tile, dO tile, base-2 lse (64 floats), D (64 floats)
-  constexpr int BUF = 2 * C::TILE + 2 * kTile * 4;
-  __shared__ __attribute__((aligned(1024))) char smem[2][BUF];
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  using PC = PairCfg<D>;
+  const int g = wave & 3, half = lane >> 5, col = lane & 31;
   int id = blockIdx.x;
   const int kt = id % a.n_ktiles;
   id /= a.n_ktiles;
@@ -547,54 +562,48 @@ void ring_attn_bwd_dkv(const BwdArgs a) {
   const long long HD = (long long)a.H * D;
   const int HD2 = (int)(HD * 2);
 
-  // this lane's key row of the block: K and V fragments (B operands)
-  const int kr = kt * kRows + wave * 32 + col;
+  const int kr = kt * kRows + g * 32 + col;
   const bool key_ok = kr < kb.len;
   const long long kpos = kb.k_pos0 + kr;
-  const long long kw_lo = kb.k_pos0 + kt * kRows + wave * 32;
+  const long long kw_lo = kb.k_pos0 + kt * kRows + g * 32;
   const long long kw_hi = kw_lo + 31;
-  DkvLane<D, PART> w;
+  PairLane<D, ROLE> w;
   {
     const long long off = ((long long)b * a.kv_rows_b + kr) * HD + (long long)h * D;
-    const __bf16* kp = (const __bf16*)kb.k + off;
-    const __bf16* vp = (const __bf16*)kb.v + off;
+    const __bf16* fp = (const __bf16*)(ROLE == 0 ? kb.k : kb.v) + off;
 #pragma unroll
-    for (int c = 0; c < C::NC; ++c) {
-      const int d = 16 * c + 8 * half;
-      w.kf[c] = key_ok ? *(const bf16x8*)(kp + d) : bf16x8{};
-      if constexpr (DK) w.vf[c] = key_ok ? *(const bf16x8*)(vp + d) : bf16x8{};
-    }
+    for (int c = 0; c < C::NC; ++c)
+      w.f[c] = key_ok ? *(const bf16x8*)(fp + 16 * c + 8 * half) : bf16x8{};
   }
 #pragma unroll
   for (int i = 0; i < C::NDT; ++i) w.acc[i] = f32x16{};
   const unsigned base = lds_addr(smem);
   w.ad.init(base, lane);
   w.sa = base + 16 * half;
-  int voff[C::DMA];
-  copy_offsets<D>(wave, lane, HD2, voff);
+  w.xa = base + PC::XB + g * kXSlot + lane * 16;
+  int voff[PC::DMA];
+  copy_offsets<D, 8>(wave, lane, HD2, voff);
 
-  // query tiles that can see a key of this workgroup (causal: from the one
-  // holding position k_lo on)
   const long long k_lo = kb.k_pos0 + (long long)kt * kRows;
   int t0 = 0;
   if (a.causal && k_lo > a.q_pos0) t0 = (int)min((long long)a.Sq, (k_lo - a.q_pos0) / kTile);
   const int n_t = (a.Sq + kTile - 1) / kTile;
-
-  // Q and dO tiles by all waves; the statistics (64 floats each) by wave 0
-  // (lse) and wave 1 (D)
   const long long stat0 = ((long long)b * a.H + h) * a.Sq;
+  // Q and dO tiles by all eight waves; the statistics rows by waves 0 (lse)
+  // and 1 (D)
   auto copy_q = [&](int ti, unsigned buf_base) {
     const long long off = (((long long)b * a.Sq + (long long)ti * kTile) * a.H + h) * D * 2;
     const int rows = min(kTile, a.Sq - ti * kTile);
-    copy_tile<D>((const char*)a.q + off, rows, HD2, voff, buf_base + wave * C::DMA * 1024);
-    copy_tile<D>((const char*)a.dout + off, rows, HD2, voff,
-                 buf_base + C::TILE + wave * C::DMA * 1024);
-    if (wave < (DK ? 2 : 1)) {
+    const unsigned dst = buf_base + wave * PC::DMA * 1024;
+    copy_tile<D, 8>((const char*)a.q + off, rows, HD2, voff, dst);
+    copy_tile<D, 8>((const char*)a.dout + off, rows, HD2, voff, dst + C::TILE);
+    if (wave < 2) {
       const float* src = a.stats + (wave ? (long long)a.B * a.H * a.Sq : 0) + stat0 + ti * kTile;
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, rows * 4, kRsrcWord3);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void_ptr)(size_t)(buf_base + 2 * C::TILE + wave * 256), 4, lane * 4, 0, 0, 0);
+          rs, (lds_void_ptr)(size_t)(buf_base + 2 * C::TILE + wave * 4 * kTile), 4, lane * 4, 0,
+          0, 0);
     }
   };
   if (t0 < n_t) copy_q(t0, base);
@@ -603,27 +612,20 @@ void ring_attn_bwd_dkv(const BwdArgs a) {
   int buf = 0;
   const float c_scale = a.scale_log2;
   for (int ti = t0; ti < n_t; ++ti) {
-    // the next tile's copy goes to the other buffer, last read in the
-    // previous iteration (before its closing barrier)
-    if (ti + 1 < n_t) copy_q(ti + 1, base + (buf ^ 1) * BUF);
+    if (ti + 1 < n_t) copy_q(ti + 1, base + (buf ^ 1) * PC::BUF);
     const long long qp0 = a.q_pos0 + (long long)ti * kTile;
     const long long qp_hi = qp0 + min(kTile, a.Sq - ti * kTile) - 1;
     const bool live = !(a.causal && kw_lo > qp_hi) && kw_lo < a.valid_len;
-    // element (query m of the tile, this lane's key) is hidden when the key
-    // is padding or (causal) after the query, i.e. m < rel with rel = key -
-    // first query of the tile (32-bit, clamped)
     const bool need = kw_hi >= a.valid_len || (a.causal && kw_hi > qp0);
     int rel = 0;
     if (kpos >= a.valid_len) rel = kTile;
     else if (a.causal) rel = (int)max(0LL, min((long long)kTile, kpos - qp0));
     const int rel_h = rel - 4 * half;
-    if (live) {
-      dkv_half<D, PART, 0>(w, c_scale, need, rel_h);
-      dkv_half<D, PART, 1>(w, c_scale, need, rel_h);
-    }
+    pair_half<D, ROLE, 0>(w, live, need, rel_h, c_scale);
+    pair_half<D, ROLE, 1>(w, live, need, rel_h, c_scale);
     wait_vmcnt<0>();
     pipeline_barrier();
-    const int delta = buf ? -BUF : BUF;
+    const int delta = buf ? -PC::BUF : PC::BUF;
     w.ad.shift(delta);
     w.sa += delta;
     buf ^= 1;
@@ -631,21 +633,30 @@ void ring_attn_bwd_dkv(const BwdArgs a) {
 
   if (key_ok) {
     const long long off = ((long long)b * a.kv_rows_b + kr) * HD + (long long)h * D;
-    float* dst = (DK ? kb.dk : kb.dv) + off;
-    const float f = DK ? a.scale : 1.0f;
+    float* dst = (ROLE == 1 ? kb.dk : kb.dv) + off;
+    const float f = ROLE == 1 ? a.scale : 1.0f;
 #pragma unroll
     for (int d = 0; d < C::NDT; ++d)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float4* p = (float4*)(dst + 32 * d + 8 * g + 4 * half);
+      for (int gg = 0; gg < 4; ++gg) {
+        float4* p = (float4*)(dst + 32 * d + 8 * gg + 4 * half);
         float4 x = *p;
-        x.x += f * w.acc[d][4 * g + 0];
-        x.y += f * w.acc[d][4 * g + 1];
-        x.z += f * w.acc[d][4 * g + 2];
-        x.w += f * w.acc[d][4 * g + 3];
+        x.x += f * w.acc[d][4 * gg + 0];
+        x.y += f * w.acc[d][4 * gg + 1];
+        x.z += f * w.acc[d][4 * gg + 2];
+        x.w += f * w.acc[d][4 * gg + 3];
         *p = x;
       }
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void ring_attn_bwd_dkv_pair(const BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[PairCfg<D>::LDS];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave < 4) pair_body<D, 0>(a, smem, wave, lane);
+  else pair_body<D, 1>(a, smem, wave, lane);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -679,13 +690,8 @@ ra_status launch_bwd(const char* name, BwdArgs& a, int D, int block_len, hipStre
   else hipLaunchKernelGGL(ring_attn_bwd_dq<64>, dim3((unsigned)n_dq), dim3(kThreads), 0, s, a);
   if (n_dkv > 0) {
     const dim3 g((unsigned)n_dkv);
-    if (D == 128) {
-      hipLaunchKernelGGL((ring_attn_bwd_dkv<128, 0>), g, dim3(kThreads), 0, s, a);
-      hipLaunchKernelGGL((ring_attn_bwd_dkv<128, 1>), g, dim3(kThreads), 0, s, a);
-    } else {
-      hipLaunchKernelGGL((ring_attn_bwd_dkv<64, 0>), g, dim3(kThreads), 0, s, a);
-      hipLaunchKernelGGL((ring_attn_bwd_dkv<64, 1>), g, dim3(kThreads), 0, s, a);
-    }
+    if (D == 128) hipLaunchKernelGGL(ring_attn_bwd_dkv_pair<128>, g, dim3(kPairThreads), 0, s, a);
+    else hipLaunchKernelGGL(ring_attn_bwd_dkv_pair<64>, g, dim3(kPairThreads), 0, s, a);
   }
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess)

@@ -52,6 +52,14 @@ __device__ __forceinline__ s16x4 lds_read_tr16(unsigned addr) {
   return r;
 }
 
+// ds_write_b128 of v at LDS byte address addr + OFF (complete once lgkmcnt
+// has counted it out, e.g. at pipeline_barrier).
+template <int OFF>
+__device__ __forceinline__ void lds_write_b128(unsigned addr, u32x4 v) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+  asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "n"(OFF));
+}
+
 // Wait until at most N LDS (or scalar-memory) operations of this wave are
 // outstanding, and make `x` depend on the wait so that no use of it is
 // scheduled before.  LDS operations complete in issue order, so with N = the
