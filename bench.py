@@ -217,6 +217,8 @@ def main():
             "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "avg_launch_ms": round(avg_launch_ms, 4),
+            "median_launch_ms": round(sorted(launch_ms)[len(launch_ms) // 2], 4),
+            "min_launch_ms": round(min(launch_ms), 4),
             "traffic": traffic,
             "traffic_unit": "bytes per launch (HBM/fabric, rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                             "copy-kernel calibrated)",
