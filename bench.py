@@ -233,8 +233,8 @@ def main():
 
 
 def side_measurements(torch, ra, W, stream):
-    """Side numbers, not the step: the DiT-shard ring (rank 0; split over the
-    slices the library's hint gives, as the binding does by default) and the
+    """Side numbers, not the step: the DiT-shard ring (rank 0; split as the
+    library plans, which the binding does by default) and the
     Ulysses seq->head / head->seq layout of one tensor."""
     out = {}
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -259,7 +259,8 @@ def side_measurements(torch, ra, W, stream):
     fl = 4.0 * w.D * Sb * w.S * w.H * w.B
     out["dit_shard_rank0"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
                               "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
-                              "slices": ra.ring_split_hint(w.B, Sb, w.H, w.P, 0)}
+                              "split_runs_per_query_tile":
+                                  ra.ring_split_plan(w.B, Sb, w.H, w.D, w.P, 0)[0]}
     del q, k, v, kb, vb, q0, o
     # Ulysses layout: one [8, 1, 2048, 32, 128] bf16 tensor each way
     w = W.ULYSSES

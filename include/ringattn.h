@@ -210,36 +210,41 @@ ra_status ra_ring_attn_fwd_gqa(const void* q_r, const void* const* k_blocks,
                                float scale, int causal, long long valid_len,
                                void* o, float* lse_opt, void* stream);
 
-/* Split form of ra_ring_attn_fwd / _gqa for shares too small to fill the
- * chip (few heads or few rows: B*H*ceil(Sb/128) workgroups against the
- * device's slots): the visited blocks, in ring order, are cut into nsplit
- * consecutive groups and ONE launch computes every (group, query tile)
- * pair, each group into its own fp32 partial -- the per-round results of
- * [RA] §3.3 grouped -- which a second launch merges with the log-sum-exp
- * combine of [SPD] §四 (n-way).  Same result as the single pass up to fp32
- * rounding.  nsplit >= 1 (RA_ERR_RANGE otherwise); it is clamped to the
- * number of visited blocks, and 1 (or fp32 inputs) runs the single pass.
- * Workspace, caller-owned, device fp32: o_part [nsplit,B,Sb,H,D] and
- * lse_part [nsplit,B,Sb,H] (16-byte aligned; overwritten).  H_kv as in
- * ra_ring_attn_fwd_gqa (H_kv = H for the plain ring).  Two launches on
- * `stream`.  Errors as ra_ring_attn_fwd_gqa, RA_ERR_NULL for a missing
- * workspace when a split happens. */
+/* Split form of ra_ring_attn_fwd / _gqa, for shares too small to fill the
+ * chip (B*H*ceil(Sb/128) workgroups of 128 query rows against the device's
+ * slots).  The visited-tile sequence of every 128-row query tile (the
+ * 64-key tiles of the visited blocks in ring order, [RA] §3.3, up to the
+ * last one with a key the tile can see) is cut into nsplit near-equal runs
+ * computed by separate workgroups of ONE launch, each leaving a normalised
+ * fp32 partial (o, lse) -- the per-round results of [RA] §3.3 grouped --
+ * which a second launch merges per row with the log-sum-exp combine of
+ * [SPD] §四 (n-way).  Same result as the single pass up to the bf16 rounding
+ * of the weights (each run rounds against its own reference max).
+ * nsplit >= 1 (RA_ERR_RANGE otherwise); 1, and fp32 inputs, run the single
+ * pass with the workspace untouched.  Workspace: caller-owned device fp32
+ * of at least ws_floats = B*H*ceil(Sb/128)*nsplit*128*(D+1) floats (what
+ * ra_ring_split_plan reports), 16-byte aligned, overwritten (RA_ERR_NULL /
+ * RA_ERR_SHAPE otherwise).  H_kv as in ra_ring_attn_fwd_gqa (H_kv = H for
+ * the plain ring).  Two launches on `stream`.  Other errors as
+ * ra_ring_attn_fwd_gqa. */
 ra_status ra_ring_attn_fwd_split(const void* q_r, const void* const* k_blocks,
                                  const void* const* v_blocks, int B, int Sb, int H,
                                  int H_kv, int D, int P, int rank, ra_dtype dt,
                                  float scale, int causal, long long valid_len,
-                                 int nsplit, float* o_part, float* lse_part,
+                                 int nsplit, float* ws, long long ws_floats,
                                  void* o, float* lse_opt, void* stream);
 
-/* Host-only: the number of slices ra_ring_attn_fwd_split should use for
- * this share (1 = the single pass; always 1 once B*H*ceil(Sb/128) fills the
- * device's 512 workgroup slots, two 128-row workgroups per compute unit on
- * 256 compute units).  Among the slice counts that divide the visited blocks
- * evenly it takes the one with the fewest (rounds of the slots x blocks per
- * slice), counting 0.15 block per slice for the merge.  Returns -1 (message
- * in ra_last_error) for bad sizes or rank. */
-int ra_ring_split_hint(int B, int Sb, int H, int P, int rank, int causal,
-                       long long valid_len);
+/* Host-only plan of the split ring for this share.  nsplit = 0 chooses:
+ * as many runs per query tile as keep the B*H*ceil(Sb/128)*nsplit
+ * workgroups within the device's 512 workgroup slots (two 128-row
+ * workgroups per compute unit on 256 compute units), each at least 8 tiles
+ * of the longest sequence, and 1 (no split) once the single pass fills the
+ * slots; nsplit >= 1 plans that count.  Returns the run count (1: the
+ * single pass; -1 on bad sizes or rank, message in ra_last_error) and, in
+ * *ws_floats (may be NULL), the workspace ra_ring_attn_fwd_split needs for
+ * it (0 for the single pass). */
+int ra_ring_split_plan(int B, int Sb, int H, int D, int P, int rank, int causal,
+                       long long valid_len, int nsplit, long long* ws_floats);
 
 /* Packed variable-length form of ra_ring_attn_fwd ([RA] §6: a packed
  * sequence carries its sample boundaries and a sample never attends to

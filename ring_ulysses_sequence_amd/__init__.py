@@ -43,7 +43,7 @@ EXPORTED = (
     "ra_ring_merge", "ra_ring_attn_fwd", "ra_seq2head", "ra_head2seq",
     "ra_zigzag_padded_len", "ra_zigzag_schedule", "ra_zigzag_attn_fwd", "ra_ring_attn_bwd",
     "ra_ring_attn_fwd_gqa", "ra_ring_attn_fwd_varlen", "ra_block_attn_bwd",
-    "ra_ring_attn_fwd_split", "ra_ring_split_hint",
+    "ra_ring_attn_fwd_split", "ra_ring_split_plan",
 )
 
 _lib = None
@@ -101,9 +101,10 @@ def _load():
                                      ctypes.POINTER(c_vp), c_vp, c_vp]),
         "ra_ring_attn_fwd_split": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp),
                                            c_int, c_int, c_int, c_int, c_int, c_int, c_int,
-                                           c_int, c_float, c_int, c_ll, c_int, c_vp, c_vp, c_vp,
+                                           c_int, c_float, c_int, c_ll, c_int, c_vp, c_ll, c_vp,
                                            c_vp, c_vp]),
-        "ra_ring_split_hint": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_ll]),
+        "ra_ring_split_plan": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_ll,
+                                       c_int, ctypes.POINTER(c_ll)]),
         "ra_block_attn_bwd": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int,
                                       c_int, c_int, c_int, c_float, c_ll, c_ll, c_int, c_ll,
                                       c_vp, c_vp, c_vp, c_vp, c_vp]),
@@ -273,13 +274,16 @@ def ring_merge(o_acc, lse_acc, o_blk, lse_blk, *, out_final=None, stream=None):
     return o_acc, lse_acc
 
 
-def ring_split_hint(B: int, Sb: int, H: int, P: int, rank: int, causal: bool = False,
-                    valid_len: int = -1) -> int:
-    """Slices the split ring should use for this share (1: no split)."""
-    n = _load().ra_ring_split_hint(B, Sb, H, P, rank, int(causal), valid_len)
+def ring_split_plan(B: int, Sb: int, H: int, D: int, P: int, rank: int, causal: bool = False,
+                    valid_len: int = -1, nsplit: int = 0):
+    """(runs per query tile, workspace floats) of the split ring for this
+    share; 1 run means the single pass (see ra_ring_split_plan)."""
+    ws = ctypes.c_longlong(0)
+    n = _load().ra_ring_split_plan(B, Sb, H, D, P, rank, int(causal), valid_len,
+                                   int(nsplit), ctypes.byref(ws))
     if n < 0:
         raise ValueError(_load().ra_last_error().decode())
-    return n
+    return n, ws.value
 
 
 def ring_attn_fwd(q_r, k_blocks: Sequence, v_blocks: Sequence, rank: int, *,
@@ -287,8 +291,9 @@ def ring_attn_fwd(q_r, k_blocks: Sequence, v_blocks: Sequence, rank: int, *,
                   want_lse: bool = True, out=None, lse_out=None, stream=None, split=None):
     """Rank ``rank``'s whole ring: (o [B,Sb,H,D] in q's dtype, lse).
     K/V blocks with fewer heads than q_r (a divisor of H) select the grouped-query
-    form: query head h reads K/V head h / (H / H_kv).  ``split``: slices of the
-    split ring (None: ra_ring_split_hint's choice for bf16, 1: one pass)."""
+    form: query head h reads K/V head h / (H / H_kv).  ``split``: runs per
+    query tile of the split ring (None: ra_ring_split_plan's choice for bf16,
+    1: the single pass)."""
     torch = _torch()
     B, Sb, H, D = q_r.shape
     P = len(k_blocks)
@@ -316,19 +321,17 @@ def ring_attn_fwd(q_r, k_blocks: Sequence, v_blocks: Sequence, rank: int, *,
             _dev(lse, "lse") if lse is not None else None, _stream(stream))
     if split is not None and split < 1:
         raise ValueError(f"split must be >= 1 (got {split})")
-    if split is None:
+    runs, ws_floats = 1, 0
+    if dt == RA_BF16 and split != 1:
         # the kernels forced by RA_KERNEL_W64 / RA_KERNEL_WS run unsplit
-        split = 1
-        if dt == RA_BF16 and get_attn_kernel() not in (RA_KERNEL_W64, RA_KERNEL_WS):
-            split = ring_split_hint(B, Sb, H, P, rank, causal, valid_len)
-    if split > 1:
-        f32 = dict(dtype=torch.float32, device=q_r.device)
-        o_part = torch.empty((split, B, Sb, H, D), **f32)
-        lse_part = torch.empty((split, B, Sb, H), **f32)
+        if split is not None or get_attn_kernel() not in (RA_KERNEL_W64, RA_KERNEL_WS):
+            runs, ws_floats = ring_split_plan(B, Sb, H, D, P, rank, causal, valid_len,
+                                              split or 0)
+    if runs > 1:
+        ws = torch.empty(ws_floats, dtype=torch.float32, device=q_r.device)
         st = _load().ra_ring_attn_fwd_split(_dev(q_r, "q_r"), kp, vp, B, Sb, H, Hkv, D, P, rank,
-                                            dt, float(scale), int(causal), valid_len, int(split),
-                                            _dev(o_part, "o_part"), _dev(lse_part, "lse_part"),
-                                            *args[3:])
+                                            dt, float(scale), int(causal), valid_len, runs,
+                                            _dev(ws, "ws"), ws_floats, *args[3:])
         _check(st, "ra_ring_attn_fwd_split")
     elif Hkv == H:
         st = _load().ra_ring_attn_fwd(_dev(q_r, "q_r"), kp, vp, B, Sb, H, D, P, rank, dt, *args)
@@ -564,7 +567,7 @@ __all__ = [
     "block_attn_fwd", "ring_merge", "ring_attn_fwd", "seq2head", "head2seq",
     "zigzag_padded_len", "zigzag_schedule", "zigzag_attn_fwd", "ring_attn_bwd",
     "ring_attn_fwd_varlen",
-    "ring_attn_composable", "block_attn_bwd", "ring_split_hint", "EXPORTED", "LIB_PATH", "LibraryMissing",
+    "ring_attn_composable", "block_attn_bwd", "ring_split_plan", "EXPORTED", "LIB_PATH", "LibraryMissing",
     "RA_BF16", "RA_FP32", "RA_SKIP", "RA_FULL", "RA_DIAG", "RA_MAX_P", "RA_PAD_MULTIPLE",
     "RA_KERNEL_AUTO", "RA_KERNEL_BR128", "RA_KERNEL_BR256", "RA_KERNEL_W64", "RA_KERNEL_WS",
     "RA_KERNEL_PP",

@@ -26,6 +26,7 @@
 // the stream continues across round boundaries without a drain.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -71,9 +72,12 @@ struct AttnArgs {
   int causal;
   int o_fp32;
   float scale_log2;    // scale * log2(e): scores live in the base-2 domain
-  int nsplit;          // > 1: the visited blocks are split into nsplit groups,
-                       // one per slice of the grid; slice s writes its fp32
-                       // partial (o, lse) at o + s*B*Sq*H*D, lse + s*B*Sq*H
+  // split ring (nsplit > 1): the visited-tile sequence of every 128-row
+  // query tile is cut into nsplit near-equal runs, one workgroup each; run
+  // j of query tile qt of (b, h) writes its fp32 partial (o normalised, lse)
+  // to slot ((b*H + h)*n_qtiles + qt)*nsplit + j of o / lse ([slot][128
+  // rows][D] and [slot][128 rows]).
+  int nsplit;
   int nblk;
   KVBlock blk[RA_MAX_P];
 };
@@ -107,7 +111,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 // wholly in the future of the workgroup's last query, or wholly padding,
 // are never read).
 template <int BC>
-__device__ __forceinline__ int tiles_of(const AttnArgs& a, int b, long long q_hi) {
+__host__ __device__ __forceinline__ int tiles_of(const AttnArgs& a, int b, long long q_hi) {
   const KVBlock& kb = a.blk[b];
   const int n = (kb.len + BC - 1) / BC;
   long long lim = a.valid_len - 1;
@@ -307,28 +311,42 @@ struct Cursor {
   int blk, t, n;
 };
 
-// The blocks a workgroup visits: [lo, hi) of a.blk (all of them unless the
-// blocks are split over grid slices), up to the workgroup's last query q_hi.
-// A cursor past the range reads blk = a.nblk.
+// A workgroup's visited-tile sequence: the tiles of every visited block in
+// ring order, each block up to the last tile with a key visible to the
+// workgroup's last query q_hi.  The span ends before tile (end_blk, end_t):
+// (a.nblk, 0) for the whole sequence.  A cursor past the span reads
+// blk = a.nblk.
 struct Span {
   long long q_hi;
-  int lo, hi;
+  int end_blk, end_t;
 };
 
-__device__ __forceinline__ Cursor cursor_first(const AttnArgs& a, const Span& sp) {
-  Cursor c{sp.lo, 0, 0};
-  while (c.blk < sp.hi && (c.n = tiles_of<64>(a, c.blk, sp.q_hi)) == 0) ++c.blk;
-  if (c.blk >= sp.hi) c.blk = a.nblk;
+// Position of tile number i of the sequence (blk = a.nblk past its end).
+__device__ __forceinline__ Cursor seq_pos(const AttnArgs& a, long long q_hi, int i) {
+  Cursor c{0, 0, 0};
+  for (; c.blk < a.nblk; ++c.blk) {
+    c.n = tiles_of<64>(a, c.blk, q_hi);
+    if (i < c.n) break;
+    i -= c.n;
+  }
+  c.t = i;
   return c;
+}
+__device__ __forceinline__ Cursor span_end(const AttnArgs& a, const Span& sp, Cursor c) {
+  if (c.blk > sp.end_blk || (c.blk == sp.end_blk && c.t >= sp.end_t)) c.blk = a.nblk;
+  return c;
+}
+__device__ __forceinline__ Cursor cursor_first(const AttnArgs& a, const Span& sp, int lo) {
+  return span_end(a, sp, seq_pos(a, sp.q_hi, lo));
 }
 __device__ __forceinline__ Cursor cursor_next(const AttnArgs& a, const Span& sp, Cursor c) {
   if (c.blk >= a.nblk) return c;
-  if (++c.t < c.n) return c;
-  c.t = 0;
-  ++c.blk;
-  while (c.blk < sp.hi && (c.n = tiles_of<64>(a, c.blk, sp.q_hi)) == 0) ++c.blk;
-  if (c.blk >= sp.hi) c.blk = a.nblk;
-  return c;
+  if (++c.t >= c.n) {
+    c.t = 0;
+    ++c.blk;
+    while (c.blk < a.nblk && (c.n = tiles_of<64>(a, c.blk, sp.q_hi)) == 0) ++c.blk;
+  }
+  return span_end(a, sp, c);
 }
 
 // Everything a wave keeps in registers across tiles.
@@ -657,10 +675,13 @@ __device__ __forceinline__ void pp_step(
   vb = (vb + 1) & 3;
 }
 
-// Kernel body shared by the 32-row-per-wave kernels; PP selects the
-// staggered form (NW = 8 only).
+// One (batch, head, query tile) over tiles [lo, hi) of its visited-tile
+// sequence, shared by the 32-row-per-wave kernels; PP selects the staggered
+// form (NW = 8 only).  slot < 0: the output rows of the tile; otherwise the
+// split partial slot (see AttnArgs).
 template <int D, int NW, bool PP>
-__device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
+__device__ __forceinline__ void attn_bf16_tile(const AttnArgs& a, char* smem, int b, int h,
+                                               int qt, int lo, int hi, long long slot) {
   using C = Bf16Cfg<D, NW>;
   static_assert(!PP || NW == 8, "the staggered form pairs waves w and w+4 on one SIMD");
 
@@ -670,19 +691,14 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  // grid slice (split of the visited blocks), then (batch, head, query tile)
-  const int ns = a.nsplit > 1 ? a.nsplit : 1;
-  int b, h, qt, split = 0;
-  if (ns > 1) {
-    const int per = (int)gridDim.x / ns;
-    split = (int)blockIdx.x / per;
-    tile_coords(a, (int)blockIdx.x - split * per, per, b, h, qt);
-  } else {
-    tile_coords(a, b, h, qt);
-  }
   const int row0 = qt * C::BR;
   const int rows_here = min(C::BR, a.Sq - row0);
-  const Span sp{qpos(a, row0 + rows_here - 1), split * a.nblk / ns, (split + 1) * a.nblk / ns};
+  Span sp{qpos(a, row0 + rows_here - 1), a.nblk, 0};
+  if (hi != INT_MAX) {
+    const Cursor e = seq_pos(a, sp.q_hi, hi);
+    sp.end_blk = e.blk;
+    sp.end_t = e.t;
+  }
   const int wrow0 = row0 + wave * 32;
   const int wrows = min(32, a.Sq - wrow0);
   const long long wq_lo = qpos(a, wrow0);
@@ -738,7 +754,7 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   }
 
   // prologue: K(0), V(0), K(1) into K0, V0, K1; scores of tile 0
-  Cursor t0 = cursor_first(a, sp);
+  Cursor t0 = cursor_first(a, sp, lo);
   Cursor t1 = cursor_next(a, sp, t0);
   Cursor t2 = cursor_next(a, sp, t1);
   f32x16 sA[2], sB[2];
@@ -788,8 +804,9 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const int r = wrow0 + col;
   if (wrows > 0 && r < a.Sq) {
-    // output row (b, r, h); a split slice writes its own partial plane
-    const long long so = (long long)split * a.B * a.Sq * a.H + ((long long)b * a.Sq + r) * a.H + h;
+    // output row (b, r, h), or row r - row0 of the split partial slot
+    const long long so = slot < 0 ? ((long long)b * a.Sq + r) * a.H + h
+                                  : slot * C::BR + (r - row0);
     const long long ro = so * D;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
@@ -816,11 +833,41 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   }
 }
 
+// Kernel body shared by the 32-row-per-wave kernels: one query tile over its
+// whole visited sequence, or (SPLIT) one run of it.
+template <int D, int NW, bool PP, bool SPLIT = false>
+__device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
+  using C = Bf16Cfg<D, NW>;
+  if constexpr (SPLIT) {
+    const int ns = a.nsplit;
+    const int j = (int)blockIdx.x % ns;
+    const int tile = (int)blockIdx.x / ns;  // (b*H + h)*n_qtiles + qt
+    const int qt = tile % a.n_qtiles, bh = tile / a.n_qtiles;
+    const int row_hi = min((qt + 1) * C::BR, a.Sq) - 1;
+    const long long q_hi = qpos(a, row_hi);
+    int total = 0;
+    for (int bi = 0; bi < a.nblk; ++bi) total += tiles_of<64>(a, bi, q_hi);
+    const int lo = (int)((long long)total * j / ns), hi = (int)((long long)total * (j + 1) / ns);
+    attn_bf16_tile<D, NW, PP>(a, smem, bh / a.H, bh % a.H, qt, lo, hi, (long long)tile * ns + j);
+  } else {
+    int b, h, qt;
+    tile_coords(a, b, h, qt);
+    attn_bf16_tile<D, NW, PP>(a, smem, b, h, qt, 0, INT_MAX, -1);
+  }
+}
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ring_attn_bf16(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[Bf16Cfg<D, NW>::LDS];
   attn_bf16_body<D, NW, false>(a, smem);
+}
+
+// The split ring on the 128-row kernel (AttnArgs.nsplit > 1).
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void ring_attn_bf16_split(const AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[Bf16Cfg<D, 4>::LDS];
+  attn_bf16_body<D, 4, false, true>(a, smem);
 }
 
 // Staggered form: 8 waves x 32 query rows, one workgroup per CU, two K and
@@ -2156,12 +2203,12 @@ void launch_bf16(const AttnArgs& a, int D, dim3 grid, hipStream_t stream) {
 }
 
 ra_status launch(AttnArgs& a, int D, ra_dtype dt, hipStream_t stream, const char* name) {
-  Bf16Kernel kk = dt == RA_BF16 ? bf16_kernel(a) : K_BR128;
-  // a split ring needs the kernels built on attn_bf16_body
-  if (a.nsplit > 1 && (kk == K_W64 || kk == K_WS)) kk = K_BR128;
+  // a split ring runs on the 128-row kernel (its slots hold 128 rows)
+  const bool split = a.nsplit > 1;
+  const Bf16Kernel kk = dt != RA_BF16 || split ? K_BR128 : bf16_kernel(a);
   const int br = dt != RA_BF16 ? kBR : kk == K_BR128 ? 128 : 256;
   a.n_qtiles = (a.Sq + br - 1) / br;
-  const long long n_wg = (long long)a.B * a.H * a.n_qtiles * (a.nsplit > 1 ? a.nsplit : 1);
+  const long long n_wg = (long long)a.B * a.H * a.n_qtiles * (split ? a.nsplit : 1);
   if (n_wg == 0) return RA_OK;
   if (n_wg > 0x7fffffffLL)
     return ra::fail(RA_ERR_UNSUPPORTED, "%s: too many query tiles", name);
@@ -2178,6 +2225,9 @@ ra_status launch(AttnArgs& a, int D, ra_dtype dt, hipStream_t stream, const char
       else hipLaunchKernelGGL(ring_attn_bf16_pp<64>, grid, dim3(512), 0, stream, a);
     } else if (kk == K_BR256) {
       launch_bf16<8>(a, D, grid, stream);
+    } else if (split) {
+      if (D == 128) hipLaunchKernelGGL(ring_attn_bf16_split<128>, grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL(ring_attn_bf16_split<64>, grid, dim3(256), 0, stream, a);
     } else {
       launch_bf16<4>(a, D, grid, stream);
     }
@@ -2256,12 +2306,43 @@ extern "C" ra_status ra_block_attn_fwd(const void* q, const void* k, const void*
 }
 
 namespace {
+// Split of the ring set up in `a` (blocks, positions, causal, valid_len):
+// every 128-row query tile's visited-tile sequence in ns runs.  ns = 0
+// chooses: as many runs as keep the B*H*n_qtiles*ns workgroups within the
+// chip's slots (one round, two per compute unit), each run at least
+// kSplitMinRun tiles of the longest sequence; 1 (no split) when the single
+// pass already fills the slots.  Returns the run count (1: no split) and, in
+// ws, the workspace floats (partial o and lse slots) it needs.
+constexpr int kSplitMinRun = 8;  // tiles: 512 keys per workgroup at least
+
+int split_plan(const AttnArgs& a, int D, int ns, long long& ws) {
+  ws = 0;
+  const int n_qt = (a.Sq + 127) / 128;
+  const long long base = (long long)a.B * a.H * n_qt;
+  if (base <= 0) return 1;
+  if (ns <= 0) {
+    if (base >= ra::kWorkgroupSlots) return 1;
+    int max_t = 0;
+    for (int qt = 0; qt < n_qt; ++qt) {
+      const long long q_hi = qpos(a, (qt + 1) * 128 < a.Sq ? (qt + 1) * 128 - 1 : a.Sq - 1);
+      int t = 0;
+      for (int bi = 0; bi < a.nblk; ++bi) t += tiles_of<64>(a, bi, q_hi);
+      if (t > max_t) max_t = t;
+    }
+    ns = (int)(ra::kWorkgroupSlots / base);
+    if (ns > max_t / kSplitMinRun) ns = max_t / kSplitMinRun;
+  }
+  if (ns <= 1) return 1;
+  ws = base * ns * 128 * (long long)(D + 1);
+  return ns;
+}
+
 // The whole ring of one rank (shared by the MHA and GQA entry points).
 ra_status ring_fwd(const char* name, const void* q_r, const void* const* k_blocks,
                    const void* const* v_blocks, int B, int Sb, int H, int Hkv, int D, int P,
                    int rank, ra_dtype dt, float scale, int causal, long long valid_len, void* o,
-                   float* lse_opt, void* stream, int nsplit = 1, float* o_part = nullptr,
-                   float* lse_part = nullptr) {
+                   float* lse_opt, void* stream, int nsplit = 1, float* ws = nullptr,
+                   long long ws_floats = 0) {
   ra::clear_error();
   ra_status st = check_common(name, B, Sb, H, D, dt);
   if (st != RA_OK) return st;
@@ -2313,21 +2394,35 @@ ra_status ring_fwd(const char* name, const void* q_r, const void* const* k_block
       return ra::fail(RA_ERR_SHAPE, "%s: block %d not 16-byte aligned", name, j);
     a.blk[a.nblk++] = KVBlock{k_blocks[j], v_blocks[j], (long long)j * Sb, Sb, cls[t]};
   }
-  // split ring: slice s of the grid visits blocks [s*nblk/ns, (s+1)*nblk/ns)
-  // of the ring order into its own fp32 partial; the partials are then
-  // merged as the rounds' results are ([SPD] §四 combine, n-way)
-  const int ns = dt == RA_BF16 ? (nsplit < a.nblk ? nsplit : a.nblk) : 1;
-  if (ns > 1) {
-    if (!o_part || !lse_part) return ra::fail(RA_ERR_NULL, "%s: NULL split workspace", name);
-    if (!aligned16(o_part))
-      return ra::fail(RA_ERR_SHAPE, "%s: o_part must be 16-byte aligned", name);
-    a.nsplit = ns;
-    a.o = o_part;
-    a.lse = lse_part;
-    a.o_fp32 = 1;
-    st = launch(a, D, dt, (hipStream_t)stream, name);
-    if (st != RA_OK) return st;
-    return ra::merge_splits(name, o_part, lse_part, ns, n_out, D, o, dt, lse_opt, stream);
+  if (nsplit > 1 && dt == RA_BF16) {
+    long long need = 0;
+    const int ns = split_plan(a, D, nsplit, need);
+    if (ns > 1) {
+      if (!ws) return ra::fail(RA_ERR_NULL, "%s: NULL split workspace", name);
+      if (ws_floats < need)
+        return ra::fail(RA_ERR_SHAPE, "%s: split workspace of %lld floats, %lld needed", name,
+                        ws_floats, need);
+      if (!aligned16(ws)) return ra::fail(RA_ERR_SHAPE, "%s: workspace not 16-byte aligned", name);
+      const long long slots = (long long)B * H * ((Sb + 127) / 128) * ns;
+      ra::SplitMergeArgs m{};
+      m.o_part = ws;
+      m.lse_part = ws + slots * 128 * D;
+      m.o = o;
+      m.lse = lse_opt;
+      m.B = B;
+      m.Sq = Sb;
+      m.H = H;
+      m.D = D;
+      m.nsplit = ns;
+      m.out_bf16 = 1;
+      a.nsplit = ns;
+      a.o = ws;
+      a.lse = ws + slots * 128 * D;
+      a.o_fp32 = 1;
+      st = launch(a, D, dt, (hipStream_t)stream, name);
+      if (st != RA_OK) return st;
+      return ra::merge_split(name, m, stream);
+    }
   }
   return launch(a, D, dt, (hipStream_t)stream, name);
 }
@@ -2436,7 +2531,7 @@ extern "C" ra_status ra_ring_attn_fwd_split(const void* q_r, const void* const* 
                                             const void* const* v_blocks, int B, int Sb, int H,
                                             int Hkv, int D, int P, int rank, ra_dtype dt,
                                             float scale, int causal, long long valid_len,
-                                            int nsplit, float* o_part, float* lse_part, void* o,
+                                            int nsplit, float* ws, long long ws_floats, void* o,
                                             float* lse_opt, void* stream) {
   if (nsplit < 1) {
     ra::clear_error();
@@ -2444,7 +2539,46 @@ extern "C" ra_status ra_ring_attn_fwd_split(const void* q_r, const void* const* 
                     nsplit);
   }
   return ring_fwd("ra_ring_attn_fwd_split", q_r, k_blocks, v_blocks, B, Sb, H, Hkv, D, P, rank,
-                  dt, scale, causal, valid_len, o, lse_opt, stream, nsplit, o_part, lse_part);
+                  dt, scale, causal, valid_len, o, lse_opt, stream, nsplit, ws, ws_floats);
+}
+
+extern "C" int ra_ring_split_plan(int B, int Sb, int H, int D, int P, int rank, int causal,
+                                  long long valid_len, int nsplit, long long* ws_floats) {
+  static const char* name = "ra_ring_split_plan";
+  ra::clear_error();
+  if (ws_floats) *ws_floats = 0;
+  if (B < 0 || Sb < 0 || H < 0 || (D != 64 && D != 128) || P <= 0 || P > RA_MAX_P) {
+    ra::fail(RA_ERR_SHAPE, "%s: bad sizes (B=%d Sb=%d H=%d D=%d P=%d)", name, B, Sb, H, D, P);
+    return -1;
+  }
+  if (rank < 0 || rank >= P) {
+    ra::fail(RA_ERR_RANGE, "%s: rank %d outside [0, %d)", name, rank, P);
+    return -1;
+  }
+  if (nsplit < 0) {
+    ra::fail(RA_ERR_RANGE, "%s: nsplit must be >= 0", name);
+    return -1;
+  }
+  const long long S = (long long)P * Sb;
+  if (valid_len < 0 || valid_len > S) valid_len = S;
+  AttnArgs a{};
+  a.q_pos0 = (long long)rank * Sb;
+  a.q_pos1 = a.q_pos0 + Sb;
+  a.q_split = Sb;
+  a.valid_len = valid_len;
+  a.B = B;
+  a.Sq = Sb;
+  a.H = H;
+  a.causal = causal != 0;
+  int src[RA_MAX_P], cls[RA_MAX_P];
+  if (ra_ring_schedule(P, rank, Sb, causal, valid_len, src, cls) != RA_OK) return -1;
+  for (int t = 0; t < P; ++t)
+    if (cls[t] != RA_SKIP)
+      a.blk[a.nblk++] = KVBlock{nullptr, nullptr, (long long)src[t] * Sb, Sb, cls[t]};
+  long long need = 0;
+  const int ns = split_plan(a, D, nsplit, need);
+  if (ws_floats) *ws_floats = need;
+  return ns;
 }
 
 extern "C" ra_status ra_zigzag_attn_fwd(const void* q_r, const void* const* k_shares,

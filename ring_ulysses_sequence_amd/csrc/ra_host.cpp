@@ -46,29 +46,6 @@ int block_class(long long q0, long long q1, long long k0, long long k1,
   return RA_DIAG;
 }
 
-// Workgroup slots of the chip for the 128-row attention kernels: two per
-// compute unit (their LDS use) on 256 compute units.
-constexpr long long kWorkgroupSlots = 512;
-
-int split_hint(long long base_workgroups, int visited) {
-  if (visited <= 1 || base_workgroups <= 0 || base_workgroups >= kWorkgroupSlots) return 1;
-  // slice counts that divide the visited blocks evenly, scored by rounds of
-  // the slots times blocks per slice, plus 0.15 block per slice for the
-  // merge's extra pass over a partial (units of 1/20 block)
-  int best = 1;
-  long long best_cost = -1;
-  for (int ns = 1; ns <= visited; ++ns) {
-    if (visited % ns) continue;
-    const long long rounds = (base_workgroups * ns + kWorkgroupSlots - 1) / kWorkgroupSlots;
-    const long long cost = 20 * rounds * (visited / ns) + 3 * ns;
-    if (best_cost < 0 || cost < best_cost) {
-      best = ns;
-      best_cost = cost;
-    }
-  }
-  return best;
-}
-
 }  // namespace ra
 
 extern "C" {
@@ -150,21 +127,6 @@ ra_status ra_ring_schedule(int P, int rank, long long block_len, int causal,
                                    causal != 0, valid_len);
   }
   return RA_OK;
-}
-
-int ra_ring_split_hint(int B, int Sb, int H, int P, int rank, int causal,
-                       long long valid_len) {
-  ra::clear_error();
-  if (B < 0 || Sb < 0 || H < 0 || P <= 0 || P > RA_MAX_P) {
-    ra::fail(RA_ERR_SHAPE, "ra_ring_split_hint: bad sizes (B=%d Sb=%d H=%d P=%d)", B, Sb, H, P);
-    return -1;
-  }
-  int src[RA_MAX_P], cls[RA_MAX_P];
-  if (ra_ring_schedule(P, rank, Sb, causal, valid_len, src, cls) != RA_OK) return -1;
-  int visited = 0;
-  for (int t = 0; t < P; ++t) visited += cls[t] != RA_SKIP;
-  const long long base = (long long)B * H * ((Sb + 127) / 128);
-  return ra::split_hint(base, visited);
 }
 
 long long ra_zigzag_padded_len(long long S, int P) {

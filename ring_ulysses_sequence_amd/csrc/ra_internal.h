@@ -22,15 +22,24 @@ void clear_error();
 int block_class(long long q0, long long q1, long long k0, long long k1,
                 bool causal, long long valid_len);
 
-// Launch the n-way merge of split-ring partials (o_part [nsplit, rows, D]
-// fp32, lse_part [nsplit, rows]) into o (rows x D in dt) and lse_opt.
-ra_status merge_splits(const char* name, const float* o_part, const float* lse_part, int nsplit,
-                       long long rows, int D, void* o, ra_dtype dt, float* lse_opt,
-                       void* stream);
+// Workgroup slots of the chip for the 128-row attention kernels: two per
+// compute unit (their LDS use) on 256 compute units.
+constexpr long long kWorkgroupSlots = 512;
 
-// Slices worth splitting a ring's visited blocks into (1: none), from the
-// grid of 128-row workgroups against the chip's workgroup slots.
-int split_hint(long long base_workgroups, int visited);
+// The merge of a split ring: output row (b, r, h) of the [B, Sq, H, D]
+// output combines row r % 128 of slots ((b*H + h)*ceil(Sq/128) + r/128)*nsplit
+// + j, j < nsplit, each a normalised fp32 partial o ([slot][128][D]) with its
+// natural lse ([slot][128]).  o is written in bf16 (out_bf16) or fp32, lse
+// when not NULL.
+struct SplitMergeArgs {
+  const float* o_part;
+  const float* lse_part;
+  void* o;
+  float* lse;
+  int B, Sq, H, D;
+  int nsplit, out_bf16;
+};
+ra_status merge_split(const char* name, const SplitMergeArgs& m, void* stream);
 
 // Current value of a process-wide option (see ra_set_option).
 int option(int which);

@@ -59,49 +59,59 @@ __global__ __launch_bounds__(kThreads) void lse_merge(
   }
 }
 
-// n-way form for a ring whose visited blocks were split over grid slices:
-// slice s left its normalised partial in o_part[s] [rows, D] and its natural
-// log-sum-exp in lse_part[s] [rows]; with L = log sum_s exp(lse_s),
+// n-way form for a split ring (layout in ra_internal.h): the runs of a
+// row's query tile each left a normalised partial o_s and its natural
+// log-sum-exp lse_s; with L = log sum_s exp(lse_s),
 //   o = sum_s exp(lse_s - L) o_s,   lse = L
-// (slices that saw no key carry lse_s = -inf and weigh 0; a row no slice saw
-// ends as (0, -inf)).  One row per D/4 consecutive lanes, as above.  NS is
-// the slice count (all loads issued before any use), 0 for a run-time count.
+// (a run that saw no key carries lse_s = -inf and weighs 0; a row no run
+// saw ends as (0, -inf)).  One row per D/4 consecutive lanes; the run loads
+// are issued before they are combined, NS at a time (NS = the run count when
+// it is small, so that the loop unrolls completely).
 template <int NS>
-__global__ __launch_bounds__(kThreads) void split_merge(
-    const float* __restrict__ o_part, const float* __restrict__ lse_part, int nsplit,
-    long long rows, int q4, void* o, int out_bf16, float* lse_out) {
+__global__ __launch_bounds__(kThreads) void split_merge(const ra::SplitMergeArgs m) {
+  const int q4 = m.D / 4;
+  const long long rows = (long long)m.B * m.Sq * m.H;
   const long long t = (long long)blockIdx.x * kThreads + threadIdx.x;
   const long long row = t / q4;
   if (row >= rows) return;
   const int c = (int)(t - row * q4);
-  const int ns = NS > 0 ? NS : nsplit;
-  constexpr int CAP = NS > 0 ? NS : 1;
-  float ls[CAP];
-  float4 xs[CAP];
-  if constexpr (NS > 0) {
+  const int h = (int)(row % m.H);
+  const long long br = row / m.H;
+  const int r = (int)(br % m.Sq), b = (int)(br / m.Sq);
+  const int qt = r >> 7, rr = r & 127;
+  const int n_qt = (m.Sq + 127) >> 7, nseg = m.nsplit;
+  const long long slot0 = ((long long)(b * m.H + h) * n_qt + qt) * nseg;
+  float mx = -INFINITY, sum = 0.0f;
+  float4 acc = float4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k0 = 0; k0 < nseg; k0 += NS) {
+    float ls[NS];
+    float4 xs[NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      ls[s] = lse_part[s * rows + row];
-      xs[s] = ((const float4*)o_part)[s * rows * q4 + t];
+    for (int k = 0; k < NS; ++k) {
+      if (k0 + k < nseg) {
+        const long long sr = (slot0 + k0 + k) * 128 + rr;
+        ls[k] = m.lse_part[sr];
+        xs[k] = ((const float4*)(m.o_part + sr * m.D))[c];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      if (k0 + k < nseg && ls[k] != -INFINITY) {
+        // running log-sum-exp over the segments, rescaled when the max moves
+        const float mn = fmaxf(mx, ls[k]);
+        const float a = __builtin_amdgcn_exp2f((mx - mn) * kLog2e);
+        const float w = __builtin_amdgcn_exp2f((ls[k] - mn) * kLog2e);
+        acc.x = fmaf(w, xs[k].x, acc.x * a);
+        acc.y = fmaf(w, xs[k].y, acc.y * a);
+        acc.z = fmaf(w, xs[k].z, acc.z * a);
+        acc.w = fmaf(w, xs[k].w, acc.w * a);
+        sum = fmaf(sum, a, w);
+        mx = mn;
+      }
     }
   }
-  float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, NS > 0 ? ls[s] : lse_part[s * rows + row]);
-  float4 acc = float4{0.0f, 0.0f, 0.0f, 0.0f};
   float lse = -INFINITY;
-  if (mx != -INFINITY) {
-    float sum = 0.0f;
-#pragma unroll
-    for (int s = 0; s < ns; ++s) {
-      const float l = NS > 0 ? ls[s] : lse_part[s * rows + row];
-      const float4 x = NS > 0 ? xs[s] : ((const float4*)o_part)[s * rows * q4 + t];
-      const float w = __builtin_amdgcn_exp2f((l - mx) * kLog2e);
-      acc.x = fmaf(w, x.x, acc.x);
-      acc.y = fmaf(w, x.y, acc.y);
-      acc.z = fmaf(w, x.z, acc.z);
-      acc.w = fmaf(w, x.w, acc.w);
-      sum += w;
-    }
+  if (sum > 0.0f) {
     const float inv = 1.0f / sum;
     acc.x *= inv;
     acc.y *= inv;
@@ -109,15 +119,15 @@ __global__ __launch_bounds__(kThreads) void split_merge(
     acc.w *= inv;
     lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
   }
-  if (out_bf16) {
+  if (m.out_bf16) {
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    bf16x4 r;
-    r[0] = (__bf16)acc.x; r[1] = (__bf16)acc.y; r[2] = (__bf16)acc.z; r[3] = (__bf16)acc.w;
-    ((bf16x4*)o)[t] = r;
+    bf16x4 y;
+    y[0] = (__bf16)acc.x; y[1] = (__bf16)acc.y; y[2] = (__bf16)acc.z; y[3] = (__bf16)acc.w;
+    ((bf16x4*)m.o)[t] = y;
   } else {
-    ((float4*)o)[t] = acc;
+    ((float4*)m.o)[t] = acc;
   }
-  if (lse_out && c == 0) lse_out[row] = lse;
+  if (m.lse && c == 0) m.lse[row] = lse;
 }
 
 }  // namespace
@@ -154,24 +164,17 @@ extern "C" ra_status ra_ring_merge(float* o_acc, float* lse_acc, const float* o_
 
 namespace ra {
 
-ra_status merge_splits(const char* name, const float* o_part, const float* lse_part, int nsplit,
-                       long long rows, int D, void* o, ra_dtype dt, float* lse_opt,
-                       void* stream) {
-  const int q4 = D / 4;
-  const long long n = rows * q4;
+ra_status merge_split(const char* name, const SplitMergeArgs& m, void* stream) {
+  const long long n = (long long)m.B * m.Sq * m.H * (m.D / 4);
   const long long blocks = (n + kThreads - 1) / kThreads;
   if (blocks > 0x7fffffffLL) return ra::fail(RA_ERR_UNSUPPORTED, "%s: too large", name);
   if (blocks == 0) return RA_OK;
   const dim3 g((unsigned)blocks), t(kThreads);
   hipStream_t s = (hipStream_t)stream;
-  const int bf = dt == RA_BF16 ? 1 : 0;
-  switch (nsplit) {
-    case 2: hipLaunchKernelGGL(split_merge<2>, g, t, 0, s, o_part, lse_part, 2, rows, q4, o, bf, lse_opt); break;
-    case 3: hipLaunchKernelGGL(split_merge<3>, g, t, 0, s, o_part, lse_part, 3, rows, q4, o, bf, lse_opt); break;
-    case 4: hipLaunchKernelGGL(split_merge<4>, g, t, 0, s, o_part, lse_part, 4, rows, q4, o, bf, lse_opt); break;
-    default:
-      hipLaunchKernelGGL(split_merge<0>, g, t, 0, s, o_part, lse_part, nsplit, rows, q4, o, bf,
-                         lse_opt);
+  switch (m.nsplit) {
+    case 2: hipLaunchKernelGGL(split_merge<2>, g, t, 0, s, m); break;
+    case 3: hipLaunchKernelGGL(split_merge<3>, g, t, 0, s, m); break;
+    default: hipLaunchKernelGGL(split_merge<4>, g, t, 0, s, m); break;
   }
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess)

@@ -123,30 +123,52 @@ def test_zigzag_padded_len(lib):
         ra.zigzag_padded_len(10, 0)
 
 
-def test_split_hint(lib):
-    """Slices only while the grid of 128-row workgroups is under the chip's
-    512 slots, a divisor of the visited blocks that minimises rounds x
-    blocks per slice (+0.15 block per slice for the merge); -1 on bad
-    sizes."""
-    def model(base, vis):
-        if vis <= 1 or base >= 512:
-            return 1
-        cost = {ns: 20 * -(-base * ns // 512) * (vis // ns) + 3 * ns
-                for ns in range(1, vis + 1) if vis % ns == 0}
-        return min(cost, key=lambda ns: (cost[ns], ns))
-    # DiT shard: 24 heads x 8 row tiles = 192 workgroups, 4 blocks visited:
-    # two slices (one round of 384) beat four (two rounds of 768)
-    assert ra.ring_split_hint(1, 1024, 24, 4, 0) == 2 == model(192, 4)
-    # causal rank 1 visits 2 blocks; rank 0 only its own
-    assert ra.ring_split_hint(1, 1024, 24, 4, 1, causal=True) == 2
-    assert ra.ring_split_hint(1, 1024, 24, 4, 0, causal=True) == 1
-    # the long-context share fills the chip
-    assert ra.ring_split_hint(1, 16384, 64, 8, 3, causal=True) == 1
-    for B, Sb, H, P in [(1, 128 * 75, 4, 8), (2, 512, 4, 4), (1, 2048, 2, 6), (1, 640, 9, 3)]:
-        base = B * H * -(-Sb // 128)
-        assert ra.ring_split_hint(B, Sb, H, P, 0) == model(base, P), (B, Sb, H, P)
+def _plan_model(B, Sb, H, D, P, rank, causal=False, valid=-1, ns=0):
+    """Independent model of the split plan: runs per 128-row query tile so
+    that the workgroups fit 512 slots once, each at least 8 of the longest
+    query tile's visited 64-key tiles; 1 when the single pass fills them."""
+    S = P * Sb
+    valid = S if valid < 0 or valid > S else valid
+    n_qt = -(-Sb // 128)
+    base = B * H * n_qt
+    if base == 0:
+        return 1, 0
+    if ns <= 0:
+        if base >= 512:
+            return 1, 0
+        src, cls = sch.ring_schedule(P, rank, Sb, causal, valid)
+        starts = [j * Sb for j, c in zip(src, cls) if c != ra.RA_SKIP]
+        max_t = 0
+        for qt in range(n_qt):
+            q_hi = rank * Sb + min((qt + 1) * 128, Sb) - 1
+            lim = min(valid - 1, q_hi) if causal else valid - 1
+            t = sum(0 if lim < k0 else min(-(-Sb // 64), (lim - k0) // 64 + 1) for k0 in starts)
+            max_t = max(max_t, t)
+        ns = min(512 // base, max_t // 8)
+    if ns <= 1:
+        return 1, 0
+    return ns, base * ns * 128 * (D + 1)
+
+
+def test_split_plan(lib):
+    """The split plan against an independent model: the DiT shard (192
+    workgroups of 128 rows, 64 tiles each) gets two runs per query tile (384
+    workgroups); the long-context share fills the chip and is not split;
+    forced counts, causal ranks and padding; -1 on bad sizes."""
+    assert ra.ring_split_plan(1, 1024, 24, 128, 4, 0) == (2, 192 * 2 * 128 * 129)
+    assert ra.ring_split_plan(1, 16384, 64, 128, 8, 3, causal=True) == (1, 0)
+    cases = [(1, 1024, 24, 128, 4, r, c, -1, n) for r in range(4) for c in (False, True)
+             for n in (0, 1, 3, 7)]
+    cases += [(2, 752, 16, 64, 4, r, True, 3000, n) for r in range(4) for n in (0, 5)]
+    cases += [(1, 512, 4, 64, 8, r, c, -1, 0) for r in range(8) for c in (False, True)]
+    cases += [(1, 128 * 70, 2, 128, 2, 0, False, -1, 0)]
+    for B, Sb, H, D, P, r, c, vl, n in cases:
+        assert ra.ring_split_plan(B, Sb, H, D, P, r, c, vl, n) == \
+            _plan_model(B, Sb, H, D, P, r, c, vl, n), (B, Sb, H, D, P, r, c, vl, n)
     with pytest.raises(ValueError):
-        ra.ring_split_hint(1, 16, 1, 0, 0)
+        ra.ring_split_plan(1, 16, 1, 64, 0, 0)
+    with pytest.raises(ValueError):
+        ra.ring_split_plan(1, 16, 1, 96, 2, 0)
 
 
 def test_classify_block_matches_brute_force(lib):
@@ -229,6 +251,10 @@ def test_device_entry_points_validate_before_launch(lib):
     st = lib.ra_ring_attn_bwd(null, arr, arr, null, null, null, 1, 16, 1, 64, 2, 0, ra.RA_BF16,
                               0.0, 0, -1, null, arr, arr, null, null)
     assert st == 1
+    # split ring: run count below 1
+    st = lib.ra_ring_attn_fwd_split(null, arr, arr, 1, 128, 1, 1, 64, 2, 0, ra.RA_BF16, 0.0, 0,
+                                    -1, 0, null, 0, null, null, null)
+    assert st == ra.RA_ERR_RANGE and b"nsplit" in lib.ra_last_error()
     # one-round backward: fp32 unsupported, D, NULL, empty
     st = lib.ra_block_attn_bwd(null, null, null, null, null, null, 1, 16, 16, 1, 64, ra.RA_FP32,
                                0.0, 0, 0, 0, -1, null, null, null, null, null)
