@@ -180,6 +180,7 @@ def main():
     extra = {}
     if not args.no_extra:
         extra = side_measurements(torch, ra, W, stream)
+        extra.update(config_measurements(torch, ra, W, stream))
         extra.update(zigzag_measurements(torch, ra, W, stream, q, k, v))
         extra.update(backward_measurement(torch, ra, W, stream, q_r, kb, vb, o, lse, flops))
         extra.update(gqa_varlen_measurements(torch, ra, stream, q_r, k, v, kb, vb))
@@ -230,6 +231,134 @@ def main():
         "extra": extra,
     }
     print(json.dumps(rec), flush=True)
+
+
+def config_measurements(torch, ra, W, stream):
+    """Side numbers for the other configurations, not the step: the Ulysses
+    local attention (all eight ranks' head shards in one launch) and the
+    whole Ulysses path (three seq->head transposes, attention, head->seq);
+    every rank of the padded causal share in sequence; the tiny fp32 ring
+    (launch-latency bound)."""
+    out = {}
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(f, n):
+        for _ in range(3):
+            f()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(n):
+            f()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    # Ulysses: [8, 1, 2048, 32, 128] per tensor; attention on 4 heads per rank
+    w = W.ULYSSES
+    P, Sl, Hl = w.P, w.S // w.P, w.H // w.P
+    q, k, v = W.make_qkv(w, device="cuda")
+    stack = lambda x: x.view(w.B, P, Sl, w.H, w.D).transpose(0, 1).contiguous()
+    qs, ks, vs = stack(q), stack(k), stack(v)
+    del q, k, v
+    qh, kh, vh = ra.seq2head(qs), ra.seq2head(ks), ra.seq2head(vs)
+    flat = lambda x: x.view(P * w.B, w.S, Hl, w.D)
+    oh = torch.empty_like(flat(qh))
+    attn = lambda: ra.ring_attn_fwd(flat(qh), [flat(kh)], [flat(vh)], 0, out=oh,
+                                    want_lse=False, stream=stream)
+    ms = timed(attn, 10)
+    fl = 4.0 * w.D * w.S * w.S * w.H * w.B
+    out["ulysses_attention_all_ranks"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+                                          "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+    osq = torch.empty_like(qs)
+
+    def path():
+        ra.seq2head(qs, out=qh, stream=stream)
+        ra.seq2head(ks, out=kh, stream=stream)
+        ra.seq2head(vs, out=vh, stream=stream)
+        attn()
+        ra.head2seq(oh.view(P, w.B, w.S, Hl, w.D), out=osq, stream=stream)
+    ms = timed(path, 10)
+    out["ulysses_path_all_ranks"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2)}
+    del qs, ks, vs, qh, kh, vh, oh, osq
+
+    # padded causal share (S = 3000 in 3008, P = 4): every rank in turn
+    w = W.PADDED_CAUSAL
+    Sb = w.block_len
+    q, k, v = W.make_qkv(w, device="cuda")
+    kb = [k[:, j * Sb:(j + 1) * Sb].contiguous() for j in range(w.P)]
+    vb = [v[:, j * Sb:(j + 1) * Sb].contiguous() for j in range(w.P)]
+    qr = [q[:, r * Sb:(r + 1) * Sb].contiguous() for r in range(w.P)]
+    outs = [torch.empty_like(x) for x in qr]
+    ranks = lambda: [ra.ring_attn_fwd(qr[r], kb, vb, r, causal=True, valid_len=w.S, out=outs[r],
+                                      want_lse=False, stream=stream) for r in range(w.P)]
+    ms = timed(ranks, 20)
+    # visible (query, key) pairs over the real rows: sum of (i + 1) for i < S
+    fl = 4.0 * w.D * w.H * w.B * w.S * (w.S + 1) / 2
+    out["padded_causal_all_ranks"] = {"ms": round(ms, 4), "us_per_rank": round(1e3 * ms / w.P, 2),
+                                      "tflops": round(fl / ms / 1e9, 2)}
+    # the same four calls replayed from a HIP graph: the GPU's own time,
+    # without the Python binding's per-call host work between launches
+    ref = [x.clone() for x in outs]
+    gms = graph_ms(torch, lambda: [ra.ring_attn_fwd(qr[r], kb, vb, r, causal=True, valid_len=w.S,
+                                                    out=outs[r], want_lse=False)
+                                   for r in range(w.P)], outs, ref, 20)
+    if gms is not None:
+        out["padded_causal_all_ranks"].update({"graph_ms": round(gms, 4),
+                                               "graph_us_per_rank": round(1e3 * gms / w.P, 2),
+                                               "graph_tflops": round(fl / gms / 1e9, 2)})
+    del q, k, v, kb, vb, qr, outs
+
+    # tiny fp32 ring (B = 1, S = 256, H = 2, D = 64, P = 2): both ranks
+    w = W.TINY_FP32
+    Sb = w.block_len
+    q, k, v = W.make_qkv(w, device="cuda")
+    kb = [k[:, j * Sb:(j + 1) * Sb].contiguous() for j in range(w.P)]
+    vb = [v[:, j * Sb:(j + 1) * Sb].contiguous() for j in range(w.P)]
+    qr = [q[:, r * Sb:(r + 1) * Sb].contiguous() for r in range(w.P)]
+    outs = [torch.empty_like(x) for x in qr]
+    ms = timed(lambda: [ra.ring_attn_fwd(qr[r], kb, vb, r, out=outs[r], want_lse=False,
+                                         stream=stream) for r in range(w.P)], 50)
+    out["tiny_fp32_both_ranks"] = {"ms": round(ms, 4), "us_per_rank": round(1e3 * ms / w.P, 2)}
+    ref = [x.clone() for x in outs]
+    gms = graph_ms(torch, lambda: [ra.ring_attn_fwd(qr[r], kb, vb, r, out=outs[r], want_lse=False)
+                                   for r in range(w.P)], outs, ref, 50)
+    if gms is not None:
+        out["tiny_fp32_both_ranks"].update({"graph_ms": round(gms, 4),
+                                            "graph_us_per_rank": round(1e3 * gms / w.P, 2)})
+    return out
+
+
+def graph_ms(torch, calls, outs, ref, n):
+    """Average time of `calls` replayed from a captured HIP graph (None if it
+    cannot be captured); every replay's outputs must equal the eager ones."""
+    try:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            calls()  # warm the graph pool's allocations outside capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            calls()
+    except Exception as e:  # capture is a convenience for timing only
+        print(f"graph capture failed: {e}", file=sys.stderr, flush=True)
+        return None
+    for _ in range(3):
+        for x in outs:
+            x.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(outs, ref):
+            if not torch.equal(x, y):
+                raise RuntimeError("graph replay differs from the eager result")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
 
 
 def side_measurements(torch, ra, W, stream):
