@@ -541,6 +541,21 @@ def zigzag_measurements(torch, ra, W, stream, q, k, v):
                                               want_lse=False, stream=stream))
         out[f"zigzag_long_rank{r}"] = {"ms": round(ms, 3), "flops": zz_flops,
                                        "tflops": round(zz_flops / ms / 1e9, 2)}
+        if r == w.ranks[-1]:
+            # the zigzag backward of the same share (five products per pair)
+            o, lse = ra.zigzag_attn_fwd(q_r, ks, vs, r, causal=True, stream=stream)
+            do = torch.randn(q_r.shape, generator=torch.Generator(device="cuda").manual_seed(43),
+                             device="cuda").to(q_r.dtype)
+            f32 = dict(dtype=torch.float32, device="cuda")
+            dq = torch.zeros(q_r.shape, **f32)
+            dks = [torch.zeros(q_r.shape, **f32) for _ in range(P)]
+            dvs = [torch.zeros(q_r.shape, **f32) for _ in range(P)]
+            ms = timed(lambda: ra.zigzag_attn_bwd(q_r, ks, vs, o, do, lse, r, causal=True, dq=dq,
+                                                  dk_shares=dks, dv_shares=dvs, stream=stream))
+            out[f"zigzag_backward_long_rank{r}"] = {
+                "ms": round(ms, 3), "flops": 2.5 * zz_flops,
+                "tflops": round(2.5 * zz_flops / ms / 1e9, 2)}
+            del lse, do, dq, dks, dvs
         del q_r, o
     del ks, vs
     Sb = w.S // P

@@ -336,6 +336,25 @@ ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_blocks,
                            float* const* dk_blocks, float* const* dv_blocks,
                            float* stats_ws, void* stream);
 
+/* Backward of rank `rank`'s zigzag ring ([RA] §3.4 load balancing with
+ * the backward of §3.3 closing paragraph, §6.2): as ra_ring_attn_bwd over
+ * the shares of ra_zigzag_attn_fwd.  q_r, o_r, do_r [B,Sr,H,D] bf16 (chunk
+ * rank then chunk 2P-1-rank), lse_r [B,Sr,H] fp32 (ra_zigzag_attn_fwd's
+ * lse); k_shares / v_shares HOST arrays of P device pointers to every
+ * rank's [B,Sr,H,D] share.  Accumulates (+=) dq_r [B,Sr,H,D] fp32 and, into
+ * dk_shares[j] / dv_shares[j] (fp32 [B,Sr,H,D], entries of shares the rank
+ * skips may be NULL), the parts of share j's two chunks; summed over all
+ * ranks they are the owners' gradients.  stats_ws: fp32 scratch of
+ * 2*B*Sr*H floats.  Sr a multiple of 128, P at most RA_MAX_P/2, only bf16
+ * inputs; other errors as ra_ring_attn_bwd.  Two launches on `stream`. */
+ra_status ra_zigzag_attn_bwd(const void* q_r, const void* const* k_shares,
+                             const void* const* v_shares, const void* o_r,
+                             const void* do_r, const float* lse_r, int B, int Sr,
+                             int H, int D, int P, int rank, ra_dtype dt, float scale,
+                             int causal, long long valid_len, float* dq_r,
+                             float* const* dk_shares, float* const* dv_shares,
+                             float* stats_ws, void* stream);
+
 /* Ulysses sequence-shard -> head-shard transpose ([RA] §3.5) of the P
  * per-rank tensors stacked rank-major:
  *   src [P, B, S/P, H, D]  ->  dst [P, B, S, H/P, D]

@@ -43,7 +43,7 @@ EXPORTED = (
     "ra_ring_merge", "ra_ring_attn_fwd", "ra_seq2head", "ra_head2seq",
     "ra_zigzag_padded_len", "ra_zigzag_schedule", "ra_zigzag_attn_fwd", "ra_ring_attn_bwd",
     "ra_ring_attn_fwd_gqa", "ra_ring_attn_fwd_varlen", "ra_block_attn_bwd",
-    "ra_ring_attn_fwd_split", "ra_ring_split_plan",
+    "ra_ring_attn_fwd_split", "ra_ring_split_plan", "ra_zigzag_attn_bwd",
 )
 
 _lib = None
@@ -95,6 +95,10 @@ def _load():
                                             c_int, c_int, c_int, c_int, c_int, c_int, c_float,
                                             c_int, ctypes.POINTER(c_ll), c_int, c_vp, c_vp,
                                             c_vp]),
+        "ra_zigzag_attn_bwd": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp,
+                                       c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int,
+                                       c_int, c_float, c_int, c_ll, c_vp, ctypes.POINTER(c_vp),
+                                       ctypes.POINTER(c_vp), c_vp, c_vp]),
         "ra_ring_attn_bwd": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp, c_vp,
                                      c_vp, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                      c_float, c_int, c_ll, c_vp, ctypes.POINTER(c_vp),
@@ -460,6 +464,22 @@ def ring_attn_bwd(q_r, k_blocks: Sequence, v_blocks: Sequence, o_r, do_r, lse_r,
     dk_blocks[j], dv_blocks[j]) (fp32, zero-initialised when not given) the
     gradients of the rank's queries and of the blocks it visits.  Returns
     (dq, dk_blocks, dv_blocks)."""
+    return _ring_bwd("ra_ring_attn_bwd", q_r, k_blocks, v_blocks, o_r, do_r, lse_r, rank,
+                     causal, valid_len, scale, dq, dk_blocks, dv_blocks, stream)
+
+
+def zigzag_attn_bwd(q_r, k_shares: Sequence, v_shares: Sequence, o_r, do_r, lse_r, rank: int, *,
+                    causal: bool = True, valid_len: int = -1, scale: float = 0.0,
+                    dq=None, dk_shares=None, dv_shares=None, stream=None):
+    """Backward of rank ``rank``'s zigzag ring (shares as in zigzag_attn_fwd):
+    accumulates into (dq [B,Sr,H,D], dk_shares[j], dv_shares[j]) (fp32,
+    zero-initialised when not given).  Returns (dq, dk_shares, dv_shares)."""
+    return _ring_bwd("ra_zigzag_attn_bwd", q_r, k_shares, v_shares, o_r, do_r, lse_r, rank,
+                     causal, valid_len, scale, dq, dk_shares, dv_shares, stream)
+
+
+def _ring_bwd(fn_name, q_r, k_blocks, v_blocks, o_r, do_r, lse_r, rank, causal, valid_len,
+              scale, dq, dk_blocks, dv_blocks, stream):
     torch = _torch()
     B, Sb, H, D = q_r.shape
     P = len(k_blocks)
@@ -493,11 +513,11 @@ def ring_attn_bwd(q_r, k_blocks: Sequence, v_blocks: Sequence, o_r, do_r, lse_r,
     if dq.shape != q_r.shape or dq.dtype != torch.float32:
         raise ValueError("dq must be fp32 of q_r's shape")
     stats = torch.empty((2, B, H, Sb), **f32)
-    st = _load().ra_ring_attn_bwd(_dev(q_r, "q_r"), kp, vp, _dev(o_r, "o_r"), _dev(do_r, "do_r"),
-                                  _dev(lse_r, "lse_r"), B, Sb, H, D, P, rank, dt, float(scale),
-                                  int(causal), valid_len, _dev(dq, "dq"), dkp, dvp,
-                                  _dev(stats, "stats"), _stream(stream))
-    _check(st, "ra_ring_attn_bwd")
+    st = getattr(_load(), fn_name)(_dev(q_r, "q_r"), kp, vp, _dev(o_r, "o_r"), _dev(do_r, "do_r"),
+                                   _dev(lse_r, "lse_r"), B, Sb, H, D, P, rank, dt, float(scale),
+                                   int(causal), valid_len, _dev(dq, "dq"), dkp, dvp,
+                                   _dev(stats, "stats"), _stream(stream))
+    _check(st, fn_name)
     return dq, dk_blocks, dv_blocks
 
 
@@ -567,7 +587,7 @@ __all__ = [
     "block_attn_fwd", "ring_merge", "ring_attn_fwd", "seq2head", "head2seq",
     "zigzag_padded_len", "zigzag_schedule", "zigzag_attn_fwd", "ring_attn_bwd",
     "ring_attn_fwd_varlen",
-    "ring_attn_composable", "block_attn_bwd", "ring_split_plan", "EXPORTED", "LIB_PATH", "LibraryMissing",
+    "ring_attn_composable", "block_attn_bwd", "ring_split_plan", "zigzag_attn_bwd", "EXPORTED", "LIB_PATH", "LibraryMissing",
     "RA_BF16", "RA_FP32", "RA_SKIP", "RA_FULL", "RA_DIAG", "RA_MAX_P", "RA_PAD_MULTIPLE",
     "RA_KERNEL_AUTO", "RA_KERNEL_BR128", "RA_KERNEL_BR256", "RA_KERNEL_W64", "RA_KERNEL_WS",
     "RA_KERNEL_PP",

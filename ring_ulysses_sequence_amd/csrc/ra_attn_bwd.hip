@@ -83,6 +83,11 @@ struct BwdArgs {
   float* stats;       // [2, B, H, Sq] fp32: base-2 lse, then rowsum(dO * O);
                       // written by the dq kernel, read by the dk/dv kernel
   long long q_pos0;   // global position of query row 0
+  // query row r sits at q_pos0 + r below q_split, at q_pos1 + (r - q_split)
+  // from it on (the two chunks of a zigzag share; q_split is a multiple of
+  // 64 and positions increase with the row)
+  long long q_pos1;
+  int q_split;
   long long valid_len;
   int B, Sq, H;
   int kv_rows_b;      // rows between consecutive batches in every K/V buffer
@@ -93,6 +98,10 @@ struct BwdArgs {
   int nblk;
   BwdBlock blk[RA_MAX_P];
 };
+
+__device__ __forceinline__ long long qpos(const BwdArgs& a, int row) {
+  return row < a.q_split ? a.q_pos0 + row : a.q_pos1 + (row - a.q_split);
+}
 
 template <int D>
 struct Cfg {
@@ -292,10 +301,10 @@ void ring_attn_bwd_dq(const BwdArgs a) {
   const int bh = blockIdx.x / n_qt, qt = blockIdx.x % n_qt;
   const int b = bh / a.H, h = bh % a.H;
   const int row0 = qt * kRows;
-  const long long q_hi = a.q_pos0 + min(row0 + kRows, a.Sq) - 1;
+  const long long q_hi = qpos(a, min(row0 + kRows, a.Sq) - 1);
   const int wrow0 = row0 + wave * 32;
   const int wrows = min(32, a.Sq - wrow0);
-  const long long wq_lo = a.q_pos0 + wrow0, wq_hi = wq_lo + wrows - 1;
+  const long long wq_lo = qpos(a, wrow0), wq_hi = wq_lo + wrows - 1;
   const long long HD = (long long)a.H * D;
   const int HD2 = (int)(HD * 2);  // bytes between K/V rows
 
@@ -586,7 +595,15 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
 
   const long long k_lo = kb.k_pos0 + (long long)kt * kRows;
   int t0 = 0;
-  if (a.causal && k_lo > a.q_pos0) t0 = (int)min((long long)a.Sq, (k_lo - a.q_pos0) / kTile);
+  if (a.causal) {
+    // the first 64-row query tile whose last query is at or after k_lo
+    // (tiles never straddle the split)
+    if (k_lo <= a.q_pos0 + a.q_split - 1)
+      t0 = k_lo > a.q_pos0 ? (int)((k_lo - a.q_pos0) / kTile) : 0;
+    else
+      t0 = a.q_split / kTile + (k_lo > a.q_pos1 ? (int)min((long long)a.Sq, (k_lo - a.q_pos1) / kTile) : 0);
+    if (t0 > (a.Sq + kTile - 1) / kTile) t0 = (a.Sq + kTile - 1) / kTile;
+  }
   const int n_t = (a.Sq + kTile - 1) / kTile;
   const long long stat0 = ((long long)b * a.H + h) * a.Sq;
   // Q and dO tiles by all eight waves; the statistics rows by waves 0 (lse)
@@ -613,7 +630,7 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
   const float c_scale = a.scale_log2;
   for (int ti = t0; ti < n_t; ++ti) {
     if (ti + 1 < n_t) copy_q(ti + 1, base + (buf ^ 1) * PC::BUF);
-    const long long qp0 = a.q_pos0 + (long long)ti * kTile;
+    const long long qp0 = qpos(a, ti * kTile);
     const long long qp_hi = qp0 + min(kTile, a.Sq - ti * kTile) - 1;
     const bool live = !(a.causal && kw_lo > qp_hi) && kw_lo < a.valid_len;
     const bool need = kw_hi >= a.valid_len || (a.causal && kw_hi > qp0);
@@ -727,6 +744,8 @@ extern "C" ra_status ra_block_attn_bwd(const void* q, const void* k, const void*
   a.dq = dq;
   a.stats = stats_ws;
   a.q_pos0 = q_pos0;
+  a.q_pos1 = q_pos0 + Sq;
+  a.q_split = Sq;
   a.valid_len = valid_len;
   a.B = B;
   a.Sq = Sq;
@@ -772,6 +791,8 @@ extern "C" ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_bloc
   a.dq = dq_r;
   a.stats = stats_ws;
   a.q_pos0 = (long long)rank * Sb;
+  a.q_pos1 = a.q_pos0 + Sb;
+  a.q_split = Sb;
   a.valid_len = valid_len;
   a.B = B;
   a.Sq = Sb;
@@ -797,4 +818,76 @@ extern "C" ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_bloc
                                (long long)j * Sb, Sb, 0};
   }
   return launch_bwd(name, a, D, Sb, (hipStream_t)stream);
+}
+
+extern "C" ra_status ra_zigzag_attn_bwd(const void* q_r, const void* const* k_shares,
+                                        const void* const* v_shares, const void* o_r,
+                                        const void* do_r, const float* lse_r, int B, int Sr,
+                                        int H, int D, int P, int rank, ra_dtype dt, float scale,
+                                        int causal, long long valid_len, float* dq_r,
+                                        float* const* dk_shares, float* const* dv_shares,
+                                        float* stats_ws, void* stream) {
+  static const char* name = "ra_zigzag_attn_bwd";
+  ra::clear_error();
+  ra_status st = check_common(name, B, Sr, H, D, dt);
+  if (st != RA_OK) return st;
+  if (P <= 0) return ra::fail(RA_ERR_SHAPE, "%s: P must be positive (got %d)", name, P);
+  if (2 * P > RA_MAX_P)
+    return ra::fail(RA_ERR_RANGE, "%s: P=%d exceeds RA_MAX_P/2=%d", name, P, RA_MAX_P / 2);
+  if (rank < 0 || rank >= P) return ra::fail(RA_ERR_RANGE, "%s: rank %d outside [0, %d)", name, rank, P);
+  if (Sr % 128 != 0)
+    return ra::fail(RA_ERR_SHAPE, "%s: rows per rank (%d) must be two chunks of a multiple "
+                    "of 64 rows; pad the sequence to ra_zigzag_padded_len(S, P)", name, Sr);
+  if ((long long)B * Sr * H == 0) return RA_OK;
+  if (!q_r || !o_r || !do_r || !lse_r || !dq_r || !stats_ws || !k_shares || !v_shares ||
+      !dk_shares || !dv_shares)
+    return ra::fail(RA_ERR_NULL, "%s: NULL argument", name);
+  if (!aligned16(q_r) || !aligned16(o_r) || !aligned16(do_r) || !aligned16(dq_r))
+    return ra::fail(RA_ERR_SHAPE, "%s: q, o, do and dq must be 16-byte aligned", name);
+  const int c = Sr / 2;  // chunk length
+  const long long S = (long long)P * Sr;
+  if (valid_len < 0 || valid_len > S) valid_len = S;
+  BwdArgs a{};
+  a.q = q_r;
+  a.o = o_r;
+  a.dout = do_r;
+  a.lse = lse_r;
+  a.dq = dq_r;
+  a.stats = stats_ws;
+  // the share is chunk rank (rows [0, c)) then chunk 2P-1-rank (rows [c, 2c))
+  a.q_pos0 = (long long)rank * c;
+  a.q_pos1 = (long long)(2 * P - 1 - rank) * c;
+  a.q_split = c;
+  a.valid_len = valid_len;
+  a.B = B;
+  a.Sq = Sr;
+  a.H = H;
+  a.kv_rows_b = Sr;
+  a.causal = causal != 0;
+  set_scale(a, scale, D);
+  // the zigzag ring: round t visits the share of rank (rank - t) mod P, each
+  // share two chunks classified against the whole query share; the dK/dV
+  // parts of a chunk go to the matching rows of its share's buffers
+  int src[RA_MAX_P], cls[2 * RA_MAX_P];
+  st = ra_zigzag_schedule(P, rank, c, causal, valid_len, src, cls);
+  if (st != RA_OK) return st;
+  a.nblk = 0;
+  const size_t in_row = (size_t)H * D * 2, g_row = (size_t)H * D;
+  for (int t = 0; t < P; ++t) {
+    const int j = src[t];
+    for (int half = 0; half < 2; ++half) {
+      if (cls[2 * t + half] == RA_SKIP) continue;
+      if (!k_shares[j] || !v_shares[j] || !dk_shares[j] || !dv_shares[j])
+        return ra::fail(RA_ERR_NULL, "%s: NULL pointer for visited share %d", name, j);
+      if (!aligned16(k_shares[j]) || !aligned16(v_shares[j]) || !aligned16(dk_shares[j]) ||
+          !aligned16(dv_shares[j]))
+        return ra::fail(RA_ERR_SHAPE, "%s: share %d not 16-byte aligned", name, j);
+      const int chunk = half == 0 ? j : 2 * P - 1 - j;
+      const size_t r0 = (size_t)half * c;
+      a.blk[a.nblk++] = BwdBlock{(const char*)k_shares[j] + r0 * in_row,
+                                 (const char*)v_shares[j] + r0 * in_row, dk_shares[j] + r0 * g_row,
+                                 dv_shares[j] + r0 * g_row, (long long)chunk * c, c, 0};
+    }
+  }
+  return launch_bwd(name, a, D, c, (hipStream_t)stream);
 }

@@ -710,6 +710,43 @@ def test_block_backward_rounds(D, causal):
     check_grad(dq_sum.cpu(), fq, "dq summed over the rounds vs the plain definition")
 
 
+@pytest.mark.parametrize("D,causal,pad", [(128, True, 0), (64, True, 41), (128, False, 0)])
+def test_zigzag_backward_all_ranks(D, causal, pad):
+    """Zigzag ring backward (chunks of 192 rows: the last 128-key tile of
+    every chunk is half full), B = 2: every rank's dq against the rows of the
+    full-sequence gradient at its share's positions, and the dk/dv parts of
+    all ranks accumulated into the share buffers against the full-sequence
+    gradients at each share's positions (real rows; the padded case masks
+    the last 41 keys)."""
+    B, S, H, P = 2, 1536, 3, 4
+    c = S // (2 * P)
+    valid = S - pad
+    q, k, v, do = (W.random_tensor((B, S, H, D), seed=s_, device="cuda") for s_ in (71, 72, 73, 74))
+    if pad:
+        for x in (q, k, v, do):
+            x[:, valid:] = 0
+    qs, ks, vs, dos = (zigzag_shares(x, P) for x in (q, k, v, do))
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dk_all = [torch.zeros(x.shape, **f32) for x in ks]
+    dv_all = [torch.zeros(x.shape, **f32) for x in ks]
+    fq, fk, fv = oracle.attention_grad(q.cpu(), k.cpu(), v.cpu(), do.cpu(), causal=causal,
+                                       valid_len=valid)
+    for r in range(P):
+        say("zigzag bwd", D, causal, pad, "rank", r)
+        o, lse = ra.zigzag_attn_fwd(qs[r], ks, vs, r, causal=causal, valid_len=valid)
+        dq, _, _ = ra.zigzag_attn_bwd(qs[r], ks, vs, o, dos[r], lse, r, causal=causal,
+                                      valid_len=valid, dk_shares=dk_all, dv_shares=dv_all)
+        torch.cuda.synchronize()
+        pos = np.asarray(oracle.zigzag_positions(P, r, c))
+        real = pos < valid
+        check_grad(dq.cpu()[:, real], fq[:, pos[real]], f"zigzag dq r{r}")
+    for j in range(P):
+        pos = np.asarray(oracle.zigzag_positions(P, j, c))
+        real = pos < valid
+        check_grad(dk_all[j].cpu()[:, real], fk[:, pos[real]], f"zigzag dk share {j}")
+        check_grad(dv_all[j].cpu()[:, real], fv[:, pos[real]], f"zigzag dv share {j}")
+
+
 def test_ring_backward_long_context_rank3():
     """L = 131072, H = 64, P = 8, rank 3 (the bench share): dq on sampled
     rows and dk / dv on sampled keys of the diagonal and the first block,

@@ -268,6 +268,16 @@ def test_device_entry_points_validate_before_launch(lib):
     st = lib.ra_block_attn_bwd(null, null, null, null, null, null, 1, 16, 0, 1, 64, ra.RA_BF16,
                                0.0, 0, 0, 0, -1, null, null, null, null, null)
     assert st == 0
+    # zigzag backward: rows per rank not two chunks of a multiple of 64; fp32
+    st = lib.ra_zigzag_attn_bwd(null, arr, arr, null, null, null, 1, 96, 1, 64, 2, 0, ra.RA_BF16,
+                                0.0, 1, -1, null, arr, arr, null, null)
+    assert st == 2 and b"ra_zigzag_padded_len" in lib.ra_last_error()
+    st = lib.ra_zigzag_attn_bwd(null, arr, arr, null, null, null, 1, 128, 1, 64, 2, 0, ra.RA_FP32,
+                                0.0, 1, -1, null, arr, arr, null, null)
+    assert st == 5
+    st = lib.ra_zigzag_attn_bwd(null, arr, arr, null, null, null, 1, 128, 1, 64, 2, 0, ra.RA_BF16,
+                                0.0, 1, -1, null, arr, arr, null, null)
+    assert st == 1
     # merge: unsupported D, unknown dtype
     st = lib.ra_ring_merge(null, null, null, null, 1, 4, 1, 12, null, ra.RA_FP32, null)
     assert st == 5
