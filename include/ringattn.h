@@ -336,6 +336,20 @@ ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_blocks,
                            float* const* dk_blocks, float* const* dv_blocks,
                            float* stats_ws, void* stream);
 
+/* Grouped-query form of ra_ring_attn_bwd ([RA] §3.5 and §6 name GQA): q_r,
+ * o_r, do_r, dq_r [B,Sb,H,D]; every k_blocks[j] / v_blocks[j] and
+ * dk_blocks[j] / dv_blocks[j] [B,Sb,H_kv,D] (bf16 / fp32).  Query head h
+ * uses K/V head h / (H / H_kv), so the dK/dV of a K/V head sum the terms of
+ * its H / H_kv query heads.  RA_ERR_SHAPE unless H_kv > 0 divides H;
+ * everything else as ra_ring_attn_bwd. */
+ra_status ra_ring_attn_bwd_gqa(const void* q_r, const void* const* k_blocks,
+                               const void* const* v_blocks, const void* o_r,
+                               const void* do_r, const float* lse_r, int B, int Sb,
+                               int H, int H_kv, int D, int P, int rank, ra_dtype dt,
+                               float scale, int causal, long long valid_len,
+                               float* dq_r, float* const* dk_blocks,
+                               float* const* dv_blocks, float* stats_ws, void* stream);
+
 /* Backward of rank `rank`'s zigzag ring ([RA] §3.4 load balancing with
  * the backward of §3.3 closing paragraph, §6.2): as ra_ring_attn_bwd over
  * the shares of ra_zigzag_attn_fwd.  q_r, o_r, do_r [B,Sr,H,D] bf16 (chunk

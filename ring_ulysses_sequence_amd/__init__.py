@@ -43,7 +43,7 @@ EXPORTED = (
     "ra_ring_merge", "ra_ring_attn_fwd", "ra_seq2head", "ra_head2seq",
     "ra_zigzag_padded_len", "ra_zigzag_schedule", "ra_zigzag_attn_fwd", "ra_ring_attn_bwd",
     "ra_ring_attn_fwd_gqa", "ra_ring_attn_fwd_varlen", "ra_block_attn_bwd",
-    "ra_ring_attn_fwd_split", "ra_ring_split_plan", "ra_zigzag_attn_bwd",
+    "ra_ring_attn_fwd_split", "ra_ring_split_plan", "ra_zigzag_attn_bwd", "ra_ring_attn_bwd_gqa",
 )
 
 _lib = None
@@ -95,6 +95,10 @@ def _load():
                                             c_int, c_int, c_int, c_int, c_int, c_int, c_float,
                                             c_int, ctypes.POINTER(c_ll), c_int, c_vp, c_vp,
                                             c_vp]),
+        "ra_ring_attn_bwd_gqa": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp,
+                                         c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int,
+                                         c_int, c_int, c_float, c_int, c_ll, c_vp,
+                                         ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp, c_vp]),
         "ra_zigzag_attn_bwd": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp,
                                        c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int,
                                        c_int, c_float, c_int, c_ll, c_vp, ctypes.POINTER(c_vp),
@@ -462,7 +466,8 @@ def ring_attn_bwd(q_r, k_blocks: Sequence, v_blocks: Sequence, o_r, do_r, lse_r,
                   dq=None, dk_blocks=None, dv_blocks=None, stream=None):
     """Backward of rank ``rank``'s ring: accumulates into (dq [B,Sb,H,D],
     dk_blocks[j], dv_blocks[j]) (fp32, zero-initialised when not given) the
-    gradients of the rank's queries and of the blocks it visits.  Returns
+    gradients of the rank's queries and of the blocks it visits.  K/V blocks
+    with fewer heads than q_r select the grouped-query form.  Returns
     (dq, dk_blocks, dv_blocks)."""
     return _ring_bwd("ra_ring_attn_bwd", q_r, k_blocks, v_blocks, o_r, do_r, lse_r, rank,
                      causal, valid_len, scale, dq, dk_blocks, dv_blocks, stream)
@@ -488,6 +493,8 @@ def _ring_bwd(fn_name, q_r, k_blocks, v_blocks, o_r, do_r, lse_r, rank, causal, 
     if P > RA_MAX_P:
         raise RuntimeError(f"P={P} exceeds {RA_MAX_P}")
     dt = _dtype_code(q_r)
+    Hkv = k_blocks[0].shape[2] if P else H
+    kv_shape = (B, Sb, Hkv, D)
     for t, n in ((o_r, "o_r"), (do_r, "do_r")):
         if t.shape != q_r.shape or t.dtype != q_r.dtype:
             raise ValueError(f"{n} must match q_r in shape and dtype")
@@ -495,26 +502,31 @@ def _ring_bwd(fn_name, q_r, k_blocks, v_blocks, o_r, do_r, lse_r, rank, causal, 
         raise ValueError("lse_r must be fp32 [B, Sb, H]")
     f32 = dict(dtype=torch.float32, device=q_r.device)
     dq = torch.zeros(q_r.shape, **f32) if dq is None else dq
-    dk_blocks = [torch.zeros(q_r.shape, **f32) for _ in range(P)] if dk_blocks is None else dk_blocks
-    dv_blocks = [torch.zeros(q_r.shape, **f32) for _ in range(P)] if dv_blocks is None else dv_blocks
+    dk_blocks = [torch.zeros(kv_shape, **f32) for _ in range(P)] if dk_blocks is None else dk_blocks
+    dv_blocks = [torch.zeros(kv_shape, **f32) for _ in range(P)] if dv_blocks is None else dv_blocks
     kp = (ctypes.c_void_p * max(P, 1))()
     vp = (ctypes.c_void_p * max(P, 1))()
     dkp = (ctypes.c_void_p * max(P, 1))()
     dvp = (ctypes.c_void_p * max(P, 1))()
     for j in range(P):
         for t, n in ((k_blocks[j], "k"), (v_blocks[j], "v")):
-            if t.shape != q_r.shape or t.dtype != q_r.dtype:
-                raise ValueError(f"{n}_blocks[{j}] must match q_r in shape and dtype")
+            if tuple(t.shape) != kv_shape or t.dtype != q_r.dtype:
+                raise ValueError(f"{n}_blocks[{j}] must be {kv_shape} of q_r's dtype")
         for t, n in ((dk_blocks[j], "dk"), (dv_blocks[j], "dv")):
-            if t.shape != q_r.shape or t.dtype != torch.float32:
-                raise ValueError(f"{n}_blocks[{j}] must be fp32 of q_r's shape")
+            if tuple(t.shape) != kv_shape or t.dtype != torch.float32:
+                raise ValueError(f"{n}_blocks[{j}] must be fp32 {kv_shape}")
         kp[j], vp[j] = _dev(k_blocks[j], "k").value, _dev(v_blocks[j], "v").value
         dkp[j], dvp[j] = _dev(dk_blocks[j], "dk").value, _dev(dv_blocks[j], "dv").value
     if dq.shape != q_r.shape or dq.dtype != torch.float32:
         raise ValueError("dq must be fp32 of q_r's shape")
     stats = torch.empty((2, B, H, Sb), **f32)
+    head = (B, Sb, H, D, P, rank) if Hkv == H else (B, Sb, H, Hkv, D, P, rank)
+    if Hkv != H:
+        if fn_name != "ra_ring_attn_bwd":
+            raise ValueError("grouped-query K/V heads are supported by the ring backward only")
+        fn_name = "ra_ring_attn_bwd_gqa"
     st = getattr(_load(), fn_name)(_dev(q_r, "q_r"), kp, vp, _dev(o_r, "o_r"), _dev(do_r, "do_r"),
-                                   _dev(lse_r, "lse_r"), B, Sb, H, D, P, rank, dt, float(scale),
+                                   _dev(lse_r, "lse_r"), *head, dt, float(scale),
                                    int(causal), valid_len, _dev(dq, "dq"), dkp, dvp,
                                    _dev(stats, "stats"), _stream(stream))
     _check(st, fn_name)

@@ -65,9 +65,9 @@ constexpr int kPF = 2;              // operand reads in flight ahead of use (pai
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdBlock {
-  const void* k;      // [B, kv_rows_b, H, D] bf16, this block's rows from 0
+  const void* k;      // [B, kv_rows_b, Hkv, D] bf16, this block's rows from 0
   const void* v;
-  float* dk;          // [B, kv_rows_b, H, D] fp32, accumulated (+=)
+  float* dk;          // [B, kv_rows_b, Hkv, D] fp32, accumulated (+=)
   float* dv;
   long long k_pos0;   // global position of key row 0
   int len;            // rows in the block
@@ -90,6 +90,8 @@ struct BwdArgs {
   int q_split;
   long long valid_len;
   int B, Sq, H;
+  int Hkv;            // K/V heads (H % Hkv == 0): query head h uses K/V head
+                      // h / (H / Hkv); dK/dV sum over the query heads of a group
   int kv_rows_b;      // rows between consecutive batches in every K/V buffer
   int causal;
   int n_ktiles;       // 128-key tiles per block (dkv grid)
@@ -306,7 +308,8 @@ void ring_attn_bwd_dq(const BwdArgs a) {
   const int wrows = min(32, a.Sq - wrow0);
   const long long wq_lo = qpos(a, wrow0), wq_hi = wq_lo + wrows - 1;
   const long long HD = (long long)a.H * D;
-  const int HD2 = (int)(HD * 2);  // bytes between K/V rows
+  const int hk = h / (a.H / a.Hkv);            // K/V head of this query head
+  const int HD2 = a.Hkv * D * 2;               // bytes between K/V rows
 
   // this lane's query row: Q and dO fragments, D and the base-2 lse
   DqLane<D> w;
@@ -362,7 +365,8 @@ void ring_attn_bwd_dq(const BwdArgs a) {
   };
   auto copy_kv = [&](int bi, int ti, unsigned dst) {
     const BwdBlock& kb = a.blk[bi];
-    const long long off = (((long long)b * a.kv_rows_b + (long long)ti * kTile) * a.H + h) * D * 2;
+    const long long off =
+        (((long long)b * a.kv_rows_b + (long long)ti * kTile) * a.Hkv + hk) * D * 2;
     const int rows = min(kTile, kb.len - ti * kTile);
     copy_tile<D>((const char*)kb.k + off, rows, HD2, voff, dst);
     copy_tile<D>((const char*)kb.v + off, rows, HD2, voff, dst + C::TILE);
@@ -563,13 +567,14 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
   int id = blockIdx.x;
   const int kt = id % a.n_ktiles;
   id /= a.n_ktiles;
-  const int h = id % a.H;
-  id /= a.H;
+  const int hk = id % a.Hkv;  // K/V head; its query heads are hk*G .. hk*G + G-1
+  id /= a.Hkv;
   const int b = id % a.B;
   const int bi = id / a.B;
+  const int G = a.H / a.Hkv;
   const BwdBlock& kb = a.blk[bi];
-  const long long HD = (long long)a.H * D;
-  const int HD2 = (int)(HD * 2);
+  const long long HDkv = (long long)a.Hkv * D;
+  const int HD2 = a.H * D * 2;  // bytes between Q / dO rows
 
   const int kr = kt * kRows + g * 32 + col;
   const bool key_ok = kr < kb.len;
@@ -578,7 +583,7 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
   const long long kw_hi = kw_lo + 31;
   PairLane<D, ROLE> w;
   {
-    const long long off = ((long long)b * a.kv_rows_b + kr) * HD + (long long)h * D;
+    const long long off = ((long long)b * a.kv_rows_b + kr) * HDkv + (long long)hk * D;
     const __bf16* fp = (const __bf16*)(ROLE == 0 ? kb.k : kb.v) + off;
 #pragma unroll
     for (int c = 0; c < C::NC; ++c)
@@ -605,10 +610,13 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
     if (t0 > (a.Sq + kTile - 1) / kTile) t0 = (a.Sq + kTile - 1) / kTile;
   }
   const int n_t = (a.Sq + kTile - 1) / kTile;
-  const long long stat0 = ((long long)b * a.H + h) * a.Sq;
+  // the query tiles t0 .. n_t-1 of each query head of the group in turn
+  const int n_per = n_t - t0, n_it = G * n_per;
   // Q and dO tiles by all eight waves; the statistics rows by waves 0 (lse)
   // and 1 (D)
-  auto copy_q = [&](int ti, unsigned buf_base) {
+  auto copy_q = [&](int it, unsigned buf_base) {
+    const int h = hk * G + it / n_per, ti = t0 + it % n_per;
+    const long long stat0 = ((long long)b * a.H + h) * a.Sq;
     const long long off = (((long long)b * a.Sq + (long long)ti * kTile) * a.H + h) * D * 2;
     const int rows = min(kTile, a.Sq - ti * kTile);
     const unsigned dst = buf_base + wave * PC::DMA * 1024;
@@ -623,13 +631,14 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
           0, 0);
     }
   };
-  if (t0 < n_t) copy_q(t0, base);
+  if (n_it > 0) copy_q(0, base);
   wait_vmcnt<0>();
   pipeline_barrier();
   int buf = 0;
   const float c_scale = a.scale_log2;
-  for (int ti = t0; ti < n_t; ++ti) {
-    if (ti + 1 < n_t) copy_q(ti + 1, base + (buf ^ 1) * PC::BUF);
+  for (int it = 0; it < n_it; ++it) {
+    if (it + 1 < n_it) copy_q(it + 1, base + (buf ^ 1) * PC::BUF);
+    const int ti = t0 + it % n_per;
     const long long qp0 = qpos(a, ti * kTile);
     const long long qp_hi = qp0 + min(kTile, a.Sq - ti * kTile) - 1;
     const bool live = !(a.causal && kw_lo > qp_hi) && kw_lo < a.valid_len;
@@ -649,7 +658,7 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
   }
 
   if (key_ok) {
-    const long long off = ((long long)b * a.kv_rows_b + kr) * HD + (long long)h * D;
+    const long long off = ((long long)b * a.kv_rows_b + kr) * HDkv + (long long)hk * D;
     float* dst = (ROLE == 1 ? kb.dk : kb.dv) + off;
     const float f = ROLE == 1 ? a.scale : 1.0f;
 #pragma unroll
@@ -699,7 +708,7 @@ void set_scale(BwdArgs& a, float scale, int D) {
 ra_status launch_bwd(const char* name, BwdArgs& a, int D, int block_len, hipStream_t s) {
   const long long n_dq = (long long)a.B * a.H * ((a.Sq + kRows - 1) / kRows);
   a.n_ktiles = (block_len + kRows - 1) / kRows;
-  const long long n_dkv = (long long)a.nblk * a.B * a.H * a.n_ktiles;
+  const long long n_dkv = (long long)a.nblk * a.B * a.Hkv * a.n_ktiles;
   if (n_dq > 0x7fffffffLL || n_dkv > 0x7fffffffLL)
     return ra::fail(RA_ERR_UNSUPPORTED, "%s: grid too large", name);
   // dq first: it writes the row statistics that the dk/dv kernels read
@@ -750,6 +759,7 @@ extern "C" ra_status ra_block_attn_bwd(const void* q, const void* k, const void*
   a.B = B;
   a.Sq = Sq;
   a.H = H;
+  a.Hkv = H;
   a.kv_rows_b = Sk;
   a.causal = causal != 0;
   set_scale(a, scale, D);
@@ -761,17 +771,20 @@ extern "C" ra_status ra_block_attn_bwd(const void* q, const void* k, const void*
   return launch_bwd(name, a, D, Sk, (hipStream_t)stream);
 }
 
-extern "C" ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_blocks,
-                                      const void* const* v_blocks, const void* o_r,
-                                      const void* do_r, const float* lse_r, int B, int Sb,
-                                      int H, int D, int P, int rank, ra_dtype dt, float scale,
-                                      int causal, long long valid_len, float* dq_r,
-                                      float* const* dk_blocks, float* const* dv_blocks,
-                                      float* stats_ws, void* stream) {
-  static const char* name = "ra_ring_attn_bwd";
+namespace {
+// The ring backward of one rank (shared by the MHA and GQA entry points).
+ra_status ring_bwd(const char* name, const void* q_r, const void* const* k_blocks,
+                   const void* const* v_blocks, const void* o_r, const void* do_r,
+                   const float* lse_r, int B, int Sb, int H, int Hkv, int D, int P, int rank,
+                   ra_dtype dt, float scale, int causal, long long valid_len, float* dq_r,
+                   float* const* dk_blocks, float* const* dv_blocks, float* stats_ws,
+                   void* stream) {
   ra::clear_error();
   ra_status st = check_common(name, B, Sb, H, D, dt);
   if (st != RA_OK) return st;
+  if (Hkv <= 0 || H % Hkv != 0)
+    return ra::fail(RA_ERR_SHAPE, "%s: %d query heads are not a multiple of %d K/V heads",
+                    name, H, Hkv);
   if (P <= 0) return ra::fail(RA_ERR_SHAPE, "%s: P must be positive (got %d)", name, P);
   if (P > RA_MAX_P) return ra::fail(RA_ERR_RANGE, "%s: P=%d exceeds RA_MAX_P=%d", name, P, RA_MAX_P);
   if (rank < 0 || rank >= P) return ra::fail(RA_ERR_RANGE, "%s: rank %d outside [0, %d)", name, rank, P);
@@ -797,6 +810,7 @@ extern "C" ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_bloc
   a.B = B;
   a.Sq = Sb;
   a.H = H;
+  a.Hkv = Hkv;
   a.kv_rows_b = Sb;
   a.causal = causal != 0;
   set_scale(a, scale, D);
@@ -818,6 +832,32 @@ extern "C" ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_bloc
                                (long long)j * Sb, Sb, 0};
   }
   return launch_bwd(name, a, D, Sb, (hipStream_t)stream);
+}
+}  // namespace
+
+extern "C" ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_blocks,
+                                      const void* const* v_blocks, const void* o_r,
+                                      const void* do_r, const float* lse_r, int B, int Sb,
+                                      int H, int D, int P, int rank, ra_dtype dt, float scale,
+                                      int causal, long long valid_len, float* dq_r,
+                                      float* const* dk_blocks, float* const* dv_blocks,
+                                      float* stats_ws, void* stream) {
+  return ring_bwd("ra_ring_attn_bwd", q_r, k_blocks, v_blocks, o_r, do_r, lse_r, B, Sb, H, H, D,
+                  P, rank, dt, scale, causal, valid_len, dq_r, dk_blocks, dv_blocks, stats_ws,
+                  stream);
+}
+
+extern "C" ra_status ra_ring_attn_bwd_gqa(const void* q_r, const void* const* k_blocks,
+                                          const void* const* v_blocks, const void* o_r,
+                                          const void* do_r, const float* lse_r, int B, int Sb,
+                                          int H, int H_kv, int D, int P, int rank, ra_dtype dt,
+                                          float scale, int causal, long long valid_len,
+                                          float* dq_r, float* const* dk_blocks,
+                                          float* const* dv_blocks, float* stats_ws,
+                                          void* stream) {
+  return ring_bwd("ra_ring_attn_bwd_gqa", q_r, k_blocks, v_blocks, o_r, do_r, lse_r, B, Sb, H,
+                  H_kv, D, P, rank, dt, scale, causal, valid_len, dq_r, dk_blocks, dv_blocks,
+                  stats_ws, stream);
 }
 
 extern "C" ra_status ra_zigzag_attn_bwd(const void* q_r, const void* const* k_shares,
@@ -862,6 +902,7 @@ extern "C" ra_status ra_zigzag_attn_bwd(const void* q_r, const void* const* k_sh
   a.B = B;
   a.Sq = Sr;
   a.H = H;
+  a.Hkv = H;
   a.kv_rows_b = Sr;
   a.causal = causal != 0;
   set_scale(a, scale, D);

@@ -747,6 +747,44 @@ def test_zigzag_backward_all_ranks(D, causal, pad):
         check_grad(dv_all[j].cpu()[:, real], fv[:, pos[real]], f"zigzag dv share {j}")
 
 
+@pytest.mark.parametrize("Hkv,causal,pad", [(1, True, 0), (2, True, 37), (2, False, 0)])
+def test_gqa_backward_all_ranks(Hkv, causal, pad):
+    """Grouped-query ring backward (4 query heads on 1 or 2 K/V heads), B =
+    2, every rank: dq against the full-sequence gradient, and the dK/dV parts
+    of all ranks accumulated into the owners' buffers against the
+    full-sequence gradients of the expanded K/V summed over each group."""
+    B, S, H, D, P = 2, 1024, 4, 128, 4
+    Sb, valid, G = S // P, S - pad, H // Hkv
+    q, do = (W.random_tensor((B, S, H, D), seed=s_, device="cuda") for s_ in (81, 84))
+    k, v = (W.random_tensor((B, S, Hkv, D), seed=s_, device="cuda") for s_ in (82, 83))
+    if pad:
+        for x in (q, k, v, do):
+            x[:, valid:] = 0
+    kb, vb = blocks_of(k, P), blocks_of(v, P)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dk_all = [torch.zeros((B, Sb, Hkv, D), **f32) for _ in range(P)]
+    dv_all = [torch.zeros((B, Sb, Hkv, D), **f32) for _ in range(P)]
+    fq, fk, fv = oracle.attention_grad(q.cpu(), oracle.gqa_expand(k.cpu(), H),
+                                       oracle.gqa_expand(v.cpu(), H), do.cpu(), causal=causal,
+                                       valid_len=valid)
+    fk = fk.reshape(B, S, Hkv, G, D).sum(axis=3)
+    fv = fv.reshape(B, S, Hkv, G, D).sum(axis=3)
+    real = np.arange(valid)
+    dqs = []
+    for r in range(P):
+        say("gqa bwd", Hkv, causal, pad, "rank", r)
+        sl = slice(r * Sb, (r + 1) * Sb)
+        q_r, do_r = q[:, sl].contiguous(), do[:, sl].contiguous()
+        o, lse = ra.ring_attn_fwd(q_r, kb, vb, r, causal=causal, valid_len=valid)
+        dq, _, _ = ra.ring_attn_bwd(q_r, kb, vb, o, do_r, lse, r, causal=causal, valid_len=valid,
+                                    dk_blocks=dk_all, dv_blocks=dv_all)
+        torch.cuda.synchronize()
+        dqs.append(dq.cpu())
+    check_grad(torch.cat(dqs, 1)[:, real], fq[:, real], "gqa dq all ranks")
+    check_grad(torch.cat([x.cpu() for x in dk_all], 1)[:, real], fk[:, real], "gqa dk owners")
+    check_grad(torch.cat([x.cpu() for x in dv_all], 1)[:, real], fv[:, real], "gqa dv owners")
+
+
 def test_ring_backward_long_context_rank3():
     """L = 131072, H = 64, P = 8, rank 3 (the bench share): dq on sampled
     rows and dk / dv on sampled keys of the diagonal and the first block,

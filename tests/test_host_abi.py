@@ -278,6 +278,10 @@ def test_device_entry_points_validate_before_launch(lib):
     st = lib.ra_zigzag_attn_bwd(null, arr, arr, null, null, null, 1, 128, 1, 64, 2, 0, ra.RA_BF16,
                                 0.0, 1, -1, null, arr, arr, null, null)
     assert st == 1
+    # grouped-query backward: K/V heads must divide H
+    st = lib.ra_ring_attn_bwd_gqa(null, arr, arr, null, null, null, 1, 16, 6, 4, 64, 2, 0,
+                                  ra.RA_BF16, 0.0, 0, -1, null, arr, arr, null, null)
+    assert st == 2 and b"K/V heads" in lib.ra_last_error()
     # merge: unsupported D, unknown dtype
     st = lib.ra_ring_merge(null, null, null, null, 1, 4, 1, 12, null, ra.RA_FP32, null)
     assert st == 5
