@@ -350,6 +350,24 @@ ra_status ra_ring_attn_bwd_gqa(const void* q_r, const void* const* k_blocks,
                                float* dq_r, float* const* dk_blocks,
                                float* const* dv_blocks, float* stats_ws, void* stream);
 
+/* Backward over packed samples (the form of ra_ring_attn_fwd_varlen): B =
+ * 1, sample i holds global positions [cu_seqlens[i], cu_seqlens[i+1]) and
+ * its rows attend only within it ([RA] §6).  q_r, o_r, do_r [1,Sb,H,D] bf16,
+ * lse_r [1,Sb,H] (ra_ring_attn_fwd_varlen's lse); k_blocks / v_blocks and
+ * dk_blocks / dv_blocks as in ra_ring_attn_bwd.  Accumulates (+=) dq_r and
+ * the dK/dV parts of the visited blocks; rows outside every sample are not
+ * touched.  One launch pair per sample that meets the rank's rows, over the
+ * parts of the visited blocks inside that sample.  stats_ws: fp32 scratch
+ * of 2*Sb*H floats.  Errors as ra_ring_attn_fwd_varlen and
+ * ra_ring_attn_bwd. */
+ra_status ra_ring_attn_bwd_varlen(const void* q_r, const void* const* k_blocks,
+                                  const void* const* v_blocks, const void* o_r,
+                                  const void* do_r, const float* lse_r, int Sb, int H,
+                                  int D, int P, int rank, ra_dtype dt, float scale,
+                                  int causal, const long long* cu_seqlens, int n_seqs,
+                                  float* dq_r, float* const* dk_blocks,
+                                  float* const* dv_blocks, float* stats_ws, void* stream);
+
 /* Backward of rank `rank`'s zigzag ring ([RA] §3.4 load balancing with
  * the backward of §3.3 closing paragraph, §6.2): as ra_ring_attn_bwd over
  * the shares of ra_zigzag_attn_fwd.  q_r, o_r, do_r [B,Sr,H,D] bf16 (chunk

@@ -44,6 +44,7 @@ EXPORTED = (
     "ra_zigzag_padded_len", "ra_zigzag_schedule", "ra_zigzag_attn_fwd", "ra_ring_attn_bwd",
     "ra_ring_attn_fwd_gqa", "ra_ring_attn_fwd_varlen", "ra_block_attn_bwd",
     "ra_ring_attn_fwd_split", "ra_ring_split_plan", "ra_zigzag_attn_bwd", "ra_ring_attn_bwd_gqa",
+    "ra_ring_attn_bwd_varlen",
 )
 
 _lib = None
@@ -94,6 +95,11 @@ def _load():
         "ra_ring_attn_fwd_varlen": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp),
                                             c_int, c_int, c_int, c_int, c_int, c_int, c_float,
                                             c_int, ctypes.POINTER(c_ll), c_int, c_vp, c_vp,
+                                            c_vp]),
+        "ra_ring_attn_bwd_varlen": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp,
+                                            c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int,
+                                            c_float, c_int, ctypes.POINTER(c_ll), c_int, c_vp,
+                                            ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp,
                                             c_vp]),
         "ra_ring_attn_bwd_gqa": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp,
                                          c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int,
@@ -483,6 +489,53 @@ def zigzag_attn_bwd(q_r, k_shares: Sequence, v_shares: Sequence, o_r, do_r, lse_
                      causal, valid_len, scale, dq, dk_shares, dv_shares, stream)
 
 
+def ring_attn_bwd_varlen(q_r, k_blocks: Sequence, v_blocks: Sequence, o_r, do_r, lse_r,
+                         rank: int, cu_seqlens: Sequence, *, causal: bool = True,
+                         scale: float = 0.0, dq=None, dk_blocks=None, dv_blocks=None,
+                         stream=None):
+    """Backward over packed samples (B = 1; see ring_attn_fwd_varlen):
+    accumulates into (dq, dk_blocks[j], dv_blocks[j]) (fp32, zero-initialised
+    when not given).  Returns (dq, dk_blocks, dv_blocks)."""
+    torch = _torch()
+    B, Sb, H, D = q_r.shape
+    if B != 1:
+        raise ValueError("packed samples need B = 1")
+    P = len(k_blocks)
+    dt = _dtype_code(q_r)
+    f32 = dict(dtype=torch.float32, device=q_r.device)
+    dq = torch.zeros(q_r.shape, **f32) if dq is None else dq
+    dk_blocks = [torch.zeros(q_r.shape, **f32) for _ in range(P)] if dk_blocks is None else dk_blocks
+    dv_blocks = [torch.zeros(q_r.shape, **f32) for _ in range(P)] if dv_blocks is None else dv_blocks
+    for t, n in ((o_r, "o_r"), (do_r, "do_r")):
+        if t.shape != q_r.shape or t.dtype != q_r.dtype:
+            raise ValueError(f"{n} must match q_r in shape and dtype")
+    if lse_r.shape != (1, Sb, H) or lse_r.dtype != torch.float32:
+        raise ValueError("lse_r must be fp32 [1, Sb, H]")
+    if dq.shape != q_r.shape or dq.dtype != torch.float32:
+        raise ValueError("dq must be fp32 of q_r's shape")
+    arrs = [(ctypes.c_void_p * max(P, 1))() for _ in range(4)]
+    for j in range(P):
+        for t, n in ((k_blocks[j], "k"), (v_blocks[j], "v")):
+            if t.shape != q_r.shape or t.dtype != q_r.dtype:
+                raise ValueError(f"{n}_blocks[{j}] must match q_r in shape and dtype")
+        for t, n in ((dk_blocks[j], "dk"), (dv_blocks[j], "dv")):
+            if t.shape != q_r.shape or t.dtype != torch.float32:
+                raise ValueError(f"{n}_blocks[{j}] must be fp32 of q_r's shape")
+        for arr, t, n in zip(arrs, (k_blocks[j], v_blocks[j], dk_blocks[j], dv_blocks[j]),
+                             ("k", "v", "dk", "dv")):
+            arr[j] = _dev(t, n).value
+    cu = list(cu_seqlens)
+    table = (ctypes.c_longlong * max(len(cu), 1))(*cu)
+    stats = torch.empty((2, 1, H, Sb), **f32)
+    st = _load().ra_ring_attn_bwd_varlen(_dev(q_r, "q_r"), arrs[0], arrs[1], _dev(o_r, "o_r"),
+                                         _dev(do_r, "do_r"), _dev(lse_r, "lse_r"), Sb, H, D, P,
+                                         rank, dt, float(scale), int(causal), table,
+                                         len(cu) - 1, _dev(dq, "dq"), arrs[2], arrs[3],
+                                         _dev(stats, "stats"), _stream(stream))
+    _check(st, "ra_ring_attn_bwd_varlen")
+    return dq, dk_blocks, dv_blocks
+
+
 def _ring_bwd(fn_name, q_r, k_blocks, v_blocks, o_r, do_r, lse_r, rank, causal, valid_len,
               scale, dq, dk_blocks, dv_blocks, stream):
     torch = _torch()
@@ -599,7 +652,8 @@ __all__ = [
     "block_attn_fwd", "ring_merge", "ring_attn_fwd", "seq2head", "head2seq",
     "zigzag_padded_len", "zigzag_schedule", "zigzag_attn_fwd", "ring_attn_bwd",
     "ring_attn_fwd_varlen",
-    "ring_attn_composable", "block_attn_bwd", "ring_split_plan", "zigzag_attn_bwd", "EXPORTED", "LIB_PATH", "LibraryMissing",
+    "ring_attn_composable", "block_attn_bwd", "ring_split_plan", "zigzag_attn_bwd", "ring_attn_bwd_varlen",
+    "EXPORTED", "LIB_PATH", "LibraryMissing",
     "RA_BF16", "RA_FP32", "RA_SKIP", "RA_FULL", "RA_DIAG", "RA_MAX_P", "RA_PAD_MULTIPLE",
     "RA_KERNEL_AUTO", "RA_KERNEL_BR128", "RA_KERNEL_BR256", "RA_KERNEL_W64", "RA_KERNEL_WS",
     "RA_KERNEL_PP",

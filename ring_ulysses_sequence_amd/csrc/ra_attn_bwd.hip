@@ -573,6 +573,7 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
   const int bi = id / a.B;
   const int G = a.H / a.Hkv;
   const BwdBlock& kb = a.blk[bi];
+  if (kt * kRows >= kb.len) return;  // a shorter block: no key of it here (uniform)
   const long long HDkv = (long long)a.Hkv * D;
   const int HD2 = a.H * D * 2;  // bytes between Q / dO rows
 
@@ -931,4 +932,93 @@ extern "C" ra_status ra_zigzag_attn_bwd(const void* q_r, const void* const* k_sh
     }
   }
   return launch_bwd(name, a, D, c, (hipStream_t)stream);
+}
+
+extern "C" ra_status ra_ring_attn_bwd_varlen(const void* q_r, const void* const* k_blocks,
+                                             const void* const* v_blocks, const void* o_r,
+                                             const void* do_r, const float* lse_r, int Sb, int H,
+                                             int D, int P, int rank, ra_dtype dt, float scale,
+                                             int causal, const long long* cu_seqlens,
+                                             int n_seqs, float* dq_r, float* const* dk_blocks,
+                                             float* const* dv_blocks, float* stats_ws,
+                                             void* stream) {
+  static const char* name = "ra_ring_attn_bwd_varlen";
+  ra::clear_error();
+  ra_status st = check_common(name, 1, Sb, H, D, dt);
+  if (st != RA_OK) return st;
+  if (P <= 0) return ra::fail(RA_ERR_SHAPE, "%s: P must be positive (got %d)", name, P);
+  if (P > RA_MAX_P) return ra::fail(RA_ERR_RANGE, "%s: P=%d exceeds RA_MAX_P=%d", name, P, RA_MAX_P);
+  if (rank < 0 || rank >= P) return ra::fail(RA_ERR_RANGE, "%s: rank %d outside [0, %d)", name, rank, P);
+  if (n_seqs < 0 || (n_seqs > 0 && !cu_seqlens))
+    return ra::fail(RA_ERR_NULL, "%s: NULL or negative sample table", name);
+  const long long S = (long long)P * Sb;
+  for (int i = 0; i < n_seqs; ++i)
+    if (cu_seqlens[i] > cu_seqlens[i + 1] || cu_seqlens[i] < 0)
+      return ra::fail(RA_ERR_SHAPE, "%s: sample boundaries must increase from 0", name);
+  if (n_seqs > 0 && (cu_seqlens[0] != 0 || cu_seqlens[n_seqs] > S))
+    return ra::fail(RA_ERR_SHAPE, "%s: samples must start at 0 and end within P*Sb = %lld",
+                    name, S);
+  if ((long long)Sb * H == 0) return RA_OK;
+  if (!q_r || !o_r || !do_r || !lse_r || !dq_r || !stats_ws || !k_blocks || !v_blocks ||
+      !dk_blocks || !dv_blocks)
+    return ra::fail(RA_ERR_NULL, "%s: NULL argument", name);
+  if (!aligned16(q_r) || !aligned16(o_r) || !aligned16(do_r) || !aligned16(dq_r))
+    return ra::fail(RA_ERR_SHAPE, "%s: q, o, do and dq must be 16-byte aligned", name);
+  const long long q0 = (long long)rank * Sb, q1 = q0 + Sb;
+  int src[RA_MAX_P], cls[RA_MAX_P];
+  st = ra_ring_schedule(P, rank, Sb, causal, S, src, cls);
+  if (st != RA_OK) return st;
+  const size_t in_row = (size_t)H * D * 2, g_row = (size_t)H * D;
+  // one launch pair per sample that meets the rank's rows: its rows of the
+  // share against the parts of the visited blocks inside that sample, in
+  // ring order (the forward's split, so each sample's gradients use only
+  // its own pairs)
+  for (int i = 0; i < n_seqs; ++i) {
+    const long long s0 = cu_seqlens[i], s1 = cu_seqlens[i + 1];
+    const long long r0 = s0 > q0 ? s0 : q0, r1 = s1 < q1 ? s1 : q1;
+    if (r1 <= r0) continue;
+    BwdArgs a{};
+    a.q = (const char*)q_r + (size_t)(r0 - q0) * in_row;
+    a.o = (const char*)o_r + (size_t)(r0 - q0) * in_row;
+    a.dout = (const char*)do_r + (size_t)(r0 - q0) * in_row;
+    a.lse = lse_r + (r0 - q0) * H;
+    a.dq = dq_r + (r0 - q0) * g_row;
+    a.stats = stats_ws;
+    a.q_pos0 = r0;
+    a.q_pos1 = r1;
+    a.q_split = (int)(r1 - r0);
+    a.valid_len = s1;  // keys past the sample's end are not real for it
+    a.B = 1;
+    a.Sq = (int)(r1 - r0);
+    a.H = H;
+    a.Hkv = H;
+    a.kv_rows_b = Sb;  // B = 1: never used for a stride
+    a.causal = causal != 0;
+    set_scale(a, scale, D);
+    a.nblk = 0;
+    int max_len = 0;
+    for (int t = 0; t < P; ++t) {
+      if (cls[t] == RA_SKIP) continue;
+      const int j = src[t];
+      const long long b0 = (long long)j * Sb, b1 = b0 + Sb;
+      const long long k0 = b0 > s0 ? b0 : s0, k1 = b1 < s1 ? b1 : s1;
+      if (k1 <= k0) continue;
+      if (ra::block_class(r0, r1, k0, k1, causal != 0, s1) == RA_SKIP) continue;
+      if (!k_blocks[j] || !v_blocks[j] || !dk_blocks[j] || !dv_blocks[j])
+        return ra::fail(RA_ERR_NULL, "%s: NULL pointer for visited block %d", name, j);
+      if (!aligned16(k_blocks[j]) || !aligned16(v_blocks[j]) || !aligned16(dk_blocks[j]) ||
+          !aligned16(dv_blocks[j]))
+        return ra::fail(RA_ERR_SHAPE, "%s: block %d not 16-byte aligned", name, j);
+      const size_t off = (size_t)(k0 - b0);
+      a.blk[a.nblk++] = BwdBlock{(const char*)k_blocks[j] + off * in_row,
+                                 (const char*)v_blocks[j] + off * in_row,
+                                 dk_blocks[j] + off * g_row, dv_blocks[j] + off * g_row, k0,
+                                 (int)(k1 - k0), 0};
+      if (k1 - k0 > max_len) max_len = (int)(k1 - k0);
+    }
+    if (a.nblk == 0) continue;
+    st = launch_bwd(name, a, D, max_len, (hipStream_t)stream);
+    if (st != RA_OK) return st;
+  }
+  return RA_OK;
 }

@@ -785,6 +785,47 @@ def test_gqa_backward_all_ranks(Hkv, causal, pad):
     check_grad(torch.cat([x.cpu() for x in dv_all], 1)[:, real], fv[:, real], "gqa dv owners")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_backward_all_ranks(causal):
+    """Backward over packed samples (boundaries across the rank shares and
+    inside blocks, a tail outside every sample), every rank: dq, and the
+    dK/dV parts of all ranks accumulated into the owners' buffers, against
+    the plain gradients of each sample on its own; rows outside every sample
+    stay zero."""
+    S, H, D, P = 2048, 3, 128, 4
+    Sb = S // P
+    cu = [0, 300, 1000, 1148, 1900]
+    q, k, v, do = (W.random_tensor((1, S, H, D), seed=s_, device="cuda") for s_ in (91, 92, 93, 94))
+    kb, vb = blocks_of(k, P), blocks_of(v, P)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dk_all = [torch.zeros((1, Sb, H, D), **f32) for _ in range(P)]
+    dv_all = [torch.zeros((1, Sb, H, D), **f32) for _ in range(P)]
+    fq, fk, fv = (np.zeros((1, S, H, D)) for _ in range(3))
+    qc, kc, vc, dc = q.cpu(), k.cpu(), v.cpu(), do.cpu()
+    for s0, s1 in zip(cu[:-1], cu[1:]):
+        g = oracle.attention_grad(qc[:, s0:s1], kc[:, s0:s1], vc[:, s0:s1], dc[:, s0:s1],
+                                  causal=causal)
+        fq[:, s0:s1], fk[:, s0:s1], fv[:, s0:s1] = g
+    dqs = []
+    for r in range(P):
+        say("varlen bwd", causal, "rank", r)
+        sl = slice(r * Sb, (r + 1) * Sb)
+        q_r, do_r = q[:, sl].contiguous(), do[:, sl].contiguous()
+        o, lse = ra.ring_attn_fwd_varlen(q_r, kb, vb, r, cu, causal=causal)
+        dq, _, _ = ra.ring_attn_bwd_varlen(q_r, kb, vb, o, do_r, lse, r, cu, causal=causal,
+                                           dk_blocks=dk_all, dv_blocks=dv_all)
+        torch.cuda.synchronize()
+        dqs.append(dq.cpu())
+    real = np.arange(cu[-1])
+    check_grad(torch.cat(dqs, 1)[:, real], fq[:, real], "varlen dq all ranks")
+    check_grad(torch.cat([x.cpu() for x in dk_all], 1)[:, real], fk[:, real], "varlen dk owners")
+    check_grad(torch.cat([x.cpu() for x in dv_all], 1)[:, real], fv[:, real], "varlen dv owners")
+    tail = np.arange(cu[-1], S)
+    for x in (torch.cat(dqs, 1), torch.cat([y.cpu() for y in dk_all], 1),
+              torch.cat([y.cpu() for y in dv_all], 1)):
+        assert not x[:, tail].any()
+
+
 def test_ring_backward_long_context_rank3():
     """L = 131072, H = 64, P = 8, rank 3 (the bench share): dq on sampled
     rows and dk / dv on sampled keys of the diagonal and the first block,

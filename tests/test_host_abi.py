@@ -282,6 +282,12 @@ def test_device_entry_points_validate_before_launch(lib):
     st = lib.ra_ring_attn_bwd_gqa(null, arr, arr, null, null, null, 1, 16, 6, 4, 64, 2, 0,
                                   ra.RA_BF16, 0.0, 0, -1, null, arr, arr, null, null)
     assert st == 2 and b"K/V heads" in lib.ra_last_error()
+    # packed-sample backward: bad boundary table
+    import ctypes as ct
+    bad = (ct.c_longlong * 3)(0, 10, 5)
+    st = lib.ra_ring_attn_bwd_varlen(null, arr, arr, null, null, null, 16, 1, 64, 2, 0,
+                                     ra.RA_BF16, 0.0, 1, bad, 2, null, arr, arr, null, null)
+    assert st == 2 and b"increase" in lib.ra_last_error()
     # merge: unsupported D, unknown dtype
     st = lib.ra_ring_merge(null, null, null, null, 1, 4, 1, 12, null, ra.RA_FP32, null)
     assert st == 5
