@@ -611,9 +611,12 @@ def check_grad(got, ref, what):
     scale = max(1.0, float(np.max(np.abs(ref))))
     say(what, {k: f"{v:.3e}" for k, v in c.items()}, f"max|ref| {scale:.3e}")
     assert np.all(np.isfinite(_f64(got)))
-    assert c["cos"] > 0.999, (what, c)
-    assert c["rel_l2"] < 1e-2, (what, c)
     assert c["max_abs_err"] <= 1e-2 * scale, (what, c)
+    # cosine and relative L2 mean nothing for a gradient that is zero up to
+    # rounding (one visible key: dS = P (dP - D) = 0 exactly)
+    if float(np.max(np.abs(ref))) > 1e-6:
+        assert c["cos"] > 0.999, (what, c)
+        assert c["rel_l2"] < 1e-2, (what, c)
 
 
 @pytest.mark.parametrize("D,causal,pad", [(128, True, 0), (128, False, 0), (64, True, 37)])
@@ -824,6 +827,61 @@ def test_varlen_backward_all_ranks(causal):
     for x in (torch.cat(dqs, 1), torch.cat([y.cpu() for y in dk_all], 1),
               torch.cat([y.cpu() for y in dv_all], 1)):
         assert not x[:, tail].any()
+
+
+def test_random_shapes_forward_and_backward():
+    """Seeded random small shares (B, P, rows per rank from 1 to 300, heads
+    and grouped K/V heads, D, causal, padding, rank): the ring forward (the
+    binding's default, split or not) against the oracle's recurrence, and the
+    ring backward against the oracle's ring backward fed the same saved O and
+    lse (grouped K/V: the oracle on expanded blocks, parts summed per
+    group)."""
+    rng = np.random.default_rng(2024)
+    for case in range(24):
+        B = int(rng.integers(1, 3))
+        P = int(rng.choice([1, 2, 3, 5]))
+        Sb = int(rng.integers(1, 301))
+        H = int(rng.choice([1, 2, 3, 4]))
+        Hkv = int(rng.choice([d for d in range(1, H + 1) if H % d == 0]))
+        D = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        r = int(rng.integers(0, P))
+        valid = P * Sb - int(rng.integers(0, Sb))
+        say("random case", case, dict(B=B, P=P, Sb=Sb, H=H, Hkv=Hkv, D=D, causal=causal, r=r,
+                                      valid=valid))
+        S = P * Sb
+        seed = 1000 + 10 * case
+        q = W.random_tensor((B, S, H, D), seed=seed)
+        k = W.random_tensor((B, S, Hkv, D), seed=seed + 1)
+        v = W.random_tensor((B, S, Hkv, D), seed=seed + 2)
+        q_r = q[:, r * Sb:(r + 1) * Sb].contiguous()
+        do_r = W.random_tensor(q_r.shape, seed=seed + 3)
+        kb, vb = blocks_of(k, P), blocks_of(v, P)
+        kg, vg = [x.cuda() for x in kb], [x.cuda() for x in vb]
+        o, lse = ra.ring_attn_fwd(q_r.cuda(), kg, vg, r, causal=causal, valid_len=valid)
+        dq, dk, dv = ra.ring_attn_bwd(q_r.cuda(), kg, vg, o, do_r.cuda(), lse, r, causal=causal,
+                                      valid_len=valid)
+        torch.cuda.synchronize()
+        ke = [oracle.gqa_expand(x, H) for x in kb]
+        ve = [oracle.gqa_expand(x, H) for x in vb]
+        ref_o, ref_lse = oracle.ring_attention_rank(q_r, ke, ve, r, causal=causal, valid_len=valid)
+        rows = np.arange(max(0, min(Sb, valid - r * Sb)))
+        if len(rows):
+            check_bf16(o.cpu()[:, rows], ref_o[:, rows], f"random {case} O")
+            assert oracle.max_abs_err(lse.cpu()[:, rows], ref_lse[:, rows]) <= LSE_BF16_ATOL
+        rq, rk, rv = oracle.ring_attention_bwd_rank(q_r, ke, ve, do_r, r, o_r=o.cpu(),
+                                                    lse_r=lse.cpu(), causal=causal,
+                                                    valid_len=valid)
+        check_grad(dq.cpu(), rq, f"random {case} dq")
+        G = H // Hkv
+        for j in range(P):
+            gk = rk[j].reshape(B, Sb, Hkv, G, D).sum(axis=3)
+            gv = rv[j].reshape(B, Sb, Hkv, G, D).sum(axis=3)
+            if np.any(gk) or np.any(gv):
+                check_grad(dk[j].cpu(), gk, f"random {case} dk {j}")
+                check_grad(dv[j].cpu(), gv, f"random {case} dv {j}")
+            else:
+                assert not dk[j].any() and not dv[j].any()
 
 
 def test_ring_backward_long_context_rank3():
