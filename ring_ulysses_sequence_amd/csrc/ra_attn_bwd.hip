@@ -470,91 +470,140 @@ struct PairLane {
   unsigned xa;         // this lane's slot in the P exchange (parity 0)
 };
 
+// The scores product of half T (query rows 32T .. 32T+31 of the tile):
+// role 0 S^T = K Q^T into sc, then P (rounded to bf16) into pb and into the
+// lane's exchange slot; role 1 dP^T = V dO^T into sc.  st receives the lane's
+// statistics (lse2 for role 0, D for role 1) of those rows.
 template <int D, int ROLE, int T>
-__device__ __forceinline__ void pair_half(PairLane<D, ROLE>& w, bool live, bool need, int rel_h,
-                                          float c_scale) {
+__device__ __forceinline__ void pair_front(PairLane<D, ROLE>& w, bool need, int rel_h,
+                                           float c_scale, f32x16& sc, u32x4 (&st)[4],
+                                           bf16x8 (&pb)[2]) {
   using C = Cfg<D>;
   constexpr int NB = kPF + 1;
   constexpr int RO = T * 32 * C::ROWB;
   constexpr int AO = (ROLE == 0 ? 0 : C::TILE) + RO;                    // Q or dO rows
-  constexpr int TO = (ROLE == 0 ? C::TILE : 0) + RO;                    // dO^T or Q^T
   constexpr int SO = 2 * C::TILE + (ROLE == 0 ? 0 : 4 * kTile) + 128 * T;  // lse2 or D
   constexpr int XO = T * 4 * kXSlot;
-  constexpr int NJ = 2 * C::NDT;
-  f32x16 sc = f32x16{};
-  u32x4 st[4];
-  s16x4 lo[NB], hi[NB];
-  bf16x8 pb[2];
-  if (live) {
-    u32x4 ra[NB];
+  sc = f32x16{};
+  u32x4 ra[NB];
 #pragma unroll
-    for (int c = 0; c < kPF; ++c) ra[c] = lds_read_b128<AO>(w.ad.row[c]);
+  for (int c = 0; c < kPF; ++c) ra[c] = lds_read_b128<AO>(w.ad.row[c]);
 #pragma unroll
-    for (int c = 0; c < C::NC; ++c) {
-      if (c + kPF < C::NC) ra[(c + kPF) % NB] = lds_read_b128<AO>(w.ad.row[c + kPF]);
-      claim_lds_n(min(kPF, C::NC - 1 - c), ra[c % NB]);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(ra[c % NB]), w.f[c], sc, 0, 0, 0);
-    }
-    st[0] = lds_read_b128<SO + 0>(w.sa);
-    st[1] = lds_read_b128<SO + 32>(w.sa);
-    st[2] = lds_read_b128<SO + 64>(w.sa);
-    st[3] = lds_read_b128<SO + 96>(w.sa);
+  for (int c = 0; c < C::NC; ++c) {
+    if (c + kPF < C::NC) ra[(c + kPF) % NB] = lds_read_b128<AO>(w.ad.row[c + kPF]);
+    claim_lds_n(min(kPF, C::NC - 1 - c), ra[c % NB]);
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(ra[c % NB]), w.f[c], sc, 0, 0, 0);
+  }
+  st[0] = lds_read_b128<SO + 0>(w.sa);
+  st[1] = lds_read_b128<SO + 32>(w.sa);
+  st[2] = lds_read_b128<SO + 64>(w.sa);
+  st[3] = lds_read_b128<SO + 96>(w.sa);
+  claim_lds<3>(st[0]);
+  claim_lds<2>(st[1]);
+  claim_lds<1>(st[2]);
+  claim_lds<0>(st[3]);
+  if constexpr (ROLE == 0) {
+    // P of (query m = 32T + 8g + 4half + i, this lane's key), hidden when
+    // m < rel_h + 4half; handed to the partner in the lane's own slot
 #pragma unroll
-    for (int j = 0; j < kPF; ++j) {
-      lo[j] = read_tr_g<D, TO>(j / C::NDT, w.ad.lo[j % C::NDT]);
-      hi[j] = read_tr_g<D, TO>(j / C::NDT, w.ad.hi[j % C::NDT]);
-    }
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 l4 = as_f32(st[g]);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) claim_lds<2 * kPF>(st[g]);
-    if constexpr (ROLE == 0) {
-      // P of (query m = 32T + 8g + 4half + i, this lane's key), hidden when
-      // m < rel_h + 4half; handed to the partner in the lane's own slot
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = as_f32(st[g]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int v = 4 * g + i;
-          float x = sc[v] * c_scale - l4[i];
-          if (need && 32 * T + 8 * g + i < rel_h) x = -INFINITY;
-          pb[v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(x);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int v = 4 * g + i;
+        float x = sc[v] * c_scale - l4[i];
+        if (need && 32 * T + 8 * g + i < rel_h) x = -INFINITY;
+        pb[v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(x);
       }
-      lds_write_b128<XO>(w.xa, __builtin_bit_cast(u32x4, pb[0]));
-      lds_write_b128<XO + 1024>(w.xa, __builtin_bit_cast(u32x4, pb[1]));
+    }
+    lds_write_b128<XO>(w.xa, __builtin_bit_cast(u32x4, pb[0]));
+    lds_write_b128<XO + 1024>(w.xa, __builtin_bit_cast(u32x4, pb[1]));
+  }
+}
+
+// Role 1, half T, once the partner's P is in LDS: dS^T = P^T o (dP^T - D),
+// rounded to bf16, into pb.
+template <int D, int T>
+__device__ __forceinline__ void pair_ds(const PairLane<D, 1>& w, const f32x16& sc,
+                                        const u32x4 (&st)[4], bf16x8 (&pb)[2]) {
+  constexpr int XO = T * 4 * kXSlot;
+  u32x4 x0 = lds_read_b128<XO>(w.xa), x1 = lds_read_b128<XO + 1024>(w.xa);
+  claim_lds<1>(x0);
+  claim_lds<0>(x1);
+  const bf16x8 p0 = as_bf16(x0), p1 = as_bf16(x1);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 d4 = as_f32(st[g]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = 4 * g + i;
+      const float p = (float)(v < 8 ? p0[v] : p1[v - 8]);
+      pb[v >> 3][v & 7] = (__bf16)(p * (sc[v] - d4[i]));
     }
   }
-  pipeline_barrier();  // P of this half is in LDS for role 1
-  if (live) {
-    if constexpr (ROLE == 1) {
-      u32x4 x0 = lds_read_b128<XO>(w.xa), x1 = lds_read_b128<XO + 1024>(w.xa);
-      claim_lds<0>(x0);
-      claim_lds<0>(x1);
-      const bf16x8 p0 = as_bf16(x0), p1 = as_bf16(x1);
+}
+
+// The gradient product of half T: role 0 dV^T += dO^T P^T, role 1
+// dK^T += Q^T dS^T (pb holds P or dS of the lane's key over the half's rows).
+template <int D, int ROLE, int T>
+__device__ __forceinline__ void pair_back(PairLane<D, ROLE>& w, const bf16x8 (&pb)[2]) {
+  using C = Cfg<D>;
+  constexpr int NB = kPF + 1;
+  constexpr int RO = T * 32 * C::ROWB;
+  constexpr int TO = (ROLE == 0 ? C::TILE : 0) + RO;  // dO^T or Q^T
+  constexpr int NJ = 2 * C::NDT;
+  s16x4 lo[NB], hi[NB];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 d4 = as_f32(st[g]);
+  for (int j = 0; j < kPF; ++j) {
+    lo[j] = read_tr_g<D, TO>(j / C::NDT, w.ad.lo[j % C::NDT]);
+    hi[j] = read_tr_g<D, TO>(j / C::NDT, w.ad.hi[j % C::NDT]);
+  }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int v = 4 * g + i;
-          const float p = (float)(v < 8 ? p0[v] : p1[v - 8]);
-          pb[v >> 3][v & 7] = (__bf16)(p * (sc[v] - d4[i]));
-        }
-      }
+  for (int j = 0; j < NJ; ++j) {
+    if (j + kPF < NJ) {
+      const int jn = j + kPF;
+      lo[jn % NB] = read_tr_g<D, TO>(jn / C::NDT, w.ad.lo[jn % C::NDT]);
+      hi[jn % NB] = read_tr_g<D, TO>(jn / C::NDT, w.ad.hi[jn % C::NDT]);
     }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      if (j + kPF < NJ) {
-        const int jn = j + kPF;
-        lo[jn % NB] = read_tr_g<D, TO>(jn / C::NDT, w.ad.lo[jn % C::NDT]);
-        hi[jn % NB] = read_tr_g<D, TO>(jn / C::NDT, w.ad.hi[jn % C::NDT]);
-      }
-      const int n = 2 * min(kPF, NJ - 1 - j);
-      claim_lds_n(n, lo[j % NB]);
-      claim_lds_n(n, hi[j % NB]);
-      const int d = j % C::NDT;
-      w.acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(lo[j % NB], hi[j % NB]),
-                                                         pb[j / C::NDT], w.acc[d], 0, 0, 0);
+    const int n = 2 * min(kPF, NJ - 1 - j);
+    claim_lds_n(n, lo[j % NB]);
+    claim_lds_n(n, hi[j % NB]);
+    const int d = j % C::NDT;
+    w.acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(lo[j % NB], hi[j % NB]),
+                                                       pb[j / C::NDT], w.acc[d], 0, 0, 0);
+  }
+}
+
+// One 64-row query tile.  P of half T is handed over at barrier T; role 0
+// computes the scores and P of half 1 before its dV product of half 0, so
+// that its exponentials overlap role 1's products instead of a barrier wait.
+template <int D, int ROLE>
+__device__ __forceinline__ void pair_tile(PairLane<D, ROLE>& w, bool live, bool need, int rel_h,
+                                          float c_scale) {
+  f32x16 sc;
+  u32x4 st[4];
+  bf16x8 p0[2], p1[2];
+  if constexpr (ROLE == 0) {
+    if (live) pair_front<D, 0, 0>(w, need, rel_h, c_scale, sc, st, p0);
+    pipeline_barrier();
+    if (live) {
+      pair_front<D, 0, 1>(w, need, rel_h, c_scale, sc, st, p1);
+      pair_back<D, 0, 0>(w, p0);
+    }
+    pipeline_barrier();
+    if (live) pair_back<D, 0, 1>(w, p1);
+  } else {
+    if (live) pair_front<D, 1, 0>(w, need, rel_h, c_scale, sc, st, p0);
+    pipeline_barrier();
+    if (live) {
+      pair_ds<D, 0>(w, sc, st, p0);
+      pair_back<D, 1, 0>(w, p0);
+      pair_front<D, 1, 1>(w, need, rel_h, c_scale, sc, st, p1);
+    }
+    pipeline_barrier();
+    if (live) {
+      pair_ds<D, 1>(w, sc, st, p1);
+      pair_back<D, 1, 1>(w, p1);
     }
   }
 }
@@ -648,8 +697,7 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
     if (kpos >= a.valid_len) rel = kTile;
     else if (a.causal) rel = (int)max(0LL, min((long long)kTile, kpos - qp0));
     const int rel_h = rel - 4 * half;
-    pair_half<D, ROLE, 0>(w, live, need, rel_h, c_scale);
-    pair_half<D, ROLE, 1>(w, live, need, rel_h, c_scale);
+    pair_tile<D, ROLE>(w, live, need, rel_h, c_scale);
     wait_vmcnt<0>();
     pipeline_barrier();
     const int delta = buf ? -PC::BUF : PC::BUF;
