@@ -455,7 +455,8 @@ constexpr int kXSlot = 32 * 32 * 2;  // P of one key group for one half tile
 template <int D>
 struct PairCfg {
   static constexpr int BUF = 2 * Cfg<D>::TILE + 2 * kTile * 4;  // Q, dO, lse2, D
-  static constexpr int XB = 2 * BUF;                            // P exchange
+  static constexpr int NBUF = 3;                                // tiles it, it+1, it+2
+  static constexpr int XB = NBUF * BUF;                         // P exchange
   static constexpr int LDS = XB + 2 * 4 * kXSlot;               // two half parities
   static constexpr int DMA = Cfg<D>::TILE / 1024 / 8;
 };
@@ -475,9 +476,9 @@ struct PairLane {
 // lane's exchange slot; role 1 dP^T = V dO^T into sc.  st receives the lane's
 // statistics (lse2 for role 0, D for role 1) of those rows.
 template <int D, int ROLE, int T>
-__device__ __forceinline__ void pair_front(PairLane<D, ROLE>& w, bool need, int rel_h,
-                                           float c_scale, f32x16& sc, u32x4 (&st)[4],
-                                           bf16x8 (&pb)[2]) {
+__device__ __forceinline__ void pair_front(PairLane<D, ROLE>& w, unsigned bo, bool need,
+                                           int rel_h, float c_scale, f32x16& sc,
+                                           u32x4 (&st)[4], bf16x8 (&pb)[2]) {
   using C = Cfg<D>;
   constexpr int NB = kPF + 1;
   constexpr int RO = T * 32 * C::ROWB;
@@ -487,17 +488,18 @@ __device__ __forceinline__ void pair_front(PairLane<D, ROLE>& w, bool need, int 
   sc = f32x16{};
   u32x4 ra[NB];
 #pragma unroll
-  for (int c = 0; c < kPF; ++c) ra[c] = lds_read_b128<AO>(w.ad.row[c]);
+  for (int c = 0; c < kPF; ++c) ra[c] = lds_read_b128<AO>(w.ad.row[c] + bo);
 #pragma unroll
   for (int c = 0; c < C::NC; ++c) {
-    if (c + kPF < C::NC) ra[(c + kPF) % NB] = lds_read_b128<AO>(w.ad.row[c + kPF]);
+    if (c + kPF < C::NC) ra[(c + kPF) % NB] = lds_read_b128<AO>(w.ad.row[c + kPF] + bo);
     claim_lds_n(min(kPF, C::NC - 1 - c), ra[c % NB]);
     sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(ra[c % NB]), w.f[c], sc, 0, 0, 0);
   }
-  st[0] = lds_read_b128<SO + 0>(w.sa);
-  st[1] = lds_read_b128<SO + 32>(w.sa);
-  st[2] = lds_read_b128<SO + 64>(w.sa);
-  st[3] = lds_read_b128<SO + 96>(w.sa);
+  const unsigned sa = w.sa + bo;
+  st[0] = lds_read_b128<SO + 0>(sa);
+  st[1] = lds_read_b128<SO + 32>(sa);
+  st[2] = lds_read_b128<SO + 64>(sa);
+  st[3] = lds_read_b128<SO + 96>(sa);
   claim_lds<3>(st[0]);
   claim_lds<2>(st[1]);
   claim_lds<1>(st[2]);
@@ -546,7 +548,8 @@ __device__ __forceinline__ void pair_ds(const PairLane<D, 1>& w, const f32x16& s
 // The gradient product of half T: role 0 dV^T += dO^T P^T, role 1
 // dK^T += Q^T dS^T (pb holds P or dS of the lane's key over the half's rows).
 template <int D, int ROLE, int T>
-__device__ __forceinline__ void pair_back(PairLane<D, ROLE>& w, const bf16x8 (&pb)[2]) {
+__device__ __forceinline__ void pair_back(PairLane<D, ROLE>& w, unsigned bo,
+                                          const bf16x8 (&pb)[2]) {
   using C = Cfg<D>;
   constexpr int NB = kPF + 1;
   constexpr int RO = T * 32 * C::ROWB;
@@ -555,15 +558,15 @@ __device__ __forceinline__ void pair_back(PairLane<D, ROLE>& w, const bf16x8 (&p
   s16x4 lo[NB], hi[NB];
 #pragma unroll
   for (int j = 0; j < kPF; ++j) {
-    lo[j] = read_tr_g<D, TO>(j / C::NDT, w.ad.lo[j % C::NDT]);
-    hi[j] = read_tr_g<D, TO>(j / C::NDT, w.ad.hi[j % C::NDT]);
+    lo[j] = read_tr_g<D, TO>(j / C::NDT, w.ad.lo[j % C::NDT] + bo);
+    hi[j] = read_tr_g<D, TO>(j / C::NDT, w.ad.hi[j % C::NDT] + bo);
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     if (j + kPF < NJ) {
       const int jn = j + kPF;
-      lo[jn % NB] = read_tr_g<D, TO>(jn / C::NDT, w.ad.lo[jn % C::NDT]);
-      hi[jn % NB] = read_tr_g<D, TO>(jn / C::NDT, w.ad.hi[jn % C::NDT]);
+      lo[jn % NB] = read_tr_g<D, TO>(jn / C::NDT, w.ad.lo[jn % C::NDT] + bo);
+      hi[jn % NB] = read_tr_g<D, TO>(jn / C::NDT, w.ad.hi[jn % C::NDT] + bo);
     }
     const int n = 2 * min(kPF, NJ - 1 - j);
     claim_lds_n(n, lo[j % NB]);
@@ -571,40 +574,6 @@ __device__ __forceinline__ void pair_back(PairLane<D, ROLE>& w, const bf16x8 (&p
     const int d = j % C::NDT;
     w.acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(lo[j % NB], hi[j % NB]),
                                                        pb[j / C::NDT], w.acc[d], 0, 0, 0);
-  }
-}
-
-// One 64-row query tile.  P of half T is handed over at barrier T; role 0
-// computes the scores and P of half 1 before its dV product of half 0, so
-// that its exponentials overlap role 1's products instead of a barrier wait.
-template <int D, int ROLE>
-__device__ __forceinline__ void pair_tile(PairLane<D, ROLE>& w, bool live, bool need, int rel_h,
-                                          float c_scale) {
-  f32x16 sc;
-  u32x4 st[4];
-  bf16x8 p0[2], p1[2];
-  if constexpr (ROLE == 0) {
-    if (live) pair_front<D, 0, 0>(w, need, rel_h, c_scale, sc, st, p0);
-    pipeline_barrier();
-    if (live) {
-      pair_front<D, 0, 1>(w, need, rel_h, c_scale, sc, st, p1);
-      pair_back<D, 0, 0>(w, p0);
-    }
-    pipeline_barrier();
-    if (live) pair_back<D, 0, 1>(w, p1);
-  } else {
-    if (live) pair_front<D, 1, 0>(w, need, rel_h, c_scale, sc, st, p0);
-    pipeline_barrier();
-    if (live) {
-      pair_ds<D, 0>(w, sc, st, p0);
-      pair_back<D, 1, 0>(w, p0);
-      pair_front<D, 1, 1>(w, need, rel_h, c_scale, sc, st, p1);
-    }
-    pipeline_barrier();
-    if (live) {
-      pair_ds<D, 1>(w, sc, st, p1);
-      pair_back<D, 1, 1>(w, p1);
-    }
   }
 }
 
@@ -681,29 +650,79 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
           0, 0);
     }
   };
-  if (n_it > 0) copy_q(0, base);
-  wait_vmcnt<0>();
-  pipeline_barrier();
-  int buf = 0;
+  // Tile it sits in buffer it % 3.  The loop runs in half steps: between
+  // barriers, role 0 forms the scores and P of the next half and then its dV
+  // product of the current one, while role 1 forms dS and its dK product of
+  // the current half and then the dP of the next; P of a half crosses over at
+  // the barrier that ends the step forming it.  Tile it+2 is copied from the
+  // step that begins tile it (its buffer held tile it-1, read to the end by
+  // then), and is waited for before the barrier ending tile it+1's first step.
   const float c_scale = a.scale_log2;
-  for (int it = 0; it < n_it; ++it) {
-    if (it + 1 < n_it) copy_q(it + 1, base + (buf ^ 1) * PC::BUF);
+  auto tile = [&](int it, bool& live, bool& need, int& rel_h) {
     const int ti = t0 + it % n_per;
     const long long qp0 = qpos(a, ti * kTile);
     const long long qp_hi = qp0 + min(kTile, a.Sq - ti * kTile) - 1;
-    const bool live = !(a.causal && kw_lo > qp_hi) && kw_lo < a.valid_len;
-    const bool need = kw_hi >= a.valid_len || (a.causal && kw_hi > qp0);
+    live = !(a.causal && kw_lo > qp_hi) && kw_lo < a.valid_len;
+    need = kw_hi >= a.valid_len || (a.causal && kw_hi > qp0);
     int rel = 0;
     if (kpos >= a.valid_len) rel = kTile;
     else if (a.causal) rel = (int)max(0LL, min((long long)kTile, kpos - qp0));
-    const int rel_h = rel - 4 * half;
-    pair_tile<D, ROLE>(w, live, need, rel_h, c_scale);
-    wait_vmcnt<0>();
-    pipeline_barrier();
-    const int delta = buf ? -PC::BUF : PC::BUF;
-    w.ad.shift(delta);
-    w.sa += delta;
-    buf ^= 1;
+    rel_h = rel - 4 * half;
+  };
+  // vector-memory operations of one tile copy issued by this wave
+  auto wait_copy = [&](bool newer) {
+    if (!newer) wait_vmcnt<0>();
+    else if (wave < 2) wait_vmcnt<2 * PC::DMA + 1>();
+    else wait_vmcnt<2 * PC::DMA>();
+  };
+  if (n_it > 0) copy_q(0, base);
+  if (n_it > 1) copy_q(1, base + PC::BUF);
+  wait_copy(n_it > 1);
+  pipeline_barrier();  // tile 0 is in LDS
+  f32x16 sc;
+  u32x4 st[4];
+  bf16x8 p0[2], p1[2];
+  bool live = false, need = false;
+  int rel_h = 0;
+  if (n_it > 0) tile(0, live, need, rel_h);
+  if (live) pair_front<D, ROLE, 0>(w, 0, need, rel_h, c_scale, sc, st, p0);
+  pipeline_barrier();  // P of tile 0, half 0
+  unsigned bo = 0;     // buffer of tile it
+  for (int it = 0; it < n_it; ++it) {
+    const unsigned bo_n = bo + PC::BUF == PC::NBUF * PC::BUF ? 0 : bo + PC::BUF;
+    if (it + 2 < n_it) copy_q(it + 2, base + (bo_n + PC::BUF == PC::NBUF * PC::BUF ? 0 : bo_n + PC::BUF));
+    // step 1: half 1 of tile it forward, half 0 backward
+    if constexpr (ROLE == 0) {
+      if (live) {
+        pair_front<D, 0, 1>(w, bo, need, rel_h, c_scale, sc, st, p1);
+        pair_back<D, 0, 0>(w, bo, p0);
+      }
+    } else if (live) {
+      pair_ds<D, 0>(w, sc, st, p0);
+      pair_back<D, 1, 0>(w, bo, p0);
+      pair_front<D, 1, 1>(w, bo, need, rel_h, c_scale, sc, st, p1);
+    }
+    if (it + 1 < n_it) wait_copy(it + 2 < n_it);
+    pipeline_barrier();  // P of half 1; tile it+1 is in LDS
+    // step 2: half 0 of tile it+1 forward, half 1 of tile it backward
+    bool live_n = false, need_n = false;
+    int rel_n = 0;
+    if (it + 1 < n_it) tile(it + 1, live_n, need_n, rel_n);
+    if constexpr (ROLE == 0) {
+      if (live_n) pair_front<D, 0, 0>(w, bo_n, need_n, rel_n, c_scale, sc, st, p0);
+      if (live) pair_back<D, 0, 1>(w, bo, p1);
+    } else {
+      if (live) {
+        pair_ds<D, 1>(w, sc, st, p1);
+        pair_back<D, 1, 1>(w, bo, p1);
+      }
+      if (live_n) pair_front<D, 1, 0>(w, bo_n, need_n, rel_n, c_scale, sc, st, p0);
+    }
+    pipeline_barrier();  // P of tile it+1, half 0; tile it read to the end
+    live = live_n;
+    need = need_n;
+    rel_h = rel_n;
+    bo = bo_n;
   }
 
   if (key_ok) {
