@@ -32,9 +32,10 @@
 //     read transposed.  (One wave doing both would not fit in 256 registers;
 //     two separate launches would compute S and P twice.)
 // Tiles of 64 rows are copied HBM -> LDS by the buffer unit (buffer_load ...
-// lds), double-buffered: the copy of tile n+1 is issued when tile n starts
-// and has the whole of tile n's compute to land; one wait and one barrier
-// per tile.  Rows are stored with an XOR swizzle of their 16-byte chunks
+// lds).  The dQ kernel double-buffers: the copy of tile n+1 is issued when
+// tile n starts and has the whole of tile n's compute to land; one wait and
+// one barrier per tile.  The dK/dV kernel keeps three buffers and runs in
+// half-tile steps with one barrier each (see pair_body).  Rows are stored with an XOR swizzle of their 16-byte chunks
 // (chunk c of row r at c ^ (r & 15) for D = 128, c ^ ((r >> 1) & 7) for
 // D = 64) so that both the row reads (ds_read_b128) and the transposed reads
 // are free of bank conflicts; the copy picks for every LDS position the
