@@ -116,8 +116,8 @@ def cpu_baseline(q, k, v, rank, Sb, H, D, n_rows=512):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU's share of the ring on ONE GPU; multi-GPU runs "
-              "are not part of this build (--gpus must be 1)", file=sys.stderr)
+        print("bench.py measures one GPU's share of the ring on ONE GPU; the library has "
+              "no multi-GPU path (--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
     import torch
     import ring_ulysses_sequence_amd as ra
