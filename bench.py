@@ -184,6 +184,7 @@ def main():
         extra.update(zigzag_measurements(torch, ra, W, stream, q, k, v))
         extra.update(backward_measurement(torch, ra, W, stream, q_r, kb, vb, o, lse, flops))
         extra.update(gqa_varlen_measurements(torch, ra, stream, q_r, k, v, kb, vb))
+        extra.update(composable_measurements(torch, ra, stream, q_r, kb, vb, flops))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -455,6 +456,46 @@ def packed_sample_bounds(S: int, n: int, seed: int):
     g = np.random.default_rng(seed)
     cuts = np.sort(g.choice(np.arange(1, S), size=n - 1, replace=False))
     return [0] + [int(x) for x in cuts] + [S]
+
+
+def composable_measurements(torch, ra, stream, q_r, kb, vb, fwd_flops):
+    """The composable form of the same rank-3 share (one block_attn_fwd per
+    visited block in ring order, each folded in by ring_merge; four rounds,
+    three merges, the last one writing bf16), and one ring_merge on the
+    share's fp32 partials alone, in GB/s of its algorithmic bytes: per
+    (b, s, h) row it reads two fp32 O rows and two lse and writes one O row
+    and one lse, 2*D*4 + 8 + D*4 + 4 bytes."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    B, Sb, H, D = q_r.shape
+    rank = 3
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    out = {}
+    ms = timed(lambda: ra.ring_attn_composable(q_r, kb, vb, rank, causal=True, stream=stream), 3)
+    out["composable_long_rank3"] = {"ms": round(ms, 3), "tflops": round(fwd_flops / ms / 1e9, 2),
+                                    "rounds": 4, "merges": 3}
+    o_acc, lse_acc, _, _ = ra.block_attn_fwd(q_r, kb[2], vb[2], q_pos0=rank * Sb, k_pos0=2 * Sb,
+                                             causal=True, want_ml=False, stream=stream)
+    o_blk, lse_blk, _, _ = ra.block_attn_fwd(q_r, kb[1], vb[1], q_pos0=rank * Sb, k_pos0=1 * Sb,
+                                             causal=True, want_ml=False, stream=stream)
+    ms = timed(lambda: ra.ring_merge(o_acc, lse_acc, o_blk, lse_blk, stream=stream), 20)
+    rows = B * Sb * H
+    byts = rows * (2 * D * 4 + 8 + D * 4 + 4)
+    out["ring_merge_long_rank3"] = {"ms": round(ms, 4), "bytes": byts,
+                                    "GBps": round(byts / ms / 1e6, 1),
+                                    "frac_hbm": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3)}
+    del o_acc, lse_acc, o_blk, lse_blk
+    return out
 
 
 def gqa_varlen_measurements(torch, ra, stream, q_r, k, v, kb, vb):
