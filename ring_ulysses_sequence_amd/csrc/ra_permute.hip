@@ -95,10 +95,13 @@ __device__ __forceinline__ unsigned h2s_src_run32(unsigned dst_run, unsigned P, 
 // stores.  Runs are a multiple of 64 units (a piece lies in one run) or
 // divide 64 (a piece covers 64 / units_per_run whole runs), so the index
 // arithmetic is a handful of 32-bit divisions per piece, not per unit.
-// Loads are ordinary (a source just written by its producer is often still
-// in the last-level cache); stores are non-temporal (the destination is not
-// read again by this kernel).
-constexpr int kPieces = 4;
+// Loads and stores are non-temporal: each byte is touched once.  Measured on
+// 128 MiB tensors whose source is not cached (three tensors in turn, more
+// than the 256 MB last-level cache): one piece per wave with non-temporal
+// loads 44 us each way, against 46-52 us with ordinary loads or four pieces
+// per wave.  (A source still in that cache reads faster with ordinary
+// loads: 39 us.)
+constexpr int kPieces = 1;
 template <bool kSeq2Head>
 __global__ __launch_bounds__(kThreads) void permute_pieces(
     const u32x4* __restrict__ src, u32x4* __restrict__ dst, unsigned n_units,
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void permute_pieces(
       const unsigned c = du - run * units_per_run;
       const unsigned sr = kSeq2Head ? s2h_src_run32(run, P, B, S, Sl)
                                     : h2s_src_run32(run, P, B, S, Sl);
-      buf[u] = src[(size_t)sr * units_per_run + c];
+      buf[u] = __builtin_nontemporal_load(&src[(size_t)sr * units_per_run + c]);
     }
   }
 #pragma unroll
