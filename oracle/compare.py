@@ -8,6 +8,12 @@ precision page (§3.1, §3.4) computes goldens in higher precision and uses the
 strict fp32 tier 1e-5.  The relative L2 error is added because with many
 visible keys the outputs are small and max_abs_err alone discriminates
 weakly.
+
+Parity: pinned by hand-computed values, by the post's own torch calls
+(``(a - b).abs().max()``, ``cosine_similarity`` of the flattened tensors) and
+by planted mistakes (mean for max, missing or wrong normaliser) that fail
+those pins; the relative L2 error is normalised by the reference, the second
+argument.
 """
 from __future__ import annotations
 
