@@ -53,14 +53,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the side measurements (Ulysses layout, DiT shard)")
-    ap.add_argument("--attn-kernel", choices=["auto", "br128", "br256", "w64", "ws", "pp"], default="auto",
-                    help="force the bf16 attention kernel (all compute the same result)")
+    ap.add_argument("--attn-kernel", choices=["auto", "rowmax"], default="auto",
+                    help="how the bf16 kernel keeps the row max (both compute the same result)")
     return ap.parse_args()
 
 
-KERNEL_NAMES = {"auto": "ring_attn_bf16<128,4>", "br128": "ring_attn_bf16<128,4>",
-                "br256": "ring_attn_bf16<128,8>", "w64": "ring_attn_bf16_w64<128>",
-                "ws": "ring_attn_bf16_ws<128>", "pp": "ring_attn_bf16_pp<128>"}
+KERNEL_NAMES = {"auto": "ring_attn_bf16<128,false>", "rowmax": "ring_attn_bf16<128,false>"}
 ATTN_SOURCE = os.path.join(ROOT, "ring_ulysses_sequence_amd", "csrc", "ra_attn.hip")
 
 
@@ -92,11 +90,21 @@ def cpu_baseline(q, k, v, rank, Sb, H, D, n_rows=512):
     kq = k[:, :(rank + 1) * Sb].cpu()
     vq = v[:, :(rank + 1) * Sb].cpu()
     qr = q[:, rank * Sb:(rank + 1) * Sb].cpu()
-    threads = None
+    threads, blas = None, None
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max((i.get("num_threads") or 0) for i in libs) or None
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in libs) or None
     except Exception:
+        pass
+    cpu_model = None
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
         pass
     t0 = time.perf_counter()
     oracle.attention(qr, kq, vq, causal=True, q_pos0=rank * Sb, k_pos0=0, rows=rows)
@@ -105,7 +113,8 @@ def cpu_baseline(q, k, v, rank, Sb, H, D, n_rows=512):
     flops = 4.0 * D * pairs
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
-        "kind": "oracle",
+        "kind": "oracle", "cpu_model": cpu_model, "blas": blas,
+        "host_logical_cpus": os.cpu_count(),
         "sample": f"rank {rank} share, {len(rows)} evenly spaced query rows x {H} heads, "
                   f"each over its full causal prefix ({flops:.3e} algorithmic FLOPs, "
                   f"{dt:.1f} s, numpy fp64)",
@@ -127,9 +136,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     ra.lib()
-    ra.set_attn_kernel({"auto": ra.RA_KERNEL_AUTO, "br128": ra.RA_KERNEL_BR128,
-                        "br256": ra.RA_KERNEL_BR256, "w64": ra.RA_KERNEL_W64,
-                        "ws": ra.RA_KERNEL_WS, "pp": ra.RA_KERNEL_PP}[args.attn_kernel])
+    ra.set_attn_kernel({"auto": ra.RA_KERNEL_AUTO, "rowmax": ra.RA_KERNEL_ROWMAX}[args.attn_kernel])
     w = W.LONG_CAUSAL
     rank, Sb, H, D, P = 3, w.block_len, w.H, w.D, w.P
     q, k, v = W.make_qkv(w, device="cuda")

@@ -67,19 +67,27 @@ typedef enum { RA_SKIP = 0, RA_FULL = 1, RA_DIAG = 2 } ra_block_class;
 #define RA_PAD_MULTIPLE 16   /* default per-rank padding granularity */
 
 /* Process-wide options (ra_set_option). */
-typedef enum { RA_OPT_ATTN_KERNEL = 0, RA_OPT_COUNT = 1 } ra_option;
-/* Values of RA_OPT_ATTN_KERNEL: which bf16 attention kernel the device
- * entry points launch.  AUTO picks the fastest one measured for the shape
- * (currently the 128-row kernel everywhere).  All compute the same
- * function to the same tolerance; they differ in how many query rows a
- * wave and a workgroup own and in how the waves of a SIMD share the work.
- * Any value other than these is rejected by ra_set_option. */
+typedef enum { RA_OPT_ATTN_KERNEL = 0, RA_OPT_ATTN_WAVES = 1, RA_OPT_COUNT = 2 } ra_option;
+/* Values of RA_OPT_ATTN_KERNEL: how the bf16 attention kernels keep the
+ * per-row reference max of the online softmax ([RA] §3.2).  Both compute
+ * the same function to the same tolerance (u and l always share the
+ * reference, so u / l does not depend on it).
+ *   RA_KERNEL_AUTO (default): a row's reference is its exact max on its
+ *     first tile with a visible key; later tiles skip the row max, and a
+ *     tile whose weights exceed 2^20 is redone against its own max.
+ *   RA_KERNEL_ROWMAX: the row max of every tile is taken and the reference
+ *     moved when the max exceeds it by more than 8 (base-2 units).
+ * The ROWMAX path also runs whenever m and l are requested.  Any other
+ * value is rejected by ra_set_option. */
 #define RA_KERNEL_AUTO 0
-#define RA_KERNEL_BR128 1  /* 4 waves x 32 query rows per workgroup */
-#define RA_KERNEL_BR256 2  /* 8 waves x 32 query rows per workgroup */
-#define RA_KERNEL_W64 3    /* 4 waves x 64 query rows, one wave per SIMD */
-#define RA_KERNEL_WS 4     /* 4 producer/consumer wave pairs x 64 query rows */
-#define RA_KERNEL_PP 5     /* 8 waves x 32 query rows in two groups half a step apart */
+#define RA_KERNEL_ROWMAX 1
+/* Values of RA_OPT_ATTN_WAVES: waves (of 32 query rows) per workgroup of
+ * the bf16 attention kernels.  0 (default) picks 8 -- 256 query rows that
+ * share one K/V stream, one workgroup per compute unit -- when the share
+ * still gives every compute unit a workgroup, else 4 (128 rows, two
+ * workgroups per compute unit).  4 or 8 force that count; the split ring
+ * always uses 4.  Results are the same to the stated tolerance.  Any
+ * other value is rejected by ra_set_option. */
 
 /* ---------------------------------------------------------------------
  * Host-only helpers (no GPU needed; exported for tests and schedule dumps)

@@ -32,9 +32,8 @@ RA_BF16, RA_FP32 = 0, 1
 RA_SKIP, RA_FULL, RA_DIAG = 0, 1, 2
 RA_MAX_P = 64
 RA_PAD_MULTIPLE = 16
-RA_OPT_ATTN_KERNEL = 0
-RA_KERNEL_AUTO, RA_KERNEL_BR128, RA_KERNEL_BR256, RA_KERNEL_W64, RA_KERNEL_WS, RA_KERNEL_PP = (
-    0, 1, 2, 3, 4, 5)
+RA_OPT_ATTN_KERNEL, RA_OPT_ATTN_WAVES = 0, 1
+RA_KERNEL_AUTO, RA_KERNEL_ROWMAX = 0, 1
 
 # Every symbol include/ringattn.h declares.
 EXPORTED = (
@@ -153,12 +152,23 @@ def abi_version() -> int:
 
 
 def set_attn_kernel(choice: int) -> None:
-    """Force the bf16 attention kernel (RA_KERNEL_AUTO / _BR128 / _BR256 / _W64 / _WS / _PP)."""
+    """How the bf16 kernels keep the row max: RA_KERNEL_AUTO (reference set
+    once per row, tiles over the weight bound redone) or RA_KERNEL_ROWMAX
+    (row max of every tile)."""
     _check(_load().ra_set_option(RA_OPT_ATTN_KERNEL, choice), "set_attn_kernel")
 
 
 def get_attn_kernel() -> int:
     return _load().ra_get_option(RA_OPT_ATTN_KERNEL)
+
+
+def set_attn_waves(waves: int) -> None:
+    """Waves per bf16 attention workgroup: 0 (the library's choice), 4 or 8."""
+    _check(_load().ra_set_option(RA_OPT_ATTN_WAVES, waves), "set_attn_waves")
+
+
+def get_attn_waves() -> int:
+    return _load().ra_get_option(RA_OPT_ATTN_WAVES)
 
 
 def padded_len(S: int, P: int, pad_multiple: int = RA_PAD_MULTIPLE) -> int:
@@ -223,18 +233,53 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
 
 
-def _dev(t, name):
+def _dev(t, name, like=None):
+    """Device pointer of a contiguous GPU tensor; with ``like``, the tensor
+    must also sit on like's device."""
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if like is not None and t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, expected {like.device}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _out(t, name, shape, dtype, like):
+    """Check a caller-supplied output buffer before the library writes into
+    it: the C ABI cannot see buffer sizes, so a wrong shape or dtype would
+    mean writes past its end."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {tuple(shape)} of {dtype}, got "
+                         f"{tuple(t.shape)} of {t.dtype}")
+    return _dev(t, name, like)
 
 
 def _stream(stream):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+class _on:
+    """Make the launch stream current while temporaries and default outputs
+    are allocated (and zero-filled), so the caching allocator ties them to
+    the stream the kernels run on and the fills are ordered before them."""
+
+    def __init__(self, stream):
+        self.stream = stream
+        self.ctx = None
+
+    def __enter__(self):
+        if self.stream is not None:
+            self.ctx = _torch().cuda.stream(self.stream)
+            self.ctx.__enter__()
+        return self
+
+    def __exit__(self, *exc):
+        if self.ctx is not None:
+            self.ctx.__exit__(*exc)
+        return False
 
 
 def block_attn_fwd(q, k, v, *, scale: float = 0.0, q_pos0: int = 0, k_pos0: int = 0,
@@ -250,16 +295,20 @@ def block_attn_fwd(q, k, v, *, scale: float = 0.0, q_pos0: int = 0, k_pos0: int 
         raise TypeError("q, k, v must share a dtype")
     dt = _dtype_code(q)
     if out is None:
-        o = torch.empty((B, Sq, H, D), dtype=torch.float32, device=q.device)
-        lse = torch.empty((B, Sq, H), dtype=torch.float32, device=q.device)
-        m = torch.empty_like(lse) if want_ml else None
-        l = torch.empty_like(lse) if want_ml else None
+        with _on(stream):
+            o = torch.empty((B, Sq, H, D), dtype=torch.float32, device=q.device)
+            lse = torch.empty((B, Sq, H), dtype=torch.float32, device=q.device)
+            m = torch.empty_like(lse) if want_ml else None
+            l = torch.empty_like(lse) if want_ml else None
     else:
         o, lse, m, l = out
+    f32, row = torch.float32, (B, Sq, H)
     st = _load().ra_block_attn_fwd(
-        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Sq, Sk, H, D, dt, float(scale),
-        q_pos0, k_pos0, int(causal), valid_len, _dev(o, "o"), _dev(lse, "lse"),
-        _dev(m, "m") if m is not None else None, _dev(l, "l") if l is not None else None,
+        _dev(q, "q"), _dev(k, "k", q), _dev(v, "v", q), B, Sq, Sk, H, D, dt, float(scale),
+        q_pos0, k_pos0, int(causal), valid_len, _out(o, "o", (B, Sq, H, D), f32, q),
+        _out(lse, "lse", row, f32, q),
+        _out(m, "m", row, f32, q) if m is not None else None,
+        _out(l, "l", row, f32, q) if l is not None else None,
         _stream(stream))
     _check(st, "ra_block_attn_fwd")
     return o, lse, m, l
@@ -281,8 +330,10 @@ def ring_merge(o_acc, lse_acc, o_blk, lse_blk, *, out_final=None, stream=None):
             raise ValueError("out_final shape mismatch")
         fdt = _dtype_code(out_final)
         fptr = _dev(out_final, "out_final")
-    st = _load().ra_ring_merge(_dev(o_acc, "o_acc"), _dev(lse_acc, "lse_acc"),
-                               _dev(o_blk, "o_blk"), _dev(lse_blk, "lse_blk"),
+    if out_final is not None:
+        _dev(out_final, "out_final", o_acc)
+    st = _load().ra_ring_merge(_dev(o_acc, "o_acc"), _dev(lse_acc, "lse_acc", o_acc),
+                               _dev(o_blk, "o_blk", o_acc), _dev(lse_blk, "lse_blk", o_acc),
                                B, Sq, H, D, fptr, fdt, _stream(stream))
     _check(st, "ra_ring_merge")
     return o_acc, lse_acc
@@ -324,25 +375,24 @@ def ring_attn_fwd(q_r, k_blocks: Sequence, v_blocks: Sequence, rank: int, *,
         for t, n in ((k_blocks[j], "k"), (v_blocks[j], "v")):
             if tuple(t.shape) != kv_shape or t.dtype != q_r.dtype:
                 raise ValueError(f"{n}_blocks[{j}] must be {kv_shape} of q_r's dtype")
-        kp[j] = k_blocks[j].data_ptr()
-        vp[j] = v_blocks[j].data_ptr()
-        _dev(k_blocks[j], f"k_blocks[{j}]"), _dev(v_blocks[j], f"v_blocks[{j}]")
-    o = torch.empty_like(q_r) if out is None else out
-    lse = lse_out
-    if lse is None and want_lse:
-        lse = torch.empty((B, Sb, H), dtype=torch.float32, device=q_r.device)
-    args = (float(scale), int(causal), valid_len, _dev(o, "o"),
-            _dev(lse, "lse") if lse is not None else None, _stream(stream))
+        kp[j] = _dev(k_blocks[j], f"k_blocks[{j}]", q_r).value
+        vp[j] = _dev(v_blocks[j], f"v_blocks[{j}]", q_r).value
+    with _on(stream):
+        o = torch.empty_like(q_r) if out is None else out
+        lse = lse_out
+        if lse is None and want_lse:
+            lse = torch.empty((B, Sb, H), dtype=torch.float32, device=q_r.device)
+    args = (float(scale), int(causal), valid_len, _out(o, "out", q_r.shape, q_r.dtype, q_r),
+            _out(lse, "lse_out", (B, Sb, H), torch.float32, q_r) if lse is not None else None,
+            _stream(stream))
     if split is not None and split < 1:
         raise ValueError(f"split must be >= 1 (got {split})")
     runs, ws_floats = 1, 0
     if dt == RA_BF16 and split != 1:
-        # the kernels forced by RA_KERNEL_W64 / RA_KERNEL_WS run unsplit
-        if split is not None or get_attn_kernel() not in (RA_KERNEL_W64, RA_KERNEL_WS):
-            runs, ws_floats = ring_split_plan(B, Sb, H, D, P, rank, causal, valid_len,
-                                              split or 0)
+        runs, ws_floats = ring_split_plan(B, Sb, H, D, P, rank, causal, valid_len, split or 0)
     if runs > 1:
-        ws = torch.empty(ws_floats, dtype=torch.float32, device=q_r.device)
+        with _on(stream):
+            ws = torch.empty(ws_floats, dtype=torch.float32, device=q_r.device)
         st = _load().ra_ring_attn_fwd_split(_dev(q_r, "q_r"), kp, vp, B, Sb, H, Hkv, D, P, rank,
                                             dt, float(scale), int(causal), valid_len, runs,
                                             _dev(ws, "ws"), ws_floats, *args[3:])
@@ -380,19 +430,20 @@ def ring_attn_fwd_varlen(q_r, k_blocks: Sequence, v_blocks: Sequence, rank: int,
         for t, n in ((k_blocks[j], "k"), (v_blocks[j], "v")):
             if t.shape != q_r.shape or t.dtype != q_r.dtype:
                 raise ValueError(f"{n}_blocks[{j}] must match q_r in shape and dtype")
-        kp[j] = k_blocks[j].data_ptr()
-        vp[j] = v_blocks[j].data_ptr()
-        _dev(k_blocks[j], f"k_blocks[{j}]"), _dev(v_blocks[j], f"v_blocks[{j}]")
-    o = torch.zeros_like(q_r) if out is None else out
-    lse = lse_out
-    if lse is None and want_lse:
-        lse = torch.full((B, Sb, H), float("-inf"), dtype=torch.float32, device=q_r.device)
+        kp[j] = _dev(k_blocks[j], f"k_blocks[{j}]", q_r).value
+        vp[j] = _dev(v_blocks[j], f"v_blocks[{j}]", q_r).value
+    with _on(stream):
+        o = torch.zeros_like(q_r) if out is None else out
+        lse = lse_out
+        if lse is None and want_lse:
+            lse = torch.full((B, Sb, H), float("-inf"), dtype=torch.float32, device=q_r.device)
     n = len(cu_seqlens) - 1
     cu = (ctypes.c_longlong * max(n + 1, 1))(*[int(x) for x in cu_seqlens])
-    st = _load().ra_ring_attn_fwd_varlen(_dev(q_r, "q_r"), kp, vp, Sb, H, D, P, rank, dt,
-                                         float(scale), int(causal), cu, max(n, 0), _dev(o, "o"),
-                                         _dev(lse, "lse") if lse is not None else None,
-                                         _stream(stream))
+    st = _load().ra_ring_attn_fwd_varlen(
+        _dev(q_r, "q_r"), kp, vp, Sb, H, D, P, rank, dt, float(scale), int(causal), cu,
+        max(n, 0), _out(o, "out", q_r.shape, q_r.dtype, q_r),
+        _out(lse, "lse_out", (B, Sb, H), torch.float32, q_r) if lse is not None else None,
+        _stream(stream))
     _check(st, "ra_ring_attn_fwd_varlen")
     return o, lse
 
@@ -417,17 +468,18 @@ def zigzag_attn_fwd(q_r, k_shares: Sequence, v_shares: Sequence, rank: int, *,
         for t, n in ((k_shares[j], "k"), (v_shares[j], "v")):
             if t.shape != q_r.shape or t.dtype != q_r.dtype:
                 raise ValueError(f"{n}_shares[{j}] must match q_r in shape and dtype")
-        kp[j] = k_shares[j].data_ptr()
-        vp[j] = v_shares[j].data_ptr()
-        _dev(k_shares[j], f"k_shares[{j}]"), _dev(v_shares[j], f"v_shares[{j}]")
-    o = torch.empty_like(q_r) if out is None else out
-    lse = lse_out
-    if lse is None and want_lse:
-        lse = torch.empty((B, Sr, H), dtype=torch.float32, device=q_r.device)
-    st = _load().ra_zigzag_attn_fwd(_dev(q_r, "q_r"), kp, vp, B, Sr, H, D, P, rank, dt,
-                                    float(scale), int(causal), valid_len, _dev(o, "o"),
-                                    _dev(lse, "lse") if lse is not None else None,
-                                    _stream(stream))
+        kp[j] = _dev(k_shares[j], f"k_shares[{j}]", q_r).value
+        vp[j] = _dev(v_shares[j], f"v_shares[{j}]", q_r).value
+    with _on(stream):
+        o = torch.empty_like(q_r) if out is None else out
+        lse = lse_out
+        if lse is None and want_lse:
+            lse = torch.empty((B, Sr, H), dtype=torch.float32, device=q_r.device)
+    st = _load().ra_zigzag_attn_fwd(
+        _dev(q_r, "q_r"), kp, vp, B, Sr, H, D, P, rank, dt, float(scale), int(causal),
+        valid_len, _out(o, "out", q_r.shape, q_r.dtype, q_r),
+        _out(lse, "lse_out", (B, Sr, H), torch.float32, q_r) if lse is not None else None,
+        _stream(stream))
     _check(st, "ra_zigzag_attn_fwd")
     return o, lse
 
@@ -452,17 +504,18 @@ def block_attn_bwd(q, k, v, o, do, lse, *, scale: float = 0.0, q_pos0: int = 0,
         raise ValueError("lse must be fp32 [B, Sq, H]")
     dt = _dtype_code(q)
     f32 = dict(dtype=torch.float32, device=q.device)
-    dq = torch.zeros(q.shape, **f32) if dq is None else dq
-    dk = torch.zeros(k.shape, **f32) if dk is None else dk
-    dv = torch.zeros(k.shape, **f32) if dv is None else dv
+    with _on(stream):
+        dq = torch.zeros(q.shape, **f32) if dq is None else dq
+        dk = torch.zeros(k.shape, **f32) if dk is None else dk
+        dv = torch.zeros(k.shape, **f32) if dv is None else dv
+        stats = torch.empty((2, B, H, Sq), **f32)
     for t, n, shp in ((dq, "dq", q.shape), (dk, "dk", k.shape), (dv, "dv", k.shape)):
-        if t.shape != shp or t.dtype != torch.float32:
-            raise ValueError(f"{n} must be fp32 of shape {tuple(shp)}")
-    stats = torch.empty((2, B, H, Sq), **f32)
+        _out(t, n, shp, torch.float32, q)
     st = _load().ra_block_attn_bwd(
-        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(do, "do"), _dev(lse, "lse"),
-        B, Sq, Sk, H, D, dt, float(scale), q_pos0, k_pos0, int(causal), valid_len,
-        _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), _dev(stats, "stats"), _stream(stream))
+        _dev(q, "q"), _dev(k, "k", q), _dev(v, "v", q), _dev(o, "o", q), _dev(do, "do", q),
+        _dev(lse, "lse", q), B, Sq, Sk, H, D, dt, float(scale), q_pos0, k_pos0, int(causal),
+        valid_len, _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), _dev(stats, "stats"),
+        _stream(stream))
     _check(st, "ra_block_attn_bwd")
     return dq, dk, dv
 
@@ -503,9 +556,15 @@ def ring_attn_bwd_varlen(q_r, k_blocks: Sequence, v_blocks: Sequence, o_r, do_r,
     P = len(k_blocks)
     dt = _dtype_code(q_r)
     f32 = dict(dtype=torch.float32, device=q_r.device)
-    dq = torch.zeros(q_r.shape, **f32) if dq is None else dq
-    dk_blocks = [torch.zeros(q_r.shape, **f32) for _ in range(P)] if dk_blocks is None else dk_blocks
-    dv_blocks = [torch.zeros(q_r.shape, **f32) for _ in range(P)] if dv_blocks is None else dv_blocks
+    with _on(stream):
+        dq = torch.zeros(q_r.shape, **f32) if dq is None else dq
+        dk_blocks = ([torch.zeros(q_r.shape, **f32) for _ in range(P)] if dk_blocks is None
+                     else dk_blocks)
+        dv_blocks = ([torch.zeros(q_r.shape, **f32) for _ in range(P)] if dv_blocks is None
+                     else dv_blocks)
+        stats = torch.empty((2, 1, H, Sb), **f32)
+    if len(dk_blocks) != P or len(dv_blocks) != P or len(v_blocks) != P:
+        raise ValueError("v_blocks, dk_blocks and dv_blocks must hold one buffer per K block")
     for t, n in ((o_r, "o_r"), (do_r, "do_r")):
         if t.shape != q_r.shape or t.dtype != q_r.dtype:
             raise ValueError(f"{n} must match q_r in shape and dtype")
@@ -523,12 +582,13 @@ def ring_attn_bwd_varlen(q_r, k_blocks: Sequence, v_blocks: Sequence, o_r, do_r,
                 raise ValueError(f"{n}_blocks[{j}] must be fp32 of q_r's shape")
         for arr, t, n in zip(arrs, (k_blocks[j], v_blocks[j], dk_blocks[j], dv_blocks[j]),
                              ("k", "v", "dk", "dv")):
-            arr[j] = _dev(t, n).value
+            arr[j] = _dev(t, f"{n}_blocks[{j}]", q_r).value
+    _dev(dq, "dq", q_r)
     cu = list(cu_seqlens)
     table = (ctypes.c_longlong * max(len(cu), 1))(*cu)
-    stats = torch.empty((2, 1, H, Sb), **f32)
-    st = _load().ra_ring_attn_bwd_varlen(_dev(q_r, "q_r"), arrs[0], arrs[1], _dev(o_r, "o_r"),
-                                         _dev(do_r, "do_r"), _dev(lse_r, "lse_r"), Sb, H, D, P,
+    st = _load().ra_ring_attn_bwd_varlen(_dev(q_r, "q_r"), arrs[0], arrs[1], _dev(o_r, "o_r", q_r),
+                                         _dev(do_r, "do_r", q_r), _dev(lse_r, "lse_r", q_r),
+                                         Sb, H, D, P,
                                          rank, dt, float(scale), int(causal), table,
                                          len(cu) - 1, _dev(dq, "dq"), arrs[2], arrs[3],
                                          _dev(stats, "stats"), _stream(stream))
@@ -554,9 +614,15 @@ def _ring_bwd(fn_name, q_r, k_blocks, v_blocks, o_r, do_r, lse_r, rank, causal, 
     if lse_r.shape != (B, Sb, H) or lse_r.dtype != torch.float32:
         raise ValueError("lse_r must be fp32 [B, Sb, H]")
     f32 = dict(dtype=torch.float32, device=q_r.device)
-    dq = torch.zeros(q_r.shape, **f32) if dq is None else dq
-    dk_blocks = [torch.zeros(kv_shape, **f32) for _ in range(P)] if dk_blocks is None else dk_blocks
-    dv_blocks = [torch.zeros(kv_shape, **f32) for _ in range(P)] if dv_blocks is None else dv_blocks
+    with _on(stream):
+        dq = torch.zeros(q_r.shape, **f32) if dq is None else dq
+        dk_blocks = ([torch.zeros(kv_shape, **f32) for _ in range(P)] if dk_blocks is None
+                     else dk_blocks)
+        dv_blocks = ([torch.zeros(kv_shape, **f32) for _ in range(P)] if dv_blocks is None
+                     else dv_blocks)
+        stats = torch.empty((2, B, H, Sb), **f32)
+    if len(dk_blocks) != P or len(dv_blocks) != P:
+        raise ValueError("dk and dv buffers must hold one buffer per K block")
     kp = (ctypes.c_void_p * max(P, 1))()
     vp = (ctypes.c_void_p * max(P, 1))()
     dkp = (ctypes.c_void_p * max(P, 1))()
@@ -568,18 +634,19 @@ def _ring_bwd(fn_name, q_r, k_blocks, v_blocks, o_r, do_r, lse_r, rank, causal, 
         for t, n in ((dk_blocks[j], "dk"), (dv_blocks[j], "dv")):
             if tuple(t.shape) != kv_shape or t.dtype != torch.float32:
                 raise ValueError(f"{n}_blocks[{j}] must be fp32 {kv_shape}")
-        kp[j], vp[j] = _dev(k_blocks[j], "k").value, _dev(v_blocks[j], "v").value
-        dkp[j], dvp[j] = _dev(dk_blocks[j], "dk").value, _dev(dv_blocks[j], "dv").value
-    if dq.shape != q_r.shape or dq.dtype != torch.float32:
-        raise ValueError("dq must be fp32 of q_r's shape")
-    stats = torch.empty((2, B, H, Sb), **f32)
+        kp[j] = _dev(k_blocks[j], f"k_blocks[{j}]", q_r).value
+        vp[j] = _dev(v_blocks[j], f"v_blocks[{j}]", q_r).value
+        dkp[j] = _dev(dk_blocks[j], f"dk_blocks[{j}]", q_r).value
+        dvp[j] = _dev(dv_blocks[j], f"dv_blocks[{j}]", q_r).value
+    _out(dq, "dq", q_r.shape, torch.float32, q_r)
     head = (B, Sb, H, D, P, rank) if Hkv == H else (B, Sb, H, Hkv, D, P, rank)
     if Hkv != H:
         if fn_name != "ra_ring_attn_bwd":
             raise ValueError("grouped-query K/V heads are supported by the ring backward only")
         fn_name = "ra_ring_attn_bwd_gqa"
-    st = getattr(_load(), fn_name)(_dev(q_r, "q_r"), kp, vp, _dev(o_r, "o_r"), _dev(do_r, "do_r"),
-                                   _dev(lse_r, "lse_r"), *head, dt, float(scale),
+    st = getattr(_load(), fn_name)(_dev(q_r, "q_r"), kp, vp, _dev(o_r, "o_r", q_r),
+                                   _dev(do_r, "do_r", q_r), _dev(lse_r, "lse_r", q_r), *head,
+                                   dt, float(scale),
                                    int(causal), valid_len, _dev(dq, "dq"), dkp, dvp,
                                    _dev(stats, "stats"), _stream(stream))
     _check(st, fn_name)
@@ -588,10 +655,10 @@ def _ring_bwd(fn_name, q_r, k_blocks, v_blocks, o_r, do_r, lse_r, rank, causal, 
 
 def _perm(fn_name, x, out_shape, P, B, S, H, D, out, stream):
     torch = _torch()
-    y = torch.empty(out_shape, dtype=x.dtype, device=x.device) if out is None else out
-    if y.shape != out_shape or y.dtype != x.dtype:
-        raise ValueError(f"out must be {out_shape} of {x.dtype}")
-    st = getattr(_load(), fn_name)(_dev(x, "src"), _dev(y, "dst"), P, B, S, H, D,
+    with _on(stream):
+        y = torch.empty(out_shape, dtype=x.dtype, device=x.device) if out is None else out
+    st = getattr(_load(), fn_name)(_dev(x, "src"), _out(y, "out", out_shape, x.dtype, x),
+                                   P, B, S, H, D,
                                    x.element_size(), _stream(stream))
     _check(st, fn_name)
     return y
@@ -625,7 +692,8 @@ def ring_attn_composable(q_r, k_blocks, v_blocks, rank: int, *, causal: bool = F
     P = len(k_blocks)
     srcs, classes = ring_schedule(P, rank, Sb, causal, valid_len)
     visit = [j for j, c in zip(srcs, classes) if c != RA_SKIP]
-    final = torch.empty_like(q_r)
+    with _on(stream):
+        final = torch.empty_like(q_r)
     kw = dict(scale=scale, q_pos0=rank * Sb, causal=causal, valid_len=valid_len,
               stream=stream)
     empty = q_r[:, :0]
@@ -634,7 +702,8 @@ def ring_attn_composable(q_r, k_blocks, v_blocks, rank: int, *, causal: bool = F
         block_attn_fwd(q_r, k_blocks[first], v_blocks[first], k_pos0=first * Sb,
                        want_ml=False, **kw) if first is not None
         else block_attn_fwd(q_r, empty, empty, want_ml=False, **kw))
-    blk = (torch.empty_like(o_acc), torch.empty_like(lse_acc), None, None)
+    with _on(stream):
+        blk = (torch.empty_like(o_acc), torch.empty_like(lse_acc), None, None)
     rest = visit[1:]
     if not rest:
         block_attn_fwd(q_r, empty, empty, out=blk, **kw)
@@ -648,13 +717,13 @@ def ring_attn_composable(q_r, k_blocks, v_blocks, rank: int, *, causal: bool = F
 
 
 __all__ = [
-    "lib", "abi_version", "set_attn_kernel", "get_attn_kernel", "padded_len", "shard_range", "classify_block", "ring_schedule",
+    "lib", "abi_version", "set_attn_kernel", "get_attn_kernel", "set_attn_waves",
+    "get_attn_waves", "padded_len", "shard_range", "classify_block", "ring_schedule",
     "block_attn_fwd", "ring_merge", "ring_attn_fwd", "seq2head", "head2seq",
     "zigzag_padded_len", "zigzag_schedule", "zigzag_attn_fwd", "ring_attn_bwd",
     "ring_attn_fwd_varlen",
     "ring_attn_composable", "block_attn_bwd", "ring_split_plan", "zigzag_attn_bwd", "ring_attn_bwd_varlen",
     "EXPORTED", "LIB_PATH", "LibraryMissing",
     "RA_BF16", "RA_FP32", "RA_SKIP", "RA_FULL", "RA_DIAG", "RA_MAX_P", "RA_PAD_MULTIPLE",
-    "RA_KERNEL_AUTO", "RA_KERNEL_BR128", "RA_KERNEL_BR256", "RA_KERNEL_W64", "RA_KERNEL_WS",
-    "RA_KERNEL_PP",
+    "RA_KERNEL_AUTO", "RA_KERNEL_ROWMAX", "RA_OPT_ATTN_WAVES",
 ]

@@ -7,8 +7,8 @@
 // score tile S^T = K Q^T on the matrix cores, so that every lane holds the
 // scores of one query column: the row max and row sum are in-lane reductions
 // plus one cross-half exchange (v_permlane32_swap), not 32-lane butterflies.
-// The probabilities P^T then feed O^T += V^T P^T directly as the B operand,
-// which needs V^T in LDS; V is transposed while it is staged.
+// The probabilities P^T then feed O^T += V^T P^T directly as the B operand;
+// the V^T operand is read from row-major V in LDS by transposing reads.
 //
 // Matrix-core operand layouts used below (64-lane wave, l = lane,
 // col = l % 32, half = l / 32):
@@ -20,10 +20,11 @@
 // A contraction index may be permuted freely as long as A and B agree; both
 // operands below are built with the same (half, element) -> index map.
 //
-// K/V tiles are double-buffered in LDS: while a tile is consumed from one
-// buffer, the next tile -- possibly the first tile of the next ring round --
-// is fetched from HBM into registers and written to the other buffer, so
-// the stream continues across round boundaries without a drain.
+// K/V tiles are multi-buffered in LDS and copied by the buffer unit straight
+// from HBM into LDS (no staging registers): while a tile is consumed, the
+// tiles two steps ahead -- possibly the first tiles of the next ring round
+// -- are in flight, so the stream continues across round boundaries without
+// a drain.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -78,6 +79,7 @@ struct AttnArgs {
   // to slot ((b*H + h)*n_qtiles + qt)*nsplit + j of o / lse ([slot][128
   // rows][D] and [slot][128 rows]).
   int nsplit;
+  int rowmax;          // take the row max of every tile (RA_KERNEL_ROWMAX)
   int nblk;
   KVBlock blk[RA_MAX_P];
 };
@@ -204,33 +206,57 @@ __device__ __forceinline__ float online_update(float (&s)[NS], RowState& st, flo
 // lanes j/4, j/4+4, j/4+8, j/4+12; supplier r = 4e + q points at
 // V[key_e][d0 + 4q .. d0 + 4q + 3], so lane j gets V[key_0..3][d0 + j].
 //
-// Software pipeline (per wave, iteration n over the visited tiles):
-//   LDS holds K(n+1), V(n) and V(n+1) (copied during iterations n-2, n-1);
-//   copy K(n+2) and V(n+2) into the buffers freed by iteration n-1;
-//   mask / row max / rescale of tile n's scores (already in registers);
-//   S^T(n+1) = K(n+1) Q^T on the matrix cores, interleaved instruction by
-//   instruction with the exponentials of tile n on the vector ALUs;
-//   O^T += V(n)^T P(n)^T;
-//   wait for this wave's K copy (the V copy may stay in flight), barrier.
-// Two K buffers and three V buffers (80 KiB at D = 128, so two workgroups
-// still share a CU).  Operand reads run four matrix ops ahead of their use.
-// The loop is unrolled by two so the K parity and the score registers are
-// constants; the V buffer index cycles mod 3 at run time.
-template <int D, int NW>
+// Software pipeline (per wave, step n over the visited tiles):
+//   LDS holds K(n+1), V(n) and V(n+1) (copied during steps n-2, n-1);
+//   copy K(n+2) and V(n+2) into the buffers step n-1 released;
+//   front: S^T(n+1) = K(n+1) Q^T on the matrix cores, interleaved with the
+//          exponentials of the second half (keys 32..63) of tile n;
+//   back:  O^T += V(n)^T P(n)^T on the matrix cores, interleaved with the
+//          mask and the exponentials of the first half of tile n+1;
+//   wait for this wave's K(n+2) copy (V(n+2) may stay in flight), barrier.
+// Every matrix phase thus carries half a tile of softmax work, so a wave on
+// its own keeps the matrix pipe fed, and the second wave of the SIMD (from
+// another workgroup) fills what is left.  Two K and three V buffers (80 KiB
+// at D = 128: two workgroups per CU).  Operand reads run four matrix ops
+// ahead of their use.  The loop is unrolled by two so the K parity, the
+// score registers and the P registers are compile-time constants; the V
+// buffer index cycles mod 3 at run time.
+//
+// Reference max ([RA] §3.2 with a moving reference).  P is formed as
+// 2^(s - m_ref) against a per-row reference m_ref that u and l share, so
+// u / l is the quotient of the recurrence whatever the reference is.  The
+// reference is set to a row's exact max on its first tile with a visible
+// key; after that the row max is not recomputed per tile.  Instead the sum
+// of each tile's weights (computed anyway for l) is checked: while every
+// weight stays below 2^20 nothing can overflow, and a tile whose sum
+// exceeds that bound (a score more than ~20 above the reference, or an
+// infinite weight) is redone after moving the reference to that tile's
+// max and rescaling u and l.  RA_KERNEL_ROWMAX takes the row max of every
+// tile instead and moves the reference lazily (when the max exceeds it by
+// more than 8); the same path runs whenever m and l are requested.
+template <int D, int NW_>
 struct Bf16Cfg {
-  static constexpr int THREADS = 64 * NW;         // NW waves per workgroup
+  static constexpr int NW = NW_;                  // waves per workgroup (4 or 8)
+  static constexpr int THREADS = 64 * NW;
   static constexpr int BR = 32 * NW;              // query rows per workgroup
   static constexpr int BC = 64;                   // keys per tile
   static constexpr int ROWB = D * 2;              // bytes per key row in LDS
   static constexpr int TILE = BC * ROWB;          // one K or V tile
-  static constexpr int KB = 0;                    // 2 K buffers at KB + p*TILE
-  static constexpr int VB = 2 * TILE;             // 3 V buffers at VB + p*TILE
-  static constexpr int LDS = 5 * TILE;
+  // copies of tile n + LEAD are issued in step n: two K and three V buffers
+  // for 4 waves (80 KiB at D = 128, two workgroups per CU), three and four
+  // for 8 waves (112 KiB, one workgroup per CU)
+  static constexpr int LEAD = NW == 8 ? 3 : 2;
+  static constexpr int KBUF = LEAD;
+  static constexpr int VBUF = LEAD + 1;
+  static constexpr int KB = 0;                    // K buffers at KB + p*TILE
+  static constexpr int VB = KBUF * TILE;          // V buffers at VB + p*TILE
+  static constexpr int LDS = (KBUF + VBUF) * TILE;
   static constexpr int CHUNKS = D / 8;            // 16-byte chunks per row
-  static constexpr int DMA = TILE / 1024 / NW;     // 1 KiB copies per wave per tile
+  static constexpr int DMA = TILE / 1024 / NW;    // 1 KiB copies per wave per tile
   static constexpr int NC = D / 16;               // k-steps of S^T = K Q^T
   static constexpr int NDT = D / 32;              // 32-row d tiles of O^T
-  static constexpr int NS = BC / 2;               // scores per lane per tile
+  static constexpr int NQK = 2 * NC;              // matrix ops of S^T per tile
+  static constexpr int NPV = 4 * NDT;             // matrix ops of O^T per tile
 };
 
 template <int D>
@@ -244,6 +270,9 @@ __device__ __forceinline__ int swz_v(int r, int c) {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.
 template <int B, int E, typename F>
@@ -253,12 +282,11 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for<B + 1, E>(f);
   }
 }
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access
-constexpr float kRescaleSlack = 8.0f;   // lazy rescale threshold (base-2 units)
+constexpr float kRescaleSlack = 8.0f;   // lazy move of the reference (base-2 units)
+constexpr float kTileSumLimit = 1048576.0f;  // 2^20: bound on one half tile's weights
+constexpr int kOperandLead = 4;  // LDS operand reads run this many matrix ops ahead
 
 // Wait until at most N vector-memory operations of this wave are in flight
 // (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
@@ -269,23 +297,27 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// ds_read_b64_tr_b16 as inline assembly.  The compiler's own form of this
-// read makes it wait for every LDS-DMA copy in flight (it cannot tell which
-// LDS bytes they write), which would stall each P V phase on the copies
-// issued at the start of the same iteration.  Here the read is invisible to
-// the compiler's wait insertion, so its result must be claimed with
-// claim_lds<N> before use; the copies it must not overtake are ordered by
-// the explicit waits and barriers of the pipeline.
-__device__ __forceinline__ s16x4 lds_read_tr16(unsigned addr_lds) {
-  s16x4 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr_lds));
-  return r;
+// LDS operand reads as inline assembly.  The compiler's own LDS reads wait
+// for every LDS-DMA copy in flight (it cannot tell which LDS bytes a copy
+// writes), which would stall each matrix phase on the copies issued at the
+// start of the same step.  These reads are invisible to the compiler's wait
+// insertion, so each result is claimed with claim_lds<N> before use; the
+// copies they must not overtake are ordered by the explicit waits and
+// barriers of the pipeline.
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_read_b128(unsigned addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  bf16x8 x;
+  __builtin_memcpy(&x, &r, 16);
+  return x;
 }
 template <int OFF>
-__device__ __forceinline__ s16x4 lds_read_tr16(unsigned addr_lds) {
+__device__ __forceinline__ s16x4 lds_read_tr16(unsigned addr) {
   static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
   s16x4 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr_lds), "n"(OFF));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
   return r;
 }
 // Wait until at most N LDS (or scalar-memory) operations of this wave are
@@ -306,406 +338,540 @@ __device__ __forceinline__ void pipeline_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Position in the visited-tile sequence: tile t (of n) of visited block blk.
-struct Cursor {
-  int blk, t, n;
+// ---- the visited-tile sequence -------------------------------------------
+// A workgroup visits the tiles of every visited block in ring order, each
+// block up to the last tile with a key visible to the workgroup's last
+// query ([RA] §3.4 applied per tile; tiles wholly in the future or wholly
+// padding are never read).  All waves of a workgroup walk the same sequence
+// (they share the copies); positions are taken relative to each wave's
+// first query so that the per-tile tests are 32-bit scalar arithmetic.
+struct SeqCtx {
+  long long q_hi;    // the workgroup's last query position
+  long long wq_lo;   // this wave's first query position
+  long long boff;    // byte offset of (batch b, K/V head) row 0 in a block
+  int end_blk, end_t;  // the sequence ends before tile end_t of block end_blk
 };
 
-// A workgroup's visited-tile sequence: the tiles of every visited block in
-// ring order, each block up to the last tile with a key visible to the
-// workgroup's last query q_hi.  The span ends before tile (end_blk, end_t):
-// (a.nblk, 0) for the whole sequence.  A cursor past the span reads
-// blk = a.nblk.
-struct Span {
-  long long q_hi;
-  int end_blk, end_t;
+// Cursor over the sequence; blk == a.nblk once past its end.  Everything
+// here is wave-uniform; the block fields are loaded once per block.
+struct Seq {
+  int blk, t, n;     // block, tile in it, visited tiles of it
+  int len;           // rows of the block
+  int rel0;          // block's first key position - wave's first query position
+  int lim0;          // real keys of the block, min(len, valid_len - first key)
+  const char* kp;    // K row 0 of (b, K/V head) in the block
+  const char* vp;    // V row 0
 };
 
-// Position of tile number i of the sequence (blk = a.nblk past its end).
-__device__ __forceinline__ Cursor seq_pos(const AttnArgs& a, long long q_hi, int i) {
-  Cursor c{0, 0, 0};
-  for (; c.blk < a.nblk; ++c.blk) {
-    c.n = tiles_of<64>(a, c.blk, q_hi);
-    if (i < c.n) break;
-    i -= c.n;
-  }
-  c.t = i;
-  return c;
-}
-__device__ __forceinline__ Cursor span_end(const AttnArgs& a, const Span& sp, Cursor c) {
-  if (c.blk > sp.end_blk || (c.blk == sp.end_blk && c.t >= sp.end_t)) c.blk = a.nblk;
-  return c;
-}
-__device__ __forceinline__ Cursor cursor_first(const AttnArgs& a, const Span& sp, int lo) {
-  return span_end(a, sp, seq_pos(a, sp.q_hi, lo));
-}
-__device__ __forceinline__ Cursor cursor_next(const AttnArgs& a, const Span& sp, Cursor c) {
-  if (c.blk >= a.nblk) return c;
-  if (++c.t >= c.n) {
-    c.t = 0;
-    ++c.blk;
-    while (c.blk < a.nblk && (c.n = tiles_of<64>(a, c.blk, sp.q_hi)) == 0) ++c.blk;
-  }
-  return span_end(a, sp, c);
+// Per-tile facts a step needs about a tile (carried along the pipeline).
+struct TDesc {
+  int valid;         // the tile exists
+  int rel;           // first key position - wave's first query position
+  int lim;           // real keys in the tile (1..64)
+};
+
+__device__ __forceinline__ long long clampll(long long x, long long lo, long long hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
 }
 
-// Everything a wave keeps in registers across tiles.
+// Move s to the first block at or after s.blk with visited tiles (t = 0).
+__device__ __forceinline__ void seq_enter(const AttnArgs& a, const SeqCtx& x, Seq& s) {
+  s.t = 0;
+  for (; s.blk < a.nblk; ++s.blk) {
+    s.n = tiles_of<64>(a, s.blk, x.q_hi);
+    if (s.n > 0) break;
+  }
+  if (s.blk >= a.nblk) return;
+  const KVBlock& kb = a.blk[s.blk];
+  s.len = kb.len;
+  s.kp = (const char*)kb.k + x.boff;
+  s.vp = (const char*)kb.v + x.boff;
+  // clamps keep rel0 + 64 t and lim0 - 64 t inside 32 bits (len <= 2^30)
+  s.rel0 = (int)clampll(kb.k_pos0 - x.wq_lo, -(1LL << 30), 1LL << 29);
+  const long long lim = a.valid_len - kb.k_pos0;
+  s.lim0 = (int)clampll(lim < kb.len ? lim : kb.len, 0, 1LL << 30);
+}
+__device__ __forceinline__ void seq_clip(const AttnArgs& a, const SeqCtx& x, Seq& s) {
+  if (s.blk > x.end_blk || (s.blk == x.end_blk && s.t >= x.end_t)) s.blk = a.nblk;
+}
+__device__ __forceinline__ void seq_next(const AttnArgs& a, const SeqCtx& x, Seq& s) {
+  if (s.blk >= a.nblk) return;
+  if (++s.t >= s.n) {
+    ++s.blk;
+    seq_enter(a, x, s);
+  }
+  seq_clip(a, x, s);
+}
+// Block and tile of tile number i of the sequence (blk = a.nblk past it).
+__device__ __forceinline__ void seq_locate(const AttnArgs& a, long long q_hi, int i, int& blk,
+                                           int& t) {
+  for (blk = 0; blk < a.nblk; ++blk) {
+    const int n = tiles_of<64>(a, blk, q_hi);
+    if (i < n) break;
+    i -= n;
+  }
+  t = i;
+}
+__device__ __forceinline__ Seq seq_first(const AttnArgs& a, const SeqCtx& x, int lo) {
+  Seq s{};
+  seq_locate(a, x.q_hi, lo, s.blk, s.t);
+  const int t = s.t;
+  if (s.blk < a.nblk) {
+    seq_enter(a, x, s);  // the located block has visited tiles
+    s.t = t;
+  }
+  seq_clip(a, x, s);
+  return s;
+}
+__device__ __forceinline__ TDesc seq_desc(const AttnArgs& a, const Seq& s) {
+  TDesc d;
+  d.valid = s.blk < a.nblk;
+  d.rel = s.rel0 + 64 * s.t;
+  const int l = s.lim0 - 64 * s.t;
+  d.lim = l < 0 ? 0 : (l > 64 ? 64 : l);
+  return d;
+}
+
+// ---- per-wave state ---------------------------------------------------------
 template <int D, int NW>
 struct WaveState {
   using C = Bf16Cfg<D, NW>;
   bf16x8 qf[C::NC];        // Q fragment (B operand of S^T)
   f32x16 oacc[C::NDT];     // O^T accumulators (unnormalised u)
-  float m_ref;             // reference max (base 2), -inf before any key
-  float m_true;            // exact running max (base 2)
-  float l_run;             // this lane's half of sum of bf16(2^(s - m_ref))
-  int kaddr[C::NC];        // LDS byte offsets of the K operand reads
-  int vaddr[C::NDT];       // LDS byte offsets of the V operand reads
+  float m_ref;             // reference (base 2), -inf before any visible key
+  float m_use;             // reference the exponentials subtract (0 while -inf)
+  float m_true;            // exact running max (base 2; row-max path only)
+  float l_run;             // this lane's half of the sum of bf16(2^(s - m_ref))
+  unsigned kaddr[C::NC];   // LDS byte address of the K operand reads (buffer 0)
+  unsigned vaddr[C::NDT];  // LDS byte offset of the V operand reads in a buffer
   int voffk[C::DMA];       // copy source offsets (K) within a tile
   int voffv[C::DMA];       // copy source offsets (V) within a tile
 };
 
-// Copy one K or V tile (rows kt0 .. kt0+63 of batch b, head h of `src`, a
-// visited block of `len` rows whose batches lie rows_b rows apart) into LDS
-// at `dst`; each wave copies C::DMA KiB.
+// Copy the K and V tile under cursor s into LDS at byte offsets kdst and
+// vdst of smem; this wave copies C::DMA KiB of each.
 template <int D, int NW>
-__device__ __forceinline__ void copy_tile(const void* src, int len, int rows_b, int ti, int b,
-                                          int h, int H, int HD2, int wave, const int* voff,
-                                          char* dst) {
+__device__ __forceinline__ void copy_tile(const Seq& s, int HD2, int wave, const int* voffk,
+                                          const int* voffv, char* smem, int kdst, int vdst) {
   using C = Bf16Cfg<D, NW>;
-  const int kt0 = ti * C::BC;
-  const int rows = min(C::BC, len - kt0);
-  const long long off = (((long long)b * rows_b + kt0) * H + h) * (D * 2);
+  const int kt0 = s.t * C::BC;
+  const int rows = min(C::BC, s.len - kt0);
   const int nrec = (rows - 1) * HD2 + D * 2;
-  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)src + off), 0, nrec, kRsrcWord3);
+  const long long off = (long long)kt0 * HD2;
+  __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(s.kp + off), 0, nrec, kRsrcWord3);
+  __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(s.vp + off), 0, nrec, kRsrcWord3);
 #pragma unroll
   for (int i = 0; i < C::DMA; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (lds_void_ptr)(dst + (wave * C::DMA + i) * 1024), 16, voff[i], 0, 0, 0);
+        rk, (lds_void_ptr)(smem + kdst + (wave * C::DMA + i) * 1024), 16, voffk[i], 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < C::DMA; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rv, (lds_void_ptr)(smem + vdst + (wave * C::DMA + i) * 1024), 16, voffv[i], 0, 0, 0);
 }
 
-// S^T of one 64-key tile: the K tile at LDS byte offset kb times Q^T.
-template <int D, int NW>
-__device__ __forceinline__ void scores_tile(char* smem, int kb, const WaveState<D, NW>& w,
-                                            f32x16 (&acc)[2]) {
-  using C = Bf16Cfg<D, NW>;
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    acc[kt] = f32x16{};
-#pragma unroll
-    for (int c = 0; c < C::NC; ++c) {
-      const bf16x8 kf = *(const bf16x8*)(smem + kb + kt * 32 * C::ROWB + w.kaddr[c]);
-      acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, w.qf[c], acc[kt], 0, 0, 0);
-    }
+// Mask of tile (rel, lim) on one score tile s: key j of the tile is masked
+// for this lane's query when j >= lim (padding / past the block) or, causal,
+// when its position exceeds the query's ([RA] §3.4 diagonal tiles).
+__device__ __forceinline__ bool tile_needs_mask(const TDesc& d, bool causal) {
+  return d.lim < 64 || (causal && d.rel > -63);
+}
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], const TDesc& d, bool causal, int col,
+                                          int half) {
+  int t = d.lim - 1 - 4 * half;
+  if (causal) {
+    // query col sees key j when j <= col - rel (rel clamped: only |rel| < 128
+    // can cut a tile)
+    const int rel = d.rel < -128 ? -128 : (d.rel > 128 ? 128 : d.rel);
+    t = min(t, max(-1, col - rel - 4 * half));
   }
-}
-
-// Exponentials of one tile against the reference max, their bf16 copy P^T
-// and the denominator over the same rounded weights ([RA] §3.2).
-__device__ __forceinline__ void exp_tile(f32x16 (&s)[2], float m_use, float c_scale,
-                                         bf16x8 (&pb)[4], float& l_run) {
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s[kt][v] = fast_exp2(fmaf(s[kt][v], c_scale, -m_use));
-#pragma unroll
-  for (int G = 0; G < 4; ++G)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pb[G][e] = (__bf16)s[G >> 1][(G & 1) * 8 + e];
-  float l0 = 0.0f, l1 = 0.0f;
-#pragma unroll
-  for (int G = 0; G < 4; ++G)
-#pragma unroll
-    for (int e = 0; e < 8; e += 4) {
-      const bf16x2 p0 = {pb[G][e], pb[G][e + 1]}, p1 = {pb[G][e + 2], pb[G][e + 3]};
-      l0 = __builtin_amdgcn_fdot2_f32_bf16(p0, kOnes2, l0, false);
-      l1 = __builtin_amdgcn_fdot2_f32_bf16(p1, kOnes2, l1, false);
-    }
-  l_run += l0 + l1;
+    for (int v = 0; v < 16; ++v)
+      if (32 * kt + 8 * (v >> 2) + (v & 3) > t) s[kt][v] = -INFINITY;
 }
 
-// Front half of pipeline step n: classification of tiles n and n+1, mask,
-// row max and lazy rescale of tile n, then S^T(n+1) = K(n+1) Q^T on the
-// matrix cores alongside the exponentials of tile n (P(n) into pb).  K(n+1)
-// sits in K buffer PAR^1.  Returns whether tile n is live for this wave.
-template <int D, int NW, int PAR>
-__device__ __forceinline__ bool step_front(
-    const AttnArgs& a, char* smem, WaveState<D, NW>& w, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
-    const Cursor& t0, const Cursor& t1, long long wq_lo, long long wq_hi, int wrows, int col,
-    int half, bf16x8 (&pb)[Bf16Cfg<D, NW>::NS / 8]) {
-  using C = Bf16Cfg<D, NW>;
-  constexpr int BC = C::BC;
-  const float c_scale = a.scale_log2;
-  // tile n: classification, mask, row max, lazy rescale
-  const KVBlock& kb0 = a.blk[t0.blk];
-  const int kt0 = t0.t * BC;
-  const long long kp0 = kb0.k_pos0 + kt0;
-  const bool live0 = wrows > 0 && !(a.causal && kp0 > wq_hi);
-  bool live1 = false;
-  if (t1.blk < a.nblk) {
-    const long long kp1 = a.blk[t1.blk].k_pos0 + (long long)t1.t * BC;
-    live1 = wrows > 0 && !(a.causal && kp1 > wq_hi);
-  }
-  float m_use = 0.0f;
-  if (live0) {
-    long long lim_ll = kb0.len - kt0;
-    if (a.valid_len - kp0 < lim_ll) lim_ll = a.valid_len - kp0;
-    if (lim_ll < BC || (a.causal && kp0 + BC - 1 > wq_lo)) {
-      // key j of the tile is masked for this lane's query when
-      // j > (query - first key) or j >= klim (32-bit, tile relative)
-      const int klim = (int)max(0LL, lim_ll);
-      int t = min(klim, BC) - 1 - 4 * half;
-      if (a.causal) {
-        // wave-uniform offset of the first query from the first key, clamped
-        // on the scalar unit so the per-lane part stays 32-bit
-        const long long d = wq_lo - kp0;
-        const int dc = (int)(d < -2 * BC ? -2 * BC : (d > 2 * BC ? 2 * BC : d));
-        const int rel = max(-1, dc + col - 4 * half);
-        t = min(t, rel);
-      }
+// Row max of a (masked) score tile in the base-2 domain.
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[2], float c_scale) {
+  float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+  for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (32 * kt + 8 * (v >> 2) + (v & 3) > t) s_cur[kt][v] = -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < C::NS; ++i) mx = fmaxf(mx, s_cur[i >> 4][i & 15]);
-    mx = pair_max(mx) * c_scale;
-    w.m_true = fmaxf(w.m_true, mx);
-    const bool need = mx > w.m_ref + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      // move the reference: u and l are rescaled together, so u / l keeps
-      // the value of [RA] §3.2's recurrence while p = 2^(s - m_ref) <= 2^8
-      // lanes that keep their reference use alpha = 1 (a lane still at
-      // -inf must not form 2^(-inf - -inf))
-      const float m_new = need ? mx : w.m_ref;
-      const float alpha = need ? fast_exp2(w.m_ref - mx) : 1.0f;
-      w.l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < C::NDT; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) w.oacc[i][v] *= alpha;
-      w.m_ref = m_new;
-    }
-    m_use = w.m_ref == -INFINITY ? 0.0f : w.m_ref;
-  }
-  // S^T(n+1) on the matrix cores alongside the exponentials of tile n
-  constexpr int kbuf_next = C::KB + (PAR ^ 1) * C::TILE;
-  if (live0 && live1) {
-    // Explicit interleave: step i issues the K read of step i+2, the
-    // matrix-core op of step i and 16/NC exponentials (with their bf16
-    // conversion and denominator update); sched_barrier keeps the steps in
-    // this order so the vector work of tile n fills the matrix-core
-    // latency of tile n+1.
-    constexpr int NSTEP = 2 * C::NC;
-    constexpr int PER = C::NS / NSTEP;  // scores per step (2 for D=128)
-    constexpr int PF = NSTEP >= 8 ? 4 : 2;  // operand read lead (matrix ops)
-    bf16x8 kf[PF + 1];
-    // step i works on score tile kt = i % 2 with k-step c = i / 2, so
-    // consecutive matrix-core ops never depend on each other
-    auto kread = [&](int i) -> bf16x8 {
-      return *(const bf16x8*)(smem + kbuf_next + (i % 2) * 32 * C::ROWB + w.kaddr[i / 2]);
-    };
-#pragma unroll
-    for (int i = 0; i < PF; ++i) kf[i] = kread(i);
-    float lp[2] = {0.0f, 0.0f};
-    float xs[3][PER];
-#pragma unroll
-    for (int t = 0; t < NSTEP + 2; ++t) {
-      // slot t: matrix op t - 2 (slots 0, 1 run ahead of the first), shift of
-      // group t, exponential of group t - 1, bf16 copy and sum of group t - 2
-      const int i = t - 2;
-      if (i >= 0) {
-        if (i + PF < NSTEP) kf[(i + PF) % (PF + 1)] = kread(i + PF);
-        const int kt = i % 2, c = i / 2;
-        s_nxt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % (PF + 1)], w.qf[c],
-                                                            c == 0 ? f32x16{} : s_nxt[kt], 0, 0, 0);
-      }
-      if (t < NSTEP) {
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-          const int v = t * PER + j;
-          xs[t % 3][j] = fmaf(s_cur[v >> 4][v & 15], c_scale, -m_use);
-        }
-      }
-      if (t >= 1 && t - 1 < NSTEP) {
-#pragma unroll
-        for (int j = 0; j < PER; ++j) xs[(t - 1) % 3][j] = fast_exp2(xs[(t - 1) % 3][j]);
-      }
-      if (i >= 0) {
-#pragma unroll
-        for (int j = 0; j < PER; j += 2) {
-          const int v = i * PER + j;
-          const int G = 2 * (v >> 4) + ((v & 15) >> 3), e = v & 7;
-          pb[G][e] = (__bf16)xs[i % 3][j];
-          pb[G][e + 1] = (__bf16)xs[i % 3][j + 1];
-          const bf16x2 pr = {pb[G][e], pb[G][e + 1]};
-          lp[(v >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, lp[(v >> 1) & 1], false);
-        }
-      }
-      if (i >= 0) __builtin_amdgcn_sched_barrier(0);
-    }
-    w.l_run += lp[0] + lp[1];
-  } else {
-    if (live1) scores_tile<D, NW>(smem, kbuf_next, w, s_nxt);
-    if (live0) exp_tile(s_cur, m_use, c_scale, pb, w.l_run);
-  }
-  return live0;
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt][v]);
+  return pair_max(mx) * c_scale;
 }
 
-// Back half of pipeline step n: O^T += V(n)^T P(n)^T from V buffer vb.
+// Move the reference of the lanes whose max mx exceeds it by more than the
+// slack; returns alpha (1 for lanes that keep theirs).  u must be rescaled
+// by alpha by the caller, after every product of the old reference.
+__device__ __forceinline__ float move_reference(float& m_ref, float& l_run, float mx) {
+  const bool need = mx > m_ref + kRescaleSlack;
+  const float alpha = need ? fast_exp2(m_ref - mx) : 1.0f;
+  l_run *= alpha;
+  m_ref = need ? mx : m_ref;
+  return alpha;
+}
+
+// Softmax of one half (score tile KT: keys 32 KT .. 32 KT + 31) as a
+// software pipeline over 8 pairs of scores: time T shifts and scales pair T,
+// exponentiates pair T-1, and packs pair T-2 to bf16 and adds the rounded
+// pair to the row sum (10 time steps).  The packed pair lands in element
+// 2 (pair % 4), +1 of fragment pair / 4 of the half; the two fragments are
+// built fresh (not as updates of the previous tile's registers, which would
+// keep those alive) and stored to P fragments 2 KT, 2 KT + 1 at the end.
+struct HalfSoftmax {
+  float x[3][2];
+  float lp[2];
+  bf16x8 g[2];
+};
+template <int KT, int T>
+__device__ __forceinline__ void half_softmax_step(HalfSoftmax& hs, const f32x16& s, float c,
+                                                  float nm, bf16x8 (&pb)[4]) {
+  if constexpr (T < 8) {
+    hs.x[T % 3][0] = fmaf(s[2 * T], c, nm);
+    hs.x[T % 3][1] = fmaf(s[2 * T + 1], c, nm);
+  }
+  if constexpr (T >= 1 && T - 1 < 8) {
+    hs.x[(T - 1) % 3][0] = fast_exp2(hs.x[(T - 1) % 3][0]);
+    hs.x[(T - 1) % 3][1] = fast_exp2(hs.x[(T - 1) % 3][1]);
+  }
+  if constexpr (T >= 2 && T - 2 < 8) {
+    constexpr int p = T - 2, g = p / 4, e = 2 * (p % 4);
+    // the row sum adds the bf16-rounded weights that enter P V, so that O
+    // stays an exact convex combination of V rows: the packed pair is
+    // unpacked to two fp32 values (a mask and a shift) and added.  These
+    // integer ops and adds run alongside the matrix ops, while a v_dot2 over
+    // the bf16 pair would hold the matrix pipe for about half a matrix op.
+    const bf16x2 pr = {(__bf16)hs.x[p % 3][0], (__bf16)hs.x[p % 3][1]};
+    unsigned d;
+    __builtin_memcpy(&d, &pr, 4);
+    hs.lp[0] += __uint_as_float(d << 16);
+    hs.lp[1] += __uint_as_float(d & 0xffff0000u);
+    hs.g[g][e] = pr[0];
+    hs.g[g][e + 1] = pr[1];
+    // pin the pair's work to this slot: without a use here the compiler
+    // sinks it below later branches, out of the matrix phase it fills
+    asm volatile("" : "+v"(hs.lp[0]), "+v"(hs.lp[1]));
+    if constexpr (p % 4 == 3) pb[2 * KT + g] = hs.g[g];
+  }
+}
+constexpr int kSoftSteps = 10;
+
+// The half-softmax time steps that go after matrix op i of n.
+template <int I, int N>
+struct SoftSlot {
+  static constexpr int lo = I * kSoftSteps / N, hi = (I + 1) * kSoftSteps / N;
+};
+
+template <int KT, int LO, int HI>
+__device__ __forceinline__ void half_softmax_range(HalfSoftmax& hs, const f32x16& s, float c,
+                                                   float nm, bf16x8 (&pb)[4]) {
+  static_for<LO, HI>([&](auto tc) {
+    half_softmax_step<KT, decltype(tc)::value>(hs, s, c, nm, pb);
+  });
+}
+
+// Both halves of a tile's softmax without matrix work (prologue, the rare
+// redo, and phases whose matrix side is idle).
+template <int KT>
+__device__ __forceinline__ float half_softmax_all(const f32x16& s, float c, float m_use,
+                                                  bf16x8 (&pb)[4]) {
+  HalfSoftmax hs;
+  hs.lp[0] = hs.lp[1] = 0.0f;
+  half_softmax_range<KT, 0, kSoftSteps>(hs, s, c, -m_use, pb);
+  return hs.lp[0] + hs.lp[1];
+}
+
+// Front half of a step: S^T(n+1) = K(n+1) Q^T from the K buffer at LDS
+// byte offset koff, interleaved with the second half of tile n's softmax.
+// Returns that half's contribution to the row sum.  Both run for every
+// step: a tile that is dead for the wave (wholly in its future) reaches
+// here fully masked, so its weights are exact zeros, and past the end of
+// the sequence the products read a stale buffer whose results are unused.
+// Keeping the matrix chains free of branches keeps the accumulators in one
+// set of registers.
 template <int D, int NW>
-__device__ __forceinline__ void step_back(char* smem, WaveState<D, NW>& w,
-                                          const bf16x8 (&pb)[Bf16Cfg<D, NW>::NS / 8], int vb,
-                                          bool live0) {
+__device__ __forceinline__ float step_front(WaveState<D, NW>& w, unsigned koff,
+                                            const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+                                            bf16x8 (&pb)[4], float c) {
   using C = Bf16Cfg<D, NW>;
-  constexpr int BC = C::BC;
-  // O^T += V(n)^T P(n)^T: fragment j = (G = j / NDT, dt = j % NDT) is read
-  // PF ops ahead, and consecutive ops accumulate into different d tiles
-  if (live0) {
-    constexpr int NJ = (BC / 16) * C::NDT;
-    constexpr int PF = NJ >= 8 ? 4 : 2;
-    unsigned vbase[C::NDT];
-    const unsigned vl = (unsigned)(size_t)(lds_void_ptr)(smem + C::VB + vb * C::TILE);
+  constexpr int N = C::NQK;
+  constexpr int PF = kOperandLead;
+  const float nm = -w.m_use;
+  HalfSoftmax hs;
+  hs.lp[0] = hs.lp[1] = 0.0f;
+  // op i: score tile kt = i % 2, k-step ci = i / 2 (consecutive ops never
+  // depend on each other)
+  unsigned kbase[C::NC];
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) vbase[dt] = vl + w.vaddr[dt];
-    // two 64-bit transposed reads per fragment: keys 16G .. 16G+7 and
-    // 16G+8 .. 16G+15 of the fragment's d tile
-    s16x8 vr[PF + 1];
-    auto vread = [&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      constexpr int off = (j / C::NDT) * 16 * C::ROWB;
-      const s16x4 lo = lds_read_tr16<off>(vbase[j % C::NDT]);
-      const s16x4 hi = lds_read_tr16<off + 8 * C::ROWB>(vbase[j % C::NDT]);
-      vr[j % (PF + 1)] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    static_for<0, PF>([&](auto jc) { vread(jc); });
-    // this phase is matrix-core bound: give it issue priority over the
-    // other wave on the SIMD, whose exponentials fill the gaps
-    __builtin_amdgcn_s_setprio(2);
-    static_for<0, NJ>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      if constexpr (j + PF < NJ) vread(std::integral_constant<int, j + PF>{});
-      // reads issued after fragment j's: those of fragments j+1 .. j+PF
-      constexpr int later = 2 * ((j + PF < NJ ? j + PF : NJ - 1) - j);
-      claim_lds<later>(vr[j % (PF + 1)]);
-      bf16x8 vf;
-      __builtin_memcpy(&vf, &vr[j % (PF + 1)], 16);
-      constexpr int G = j / C::NDT, dt = j % C::NDT;
-      w.oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[G], w.oacc[dt], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    __builtin_amdgcn_s_setprio(0);
-  }
+  for (int ci = 0; ci < C::NC; ++ci) kbase[ci] = w.kaddr[ci] + koff;
+  bf16x8 kf[PF + 1];
+  auto kread = [&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    kf[i % (PF + 1)] = lds_read_b128<(i % 2) * 32 * C::ROWB>(kbase[i / 2]);
+  };
+  static_for<0, PF>([&](auto ic) { kread(ic); });
+  static_for<0, N>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i + PF < N) kread(std::integral_constant<int, i + PF>{});
+    constexpr int later = (i + PF < N ? i + PF : N - 1) - i;
+    claim_lds<later>(kf[i % (PF + 1)]);
+    constexpr int kt = i % 2, ci = i / 2;
+    s_nxt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % (PF + 1)], w.qf[ci],
+                                                        ci == 0 ? f32x16{} : s_nxt[kt], 0, 0, 0);
+    half_softmax_range<1, SoftSlot<i, N>::lo, SoftSlot<i, N>::hi>(hs, s_cur[1], c, nm, pb);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  return hs.lp[0] + hs.lp[1];
 }
 
-// One pipeline step.  PAR = n & 1: K(n+1) sits in K buffer PAR^1, V(n) in
-// V buffer PAR; the copies go to K buffer PAR and V buffer PAR^1.
-template <int D, int NW, int PAR>
-__device__ __forceinline__ void pipeline_step(
-    const AttnArgs& a, char* smem, WaveState<D, NW>& w, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
-    Cursor& t0, Cursor& t1, Cursor& t2, int& vb,
-    const Span& sp, long long wq_lo, long long wq_hi, int wrows, int col, int half, int b,
-    int h, int HD2, int wave) {
+// Back half of a step: O^T += V(n)^T P(n)^T from the V buffer at LDS byte
+// offset vbuf, interleaved with the first half of tile n+1's softmax.
+// Returns that half's contribution to the row sum (unconditional, as above).
+template <int D, int NW>
+__device__ __forceinline__ float step_back(WaveState<D, NW>& w, unsigned vbuf,
+                                           const bf16x8 (&pb)[4], const f32x16 (&s_nxt)[2],
+                                           bf16x8 (&pb_nxt)[4], float c) {
   using C = Bf16Cfg<D, NW>;
-  // copies of tile n+2: K first, so that waiting for it leaves V in flight
-  const int vb2 = vb == 0 ? 2 : vb - 1;  // (vb + 2) % 3
-  const bool copy2 = t2.blk < a.nblk;
-  if (copy2) {
-    const KVBlock& kb2 = a.blk[t2.blk];
-    copy_tile<D, NW>(kb2.k, kb2.len, a.kv_rows_b, t2.t, b, h, a.Hkv, HD2, wave, w.voffk,
-                 smem + C::KB + PAR * C::TILE);
-    copy_tile<D, NW>(kb2.v, kb2.len, a.kv_rows_b, t2.t, b, h, a.Hkv, HD2, wave, w.voffv,
-                 smem + C::VB + vb2 * C::TILE);
-  }
-  bf16x8 pb[C::NS / 8];
-  const bool live0 = step_front<D, NW, PAR>(a, smem, w, s_cur, s_nxt, t0, t1, wq_lo, wq_hi,
-                                            wrows, col, half, pb);
-  step_back<D, NW>(smem, w, pb, vb, live0);
-  // this wave's K(n+2) copy (and everything older) landed; V(n+2) may fly
-  if (copy2) wait_vmcnt<C::DMA>();
-  else wait_vmcnt<0>();
-  pipeline_barrier();  // everyone's copies landed, everyone done reading
-  t0 = t1;
-  t1 = t2;
-  t2 = cursor_next(a, sp, t2);
-  vb = vb == 2 ? 0 : vb + 1;
+  constexpr int N = C::NPV;
+  constexpr int PF = kOperandLead;
+  const float nm = -w.m_use;
+  HalfSoftmax hs;
+  hs.lp[0] = hs.lp[1] = 0.0f;
+  // fragment j = (G = j / NDT, dt = j % NDT): two 64-bit transposed reads
+  // (keys 16G .. 16G+7 and 16G+8 .. 16G+15 of d tile dt); consecutive ops
+  // accumulate into different d tiles
+  unsigned vbase[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt) vbase[dt] = vbuf + w.vaddr[dt];
+  s16x8 vr[PF + 1];
+  auto vread = [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int off = (j / C::NDT) * 16 * C::ROWB;
+    const s16x4 lo = lds_read_tr16<off>(vbase[j % C::NDT]);
+    const s16x4 hi = lds_read_tr16<off + 8 * C::ROWB>(vbase[j % C::NDT]);
+    vr[j % (PF + 1)] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  static_for<0, PF>([&](auto jc) { vread(jc); });
+  static_for<0, N>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (j + PF < N) vread(std::integral_constant<int, j + PF>{});
+    // reads issued after fragment j's: those of fragments j+1 .. j+PF
+    constexpr int later = 2 * ((j + PF < N ? j + PF : N - 1) - j);
+    claim_lds<later>(vr[j % (PF + 1)]);
+    bf16x8 vf;
+    __builtin_memcpy(&vf, &vr[j % (PF + 1)], 16);
+    constexpr int G = j / C::NDT, dt = j % C::NDT;
+    w.oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[G], w.oacc[dt], 0, 0, 0);
+    half_softmax_range<0, SoftSlot<j, N>::lo, SoftSlot<j, N>::hi>(hs, s_nxt[0], c, nm, pb_nxt);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  return hs.lp[0] + hs.lp[1];
 }
 
-// One step of the staggered form (8 waves, 256 query rows, one barrier per
-// step).  Both groups run front(n) then back(n), but group 0 (waves 0-3)
-// passes its barrier after back(n) and group 1 (waves 4-7) after front(n).
-// Between two barriers the group-0 wave thus computes front(n), back(n)
-// while its partner on the same SIMD computes back(n-1), front(n): one is
-// in its vector-heavy half while the other is in its matrix-bound half.
-// Group 0 copies whole tiles: K(n+2) into K(n)'s buffer and V(n+2) into
-// V(n-2)'s (four V buffers, as group 1 reads V(n-1) during step n), and
-// waits for its K(n+2) before its barrier.
-template <int D, int PAR>
-__device__ __forceinline__ void pp_step(
-    const AttnArgs& a, char* smem, WaveState<D, 8>& w, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
-    Cursor& t0, Cursor& t1, Cursor& t2, int& vb, const Span& sp, long long wq_lo,
-    long long wq_hi, int wrows, int col, int half, int b, int h, int HD2, int gw, int grp,
-    const int* voffk4, const int* voffv4) {
-  using C = Bf16Cfg<D, 8>;
-  const bool copy2 = grp == 0 && t2.blk < a.nblk;
-  if (copy2) {
-    const KVBlock& kb2 = a.blk[t2.blk];
-    copy_tile<D, 4>(kb2.k, kb2.len, a.kv_rows_b, t2.t, b, h, a.Hkv, HD2, gw, voffk4,
-                    smem + C::KB + PAR * C::TILE);
-    copy_tile<D, 4>(kb2.v, kb2.len, a.kv_rows_b, t2.t, b, h, a.Hkv, HD2, gw, voffv4,
-                    smem + C::VB + ((vb + 2) & 3) * C::TILE);
+template <int D, int NW>
+__device__ __forceinline__ void scale_o(WaveState<D, NW>& w, float alpha) {
+#pragma unroll
+  for (int i = 0; i < Bf16Cfg<D, NW>::NDT; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) w.oacc[i][v] *= alpha;
+}
+
+// Row max of one half (score tile s of 16 values per lane) in base 2.
+__device__ __forceinline__ float half_max(const f32x16& s, float c_scale) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
+  return pair_max(mx) * c_scale;
+}
+
+// A half whose weights exceed the bound (a score more than ~20 above the
+// reference, or an infinite weight): move the reference of the lanes whose
+// half max mx lies above it by the whole number of octaves k that brings
+// every weight of the half to at most 1, and scale u, l and the other
+// weights already formed against the old reference by 2^-k -- exact, as
+// scaling by a power of two commutes with rounding.  Returns 2^-k (1 for
+// lanes that keep their reference).
+__device__ __forceinline__ float move_reference_octaves(float& m_ref, float& l_run, float mx) {
+  const bool need = mx > m_ref;
+  const float k = need ? ceilf(mx - m_ref) : 0.0f;
+  const float f = fast_exp2(-k);
+  m_ref += k;
+  l_run *= f;
+  return f;
+}
+
+__device__ __forceinline__ void scale_p(bf16x8& p, float f) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) p[e] = (__bf16)((float)p[e] * f);
+}
+
+// S^T of one tile from the K buffer at KOFF, without interleaved work.
+template <int D, int NW, int KOFF>
+__device__ __forceinline__ void scores_tile(const WaveState<D, NW>& w, f32x16 (&acc)[2]) {
+  using C = Bf16Cfg<D, NW>;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) acc[kt] = f32x16{};
+  static_for<0, C::NQK>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    bf16x8 kf = lds_read_b128<KOFF + (i % 2) * 32 * C::ROWB>(w.kaddr[i / 2]);
+    claim_lds<0>(kf);
+    acc[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, w.qf[i / 2], acc[i % 2], 0, 0, 0);
+  });
+}
+
+// Per-step context that stays fixed over the loop.
+struct StepCtx {
+  const AttnArgs* a;
+  SeqCtx x;
+  int HD2, wave, col, half, wrows;
+  bool causal, rowmax;
+  float c;
+};
+
+// Set up tile n+1 for its softmax (before its first half runs): mask, and,
+// on the row-max path or while some row of the wave has no reference yet,
+// the row max and a lazy move of the reference.  Returns alpha for the
+// deferred rescale of u (1 when nothing moved) and sets `moved`.
+template <int D, int NW, bool ML>
+__device__ __forceinline__ float tile_setup(const StepCtx& k, WaveState<D, NW>& w, f32x16 (&s)[2],
+                                            const TDesc& d, bool& moved) {
+  if (tile_needs_mask(d, k.causal)) mask_tile(s, d, k.causal, k.col, k.half);
+  float alpha = 1.0f;
+  moved = false;
+  if (ML || k.rowmax || __builtin_amdgcn_ballot_w64(w.m_ref == -INFINITY)) {
+    const float mx = tile_max(s, k.c);
+    if (ML) w.m_true = fmaxf(w.m_true, mx);
+    if (__builtin_amdgcn_ballot_w64(mx > w.m_ref + kRescaleSlack)) {
+      alpha = move_reference(w.m_ref, w.l_run, mx);
+      moved = true;
+    }
   }
-  bf16x8 pb[C::NS / 8];
-  const bool live0 = step_front<D, 8, PAR>(a, smem, w, s_cur, s_nxt, t0, t1, wq_lo, wq_hi,
-                                           wrows, col, half, pb);
-  if (grp == 1) pipeline_barrier();
-  step_back<D, 8>(smem, w, pb, vb, live0);
-  if (grp == 0) {
-    // this wave's K(n+2) copy (and everything older) landed; V(n+2) may fly
-    if (copy2) wait_vmcnt<Bf16Cfg<D, 4>::DMA>();
+  w.m_use = w.m_ref == -INFINITY ? 0.0f : w.m_ref;
+  return alpha;
+}
+
+// First half of a tile over the bound: move the reference, scale u and l
+// (every product of the old reference has been issued), redo the half.
+template <int D, int NW>
+__device__ __forceinline__ void first_half_check(const StepCtx& k, WaveState<D, NW>& w,
+                                                 const f32x16& s0, bf16x8 (&pb)[4], float& l1) {
+  if (__builtin_amdgcn_ballot_w64(l1 > kTileSumLimit)) {
+    const float f = move_reference_octaves(w.m_ref, w.l_run, half_max(s0, k.c));
+    scale_o<D, NW>(w, f);
+    w.m_use = w.m_ref;
+    l1 = half_softmax_all<0>(s0, k.c, w.m_use, pb);
+  }
+}
+
+// One pipeline step.  PAR = n & 1 only swaps the roles of the two score
+// and P register sets.  K(n) sits in K buffer kb, K(n+1) in the next one,
+// V(n) in V buffer vb; the copies of tile n + LEAD go to K(n)'s buffer
+// (read in the step before) and to V(n-1)'s.  d0, d1, d2 describe tiles n,
+// n+1, n+2 (d2 only with LEAD = 3) and cur stands at tile n + LEAD.
+template <int D, int NW, bool ML, int PAR>
+__device__ __forceinline__ void pipeline_step(const StepCtx& k, char* smem, WaveState<D, NW>& w,
+                                              f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+                                              bf16x8 (&pb_cur)[4], bf16x8 (&pb_nxt)[4],
+                                              float& lsum_cur, float& lsum_nxt, Seq& cur,
+                                              TDesc& d0, TDesc& d1, TDesc& d2, int& kb, int& vb) {
+  using C = Bf16Cfg<D, NW>;
+  const AttnArgs& a = *k.a;
+  const int kb1 = kb + 1 == C::KBUF ? 0 : kb + 1;  // K(n+1)
+  const int vcp = vb == 0 ? C::VBUF - 1 : vb - 1;  // V(n-1)'s buffer
+  // copies of tile n + LEAD: K first, so that waiting for K leaves V in flight
+  const TDesc dl = seq_desc(a, cur);
+  if (dl.valid)
+    copy_tile<D, NW>(cur, k.HD2, k.wave, w.voffk, w.voffv, smem, C::KB + kb * C::TILE,
+                     C::VB + vcp * C::TILE);
+  const unsigned lds0 = (unsigned)(size_t)(lds_void_ptr)smem;
+
+  // front: S^T(n+1) with the second half of P(n) (tile n is valid here)
+  float l2 = step_front<D, NW>(w, lds0 + C::KB + kb1 * C::TILE, s_cur, s_nxt, pb_cur, k.c);
+  {
+    // second half over the bound: move the reference, scale u, l and the
+    // first half's weights, redo the second half
+    if (__builtin_amdgcn_ballot_w64(l2 > kTileSumLimit)) {
+      const float f = move_reference_octaves(w.m_ref, w.l_run, half_max(s_cur[1], k.c));
+      scale_o<D, NW>(w, f);
+      scale_p(pb_cur[0], f);
+      scale_p(pb_cur[1], f);
+      lsum_cur *= f;
+      w.m_use = w.m_ref;
+      l2 = half_softmax_all<1>(s_cur[1], k.c, w.m_use, pb_cur);
+    }
+    w.l_run += lsum_cur + l2;
+  }
+
+  // back: P(n) V(n) with the first half of P(n+1)
+  float alpha = 1.0f;
+  bool moved = false;
+  if (d1.valid) alpha = tile_setup<D, NW, ML>(k, w, s_nxt, d1, moved);
+  lsum_nxt = step_back<D, NW>(w, lds0 + C::VB + vb * C::TILE, pb_cur, s_nxt, pb_nxt, k.c);
+  if (moved) scale_o<D, NW>(w, alpha);  // after every product of the old reference
+  if (d1.valid) first_half_check<D, NW>(k, w, s_nxt[0], pb_nxt, lsum_nxt);
+
+  // K(n+2) and V(n+1) (and everything older) landed; the later copies may
+  // stay in flight
+  if constexpr (C::LEAD == 3) {
+    if (dl.valid) wait_vmcnt<3 * C::DMA>();
+    else if (d2.valid) wait_vmcnt<C::DMA>();
     else wait_vmcnt<0>();
-    pipeline_barrier();
+  } else {
+    if (dl.valid) wait_vmcnt<C::DMA>();
+    else wait_vmcnt<0>();
   }
-  t0 = t1;
-  t1 = t2;
-  t2 = cursor_next(a, sp, t2);
-  vb = (vb + 1) & 3;
+  pipeline_barrier();  // everyone's copies landed, everyone done reading
+  d0 = d1;
+  if constexpr (C::LEAD == 3) {
+    d1 = d2;
+    d2 = dl;
+  } else {
+    d1 = dl;
+  }
+  seq_next(a, k.x, cur);
+  kb = kb1;
+  vb = vb + 1 == C::VBUF ? 0 : vb + 1;
 }
 
 // One (batch, head, query tile) over tiles [lo, hi) of its visited-tile
-// sequence, shared by the 32-row-per-wave kernels; PP selects the staggered
-// form (NW = 8 only).  slot < 0: the output rows of the tile; otherwise the
-// split partial slot (see AttnArgs).
-template <int D, int NW, bool PP>
+// sequence.  slot < 0: the output rows of the tile; otherwise the split
+// partial slot (see AttnArgs).  ML: also track the exact max for m / l.
+template <int D, int NW, bool ML>
 __device__ __forceinline__ void attn_bf16_tile(const AttnArgs& a, char* smem, int b, int h,
                                                int qt, int lo, int hi, long long slot) {
   using C = Bf16Cfg<D, NW>;
-  static_assert(!PP || NW == 8, "the staggered form pairs waves w and w+4 on one SIMD");
-
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
 
   const int row0 = qt * C::BR;
   const int rows_here = min(C::BR, a.Sq - row0);
-  Span sp{qpos(a, row0 + rows_here - 1), a.nblk, 0};
-  if (hi != INT_MAX) {
-    const Cursor e = seq_pos(a, sp.q_hi, hi);
-    sp.end_blk = e.blk;
-    sp.end_t = e.t;
-  }
   const int wrow0 = row0 + wave * 32;
-  const int wrows = min(32, a.Sq - wrow0);
-  const long long wq_lo = qpos(a, wrow0);
-  const long long wq_hi = wq_lo + wrows - 1;
   const long long HD = (long long)a.H * D;
-  const int HD2 = a.Hkv * D * 2;  // bytes between consecutive key rows
   const int hk = h / (a.H / a.Hkv);  // K/V head of this query head
+
+  StepCtx k;
+  k.a = &a;
+  k.HD2 = a.Hkv * D * 2;  // bytes between consecutive key rows
+  k.wave = wave;
+  k.col = col;
+  k.half = half;
+  k.wrows = min(32, a.Sq - wrow0);
+  k.causal = a.causal != 0;
+  k.rowmax = a.rowmax != 0;
+  k.c = a.scale_log2;
+  k.x.q_hi = qpos(a, row0 + rows_here - 1);
+  k.x.wq_lo = qpos(a, wrow0);
+  k.x.boff = ((long long)b * a.kv_rows_b * a.Hkv + hk) * (D * 2);
+  k.x.end_blk = a.nblk;
+  k.x.end_t = 0;
+  if (hi != INT_MAX) seq_locate(a, k.x.q_hi, hi, k.x.end_blk, k.x.end_t);
 
   WaveState<D, NW> w;
   {
@@ -719,11 +885,13 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs& a, char* smem, in
   for (int i = 0; i < C::DMA; ++i) {
     const int p = (wave * C::DMA + i) * 64 + lane;  // physical 16B chunk in the tile
     const int r = p / C::CHUNKS, pc = p % C::CHUNKS;
-    w.voffk[i] = r * HD2 + swz_k<D>(r, pc) * 16;
-    w.voffv[i] = r * HD2 + swz_v<D>(r, pc) * 16;
+    w.voffk[i] = r * k.HD2 + swz_k<D>(r, pc) * 16;
+    w.voffv[i] = r * k.HD2 + swz_v<D>(r, pc) * 16;
   }
+  const unsigned lds0 = (unsigned)(size_t)(lds_void_ptr)smem;
 #pragma unroll
-  for (int c = 0; c < C::NC; ++c) w.kaddr[c] = col * C::ROWB + swz_k<D>(col, 2 * c + half) * 16;
+  for (int c = 0; c < C::NC; ++c)
+    w.kaddr[c] = lds0 + col * C::ROWB + swz_k<D>(col, 2 * c + half) * 16;
   {
     const int j = lane & 15, e = j >> 2, q = j & 3, g = lane >> 4;
     const int kl = 4 * half + e;  // supplier row within a 16-key group
@@ -736,74 +904,50 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs& a, char* smem, in
 #pragma unroll
   for (int i = 0; i < C::NDT; ++i) w.oacc[i] = f32x16{};
   w.m_ref = -INFINITY;
+  w.m_use = 0.0f;
   w.m_true = -INFINITY;
   w.l_run = 0.0f;
 
-  // staggered form: group of the wave, its index in the group and, for
-  // group 0, the copy offsets of whole tiles over four waves
-  const int grp = wave >> 2, gw = wave & 3;
-  int voffk4[PP ? Bf16Cfg<D, 4>::DMA : 1], voffv4[PP ? Bf16Cfg<D, 4>::DMA : 1];
-  if constexpr (PP) {
-#pragma unroll
-    for (int i = 0; i < Bf16Cfg<D, 4>::DMA; ++i) {
-      const int p = (gw * Bf16Cfg<D, 4>::DMA + i) * 64 + lane;
-      const int r = p / C::CHUNKS, pc = p % C::CHUNKS;
-      voffk4[i] = r * HD2 + swz_k<D>(r, pc) * 16;
-      voffv4[i] = r * HD2 + swz_v<D>(r, pc) * 16;
-    }
-  }
-
-  // prologue: K(0), V(0), K(1) into K0, V0, K1; scores of tile 0
-  Cursor t0 = cursor_first(a, sp, lo);
-  Cursor t1 = cursor_next(a, sp, t0);
-  Cursor t2 = cursor_next(a, sp, t1);
-  f32x16 sA[2], sB[2];
-  if (t0.blk < a.nblk) {
-    const KVBlock& kb = a.blk[t0.blk];
-    copy_tile<D, NW>(kb.k, kb.len, a.kv_rows_b, t0.t, b, hk, a.Hkv, HD2, wave, w.voffk,
-                     smem + C::KB);
-    copy_tile<D, NW>(kb.v, kb.len, a.kv_rows_b, t0.t, b, hk, a.Hkv, HD2, wave, w.voffv,
-                     smem + C::VB);
-  }
-  if (t1.blk < a.nblk) {
-    const KVBlock& kb = a.blk[t1.blk];
-    copy_tile<D, NW>(kb.k, kb.len, a.kv_rows_b, t1.t, b, hk, a.Hkv, HD2, wave, w.voffk,
-                     smem + C::KB + C::TILE);
-    copy_tile<D, NW>(kb.v, kb.len, a.kv_rows_b, t1.t, b, hk, a.Hkv, HD2, wave, w.voffv,
-                     smem + C::VB + C::TILE);
-  }
+  // prologue: tiles 0 .. LEAD-1 into K and V buffers 0 .. LEAD-1; scores of
+  // tile 0 and the first half of its softmax
+  Seq cur = seq_first(a, k.x, lo);
+  TDesc d0 = seq_desc(a, cur), d1{}, d2{};
+  static_for<0, C::LEAD>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    const TDesc d = seq_desc(a, cur);
+    if (d.valid)
+      copy_tile<D, NW>(cur, k.HD2, wave, w.voffk, w.voffv, smem, C::KB + t * C::TILE,
+                       C::VB + t * C::TILE);
+    if constexpr (t == 1) d1 = d;
+    if constexpr (t == 2) d2 = d;
+    seq_next(a, k.x, cur);
+  });
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (t0.blk < a.nblk) {
-    const long long kp0 = a.blk[t0.blk].k_pos0 + (long long)t0.t * C::BC;
-    if (wrows > 0 && !(a.causal && kp0 > wq_hi)) scores_tile<D, NW>(smem, C::KB, w, sA);
+  f32x16 sA[2], sB[2];
+  bf16x8 pA[4], pB[4];
+  float lA = 0.0f, lB = 0.0f;
+  if (d0.valid) {
+    scores_tile<D, NW, C::KB>(w, sA);
+    bool moved;
+    tile_setup<D, NW, ML>(k, w, sA, d0, moved);
+    lA = half_softmax_all<0>(sA[0], k.c, w.m_use, pA);
+    first_half_check<D, NW>(k, w, sA[0], pA, lA);
   }
-  __syncthreads();  // K buffer 0 is free for K(2)
+  __syncthreads();  // K buffer 0 is free for K(LEAD)
 
-  int vb = 0;  // V buffer of tile n
-  if constexpr (PP) {
-    while (t0.blk < a.nblk) {
-      pp_step<D, 0>(a, smem, w, sA, sB, t0, t1, t2, vb, sp, wq_lo, wq_hi, wrows, col, half, b,
-                    hk, HD2, gw, grp, voffk4, voffv4);
-      if (t0.blk >= a.nblk) break;
-      pp_step<D, 1>(a, smem, w, sB, sA, t0, t1, t2, vb, sp, wq_lo, wq_hi, wrows, col, half, b,
-                    hk, HD2, gw, grp, voffk4, voffv4);
-    }
-  } else {
-    while (t0.blk < a.nblk) {
-      pipeline_step<D, NW, 0>(a, smem, w, sA, sB, t0, t1, t2, vb, sp, wq_lo, wq_hi, wrows,
-                              col, half, b, hk, HD2, wave);
-      if (t0.blk >= a.nblk) break;
-      pipeline_step<D, NW, 1>(a, smem, w, sB, sA, t0, t1, t2, vb, sp, wq_lo, wq_hi, wrows,
-                              col, half, b, hk, HD2, wave);
-    }
+  int kb = 0, vb = 0;  // K and V buffers of tile n
+  while (d0.valid) {
+    pipeline_step<D, NW, ML, 0>(k, smem, w, sA, sB, pA, pB, lA, lB, cur, d0, d1, d2, kb, vb);
+    if (!d0.valid) break;
+    pipeline_step<D, NW, ML, 1>(k, smem, w, sB, sA, pB, pA, lB, lA, cur, d0, d1, d2, kb, vb);
   }
 
   // ---- epilogue: o = u / l, lse = m + ln l ([RA] §3.2; [SPD] §四) ----
   const float l_tot = pair_sum(w.l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const int r = wrow0 + col;
-  if (wrows > 0 && r < a.Sq) {
+  if (k.wrows > 0 && r < a.Sq) {
     // output row (b, r, h), or row r - row0 of the split partial slot
     const long long so = slot < 0 ? ((long long)b * a.Sq + r) * a.H + h
                                   : slot * C::BR + (r - row0);
@@ -827,15 +971,17 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs& a, char* smem, in
     if (half == 0) {
       const bool seen = l_tot > 0.0f;
       if (a.lse) a.lse[so] = seen ? (w.m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
-      if (a.m_out) a.m_out[so] = seen ? w.m_true * kLn2 : -INFINITY;
-      if (a.l_out) a.l_out[so] = seen ? l_tot * fast_exp2(w.m_ref - w.m_true) : 0.0f;
+      if (ML) {
+        if (a.m_out) a.m_out[so] = seen ? w.m_true * kLn2 : -INFINITY;
+        if (a.l_out) a.l_out[so] = seen ? l_tot * fast_exp2(w.m_ref - w.m_true) : 0.0f;
+      }
     }
   }
 }
 
-// Kernel body shared by the 32-row-per-wave kernels: one query tile over its
-// whole visited sequence, or (SPLIT) one run of it.
-template <int D, int NW, bool PP, bool SPLIT = false>
+// Kernel body: one query tile over its whole visited sequence, or (SPLIT)
+// one run of it.
+template <int D, int NW, bool ML, bool SPLIT>
 __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   using C = Bf16Cfg<D, NW>;
   if constexpr (SPLIT) {
@@ -848,1137 +994,28 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
     int total = 0;
     for (int bi = 0; bi < a.nblk; ++bi) total += tiles_of<64>(a, bi, q_hi);
     const int lo = (int)((long long)total * j / ns), hi = (int)((long long)total * (j + 1) / ns);
-    attn_bf16_tile<D, NW, PP>(a, smem, bh / a.H, bh % a.H, qt, lo, hi, (long long)tile * ns + j);
+    attn_bf16_tile<D, NW, ML>(a, smem, bh / a.H, bh % a.H, qt, lo, hi, (long long)tile * ns + j);
   } else {
     int b, h, qt;
     tile_coords(a, b, h, qt);
-    attn_bf16_tile<D, NW, PP>(a, smem, b, h, qt, 0, INT_MAX, -1);
+    attn_bf16_tile<D, NW, ML>(a, smem, b, h, qt, 0, INT_MAX, -1);
   }
 }
-template <int D, int NW>
+
+template <int D, int NW, bool ML>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ring_attn_bf16(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[Bf16Cfg<D, NW>::LDS];
-  attn_bf16_body<D, NW, false>(a, smem);
+  attn_bf16_body<D, NW, ML, false>(a, smem);
 }
 
-// The split ring on the 128-row kernel (AttnArgs.nsplit > 1).
+// The split ring (AttnArgs.nsplit > 1).
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ring_attn_bf16_split(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[Bf16Cfg<D, 4>::LDS];
   attn_bf16_body<D, 4, false, true>(a, smem);
 }
-
-// Staggered form: 8 waves x 32 query rows, one workgroup per CU, two K and
-// four V buffers.
-template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void ring_attn_bf16_pp(const AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[Bf16Cfg<D, 8>::LDS + Bf16Cfg<D, 8>::TILE];
-  attn_bf16_body<D, 8, true>(a, smem);
-}
-
-// ---------------------------------------------------------------------------
-// bf16 kernel, 64 query rows per wave
-// ---------------------------------------------------------------------------
-// Same arithmetic as ring_attn_bf16, but each wave owns 64 query rows (two
-// 32-row column blocks cb = 0, 1) and runs alone on its SIMD with the whole
-// register file (512 registers; the O^T accumulators live in AGPRs).  Every
-// K or V fragment read from LDS then feeds two matrix ops instead of one,
-// which halves LDS read traffic per FLOP, and a workgroup of four waves
-// covers 256 query rows, which halves the HBM/L2 -> LDS copies per FLOP.
-//
-// K/V move through LDS in stages of 64 keys; the wave computes in sub-tiles
-// of 32 keys.  Sub-step j (two per stage) runs
-//   phase B: S^T(j+1) = K(j+1) Q^T on the matrix cores, interleaved with
-//            the exponentials of tile j and their bf16 copy P(j);
-//   phase C: O^T += V(j)^T P(j)^T, interleaved with the denominator of P(j),
-//            the mask and row max of S(j+1), the choice of its reference max
-//            and the scaled, shifted scores of S(j+1).
-// A rescale of O and l forced by a new reference max (rare, see the lazy
-// reference above) is applied at the start of the next sub-step, after the
-// P V products of the old reference were issued.
-//
-// Stage pipeline (n = stage of the iteration): LDS holds K(n), K(n+1), V(n);
-// the iteration issues the copies of K(n+3) and V(n+2) and, before its
-// closing barrier, waits for those of K(n+2) and V(n+1), issued one
-// iteration earlier: every copy has two iterations to land.  Four K and
-// three V buffers (112 KiB at D = 128).
-template <int D>
-struct W64Cfg {
-  static constexpr int NW = 4;                    // waves per workgroup
-  static constexpr int THREADS = 64 * NW;
-  static constexpr int WR = 64;                   // query rows per wave
-  static constexpr int BR = NW * WR;              // query rows per workgroup
-  static constexpr int BC = 64;                   // keys per LDS stage
-  static constexpr int ROWB = D * 2;              // bytes per key row in LDS
-  static constexpr int TILE = BC * ROWB;          // one K or V stage
-  static constexpr int NKB = 4, NVB = 3;          // stage buffers
-  static constexpr int KB = 0, VB = NKB * TILE;
-  static constexpr int LDS = (NKB + NVB) * TILE;
-  static constexpr int CHUNKS = D / 8;
-  static constexpr int DMA = TILE / 1024 / NW;    // 1 KiB copies per wave per stage
-  static constexpr int NC = D / 16;               // k-steps of S^T
-  static constexpr int NDT = D / 32;              // 32-row d tiles of O^T
-  static constexpr int KPF = 4;                   // K fragment lead (fragments)
-  static constexpr int VPF = 3;                   // V fragment lead (fragments)
-};
-
-// A 64-key stage of the visited sequence with everything the loop needs
-// about it.  The kernel arguments (the block table) are read only when the
-// sequence enters a new block; inside a block a stage advances by pointer
-// arithmetic.  Positions are 32-bit here (the host routes longer sequences
-// to the other kernels).
-struct Stage {
-  int blk;           // visited block, a.nblk once past the end
-  int t, n;          // stage t of the n this workgroup visits in the block
-  int kp;            // global position of the stage's first key
-  int rows;          // rows of the block from that key on (>= 64: a full stage)
-  const char* k;     // K of this (batch, head) from that key on
-  const char* v;     // V likewise
-};
-
-__device__ __forceinline__ Stage stage_enter(const AttnArgs& a, int blk, long long q_hi, int b,
-                                             int h, int D2, int HD2) {
-  Stage s;
-  s.blk = blk;
-  s.t = 0;
-  s.n = 0;
-  while (s.blk < a.nblk && (s.n = tiles_of<64>(a, s.blk, q_hi)) == 0) ++s.blk;
-  s.kp = 0;
-  s.rows = 0;
-  s.k = s.v = nullptr;
-  if (s.blk < a.nblk) {
-    const KVBlock& kb = a.blk[s.blk];
-    const long long off = (long long)b * a.kv_rows_b * HD2 + (long long)h * D2;
-    s.kp = (int)kb.k_pos0;
-    s.rows = kb.len;
-    s.k = (const char*)kb.k + off;
-    s.v = (const char*)kb.v + off;
-  }
-  return s;
-}
-
-__device__ __forceinline__ Stage stage_next(const AttnArgs& a, Stage s, long long q_hi, int b,
-                                            int h, int D2, int HD2) {
-  if (s.blk >= a.nblk) return s;
-  if (++s.t < s.n) {
-    s.kp += 64;
-    s.rows -= 64;
-    s.k += 64LL * HD2;
-    s.v += 64LL * HD2;
-    return s;
-  }
-  return stage_enter(a, s.blk + 1, q_hi, b, h, D2, HD2);
-}
-
-// Copy one stage (64 key rows of K or V from src) into LDS at dst; each wave
-// copies its share.  Rows past the block's end come back as zeros from the
-// buffer range check.  lds_wave is this wave's first 1 KiB slot (uniform).
-template <int D>
-__device__ __forceinline__ void copy_stage(const char* src, int rows, int HD2, const int* voff,
-                                           unsigned dst) {
-  using C = W64Cfg<D>;
-  const int nrec = (min(rows, C::BC) - 1) * HD2 + D * 2;
-  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, nrec, kRsrcWord3);
-#pragma unroll
-  for (int i = 0; i < C::DMA; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(size_t)(dst + i * 1024), 16,
-                                             voff[i], 0, 0, 0);
-}
-
-// A stage copy to be issued during a sub-step, one 1 KiB instruction at a
-// time between matrix ops, so that the wave's vector-memory issue hides
-// under them (issued back to back, the copies stall a wave that has no
-// other to cover for it).
-struct StageCopy {
-  __amdgpu_buffer_rsrc_t rs;
-  const int* voff;
-  unsigned dst;    // this wave's first 1 KiB slot
-  bool on;
-};
-
-template <int D>
-__device__ __forceinline__ StageCopy stage_copy(const char* src, int rows, int HD2,
-                                                const int* voff, unsigned dst, bool on) {
-  using C = W64Cfg<D>;
-  StageCopy c;
-  const int nrec = (min(rows, C::BC) - 1) * HD2 + D * 2;
-  c.rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, nrec, kRsrcWord3);
-  c.voff = voff;
-  c.dst = dst;
-  c.on = on;
-  return c;
-}
-
-__device__ __forceinline__ void stage_copy_part(const StageCopy& c, int i) {
-  if (c.on)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, (lds_void_ptr)(size_t)(c.dst + i * 1024), 16,
-                                             c.voff[i], 0, 0, 0);
-}
-
-// One 32-key sub-tile as this wave sees it.
-struct Sub {
-  bool mask;       // some (row, key) pair of it must be masked (all, if dead)
-  int kp;          // global position of its first key
-  int klim;        // keys [0, klim) exist, are not padding and may be visible
-};
-
-__device__ __forceinline__ Sub sub_info(const Stage& st, int sub, bool causal, int valid_len,
-                                        int wq_lo, int wq_hi, bool wave_live) {
-  Sub s{true, 0, 0};  // dead: every pair masked
-  if (!wave_live || st.n == 0) return s;
-  s.kp = st.kp + 32 * sub;
-  int lim = min(st.rows - 32 * sub, valid_len - s.kp);
-  lim = min(lim, 32);
-  const bool live = lim > 0 && !(causal && s.kp > wq_hi);
-  s.klim = live ? lim : 0;
-  s.mask = !live || lim < 32 || (causal && s.kp + 31 > wq_lo);
-  return s;
-}
-
-template <int D>
-struct W64State {
-  using C = W64Cfg<D>;
-  bf16x8 qf[2][C::NC];     // Q^T fragments of the two column blocks
-  f32x16 oacc[2][C::NDT];  // O^T accumulators (unnormalised u)
-  float m_ref[2];          // reference max (base 2), -inf before any key
-  float m_true[2];         // exact running max (base 2)
-  float m_use[2];          // shift applied to the scores in flight
-  float alpha[2];          // pending rescale factor of O and l
-  float l_run[2];          // this lane's half of sum of bf16(2^(s - m_ref))
-  int kaddr[C::NC];
-  int vaddr[C::NDT];
-  int voffk[C::DMA];
-  int voffv[C::DMA];
-};
-
-// Mask of S^T for column block cb of a sub-tile: key j (0..31) of lane
-// (col, half) at register v is 8*(v/4) + v%4 + 4*half; it is masked when
-// j >= klim or, causal, when its position exceeds the query's.
-__device__ __forceinline__ void mask_sub(f32x16& s, const Sub& st, bool causal, int wq_lo,
-                                         int cb, int col, int half) {
-  int t = st.klim - 1 - 4 * half;
-  if (causal) {
-    const int dc = min(64, max(-64, wq_lo + 32 * cb - st.kp));
-    t = min(t, max(-1, dc + col - 4 * half));
-  }
-#pragma unroll
-  for (int v = 0; v < 16; ++v)
-    if (8 * (v >> 2) + (v & 3) > t) s[v] = -INFINITY;
-}
-
-// max(a, b, c) in one instruction.  Written as assembly because the
-// compiler's fmaxf first quiets signalling NaNs (an extra v_max per operand)
-// for values it cannot prove canonical, such as matrix-core results.
-__device__ __forceinline__ float vmax3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-// S^T = K Q^T products with the accumulator in VGPRs, written as assembly.
-// The compiler would put every matrix-core accumulator of this kernel in
-// AGPRs (it needs more than 256 registers), and the scores would then have
-// to be copied out before any vector instruction could read them.  As the
-// compiler does not see these as matrix ops, the reader of a result must
-// first let the matrix pipe drain (mfma_results_ready); dependent products
-// on the same accumulator need no wait.
-__device__ __forceinline__ void mfma_v_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_v_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-// 16 wait states: more than an 8-pass matrix op needs before a vector
-// instruction may read its result.
-__device__ __forceinline__ void mfma_results_ready() {
-  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-}
-
-__device__ __forceinline__ float max16(const f32x16& s) {
-  float a = fmaxf(fmaxf(s[0], s[1]), s[2]), b = fmaxf(fmaxf(s[3], s[4]), s[5]);
-  float c = fmaxf(fmaxf(s[6], s[7]), s[8]), d = fmaxf(fmaxf(s[9], s[10]), s[11]);
-  float e = fmaxf(fmaxf(s[12], s[13]), s[14]);
-  return fmaxf(fmaxf(fmaxf(a, b), fmaxf(c, d)), fmaxf(e, s[15]));
-}
-
-// Row max of the (masked) scores of the next sub-tile and the choice of
-// its reference ([RA] §3.2 with the lazy reference): sets m_use and, when
-// the reference moves, alpha and the returned flag.
-template <int D>
-__device__ __forceinline__ bool decide(W64State<D>& w, const float (&mlane)[2], float c_scale) {
-  float mx[2];
-  bool need[2];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    mx[cb] = pair_max(mlane[cb]) * c_scale;
-    w.m_true[cb] = fmaxf(w.m_true[cb], mx[cb]);
-    need[cb] = mx[cb] > w.m_ref[cb] + kRescaleSlack;
-  }
-  const bool any = __builtin_amdgcn_ballot_w64(need[0] || need[1]) != 0;
-  if (any) {
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      w.alpha[cb] = need[cb] ? fast_exp2(w.m_ref[cb] - mx[cb]) : 1.0f;
-      w.m_ref[cb] = need[cb] ? mx[cb] : w.m_ref[cb];
-    }
-  }
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) w.m_use[cb] = w.m_ref[cb] == -INFINITY ? 0.0f : w.m_ref[cb];
-  return any;
-}
-
-// acc *= alpha for an accumulator held in AGPRs.  The product is formed in
-// inline assembly on each AGPR in place, so the accumulator never has to
-// leave the AGPR file (vector ALU instructions cannot name AGPRs).
-__device__ __forceinline__ void scale_agpr(f32x16& acc, float alpha) {
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    float x = acc[v], t;
-    asm volatile(
-        "v_accvgpr_read_b32 %1, %0\n\t"
-        "v_mul_f32 %1, %1, %2\n\t"
-        "v_accvgpr_write_b32 %0, %1"
-        : "+a"(x), "=&v"(t)
-        : "v"(alpha));
-    acc[v] = x;
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void apply_rescale(W64State<D>& w) {
-  using C = W64Cfg<D>;
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    w.l_run[cb] *= w.alpha[cb];
-#pragma unroll
-    for (int i = 0; i < C::NDT; ++i) scale_agpr(w.oacc[cb][i], w.alpha[cb]);
-  }
-}
-
-// S^T of one sub-tile (no interleave): K rows at LDS offset kofs; results
-// readable after mfma_results_ready().
-template <int D>
-__device__ __forceinline__ void scores_sub(char* smem, int kofs, const W64State<D>& w,
-                                           f32x16 (&s)[2]) {
-  using C = W64Cfg<D>;
-#pragma unroll
-  for (int c = 0; c < C::NC; ++c) {
-    const bf16x8 kf = *(const bf16x8*)(smem + kofs + w.kaddr[c]);
-    if (c == 0) {
-      mfma_v_first(s[0], kf, w.qf[0][c]);
-      mfma_v_first(s[1], kf, w.qf[1][c]);
-    } else {
-      mfma_v_acc(s[0], kf, w.qf[0][c]);
-      mfma_v_acc(s[1], kf, w.qf[1][c]);
-    }
-  }
-}
-
-// One sub-step.  s_cur holds the raw scores of sub-tile j (cur, masked,
-// reference already chosen), s_nxt receives S^T of sub-tile j+1 (nxt) from
-// the K rows at LDS offset kofs; P(j) V(j) uses the V rows at LDS offset
-// vofs (32 keys).  The code has no branch on liveness: a sub-tile that is
-// dead for this wave is masked entirely (its scores become -inf, its
-// weights 0), which keeps the O^T accumulators in one register class across
-// the loop.  The V rows of cur always belong to a copied stage (zero-filled
-// past a block's end), so 0 * V stays 0; the K rows of a dead nxt may be
-// stale, but are always rows of a copied stage, and the mask replaces every
-// score they produce.
-//
-// Operand reads run ahead across phase boundaries: the first K fragments of
-// a sub-step are read (into kf) during the previous sub-step's last matrix
-// ops, the first V fragments of phase C during phase B's last ones.
-template <int D>
-__device__ __forceinline__ void w64_substep(const AttnArgs& a, char* smem, W64State<D>& w,
-                                            f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
-                                            bf16x8 (&kf)[W64Cfg<D>::KPF + 1], const Sub& nxt,
-                                            int kofs, int kofs_next, unsigned vofs,
-                                            const StageCopy& cp, bool& pending, int wq_lo,
-                                            int col, int half) {
-  using C = W64Cfg<D>;
-  constexpr int NF = 2 * C::NDT;         // V fragments (G, dt) of the sub-tile
-  constexpr int VPF = C::VPF;
-  const float c_scale = a.scale_log2;
-  if (pending) {  // the reference moved when cur's reference was chosen
-    apply_rescale(w);
-    pending = false;
-  }
-  s16x8 vr[VPF + 1];
-  auto vread = [&](auto fc) {
-    constexpr int f = decltype(fc)::value;
-    constexpr int off = (f / C::NDT) * 16 * C::ROWB;
-    const unsigned base = vofs + w.vaddr[f % C::NDT];
-    const s16x4 lo = lds_read_tr16<off>(base);
-    const s16x4 hi = lds_read_tr16<off + 8 * C::ROWB>(base);
-    vr[f % (VPF + 1)] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
-  // ---- phase B: S^T(nxt) alongside the weights P(cur) ----
-  // The weights go through three stages one matrix op apart, so that no
-  // vector instruction waits on the one just before it: pair x (scores 2x,
-  // 2x+1: block x / 8, registers 2 (x % 8), +1) is scaled and shifted
-  // (t = s * scale - m_use) at op x / PPS, exponentiated at the next op and
-  // rounded to bf16 at the one after; the last pairs finish under the first
-  // ops of phase C.
-  constexpr int NSTEP = 2 * C::NC;       // phase B matrix ops (k-step c, block cb)
-  constexpr int PPS = 16 / NSTEP;        // weight pairs per op
-  bf16x8 pb[2][2];
-  float tq[3][PPS][2], eq[3][PPS][2];
-  auto w_stage = [&](auto ic) {  // the weight stages that belong to op i
-    constexpr int i = decltype(ic)::value;
-    static_for<0, PPS>([&](auto uc) {
-      constexpr int u = decltype(uc)::value;
-      // (each stage's results are pinned to its op: left alone, the
-      // compiler sinks the whole chain to the first use in phase C)
-      if constexpr (i >= 2 && i - 2 < NSTEP) {  // round to bf16
-        constexpr int x = (i - 2) * PPS + u, eb = x >> 3, v = 2 * (x & 7);
-        pb[eb][v >> 3][v & 7] = (__bf16)eq[(i - 2) % 3][u][0];
-        pb[eb][v >> 3][(v & 7) + 1] = (__bf16)eq[(i - 2) % 3][u][1];
-        asm volatile("" ::"v"(pb[eb][v >> 3]));
-      }
-      if constexpr (i >= 1 && i - 1 < NSTEP) {  // exponentiate
-        eq[(i - 1) % 3][u][0] = fast_exp2(tq[(i - 1) % 3][u][0]);
-        eq[(i - 1) % 3][u][1] = fast_exp2(tq[(i - 1) % 3][u][1]);
-        asm volatile("" ::"v"(eq[(i - 1) % 3][u][0]), "v"(eq[(i - 1) % 3][u][1]));
-      }
-      if constexpr (i < NSTEP) {  // scale and shift
-        constexpr int x = i * PPS + u, eb = x >> 3, v = 2 * (x & 7);
-        tq[i % 3][u][0] = fmaf(s_cur[eb][v], c_scale, -w.m_use[eb]);
-        tq[i % 3][u][1] = fmaf(s_cur[eb][v + 1], c_scale, -w.m_use[eb]);
-        asm volatile("" ::"v"(tq[i % 3][u][0]), "v"(tq[i % 3][u][1]));
-      }
-    });
-  };
-  {
-    constexpr int PF = C::KPF;
-    auto kread = [&](int c) -> bf16x8 { return *(const bf16x8*)(smem + kofs + w.kaddr[c]); };
-    static_for<0, NSTEP>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      constexpr int c = i >> 1, cb = i & 1;
-      if constexpr (cb == 0 && c + PF < C::NC) kf[(c + PF) % (PF + 1)] = kread(c + PF);
-      if constexpr (c == 0) mfma_v_first(s_nxt[cb], kf[c % (PF + 1)], w.qf[cb][c]);
-      else mfma_v_acc(s_nxt[cb], kf[c % (PF + 1)], w.qf[cb][c]);
-      w_stage(ic);
-      // the last K fragment is in registers: start phase C's V reads
-      if constexpr (i == NSTEP - 2) static_for<0, VPF>([&](auto fc) { vread(fc); });
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  }
-  mfma_results_ready();
-  if (nxt.mask) {  // diagonal, ragged or dead sub-tile
-    mask_sub(s_nxt[0], nxt, a.causal, wq_lo, 0, col, half);
-    mask_sub(s_nxt[1], nxt, a.causal, wq_lo, 1, col, half);
-  }
-  // ---- phase C: O^T += V(cur)^T P(cur)^T alongside the max of nxt (first
-  // half of the ops) and the denominator of P(cur) (second half) ----
-  {
-    constexpr int NJ = 2 * NF;           // matrix ops (fragment, block cb)
-    constexpr int PF = VPF;
-    float lp[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-    float mxp[2] = {-INFINITY, -INFINITY};  // this lane's max of nxt per block
-    auto pv_op = [&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      constexpr int f = j / 2, cb = j % 2;
-      if constexpr (cb == 0) {
-        if constexpr (f + PF < NF) vread(std::integral_constant<int, f + PF>{});
-        constexpr int later = 2 * ((f + PF < NF ? f + PF : NF - 1) - f);
-        claim_lds<later>(vr[f % (PF + 1)]);
-      }
-      bf16x8 vf;
-      __builtin_memcpy(&vf, &vr[f % (PF + 1)], 16);
-      constexpr int G = f / C::NDT, dt = f % C::NDT;
-      w.oacc[cb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[cb][G], w.oacc[cb][dt],
-                                                               0, 0, 0);
-    };
-    constexpr int NH = NJ / 2;
-    static_for<0, NH>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      pv_op(jc);
-      // the last weight pairs of cur: needed from op 2 NDT + 1 on
-      if constexpr (j < 2) w_stage(std::integral_constant<int, NSTEP + j>{});
-      if constexpr (j == 1)
-        asm volatile("" ::"v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[1][0]), "v"(pb[1][1]));
-      if constexpr ((j & 1) && (j >> 1) < C::DMA) stage_copy_part(cp, j >> 1);
-      // 32 / NH scores of nxt into its row max (score x: block x / 16)
-      static_for<0, 32 / NH / 2>([&](auto yc) {
-        constexpr int x = j * 32 / NH + 2 * decltype(yc)::value;
-        constexpr int mb = x >> 4, q = x & 15;
-        mxp[mb] = vmax3(mxp[mb], s_nxt[mb][q], s_nxt[mb][q + 1]);
-      });
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    pending = decide(w, mxp, c_scale);
-    static_for<NH, NJ>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      pv_op(jc);
-      // 16 / NH bf16 pairs of P(cur) into the denominator (pair x: block
-      // x / 8, fragment (x / 4) % 2, elements 2 (x % 4), +1)
-      static_for<(j - NH) * 16 / NH, (j - NH + 1) * 16 / NH>([&](auto xc) {
-        constexpr int x = decltype(xc)::value;
-        constexpr int eb = x >> 3, G2 = (x >> 2) & 1, e = 2 * (x & 3);
-        const bf16x2 pr = {pb[eb][G2][e], pb[eb][G2][e + 1]};
-        lp[eb][x & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, lp[eb][x & 1], false);
-      });
-      // every V read is claimed: start the next sub-step's K reads
-      if constexpr (j == NJ - 2) {
-#pragma unroll
-        for (int c = 0; c < C::KPF; ++c)
-          kf[c] = *(const bf16x8*)(smem + kofs_next + w.kaddr[c]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    // keep the denominator updates under the matrix ops as well
-    asm volatile("" ::"v"(lp[0][0]), "v"(lp[0][1]), "v"(lp[1][0]), "v"(lp[1][1]));
-    w.l_run[0] += lp[0][0] + lp[0][1];
-    w.l_run[1] += lp[1][0] + lp[1][1];
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void ring_attn_bf16_w64(const AttnArgs a) {
-  using C = W64Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int col = lane & 31;
-  const int half = lane >> 5;
-
-  int b, h, qt;
-  tile_coords(a, b, h, qt);
-  const int row0 = qt * C::BR;
-  const int rows_here = min(C::BR, a.Sq - row0);
-  const long long q_hi = qpos(a, row0 + rows_here - 1);
-  const int wrow0 = row0 + wave * C::WR;
-  const int wrows = min(C::WR, a.Sq - wrow0);
-  const bool wave_live = wrows > 0;
-  const int wq_lo = (int)qpos(a, wrow0);
-  const int wq_hi = wq_lo + wrows - 1;
-  const int valid_len = a.valid_len > 0x7fffffffLL ? 0x7fffffff : (int)a.valid_len;
-  const bool causal = a.causal != 0;
-  const long long HD = (long long)a.H * D;
-  const int D2 = D * 2;
-  const int HD2 = a.Hkv * D2;
-  const int hk = h / (a.H / a.Hkv);  // K/V head of this query head
-
-  W64State<D> w;
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int r = wrow0 + 32 * cb + col;
-    const __bf16* qp = (const __bf16*)a.q + ((long long)b * a.Sq + r) * HD + (long long)h * D;
-#pragma unroll
-    for (int c = 0; c < C::NC; ++c)
-      w.qf[cb][c] = r < a.Sq ? *(const bf16x8*)(qp + 16 * c + 8 * half) : bf16x8{};
-  }
-#pragma unroll
-  for (int i = 0; i < C::DMA; ++i) {
-    const int p = (wave * C::DMA + i) * 64 + lane;
-    const int r = p / C::CHUNKS, pc = p % C::CHUNKS;
-    w.voffk[i] = r * HD2 + swz_k<D>(r, pc) * 16;
-    w.voffv[i] = r * HD2 + swz_v<D>(r, pc) * 16;
-  }
-#pragma unroll
-  for (int c = 0; c < C::NC; ++c) w.kaddr[c] = col * C::ROWB + swz_k<D>(col, 2 * c + half) * 16;
-  {
-    const int j = lane & 15, e = j >> 2, q = j & 3, g = lane >> 4;
-    const int kl = 4 * half + e;
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) {
-      const int d0 = 32 * dt + 16 * (g & 1) + 4 * q;
-      w.vaddr[dt] = kl * C::ROWB + swz_v<D>(kl, d0 >> 3) * 16 + (d0 & 7) * 2;
-    }
-  }
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-#pragma unroll
-    for (int i = 0; i < C::NDT; ++i) w.oacc[cb][i] = f32x16{};
-    w.m_ref[cb] = -INFINITY;
-    w.m_true[cb] = -INFINITY;
-    w.m_use[cb] = 0.0f;
-    w.alpha[cb] = 1.0f;
-    w.l_run[cb] = 0.0f;
-  }
-  const unsigned smem_lds = (unsigned)(size_t)(lds_void_ptr)smem;
-  // this wave's 1 KiB copy slots within a stage buffer
-  const unsigned kdst0 = smem_lds + C::KB + wave * C::DMA * 1024;
-  const unsigned vdst0 = smem_lds + C::VB + wave * C::DMA * 1024;
-
-  // prologue: stages 0..2 of K, 0..1 of V; scores of sub-tile 0
-  Stage t0 = stage_enter(a, 0, q_hi, b, hk, D2, HD2);
-  Stage t1 = stage_next(a, t0, q_hi, b, hk, D2, HD2);
-  Stage t2 = stage_next(a, t1, q_hi, b, hk, D2, HD2);
-  Stage t3 = stage_next(a, t2, q_hi, b, hk, D2, HD2);
-  if (t0.blk < a.nblk) {
-    copy_stage<D>(t0.k, t0.rows, HD2, w.voffk, kdst0);
-    copy_stage<D>(t0.v, t0.rows, HD2, w.voffv, vdst0);
-  }
-  if (t1.blk < a.nblk) {
-    copy_stage<D>(t1.k, t1.rows, HD2, w.voffk, kdst0 + C::TILE);
-    copy_stage<D>(t1.v, t1.rows, HD2, w.voffv, vdst0 + C::TILE);
-  }
-  if (t2.blk < a.nblk) copy_stage<D>(t2.k, t2.rows, HD2, w.voffk, kdst0 + 2 * C::TILE);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  f32x16 sA[2], sB[2];
-  bool pending = false;
-  if (t0.blk < a.nblk) {
-    const Sub s0 = sub_info(t0, 0, causal, valid_len, wq_lo, wq_hi, wave_live);
-    scores_sub<D>(smem, C::KB, w, sA);
-    mfma_results_ready();
-    if (s0.mask) {
-      mask_sub(sA[0], s0, causal, wq_lo, 0, col, half);
-      mask_sub(sA[1], s0, causal, wq_lo, 1, col, half);
-    }
-    const float ml[2] = {max16(sA[0]), max16(sA[1])};
-    decide(w, ml, a.scale_log2);  // nothing accumulated yet: no rescale
-  }
-
-  // K fragments of the first sub-step (stage 0, sub-tile 1)
-  bf16x8 kf[C::KPF + 1];
-#pragma unroll
-  for (int c = 0; c < C::KPF; ++c) kf[c] = *(const bf16x8*)(smem + C::KB + 32 * C::ROWB + w.kaddr[c]);
-  int kb0 = 0, vb0 = 0;  // K / V buffer of stage n
-  while (t0.blk < a.nblk) {
-    // copies of V(n+2) and K(n+3) into the buffers stage n-1 released,
-    // issued piecewise during the two sub-steps
-    const bool ck = t3.blk < a.nblk, cv = t2.blk < a.nblk;
-    const int vbuf = vb0 == 0 ? 2 : vb0 - 1;  // (n + 2) % 3
-    const StageCopy cpv =
-        stage_copy<D>(t2.v, t2.rows, HD2, w.voffv, vdst0 + vbuf * C::TILE, cv);
-    const StageCopy cpk =
-        stage_copy<D>(t3.k, t3.rows, HD2, w.voffk, kdst0 + ((kb0 + 3) & 3) * C::TILE, ck);
-    const Sub s01 = sub_info(t0, 1, causal, valid_len, wq_lo, wq_hi, wave_live);
-    const Sub s10 = sub_info(t1, 0, causal, valid_len, wq_lo, wq_hi, wave_live);
-    const int k_n = C::KB + kb0 * C::TILE;
-    // past the last stage nxt is dead: point it at rows that were copied
-    const int k_n1 = t1.blk < a.nblk ? C::KB + ((kb0 + 1) & 3) * C::TILE : k_n;
-    const unsigned v_n = smem_lds + C::VB + vb0 * C::TILE;
-    // sub-step 2n: S(stage n, sub 1), P V of (stage n, sub 0)
-    w64_substep<D>(a, smem, w, sA, sB, kf, s01, k_n + 32 * C::ROWB, k_n1, v_n, cpv, pending,
-                   wq_lo, col, half);
-    // sub-step 2n+1: S(stage n+1, sub 0), P V of (stage n, sub 1); its
-    // K(n+1) stays resident across the barrier, so the next sub-step's
-    // (stage n+1, sub-tile 1) K reads may start before it
-    w64_substep<D>(a, smem, w, sB, sA, kf, s10, k_n1, k_n1 + 32 * C::ROWB,
-                   v_n + 2 * 16 * C::ROWB, cpk, pending, wq_lo, col, half);
-    // this wave's copies of K(n+2) and V(n+1) landed; K(n+3), V(n+2) may fly
-    if (ck) wait_vmcnt<2 * C::DMA>();
-    else if (cv) wait_vmcnt<C::DMA>();
-    else wait_vmcnt<0>();
-    // every LDS read of K(n) and V(n) has been consumed by a matrix op; the
-    // K(n+1) reads still in flight target a buffer no copy overwrites next
-    asm volatile("s_barrier" ::: "memory");
-    t0 = t1;
-    t1 = t2;
-    t2 = t3;
-    t3 = stage_next(a, t3, q_hi, b, hk, D2, HD2);
-    kb0 = (kb0 + 1) & 3;
-    vb0 = vb0 == 2 ? 0 : vb0 + 1;
-  }
-  if (pending) apply_rescale(w);
-
-  // ---- epilogue: o = u / l, lse = m + ln l ([RA] §3.2; [SPD] §四) ----
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const float l_tot = pair_sum(w.l_run[cb]);
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const int r = wrow0 + 32 * cb + col;
-    if (r >= a.Sq) continue;
-    const long long ro = ((long long)b * a.Sq + r) * HD + (long long)h * D;
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * half;
-        const float x0 = w.oacc[cb][dt][4 * g + 0] * inv, x1 = w.oacc[cb][dt][4 * g + 1] * inv;
-        const float x2 = w.oacc[cb][dt][4 * g + 2] * inv, x3 = w.oacc[cb][dt][4 * g + 3] * inv;
-        if (a.o_fp32) {
-          *(float4*)((float*)a.o + ro + d) = float4{x0, x1, x2, x3};
-        } else {
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          bf16x4 y;
-          y[0] = (__bf16)x0; y[1] = (__bf16)x1; y[2] = (__bf16)x2; y[3] = (__bf16)x3;
-          *(bf16x4*)((__bf16*)a.o + ro + d) = y;
-        }
-      }
-    if (half == 0) {
-      const long long so = ((long long)b * a.Sq + r) * a.H + h;
-      const bool seen = l_tot > 0.0f;
-      if (a.lse) a.lse[so] = seen ? (w.m_ref[cb] + fast_log2(l_tot)) * kLn2 : -INFINITY;
-      if (a.m_out) a.m_out[so] = seen ? w.m_true[cb] * kLn2 : -INFINITY;
-      if (a.l_out) a.l_out[so] = seen ? l_tot * fast_exp2(w.m_ref[cb] - w.m_true[cb]) : 0.0f;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// bf16 kernel, producer / consumer waves
-// ---------------------------------------------------------------------------
-// Eight waves per workgroup = four (producer, consumer) pairs, each pair
-// owning 64 query rows, the pair's two waves sharing one SIMD.  The producer
-// holds Q and computes S^T = K Q^T, the mask, the row max, the reference
-// choice and the weights P = 2^(s - m) (bf16), which it hands to its
-// consumer through LDS; the consumer holds O^T and computes O^T += V^T P^T.
-// The softmax's vector work of one wave thus runs beside the other wave's
-// matrix ops on the same SIMD, while each K or V fragment read from LDS
-// still feeds two matrix ops (64 rows), as in the 64-row kernel.
-//
-// Steps run over 32-key sub-tiles t = 0, 1, ...: at step t the producer
-// chooses the reference of t (its rescale factor into alpha slot t % 3),
-// computes P(t) (into P buffer t % 2) and S^T(t+1); the consumer applies
-// alpha(t-1) to O and adds P(t-1) V(t-1).  A barrier ends each step.
-// K and V move through LDS in 64-key stages; at step 2n the producers copy
-// K(n+2) and the consumers V(n+1), each waited for at the end of step 2n+2:
-// three K and three V stage buffers.
-template <int D>
-struct WsCfg {
-  static constexpr int NP = 4;                    // pairs
-  static constexpr int THREADS = 128 * NP;        // 8 waves
-  static constexpr int WR = 64;                   // query rows per pair
-  static constexpr int BR = NP * WR;              // query rows per workgroup
-  static constexpr int BC = 64;                   // keys per LDS stage
-  static constexpr int ROWB = D * 2;
-  static constexpr int TILE = BC * ROWB;
-  static constexpr int NKB = 3, NVB = 3;
-  static constexpr int KB = 0, VB = NKB * TILE;
-  static constexpr int PBUF = 4 * 1024;           // one pair's P of a sub-tile
-  static constexpr int PB = VB + NVB * TILE;      // 2 x NP P buffers
-  static constexpr int ASLOT = 64 * 8;            // one pair's alpha (2 floats / lane)
-  static constexpr int AB = PB + 2 * NP * PBUF;   // 3 x NP alpha slots
-  static constexpr int LDS = AB + 3 * NP * ASLOT;
-  static constexpr int CHUNKS = D / 8;
-  static constexpr int DMA = TILE / 1024 / NP;    // 1 KiB copies per wave per stage
-  static constexpr int NC = D / 16;
-  static constexpr int NDT = D / 32;
-  static constexpr int VPF = 3;                   // V fragment lead (fragments)
-};
-static_assert(W64Cfg<128>::DMA == WsCfg<128>::DMA && W64Cfg<64>::DMA == WsCfg<64>::DMA,
-              "copy_stage is shared with the 64-row kernel");
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ s16x8 lds_read_b128_asm(unsigned addr_lds) {
-  s16x8 r;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr_lds));
-  return r;
-}
-__device__ __forceinline__ f32x2 lds_read_b64_asm(unsigned addr_lds) {
-  f32x2 r;
-  asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(addr_lds));
-  return r;
-}
-
-template <int D>
-struct WsProducer {
-  using C = WsCfg<D>;
-  bf16x8 qf[2][C::NC];
-  float m_ref[2], m_true[2], m_use[2];
-  int kaddr[C::NC];
-  int voff[C::DMA];
-};
-
-template <int D>
-struct WsConsumer {
-  using C = WsCfg<D>;
-  f32x16 oacc[2][C::NDT];
-  float l_run[2];          // this lane's half of sum of the bf16 weights
-  int vaddr[C::NDT];
-  int voff[C::DMA];
-};
-
-// Producer step t.  cur = sub-tile t (masked raw scores in s_cur), nxt =
-// t+1.  The matrix ops of S^T(nxt) (if has_nxt, from the K rows at kofs)
-// carry the vector work of cur: during the first quarter of them the row
-// max of cur and the choice of its reference ([RA] §3.2 with the lazy
-// reference; rescale factor alpha(t) into al_dst), during the rest the
-// weights P(cur) = bf16(2^(s * scale - m)), handed to the consumer at p_dst
-// (which sums them into the denominator).  The weights go through three stages
-// one step apart (scale and shift, exponential, bf16 and sum), so that no
-// instruction waits on the one just before it; every stage's results are
-// pinned to their op, as the compiler would otherwise sink the chain.
-template <int D>
-__device__ __forceinline__ void ws_produce(const AttnArgs& a, char* smem, WsProducer<D>& w,
-                                           const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
-                                           const Sub& nxt, bool has_nxt, int kofs, char* p_dst,
-                                           char* al_dst, int wq_lo, int lane, int col,
-                                           int half) {
-  using C = WsCfg<D>;
-  constexpr int NSTEP = 2 * C::NC;    // matrix ops (k-step c, block cb)
-  constexpr int NMAX = NSTEP / 4;     // ops carrying the row max
-  constexpr int NT = 18;              // weight pipeline times (16 pairs + 2)
-  const float c_scale = a.scale_log2;
-  bf16x8 pb[2][2];
-  float tq[16][2], eq[16][2];
-  float mq[2][2] = {{-INFINITY, -INFINITY}, {-INFINITY, -INFINITY}};
-  // row max: 32 scores of this lane, 32 / NMAX per op, two chains per block
-  auto max_part = [&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    static_for<0, 16 / NMAX>([&](auto yc) {
-      constexpr int x = (i * 16 / NMAX + decltype(yc)::value) * 2;  // score index, even
-      constexpr int mb = x >> 4, q = x & 15;
-      mq[mb][(q >> 1) & 1] = vmax3(mq[mb][(q >> 1) & 1], s_cur[mb][q], s_cur[mb][q + 1]);
-    });
-  };
-  auto decide_cur = [&]() {
-    float alpha[2] = {1.0f, 1.0f}, mx[2];
-    bool need[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      mx[cb] = pair_max(fmaxf(mq[cb][0], mq[cb][1])) * c_scale;
-      w.m_true[cb] = fmaxf(w.m_true[cb], mx[cb]);
-      need[cb] = mx[cb] > w.m_ref[cb] + kRescaleSlack;
-    }
-    if (__builtin_amdgcn_ballot_w64(need[0] || need[1])) {
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        alpha[cb] = need[cb] ? fast_exp2(w.m_ref[cb] - mx[cb]) : 1.0f;
-        w.m_ref[cb] = need[cb] ? mx[cb] : w.m_ref[cb];
-      }
-    }
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) w.m_use[cb] = w.m_ref[cb] == -INFINITY ? 0.0f : w.m_ref[cb];
-    *(f32x2*)(al_dst + lane * 8) = f32x2{alpha[0], alpha[1]};
-  };
-  // weight pipeline time k: bf16 of pair k-2, exponential of pair k-1,
-  // scale and shift of pair k (pair x: block x / 8, registers 2 (x % 8), +1)
-  auto w_time = [&](auto kc) {
-    constexpr int k = decltype(kc)::value;
-    if constexpr (k >= 2 && k - 2 < 16) {
-      constexpr int x = k - 2, eb = x >> 3, v = 2 * (x & 7);
-      pb[eb][v >> 3][v & 7] = (__bf16)eq[x][0];
-      pb[eb][v >> 3][(v & 7) + 1] = (__bf16)eq[x][1];
-      asm volatile("" ::"v"(pb[eb][v >> 3]));
-      // a complete fragment (cb, G) goes to the consumer right away, at
-      // p_dst + (2 cb + G) KiB + 16 lane, the layout it reads back
-      if constexpr ((x & 3) == 3)
-        *(bf16x8*)(p_dst + (2 * eb + (v >> 3)) * 1024 + lane * 16) = pb[eb][v >> 3];
-    }
-    if constexpr (k >= 1 && k - 1 < 16) {
-      constexpr int x = k - 1;
-      eq[x][0] = fast_exp2(tq[x][0]);
-      eq[x][1] = fast_exp2(tq[x][1]);
-      asm volatile("" ::"v"(eq[x][0]), "v"(eq[x][1]));
-    }
-    if constexpr (k < 16) {
-      constexpr int x = k, eb = x >> 3, v = 2 * (x & 7);
-      tq[x][0] = fmaf(s_cur[eb][v], c_scale, -w.m_use[eb]);
-      tq[x][1] = fmaf(s_cur[eb][v + 1], c_scale, -w.m_use[eb]);
-      asm volatile("" ::"v"(tq[x][0]), "v"(tq[x][1]));
-    }
-  };
-  // the pipeline times carried by op i (i >= NMAX)
-  auto w_part = [&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    constexpr int E = NSTEP - NMAX;
-    static_for<(i - NMAX) * NT / E, (i - NMAX + 1) * NT / E>([&](auto kc) { w_time(kc); });
-  };
-  if (has_nxt) {
-    constexpr int PF = 3;
-    bf16x8 kf[PF + 1];
-    auto kread = [&](int c) -> bf16x8 { return *(const bf16x8*)(smem + kofs + w.kaddr[c]); };
-#pragma unroll
-    for (int c = 0; c < PF; ++c) kf[c] = kread(c);
-    static_for<0, NSTEP>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      constexpr int c = i >> 1, cb = i & 1;
-      if constexpr (cb == 0 && c + PF < C::NC) kf[(c + PF) % (PF + 1)] = kread(c + PF);
-      s_nxt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c % (PF + 1)], w.qf[cb][c],
-                                                          c == 0 ? f32x16{} : s_nxt[cb], 0, 0, 0);
-      if constexpr (i < NMAX) max_part(ic);
-      if constexpr (i == NMAX - 1) decide_cur();
-      if constexpr (i >= NMAX) w_part(ic);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  } else {
-    static_for<0, NMAX>([&](auto ic) { max_part(ic); });
-    decide_cur();
-    static_for<0, NT>([&](auto kc) { w_time(kc); });
-  }
-  if (has_nxt && nxt.mask) {
-    mask_sub(s_nxt[0], nxt, a.causal, wq_lo, 0, col, half);
-    mask_sub(s_nxt[1], nxt, a.causal, wq_lo, 1, col, half);
-  }
-}
-
-// Consumer step: O^T *= alpha (when any row's reference moved), then
-// O^T += V^T P^T with P from the LDS buffer at p_src and V rows at vofs.
-template <int D>
-__device__ __forceinline__ void ws_consume(WsConsumer<D>& w, unsigned vofs, unsigned p_src,
-                                           unsigned al_src, int lane) {
-  using C = WsCfg<D>;
-  constexpr int NF = 2 * C::NDT;
-  constexpr int NJ = 2 * NF;
-  constexpr int PF = C::VPF;
-  const f32x2 al = lds_read_b64_asm(al_src + lane * 8);
-  s16x8 pr[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pr[i] = lds_read_b128_asm(p_src + i * 1024 + lane * 16);
-  s16x8 vr[PF + 1];
-  auto vread = [&](auto fc) {
-    constexpr int f = decltype(fc)::value;
-    constexpr int off = (f / C::NDT) * 16 * C::ROWB;
-    const unsigned base = vofs + w.vaddr[f % C::NDT];
-    const s16x4 lo = lds_read_tr16<off>(base);
-    const s16x4 hi = lds_read_tr16<off + 8 * C::ROWB>(base);
-    vr[f % (PF + 1)] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
-  static_for<0, PF>([&](auto fc) { vread(fc); });
-  f32x2 alc = al;
-  claim_lds<4 + 2 * PF>(alc);
-  if (__builtin_amdgcn_ballot_w64(alc[0] != 1.0f || alc[1] != 1.0f)) {
-    w.l_run[0] *= alc[0];
-    w.l_run[1] *= alc[1];
-#pragma unroll
-    for (int i = 0; i < C::NDT; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        w.oacc[0][i][v] *= alc[0];
-        w.oacc[1][i][v] *= alc[1];
-      }
-  }
-  claim_lds<3 + 2 * PF>(pr[0]);
-  claim_lds<2 + 2 * PF>(pr[1]);
-  claim_lds<1 + 2 * PF>(pr[2]);
-  claim_lds<2 * PF>(pr[3]);
-  bf16x8 pb[2][2];
-  __builtin_memcpy(&pb[0][0], &pr[0], 16);
-  __builtin_memcpy(&pb[0][1], &pr[1], 16);
-  __builtin_memcpy(&pb[1][0], &pr[2], 16);
-  __builtin_memcpy(&pb[1][1], &pr[3], 16);
-  float lp[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-  static_for<0, NJ>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    constexpr int f = j / 2, cb = j % 2;
-    // the denominator of P: 16 / NJ bf16 pairs per op (pair x: block x / 8,
-    // fragment (x / 4) % 2, elements 2 (x % 4), +1)
-    static_for<j * 16 / NJ, (j + 1) * 16 / NJ>([&](auto xc) {
-      constexpr int x = decltype(xc)::value;
-      constexpr int eb = x >> 3, G2 = (x >> 2) & 1, e = 2 * (x & 3);
-      const bf16x2 pq = {pb[eb][G2][e], pb[eb][G2][e + 1]};
-      lp[eb][x & 1] = __builtin_amdgcn_fdot2_f32_bf16(pq, kOnes2, lp[eb][x & 1], false);
-    });
-    if constexpr (cb == 0) {
-      if constexpr (f + PF < NF) vread(std::integral_constant<int, f + PF>{});
-      constexpr int later = 2 * ((f + PF < NF ? f + PF : NF - 1) - f);
-      claim_lds<later>(vr[f % (PF + 1)]);
-    }
-    bf16x8 vf;
-    __builtin_memcpy(&vf, &vr[f % (PF + 1)], 16);
-    constexpr int G = f / C::NDT, dt = f % C::NDT;
-    w.oacc[cb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[cb][G], w.oacc[cb][dt],
-                                                             0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  });
-  w.l_run[0] += lp[0][0] + lp[0][1];
-  w.l_run[1] += lp[1][0] + lp[1][1];
-}
-
-template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void ring_attn_bf16_ws(const AttnArgs a) {
-  using C = WsCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int col = lane & 31;
-  const int half = lane >> 5;
-  const bool producer = wave < C::NP;
-  const int pair = wave & (C::NP - 1);
-
-  int b, h, qt;
-  tile_coords(a, b, h, qt);
-  const int row0 = qt * C::BR;
-  const int rows_here = min(C::BR, a.Sq - row0);
-  const long long q_hi = qpos(a, row0 + rows_here - 1);
-  const int wrow0 = row0 + pair * C::WR;
-  const int wrows = min(C::WR, a.Sq - wrow0);
-  const bool wave_live = wrows > 0;
-  const int wq_lo = (int)qpos(a, wrow0);
-  const int wq_hi = wq_lo + wrows - 1;
-  const int valid_len = a.valid_len > 0x7fffffffLL ? 0x7fffffff : (int)a.valid_len;
-  const bool causal = a.causal != 0;
-  const long long HD = (long long)a.H * D;
-  const int D2 = D * 2;
-  const int HD2 = a.Hkv * D2;
-  const int hk = h / (a.H / a.Hkv);  // K/V head of this query head
-  const unsigned smem_lds = (unsigned)(size_t)(lds_void_ptr)smem;
-  // copy slots: producers copy K stages, consumers V stages
-  int voff[C::DMA];
-#pragma unroll
-  for (int i = 0; i < C::DMA; ++i) {
-    const int p = (pair * C::DMA + i) * 64 + lane;
-    const int r = p / C::CHUNKS, pc = p % C::CHUNKS;
-    voff[i] = r * HD2 + (producer ? swz_k<D>(r, pc) : swz_v<D>(r, pc)) * 16;
-  }
-  const unsigned cdst0 = smem_lds + (producer ? C::KB : C::VB) + pair * C::DMA * 1024;
-  char* const p_base = smem + C::PB + pair * C::PBUF;
-  char* const a_base = smem + C::AB + pair * C::ASLOT;
-
-  Stage c0 = stage_enter(a, 0, q_hi, b, hk, D2, HD2);    // stage n
-  Stage c1 = stage_next(a, c0, q_hi, b, hk, D2, HD2);    // n + 1
-  Stage c2 = stage_next(a, c1, q_hi, b, hk, D2, HD2);    // n + 2
-  // prologue copies: K(0), K(1) by the producers, V(0) by the consumers
-  if (producer) {
-    if (c0.blk < a.nblk) copy_stage<D>(c0.k, c0.rows, HD2, voff, cdst0);
-    if (c1.blk < a.nblk) copy_stage<D>(c1.k, c1.rows, HD2, voff, cdst0 + C::TILE);
-  } else {
-    if (c0.blk < a.nblk) copy_stage<D>(c0.v, c0.rows, HD2, voff, cdst0);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  if (producer) {
-    WsProducer<D> w;
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int r = wrow0 + 32 * cb + col;
-      const __bf16* qp = (const __bf16*)a.q + ((long long)b * a.Sq + r) * HD + (long long)h * D;
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c)
-        w.qf[cb][c] = r < a.Sq ? *(const bf16x8*)(qp + 16 * c + 8 * half) : bf16x8{};
-      w.m_ref[cb] = -INFINITY;
-      w.m_true[cb] = -INFINITY;
-      w.m_use[cb] = 0.0f;
-    }
-#pragma unroll
-    for (int c = 0; c < C::NC; ++c) w.kaddr[c] = col * C::ROWB + swz_k<D>(col, 2 * c + half) * 16;
-    f32x16 sA[2], sB[2];
-    if (c0.blk < a.nblk) {  // S^T of sub-tile 0, its reference
-      const Sub s0 = sub_info(c0, 0, causal, valid_len, wq_lo, wq_hi, wave_live);
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) sA[cb] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c) {
-        const bf16x8 kf = *(const bf16x8*)(smem + C::KB + w.kaddr[c]);
-        sA[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, w.qf[0][c], sA[0], 0, 0, 0);
-        sA[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, w.qf[1][c], sA[1], 0, 0, 0);
-      }
-      if (s0.mask) {
-        mask_sub(sA[0], s0, causal, wq_lo, 0, col, half);
-        mask_sub(sA[1], s0, causal, wq_lo, 1, col, half);
-      }
-    }
-    int kb0 = 0;  // K buffer of stage n
-    for (int n = 0;; ++n) {
-      // even step 2n: P(2n), S(2n+1); copy K(n+2)
-      const bool live = c0.blk < a.nblk;
-      const bool ck = c2.blk < a.nblk;
-      if (ck) copy_stage<D>(c2.k, c2.rows, HD2, voff, cdst0 + ((kb0 + 2) % 3) * C::TILE);
-      if (live) {
-        const Sub s01 = sub_info(c0, 1, causal, valid_len, wq_lo, wq_hi, wave_live);
-        ws_produce<D>(a, smem, w, sA, sB, s01, true, C::KB + kb0 * C::TILE + 32 * C::ROWB,
-                      p_base, a_base + ((2 * n) % 3) * C::NP * C::ASLOT, wq_lo, lane, col, half);
-      }
-      if (ck) wait_vmcnt<C::DMA>();
-      else wait_vmcnt<0>();
-      pipeline_barrier();
-      if (!live) break;
-      // odd step 2n+1: P(2n+1), S(2n+2)
-      {
-        const bool has = c1.blk < a.nblk;
-        const Sub s10 = sub_info(c1, 0, causal, valid_len, wq_lo, wq_hi, wave_live);
-        ws_produce<D>(a, smem, w, sB, sA, s10, has, C::KB + ((kb0 + 1) % 3) * C::TILE,
-                      p_base + C::NP * C::PBUF, a_base + ((2 * n + 1) % 3) * C::NP * C::ASLOT,
-                      wq_lo, lane, col, half);
-      }
-      pipeline_barrier();
-      c0 = c1;
-      c1 = c2;
-      c2 = stage_next(a, c2, q_hi, b, hk, D2, HD2);
-      kb0 = kb0 == 2 ? 0 : kb0 + 1;
-    }
-    // hand the reference and the exact max of every row to the consumer
-    if (half == 0) {
-      *(f32x2*)(a_base + col * 8) = f32x2{w.m_ref[0], w.m_ref[1]};
-      *(f32x2*)(a_base + 256 + col * 8) = f32x2{w.m_true[0], w.m_true[1]};
-    }
-    __syncthreads();
-  } else {
-    WsConsumer<D> w;
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-#pragma unroll
-      for (int i = 0; i < C::NDT; ++i) w.oacc[cb][i] = f32x16{};
-      w.l_run[cb] = 0.0f;
-    }
-    {
-      const int j = lane & 15, e = j >> 2, q = j & 3, g = lane >> 4;
-      const int kl = 4 * half + e;
-#pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt) {
-        const int d0 = 32 * dt + 16 * (g & 1) + 4 * q;
-        w.vaddr[dt] = kl * C::ROWB + swz_v<D>(kl, d0 >> 3) * 16 + (d0 & 7) * 2;
-      }
-    }
-    const unsigned p0 = (unsigned)(size_t)(lds_void_ptr)p_base;
-    const unsigned al0 = (unsigned)(size_t)(lds_void_ptr)a_base;
-    int vbp = 2;  // V buffer of stage n - 1
-    for (int n = 0;; ++n) {
-      // even step 2n: P(2n-1) V(2n-1); copy V(n+1)
-      const bool live = c0.blk < a.nblk;
-      const bool cv = c1.blk < a.nblk;
-      const int vb0 = vbp == 2 ? 0 : vbp + 1;
-      if (cv) copy_stage<D>(c1.v, c1.rows, HD2, voff, cdst0 + ((vb0 + 1) % 3) * C::TILE);
-      if (n > 0)
-        ws_consume<D>(w, smem_lds + C::VB + vbp * C::TILE + 32 * C::ROWB,
-                      p0 + C::NP * C::PBUF, al0 + ((2 * n - 1) % 3) * C::NP * C::ASLOT, lane);
-      if (cv) wait_vmcnt<C::DMA>();
-      else wait_vmcnt<0>();
-      pipeline_barrier();
-      if (!live) break;
-      // odd step 2n+1: P(2n) V(2n)
-      ws_consume<D>(w, smem_lds + C::VB + vb0 * C::TILE, p0,
-                    al0 + ((2 * n) % 3) * C::NP * C::ASLOT, lane);
-      pipeline_barrier();
-      c0 = c1;
-      c1 = c2;
-      c2 = stage_next(a, c2, q_hi, b, hk, D2, HD2);
-      vbp = vb0;
-    }
-    __syncthreads();  // the producer's reference and max
-    const f32x2 m_ref = *(const f32x2*)(a_base + col * 8);
-    const f32x2 m_true = *(const f32x2*)(a_base + 256 + col * 8);
-    // ---- epilogue: o = u / l, lse = m + ln l ([RA] §3.2; [SPD] §四) ----
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const float l_tot = pair_sum(w.l_run[cb]);
-      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-      const int r = wrow0 + 32 * cb + col;
-      if (half == 0 && r < a.Sq) {
-        const long long so = ((long long)b * a.Sq + r) * a.H + h;
-        const bool seen = l_tot > 0.0f;
-        if (a.lse) a.lse[so] = seen ? (m_ref[cb] + fast_log2(l_tot)) * kLn2 : -INFINITY;
-        if (a.m_out) a.m_out[so] = seen ? m_true[cb] * kLn2 : -INFINITY;
-        if (a.l_out) a.l_out[so] = seen ? l_tot * fast_exp2(m_ref[cb] - m_true[cb]) : 0.0f;
-      }
-      if (r >= a.Sq) continue;
-      const long long ro = ((long long)b * a.Sq + r) * HD + (long long)h * D;
-#pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = 32 * dt + 8 * g + 4 * half;
-          const float x0 = w.oacc[cb][dt][4 * g + 0] * inv, x1 = w.oacc[cb][dt][4 * g + 1] * inv;
-          const float x2 = w.oacc[cb][dt][4 * g + 2] * inv, x3 = w.oacc[cb][dt][4 * g + 3] * inv;
-          if (a.o_fp32) {
-            *(float4*)((float*)a.o + ro + d) = float4{x0, x1, x2, x3};
-          } else {
-            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-            bf16x4 y;
-            y[0] = (__bf16)x0; y[1] = (__bf16)x1; y[2] = (__bf16)x2; y[3] = (__bf16)x3;
-            *(bf16x4*)((__bf16*)a.o + ro + d) = y;
-          }
-        }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // fp32 kernel (no bf16 rounding anywhere; fp32 matrix-core products)
 // ---------------------------------------------------------------------------
@@ -2170,66 +1207,51 @@ void ring_attn_f32(const AttnArgs a) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-// Kernel choice for bf16 (RA_OPT_ATTN_KERNEL): 4 or 8 waves of 32 rows
-// (two waves per SIMD), 4 waves of 64 rows (one wave per SIMD), 4
-// producer / consumer pairs of 64 rows (two waves per SIMD), or the
-// ping-pong form of 8 waves of 32 rows.
-enum Bf16Kernel { K_BR128, K_BR256, K_W64, K_WS, K_PP };
-
-// The 64-row kernel keeps positions in 32 bits: usable when every query
-// and key position (plus a tile of slack) stays below 2^31.
-bool positions_fit_32(const AttnArgs& a) {
-  const long long lim = 0x7fffffffLL - 256;
-  if (qpos(a, a.Sq - 1) + 1 > lim) return false;
-  for (int i = 0; i < a.nblk; ++i)
-    if (a.blk[i].k_pos0 + a.blk[i].len > lim) return false;
-  return true;
+// Waves per bf16 workgroup (RA_OPT_ATTN_WAVES): 8 (256 query rows sharing
+// one K/V stream, half the copies per FLOP) once that still gives every
+// compute unit a workgroup, else 4 (128 rows, two workgroups per compute
+// unit).
+int bf16_waves(const AttnArgs& a) {
+  const int forced = ra::option(RA_OPT_ATTN_WAVES);
+  if (forced == 4 || forced == 8) return forced;
+  const long long wg8 = (long long)a.B * a.H * ((a.Sq + 255) / 256);
+  return wg8 >= 256 ? 8 : 4;
 }
 
-Bf16Kernel bf16_kernel(const AttnArgs& a) {
-  const int mode = ra::option(RA_OPT_ATTN_KERNEL);
-  if (mode == RA_KERNEL_BR128) return K_BR128;
-  if (mode == RA_KERNEL_BR256) return K_BR256;
-  if (mode == RA_KERNEL_W64) return positions_fit_32(a) ? K_W64 : K_BR128;
-  if (mode == RA_KERNEL_WS) return positions_fit_32(a) ? K_WS : K_BR128;
-  if (mode == RA_KERNEL_PP) return K_PP;
-  return K_BR128;
-}
-
-template <int NW>
-void launch_bf16(const AttnArgs& a, int D, dim3 grid, hipStream_t stream) {
-  if (D == 128) hipLaunchKernelGGL((ring_attn_bf16<128, NW>), grid, dim3(64 * NW), 0, stream, a);
-  else hipLaunchKernelGGL((ring_attn_bf16<64, NW>), grid, dim3(64 * NW), 0, stream, a);
+template <int D, int NW>
+void launch_bf16(const AttnArgs& a, bool ml, dim3 grid, hipStream_t stream) {
+  if (ml) hipLaunchKernelGGL((ring_attn_bf16<D, NW, true>), grid, dim3(64 * NW), 0, stream, a);
+  else hipLaunchKernelGGL((ring_attn_bf16<D, NW, false>), grid, dim3(64 * NW), 0, stream, a);
 }
 
 ra_status launch(AttnArgs& a, int D, ra_dtype dt, hipStream_t stream, const char* name) {
-  // a split ring runs on the 128-row kernel (its slots hold 128 rows)
   const bool split = a.nsplit > 1;
-  const Bf16Kernel kk = dt != RA_BF16 || split ? K_BR128 : bf16_kernel(a);
-  const int br = dt != RA_BF16 ? kBR : kk == K_BR128 ? 128 : 256;
+  // a split ring keeps 128-row workgroups (its partial slots hold 128 rows)
+  const int nw = dt == RA_BF16 && !split ? bf16_waves(a) : 4;
+  const int br = 32 * nw;
   a.n_qtiles = (a.Sq + br - 1) / br;
+  a.rowmax = ra::option(RA_OPT_ATTN_KERNEL) == RA_KERNEL_ROWMAX;
   const long long n_wg = (long long)a.B * a.H * a.n_qtiles * (split ? a.nsplit : 1);
   if (n_wg == 0) return RA_OK;
   if (n_wg > 0x7fffffffLL)
     return ra::fail(RA_ERR_UNSUPPORTED, "%s: too many query tiles", name);
+  for (int i = 0; i < a.nblk; ++i)
+    if (a.blk[i].len > (1 << 30))
+      return ra::fail(RA_ERR_UNSUPPORTED, "%s: K/V block of %d rows (at most 2^30)", name,
+                      a.blk[i].len);
   const dim3 grid((unsigned)n_wg);
   if (dt == RA_BF16) {
-    if (kk == K_W64) {
-      if (D == 128) hipLaunchKernelGGL(ring_attn_bf16_w64<128>, grid, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL(ring_attn_bf16_w64<64>, grid, dim3(256), 0, stream, a);
-    } else if (kk == K_WS) {
-      if (D == 128) hipLaunchKernelGGL(ring_attn_bf16_ws<128>, grid, dim3(512), 0, stream, a);
-      else hipLaunchKernelGGL(ring_attn_bf16_ws<64>, grid, dim3(512), 0, stream, a);
-    } else if (kk == K_PP) {
-      if (D == 128) hipLaunchKernelGGL(ring_attn_bf16_pp<128>, grid, dim3(512), 0, stream, a);
-      else hipLaunchKernelGGL(ring_attn_bf16_pp<64>, grid, dim3(512), 0, stream, a);
-    } else if (kk == K_BR256) {
-      launch_bf16<8>(a, D, grid, stream);
-    } else if (split) {
+    // m and l are tracked only when asked for
+    const bool ml = a.m_out != nullptr || a.l_out != nullptr;
+    if (split) {
       if (D == 128) hipLaunchKernelGGL(ring_attn_bf16_split<128>, grid, dim3(256), 0, stream, a);
       else hipLaunchKernelGGL(ring_attn_bf16_split<64>, grid, dim3(256), 0, stream, a);
+    } else if (nw == 8) {
+      if (D == 128) launch_bf16<128, 8>(a, ml, grid, stream);
+      else launch_bf16<64, 8>(a, ml, grid, stream);
     } else {
-      launch_bf16<4>(a, D, grid, stream);
+      if (D == 128) launch_bf16<128, 4>(a, ml, grid, stream);
+      else launch_bf16<64, 4>(a, ml, grid, stream);
     }
   } else {
     if (D == 128) hipLaunchKernelGGL(ring_attn_f32<128>, grid, dim3(kThreads), 0, stream, a);

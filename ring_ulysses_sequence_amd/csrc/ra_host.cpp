@@ -50,14 +50,20 @@ int block_class(long long q0, long long q1, long long k0, long long k1,
 
 extern "C" {
 
-int ra_abi_version(void) { return 1; }
+int ra_abi_version(void) { return 2; }
 
 ra_status ra_set_option(int opt, int value) {
   ra::clear_error();
   if (opt == RA_OPT_ATTN_KERNEL) {
-    if (value != RA_KERNEL_AUTO && value != RA_KERNEL_BR128 && value != RA_KERNEL_BR256 &&
-        value != RA_KERNEL_W64 && value != RA_KERNEL_WS && value != RA_KERNEL_PP)
+    if (value != RA_KERNEL_AUTO && value != RA_KERNEL_ROWMAX)
       return ra::fail(RA_ERR_RANGE, "ra_set_option: unknown kernel choice %d", value);
+    ra::g_options[opt].store(value, std::memory_order_relaxed);
+    return RA_OK;
+  }
+  if (opt == RA_OPT_ATTN_WAVES) {
+    if (value != 0 && value != 4 && value != 8)
+      return ra::fail(RA_ERR_RANGE, "ra_set_option: waves per workgroup must be 0, 4 or 8 "
+                      "(got %d)", value);
     ra::g_options[opt].store(value, std::memory_order_relaxed);
     return RA_OK;
   }

@@ -46,16 +46,18 @@ def gpu():
     torch.cuda.synchronize()
 
 
-@pytest.fixture(params=["br128", "br256", "w64", "ws", "pp"])
+@pytest.fixture(params=["auto", "rowmax-w4", "auto-w8", "rowmax-w8"])
 def variant(request):
-    """Run a bf16 test with each attention kernel forced (all compute the
-    same function with different tilings)."""
-    choice = {"br128": ra.RA_KERNEL_BR128, "br256": ra.RA_KERNEL_BR256,
-              "w64": ra.RA_KERNEL_W64, "ws": ra.RA_KERNEL_WS,
-              "pp": ra.RA_KERNEL_PP}[request.param]
-    ra.set_attn_kernel(choice)
+    """Run a bf16 test under each kernel configuration (all compute the same
+    function): the way of keeping the row max (the reference set once per
+    row with tiles over the weight bound redone, or the row max of every
+    tile) and the waves per workgroup (the library's choice, 4 or 8)."""
+    mx, _, wv = request.param.partition("-")
+    ra.set_attn_kernel({"auto": ra.RA_KERNEL_AUTO, "rowmax": ra.RA_KERNEL_ROWMAX}[mx])
+    ra.set_attn_waves({"": 0, "w4": 4, "w8": 8}[wv])
     yield request.param
     ra.set_attn_kernel(ra.RA_KERNEL_AUTO)
+    ra.set_attn_waves(0)
 
 
 def check_bf16(got, ref, what):

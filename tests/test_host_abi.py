@@ -41,18 +41,26 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert ra.abi_version() == 1
+    assert ra.abi_version() == 2
 
 
 def test_kernel_option(lib):
     assert ra.get_attn_kernel() == ra.RA_KERNEL_AUTO
-    for c in (ra.RA_KERNEL_BR128, ra.RA_KERNEL_BR256, ra.RA_KERNEL_W64, ra.RA_KERNEL_WS,
-              ra.RA_KERNEL_PP,
-              ra.RA_KERNEL_AUTO):
+    for c in (ra.RA_KERNEL_ROWMAX, ra.RA_KERNEL_AUTO):
         ra.set_attn_kernel(c)
         assert ra.get_attn_kernel() == c
-    with pytest.raises(RuntimeError):
-        ra.set_attn_kernel(7)
+    for bad in (2, 5, 7, -1):
+        with pytest.raises(RuntimeError):
+            ra.set_attn_kernel(bad)
+    assert ra.get_attn_kernel() == ra.RA_KERNEL_AUTO
+    assert ra.get_attn_waves() == 0
+    for wv in (4, 8, 0):
+        ra.set_attn_waves(wv)
+        assert ra.get_attn_waves() == wv
+    for bad in (1, 2, 16, -4):
+        with pytest.raises(RuntimeError):
+            ra.set_attn_waves(bad)
+    assert ra.get_attn_waves() == 0
     assert lib.ra_set_option(99, 0) == 4
 
 
@@ -303,3 +311,20 @@ def test_binding_refuses_cpu_tensors(lib):
         ra.block_attn_fwd(q, q, q)
     with pytest.raises(ValueError, match="GPU"):
         ra.seq2head(torch.zeros(2, 1, 4, 2, 8, dtype=torch.bfloat16))
+
+
+def test_binding_checks_output_buffers_before_the_library(lib):
+    """Caller-supplied outputs are checked for shape, dtype and device before
+    any pointer reaches the library, which cannot see buffer sizes."""
+    import torch
+    like = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    good = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    for bad, what in ((torch.zeros(1, 3, 2, 64, dtype=torch.bfloat16), "shape"),
+                      (torch.zeros(1, 4, 2, 64, dtype=torch.float32), "dtype"),
+                      (torch.zeros(1, 4, 2, 32, dtype=torch.bfloat16), "shape")):
+        with pytest.raises(ValueError, match=r"\(1, 4, 2, 64\)"):
+            ra._out(bad, "out", like.shape, like.dtype, like)
+    # a well-formed CPU buffer passes the shape check and is then refused as
+    # a host buffer
+    with pytest.raises(ValueError, match="GPU"):
+        ra._out(good, "out", like.shape, like.dtype, like)
