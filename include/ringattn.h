@@ -242,6 +242,25 @@ ra_status ra_ring_attn_fwd_split(const void* q_r, const void* const* k_blocks,
                                  int nsplit, float* ws, long long ws_floats,
                                  void* o, float* lse_opt, void* stream);
 
+/* ra_ring_attn_fwd_split for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and result, with the partials in a fixed
+ * device array of the library (32 MiB = 8 Mi floats per GPU, held until
+ * the process ends) instead of a caller workspace.  nsplit = 0 takes
+ * ra_ring_split_plan's choice, nsplit >= 1 that run count (RA_ERR_RANGE for
+ * nsplit < 0).  A plan of one run, and fp32 inputs, run the single pass.
+ * RA_ERR_RANGE, before any launch, when the plan needs more than 8 Mi
+ * floats (ra_ring_split_plan's ws_floats).  Calls no allocating routine.
+ * The array is shared by every call on a GPU and keeps the last call's
+ * contents; calls that overlap on one GPU (several streams or threads)
+ * race and must be serialised by the caller.  Other arguments and errors
+ * as ra_ring_attn_fwd_split. */
+ra_status ra_ring_attn_fwd_split_noalloc(const void* q_r, const void* const* k_blocks,
+                                         const void* const* v_blocks, int B, int Sb, int H,
+                                         int H_kv, int D, int P, int rank, ra_dtype dt,
+                                         float scale, int causal, long long valid_len,
+                                         int nsplit, void* o, float* lse_opt, void* stream);
+
 /* Host-only plan of the split ring for this share.  nsplit = 0 chooses:
  * as many runs per query tile as keep the B*H*ceil(Sb/128)*nsplit
  * workgroups within the device's 512 workgroup slots (two 128-row

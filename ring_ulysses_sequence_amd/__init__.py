@@ -43,7 +43,7 @@ EXPORTED = (
     "ra_zigzag_padded_len", "ra_zigzag_schedule", "ra_zigzag_attn_fwd", "ra_ring_attn_bwd",
     "ra_ring_attn_fwd_gqa", "ra_ring_attn_fwd_varlen", "ra_block_attn_bwd",
     "ra_ring_attn_fwd_split", "ra_ring_split_plan", "ra_zigzag_attn_bwd", "ra_ring_attn_bwd_gqa",
-    "ra_ring_attn_bwd_varlen",
+    "ra_ring_attn_bwd_varlen", "ra_ring_attn_fwd_split_noalloc",
 )
 
 _lib = None
@@ -116,6 +116,10 @@ def _load():
                                            c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                            c_int, c_float, c_int, c_ll, c_int, c_vp, c_ll, c_vp,
                                            c_vp, c_vp]),
+        "ra_ring_attn_fwd_split_noalloc": (c_int, [c_vp, ctypes.POINTER(c_vp),
+                                                   ctypes.POINTER(c_vp), c_int, c_int, c_int,
+                                                   c_int, c_int, c_int, c_int, c_int, c_float,
+                                                   c_int, c_ll, c_int, c_vp, c_vp, c_vp]),
         "ra_ring_split_plan": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_ll,
                                        c_int, ctypes.POINTER(c_ll)]),
         "ra_block_attn_bwd": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int,
@@ -405,6 +409,41 @@ def ring_attn_fwd(q_r, k_blocks: Sequence, v_blocks: Sequence, rank: int, *,
                                           dt, *args)
         _check(st, "ra_ring_attn_fwd_gqa")
     return o, lse
+
+
+def ring_attn_fwd_split_noalloc(q_r, k_blocks: Sequence, v_blocks: Sequence, rank: int, out,
+                                lse_out=None, *, causal: bool = False, valid_len: int = -1,
+                                scale: float = 0.0, nsplit: int = 0, stream=None):
+    """The split ring with its partials in the library's fixed device
+    scratch (ra_ring_attn_fwd_split_noalloc): nothing is allocated, so the
+    caller passes ``out`` (q_r's shape and dtype) and, optionally,
+    ``lse_out`` (fp32 [B, Sb, H]).  Calls on one GPU share the scratch and
+    must not overlap.  Returns (out, lse_out)."""
+    torch = _torch()
+    B, Sb, H, D = q_r.shape
+    P = len(k_blocks)
+    if len(v_blocks) != P:
+        raise ValueError("k_blocks and v_blocks differ in length")
+    if P > RA_MAX_P:
+        raise RuntimeError(f"P={P} exceeds {RA_MAX_P}")
+    dt = _dtype_code(q_r)
+    Hkv = k_blocks[0].shape[2] if P else H
+    kv_shape = (B, Sb, Hkv, D)
+    kp = (ctypes.c_void_p * max(P, 1))()
+    vp = (ctypes.c_void_p * max(P, 1))()
+    for j in range(P):
+        for t, n in ((k_blocks[j], "k"), (v_blocks[j], "v")):
+            if tuple(t.shape) != kv_shape or t.dtype != q_r.dtype:
+                raise ValueError(f"{n}_blocks[{j}] must be {kv_shape} of q_r's dtype")
+        kp[j] = _dev(k_blocks[j], f"k_blocks[{j}]", q_r).value
+        vp[j] = _dev(v_blocks[j], f"v_blocks[{j}]", q_r).value
+    st = _load().ra_ring_attn_fwd_split_noalloc(
+        _dev(q_r, "q_r"), kp, vp, B, Sb, H, Hkv, D, P, rank, dt, float(scale), int(causal),
+        valid_len, int(nsplit), _out(out, "out", q_r.shape, q_r.dtype, q_r),
+        _out(lse_out, "lse_out", (B, Sb, H), torch.float32, q_r) if lse_out is not None else None,
+        _stream(stream))
+    _check(st, "ra_ring_attn_fwd_split_noalloc")
+    return out, lse_out
 
 
 def ring_attn_fwd_varlen(q_r, k_blocks: Sequence, v_blocks: Sequence, rank: int,
@@ -721,7 +760,7 @@ __all__ = [
     "get_attn_waves", "padded_len", "shard_range", "classify_block", "ring_schedule",
     "block_attn_fwd", "ring_merge", "ring_attn_fwd", "seq2head", "head2seq",
     "zigzag_padded_len", "zigzag_schedule", "zigzag_attn_fwd", "ring_attn_bwd",
-    "ring_attn_fwd_varlen",
+    "ring_attn_fwd_varlen", "ring_attn_fwd_split_noalloc",
     "ring_attn_composable", "block_attn_bwd", "ring_split_plan", "zigzag_attn_bwd", "ring_attn_bwd_varlen",
     "EXPORTED", "LIB_PATH", "LibraryMissing",
     "RA_BF16", "RA_FP32", "RA_SKIP", "RA_FULL", "RA_DIAG", "RA_MAX_P", "RA_PAD_MULTIPLE",

@@ -30,6 +30,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "ra_internal.h"
@@ -1601,6 +1602,68 @@ extern "C" int ra_ring_split_plan(int B, int Sb, int H, int D, int P, int rank, 
   const int ns = split_plan(a, D, nsplit, need);
   if (ws_floats) *ws_floats = need;
   return ns;
+}
+
+// ---------------------------------------------------------------------------
+// Split ring without allocation: the workspace is a fixed device array
+// ---------------------------------------------------------------------------
+namespace {
+// Partials of the split ring (o and lse slots, as the caller's workspace
+// of ra_ring_attn_fwd_split) for callers that cannot allocate.  Every GPU
+// the library runs on holds its own copy until the process ends.
+constexpr long long kScratchFloats = 8LL << 20;  // 32 MiB
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+// Device address of this device's copy of `scratch`, looked up once per
+// device with that device current.  In host code the array's name is only
+// a stand-in for the symbol, never an address a kernel may be given.
+ra_status scratch_ptr(const char* name, float** out) {
+  static std::mutex mu;
+  static float* ptr[64] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64)
+    return ra::fail(RA_ERR_HIP, "%s: no current device (%s)", name, hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return ra::fail(RA_ERR_HIP, "%s: scratch address: %s", name, hipGetErrorString(e));
+    ptr[dev] = (float*)p;
+  }
+  *out = ptr[dev];
+  return RA_OK;
+}
+}  // namespace
+
+extern "C" ra_status ra_ring_attn_fwd_split_noalloc(const void* q_r, const void* const* k_blocks,
+                                                    const void* const* v_blocks, int B, int Sb,
+                                                    int H, int Hkv, int D, int P, int rank,
+                                                    ra_dtype dt, float scale, int causal,
+                                                    long long valid_len, int nsplit, void* o,
+                                                    float* lse_opt, void* stream) {
+  static const char* name = "ra_ring_attn_fwd_split_noalloc";
+  ra::clear_error();
+  if (nsplit < 0) return ra::fail(RA_ERR_RANGE, "%s: nsplit must be >= 0 (got %d)", name, nsplit);
+  long long need = 0;
+  int ns = 1;
+  if (dt == RA_BF16) {
+    ns = ra_ring_split_plan(B, Sb, H, D, P, rank, causal, valid_len, nsplit, &need);
+    if (ns < 0) return ra::fail(RA_ERR_SHAPE, "%s: %s", name, ra_last_error());
+  }
+  if (ns <= 1)  // the single pass needs no workspace
+    return ring_fwd(name, q_r, k_blocks, v_blocks, B, Sb, H, Hkv, D, P, rank, dt, scale, causal,
+                    valid_len, o, lse_opt, stream);
+  if (need > kScratchFloats)
+    return ra::fail(RA_ERR_RANGE, "%s: %d runs per query tile need %lld floats of workspace; "
+                    "the fixed scratch holds %lld (use ra_ring_attn_fwd_split with a workspace)",
+                    name, ns, need, kScratchFloats);
+  float* ws = nullptr;
+  ra_status st = scratch_ptr(name, &ws);
+  if (st != RA_OK) return st;
+  return ring_fwd(name, q_r, k_blocks, v_blocks, B, Sb, H, Hkv, D, P, rank, dt, scale, causal,
+                  valid_len, o, lse_opt, stream, ns, ws, kScratchFloats);
 }
 
 extern "C" ra_status ra_zigzag_attn_fwd(const void* q_r, const void* const* k_shares,
