@@ -58,7 +58,7 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_NAMES = {"auto": "ring_attn_bf16<128,false>", "rowmax": "ring_attn_bf16<128,false>"}
+KERNEL_NAMES = {"auto": "ring_attn_bf16<128,8,false>", "rowmax": "ring_attn_bf16<128,8,false>"}
 ATTN_SOURCE = os.path.join(ROOT, "ring_ulysses_sequence_amd", "csrc", "ra_attn.hip")
 
 

@@ -346,6 +346,9 @@ ra_status ra_block_attn_bwd(const void* q, const void* k, const void* v,
  *   dq_r          += scale * sum_j (P_j * (dO V_j^T - D)) K_j
  *   dk_blocks[j]  += scale * (P_j * (dO V_j^T - D))^T Q_r
  *   dv_blocks[j]  += P_j^T dO
+ * Padding queries (global position >= valid_len) are discarded outputs,
+ * not part of the loss: their rows of P are taken as zero, so whatever
+ * do_r holds there reaches no gradient and their dq rows get nothing.
  * All three are fp32 [B,Sb,H,D] device buffers, ACCUMULATED into (the
  * caller zeroes them; summing dk/dv over all ranks' calls gives the owners'
  * gradients, as the ring returns them).  dk_blocks / dv_blocks are HOST

@@ -40,9 +40,20 @@ from .attention import _f64, attention
 from .schedule import ring_sources, visible_mask
 
 
+def _discard_pad_rows(do, q_pos, valid_len):
+    """dO with the rows of padding queries (global position >= valid_len)
+    set to zero: padding queries are computed but discarded (the
+    Ulysses guidelines pad the sequence and drop the pad rows of the
+    output), so they are not part of the loss and none of their terms
+    reaches any gradient."""
+    real = np.asarray(q_pos, dtype=np.int64) < valid_len
+    return np.where(real[None, :, None, None], do, 0.0)
+
+
 def attention_grad(q, k, v, do, *, scale=None, causal=False, q_pos0=0, k_pos0=0,
                    valid_len=None):
-    """(dq, dk, dv) of L = sum(do * attention(q, k, v)), all [B, S, H, D] fp64."""
+    """(dq, dk, dv) of L = sum(do * attention(q, k, v)) over the real query
+    rows (position < valid_len), all [B, S, H, D] fp64."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, Sq, H, D = q.shape
     Sk = k.shape[1]
@@ -50,6 +61,7 @@ def attention_grad(q, k, v, do, *, scale=None, causal=False, q_pos0=0, k_pos0=0,
         scale = 1.0 / np.sqrt(D)
     if valid_len is None:
         valid_len = np.iinfo(np.int64).max
+    do = _discard_pad_rows(do, q_pos0 + np.arange(Sq), valid_len)
     vis = visible_mask(q_pos0 + np.arange(Sq), k_pos0 + np.arange(Sk), causal, valid_len)
     any_vis = vis.any(axis=1)
     dq = np.zeros_like(q)
@@ -101,8 +113,9 @@ def ring_attention_bwd_rank(q_r, k_blocks, v_blocks, do_r, rank, *, o_r=None, ls
         lse_r = lse_f if lse_r is None else lse_r
     o = _f64(o_r)
     lse = _f64(lse_r)
-    dsum = (do * o).sum(axis=3)                       # [B, Sb, H]
     q_pos = rank * Sb + np.arange(Sb)
+    do = _discard_pad_rows(do, q_pos, valid_len)
+    dsum = (do * o).sum(axis=3)                       # [B, Sb, H]
     dq = np.zeros_like(q)
     dk_parts = [np.zeros_like(q) for _ in range(P)]
     dv_parts = [np.zeros_like(q) for _ in range(P)]
@@ -150,6 +163,7 @@ def attention_grad_sampled(q, k, v, do, o, lse, *, q_rows, k_rows, scale=None, c
         valid_len = np.iinfo(np.int64).max
     q_rows = np.asarray(q_rows, dtype=np.int64)
     k_rows = np.asarray(k_rows, dtype=np.int64)
+    do = _discard_pad_rows(do, q_pos0 + np.arange(Sq), valid_len)
     dsum = (do * o).sum(axis=3)                                   # [B, Sq, H]
     lse_ref = np.where(np.isfinite(lse), lse, np.inf)            # no key seen: P = 0
     dq = np.zeros((B, len(q_rows), H, D))

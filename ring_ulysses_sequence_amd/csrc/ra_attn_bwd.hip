@@ -334,11 +334,16 @@ void ring_attn_bwd_dq(const BwdArgs a) {
   }
   dsum = pair_sum(dsum);
   // a row that saw no key in the forward gets +inf, so every probability of
-  // it is 0 (its scores are all masked anyway)
+  // it is 0 (its scores are all masked anyway); so does a padding query
+  // (position >= valid_len): padding rows are discarded, not part of the
+  // loss, and with P = 0 and D = 0 none of their terms reaches dq, dk or dv
+  // whatever dO holds there
   float lse2 = INFINITY;
+  const bool row_real = row_ok && qpos(a, r) < a.valid_len;
+  if (!row_real) dsum = 0.0f;
   if (row_ok) {
     const float l = a.lse[((long long)b * a.Sq + r) * a.H + h];
-    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    lse2 = l == -INFINITY || !row_real ? INFINITY : l * kLog2e;
     if (half == 0) {
       const long long so = ((long long)b * a.H + h) * a.Sq + r;
       a.stats[so] = lse2;

@@ -321,10 +321,9 @@ def test_ulysses_layout_and_attention(variant):
     # sampled rows of the final sequence-sharded output vs the oracle
     rows = np.unique(np.concatenate([np.arange(0, w.S, 61), [w.S - 1]]))
     qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
-    heads = [0, 5, 13, 31]
-    ref, _, _, _ = oracle.attention(qc[:, :, heads], kc[:, :, heads], vc[:, :, heads],
-                                    rows=rows)
-    got = os_.transpose(0, 1).reshape(w.B, w.S, w.H, w.D)[:, rows][:, :, heads].cpu()
+    # every head (each rank's head group and every position inside it)
+    ref, _, _, _ = oracle.attention(qc, kc, vc, rows=rows)
+    got = os_.transpose(0, 1).reshape(w.B, w.S, w.H, w.D)[:, rows].cpu()
     check_bf16(got, ref, f"{w.name} O sampled rows")
 
 
@@ -341,12 +340,14 @@ def test_long_context_causal_rank3(variant):
     o, lse = ra.ring_attn_fwd(q_r, kb, vb, r, causal=True)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all()
-    # sampled rows: every 128th, both edges, and rows around the diagonal
-    # tile boundaries (query tile 128 rows, key tile 64 keys)
+    # sampled rows: a stride co-prime to the 128- and 256-row query tiles
+    # (so the samples meet every wave and lane position of interior tiles),
+    # both edges, and rows around the diagonal tile boundaries (key tile 64)
     rows = np.unique(np.concatenate([
-        np.arange(0, Sb, 128), np.arange(0, 32), np.arange(Sb - 32, Sb),
-        np.arange(8192 - 3, 8192 + 3), np.arange(127, 130), np.arange(63, 66)]))
-    heads = list(range(0, w.H, 4))
+        np.arange(0, Sb, 127), np.arange(0, 32), np.arange(Sb - 32, Sb),
+        np.arange(8192 - 3, 8192 + 3), np.arange(127, 130), np.arange(63, 66),
+        np.arange(255, 258)]))
+    heads = list(range(1, w.H, 3))
     say(w.name, "oracle on", len(rows), "rows x", len(heads), "heads")
     kc = k[:, :(r + 1) * Sb].cpu()
     vc = v[:, :(r + 1) * Sb].cpu()
@@ -633,7 +634,9 @@ def test_ring_backward_all_ranks(D, causal, pad):
     valid = S - pad
     q, k, v, do = (W.random_tensor((B, S, H, D), seed=s_, device="cuda") for s_ in (31, 32, 33, 34))
     if pad:
-        for x in (q, k, v, do):
+        # padding rows of the inputs are zero; dO stays random there: the
+        # padding queries are discarded and must not reach any gradient
+        for x in (q, k, v):
             x[:, valid:] = 0
     kb, vb = blocks_of(k, P), blocks_of(v, P)
     kc, vc = [x.cpu() for x in kb], [x.cpu() for x in vb]
@@ -728,7 +731,9 @@ def test_zigzag_backward_all_ranks(D, causal, pad):
     valid = S - pad
     q, k, v, do = (W.random_tensor((B, S, H, D), seed=s_, device="cuda") for s_ in (71, 72, 73, 74))
     if pad:
-        for x in (q, k, v, do):
+        # padding rows of the inputs are zero; dO stays random there: the
+        # padding queries are discarded and must not reach any gradient
+        for x in (q, k, v):
             x[:, valid:] = 0
     qs, ks, vs, dos = (zigzag_shares(x, P) for x in (q, k, v, do))
     f32 = dict(dtype=torch.float32, device="cuda")
@@ -763,7 +768,9 @@ def test_gqa_backward_all_ranks(Hkv, causal, pad):
     q, do = (W.random_tensor((B, S, H, D), seed=s_, device="cuda") for s_ in (81, 84))
     k, v = (W.random_tensor((B, S, Hkv, D), seed=s_, device="cuda") for s_ in (82, 83))
     if pad:
-        for x in (q, k, v, do):
+        # padding rows of the inputs are zero; dO stays random there: the
+        # padding queries are discarded and must not reach any gradient
+        for x in (q, k, v):
             x[:, valid:] = 0
     kb, vb = blocks_of(k, P), blocks_of(v, P)
     f32 = dict(dtype=torch.float32, device="cuda")
@@ -905,8 +912,10 @@ def test_ring_backward_long_context_rank3():
     assert torch.isfinite(dq).all()
     for j in range(r + 1, w.P):
         assert not dk[j].any() and not dv[j].any()
-    q_rows = np.unique(np.concatenate([np.arange(0, Sb, 1024), [1, 63, 64, 127, Sb - 1]]))
-    k_local = np.array([0, 1, 63, 64, 5000, Sb - 2, Sb - 1])
+    # query rows at a stride co-prime to the tiles, keys likewise
+    q_rows = np.unique(np.concatenate([np.arange(0, Sb, 1021), [1, 63, 64, 127, Sb - 1]]))
+    k_local = np.unique(np.concatenate([[0, 1, 63, 64, 5000, Sb - 2, Sb - 1],
+                                        np.arange(37, Sb, 1531)]))
     heads = [0, 21, 42, 63]
     kc = k[:, :(r + 1) * Sb].cpu()
     vc = v[:, :(r + 1) * Sb].cpu()

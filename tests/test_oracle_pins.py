@@ -518,8 +518,13 @@ def test_zigzag_wrong_chunk_order_is_caught():
 
 # ---------------------------------------------------------------- backward
 def _loss(q, k, v, do, **kw):
+    """L = sum(dO * O) over the real query rows: padding queries (position
+    >= valid_len) are computed but discarded, so they are not in the loss."""
     o, _, _, _ = oracle.attention(q, k, v, **kw)
-    return float((o * do).sum())
+    vl = kw.get("valid_len")
+    pos = kw.get("q_pos0", 0) + np.arange(o.shape[1])
+    real = np.ones(o.shape[1], bool) if vl is None else pos < vl
+    return float((o * do)[:, real].sum())
 
 
 @pytest.mark.parametrize("causal,valid", [(False, None), (True, None), (True, 4), (False, 3)])
@@ -543,6 +548,37 @@ def test_grad_matches_finite_differences(causal, valid):
             x[idx] = old
             num[idx] = (lp - lm) / (2 * eps)
         np.testing.assert_allclose(g, num, atol=1e-8, rtol=0)
+
+
+def test_grad_ignores_do_of_padding_queries():
+    """Changing dO on the padding rows changes no gradient, and the padding
+    rows' dq is zero (they are not part of the loss); changing dO on a real
+    row does change them."""
+    rng = np.random.default_rng(8)
+    B, S, H, D = 2, 9, 2, 4
+    q, k, v, do = (rng.standard_normal((B, S, H, D)) for _ in range(4))
+    kw = dict(causal=True, valid_len=6)
+    base = oracle.attention_grad(q, k, v, do, **kw)
+    do2 = do.copy()
+    do2[:, 6:] = rng.standard_normal(do2[:, 6:].shape) * 100
+    for a, b in zip(base, oracle.attention_grad(q, k, v, do2, **kw)):
+        np.testing.assert_array_equal(a, b)
+    assert not base[0][:, 6:].any()
+    do3 = do.copy()
+    do3[:, 2] += 1.0
+    assert np.abs(oracle.attention_grad(q, k, v, do3, **kw)[1] - base[1]).max() > 1e-3
+    # the ring backward and the sampled form agree with it
+    Sb = 3
+    kb = [k[:, j * Sb:(j + 1) * Sb] for j in range(3)]
+    vb = [v[:, j * Sb:(j + 1) * Sb] for j in range(3)]
+    rq, rk, rv = oracle.ring_attention_bwd_rank(q[:, 6:9], kb, vb, do2[:, 6:9], 2, **kw)
+    assert not rq.any() and not any(x.any() for x in rk) and not any(x.any() for x in rv)
+    o, lse, _, _ = oracle.attention(q, k, v, **kw)
+    sq, sk, sv = oracle.attention_grad_sampled(q, k, v, do2, o, lse, q_rows=[1, 7],
+                                               k_rows=[0, 4], **kw)
+    np.testing.assert_allclose(sq, base[0][:, [1, 7]], atol=1e-12)
+    np.testing.assert_allclose(sk, base[1][:, [0, 4]], atol=1e-12)
+    np.testing.assert_allclose(sv, base[2][:, [0, 4]], atol=1e-12)
 
 
 @pytest.mark.parametrize("causal", [False, True])
