@@ -192,6 +192,7 @@ def main():
         extra.update(backward_measurement(torch, ra, W, stream, q_r, kb, vb, o, lse, flops))
         extra.update(gqa_varlen_measurements(torch, ra, stream, q_r, k, v, kb, vb))
         extra.update(composable_measurements(torch, ra, stream, q_r, kb, vb, flops))
+        extra.update(gemm_reference(torch, stream))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -367,6 +368,32 @@ def graph_ms(torch, calls, outs, ref, n):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / n
+
+
+def gemm_reference(torch, stream, n=8192, reps=30):
+    """A reference point for the board's dense bf16 matrix-core throughput
+    at its power limit, outside this library: torch.matmul (hipBLASLt) on
+    random N(0,1) bf16 operands of n x n x n, timed over `reps` products
+    after a warmup long enough for the clock to settle.  Context for the
+    attention figure, not part of the step."""
+    g = torch.Generator(device="cuda").manual_seed(1)
+    a = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    with torch.cuda.stream(stream):
+        for _ in range(10):
+            torch.matmul(a, b, out=c)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            torch.matmul(a, b, out=c)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = 2.0 * n ** 3 / ms / 1e9
+    return {"gemm_bf16_reference": {"n": n, "ms": round(ms, 4), "tflops": round(tf, 1),
+                                    "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                                    "library": "torch.matmul (hipBLASLt), N(0,1) operands"}}
 
 
 def side_measurements(torch, ra, W, stream):
