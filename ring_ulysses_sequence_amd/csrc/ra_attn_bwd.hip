@@ -35,12 +35,20 @@
 // lds).  The dQ kernel double-buffers: the copy of tile n+1 is issued when
 // tile n starts and has the whole of tile n's compute to land; one wait and
 // one barrier per tile.  The dK/dV kernel keeps three buffers and runs in
-// half-tile steps with one barrier each (see pair_body).  Rows are stored with an XOR swizzle of their 16-byte chunks
-// (chunk c of row r at c ^ (r & 15) for D = 128, c ^ ((r >> 1) & 7) for
-// D = 64) so that both the row reads (ds_read_b128) and the transposed reads
-// are free of bank conflicts; the copy picks for every LDS position the
-// global chunk that belongs there.  Operand reads run kPF matrix-op pairs
-// ahead of their use.
+// half-tile steps with one barrier each (see pair_body).  Every tile is read
+// both ways -- by rows (ds_read_b128, 16 lanes a pass: rows 0..15 at one
+// chunk) and transposed (ds_read_b64_tr_b16, 32 lanes a pass: rows 4k..4k+3
+// at four adjacent chunks 4t..4t+3) -- so rows are stored with an XOR swizzle
+// of their 16-byte chunks that keeps both free of bank conflicts (64 banks of
+// 4 bytes): chunk c of row r sits at c ^ h(r) with
+//   D = 128: h(r) = (r & 3) << 2 | (r >> 2) & 3
+//            (a permutation of 0..15 over any 16 rows, and the four rows of
+//            an aligned group of 4 fall into four different chunk groups)
+//   D = 64:  with s = (r >> 1) & 7, h(r) = (s & 1) << 2 | s >> 1
+//            (two rows share a 256-byte bank line; the same two properties
+//            for the rows of one parity)
+// The copy picks for every LDS position the global chunk that belongs there.
+// Operand reads run kPF matrix-op pairs ahead of their use.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -118,7 +126,9 @@ struct Cfg {
 
 template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
-  return D == 128 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+  if constexpr (D == 128) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  const int s = (r >> 1) & 7;
+  return c ^ (((s & 1) << 2) | (s >> 1));
 }
 
 __device__ __forceinline__ float pair_sum(float x) {
@@ -453,7 +463,9 @@ void ring_attn_bwd_dq(const BwdArgs a) {
 // so the scores and exponentials are computed once per key, not once per
 // gradient.  Both roles share the Q / dO tiles in LDS; each half tile (32
 // query rows) has one barrier for the P hand-over, each tile one more for
-// its copies.
+// its copies.  Within a step each wave runs its two matrix chains as one
+// stream of operand reads (the second chain's first reads fly during the
+// first chain) with its element-wise work placed between matrix ops.
 // ---------------------------------------------------------------------------
 constexpr int kPairThreads = 512;
 constexpr int kXSlot = 32 * 32 * 2;  // P of one key group for one half tile
@@ -477,109 +489,213 @@ struct PairLane {
   unsigned xa;         // this lane's slot in the P exchange (parity 0)
 };
 
-// The scores product of half T (query rows 32T .. 32T+31 of the tile):
-// role 0 S^T = K Q^T into sc, then P (rounded to bf16) into pb and into the
-// lane's exchange slot; role 1 dP^T = V dO^T into sc.  st receives the lane's
-// statistics (lse2 for role 0, D for role 1) of those rows.
-template <int D, int ROLE, int T>
-__device__ __forceinline__ void pair_front(PairLane<D, ROLE>& w, unsigned bo, bool need,
-                                           int rel_h, float c_scale, f32x16& sc,
-                                           u32x4 (&st)[4], bf16x8 (&pb)[2]) {
-  using C = Cfg<D>;
-  constexpr int NB = kPF + 1;
-  constexpr int RO = T * 32 * C::ROWB;
-  constexpr int AO = (ROLE == 0 ? 0 : C::TILE) + RO;                    // Q or dO rows
-  constexpr int SO = 2 * C::TILE + (ROLE == 0 ? 0 : 4 * kTile) + 128 * T;  // lse2 or D
-  constexpr int XO = T * 4 * kXSlot;
-  sc = f32x16{};
-  u32x4 ra[NB];
-#pragma unroll
-  for (int c = 0; c < kPF; ++c) ra[c] = lds_read_b128<AO>(w.ad.row[c] + bo);
-#pragma unroll
-  for (int c = 0; c < C::NC; ++c) {
-    if (c + kPF < C::NC) ra[(c + kPF) % NB] = lds_read_b128<AO>(w.ad.row[c + kPF] + bo);
-    claim_lds_n(min(kPF, C::NC - 1 - c), ra[c % NB]);
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(ra[c % NB]), w.f[c], sc, 0, 0, 0);
+// The LDS operand stream of one step: N1 row reads (one instruction each)
+// for the first matrix chain, then N2 transposed pairs (two each) for the
+// second, issued kPairLead operands ahead of their matrix ops across the
+// boundary between the chains.  after(i): the LDS instructions issued after
+// operand i's own when matrix op i waits for it.
+constexpr int kPairLead = 2;
+
+template <int N1, int N2>
+struct OpStream {
+  static constexpr int N = N1 + N2;
+  static constexpr int cnt(int i) { return i < N1 ? 1 : 2; }
+  static constexpr int after(int i) {
+    int n = 0;
+    for (int m = i + 1; m <= i + kPairLead && m < N; ++m) n += cnt(m);
+    return n;
   }
-  const unsigned sa = w.sa + bo;
-  st[0] = lds_read_b128<SO + 0>(sa);
-  st[1] = lds_read_b128<SO + 32>(sa);
-  st[2] = lds_read_b128<SO + 64>(sa);
-  st[3] = lds_read_b128<SO + 96>(sa);
-  claim_lds<3>(st[0]);
-  claim_lds<2>(st[1]);
-  claim_lds<1>(st[2]);
-  claim_lds<0>(st[3]);
-  if constexpr (ROLE == 0) {
-    // P of (query m = 32T + 8g + 4half + i, this lane's key), hidden when
-    // m < rel_h + 4half; handed to the partner in the lane's own slot
+};
+
+// Role 0, one step.  F: the scores S^T = K Q^T of half TF (query rows
+// 32TF .. 32TF+31) of the tile in buffer bof, and from them P (masked,
+// rounded to bf16) into pf and into the lane's exchange slot.  B: dV^T +=
+// dO^T P^T of half TB of the tile in buffer bob, with that half's P in pb.
+// The exponentials of the new P run between the dV matrix ops.
+template <int D, bool F, bool B, int TF, int TB>
+__device__ __forceinline__ void step_p(PairLane<D, 0>& w, unsigned bof, unsigned bob, bool need,
+                                       int rel_h, float c_scale, bf16x8 (&pf)[2],
+                                       const bf16x8 (&pb)[2]) {
+  using C = Cfg<D>;
+  constexpr int N1 = F ? C::NC : 0, N2 = B ? 2 * C::NDT : 0;
+  using S = OpStream<N1, N2>;
+  constexpr int NB = kPairLead + 1;
+  constexpr int AO = TF * 32 * C::ROWB;            // Q rows
+  constexpr int TO = C::TILE + TB * 32 * C::ROWB;  // dO^T
+  constexpr int SO = 2 * C::TILE + 128 * TF;       // lse2
+  constexpr int XO = TF * 4 * kXSlot;
+  constexpr int PV = 16 / (2 * C::NDT);            // P values per dV matrix op
+  u32x4 ra[NB], st[4];
+  s16x4 lo[NB], hi[NB];
+  f32x16 sc = f32x16{};
+  if constexpr (F) {
+    const unsigned sa = w.sa + bof;
+    st[0] = lds_read_b128<SO + 0>(sa);
+    st[1] = lds_read_b128<SO + 32>(sa);
+    st[2] = lds_read_b128<SO + 64>(sa);
+    st[3] = lds_read_b128<SO + 96>(sa);
+  }
+  auto issue = [&](int i) {
+    if (i < N1) {
+      ra[i % NB] = lds_read_b128<AO>(w.ad.row[i] + bof);
+    } else {
+      const int j = i - N1;
+      lo[i % NB] = read_tr_g<D, TO>(j / C::NDT, w.ad.lo[j % C::NDT] + bob);
+      hi[i % NB] = read_tr_g<D, TO>(j / C::NDT, w.ad.hi[j % C::NDT] + bob);
+    }
+  };
+  // P of (query m = 32TF + 8g + 4half + i, this lane's key) for v = 4g + i,
+  // hidden when m < rel_h + 4half
+  auto p_val = [&](int v) {
+    const int g = v >> 2, i = v & 3;
+    float x = sc[v] * c_scale - as_f32(st[g])[i];
+    if (need && 32 * TF + 8 * g + i < rel_h) x = -INFINITY;
+    pf[v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(x);
+  };
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 l4 = as_f32(st[g]);
+  for (int i = 0; i < kPairLead; ++i)
+    if (i < S::N) issue(i);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = 4 * g + i;
-        float x = sc[v] * c_scale - l4[i];
-        if (need && 32 * T + 8 * g + i < rel_h) x = -INFINITY;
-        pb[v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(x);
+  for (int i = 0; i < S::N; ++i) {
+    if (i + kPairLead < S::N) issue(i + kPairLead);
+    const int n = S::after(i);
+    if (i < N1) {
+      claim_lds_n(n, ra[i % NB]);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(ra[i % NB]), w.f[i], sc, 0, 0, 0);
+    } else {
+      const int j = i - N1;
+      claim_lds_n(n, lo[i % NB]);
+      claim_lds_n(n, hi[i % NB]);
+      if (F && j == 0) {
+        // the statistics were read before every operand
+        claim_lds_n(n, st[0]);
+        claim_lds_n(n, st[1]);
+        claim_lds_n(n, st[2]);
+        claim_lds_n(n, st[3]);
+      }
+      w.acc[j % C::NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          join(lo[i % NB], hi[i % NB]), pb[j / C::NDT], w.acc[j % C::NDT], 0, 0, 0);
+      if constexpr (F) {
+#pragma unroll
+        for (int e = 0; e < PV; ++e) p_val(PV * j + e);
       }
     }
-    lds_write_b128<XO>(w.xa, __builtin_bit_cast(u32x4, pb[0]));
-    lds_write_b128<XO + 1024>(w.xa, __builtin_bit_cast(u32x4, pb[1]));
   }
-}
-
-// Role 1, half T, once the partner's P is in LDS: dS^T = P^T o (dP^T - D),
-// rounded to bf16, into pb.
-template <int D, int T>
-__device__ __forceinline__ void pair_ds(const PairLane<D, 1>& w, const f32x16& sc,
-                                        const u32x4 (&st)[4], bf16x8 (&pb)[2]) {
-  constexpr int XO = T * 4 * kXSlot;
-  u32x4 x0 = lds_read_b128<XO>(w.xa), x1 = lds_read_b128<XO + 1024>(w.xa);
-  claim_lds<1>(x0);
-  claim_lds<0>(x1);
-  const bf16x8 p0 = as_bf16(x0), p1 = as_bf16(x1);
+  if constexpr (F) {
+    if constexpr (!B) {
+      claim_lds<0>(st[0]);
+      claim_lds<0>(st[1]);
+      claim_lds<0>(st[2]);
+      claim_lds<0>(st[3]);
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const f32x4 d4 = as_f32(st[g]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v = 4 * g + i;
-      const float p = (float)(v < 8 ? p0[v] : p1[v - 8]);
-      pb[v >> 3][v & 7] = (__bf16)(p * (sc[v] - d4[i]));
+      for (int v = 0; v < 16; ++v) p_val(v);
     }
+    lds_write_b128<XO>(w.xa, __builtin_bit_cast(u32x4, pf[0]));
+    lds_write_b128<XO + 1024>(w.xa, __builtin_bit_cast(u32x4, pf[1]));
   }
 }
 
-// The gradient product of half T: role 0 dV^T += dO^T P^T, role 1
-// dK^T += Q^T dS^T (pb holds P or dS of the lane's key over the half's rows).
-template <int D, int ROLE, int T>
-__device__ __forceinline__ void pair_back(PairLane<D, ROLE>& w, unsigned bo,
-                                          const bf16x8 (&pb)[2]) {
+// Role 1, one step.  B: dS^T = P^T o (dP^T - D) of half TB from its dP in
+// scb, its D in stb and the partner's P in the exchange (rounded to bf16),
+// then dK^T += Q^T dS^T of that half (tile in buffer bob).  F: dP^T = V dO^T
+// of half TF of the tile in buffer bof into scf, with that half's D into stf.
+// dS is formed between the dP matrix ops.
+template <int D, bool F, bool B, int TF, int TB>
+__device__ __forceinline__ void step_ds(PairLane<D, 1>& w, unsigned bof, unsigned bob,
+                                        f32x16& scf, u32x4 (&stf)[4], const f32x16& scb,
+                                        u32x4 (&stb)[4]) {
   using C = Cfg<D>;
-  constexpr int NB = kPF + 1;
-  constexpr int RO = T * 32 * C::ROWB;
-  constexpr int TO = (ROLE == 0 ? C::TILE : 0) + RO;  // dO^T or Q^T
-  constexpr int NJ = 2 * C::NDT;
+  constexpr int N1 = F ? C::NC : 0, N2 = B ? 2 * C::NDT : 0;
+  using S = OpStream<N1, N2>;
+  constexpr int NB = kPairLead + 1;
+  constexpr int AO = C::TILE + TF * 32 * C::ROWB;        // dO rows
+  constexpr int TO = TB * 32 * C::ROWB;                  // Q^T
+  constexpr int SO = 2 * C::TILE + 4 * kTile + 128 * TF;  // D
+  constexpr int XO = TB * 4 * kXSlot;
+  constexpr int PV = 16 / C::NC;                         // dS values per dP matrix op
+  u32x4 ra[NB], x0, x1;
   s16x4 lo[NB], hi[NB];
+  bf16x8 ds[2];
+  if constexpr (B) {
+    x0 = lds_read_b128<XO>(w.xa);
+    x1 = lds_read_b128<XO + 1024>(w.xa);
+  }
+  if constexpr (F) {
+    const unsigned sa = w.sa + bof;
+    stf[0] = lds_read_b128<SO + 0>(sa);
+    stf[1] = lds_read_b128<SO + 32>(sa);
+    stf[2] = lds_read_b128<SO + 64>(sa);
+    stf[3] = lds_read_b128<SO + 96>(sa);
+    scf = f32x16{};
+  }
+  auto issue = [&](int i) {
+    if (i < N1) {
+      ra[i % NB] = lds_read_b128<AO>(w.ad.row[i] + bof);
+    } else {
+      const int j = i - N1;
+      lo[i % NB] = read_tr_g<D, TO>(j / C::NDT, w.ad.lo[j % C::NDT] + bob);
+      hi[i % NB] = read_tr_g<D, TO>(j / C::NDT, w.ad.hi[j % C::NDT] + bob);
+    }
+  };
+  auto ds_val = [&](int v) {
+    const bf16x8 p8 = as_bf16(v < 8 ? x0 : x1);
+    const float p = (float)p8[v & 7];
+    ds[v >> 3][v & 7] = (__bf16)(p * (scb[v] - as_f32(stb[v >> 2])[v & 3]));
+  };
+  auto claim_b = [&](int n) {
+    claim_lds_n(n, x0);
+    claim_lds_n(n, x1);
+    claim_lds_n(n, stb[0]);
+    claim_lds_n(n, stb[1]);
+    claim_lds_n(n, stb[2]);
+    claim_lds_n(n, stb[3]);
+  };
+  if constexpr (B && !F) {
+    claim_b(0);
 #pragma unroll
-  for (int j = 0; j < kPF; ++j) {
-    lo[j] = read_tr_g<D, TO>(j / C::NDT, w.ad.lo[j % C::NDT] + bo);
-    hi[j] = read_tr_g<D, TO>(j / C::NDT, w.ad.hi[j % C::NDT] + bo);
+    for (int v = 0; v < 16; ++v) ds_val(v);
   }
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    if (j + kPF < NJ) {
-      const int jn = j + kPF;
-      lo[jn % NB] = read_tr_g<D, TO>(jn / C::NDT, w.ad.lo[jn % C::NDT] + bo);
-      hi[jn % NB] = read_tr_g<D, TO>(jn / C::NDT, w.ad.hi[jn % C::NDT] + bo);
+  for (int i = 0; i < kPairLead; ++i)
+    if (i < S::N) issue(i);
+#pragma unroll
+  for (int i = 0; i < S::N; ++i) {
+    if (i + kPairLead < S::N) issue(i + kPairLead);
+    const int n = S::after(i);
+    if (i < N1) {
+      claim_lds_n(n, ra[i % NB]);
+      // the exchange and the previous statistics were read before every operand
+      if (B && i == 0) claim_b(n);
+      scf = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(ra[i % NB]), w.f[i], scf, 0, 0, 0);
+      if constexpr (B) {
+#pragma unroll
+        for (int e = 0; e < PV; ++e) ds_val(PV * i + e);
+      }
+    } else {
+      const int j = i - N1;
+      claim_lds_n(n, lo[i % NB]);
+      claim_lds_n(n, hi[i % NB]);
+      w.acc[j % C::NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          join(lo[i % NB], hi[i % NB]), ds[j / C::NDT], w.acc[j % C::NDT], 0, 0, 0);
     }
-    const int n = 2 * min(kPF, NJ - 1 - j);
-    claim_lds_n(n, lo[j % NB]);
-    claim_lds_n(n, hi[j % NB]);
-    const int d = j % C::NDT;
-    w.acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(lo[j % NB], hi[j % NB]),
-                                                       pb[j / C::NDT], w.acc[d], 0, 0, 0);
+  }
+}
+
+// One step of either role with the parts that are live: f (the front half,
+// TF) and b (the back half, TB).
+template <int D, int ROLE, int TF, int TB>
+__device__ __forceinline__ void pair_step(PairLane<D, ROLE>& w, bool f, bool b, unsigned bof,
+                                          unsigned bob, bool need, int rel_h, float c_scale,
+                                          bf16x8 (&pf)[2], const bf16x8 (&pb)[2], f32x16& scf,
+                                          u32x4 (&stf)[4], const f32x16& scb, u32x4 (&stb)[4]) {
+  if constexpr (ROLE == 0) {
+    if (f && b) step_p<D, true, true, TF, TB>(w, bof, bob, need, rel_h, c_scale, pf, pb);
+    else if (f) step_p<D, true, false, TF, TB>(w, bof, bob, need, rel_h, c_scale, pf, pb);
+    else if (b) step_p<D, false, true, TF, TB>(w, bof, bob, need, rel_h, c_scale, pf, pb);
+  } else {
+    if (f && b) step_ds<D, true, true, TF, TB>(w, bof, bob, scf, stf, scb, stb);
+    else if (f) step_ds<D, true, false, TF, TB>(w, bof, bob, scf, stf, scb, stb);
+    else if (b) step_ds<D, false, true, TF, TB>(w, bof, bob, scf, stf, scb, stb);
   }
 }
 
@@ -657,10 +773,12 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
     }
   };
   // Tile it sits in buffer it % 3.  The loop runs in half steps: between
-  // barriers, role 0 forms the scores and P of the next half and then its dV
-  // product of the current one, while role 1 forms dS and its dK product of
-  // the current half and then the dP of the next; P of a half crosses over at
-  // the barrier that ends the step forming it.  Tile it+2 is copied from the
+  // barriers, role 0 forms the scores of the next half and then its dV
+  // product of the current one, with the next half's P computed between the
+  // dV matrix ops; role 1 forms the dP of the next half, with the current
+  // half's dS computed between those matrix ops, and then its dK product of
+  // the current half.  P of a half crosses over at the barrier that ends the
+  // step forming it.  Tile it+2 is copied from the
   // step that begins tile it (its buffer held tile it-1, read to the end by
   // then), and is waited for before the barrier ending tile it+1's first step.
   const float c_scale = a.scale_log2;
@@ -685,45 +803,31 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
   if (n_it > 1) copy_q(1, base + PC::BUF);
   wait_copy(n_it > 1);
   pipeline_barrier();  // tile 0 is in LDS
-  f32x16 sc;
-  u32x4 st[4];
+  // role 0: P of halves 0 and 1; role 1: dP and D of the half whose dS is
+  // formed next (A: half 0, B: half 1)
   bf16x8 p0[2], p1[2];
+  f32x16 scA = f32x16{}, scB = f32x16{};
+  u32x4 stA[4] = {}, stB[4] = {};
   bool live = false, need = false;
   int rel_h = 0;
   if (n_it > 0) tile(0, live, need, rel_h);
-  if (live) pair_front<D, ROLE, 0>(w, 0, need, rel_h, c_scale, sc, st, p0);
+  pair_step<D, ROLE, 0, 1>(w, live, false, 0, 0, need, rel_h, c_scale, p0, p1, scA, stA, scB, stB);
   pipeline_barrier();  // P of tile 0, half 0
   unsigned bo = 0;     // buffer of tile it
   for (int it = 0; it < n_it; ++it) {
     const unsigned bo_n = bo + PC::BUF == PC::NBUF * PC::BUF ? 0 : bo + PC::BUF;
     if (it + 2 < n_it) copy_q(it + 2, base + (bo_n + PC::BUF == PC::NBUF * PC::BUF ? 0 : bo_n + PC::BUF));
     // step 1: half 1 of tile it forward, half 0 backward
-    if constexpr (ROLE == 0) {
-      if (live) {
-        pair_front<D, 0, 1>(w, bo, need, rel_h, c_scale, sc, st, p1);
-        pair_back<D, 0, 0>(w, bo, p0);
-      }
-    } else if (live) {
-      pair_ds<D, 0>(w, sc, st, p0);
-      pair_back<D, 1, 0>(w, bo, p0);
-      pair_front<D, 1, 1>(w, bo, need, rel_h, c_scale, sc, st, p1);
-    }
+    pair_step<D, ROLE, 1, 0>(w, live, live, bo, bo, need, rel_h, c_scale, p1, p0, scB, stB, scA,
+                             stA);
     if (it + 1 < n_it) wait_copy(it + 2 < n_it);
     pipeline_barrier();  // P of half 1; tile it+1 is in LDS
     // step 2: half 0 of tile it+1 forward, half 1 of tile it backward
     bool live_n = false, need_n = false;
     int rel_n = 0;
     if (it + 1 < n_it) tile(it + 1, live_n, need_n, rel_n);
-    if constexpr (ROLE == 0) {
-      if (live_n) pair_front<D, 0, 0>(w, bo_n, need_n, rel_n, c_scale, sc, st, p0);
-      if (live) pair_back<D, 0, 1>(w, bo, p1);
-    } else {
-      if (live) {
-        pair_ds<D, 1>(w, sc, st, p1);
-        pair_back<D, 1, 1>(w, bo, p1);
-      }
-      if (live_n) pair_front<D, 1, 0>(w, bo_n, need_n, rel_n, c_scale, sc, st, p0);
-    }
+    pair_step<D, ROLE, 0, 1>(w, live_n, live, bo_n, bo, need_n, rel_n, c_scale, p0, p1, scA, stA,
+                             scB, stB);
     pipeline_barrier();  // P of tile it+1, half 0; tile it read to the end
     live = live_n;
     need = need_n;
