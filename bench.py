@@ -500,9 +500,11 @@ def packed_sample_bounds(S: int, n: int, seed: int):
 
 
 def composable_measurements(torch, ra, stream, q_r, kb, vb, fwd_flops):
-    """The composable form of the same rank-3 share (one block_attn_fwd per
-    visited block in ring order, each folded in by ring_merge; four rounds,
-    three merges, the last one writing bf16), and one ring_merge on the
+    """The composable form of the same rank-3 share (one launch per visited
+    block in ring order: block_attn_fwd for the first, block_attn_fwd_acc
+    folding each later one into the running partial in its own epilogue,
+    the last one writing bf16; four rounds, no separate merge launch), its
+    ratio to the fused ring measured beside it, and one ring_merge on the
     share's fp32 partials alone, in GB/s of its algorithmic bytes: per
     (b, s, h) row it reads two fp32 O rows and two lse and writes one O row
     and one lse, 2*D*4 + 8 + D*4 + 4 bytes."""
@@ -523,8 +525,10 @@ def composable_measurements(torch, ra, stream, q_r, kb, vb, fwd_flops):
 
     out = {}
     ms = timed(lambda: ra.ring_attn_composable(q_r, kb, vb, rank, causal=True, stream=stream), 3)
+    ms_f = timed(lambda: ra.ring_attn_fwd(q_r, kb, vb, rank, causal=True, stream=stream), 3)
     out["composable_long_rank3"] = {"ms": round(ms, 3), "tflops": round(fwd_flops / ms / 1e9, 2),
-                                    "rounds": 4, "merges": 3}
+                                    "rounds": 4, "fused_ms": round(ms_f, 3),
+                                    "vs_fused": round(ms / ms_f, 4)}
     o_acc, lse_acc, _, _ = ra.block_attn_fwd(q_r, kb[2], vb[2], q_pos0=rank * Sb, k_pos0=2 * Sb,
                                              causal=True, want_ml=False, stream=stream)
     o_blk, lse_blk, _, _ = ra.block_attn_fwd(q_r, kb[1], vb[1], q_pos0=rank * Sb, k_pos0=1 * Sb,

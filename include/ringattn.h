@@ -178,6 +178,30 @@ ra_status ra_block_attn_fwd(const void* q, const void* k, const void* v,
                             float* lse, float* m_opt, float* l_opt,
                             void* stream);
 
+/* One ring round folded into the running result in the same launch ([RA]
+ * §3.2 block step followed by the [SPD] §四 combine of ra_ring_merge): the
+ * attention of q over the block k, v exactly as ra_block_attn_fwd computes
+ * it, then, per row, with lse_b its log-sum-exp and o_b its normalised
+ * output,
+ *   lse' = logaddexp(lse_acc, lse_b)
+ *   o'   = o_acc * exp(lse_acc - lse') + o_b * exp(lse_b - lse')
+ * o_acc [B,Sq,H,D] and lse_acc [B,Sq,H] (device, fp32, caller-owned) must
+ * hold a valid partial: the output of ra_block_attn_fwd or of an earlier
+ * call, or o = 0 / lse = -inf rows for an empty start.  With o_final NULL
+ * the combined partial is written back to o_acc and lse_acc.  Otherwise the
+ * combined output goes to o_final [B,Sq,H,D] in dt (the ring's last round:
+ * no fp32 copy), lse_acc receives the final log-sum-exp and o_acc is not
+ * written.  A block with no visible pair ([RA] §3.4 SKIP) leaves the
+ * partial as it is (no launch unless o_final is given).  Positions, causal,
+ * valid_len and scale as ra_block_attn_fwd.  Errors: those of
+ * ra_block_attn_fwd (o_acc, lse_acc in place of o, lse; o_final must be
+ * 16-byte aligned). */
+ra_status ra_block_attn_fwd_acc(const void* q, const void* k, const void* v,
+                                int B, int Sq, int Sk, int H, int D, ra_dtype dt,
+                                float scale, long long q_pos0, long long k_pos0,
+                                int causal, long long valid_len, float* o_acc,
+                                float* lse_acc, void* o_final, void* stream);
+
 /* Fold one round's partial into the running result ([SPD] §四 combine):
  *   lse' = logaddexp(lse_acc, lse_blk)
  *   o'   = o_acc * exp(lse_acc - lse') + o_blk * exp(lse_blk - lse')

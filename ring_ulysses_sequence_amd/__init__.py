@@ -43,7 +43,7 @@ EXPORTED = (
     "ra_zigzag_padded_len", "ra_zigzag_schedule", "ra_zigzag_attn_fwd", "ra_ring_attn_bwd",
     "ra_ring_attn_fwd_gqa", "ra_ring_attn_fwd_varlen", "ra_block_attn_bwd",
     "ra_ring_attn_fwd_split", "ra_ring_split_plan", "ra_zigzag_attn_bwd", "ra_ring_attn_bwd_gqa",
-    "ra_ring_attn_bwd_varlen", "ra_ring_attn_fwd_split_noalloc",
+    "ra_ring_attn_bwd_varlen", "ra_ring_attn_fwd_split_noalloc", "ra_block_attn_fwd_acc",
 )
 
 _lib = None
@@ -77,6 +77,9 @@ def _load():
         "ra_block_attn_fwd": (c_int, [c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int,
                                       c_int, c_float, c_ll, c_ll, c_int, c_ll,
                                       c_vp, c_vp, c_vp, c_vp, c_vp]),
+        "ra_block_attn_fwd_acc": (c_int, [c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int,
+                                          c_int, c_float, c_ll, c_ll, c_int, c_ll,
+                                          c_vp, c_vp, c_vp, c_vp]),
         "ra_ring_merge": (c_int, [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
                                   c_vp, c_int, c_vp]),
         "ra_ring_attn_fwd": (c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp),
@@ -316,6 +319,33 @@ def block_attn_fwd(q, k, v, *, scale: float = 0.0, q_pos0: int = 0, k_pos0: int 
         _stream(stream))
     _check(st, "ra_block_attn_fwd")
     return o, lse, m, l
+
+
+def block_attn_fwd_acc(q, k, v, o_acc, lse_acc, *, scale: float = 0.0, q_pos0: int = 0,
+                       k_pos0: int = 0, causal: bool = False, valid_len: int = -1,
+                       out_final=None, stream=None):
+    """One ring round folded into the running partial (o_acc fp32 [B,Sq,H,D],
+    lse_acc [B,Sq,H]) in the same launch; with ``out_final`` (q's dtype and
+    shape) the combined output goes there and o_acc is left as it was.
+    Returns (o_acc, lse_acc) or (out_final, lse_acc)."""
+    torch = _torch()
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if k.shape != (B, Sk, H, D) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    dt = _dtype_code(q)
+    f32, row = torch.float32, (B, Sq, H)
+    st = _load().ra_block_attn_fwd_acc(
+        _dev(q, "q"), _dev(k, "k", q), _dev(v, "v", q), B, Sq, Sk, H, D, dt, float(scale),
+        q_pos0, k_pos0, int(causal), valid_len, _out(o_acc, "o_acc", (B, Sq, H, D), f32, q),
+        _out(lse_acc, "lse_acc", row, f32, q),
+        _out(out_final, "out_final", (B, Sq, H, D), q.dtype, q) if out_final is not None
+        else None,
+        _stream(stream))
+    _check(st, "ra_block_attn_fwd_acc")
+    return (o_acc if out_final is None else out_final), lse_acc
 
 
 def ring_merge(o_acc, lse_acc, o_blk, lse_blk, *, out_final=None, stream=None):
@@ -721,11 +751,11 @@ def head2seq(x, *, out=None, stream=None):
 
 def ring_attn_composable(q_r, k_blocks, v_blocks, rank: int, *, causal: bool = False,
                          valid_len: int = -1, scale: float = 0.0, stream=None):
-    """The same ring as ``ring_attn_fwd`` done round by round: one
-    ``block_attn_fwd`` per visited block in ring order, folded in with
-    ``ring_merge``; the last merge writes the output in q's dtype.  With a
-    single visited block the fold is against an empty partial (a zero-key
-    block: o = 0, lse = -inf), so the conversion also runs in the merge."""
+    """The same ring as ``ring_attn_fwd`` done round by round: the first
+    visited block by ``block_attn_fwd``, every later one folded into that
+    partial by ``block_attn_fwd_acc`` in its own launch (the last one writing
+    the output in q's dtype).  With a single visited block (or none) the
+    output is written by folding in an empty block."""
     torch = _torch()
     B, Sb, H, D = q_r.shape
     P = len(k_blocks)
@@ -741,24 +771,20 @@ def ring_attn_composable(q_r, k_blocks, v_blocks, rank: int, *, causal: bool = F
         block_attn_fwd(q_r, k_blocks[first], v_blocks[first], k_pos0=first * Sb,
                        want_ml=False, **kw) if first is not None
         else block_attn_fwd(q_r, empty, empty, want_ml=False, **kw))
-    with _on(stream):
-        blk = (torch.empty_like(o_acc), torch.empty_like(lse_acc), None, None)
     rest = visit[1:]
     if not rest:
-        block_attn_fwd(q_r, empty, empty, out=blk, **kw)
-        ring_merge(o_acc, lse_acc, blk[0], blk[1], out_final=final, stream=stream)
+        block_attn_fwd_acc(q_r, empty, empty, o_acc, lse_acc, out_final=final, **kw)
         return final, lse_acc
     for n, j in enumerate(rest):
-        block_attn_fwd(q_r, k_blocks[j], v_blocks[j], k_pos0=j * Sb, out=blk, **kw)
-        ring_merge(o_acc, lse_acc, blk[0], blk[1],
-                   out_final=final if n == len(rest) - 1 else None, stream=stream)
+        block_attn_fwd_acc(q_r, k_blocks[j], v_blocks[j], o_acc, lse_acc, k_pos0=j * Sb,
+                           out_final=final if n == len(rest) - 1 else None, **kw)
     return final, lse_acc
 
 
 __all__ = [
     "lib", "abi_version", "set_attn_kernel", "get_attn_kernel", "set_attn_waves",
     "get_attn_waves", "padded_len", "shard_range", "classify_block", "ring_schedule",
-    "block_attn_fwd", "ring_merge", "ring_attn_fwd", "seq2head", "head2seq",
+    "block_attn_fwd", "block_attn_fwd_acc", "ring_merge", "ring_attn_fwd", "seq2head", "head2seq",
     "zigzag_padded_len", "zigzag_schedule", "zigzag_attn_fwd", "ring_attn_bwd",
     "ring_attn_fwd_varlen", "ring_attn_fwd_split_noalloc",
     "ring_attn_composable", "block_attn_bwd", "ring_split_plan", "zigzag_attn_bwd", "ring_attn_bwd_varlen",

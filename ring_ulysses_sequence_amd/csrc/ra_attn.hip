@@ -81,11 +81,19 @@ struct AttnArgs {
   // rows][D] and [slot][128 rows]).
   int nsplit;
   int rowmax;          // take the row max of every tile (RA_KERNEL_ROWMAX)
+  // accumulate mode (acc != 0, never split): o (fp32) and lse hold the
+  // running partial of the blocks folded in so far; the epilogue combines
+  // this launch's partial with it and writes the result back, or -- with
+  // o_final -- writes the combined output in the input dtype to o_final and
+  // only lse back
+  int acc;
+  void* o_final;
   int nblk;
   KVBlock blk[RA_MAX_P];
 };
 
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2eF = 1.4426950408889634f;
 
 __host__ __device__ __forceinline__ long long qpos(const AttnArgs& a, int row) {
   return row < a.q_split ? a.q_pos0 + row : a.q_pos1 + (row - a.q_split);
@@ -838,6 +846,60 @@ __device__ __forceinline__ void pipeline_step(const StepCtx& k, char* smem, Wave
   vb = vb + 1 == C::VBUF ? 0 : vb + 1;
 }
 
+// Accumulate mode: fold this launch's partial of output row `so` (the
+// normalised values oacc * inv and log-sum-exp lb) into the running partial
+// (a.o fp32, a.lse) with the pairwise combine of the merge kernel
+// ([SPD] §四):
+//   lse' = logaddexp(lse_acc, lb),  o' = o_acc e^(lse_acc - lse') + o e^(lb - lse')
+// and write it back, or with a.o_final the combined output there (bf16 when
+// FINAL_BF16).  Lane (col, half) holds features 32dt + 8g + 4half .. +3 of
+// the row; both halves read lse_acc before half 0 rewrites it (the write
+// depends on the value read).
+template <int D, bool FINAL_BF16>
+__device__ __forceinline__ void fold_row(const AttnArgs& a, long long so, int half,
+                                         const f32x16 (&oacc)[D / 32], float inv, float lb) {
+  constexpr int NDT = D / 32;
+  float* oa = (float*)a.o + so * D;
+  float4 x[NDT][4];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) x[dt][g] = *(const float4*)(oa + 32 * dt + 8 * g + 4 * half);
+  const float la = a.lse[so];
+  const float mx = fmaxf(la, lb);
+  float wa = 0.0f, wb = 0.0f, lse = -INFINITY;
+  if (mx != -INFINITY) {
+    const float ea = fast_exp2((la - mx) * kLog2eF);
+    const float eb = fast_exp2((lb - mx) * kLog2eF);
+    const float sum = ea + eb;
+    lse = mx + fast_log2(sum) * kLn2;
+    const float r = 1.0f / sum;
+    wa = ea * r;
+    wb = eb * r;
+  }
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * dt + 8 * g + 4 * half;
+      const float4 y = float4{oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv,
+                              oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv};
+      const float4 z = float4{fmaf(x[dt][g].x, wa, y.x * wb), fmaf(x[dt][g].y, wa, y.y * wb),
+                              fmaf(x[dt][g].z, wa, y.z * wb), fmaf(x[dt][g].w, wa, y.w * wb)};
+      if (!a.o_final) {
+        *(float4*)(oa + d) = z;
+      } else if constexpr (FINAL_BF16) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 t;
+        t[0] = (__bf16)z.x; t[1] = (__bf16)z.y; t[2] = (__bf16)z.z; t[3] = (__bf16)z.w;
+        *(bf16x4*)((__bf16*)a.o_final + so * D + d) = t;
+      } else {
+        *(float4*)((float*)a.o_final + so * D + d) = z;
+      }
+    }
+  if (half == 0) a.lse[so] = lse;
+}
+
 // One (batch, head, query tile) over tiles [lo, hi) of its visited-tile
 // sequence.  slot < 0: the output rows of the tile; otherwise the split
 // partial slot (see AttnArgs).  ML: also track the exact max for m / l.
@@ -953,6 +1015,11 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs& a, char* smem, in
     const long long so = slot < 0 ? ((long long)b * a.Sq + r) * a.H + h
                                   : slot * C::BR + (r - row0);
     const long long ro = so * D;
+    if (a.acc) {
+      const float lb = l_tot > 0.0f ? (w.m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
+      fold_row<D, true>(a, so, half, w.oacc, inv, lb);
+      return;
+    }
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
@@ -1186,6 +1253,11 @@ void ring_attn_f32(const AttnArgs a) {
   const int r = wrow0 + col;
   if (wrows > 0 && r < a.Sq) {
     const long long ro = ((long long)b * a.Sq + r) * HD + (long long)h * D;
+    if (a.acc) {
+      const float lb = l_tot > 0.0f ? (st.m + fast_log2(l_tot)) * kLn2 : -INFINITY;
+      fold_row<D, false>(a, ((long long)b * a.Sq + r) * a.H + h, half, oacc, inv, lb);
+      return;
+    }
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
@@ -1325,6 +1397,60 @@ extern "C" ra_status ra_block_attn_fwd(const void* q, const void* k, const void*
     a.blk[0] = KVBlock{k, v, k_pos0, Sk, cls};
     a.nblk = 1;
   }
+  return launch(a, D, dt, (hipStream_t)stream, name);
+}
+
+extern "C" ra_status ra_block_attn_fwd_acc(const void* q, const void* k, const void* v,
+                                           int B, int Sq, int Sk, int H, int D,
+                                           ra_dtype dt, float scale, long long q_pos0,
+                                           long long k_pos0, int causal,
+                                           long long valid_len, float* o_acc,
+                                           float* lse_acc, void* o_final, void* stream) {
+  static const char* name = "ra_block_attn_fwd_acc";
+  ra::clear_error();
+  ra_status st = check_common(name, B, Sq, H, D, dt);
+  if (st != RA_OK) return st;
+  if (Sk < 0) return ra::fail(RA_ERR_SHAPE, "%s: negative Sk", name);
+  const long long n_out = (long long)B * Sq * H;
+  if (n_out == 0) return RA_OK;
+  if (!q || !o_acc || !lse_acc || (Sk > 0 && (!k || !v)))
+    return ra::fail(RA_ERR_NULL, "%s: NULL q/k/v/o_acc/lse_acc", name);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_acc) ||
+      !aligned16(o_final))
+    return ra::fail(RA_ERR_SHAPE, "%s: q, k, v, o_acc and o_final must be 16-byte aligned",
+                    name);
+  if (q_pos0 < 0 || k_pos0 < 0)
+    return ra::fail(RA_ERR_RANGE, "%s: negative global position", name);
+  if (valid_len < 0) valid_len = INT64_MAX;
+  AttnArgs a{};
+  a.q = q;
+  a.o = o_acc;
+  a.lse = lse_acc;
+  a.acc = 1;
+  a.o_final = o_final;
+  a.q_pos0 = q_pos0;
+  a.q_pos1 = q_pos0 + Sq;
+  a.q_split = Sq;
+  a.kv_rows_b = Sk;
+  a.Hkv = H;
+  a.valid_len = valid_len;
+  a.B = B;
+  a.Sq = Sq;
+  a.H = H;
+  a.causal = causal != 0;
+  a.o_fp32 = 1;
+  const double sc = scale > 0.0f ? (double)scale : 1.0 / std::sqrt((double)D);
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  a.nblk = 0;
+  const int cls = ra::block_class(q_pos0, q_pos0 + Sq, k_pos0, k_pos0 + Sk,
+                                  a.causal, valid_len);
+  if (cls != RA_SKIP) {
+    a.blk[0] = KVBlock{k, v, k_pos0, Sk, cls};
+    a.nblk = 1;
+  }
+  // a block with no visible pair leaves the partial unchanged: no launch
+  // unless the combined output is asked for
+  if (a.nblk == 0 && !o_final) return RA_OK;
   return launch(a, D, dt, (hipStream_t)stream, name);
 }
 

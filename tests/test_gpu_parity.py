@@ -230,6 +230,59 @@ def test_block_attn_partials_and_stats(dit, variant):
                                m.cpu().numpy() + np.log(l.cpu().numpy()), atol=1e-5)
 
 
+# ------------------------------------------------------------ accumulate mode
+@pytest.mark.parametrize("dtype,D,causal", [(torch.bfloat16, 128, True), (torch.bfloat16, 64, False),
+                                            (torch.bfloat16, 128, False), (torch.float32, 64, True)])
+def test_block_attn_fwd_acc_rounds(dtype, D, causal):
+    """ra_block_attn_fwd_acc one round at a time, in a scrambled order, from
+    an empty start (o = 0, lse = -inf): a query shard of 200 rows (global
+    rows 300..499) against four K/V blocks of uneven, ragged lengths (130,
+    170, 220, 180 keys; real length 610, the rest padding).  After every
+    fold the running (o_acc, lse_acc) against the oracle's lse_combine of
+    the plain per-block attentions; the last fold writes the output in the
+    input dtype and must leave o_acc as it was.  Causal: the block after
+    every query is SKIP and leaves the partial bitwise unchanged."""
+    B, H, Sq, q0, valid = 2, 3, 200, 300, 610
+    bounds = [0, 130, 300, 520, 700]
+    S = bounds[-1]
+    q, k, v = (W.random_tensor((B, S, H, D), seed=s_, dtype=dtype) for s_ in (61, 62, 63))
+    q = q[:, q0:q0 + Sq].contiguous()
+    qg = q.cuda()
+    o_acc = torch.zeros((B, Sq, H, D), dtype=torch.float32, device="cuda")
+    lse_acc = torch.full((B, Sq, H), -math.inf, dtype=torch.float32, device="cuda")
+    ref_o = ref_l = None
+    order = [2, 0, 3, 1]
+    atol, latol = (BF16_ATOL, LSE_BF16_ATOL) if dtype == torch.bfloat16 else (FP32_ATOL, 1e-5)
+    for n, j in enumerate(order):
+        a_, b_ = bounds[j], bounds[j + 1]
+        kb, vb = k[:, a_:b_].contiguous(), v[:, a_:b_].contiguous()
+        last = n == len(order) - 1
+        final = torch.full((B, Sq, H, D), 7.0, dtype=dtype, device="cuda") if last else None
+        before = o_acc.clone(), lse_acc.clone()
+        say("block_attn_fwd_acc", dtype, D, causal, "keys", a_, b_, "final" if last else "")
+        ra.block_attn_fwd_acc(qg, kb.cuda(), vb.cuda(), o_acc, lse_acc, q_pos0=q0, k_pos0=a_,
+                              causal=causal, valid_len=valid, out_final=final)
+        torch.cuda.synchronize()
+        bo, bl, _, _ = oracle.attention(q, kb, vb, causal=causal, q_pos0=q0, k_pos0=a_,
+                                        valid_len=valid)
+        ref_o, ref_l = (bo, bl) if ref_o is None else oracle.lse_combine(ref_o, ref_l, bo, bl)
+        got_o = final if last else o_acc
+        if causal and a_ > q0 + Sq - 1:
+            assert torch.equal(o_acc, before[0]) and torch.equal(lse_acc, before[1])
+        if last:
+            assert torch.equal(o_acc, before[0]), "o_acc written in the final round"
+        c = oracle.compare(got_o.float().cpu(), ref_o)
+        say("  o", {kk: f"{vv:.3e}" for kk, vv in c.items()})
+        assert c["max_abs_err"] <= atol, c
+        gl = lse_acc.cpu().numpy().astype(np.float64)
+        fin = np.isfinite(ref_l)
+        assert np.array_equal(np.isfinite(gl), fin)
+        assert np.max(np.abs(gl[fin] - ref_l[fin]), initial=0.0) <= latol
+    full, full_l, _, _ = oracle.attention(q, k, v, causal=causal, q_pos0=q0, valid_len=valid)
+    check = check_bf16 if dtype == torch.bfloat16 else check_fp32
+    check(final.float().cpu(), full, f"acc rounds {dtype} D={D} causal={causal} final")
+
+
 # ------------------------------------------------------------ split ring
 @pytest.mark.parametrize("causal,D,pad,Hkv,P", [(False, 128, 0, 4, 4), (True, 128, 0, 4, 4),
                                                 (True, 64, 37, 4, 4), (True, 128, 0, 2, 4),
