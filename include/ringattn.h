@@ -86,8 +86,10 @@ typedef enum { RA_OPT_ATTN_KERNEL = 0, RA_OPT_ATTN_WAVES = 1, RA_OPT_COUNT = 2 }
  * share one K/V stream, one workgroup per compute unit -- when the share
  * still gives every compute unit a workgroup, else 4 (128 rows, two
  * workgroups per compute unit).  4 or 8 force that count; the split ring
- * always uses 4.  Results are the same to the stated tolerance.  Any
- * other value is rejected by ra_set_option. */
+ * always uses 4.  Results are the same to the stated tolerance.  The
+ * backward's dQ kernel follows the same rule and setting (its result does
+ * not depend on it, bit for bit).  Any other value is rejected by
+ * ra_set_option. */
 
 /* ---------------------------------------------------------------------
  * Host-only helpers (no GPU needed; exported for tests and schedule dumps)

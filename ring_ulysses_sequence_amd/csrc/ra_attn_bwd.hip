@@ -18,8 +18,9 @@
 // kernels: A[m][k] lane holds m = col, k = 8*half ..; B[k][n] lane holds
 // n = col, k = 8*half ..; C[m][n] lane holds n = col, m = 8*(v/4) + 4*half +
 // v%4):
-//   ring_attn_bwd_dq<D>: one workgroup per 128 query rows (4 waves x 32).
-//     Each lane holds one query column: S^T = K Q^T and dP^T = V dO^T from
+//   ring_attn_bwd_dq<D, NW>: one workgroup per 32*NW query rows (NW = 8
+//     waves when that still fills the compute units, else 4).  Each lane
+//     holds one query column: S^T = K Q^T and dP^T = V dO^T from
 //     K/V rows in LDS, then dQ^T += K^T dS^T with K^T read transposed
 //     (ds_read_b64_tr_b16) and dS^T from registers -- the forward's P V step
 //     with V replaced by K.  It also writes the per-row statistics the second
@@ -119,7 +120,6 @@ struct Cfg {
   static constexpr int ROWB = D * 2;                   // bytes per row in LDS
   static constexpr int TILE = kTile * ROWB;            // one copied tile
   static constexpr int CHUNKS = D / 8;                 // 16-byte chunks per row
-  static constexpr int DMA = TILE / 1024 / kWaves;     // 1 KiB copies per wave per tile
   static constexpr int NC = D / 16;                    // k-steps of the score products
   static constexpr int NDT = D / 32;                   // 32-feature tiles of the gradients
 };
@@ -301,20 +301,31 @@ __device__ __forceinline__ void dq_half(DqLane<D>& w, float dsum, float lse2, fl
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// NW waves of 32 query rows share each K/V tile in LDS: 8 (one workgroup
+// per compute unit, half the K/V streamed per query row) when that still
+// gives every compute unit a workgroup, else 4 (two per compute unit).
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ring_attn_bwd_dq(const BwdArgs a) {
   using C = Cfg<D>;
+  constexpr int ROWS = 32 * NW;                 // query rows per workgroup
+  constexpr int DMA = C::TILE / 1024 / NW;      // 1 KiB copies per wave per tile
   // two buffers, each a K tile then a V tile
   __shared__ __attribute__((aligned(1024))) char smem[2][2 * C::TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
-  const int n_qt = (a.Sq + kRows - 1) / kRows;
-  const int bh = blockIdx.x / n_qt, qt = blockIdx.x % n_qt;
+  const int n_qt = (a.Sq + ROWS - 1) / ROWS;
+  // Workgroups are dispatched round-robin over the 8 XCDs: remap so that
+  // every XCD takes a contiguous range of heads, and the workgroups resident
+  // on it (neighbouring query tiles of one head) stream the same K/V tiles
+  // through its L2; later query tiles (more causal work) first.
+  int id = blockIdx.x;
+  if ((gridDim.x & 7) == 0) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
+  const int bh = id / n_qt, qt = n_qt - 1 - id % n_qt;
   const int b = bh / a.H, h = bh % a.H;
-  const int row0 = qt * kRows;
-  const long long q_hi = qpos(a, min(row0 + kRows, a.Sq) - 1);
+  const int row0 = qt * ROWS;
+  const long long q_hi = qpos(a, min(row0 + ROWS, a.Sq) - 1);
   const int wrow0 = row0 + wave * 32;
   const int wrows = min(32, a.Sq - wrow0);
   const long long wq_lo = qpos(a, wrow0), wq_hi = wq_lo + wrows - 1;
@@ -364,9 +375,9 @@ void ring_attn_bwd_dq(const BwdArgs a) {
   for (int i = 0; i < C::NDT; ++i) w.acc[i] = f32x16{};
   const unsigned base = lds_addr(smem);
   w.ad.init(base, lane);
-  int voff[C::DMA];
-  copy_offsets<D>(wave, lane, HD2, voff);
-  const unsigned dst0 = base + wave * C::DMA * 1024;
+  int voff[DMA];
+  copy_offsets<D, NW>(wave, lane, HD2, voff);
+  const unsigned dst0 = base + wave * DMA * 1024;
 
   // visited tiles: all blocks in order, tiles up to the last one with a
   // key visible to the workgroup's last query
@@ -384,8 +395,8 @@ void ring_attn_bwd_dq(const BwdArgs a) {
     const long long off =
         (((long long)b * a.kv_rows_b + (long long)ti * kTile) * a.Hkv + hk) * D * 2;
     const int rows = min(kTile, kb.len - ti * kTile);
-    copy_tile<D>((const char*)kb.k + off, rows, HD2, voff, dst);
-    copy_tile<D>((const char*)kb.v + off, rows, HD2, voff, dst + C::TILE);
+    copy_tile<D, NW>((const char*)kb.k + off, rows, HD2, voff, dst);
+    copy_tile<D, NW>((const char*)kb.v + off, rows, HD2, voff, dst + C::TILE);
   };
   int cb = 0, ct = 0, cn = 0;
   while (cb < a.nblk && (cn = ntiles(cb)) == 0) ++cb;
@@ -704,13 +715,19 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
   using C = Cfg<D>;
   using PC = PairCfg<D>;
   const int g = wave & 3, half = lane >> 5, col = lane & 31;
+  // XCD-contiguous ranges as in the dQ kernel, over (batch, K/V head) major,
+  // then visited block, then key tile: the workgroups resident on one XCD
+  // are neighbouring key tiles of one block and head, which stream the same
+  // Q / dO tiles through its L2, and every XCD's range spans all blocks (the
+  // diagonal block's lighter work spread evenly)
   int id = blockIdx.x;
+  if ((gridDim.x & 7) == 0) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
   const int kt = id % a.n_ktiles;
   id /= a.n_ktiles;
+  const int bi = id % a.nblk;
+  id /= a.nblk;
   const int hk = id % a.Hkv;  // K/V head; its query heads are hk*G .. hk*G + G-1
-  id /= a.Hkv;
-  const int b = id % a.B;
-  const int bi = id / a.B;
+  const int b = id / a.Hkv;
   const int G = a.H / a.Hkv;
   const BwdBlock& kb = a.blk[bi];
   if (kt * kRows >= kb.len) return;  // a shorter block: no key of it here (uniform)
@@ -884,14 +901,24 @@ void set_scale(BwdArgs& a, float scale, int D) {
 
 // The three launches over a.nblk visited blocks of block_len rows each.
 ra_status launch_bwd(const char* name, BwdArgs& a, int D, int block_len, hipStream_t s) {
-  const long long n_dq = (long long)a.B * a.H * ((a.Sq + kRows - 1) / kRows);
+  // RA_OPT_ATTN_WAVES (4 or 8) forces the dQ workgroup size as it does the
+  // forward's
+  const int forced = ra::option(RA_OPT_ATTN_WAVES);
+  const bool dq8 = forced ? forced == 8 : (long long)a.B * a.H * ((a.Sq + 255) / 256) >= 256;
+  const long long n_dq = (long long)a.B * a.H * ((a.Sq + (dq8 ? 255 : 127)) / (dq8 ? 256 : 128));
   a.n_ktiles = (block_len + kRows - 1) / kRows;
   const long long n_dkv = (long long)a.nblk * a.B * a.Hkv * a.n_ktiles;
   if (n_dq > 0x7fffffffLL || n_dkv > 0x7fffffffLL)
     return ra::fail(RA_ERR_UNSUPPORTED, "%s: grid too large", name);
   // dq first: it writes the row statistics that the dk/dv kernels read
-  if (D == 128) hipLaunchKernelGGL(ring_attn_bwd_dq<128>, dim3((unsigned)n_dq), dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(ring_attn_bwd_dq<64>, dim3((unsigned)n_dq), dim3(kThreads), 0, s, a);
+  const dim3 gq((unsigned)n_dq);
+  if (dq8) {
+    if (D == 128) hipLaunchKernelGGL((ring_attn_bwd_dq<128, 8>), gq, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((ring_attn_bwd_dq<64, 8>), gq, dim3(512), 0, s, a);
+  } else {
+    if (D == 128) hipLaunchKernelGGL((ring_attn_bwd_dq<128, 4>), gq, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((ring_attn_bwd_dq<64, 4>), gq, dim3(256), 0, s, a);
+  }
   if (n_dkv > 0) {
     const dim3 g((unsigned)n_dkv);
     if (D == 128) hipLaunchKernelGGL(ring_attn_bwd_dkv_pair<128>, g, dim3(kPairThreads), 0, s, a);

@@ -725,6 +725,45 @@ def test_ring_backward_all_ranks(D, causal, pad):
     check_grad(torch.cat([x.cpu() for x in dv_all], 1)[:, real], fv[:, real], "dv owners vs full")
 
 
+@pytest.mark.parametrize("D,causal,pad", [(128, True, 0), (64, True, 37), (64, False, 0)])
+def test_ring_backward_dq_waves(D, causal, pad):
+    """The dQ kernel in 4- and 8-wave workgroups (RA_OPT_ATTN_WAVES forces
+    either): every row's dq is formed by one wave in the same order both
+    ways, so the two are bit-identical, and both match the oracle.  320 rows
+    per rank leave the last 8-wave workgroup with six empty waves."""
+    B, H, P, Sb = 2, 3, 4, 320
+    S = P * Sb
+    valid = S - pad
+    q, k, v, do = (W.random_tensor((B, S, H, D), seed=s_, device="cuda") for s_ in (71, 72, 73, 74))
+    kb, vb = blocks_of(k, P), blocks_of(v, P)
+    kc, vc = [x.cpu() for x in kb], [x.cpu() for x in vb]
+    for r in (1, P - 1):
+        sl = slice(r * Sb, (r + 1) * Sb)
+        q_r, do_r = q[:, sl].contiguous(), do[:, sl].contiguous()
+        o_r, lse_r = ra.ring_attn_fwd(q_r, kb, vb, r, causal=causal, valid_len=valid)
+        got = {}
+        try:
+            for wv in (4, 8):
+                ra.set_attn_waves(wv)
+                say("ring bwd dq waves", wv, D, causal, pad, "rank", r)
+                got[wv] = ra.ring_attn_bwd(q_r, kb, vb, o_r, do_r, lse_r, r, causal=causal,
+                                           valid_len=valid)
+                torch.cuda.synchronize()
+        finally:
+            ra.set_attn_waves(0)
+        assert torch.equal(got[4][0], got[8][0])
+        for j in range(P):
+            assert torch.equal(got[4][1][j], got[8][1][j]) and torch.equal(got[4][2][j], got[8][2][j])
+        rq, rk, rv = oracle.ring_attention_bwd_rank(q_r.cpu(), kc, vc, do_r.cpu(), r,
+                                                    o_r=o_r.cpu(), lse_r=lse_r.cpu(),
+                                                    causal=causal, valid_len=valid)
+        check_grad(got[8][0].cpu(), rq, f"dq 8 waves r{r}")
+        for j in range(P):
+            if np.any(rk[j]):
+                check_grad(got[8][1][j].cpu(), rk[j], f"dk r{r} block {j}")
+                check_grad(got[8][2][j].cpu(), rv[j], f"dv r{r} block {j}")
+
+
 @pytest.mark.parametrize("D,causal", [(128, True), (64, False)])
 def test_block_backward_rounds(D, causal):
     """ra_block_attn_bwd one round at a time: a query shard of 200 rows
