@@ -1054,8 +1054,12 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
   using C = Bf16Cfg<D, NW>;
   if constexpr (SPLIT) {
     const int ns = a.nsplit;
-    const int j = (int)blockIdx.x % ns;
-    const int tile = (int)blockIdx.x / ns;  // (b*H + h)*n_qtiles + qt
+    // XCD-contiguous ranges as in tile_coords: the runs of one head's query
+    // tiles stay on one XCD and share its K/V stream in L2
+    int id = (int)blockIdx.x;
+    if ((gridDim.x & 7) == 0) id = (id & 7) * (int)(gridDim.x >> 3) + (id >> 3);
+    const int j = id % ns;
+    const int tile = id / ns;  // (b*H + h)*n_qtiles + qt
     const int qt = tile % a.n_qtiles, bh = tile / a.n_qtiles;
     const int row_hi = min((qt + 1) * C::BR, a.Sq) - 1;
     const long long q_hi = qpos(a, row_hi);
