@@ -772,8 +772,19 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
   const int n_per = n_t - t0, n_it = G * n_per;
   // Q and dO tiles by all eight waves; the statistics rows by waves 0 (lse)
   // and 1 (D)
-  auto copy_q = [&](int it, unsigned buf_base) {
-    const int h = hk * G + it / n_per, ti = t0 + it % n_per;
+  // (query head, query tile) of an iteration, advanced by one per
+  // iteration (no division in the loop)
+  struct ItCur {
+    int h, ti;
+  };
+  auto it_next = [&](ItCur& c) {
+    if (++c.ti == n_t) {
+      c.ti = t0;
+      ++c.h;
+    }
+  };
+  auto copy_q = [&](const ItCur& c, unsigned buf_base) {
+    const int h = c.h, ti = c.ti;
     const long long stat0 = ((long long)b * a.H + h) * a.Sq;
     const long long off = (((long long)b * a.Sq + (long long)ti * kTile) * a.H + h) * D * 2;
     const int rows = min(kTile, a.Sq - ti * kTile);
@@ -799,8 +810,8 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
   // step that begins tile it (its buffer held tile it-1, read to the end by
   // then), and is waited for before the barrier ending tile it+1's first step.
   const float c_scale = a.scale_log2;
-  auto tile = [&](int it, bool& live, bool& need, int& rel_h) {
-    const int ti = t0 + it % n_per;
+  auto tile = [&](const ItCur& c, bool& live, bool& need, int& rel_h) {
+    const int ti = c.ti;
     const long long qp0 = qpos(a, ti * kTile);
     const long long qp_hi = qp0 + min(kTile, a.Sq - ti * kTile) - 1;
     live = !(a.causal && kw_lo > qp_hi) && kw_lo < a.valid_len;
@@ -816,8 +827,11 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
     else if (wave < 2) wait_vmcnt<2 * PC::DMA + 1>();
     else wait_vmcnt<2 * PC::DMA>();
   };
-  if (n_it > 0) copy_q(0, base);
-  if (n_it > 1) copy_q(1, base + PC::BUF);
+  ItCur cq{hk * G, t0}, ct{hk * G, t0};  // the next copy's iteration, tile()'s
+  if (n_it > 0) copy_q(cq, base);
+  it_next(cq);
+  if (n_it > 1) copy_q(cq, base + PC::BUF);
+  it_next(cq);
   wait_copy(n_it > 1);
   pipeline_barrier();  // tile 0 is in LDS
   // role 0: P of halves 0 and 1; role 1: dP and D of the half whose dS is
@@ -827,13 +841,16 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
   u32x4 stA[4] = {}, stB[4] = {};
   bool live = false, need = false;
   int rel_h = 0;
-  if (n_it > 0) tile(0, live, need, rel_h);
+  if (n_it > 0) tile(ct, live, need, rel_h);
   pair_step<D, ROLE, 0, 1>(w, live, false, 0, 0, need, rel_h, c_scale, p0, p1, scA, stA, scB, stB);
   pipeline_barrier();  // P of tile 0, half 0
   unsigned bo = 0;     // buffer of tile it
   for (int it = 0; it < n_it; ++it) {
     const unsigned bo_n = bo + PC::BUF == PC::NBUF * PC::BUF ? 0 : bo + PC::BUF;
-    if (it + 2 < n_it) copy_q(it + 2, base + (bo_n + PC::BUF == PC::NBUF * PC::BUF ? 0 : bo_n + PC::BUF));
+    if (it + 2 < n_it) {
+      copy_q(cq, base + (bo_n + PC::BUF == PC::NBUF * PC::BUF ? 0 : bo_n + PC::BUF));
+      it_next(cq);
+    }
     // step 1: half 1 of tile it forward, half 0 backward
     pair_step<D, ROLE, 1, 0>(w, live, live, bo, bo, need, rel_h, c_scale, p1, p0, scB, stB, scA,
                              stA);
@@ -842,7 +859,10 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
     // step 2: half 0 of tile it+1 forward, half 1 of tile it backward
     bool live_n = false, need_n = false;
     int rel_n = 0;
-    if (it + 1 < n_it) tile(it + 1, live_n, need_n, rel_n);
+    if (it + 1 < n_it) {
+      it_next(ct);
+      tile(ct, live_n, need_n, rel_n);
+    }
     pair_step<D, ROLE, 0, 1>(w, live_n, live, bo_n, bo, need_n, rel_n, c_scale, p0, p1, scA, stA,
                              scB, stB);
     pipeline_barrier();  // P of tile it+1, half 0; tile it read to the end

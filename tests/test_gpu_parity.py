@@ -332,6 +332,52 @@ def test_split_ring_all_ranks(causal, D, pad, Hkv, P):
             assert float((lse - l1).abs().max()) <= LSE_BF16_ATOL
 
 
+def test_noalloc_split_under_graph_capture():
+    """ra_ring_attn_fwd_split_noalloc is for callers that cannot allocate,
+    such as code under HIP graph capture: captured once (it allocates nothing
+    and records no memset), replayed three times with the library's own eager
+    work and synchronisations in between (an eager call on another share that
+    overwrites the same scratch, and fills of the outputs), every replay bit-
+    identical to the eager result of the captured call."""
+    B, S, H, D, P, rank = 1, 4096, 24, 128, 4, 0
+    q, k, v = (W.random_tensor((B, S, H, D), seed=s_, device="cuda") for s_ in (81, 82, 83))
+    kb, vb = blocks_of(k, P), blocks_of(v, P)
+    Sb = S // P
+    q_r = q[:, rank * Sb:(rank + 1) * Sb].contiguous()
+    runs, _ = ra.ring_split_plan(B, Sb, H, D, P, rank, False, -1, 0)
+    assert runs > 1, "the case must exercise the split"
+    o_e = torch.empty_like(q_r)
+    l_e = torch.empty((B, Sb, H), dtype=torch.float32, device="cuda")
+    ra.ring_attn_fwd_split_noalloc(q_r, kb, vb, rank, o_e, l_e)
+    # another share for the eager calls between replays (same scratch)
+    q2, k2, v2 = (W.random_tensor((1, 1024, 4, 64), seed=s_, device="cuda") for s_ in (84, 85, 86))
+    kb2, vb2 = blocks_of(k2, 2), blocks_of(v2, 2)
+    q2_r = q2[:, 512:].contiguous()
+    o2 = torch.empty_like(q2_r)
+    o_g = torch.empty_like(q_r)
+    l_g = torch.empty_like(l_e)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ra.ring_attn_fwd_split_noalloc(q_r, kb, vb, rank, o_g, l_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    say("noalloc split: capture")
+    with torch.cuda.graph(graph):
+        ra.ring_attn_fwd_split_noalloc(q_r, kb, vb, rank, o_g, l_g)
+    for rep in range(3):
+        o_g.fill_(float("nan"))
+        l_g.fill_(float("nan"))
+        ra.ring_attn_fwd_split_noalloc(q2_r, kb2, vb2, 1, o2, causal=True, nsplit=2)
+        torch.cuda.synchronize()
+        say("noalloc split: replay", rep)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g.view(torch.int16), o_e.view(torch.int16)), rep
+        assert torch.equal(l_g.view(torch.int32), l_e.view(torch.int32)), rep
+
+
 def test_split_ring_errors():
     """A run count below one is refused; a split without workspace or with
     too small a workspace is refused before any launch."""
