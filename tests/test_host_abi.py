@@ -296,6 +296,27 @@ def test_device_entry_points_validate_before_launch(lib):
     st = lib.ra_ring_attn_bwd_varlen(null, arr, arr, null, null, null, 16, 1, 64, 2, 0,
                                      ra.RA_BF16, 0.0, 1, bad, 2, null, arr, arr, null, null)
     assert st == 2 and b"increase" in lib.ra_last_error()
+    # accumulate mode: unsupported D, missing accumulators, misaligned final
+    # output, negative positions; an empty problem is a no-op
+    st = lib.ra_block_attn_fwd_acc(null, null, null, 1, 4, 4, 1, 96, ra.RA_BF16, 0.0, 0, 0,
+                                   0, -1, null, null, null, null)
+    assert st == 5 and b"96" in lib.ra_last_error()
+    st = lib.ra_block_attn_fwd_acc(ctypes.c_void_p(256), ctypes.c_void_p(256),
+                                   ctypes.c_void_p(256), 1, 4, 4, 1, 64, ra.RA_BF16, 0.0, 0, 0,
+                                   0, -1, null, null, null, null)
+    assert st == 1 and b"ra_block_attn_fwd_acc" in lib.ra_last_error()
+    st = lib.ra_block_attn_fwd_acc(ctypes.c_void_p(256), ctypes.c_void_p(256),
+                                   ctypes.c_void_p(256), 1, 4, 4, 1, 64, ra.RA_BF16, 0.0, 0, 0,
+                                   0, -1, ctypes.c_void_p(256), ctypes.c_void_p(256),
+                                   ctypes.c_void_p(258), null)
+    assert st == 2 and b"aligned" in lib.ra_last_error()
+    st = lib.ra_block_attn_fwd_acc(ctypes.c_void_p(256), ctypes.c_void_p(256),
+                                   ctypes.c_void_p(256), 1, 4, 4, 1, 64, ra.RA_BF16, 0.0, -1, 0,
+                                   0, -1, ctypes.c_void_p(256), ctypes.c_void_p(256), null, null)
+    assert st == 4
+    st = lib.ra_block_attn_fwd_acc(null, null, null, 1, 0, 4, 1, 64, ra.RA_BF16, 0.0, 0, 0,
+                                   0, -1, null, null, null, null)
+    assert st == 0
     # merge: unsupported D, unknown dtype
     st = lib.ra_ring_merge(null, null, null, null, 1, 4, 1, 12, null, ra.RA_FP32, null)
     assert st == 5
@@ -311,6 +332,9 @@ def test_binding_refuses_cpu_tensors(lib):
         ra.block_attn_fwd(q, q, q)
     with pytest.raises(ValueError, match="GPU"):
         ra.seq2head(torch.zeros(2, 1, 4, 2, 8, dtype=torch.bfloat16))
+    acc = torch.zeros(1, 4, 1, 64, dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU"):
+        ra.block_attn_fwd_acc(q, q, q, acc, torch.zeros(1, 4, 1))
 
 
 def test_binding_checks_output_buffers_before_the_library(lib):
