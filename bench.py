@@ -451,6 +451,22 @@ def side_measurements(torch, ra, W, stream):
             rec.update({f"{tag}ms": round(ms, 4), f"{tag}GBps": round(byts / ms / 1e6, 1),
                         f"{tag}frac_hbm": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3)})
         out[f"ulysses_{name}"] = rec
+    # the practical copy ceiling of the board for comparison: a library
+    # device-to-device copy (torch copy_) of the same tensors, same rotation
+    a, b = ev(), ev()
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            ys[i].view(-1).copy_(xs[i].view(-1))
+        a.record(stream)
+        for i in range(n):
+            ys[i % 3].view(-1).copy_(xs[i % 3].view(-1))
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / n
+    byts = 2.0 * xs[0].numel() * xs[0].element_size()
+    out["copy_reference"] = {"ms": round(ms, 4), "GBps": round(byts / ms / 1e6, 1),
+                             "frac_hbm": round(byts / ms / 1e6 / PEAK_HBM_GBS, 3),
+                             "library": "torch copy_ (device to device), same three tensors"}
     del xs, ys, zs
     return out
 
