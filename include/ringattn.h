@@ -307,9 +307,11 @@ int ra_ring_split_plan(int B, int Sb, int H, int D, int P, int rank, int causal,
  * padding).  Query at position p attends to the keys of its own sample
  * (causal: at or before p).  q_r [1,Sb,H,D], blocks [1,Sb,H,D] as in
  * ra_ring_attn_fwd; rows of the share outside every sample are left
- * untouched in o and lse_opt.  One launch per sample that meets the rank's
- * rows, each over the parts of the visited blocks inside the sample, in
- * ring order.  RA_ERR_SHAPE for boundaries that do not increase from 0 or
+ * untouched in o and lse_opt.  Every sample that meets the rank's rows is
+ * computed over the parts of the visited blocks inside it, in ring order:
+ * bf16 samples eight to a launch (a sample spanning more than eight visited
+ * blocks in a launch of its own), fp32 samples one launch each.
+ * RA_ERR_SHAPE for boundaries that do not increase from 0 or
  * end past P*Sb; otherwise as ra_ring_attn_fwd. */
 ra_status ra_ring_attn_fwd_varlen(const void* q_r, const void* const* k_blocks,
                                   const void* const* v_blocks, int Sb, int H, int D,

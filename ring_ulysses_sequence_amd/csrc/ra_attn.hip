@@ -31,6 +31,8 @@
 #include <cmath>
 #include <cstdint>
 #include <mutex>
+#include <algorithm>
+#include <vector>
 #include <type_traits>
 
 #include "ra_internal.h"
@@ -52,7 +54,8 @@ struct KVBlock {
   int cls;             // RA_FULL or RA_DIAG (SKIP blocks are not passed)
 };
 
-struct AttnArgs {
+// Everything of one attention problem but its block table.
+struct AttnHead {
   const void* q;       // [B, Sq, H, D]
   void* o;             // [B, Sq, H, D]: fp32 if o_fp32, else the input dtype
   float* lse;          // [B, Sq, H] or null
@@ -89,13 +92,20 @@ struct AttnArgs {
   int acc;
   void* o_final;
   int nblk;
-  KVBlock blk[RA_MAX_P];
 };
+// A problem with room for N visited blocks; AttnArgs (RA_MAX_P) for a whole
+// ring, a smaller table where many problems share one launch's arguments.
+template <int N>
+struct AttnArgsT : AttnHead {
+  KVBlock blk[N];
+};
+using AttnArgs = AttnArgsT<RA_MAX_P>;
 
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2eF = 1.4426950408889634f;
 
-__host__ __device__ __forceinline__ long long qpos(const AttnArgs& a, int row) {
+template <class A>
+__host__ __device__ __forceinline__ long long qpos(const A& a, int row) {
   return row < a.q_split ? a.q_pos0 + row : a.q_pos1 + (row - a.q_split);
 }
 
@@ -121,8 +131,8 @@ __device__ __forceinline__ float pair_sum(float x) {
 // to the last one holding a visible key ([RA] §3.4 applied per tile: tiles
 // wholly in the future of the workgroup's last query, or wholly padding,
 // are never read).
-template <int BC>
-__host__ __device__ __forceinline__ int tiles_of(const AttnArgs& a, int b, long long q_hi) {
+template <int BC, class A>
+__host__ __device__ __forceinline__ int tiles_of(const A& a, int b, long long q_hi) {
   const KVBlock& kb = a.blk[b];
   const int n = (kb.len + BC - 1) / BC;
   long long lim = a.valid_len - 1;
@@ -144,9 +154,9 @@ __host__ __device__ __forceinline__ int tiles_of(const AttnArgs& a, int b, long 
 // the heads one after another.
 constexpr int kHeadGroup = 4, kTileRun = 8;
 
-__device__ __forceinline__ void tile_coords(const AttnArgs& a, int id, int n, int& b, int& h,
-                                            int& qt) {
-  if ((n & 7) == 0) id = (id & 7) * (n >> 3) + (id >> 3);
+template <class A>
+__device__ __forceinline__ void tile_coords_in(const A& a, int id, int& b, int& h,
+                                               int& qt) {
   const int Q = a.n_qtiles, BH = a.B * a.H;
   int bh;
   if (Q % kTileRun == 0 && BH % kHeadGroup == 0) {
@@ -161,7 +171,14 @@ __device__ __forceinline__ void tile_coords(const AttnArgs& a, int id, int n, in
   h = bh % a.H;
   b = bh / a.H;
 }
-__device__ __forceinline__ void tile_coords(const AttnArgs& a, int& b, int& h, int& qt) {
+template <class A>
+__device__ __forceinline__ void tile_coords(const A& a, int id, int n, int& b, int& h,
+                                            int& qt) {
+  if ((n & 7) == 0) id = (id & 7) * (n >> 3) + (id >> 3);
+  tile_coords_in(a, id, b, h, qt);
+}
+template <class A>
+__device__ __forceinline__ void tile_coords(const A& a, int& b, int& h, int& qt) {
   tile_coords(a, (int)blockIdx.x, (int)gridDim.x, b, h, qt);
 }
 
@@ -384,7 +401,8 @@ __device__ __forceinline__ long long clampll(long long x, long long lo, long lon
 }
 
 // Move s to the first block at or after s.blk with visited tiles (t = 0).
-__device__ __forceinline__ void seq_enter(const AttnArgs& a, const SeqCtx& x, Seq& s) {
+template <class A>
+__device__ __forceinline__ void seq_enter(const A& a, const SeqCtx& x, Seq& s) {
   s.t = 0;
   for (; s.blk < a.nblk; ++s.blk) {
     s.n = tiles_of<64>(a, s.blk, x.q_hi);
@@ -400,10 +418,12 @@ __device__ __forceinline__ void seq_enter(const AttnArgs& a, const SeqCtx& x, Se
   const long long lim = a.valid_len - kb.k_pos0;
   s.lim0 = (int)clampll(lim < kb.len ? lim : kb.len, 0, 1LL << 30);
 }
-__device__ __forceinline__ void seq_clip(const AttnArgs& a, const SeqCtx& x, Seq& s) {
+template <class A>
+__device__ __forceinline__ void seq_clip(const A& a, const SeqCtx& x, Seq& s) {
   if (s.blk > x.end_blk || (s.blk == x.end_blk && s.t >= x.end_t)) s.blk = a.nblk;
 }
-__device__ __forceinline__ void seq_next(const AttnArgs& a, const SeqCtx& x, Seq& s) {
+template <class A>
+__device__ __forceinline__ void seq_next(const A& a, const SeqCtx& x, Seq& s) {
   if (s.blk >= a.nblk) return;
   if (++s.t >= s.n) {
     ++s.blk;
@@ -412,7 +432,8 @@ __device__ __forceinline__ void seq_next(const AttnArgs& a, const SeqCtx& x, Seq
   seq_clip(a, x, s);
 }
 // Block and tile of tile number i of the sequence (blk = a.nblk past it).
-__device__ __forceinline__ void seq_locate(const AttnArgs& a, long long q_hi, int i, int& blk,
+template <class A>
+__device__ __forceinline__ void seq_locate(const A& a, long long q_hi, int i, int& blk,
                                            int& t) {
   for (blk = 0; blk < a.nblk; ++blk) {
     const int n = tiles_of<64>(a, blk, q_hi);
@@ -421,7 +442,8 @@ __device__ __forceinline__ void seq_locate(const AttnArgs& a, long long q_hi, in
   }
   t = i;
 }
-__device__ __forceinline__ Seq seq_first(const AttnArgs& a, const SeqCtx& x, int lo) {
+template <class A>
+__device__ __forceinline__ Seq seq_first(const A& a, const SeqCtx& x, int lo) {
   Seq s{};
   seq_locate(a, x.q_hi, lo, s.blk, s.t);
   const int t = s.t;
@@ -432,7 +454,8 @@ __device__ __forceinline__ Seq seq_first(const AttnArgs& a, const SeqCtx& x, int
   seq_clip(a, x, s);
   return s;
 }
-__device__ __forceinline__ TDesc seq_desc(const AttnArgs& a, const Seq& s) {
+template <class A>
+__device__ __forceinline__ TDesc seq_desc(const A& a, const Seq& s) {
   TDesc d;
   d.valid = s.blk < a.nblk;
   d.rel = s.rel0 + 64 * s.t;
@@ -733,8 +756,9 @@ __device__ __forceinline__ void scores_tile(const WaveState<D, NW>& w, f32x16 (&
 }
 
 // Per-step context that stays fixed over the loop.
+template <class A>
 struct StepCtx {
-  const AttnArgs* a;
+  const A* a;
   SeqCtx x;
   int HD2, wave, col, half, wrows;
   bool causal, rowmax;
@@ -745,8 +769,8 @@ struct StepCtx {
 // on the row-max path or while some row of the wave has no reference yet,
 // the row max and a lazy move of the reference.  Returns alpha for the
 // deferred rescale of u (1 when nothing moved) and sets `moved`.
-template <int D, int NW, bool ML>
-__device__ __forceinline__ float tile_setup(const StepCtx& k, WaveState<D, NW>& w, f32x16 (&s)[2],
+template <int D, int NW, bool ML, class A>
+__device__ __forceinline__ float tile_setup(const StepCtx<A>& k, WaveState<D, NW>& w, f32x16 (&s)[2],
                                             const TDesc& d, bool& moved) {
   if (tile_needs_mask(d, k.causal)) mask_tile(s, d, k.causal, k.col, k.half);
   float alpha = 1.0f;
@@ -765,8 +789,8 @@ __device__ __forceinline__ float tile_setup(const StepCtx& k, WaveState<D, NW>& 
 
 // First half of a tile over the bound: move the reference, scale u and l
 // (every product of the old reference has been issued), redo the half.
-template <int D, int NW>
-__device__ __forceinline__ void first_half_check(const StepCtx& k, WaveState<D, NW>& w,
+template <int D, int NW, class A>
+__device__ __forceinline__ void first_half_check(const StepCtx<A>& k, WaveState<D, NW>& w,
                                                  const f32x16& s0, bf16x8 (&pb)[4], float& l1) {
   if (__builtin_amdgcn_ballot_w64(l1 > kTileSumLimit)) {
     const float f = move_reference_octaves(w.m_ref, w.l_run, half_max(s0, k.c));
@@ -781,14 +805,14 @@ __device__ __forceinline__ void first_half_check(const StepCtx& k, WaveState<D, 
 // V(n) in V buffer vb; the copies of tile n + LEAD go to K(n)'s buffer
 // (read in the step before) and to V(n-1)'s.  d0, d1, d2 describe tiles n,
 // n+1, n+2 (d2 only with LEAD = 3) and cur stands at tile n + LEAD.
-template <int D, int NW, bool ML, int PAR>
-__device__ __forceinline__ void pipeline_step(const StepCtx& k, char* smem, WaveState<D, NW>& w,
+template <int D, int NW, bool ML, int PAR, class A>
+__device__ __forceinline__ void pipeline_step(const StepCtx<A>& k, char* smem, WaveState<D, NW>& w,
                                               f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
                                               bf16x8 (&pb_cur)[4], bf16x8 (&pb_nxt)[4],
                                               float& lsum_cur, float& lsum_nxt, Seq& cur,
                                               TDesc& d0, TDesc& d1, TDesc& d2, int& kb, int& vb) {
   using C = Bf16Cfg<D, NW>;
-  const AttnArgs& a = *k.a;
+  const A& a = *k.a;
   const int kb1 = kb + 1 == C::KBUF ? 0 : kb + 1;  // K(n+1)
   const int vcp = vb == 0 ? C::VBUF - 1 : vb - 1;  // V(n-1)'s buffer
   // copies of tile n + LEAD: K first, so that waiting for K leaves V in flight
@@ -855,8 +879,8 @@ __device__ __forceinline__ void pipeline_step(const StepCtx& k, char* smem, Wave
 // FINAL_BF16).  Lane (col, half) holds features 32dt + 8g + 4half .. +3 of
 // the row; both halves read lse_acc before half 0 rewrites it (the write
 // depends on the value read).
-template <int D, bool FINAL_BF16>
-__device__ __forceinline__ void fold_row(const AttnArgs& a, long long so, int half,
+template <int D, bool FINAL_BF16, class A>
+__device__ __forceinline__ void fold_row(const A& a, long long so, int half,
                                          const f32x16 (&oacc)[D / 32], float inv, float lb) {
   constexpr int NDT = D / 32;
   float* oa = (float*)a.o + so * D;
@@ -903,8 +927,8 @@ __device__ __forceinline__ void fold_row(const AttnArgs& a, long long so, int ha
 // One (batch, head, query tile) over tiles [lo, hi) of its visited-tile
 // sequence.  slot < 0: the output rows of the tile; otherwise the split
 // partial slot (see AttnArgs).  ML: also track the exact max for m / l.
-template <int D, int NW, bool ML>
-__device__ __forceinline__ void attn_bf16_tile(const AttnArgs& a, char* smem, int b, int h,
+template <int D, int NW, bool ML, class A>
+__device__ __forceinline__ void attn_bf16_tile(const A& a, char* smem, int b, int h,
                                                int qt, int lo, int hi, long long slot) {
   using C = Bf16Cfg<D, NW>;
   const int tid = threadIdx.x;
@@ -919,7 +943,7 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs& a, char* smem, in
   const long long HD = (long long)a.H * D;
   const int hk = h / (a.H / a.Hkv);  // K/V head of this query head
 
-  StepCtx k;
+  StepCtx<A> k;
   k.a = &a;
   k.HD2 = a.Hkv * D * 2;  // bytes between consecutive key rows
   k.wave = wave;
@@ -1049,8 +1073,8 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs& a, char* smem, in
 
 // Kernel body: one query tile over its whole visited sequence, or (SPLIT)
 // one run of it.
-template <int D, int NW, bool ML, bool SPLIT>
-__device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, char* smem) {
+template <int D, int NW, bool ML, bool SPLIT, class A>
+__device__ __forceinline__ void attn_bf16_body(const A& a, char* smem) {
   using C = Bf16Cfg<D, NW>;
   if constexpr (SPLIT) {
     const int ns = a.nsplit;
@@ -1087,6 +1111,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ring_attn_bf16_split(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[Bf16Cfg<D, 4>::LDS];
   attn_bf16_body<D, 4, false, true>(a, smem);
+}
+
+// Several independent problems in one launch (the packed samples of a
+// share): each segment's arguments exactly as its own launch would take
+// them (same waves per workgroup; a smaller block table), so that the
+// workgroups of all segments fill the chip together instead of each launch
+// draining its last, partial round before the next begins.  Workgroups are
+// dispatched round-robin over the 8 XCDs: XCD x walks the segments in turn
+// and takes the x-th contiguous eighth of each one's tiles (neighbouring
+// tiles of the same heads, which share K/V in its L2), so every XCD gets an
+// equal share of every segment.  Each segment's workgroup count is padded to
+// a multiple of 8; padding workgroups return at once.
+constexpr int kMaxSeg = 8, kSegBlk = 8;
+using SegProblem = AttnArgsT<kSegBlk>;
+struct SegArgs {
+  int nseg;
+  int c8[kMaxSeg + 1];  // workgroups per XCD before segment s (cumulative)
+  SegProblem seg[kMaxSeg];
+};
+static_assert(sizeof(SegArgs) <= 4096, "kernel arguments of one launch");
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void ring_attn_bf16_seg(const SegArgs sa) {
+  __shared__ __attribute__((aligned(1024))) char smem[Bf16Cfg<D, NW>::LDS];
+  const int x = (int)blockIdx.x & 7, kx = (int)blockIdx.x >> 3;
+  int sg = 0;
+  while (sg + 1 < sa.nseg && kx >= sa.c8[sg + 1]) ++sg;
+  const SegProblem& a = sa.seg[sg];
+  const int per = sa.c8[sg + 1] - sa.c8[sg];  // this segment's workgroups per XCD
+  const int j = x * per + (kx - sa.c8[sg]);
+  if (j >= a.B * a.H * a.n_qtiles) return;  // padding
+  int b, h, qt;
+  tile_coords_in(a, j, b, h, qt);
+  attn_bf16_tile<D, NW, false>(a, smem, b, h, qt, 0, INT_MAX, -1);
 }
 // ---------------------------------------------------------------------------
 // fp32 kernel (no bf16 rounding anywhere; fp32 matrix-core products)
@@ -1338,6 +1397,70 @@ ra_status launch(AttnArgs& a, int D, ra_dtype dt, hipStream_t stream, const char
   if (err != hipSuccess)
     return ra::fail(RA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
   return RA_OK;
+}
+
+// bf16 problems of one head dimension in as few launches as possible:
+// kMaxSeg per launch, in the order given, all with the same waves per
+// workgroup (the choice bf16_waves makes for their workgroups together); a
+// problem with more than kSegBlk visited blocks takes a launch of its own.
+ra_status launch_segments(const AttnArgs* segs, int n, int D, hipStream_t stream,
+                          const char* name) {
+  long long wg8 = 0;
+  for (int i = 0; i < n; ++i) wg8 += (long long)segs[i].B * segs[i].H * ((segs[i].Sq + 255) / 256);
+  const int forced = ra::option(RA_OPT_ATTN_WAVES);
+  const int nw = forced == 4 || forced == 8 ? forced : wg8 >= 256 ? 8 : 4;
+  const int br = 32 * nw;
+  const int rowmax = ra::option(RA_OPT_ATTN_KERNEL) == RA_KERNEL_ROWMAX;
+  SegArgs sa{};
+  long long total = 0;  // workgroups per XCD so far
+  auto flush = [&]() -> ra_status {
+    if (sa.nseg == 0) return RA_OK;
+    sa.c8[sa.nseg] = (int)total;
+    if (total > 0) {
+      const dim3 grid((unsigned)(8 * total)), blk(64 * nw);
+      if (nw == 8) {
+        if (D == 128) hipLaunchKernelGGL((ring_attn_bf16_seg<128, 8>), grid, blk, 0, stream, sa);
+        else hipLaunchKernelGGL((ring_attn_bf16_seg<64, 8>), grid, blk, 0, stream, sa);
+      } else {
+        if (D == 128) hipLaunchKernelGGL((ring_attn_bf16_seg<128, 4>), grid, blk, 0, stream, sa);
+        else hipLaunchKernelGGL((ring_attn_bf16_seg<64, 4>), grid, blk, 0, stream, sa);
+      }
+      const hipError_t err = hipGetLastError();
+      if (err != hipSuccess)
+        return ra::fail(RA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
+    }
+    sa = SegArgs{};
+    total = 0;
+    return RA_OK;
+  };
+  for (int i = 0; i < n; ++i) {
+    const AttnArgs& s = segs[i];
+    if (s.nblk > kSegBlk) {  // rare: more visited blocks than a table entry holds
+      AttnArgs own = s;
+      const ra_status st = launch(own, D, RA_BF16, stream, name);
+      if (st != RA_OK) return st;
+      continue;
+    }
+    for (int bi = 0; bi < s.nblk; ++bi)
+      if (s.blk[bi].len > (1 << 30))
+        return ra::fail(RA_ERR_UNSUPPORTED, "%s: K/V block of %d rows (at most 2^30)", name,
+                        s.blk[bi].len);
+    const long long wgs = (long long)s.B * s.H * ((s.Sq + br - 1) / br);
+    const long long per = (wgs + 7) / 8;
+    if (sa.nseg == kMaxSeg || 8 * (total + per) > 0x7fffffffLL) {
+      const ra_status st = flush();
+      if (st != RA_OK) return st;
+    }
+    if (8 * per > 0x7fffffffLL) return ra::fail(RA_ERR_UNSUPPORTED, "%s: too many query tiles", name);
+    SegProblem& a = sa.seg[sa.nseg];
+    static_cast<AttnHead&>(a) = static_cast<const AttnHead&>(s);
+    for (int bi = 0; bi < s.nblk; ++bi) a.blk[bi] = s.blk[bi];
+    a.n_qtiles = (a.Sq + br - 1) / br;
+    a.rowmax = rowmax;
+    sa.c8[sa.nseg++] = (int)total;
+    total += per;
+  }
+  return flush();
 }
 
 ra_status check_common(const char* name, int B, int S, int H, int D, ra_dtype dt) {
@@ -1616,9 +1739,13 @@ extern "C" ra_status ra_ring_attn_fwd_varlen(const void* q_r, const void* const*
   int src[RA_MAX_P], cls[RA_MAX_P];
   st = ra_ring_schedule(P, rank, Sb, causal, S, src, cls);
   if (st != RA_OK) return st;
-  // one launch per sample that meets the rank's rows: its rows of the share
-  // against the parts of the visited blocks that lie inside the sample, in
-  // ring order (a packed sequence never attends across samples)
+  // every sample that meets the rank's rows is its own problem: its rows of
+  // the share against the parts of the visited blocks that lie inside the
+  // sample, in ring order (a packed sequence never attends across samples).
+  // bf16: the problems go to one launch (kMaxSeg at a time), the ones whose
+  // last query tile sees the most keys first; fp32: one launch each.
+  std::vector<AttnArgs> segs;
+  std::vector<long long> seg_work;
   for (int i = 0; i < n_seqs; ++i) {
     const long long s0 = cu_seqlens[i], s1 = cu_seqlens[i + 1];
     const long long r0 = s0 > q0 ? s0 : q0, r1 = s1 < q1 ? s1 : q1;
@@ -1656,10 +1783,23 @@ extern "C" ra_status ra_ring_attn_fwd_varlen(const void* q_r, const void* const*
       a.blk[a.nblk++] = KVBlock{(const char*)k_blocks[j] + off, (const char*)v_blocks[j] + off,
                                 k0, (int)(k1 - k0), c};
     }
+    if (dt == RA_BF16) {
+      segs.push_back(a);
+      seg_work.push_back((causal ? r1 : s1) - s0);
+      continue;
+    }
     st = launch(a, D, dt, (hipStream_t)stream, name);
     if (st != RA_OK) return st;
   }
-  return RA_OK;
+  if (segs.empty()) return RA_OK;
+  std::vector<int> order(segs.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int x, int y) { return seg_work[x] > seg_work[y]; });
+  std::vector<AttnArgs> sorted;
+  sorted.reserve(segs.size());
+  for (int i : order) sorted.push_back(segs[i]);
+  return launch_segments(sorted.data(), (int)sorted.size(), D, (hipStream_t)stream, name);
 }
 
 extern "C" ra_status ra_ring_attn_fwd(const void* q_r, const void* const* k_blocks,

@@ -688,6 +688,31 @@ def test_varlen_all_ranks(variant, causal):
             assert torch.isneginf(lse[:, outside]).all()
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_many_samples_one_launch(causal):
+    """The bf16 samples of a share go to one launch, eight at a time, and a
+    sample that spans more than eight visited blocks takes a launch of its
+    own: P = 16 shares of 256 rows, 44 short samples (up to 11 meeting one
+    share, some across two shares) over the first 1100 rows, then one sample
+    over the remaining 2996 rows (up to 12 visited blocks for the last
+    ranks), every rank against the oracle's same-sample attention."""
+    S, H, D, P = 4096, 2, 64, 16
+    Sb = S // P
+    cu = [0] + [37 + 25 * i for i in range(43)] + [1100, S]
+    q, k, v = (W.random_tensor((1, S, H, D), seed=s_, device="cuda") for s_ in (91, 92, 93))
+    kb, vb = blocks_of(k, P), blocks_of(v, P)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    for r in range(P):
+        q_r = q[:, r * Sb:(r + 1) * Sb].contiguous()
+        say("varlen many samples", causal, "rank", r)
+        o, lse = ra.ring_attn_fwd_varlen(q_r, kb, vb, r, cu, causal=causal)
+        torch.cuda.synchronize()
+        ref_o, ref_lse = oracle.packed_attention(qc[:, r * Sb:(r + 1) * Sb], kc, vc, cu,
+                                                 causal=causal, q_pos0=r * Sb)
+        check_bf16(o.cpu(), ref_o, f"varlen many causal={causal} r{r}")
+        check_lse(lse.cpu(), ref_lse, f"varlen many causal={causal} r{r}")
+
+
 def test_varlen_fp32_and_bad_tables():
     """fp32 through the fp32 kernel to 1e-5; boundaries that do not start at
     0, decrease or run past the sequence are refused before any launch."""
