@@ -314,7 +314,8 @@ void ring_attn_bwd_dq(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[2][2 * C::TILE];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, col = lane & 31,
+            half = lane >> 5;
   const int n_qt = (a.Sq + ROWS - 1) / ROWS;
   // Workgroups are dispatched round-robin over the 8 XCDs: remap so that
   // every XCD takes a contiguous range of heads, and the workgroups resident
@@ -557,10 +558,15 @@ __device__ __forceinline__ void step_p(PairLane<D, 0>& w, unsigned bof, unsigned
   };
   // P of (query m = 32TF + 8g + 4half + i, this lane's key) for v = 4g + i,
   // hidden when m < rel_h + 4half
+  // the mask bound with the tile's need folded in, once per step; opaque to
+  // the compiler, which would otherwise split it back into a scalar test
+  // per weight
+  int rel_m = need ? rel_h : INT_MIN;
+  asm volatile("" : "+v"(rel_m));
   auto p_val = [&](int v) {
     const int g = v >> 2, i = v & 3;
     float x = sc[v] * c_scale - as_f32(st[g])[i];
-    if (need && 32 * TF + 8 * g + i < rel_h) x = -INFINITY;
+    if (32 * TF + 8 * g + i < rel_m) x = -INFINITY;
     pf[v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(x);
   };
 #pragma unroll
@@ -710,6 +716,16 @@ __device__ __forceinline__ void pair_step(PairLane<D, ROLE>& w, bool f, bool b, 
   }
 }
 
+// Both parts of a step of either role (the steady state).
+template <int D, int ROLE, int TF, int TB>
+__device__ __forceinline__ void step_both(PairLane<D, ROLE>& w, unsigned bof, unsigned bob,
+                                          bool need, int rel_h, float c_scale, bf16x8 (&pf)[2],
+                                          const bf16x8 (&pb)[2], f32x16& scf, u32x4 (&stf)[4],
+                                          const f32x16& scb, u32x4 (&stb)[4]) {
+  if constexpr (ROLE == 0) step_p<D, true, true, TF, TB>(w, bof, bob, need, rel_h, c_scale, pf, pb);
+  else step_ds<D, true, true, TF, TB>(w, bof, bob, scf, stf, scb, stb);
+}
+
 template <int D, int ROLE>
 __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave, int lane) {
   using C = Cfg<D>;
@@ -774,25 +790,37 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
   // and 1 (D)
   // (query head, query tile) of an iteration, advanced by one per
   // iteration (no division in the loop)
+  // The copy cursor also carries its tile's byte offset in Q / dO, its
+  // offset in the statistics rows and the rows left in the head, advanced
+  // by additions.
   struct ItCur {
     int h, ti;
+    long long qoff, soff;
+    int left;
+  };
+  const long long q_step = (long long)kTile * HD2;
+  auto it_start = [&](int h) {
+    return ItCur{h, t0, (((long long)b * a.Sq + (long long)t0 * kTile) * a.H + h) * D * 2,
+                 ((long long)b * a.H + h) * a.Sq + (long long)t0 * kTile, a.Sq - t0 * kTile};
   };
   auto it_next = [&](ItCur& c) {
     if (++c.ti == n_t) {
-      c.ti = t0;
-      ++c.h;
+      c = it_start(c.h + 1);
+    } else {
+      c.qoff += q_step;
+      c.soff += kTile;
+      c.left -= kTile;
     }
   };
+  const long long stat_plane = wave ? (long long)a.B * a.H * a.Sq : 0;
   auto copy_q = [&](const ItCur& c, unsigned buf_base) {
-    const int h = c.h, ti = c.ti;
-    const long long stat0 = ((long long)b * a.H + h) * a.Sq;
-    const long long off = (((long long)b * a.Sq + (long long)ti * kTile) * a.H + h) * D * 2;
-    const int rows = min(kTile, a.Sq - ti * kTile);
+    const long long off = c.qoff;
+    const int rows = min(kTile, c.left);
     const unsigned dst = buf_base + wave * PC::DMA * 1024;
     copy_tile<D, 8>((const char*)a.q + off, rows, HD2, voff, dst);
     copy_tile<D, 8>((const char*)a.dout + off, rows, HD2, voff, dst + C::TILE);
     if (wave < 2) {
-      const float* src = a.stats + (wave ? (long long)a.B * a.H * a.Sq : 0) + stat0 + ti * kTile;
+      const float* src = a.stats + stat_plane + c.soff;
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, rows * 4, kRsrcWord3);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -810,11 +838,13 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
   // step that begins tile it (its buffer held tile it-1, read to the end by
   // then), and is waited for before the barrier ending tile it+1's first step.
   const float c_scale = a.scale_log2;
-  auto tile = [&](const ItCur& c, bool& live, bool& need, int& rel_h) {
+  // need: the tile takes the mask.  That includes every tile dead for the
+  // wave's keys (wholly in their causal past, or keys all at or past
+  // valid_len): it runs fully masked, so its weights are exact zeros and the
+  // loop needs no branch around matrix work.
+  auto tile = [&](const ItCur& c, bool& need, int& rel_h) {
     const int ti = c.ti;
     const long long qp0 = qpos(a, ti * kTile);
-    const long long qp_hi = qp0 + min(kTile, a.Sq - ti * kTile) - 1;
-    live = !(a.causal && kw_lo > qp_hi) && kw_lo < a.valid_len;
     need = kw_hi >= a.valid_len || (a.causal && kw_hi > qp0);
     int rel = 0;
     if (kpos >= a.valid_len) rel = kTile;
@@ -827,7 +857,7 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
     else if (wave < 2) wait_vmcnt<2 * PC::DMA + 1>();
     else wait_vmcnt<2 * PC::DMA>();
   };
-  ItCur cq{hk * G, t0}, ct{hk * G, t0};  // the next copy's iteration, tile()'s
+  ItCur cq = it_start(hk * G), ct = cq;  // the next copy's iteration, tile()'s
   if (n_it > 0) copy_q(cq, base);
   it_next(cq);
   if (n_it > 1) copy_q(cq, base + PC::BUF);
@@ -839,37 +869,39 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
   bf16x8 p0[2], p1[2];
   f32x16 scA = f32x16{}, scB = f32x16{};
   u32x4 stA[4] = {}, stB[4] = {};
-  bool live = false, need = false;
+  bool need = false;
   int rel_h = 0;
-  if (n_it > 0) tile(ct, live, need, rel_h);
-  pair_step<D, ROLE, 0, 1>(w, live, false, 0, 0, need, rel_h, c_scale, p0, p1, scA, stA, scB, stB);
+  if (n_it > 0) tile(ct, need, rel_h);
+  pair_step<D, ROLE, 0, 1>(w, n_it > 0, false, 0, 0, need, rel_h, c_scale, p0, p1, scA, stA, scB,
+                           stB);
   pipeline_barrier();  // P of tile 0, half 0
   unsigned bo = 0;     // buffer of tile it
-  for (int it = 0; it < n_it; ++it) {
+  // Every tile but the last: both parts of both steps always run (dead
+  // tiles fully masked, as above).
+  for (int it = 0; it + 1 < n_it; ++it) {
     const unsigned bo_n = bo + PC::BUF == PC::NBUF * PC::BUF ? 0 : bo + PC::BUF;
     if (it + 2 < n_it) {
       copy_q(cq, base + (bo_n + PC::BUF == PC::NBUF * PC::BUF ? 0 : bo_n + PC::BUF));
       it_next(cq);
     }
     // step 1: half 1 of tile it forward, half 0 backward
-    pair_step<D, ROLE, 1, 0>(w, live, live, bo, bo, need, rel_h, c_scale, p1, p0, scB, stB, scA,
-                             stA);
-    if (it + 1 < n_it) wait_copy(it + 2 < n_it);
+    step_both<D, ROLE, 1, 0>(w, bo, bo, need, rel_h, c_scale, p1, p0, scB, stB, scA, stA);
+    wait_copy(it + 2 < n_it);
     pipeline_barrier();  // P of half 1; tile it+1 is in LDS
     // step 2: half 0 of tile it+1 forward, half 1 of tile it backward
-    bool live_n = false, need_n = false;
-    int rel_n = 0;
-    if (it + 1 < n_it) {
-      it_next(ct);
-      tile(ct, live_n, need_n, rel_n);
-    }
-    pair_step<D, ROLE, 0, 1>(w, live_n, live, bo_n, bo, need_n, rel_n, c_scale, p0, p1, scA, stA,
-                             scB, stB);
+    it_next(ct);
+    tile(ct, need, rel_h);
+    step_both<D, ROLE, 0, 1>(w, bo_n, bo, need, rel_h, c_scale, p0, p1, scA, stA, scB, stB);
     pipeline_barrier();  // P of tile it+1, half 0; tile it read to the end
-    live = live_n;
-    need = need_n;
-    rel_h = rel_n;
     bo = bo_n;
+  }
+  if (n_it > 0) {
+    // the last tile: its second half, then nothing new
+    step_both<D, ROLE, 1, 0>(w, bo, bo, need, rel_h, c_scale, p1, p0, scB, stB, scA, stA);
+    pipeline_barrier();  // P of half 1
+    pair_step<D, ROLE, 0, 1>(w, false, true, bo, bo, need, rel_h, c_scale, p0, p1, scA, stA, scB,
+                             stB);
+    pipeline_barrier();
   }
 
   if (key_ok) {
@@ -895,7 +927,7 @@ template <int D>
 __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ring_attn_bwd_dkv_pair(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[PairCfg<D>::LDS];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (wave < 4) pair_body<D, 0>(a, smem, wave, lane);
   else pair_body<D, 1>(a, smem, wave, lane);
 }
