@@ -378,6 +378,41 @@ def test_noalloc_split_under_graph_capture():
         assert torch.equal(l_g.view(torch.int32), l_e.view(torch.int32)), rep
 
 
+def test_explicit_stream_orders_default_buffers():
+    """Calls given stream= allocate and zero-fill their default outputs and
+    scratch on that stream: with the current stream still busy (and the
+    side stream not waiting for it), the backward (zero-filled dq / dk / dv,
+    statistics scratch) and a split forward (partial workspace) on the side
+    stream give the same bits as on the current stream."""
+    B, S, H, D, P, rank = 1, 2048, 4, 64, 2, 1
+    q, k, v, do = (W.random_tensor((B, S, H, D), seed=s_, device="cuda") for s_ in (91, 92, 93, 94))
+    Sb = S // P
+    q_r, do_r = q[:, rank * Sb:].contiguous(), do[:, rank * Sb:].contiguous()
+    kb, vb = blocks_of(k, P), blocks_of(v, P)
+    o_r, lse_r = ra.ring_attn_fwd(q_r, kb, vb, rank, causal=True)
+    ref_b = ra.ring_attn_bwd(q_r, kb, vb, o_r, do_r, lse_r, rank, causal=True)
+    ref_f = ra.ring_attn_fwd(q_r, kb, vb, rank, split=2)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    # keep the current stream busy for a while (fp32 products, no transposed views)
+    a = torch.randn(4096, 4096, device="cuda")
+    for _ in range(12):
+        a = torch.mm(a, a) * 1e-3
+    say("explicit stream: calls on the side stream while the current one is busy")
+    got_b = ra.ring_attn_bwd(q_r, kb, vb, o_r, do_r, lse_r, rank, causal=True, stream=side)
+    got_f = ra.ring_attn_fwd(q_r, kb, vb, rank, split=2, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(got_b[0], ref_b[0])
+    for j in range(P):
+        assert torch.equal(got_b[1][j], ref_b[1][j]), j
+        assert torch.equal(got_b[2][j], ref_b[2][j]), j
+    assert torch.equal(got_f[0].view(torch.int16), ref_f[0].view(torch.int16))
+    assert torch.equal(got_f[1].view(torch.int32), ref_f[1].view(torch.int32))
+    assert torch.isfinite(a).all()
+
+
 def test_split_ring_errors():
     """A run count below one is refused; a split without workspace or with
     too small a workspace is refused before any launch."""
