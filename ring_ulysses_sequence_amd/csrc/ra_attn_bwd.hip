@@ -67,9 +67,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRows = 32 * kWaves;  // query rows (dq) or keys (dkv) per workgroup
+constexpr int kRows = 128;          // keys per dK/dV workgroup (4 wave pairs x 32)
 constexpr int kTile = 64;           // rows per copied tile
 constexpr int kPF = 2;              // operand reads in flight ahead of use (pairs)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -152,7 +150,7 @@ __device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
 // wave's TILE / 1024 / NWV KiB land at byte address dst, dst + 1024, ..;
 // voff[i] is the source offset of this lane's chunk (row * HD2 + swizzled
 // chunk * 16).
-template <int D, int NWV = kWaves>
+template <int D, int NWV>
 __device__ __forceinline__ void copy_tile(const char* src, int rows, int HD2, const int* voff,
                                           unsigned dst) {
   using C = Cfg<D>;
@@ -211,7 +209,7 @@ __device__ __forceinline__ s16x4 read_tr_g(int g, unsigned addr) {
 
 // Source offsets of this lane's copy chunks within a tile copied by NWV
 // waves.
-template <int D, int NWV = kWaves>
+template <int D, int NWV>
 __device__ __forceinline__ void copy_offsets(int wave, int lane, int HD2, int* voff) {
   using C = Cfg<D>;
   constexpr int DMA = C::TILE / 1024 / NWV;
