@@ -837,9 +837,9 @@ __device__ __forceinline__ void pair_body(const BwdArgs& a, char* smem, int wave
   // then), and is waited for before the barrier ending tile it+1's first step.
   const float c_scale = a.scale_log2;
   // need: the tile takes the mask.  That includes every tile dead for the
-  // wave's keys (wholly in their causal past, or keys all at or past
-  // valid_len): it runs fully masked, so its weights are exact zeros and the
-  // loop needs no branch around matrix work.
+  // wave's keys (causal: all its queries before the first of those keys; or
+  // those keys all at or past valid_len): it runs fully masked, so its
+  // weights are exact zeros and the loop needs no branch around matrix work.
   auto tile = [&](const ItCur& c, bool& need, int& rel_h) {
     const int ti = c.ti;
     const long long qp0 = qpos(a, ti * kTile);
