@@ -232,21 +232,24 @@ __device__ __forceinline__ float online_update(float (&s)[NS], RowState& st, flo
 // lanes j/4, j/4+4, j/4+8, j/4+12; supplier r = 4e + q points at
 // V[key_e][d0 + 4q .. d0 + 4q + 3], so lane j gets V[key_0..3][d0 + j].
 //
-// Software pipeline (per wave, step n over the visited tiles):
-//   LDS holds K(n+1), V(n) and V(n+1) (copied during steps n-2, n-1);
-//   copy K(n+2) and V(n+2) into the buffers step n-1 released;
+// Software pipeline (per wave, step n over the visited tiles; tiles are
+// copied LEAD steps ahead, LEAD = 2 with 4 waves, 3 with 8):
+//   copy K(n+LEAD) and V(n+LEAD) into buffers that earlier steps released;
 //   front: S^T(n+1) = K(n+1) Q^T on the matrix cores, interleaved with the
 //          exponentials of the second half (keys 32..63) of tile n;
 //   back:  O^T += V(n)^T P(n)^T on the matrix cores, interleaved with the
 //          mask and the exponentials of the first half of tile n+1;
-//   wait for this wave's K(n+2) copy (V(n+2) may stay in flight), barrier.
+//   wait for this wave's copies of K(n+2) and V(n+1) (later ones may stay
+//   in flight), barrier.
 // Every matrix phase thus carries half a tile of softmax work, so a wave on
-// its own keeps the matrix pipe fed, and the second wave of the SIMD (from
-// another workgroup) fills what is left.  Two K and three V buffers (80 KiB
-// at D = 128: two workgroups per CU).  Operand reads run four matrix ops
-// ahead of their use.  The loop is unrolled by two so the K parity, the
-// score registers and the P registers are compile-time constants; the V
-// buffer index cycles mod 3 at run time.
+// its own keeps the matrix pipe fed, and the second wave of the SIMD fills
+// what is left.  4 waves: two K and three V buffers (80 KiB at D = 128, two
+// workgroups per CU), buffer indices at run time, the loop unrolled by two
+// (the score and P register sets swap roles).  8 waves: four K and four V
+// buffers (128 KiB, one workgroup per CU) and the loop unrolled by four, so
+// that every buffer index is a constant and the operand reads carry the
+// buffer offset as an immediate.  Operand reads run four matrix ops ahead
+// of their use.
 //
 // Reference max ([RA] §3.2 with a moving reference).  P is formed as
 // 2^(s - m_ref) against a per-row reference m_ref that u and l share, so
@@ -269,11 +272,14 @@ struct Bf16Cfg {
   static constexpr int ROWB = D * 2;              // bytes per key row in LDS
   static constexpr int TILE = BC * ROWB;          // one K or V tile
   // copies of tile n + LEAD are issued in step n: two K and three V buffers
-  // for 4 waves (80 KiB at D = 128, two workgroups per CU), three and four
-  // for 8 waves (112 KiB, one workgroup per CU)
+  // for 4 waves (80 KiB at D = 128, two workgroups per CU), four and four
+  // for 8 waves (128 KiB, one workgroup per CU).  The 8-wave loop runs four
+  // steps per iteration, so that every buffer index in it is a constant and
+  // the operand reads take the buffer offset as an immediate.
   static constexpr int LEAD = NW == 8 ? 3 : 2;
-  static constexpr int KBUF = LEAD;
+  static constexpr int KBUF = NW == 8 ? 4 : LEAD;
   static constexpr int VBUF = LEAD + 1;
+  static constexpr bool FIXED = NW == 8;
   static constexpr int KB = 0;                    // K buffers at KB + p*TILE
   static constexpr int VB = KBUF * TILE;          // V buffers at VB + p*TILE
   static constexpr int LDS = (KBUF + VBUF) * TILE;
@@ -475,7 +481,7 @@ struct WaveState {
   float m_true;            // exact running max (base 2; row-max path only)
   float l_run;             // this lane's half of the sum of bf16(2^(s - m_ref))
   unsigned kaddr[C::NC];   // LDS byte address of the K operand reads (buffer 0)
-  unsigned vaddr[C::NDT];  // LDS byte offset of the V operand reads in a buffer
+  unsigned vaddr[C::NDT];  // LDS byte address of the V operand reads (buffer 0)
   int voffk[C::DMA];       // copy source offsets (K) within a tile
   int voffv[C::DMA];       // copy source offsets (V) within a tile
 };
@@ -550,14 +556,14 @@ __device__ __forceinline__ float move_reference(float& m_ref, float& l_run, floa
 // Softmax of one half (score tile KT: keys 32 KT .. 32 KT + 31) as a
 // software pipeline over 8 pairs of scores: time T shifts and scales pair T,
 // exponentiates pair T-1, and packs pair T-2 to bf16 and adds the rounded
-// pair to the row sum (10 time steps).  The packed pair lands in element
-// 2 (pair % 4), +1 of fragment pair / 4 of the half; the two fragments are
-// built fresh (not as updates of the previous tile's registers, which would
-// keep those alive) and stored to P fragments 2 KT, 2 KT + 1 at the end.
+// pair to the row sum (10 time steps).  The packed pair is dword pair % 4
+// of fragment pair / 4 of the half; the two fragments are built fresh (not
+// as updates of the previous tile's registers, which would keep those
+// alive) and stored to P fragments 2 KT, 2 KT + 1 at the end.
 struct HalfSoftmax {
   float x[3][2];
   float lp[2];
-  bf16x8 g[2];
+  u32x4 g[2];
 };
 template <int KT, int T>
 __device__ __forceinline__ void half_softmax_step(HalfSoftmax& hs, const f32x16& s, float c,
@@ -580,14 +586,21 @@ __device__ __forceinline__ void half_softmax_step(HalfSoftmax& hs, const f32x16&
     const bf16x2 pr = {(__bf16)hs.x[p % 3][0], (__bf16)hs.x[p % 3][1]};
     unsigned d;
     __builtin_memcpy(&d, &pr, 4);
-    hs.lp[0] += __uint_as_float(d << 16);
-    hs.lp[1] += __uint_as_float(d & 0xffff0000u);
-    hs.g[g][e] = pr[0];
-    hs.g[g][e + 1] = pr[1];
+    // one packed pair serves the fragment and both sums (left visible to the
+    // compiler, it converts the low weight a second time for its sum)
+    asm volatile("" : "+v"(d));
+    if constexpr (p == 0) {  // the sums start at the first pair, not at 0 + it
+      hs.lp[0] = __uint_as_float(d << 16);
+      hs.lp[1] = __uint_as_float(d & 0xffff0000u);
+    } else {
+      hs.lp[0] += __uint_as_float(d << 16);
+      hs.lp[1] += __uint_as_float(d & 0xffff0000u);
+    }
+    hs.g[g][e / 2] = d;
     // pin the pair's work to this slot: without a use here the compiler
     // sinks it below later branches, out of the matrix phase it fills
     asm volatile("" : "+v"(hs.lp[0]), "+v"(hs.lp[1]));
-    if constexpr (p % 4 == 3) pb[2 * KT + g] = hs.g[g];
+    if constexpr (p % 4 == 3) pb[2 * KT + g] = __builtin_bit_cast(bf16x8, hs.g[g]);
   }
 }
 constexpr int kSoftSteps = 10;
@@ -625,7 +638,8 @@ __device__ __forceinline__ float half_softmax_all(const f32x16& s, float c, floa
 // the sequence the products read a stale buffer whose results are unused.
 // Keeping the matrix chains free of branches keeps the accumulators in one
 // set of registers.
-template <int D, int NW>
+// KOFF >= 0: the K buffer's byte offset as a constant (koff unused).
+template <int D, int NW, int KOFF = -1>
 __device__ __forceinline__ float step_front(WaveState<D, NW>& w, unsigned koff,
                                             const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
                                             bf16x8 (&pb)[4], float c) {
@@ -638,12 +652,17 @@ __device__ __forceinline__ float step_front(WaveState<D, NW>& w, unsigned koff,
   // op i: score tile kt = i % 2, k-step ci = i / 2 (consecutive ops never
   // depend on each other)
   unsigned kbase[C::NC];
+  if constexpr (KOFF < 0) {
 #pragma unroll
-  for (int ci = 0; ci < C::NC; ++ci) kbase[ci] = w.kaddr[ci] + koff;
+    for (int ci = 0; ci < C::NC; ++ci) kbase[ci] = w.kaddr[ci] + koff;
+  }
   bf16x8 kf[PF + 1];
   auto kread = [&](auto ic) {
     constexpr int i = decltype(ic)::value;
-    kf[i % (PF + 1)] = lds_read_b128<(i % 2) * 32 * C::ROWB>(kbase[i / 2]);
+    if constexpr (KOFF < 0)
+      kf[i % (PF + 1)] = lds_read_b128<(i % 2) * 32 * C::ROWB>(kbase[i / 2]);
+    else
+      kf[i % (PF + 1)] = lds_read_b128<KOFF + (i % 2) * 32 * C::ROWB>(w.kaddr[i / 2]);
   };
   static_for<0, PF>([&](auto ic) { kread(ic); });
   static_for<0, N>([&](auto ic) {
@@ -663,7 +682,9 @@ __device__ __forceinline__ float step_front(WaveState<D, NW>& w, unsigned koff,
 // Back half of a step: O^T += V(n)^T P(n)^T from the V buffer at LDS byte
 // offset vbuf, interleaved with the first half of tile n+1's softmax.
 // Returns that half's contribution to the row sum (unconditional, as above).
-template <int D, int NW>
+// VOFF >= 0: the V buffer's byte offset from buffer 0 as a constant (vbuf
+// unused).
+template <int D, int NW, int VOFF = -1>
 __device__ __forceinline__ float step_back(WaveState<D, NW>& w, unsigned vbuf,
                                            const bf16x8 (&pb)[4], const f32x16 (&s_nxt)[2],
                                            bf16x8 (&pb_nxt)[4], float c) {
@@ -677,12 +698,17 @@ __device__ __forceinline__ float step_back(WaveState<D, NW>& w, unsigned vbuf,
   // (keys 16G .. 16G+7 and 16G+8 .. 16G+15 of d tile dt); consecutive ops
   // accumulate into different d tiles
   unsigned vbase[C::NDT];
+  if constexpr (VOFF < 0) {
 #pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt) vbase[dt] = vbuf + w.vaddr[dt];
+    for (int dt = 0; dt < C::NDT; ++dt) vbase[dt] = vbuf + w.vaddr[dt];
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) vbase[dt] = w.vaddr[dt];
+  }
   s16x8 vr[PF + 1];
   auto vread = [&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    constexpr int off = (j / C::NDT) * 16 * C::ROWB;
+    constexpr int off = (VOFF < 0 ? 0 : VOFF) + (j / C::NDT) * 16 * C::ROWB;
     const s16x4 lo = lds_read_tr16<off>(vbase[j % C::NDT]);
     const s16x4 hi = lds_read_tr16<off + 8 * C::ROWB>(vbase[j % C::NDT]);
     vr[j % (PF + 1)] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -802,28 +828,38 @@ __device__ __forceinline__ void first_half_check(const StepCtx<A>& k, WaveState<
 
 // One pipeline step.  PAR = n & 1 only swaps the roles of the two score
 // and P register sets.  K(n) sits in K buffer kb, K(n+1) in the next one,
-// V(n) in V buffer vb; the copies of tile n + LEAD go to K(n)'s buffer
-// (read in the step before) and to V(n-1)'s.  d0, d1, d2 describe tiles n,
-// n+1, n+2 (d2 only with LEAD = 3) and cur stands at tile n + LEAD.
-template <int D, int NW, bool ML, int PAR, class A>
+// V(n) in V buffer vb; the copies of tile n + LEAD go to K buffer
+// kb + LEAD and V buffer vb + LEAD (modulo the buffer counts: K(n)'s or
+// K(n-1)'s buffer and V(n-1)'s, read in earlier steps).  FS >= 0: the
+// step's place in a loop iteration of KBUF = VBUF steps, which makes every
+// buffer index a constant (kb and vb are then unused).  d0, d1, d2 describe
+// tiles n, n+1, n+2 (d2 only with LEAD = 3) and cur stands at tile n + LEAD.
+template <int D, int NW, bool ML, int PAR, int FS = -1, class A>
 __device__ __forceinline__ void pipeline_step(const StepCtx<A>& k, char* smem, WaveState<D, NW>& w,
                                               f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
                                               bf16x8 (&pb_cur)[4], bf16x8 (&pb_nxt)[4],
                                               float& lsum_cur, float& lsum_nxt, Seq& cur,
                                               TDesc& d0, TDesc& d1, TDesc& d2, int& kb, int& vb) {
   using C = Bf16Cfg<D, NW>;
+  static_assert(FS < 0 || C::KBUF == C::VBUF, "constant buffers need equal K and V counts");
   const A& a = *k.a;
   const int kb1 = kb + 1 == C::KBUF ? 0 : kb + 1;  // K(n+1)
-  const int vcp = vb == 0 ? C::VBUF - 1 : vb - 1;  // V(n-1)'s buffer
+  const int kcp = kb + C::LEAD >= C::KBUF ? kb + C::LEAD - C::KBUF : kb + C::LEAD;
+  const int vcp = vb == 0 ? C::VBUF - 1 : vb - 1;  // V(n-1)'s buffer = vb + LEAD
   // copies of tile n + LEAD: K first, so that waiting for K leaves V in flight
   const TDesc dl = seq_desc(a, cur);
   if (dl.valid)
-    copy_tile<D, NW>(cur, k.HD2, k.wave, w.voffk, w.voffv, smem, C::KB + kb * C::TILE,
-                     C::VB + vcp * C::TILE);
-  const unsigned lds0 = (unsigned)(size_t)(lds_void_ptr)smem;
+    copy_tile<D, NW>(cur, k.HD2, k.wave, w.voffk, w.voffv, smem,
+                     C::KB + (FS >= 0 ? (FS + C::LEAD) % C::KBUF : kcp) * C::TILE,
+                     C::VB + (FS >= 0 ? (FS + C::LEAD) % C::VBUF : vcp) * C::TILE);
 
   // front: S^T(n+1) with the second half of P(n) (tile n is valid here)
-  float l2 = step_front<D, NW>(w, lds0 + C::KB + kb1 * C::TILE, s_cur, s_nxt, pb_cur, k.c);
+  float l2;
+  if constexpr (FS >= 0)
+    l2 = step_front<D, NW, C::KB + (FS + 1) % C::KBUF * C::TILE>(w, 0u, s_cur, s_nxt, pb_cur,
+                                                                   k.c);
+  else
+    l2 = step_front<D, NW>(w, C::KB + kb1 * C::TILE, s_cur, s_nxt, pb_cur, k.c);
   {
     // second half over the bound: move the reference, scale u, l and the
     // first half's weights, redo the second half
@@ -843,7 +879,10 @@ __device__ __forceinline__ void pipeline_step(const StepCtx<A>& k, char* smem, W
   float alpha = 1.0f;
   bool moved = false;
   if (d1.valid) alpha = tile_setup<D, NW, ML>(k, w, s_nxt, d1, moved);
-  lsum_nxt = step_back<D, NW>(w, lds0 + C::VB + vb * C::TILE, pb_cur, s_nxt, pb_nxt, k.c);
+  if constexpr (FS >= 0)
+    lsum_nxt = step_back<D, NW, FS % C::VBUF * C::TILE>(w, 0u, pb_cur, s_nxt, pb_nxt, k.c);
+  else
+    lsum_nxt = step_back<D, NW>(w, vb * C::TILE, pb_cur, s_nxt, pb_nxt, k.c);
   if (moved) scale_o<D, NW>(w, alpha);  // after every product of the old reference
   if (d1.valid) first_half_check<D, NW>(k, w, s_nxt[0], pb_nxt, lsum_nxt);
 
@@ -985,7 +1024,7 @@ __device__ __forceinline__ void attn_bf16_tile(const A& a, char* smem, int b, in
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) {
       const int d0 = 32 * dt + 16 * (g & 1) + 4 * q;
-      w.vaddr[dt] = kl * C::ROWB + swz_v<D>(kl, d0 >> 3) * 16 + (d0 & 7) * 2;
+      w.vaddr[dt] = lds0 + C::VB + kl * C::ROWB + swz_v<D>(kl, d0 >> 3) * 16 + (d0 & 7) * 2;
     }
   }
 #pragma unroll
@@ -1021,13 +1060,26 @@ __device__ __forceinline__ void attn_bf16_tile(const A& a, char* smem, int b, in
     lA = half_softmax_all<0>(sA[0], k.c, w.m_use, pA);
     first_half_check<D, NW>(k, w, sA[0], pA, lA);
   }
-  __syncthreads();  // K buffer 0 is free for K(LEAD)
+  __syncthreads();  // every wave is done with tile 0's K before any new copy
 
   int kb = 0, vb = 0;  // K and V buffers of tile n
-  while (d0.valid) {
-    pipeline_step<D, NW, ML, 0>(k, smem, w, sA, sB, pA, pB, lA, lB, cur, d0, d1, d2, kb, vb);
-    if (!d0.valid) break;
-    pipeline_step<D, NW, ML, 1>(k, smem, w, sB, sA, pB, pA, lB, lA, cur, d0, d1, d2, kb, vb);
+  if constexpr (C::FIXED) {
+    static_assert(C::KBUF == 4 && C::VBUF == 4, "four steps per iteration");
+    while (d0.valid) {
+      pipeline_step<D, NW, ML, 0, 0>(k, smem, w, sA, sB, pA, pB, lA, lB, cur, d0, d1, d2, kb, vb);
+      if (!d0.valid) break;
+      pipeline_step<D, NW, ML, 1, 1>(k, smem, w, sB, sA, pB, pA, lB, lA, cur, d0, d1, d2, kb, vb);
+      if (!d0.valid) break;
+      pipeline_step<D, NW, ML, 0, 2>(k, smem, w, sA, sB, pA, pB, lA, lB, cur, d0, d1, d2, kb, vb);
+      if (!d0.valid) break;
+      pipeline_step<D, NW, ML, 1, 3>(k, smem, w, sB, sA, pB, pA, lB, lA, cur, d0, d1, d2, kb, vb);
+    }
+  } else {
+    while (d0.valid) {
+      pipeline_step<D, NW, ML, 0>(k, smem, w, sA, sB, pA, pB, lA, lB, cur, d0, d1, d2, kb, vb);
+      if (!d0.valid) break;
+      pipeline_step<D, NW, ML, 1>(k, smem, w, sB, sA, pB, pA, lB, lA, cur, d0, d1, d2, kb, vb);
+    }
   }
 
   // ---- epilogue: o = u / l, lse = m + ln l ([RA] §3.2; [SPD] §四) ----
