@@ -55,6 +55,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "ra_cdna4.h"
 #include "ra_internal.h"
@@ -188,15 +189,6 @@ struct LaneAddr {
       hi[dt] = base + (kl + 8) * C::ROWB + swz<D>(kl + 8, d0 >> 3) * 16 + (d0 & 7) * 2;
     }
   }
-  __device__ __forceinline__ void shift(int delta) {
-#pragma unroll
-    for (int c = 0; c < C::NC; ++c) row[c] += delta;
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) {
-      lo[dt] += delta;
-      hi[dt] += delta;
-    }
-  }
 };
 
 // Transposed read of rows 16G + .. (G = 2T + g, g a constant after unrolling)
@@ -232,13 +224,14 @@ struct DqLane {
   LaneAddr<D> ad;
 };
 
-// Rows 32T .. 32T+31 of the K/V tiles in the current buffer (K at 0, V at
-// TILE): S^T, dP^T, the mask, dS^T and dQ^T += K^T dS^T.
-template <int D, int T>
+// Rows 32T .. 32T+31 of the K/V tiles in the buffer at byte offset BO from
+// buffer 0 (K at BO, V at BO + TILE): S^T, dP^T, the mask, dS^T and
+// dQ^T += K^T dS^T.
+template <int D, int T, int BO>
 __device__ __forceinline__ void dq_half(DqLane<D>& w, float dsum, float lse2, float c_scale,
                                         bool need, int lim_h) {
   using C = Cfg<D>;
-  constexpr int RO = T * 32 * C::ROWB;
+  constexpr int RO = BO + T * 32 * C::ROWB;
   constexpr int NB = kPF + 1;
   f32x16 sc = f32x16{}, dpt = f32x16{};
   {
@@ -266,8 +259,8 @@ __device__ __forceinline__ void dq_half(DqLane<D>& w, float dsum, float lse2, fl
   s16x4 lo[NB], hi[NB];
 #pragma unroll
   for (int j = 0; j < kPF; ++j) {
-    lo[j] = read_tr_g<D, 32 * T * C::ROWB>(j / C::NDT, w.ad.lo[j % C::NDT]);
-    hi[j] = read_tr_g<D, 32 * T * C::ROWB>(j / C::NDT, w.ad.hi[j % C::NDT]);
+    lo[j] = read_tr_g<D, BO + 32 * T * C::ROWB>(j / C::NDT, w.ad.lo[j % C::NDT]);
+    hi[j] = read_tr_g<D, BO + 32 * T * C::ROWB>(j / C::NDT, w.ad.hi[j % C::NDT]);
   }
   // key j of the tile (j = 32T + 8(v/4) + 4half + v%4) is hidden for this
   // lane's query when j >= lim_h + 4half
@@ -287,8 +280,8 @@ __device__ __forceinline__ void dq_half(DqLane<D>& w, float dsum, float lse2, fl
   for (int j = 0; j < NJ; ++j) {
     if (j + kPF < NJ) {
       const int jn = j + kPF;
-      lo[jn % NB] = read_tr_g<D, 32 * T * C::ROWB>(jn / C::NDT, w.ad.lo[jn % C::NDT]);
-      hi[jn % NB] = read_tr_g<D, 32 * T * C::ROWB>(jn / C::NDT, w.ad.hi[jn % C::NDT]);
+      lo[jn % NB] = read_tr_g<D, BO + 32 * T * C::ROWB>(jn / C::NDT, w.ad.lo[jn % C::NDT]);
+      hi[jn % NB] = read_tr_g<D, BO + 32 * T * C::ROWB>(jn / C::NDT, w.ad.hi[jn % C::NDT]);
     }
     const int n = 2 * min(kPF, NJ - 1 - j);
     claim_lds_n(n, lo[j % NB]);
@@ -402,18 +395,21 @@ void ring_attn_bwd_dq(const BwdArgs a) {
   if (cb < a.nblk) copy_kv(cb, 0, dst0);
   wait_vmcnt<0>();
   pipeline_barrier();
-  int buf = 0;
   const float c_scale = a.scale_log2;
-  while (cb < a.nblk) {
+  // one tile from the buffer at byte offset BO (0 or 2 TILE); the loop below
+  // alternates the two, so that every operand read carries its buffer
+  // offset as an immediate
+  auto step = [&](auto boc) {
+    constexpr int BO = decltype(boc)::value;
     // the next tile's copy goes to the other buffer, last read in the
-    // previous iteration (before its closing barrier)
+    // previous step (before its closing barrier)
     int nb = cb, nt = ct + 1, nn = cn;
     if (nt >= nn) {
       nt = 0;
       ++nb;
       while (nb < a.nblk && (nn = ntiles(nb)) == 0) ++nb;
     }
-    if (nb < a.nblk) copy_kv(nb, nt, dst0 + (buf ^ 1) * 2 * C::TILE);
+    if (nb < a.nblk) copy_kv(nb, nt, dst0 + (BO ? 0 : 2 * C::TILE));
 
     const BwdBlock& kb = a.blk[cb];
     const long long kp0 = kb.k_pos0 + (long long)ct * kTile;
@@ -432,16 +428,19 @@ void ring_attn_bwd_dq(const BwdArgs a) {
     // as a 32-bit bound relative to this lane's first key of each group
     const int lim_h = (int)(lim < 0 ? 0 : (lim > kTile ? kTile : lim)) - 4 * half;
     if (live) {
-      dq_half<D, 0>(w, dsum, lse2, c_scale, need, lim_h);
-      dq_half<D, 1>(w, dsum, lse2, c_scale, need, lim_h);
+      dq_half<D, 0, BO>(w, dsum, lse2, c_scale, need, lim_h);
+      dq_half<D, 1, BO>(w, dsum, lse2, c_scale, need, lim_h);
     }
     wait_vmcnt<0>();
     pipeline_barrier();
-    w.ad.shift(buf ? -2 * C::TILE : 2 * C::TILE);
-    buf ^= 1;
     cb = nb;
     ct = nt;
     cn = nn;
+  };
+  while (cb < a.nblk) {
+    step(std::integral_constant<int, 0>{});
+    if (cb >= a.nblk) break;
+    step(std::integral_constant<int, 2 * C::TILE>{});
   }
 
   // dQ += scale * (dS K): this lane's row, features 32dt + 8g + 4half .. +3
