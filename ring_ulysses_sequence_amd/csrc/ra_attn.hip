@@ -639,10 +639,12 @@ __device__ __forceinline__ float half_softmax_all(const f32x16& s, float c, floa
 // Keeping the matrix chains free of branches keeps the accumulators in one
 // set of registers.
 // KOFF >= 0: the K buffer's byte offset as a constant (koff unused).
-template <int D, int NW, int KOFF = -1>
+// after_first: scalar work (the step's tile copies) issued once the first
+// two matrix ops are under way, instead of ahead of them.
+template <int D, int NW, int KOFF = -1, class Hook>
 __device__ __forceinline__ float step_front(WaveState<D, NW>& w, unsigned koff,
                                             const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
-                                            bf16x8 (&pb)[4], float c) {
+                                            bf16x8 (&pb)[4], float c, const Hook& after_first) {
   using C = Bf16Cfg<D, NW>;
   constexpr int N = C::NQK;
   constexpr int PF = kOperandLead;
@@ -674,6 +676,7 @@ __device__ __forceinline__ float step_front(WaveState<D, NW>& w, unsigned koff,
     s_nxt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % (PF + 1)], w.qf[ci],
                                                         ci == 0 ? f32x16{} : s_nxt[kt], 0, 0, 0);
     half_softmax_range<1, SoftSlot<i, N>::lo, SoftSlot<i, N>::hi>(hs, s_cur[1], c, nm, pb);
+    if constexpr (i == 1) after_first();
     __builtin_amdgcn_sched_barrier(0);
   });
   return hs.lp[0] + hs.lp[1];
@@ -846,20 +849,24 @@ __device__ __forceinline__ void pipeline_step(const StepCtx<A>& k, char* smem, W
   const int kb1 = kb + 1 == C::KBUF ? 0 : kb + 1;  // K(n+1)
   const int kcp = kb + C::LEAD >= C::KBUF ? kb + C::LEAD - C::KBUF : kb + C::LEAD;
   const int vcp = vb == 0 ? C::VBUF - 1 : vb - 1;  // V(n-1)'s buffer = vb + LEAD
-  // copies of tile n + LEAD: K first, so that waiting for K leaves V in flight
+  // copies of tile n + LEAD: K first, so that waiting for K leaves V in flight;
+  // issued from the front phase once its first matrix ops are under way (the
+  // buffers they overwrite were released by the barrier that ended step n-1)
   const TDesc dl = seq_desc(a, cur);
-  if (dl.valid)
-    copy_tile<D, NW>(cur, k.HD2, k.wave, w.voffk, w.voffv, smem,
-                     C::KB + (FS >= 0 ? (FS + C::LEAD) % C::KBUF : kcp) * C::TILE,
-                     C::VB + (FS >= 0 ? (FS + C::LEAD) % C::VBUF : vcp) * C::TILE);
+  auto copies = [&]() {
+    if (dl.valid)
+      copy_tile<D, NW>(cur, k.HD2, k.wave, w.voffk, w.voffv, smem,
+                       C::KB + (FS >= 0 ? (FS + C::LEAD) % C::KBUF : kcp) * C::TILE,
+                       C::VB + (FS >= 0 ? (FS + C::LEAD) % C::VBUF : vcp) * C::TILE);
+  };
 
   // front: S^T(n+1) with the second half of P(n) (tile n is valid here)
   float l2;
   if constexpr (FS >= 0)
     l2 = step_front<D, NW, C::KB + (FS + 1) % C::KBUF * C::TILE>(w, 0u, s_cur, s_nxt, pb_cur,
-                                                                   k.c);
+                                                                   k.c, copies);
   else
-    l2 = step_front<D, NW>(w, C::KB + kb1 * C::TILE, s_cur, s_nxt, pb_cur, k.c);
+    l2 = step_front<D, NW>(w, C::KB + kb1 * C::TILE, s_cur, s_nxt, pb_cur, k.c, copies);
   {
     // second half over the bound: move the reference, scale u, l and the
     // first half's weights, redo the second half
