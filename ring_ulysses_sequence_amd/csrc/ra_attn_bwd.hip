@@ -227,9 +227,15 @@ struct DqLane {
 // Rows 32T .. 32T+31 of the K/V tiles in the buffer at byte offset BO from
 // buffer 0 (K at BO, V at BO + TILE): S^T, dP^T, the mask, dS^T and
 // dQ^T += K^T dS^T.
-template <int D, int T, int BO>
+struct NoWork {
+  __device__ void operator()() const {}
+};
+// after_first: scalar work (the next tile's copy) issued once the first
+// matrix ops are under way.
+template <int D, int T, int BO, class Hook = NoWork>
 __device__ __forceinline__ void dq_half(DqLane<D>& w, float dsum, float lse2, float c_scale,
-                                        bool need, int lim_h) {
+                                        bool need, int lim_h,
+                                        const Hook& after_first = Hook{}) {
   using C = Cfg<D>;
   constexpr int RO = BO + T * 32 * C::ROWB;
   constexpr int NB = kPF + 1;
@@ -252,6 +258,7 @@ __device__ __forceinline__ void dq_half(DqLane<D>& w, float dsum, float lse2, fl
       claim_lds_n(n, va[c % NB]);
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(ka[c % NB]), w.qf[c], sc, 0, 0, 0);
       dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(va[c % NB]), w.df[c], dpt, 0, 0, 0);
+      if (c == 0) after_first();
     }
   }
   // the first K^T reads of the dQ product fly during the exponentials
@@ -409,7 +416,11 @@ void ring_attn_bwd_dq(const BwdArgs a) {
       ++nb;
       while (nb < a.nblk && (nn = ntiles(nb)) == 0) ++nb;
     }
-    if (nb < a.nblk) copy_kv(nb, nt, dst0 + (BO ? 0 : 2 * C::TILE));
+    // issued from the first matrix ops of the tile (the target buffer was
+    // released by the barrier that ended the previous step)
+    auto copies = [&]() {
+      if (nb < a.nblk) copy_kv(nb, nt, dst0 + (BO ? 0 : 2 * C::TILE));
+    };
 
     const BwdBlock& kb = a.blk[cb];
     const long long kp0 = kb.k_pos0 + (long long)ct * kTile;
@@ -428,8 +439,10 @@ void ring_attn_bwd_dq(const BwdArgs a) {
     // as a 32-bit bound relative to this lane's first key of each group
     const int lim_h = (int)(lim < 0 ? 0 : (lim > kTile ? kTile : lim)) - 4 * half;
     if (live) {
-      dq_half<D, 0, BO>(w, dsum, lse2, c_scale, need, lim_h);
+      dq_half<D, 0, BO>(w, dsum, lse2, c_scale, need, lim_h, copies);
       dq_half<D, 1, BO>(w, dsum, lse2, c_scale, need, lim_h);
+    } else {
+      copies();
     }
     wait_vmcnt<0>();
     pipeline_barrier();
