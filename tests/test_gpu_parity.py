@@ -1256,6 +1256,37 @@ def test_edge_cases_bf16(variant):
             assert np.all(og[~fin] == 0)
 
 
+def test_eight_wave_loop_exits():
+    """The 8-wave kernel runs four pipeline steps per loop iteration (its
+    buffer indices are constants): one 256-row workgroup per head over 1 to
+    9 key tiles and a ragged tenth, so the sequence ends after each of the
+    four steps, with and without the exact row max, causal and not, at
+    D = 128 and 64, against the oracle."""
+    g = torch.Generator().manual_seed(23)
+    mk = lambda *s: torch.randn(*s, generator=g).to(torch.bfloat16)
+    ra.set_attn_waves(8)
+    try:
+        for D in (128, 64):
+            q = mk(1, 256, 2, D)
+            for Sk in [64 * n for n in range(1, 10)] + [64 * 9 + 17]:
+                k, v = mk(1, Sk, 2, D), mk(1, Sk, 2, D)
+                for causal, qp in [(False, 0), (True, max(0, Sk - 200))]:
+                    for want_ml in (False, True):
+                        say("8-wave loop exits", D, Sk, causal, want_ml)
+                        o, lse, _, _ = ra.block_attn_fwd(q.cuda(), k.cuda(), v.cuda(), q_pos0=qp,
+                                                         causal=causal, want_ml=want_ml)
+                        torch.cuda.synchronize()
+                        ro, rl, _, _ = oracle.attention(q, k, v, q_pos0=qp, causal=causal)
+                        og = o.cpu().numpy()
+                        assert oracle.max_abs_err(og, ro) <= BF16_ATOL, (D, Sk, causal, want_ml)
+                        fin = np.isfinite(rl)
+                        assert np.array_equal(np.isneginf(lse.cpu().numpy()), np.isneginf(rl))
+                        check_lse(lse.cpu().numpy()[fin], rl[fin])
+                        assert np.all(og[~fin] == 0)
+    finally:
+        ra.set_attn_waves(0)
+
+
 # ------------------------------------------------------------ permutations
 @pytest.mark.parametrize("P,B,S,H,D,dtype", [
     (8, 1, 16384, 32, 128, torch.int16),      # the Ulysses workload's shape (1 KiB runs)
