@@ -2,11 +2,13 @@
 // on chip while K/V blocks stream through LDS in ring order, merged by the
 // online-softmax recurrence ([RA] §3.2-§3.4).
 //
-// One workgroup = 4 wavefronts = 128 query rows of one (batch, head); each
-// wave owns 32 rows.  Per K/V tile of 64 keys a wave computes the TRANSPOSED
-// score tile S^T = K Q^T on the matrix cores, so that every lane holds the
-// scores of one query column: the row max and row sum are in-lane reductions
-// plus one cross-half exchange (v_permlane32_swap), not 32-lane butterflies.
+// One workgroup = 4 or 8 wavefronts = 128 or 256 query rows of one (batch,
+// head); each wave owns 32 rows.  Per K/V tile of 64 keys a wave computes the
+// TRANSPOSED score tile S^T = K Q^T on the matrix cores, so that every lane
+// holds the scores of one query column: the row max is an in-lane reduction
+// plus one cross-half exchange (v_permlane32_swap), not a 32-lane butterfly.
+// The bf16 kernels take the row sum on the matrix cores as well (a 0/1
+// selector times the P fragments); the fp32 kernel reduces it like the max.
 // The probabilities P^T then feed O^T += V^T P^T directly as the B operand;
 // the V^T operand is read from row-major V in LDS by transposing reads.
 //
@@ -17,12 +19,15 @@
 //                  C[m][n]: lane holds n = col, m = 8*(v/4) + 4*half + v%4,
 //                           v = 0..15
 //   32x32x2 f32    A: m = col, k = half;  B: n = col, k = half;  C as above.
+//   16x16x32 bf16  A[m][k]: lane holds m = l % 16, k = 8*(l/16) .. +7
+//                  B[k][n]: lane holds n = l % 16, k = 8*(l/16) .. +7
+//                  C[m][n]: lane holds n = l % 16, m = 4*(l/16) + v, v = 0..3
 // A contraction index may be permuted freely as long as A and B agree; both
 // operands below are built with the same (half, element) -> index map.
 //
 // K/V tiles are multi-buffered in LDS and copied by the buffer unit straight
 // from HBM into LDS (no staging registers): while a tile is consumed, the
-// tiles two steps ahead -- possibly the first tiles of the next ring round
+// tiles two or three steps ahead -- possibly the first tiles of the next ring round
 // -- are in flight, so the stream continues across round boundaries without
 // a drain.
 #include <hip/hip_runtime.h>
@@ -41,6 +46,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -258,8 +264,8 @@ __device__ __forceinline__ float online_update(float (&s)[NS], RowState& st, flo
 // key; after that the row max is not recomputed per tile.  Instead the sum
 // of each tile's weights (computed anyway for l) is checked: while every
 // weight stays below 2^20 nothing can overflow, and a tile whose sum
-// exceeds that bound (a score more than ~20 above the reference, or an
-// infinite weight) is redone after moving the reference to that tile's
+// exceeds that bound or is NaN (a score more than ~20 above the reference,
+// or an infinite weight) is redone after moving the reference to that tile's
 // max and rescaling u and l.  RA_KERNEL_ROWMAX takes the row max of every
 // tile instead and moves the reference lazily (when the max exceeds it by
 // more than 8); the same path runs whenever m and l are requested.
@@ -479,7 +485,8 @@ struct WaveState {
   float m_ref;             // reference (base 2), -inf before any visible key
   float m_use;             // reference the exponentials subtract (0 while -inf)
   float m_true;            // exact running max (base 2; row-max path only)
-  float l_run;             // this lane's half of the sum of bf16(2^(s - m_ref))
+  float l_run;             // sum of bf16(2^(s - m_ref)) over the row (both lane halves)
+  bf16x8 sel;              // 0/1 selector, A operand of the row sums (see HalfSoftmax)
   unsigned kaddr[C::NC];   // LDS byte address of the K operand reads (buffer 0)
   unsigned vaddr[C::NDT];  // LDS byte address of the V operand reads (buffer 0)
   int voffk[C::DMA];       // copy source offsets (K) within a tile
@@ -555,19 +562,34 @@ __device__ __forceinline__ float move_reference(float& m_ref, float& l_run, floa
 
 // Softmax of one half (score tile KT: keys 32 KT .. 32 KT + 31) as a
 // software pipeline over 8 pairs of scores: time T shifts and scales pair T,
-// exponentiates pair T-1, and packs pair T-2 to bf16 and adds the rounded
-// pair to the row sum (10 time steps).  The packed pair is dword pair % 4
-// of fragment pair / 4 of the half; the two fragments are built fresh (not
-// as updates of the previous tile's registers, which would keep those
-// alive) and stored to P fragments 2 KT, 2 KT + 1 at the end.
+// exponentiates pair T-1, and packs pair T-2 to bf16 (10 time steps).  The
+// packed pair is dword pair % 4 of fragment pair / 4 of the half; the two
+// fragments are built fresh (not as updates of the previous tile's
+// registers, which would keep those alive) and stored to P fragments 2 KT,
+// 2 KT + 1 as they complete.
+//
+// Row sums on the matrix cores.  l adds the bf16-rounded weights that enter
+// P V, so that O stays an exact convex combination of V rows.  Each
+// completed fragment (16 keys x 32 queries, lane L holding 8 keys of query
+// L % 32) is the B operand of one v_mfma_f32_16x16x32_bf16 whose A operand
+// is a 0/1 selector: B lane L sits in k-group L / 16 and column L % 16, so
+// k-groups of odd index hold queries 16 .. 31 and even ones queries 0 .. 15;
+// A row i selects the k-groups of the parity of i / 4.  Output lane L holds
+// rows 4 (L / 16) .. + 3 of column L % 16, i.e. the sum over all 16 keys of
+// exactly its own query L % 32, in every one of its four registers, already
+// combined over the two lane halves.  Two such ops per half replace 32
+// vector instructions (unpacking each pair by a mask and a shift, two fp32
+// adds); the products by 0 and 1 are exact and the accumulation is fp32.
+// A 0 x inf product of an overflowed weight of the partner query gives NaN,
+// which the bound checks below treat like an overflow of the lane's own.
 struct HalfSoftmax {
   float x[3][2];
-  float lp[2];
+  f32x4 ls;  // running sum of the half's completed fragments (16x16x32 output)
   u32x4 g[2];
 };
 template <int KT, int T>
 __device__ __forceinline__ void half_softmax_step(HalfSoftmax& hs, const f32x16& s, float c,
-                                                  float nm, bf16x8 (&pb)[4]) {
+                                                  float nm, const bf16x8& sel, bf16x8 (&pb)[4]) {
   if constexpr (T < 8) {
     hs.x[T % 3][0] = fmaf(s[2 * T], c, nm);
     hs.x[T % 3][1] = fmaf(s[2 * T + 1], c, nm);
@@ -578,29 +600,18 @@ __device__ __forceinline__ void half_softmax_step(HalfSoftmax& hs, const f32x16&
   }
   if constexpr (T >= 2 && T - 2 < 8) {
     constexpr int p = T - 2, g = p / 4, e = 2 * (p % 4);
-    // the row sum adds the bf16-rounded weights that enter P V, so that O
-    // stays an exact convex combination of V rows: the packed pair is
-    // unpacked to two fp32 values (a mask and a shift) and added.  These
-    // integer ops and adds run alongside the matrix ops, while a v_dot2 over
-    // the bf16 pair would hold the matrix pipe for about half a matrix op.
     const bf16x2 pr = {(__bf16)hs.x[p % 3][0], (__bf16)hs.x[p % 3][1]};
     unsigned d;
     __builtin_memcpy(&d, &pr, 4);
-    // one packed pair serves the fragment and both sums (left visible to the
-    // compiler, it converts the low weight a second time for its sum)
-    asm volatile("" : "+v"(d));
-    if constexpr (p == 0) {  // the sums start at the first pair, not at 0 + it
-      hs.lp[0] = __uint_as_float(d << 16);
-      hs.lp[1] = __uint_as_float(d & 0xffff0000u);
-    } else {
-      hs.lp[0] += __uint_as_float(d << 16);
-      hs.lp[1] += __uint_as_float(d & 0xffff0000u);
-    }
-    hs.g[g][e / 2] = d;
     // pin the pair's work to this slot: without a use here the compiler
-    // sinks it below later branches, out of the matrix phase it fills
-    asm volatile("" : "+v"(hs.lp[0]), "+v"(hs.lp[1]));
-    if constexpr (p % 4 == 3) pb[2 * KT + g] = __builtin_bit_cast(bf16x8, hs.g[g]);
+    // sinks it out of the matrix phase it fills
+    asm volatile("" : "+v"(d));
+    hs.g[g][e / 2] = d;
+    if constexpr (p % 4 == 3) {
+      pb[2 * KT + g] = __builtin_bit_cast(bf16x8, hs.g[g]);
+      hs.ls = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[2 * KT + g],
+                                                      g == 0 ? f32x4{} : hs.ls, 0, 0, 0);
+    }
   }
 }
 constexpr int kSoftSteps = 10;
@@ -613,9 +624,9 @@ struct SoftSlot {
 
 template <int KT, int LO, int HI>
 __device__ __forceinline__ void half_softmax_range(HalfSoftmax& hs, const f32x16& s, float c,
-                                                   float nm, bf16x8 (&pb)[4]) {
+                                                   float nm, const bf16x8& sel, bf16x8 (&pb)[4]) {
   static_for<LO, HI>([&](auto tc) {
-    half_softmax_step<KT, decltype(tc)::value>(hs, s, c, nm, pb);
+    half_softmax_step<KT, decltype(tc)::value>(hs, s, c, nm, sel, pb);
   });
 }
 
@@ -623,11 +634,10 @@ __device__ __forceinline__ void half_softmax_range(HalfSoftmax& hs, const f32x16
 // redo, and phases whose matrix side is idle).
 template <int KT>
 __device__ __forceinline__ float half_softmax_all(const f32x16& s, float c, float m_use,
-                                                  bf16x8 (&pb)[4]) {
+                                                  const bf16x8& sel, bf16x8 (&pb)[4]) {
   HalfSoftmax hs;
-  hs.lp[0] = hs.lp[1] = 0.0f;
-  half_softmax_range<KT, 0, kSoftSteps>(hs, s, c, -m_use, pb);
-  return hs.lp[0] + hs.lp[1];
+  half_softmax_range<KT, 0, kSoftSteps>(hs, s, c, -m_use, sel, pb);
+  return hs.ls[0];
 }
 
 // Front half of a step: S^T(n+1) = K(n+1) Q^T from the K buffer at LDS
@@ -650,7 +660,6 @@ __device__ __forceinline__ float step_front(WaveState<D, NW>& w, unsigned koff,
   constexpr int PF = kOperandLead;
   const float nm = -w.m_use;
   HalfSoftmax hs;
-  hs.lp[0] = hs.lp[1] = 0.0f;
   // op i: score tile kt = i % 2, k-step ci = i / 2 (consecutive ops never
   // depend on each other)
   unsigned kbase[C::NC];
@@ -675,11 +684,11 @@ __device__ __forceinline__ float step_front(WaveState<D, NW>& w, unsigned koff,
     constexpr int kt = i % 2, ci = i / 2;
     s_nxt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % (PF + 1)], w.qf[ci],
                                                         ci == 0 ? f32x16{} : s_nxt[kt], 0, 0, 0);
-    half_softmax_range<1, SoftSlot<i, N>::lo, SoftSlot<i, N>::hi>(hs, s_cur[1], c, nm, pb);
+    half_softmax_range<1, SoftSlot<i, N>::lo, SoftSlot<i, N>::hi>(hs, s_cur[1], c, nm, w.sel, pb);
     if constexpr (i == 1) after_first();
     __builtin_amdgcn_sched_barrier(0);
   });
-  return hs.lp[0] + hs.lp[1];
+  return hs.ls[0];
 }
 
 // Back half of a step: O^T += V(n)^T P(n)^T from the V buffer at LDS byte
@@ -696,7 +705,6 @@ __device__ __forceinline__ float step_back(WaveState<D, NW>& w, unsigned vbuf,
   constexpr int PF = kOperandLead;
   const float nm = -w.m_use;
   HalfSoftmax hs;
-  hs.lp[0] = hs.lp[1] = 0.0f;
   // fragment j = (G = j / NDT, dt = j % NDT): two 64-bit transposed reads
   // (keys 16G .. 16G+7 and 16G+8 .. 16G+15 of d tile dt); consecutive ops
   // accumulate into different d tiles
@@ -727,10 +735,10 @@ __device__ __forceinline__ float step_back(WaveState<D, NW>& w, unsigned vbuf,
     __builtin_memcpy(&vf, &vr[j % (PF + 1)], 16);
     constexpr int G = j / C::NDT, dt = j % C::NDT;
     w.oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[G], w.oacc[dt], 0, 0, 0);
-    half_softmax_range<0, SoftSlot<j, N>::lo, SoftSlot<j, N>::hi>(hs, s_nxt[0], c, nm, pb_nxt);
+    half_softmax_range<0, SoftSlot<j, N>::lo, SoftSlot<j, N>::hi>(hs, s_nxt[0], c, nm, w.sel, pb_nxt);
     __builtin_amdgcn_sched_barrier(0);
   });
-  return hs.lp[0] + hs.lp[1];
+  return hs.ls[0];
 }
 
 template <int D, int NW>
@@ -821,11 +829,11 @@ __device__ __forceinline__ float tile_setup(const StepCtx<A>& k, WaveState<D, NW
 template <int D, int NW, class A>
 __device__ __forceinline__ void first_half_check(const StepCtx<A>& k, WaveState<D, NW>& w,
                                                  const f32x16& s0, bf16x8 (&pb)[4], float& l1) {
-  if (__builtin_amdgcn_ballot_w64(l1 > kTileSumLimit)) {
+  if (__builtin_amdgcn_ballot_w64(!(l1 <= kTileSumLimit))) {
     const float f = move_reference_octaves(w.m_ref, w.l_run, half_max(s0, k.c));
     scale_o<D, NW>(w, f);
     w.m_use = w.m_ref;
-    l1 = half_softmax_all<0>(s0, k.c, w.m_use, pb);
+    l1 = half_softmax_all<0>(s0, k.c, w.m_use, w.sel, pb);
   }
 }
 
@@ -870,14 +878,14 @@ __device__ __forceinline__ void pipeline_step(const StepCtx<A>& k, char* smem, W
   {
     // second half over the bound: move the reference, scale u, l and the
     // first half's weights, redo the second half
-    if (__builtin_amdgcn_ballot_w64(l2 > kTileSumLimit)) {
+    if (__builtin_amdgcn_ballot_w64(!(l2 <= kTileSumLimit))) {
       const float f = move_reference_octaves(w.m_ref, w.l_run, half_max(s_cur[1], k.c));
       scale_o<D, NW>(w, f);
       scale_p(pb_cur[0], f);
       scale_p(pb_cur[1], f);
       lsum_cur *= f;
       w.m_use = w.m_ref;
-      l2 = half_softmax_all<1>(s_cur[1], k.c, w.m_use, pb_cur);
+      l2 = half_softmax_all<1>(s_cur[1], k.c, w.m_use, w.sel, pb_cur);
     }
     w.l_run += lsum_cur + l2;
   }
@@ -1040,6 +1048,13 @@ __device__ __forceinline__ void attn_bf16_tile(const A& a, char* smem, int b, in
   w.m_use = 0.0f;
   w.m_true = -INFINITY;
   w.l_run = 0.0f;
+  {
+    // A row lane % 16 in k-group lane / 16: 1 where the parities of the
+    // k-group and of row / 4 agree
+    const __bf16 one = (((lane >> 4) ^ (lane >> 2)) & 1) ? (__bf16)0.0f : (__bf16)1.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w.sel[e] = one;
+  }
 
   // prologue: tiles 0 .. LEAD-1 into K and V buffers 0 .. LEAD-1; scores of
   // tile 0 and the first half of its softmax
@@ -1064,7 +1079,7 @@ __device__ __forceinline__ void attn_bf16_tile(const A& a, char* smem, int b, in
     scores_tile<D, NW, C::KB>(w, sA);
     bool moved;
     tile_setup<D, NW, ML>(k, w, sA, d0, moved);
-    lA = half_softmax_all<0>(sA[0], k.c, w.m_use, pA);
+    lA = half_softmax_all<0>(sA[0], k.c, w.m_use, w.sel, pA);
     first_half_check<D, NW>(k, w, sA[0], pA, lA);
   }
   __syncthreads();  // every wave is done with tile 0's K before any new copy
@@ -1090,7 +1105,7 @@ __device__ __forceinline__ void attn_bf16_tile(const A& a, char* smem, int b, in
   }
 
   // ---- epilogue: o = u / l, lse = m + ln l ([RA] §3.2; [SPD] §四) ----
-  const float l_tot = pair_sum(w.l_run);
+  const float l_tot = w.l_run;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const int r = wrow0 + col;
   if (k.wrows > 0 && r < a.Sq) {
