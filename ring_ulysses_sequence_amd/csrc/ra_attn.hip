@@ -97,6 +97,10 @@ struct AttnHead {
   // only lse back
   int acc;
   void* o_final;
+  // set by the host when every visited block after the first is FULL: the
+  // 8-wave kernel may then visit the blocks of a query tile starting from
+  // the second (the first, diagonal one last) -- see tile_coords_lockstep
+  int lockstep;
   int nblk;
 };
 // A problem with room for N visited blocks; AttnArgs (RA_MAX_P) for a whole
@@ -176,6 +180,41 @@ __device__ __forceinline__ void tile_coords_in(const A& a, int id, int& b, int& 
   }
   h = bh % a.H;
   b = bh / a.H;
+}
+// Lockstep order of the 8-wave ring kernel (one workgroup per CU, 32 CUs
+// per XCD).  Each XCD takes whole heads, one at a time, so the 32 resident
+// workgroups share one head's K/V stream in that XCD's L2 -- if they walk it
+// at the same time.  A head's query tiles are taken in pairs of 32-tile
+// chunks from the top.  The later chunk starts together and visits the FULL
+// blocks first and the diagonal block last: all 32 stream the full blocks in
+// step, then the diagonal block from its first tile, and tile t of the chunk
+// finishes 4 key tiles (per 256 rows) after tile t-1.  The earlier chunk is
+// dispatched in decreasing tile order, so its workgroups land on CUs as the
+// later chunk's finish, and visits the diagonal block first: a workgroup
+// that starts later has that many fewer diagonal tiles, and all of them
+// reach the full blocks at the same step (then finish together, so the next
+// head starts in step again).  The result is the ring's up to the order in
+// which the online softmax folds the blocks in.  Returns false (caller takes
+// the plain order) unless the flag is set and the grid holds whole heads
+// per XCD and whole chunk pairs per head.
+template <class A>
+__device__ __forceinline__ bool tile_coords_lockstep(const A& a, int id, int n, int& b,
+                                                     int& h, int& qt, int& rot) {
+  const int Q = a.n_qtiles, BH = a.B * a.H;
+  if (!a.lockstep || (n & 7) != 0 || (Q & 63) != 0 || (BH & 7) != 0) return false;
+  const int j = (id & 7) * (n >> 3) + (id >> 3);
+  const int bh = j / Q, r = j % Q;
+  const int top = Q - 64 * (r >> 6), pos = r & 31;
+  if (r & 32) {
+    qt = top - 33 - pos;
+    rot = 0;
+  } else {
+    qt = top - 32 + pos;
+    rot = 1;
+  }
+  h = bh % a.H;
+  b = bh / a.H;
+  return true;
 }
 template <class A>
 __device__ __forceinline__ void tile_coords(const A& a, int id, int n, int& b, int& h,
@@ -388,7 +427,15 @@ struct SeqCtx {
   long long wq_lo;   // this wave's first query position
   long long boff;    // byte offset of (batch b, K/V head) row 0 in a block
   int end_blk, end_t;  // the sequence ends before tile end_t of block end_blk
+  int rot;           // visit the table from entry rot on, wrapping around
 };
+
+// Table entry of the p-th visited block.
+template <class A>
+__device__ __forceinline__ int seq_bidx(const A& a, const SeqCtx& x, int p) {
+  const int i = p + x.rot;
+  return i >= a.nblk ? i - a.nblk : i;
+}
 
 // Cursor over the sequence; blk == a.nblk once past its end.  Everything
 // here is wave-uniform; the block fields are loaded once per block.
@@ -417,11 +464,11 @@ template <class A>
 __device__ __forceinline__ void seq_enter(const A& a, const SeqCtx& x, Seq& s) {
   s.t = 0;
   for (; s.blk < a.nblk; ++s.blk) {
-    s.n = tiles_of<64>(a, s.blk, x.q_hi);
+    s.n = tiles_of<64>(a, seq_bidx(a, x, s.blk), x.q_hi);
     if (s.n > 0) break;
   }
   if (s.blk >= a.nblk) return;
-  const KVBlock& kb = a.blk[s.blk];
+  const KVBlock& kb = a.blk[seq_bidx(a, x, s.blk)];
   s.len = kb.len;
   s.kp = (const char*)kb.k + x.boff;
   s.vp = (const char*)kb.v + x.boff;
@@ -445,10 +492,10 @@ __device__ __forceinline__ void seq_next(const A& a, const SeqCtx& x, Seq& s) {
 }
 // Block and tile of tile number i of the sequence (blk = a.nblk past it).
 template <class A>
-__device__ __forceinline__ void seq_locate(const A& a, long long q_hi, int i, int& blk,
+__device__ __forceinline__ void seq_locate(const A& a, const SeqCtx& x, int i, int& blk,
                                            int& t) {
   for (blk = 0; blk < a.nblk; ++blk) {
-    const int n = tiles_of<64>(a, blk, q_hi);
+    const int n = tiles_of<64>(a, seq_bidx(a, x, blk), x.q_hi);
     if (i < n) break;
     i -= n;
   }
@@ -457,7 +504,7 @@ __device__ __forceinline__ void seq_locate(const A& a, long long q_hi, int i, in
 template <class A>
 __device__ __forceinline__ Seq seq_first(const A& a, const SeqCtx& x, int lo) {
   Seq s{};
-  seq_locate(a, x.q_hi, lo, s.blk, s.t);
+  seq_locate(a, x, lo, s.blk, s.t);
   const int t = s.t;
   if (s.blk < a.nblk) {
     seq_enter(a, x, s);  // the located block has visited tiles
@@ -983,7 +1030,8 @@ __device__ __forceinline__ void fold_row(const A& a, long long so, int half,
 // partial slot (see AttnArgs).  ML: also track the exact max for m / l.
 template <int D, int NW, bool ML, class A>
 __device__ __forceinline__ void attn_bf16_tile(const A& a, char* smem, int b, int h,
-                                               int qt, int lo, int hi, long long slot) {
+                                               int qt, int lo, int hi, long long slot,
+                                               int rot = 0) {
   using C = Bf16Cfg<D, NW>;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1012,7 +1060,8 @@ __device__ __forceinline__ void attn_bf16_tile(const A& a, char* smem, int b, in
   k.x.boff = ((long long)b * a.kv_rows_b * a.Hkv + hk) * (D * 2);
   k.x.end_blk = a.nblk;
   k.x.end_t = 0;
-  if (hi != INT_MAX) seq_locate(a, k.x.q_hi, hi, k.x.end_blk, k.x.end_t);
+  k.x.rot = rot;
+  if (hi != INT_MAX) seq_locate(a, k.x, hi, k.x.end_blk, k.x.end_t);
 
   WaveState<D, NW> w;
   {
@@ -1166,9 +1215,11 @@ __device__ __forceinline__ void attn_bf16_body(const A& a, char* smem) {
     const int lo = (int)((long long)total * j / ns), hi = (int)((long long)total * (j + 1) / ns);
     attn_bf16_tile<D, NW, ML>(a, smem, bh / a.H, bh % a.H, qt, lo, hi, (long long)tile * ns + j);
   } else {
-    int b, h, qt;
-    tile_coords(a, b, h, qt);
-    attn_bf16_tile<D, NW, ML>(a, smem, b, h, qt, 0, INT_MAX, -1);
+    int b, h, qt, rot = 0;
+    if (NW != 8 ||
+        !tile_coords_lockstep(a, (int)blockIdx.x, (int)gridDim.x, b, h, qt, rot))
+      tile_coords(a, b, h, qt);
+    attn_bf16_tile<D, NW, ML>(a, smem, b, h, qt, 0, INT_MAX, -1, rot);
   }
 }
 
@@ -1450,6 +1501,9 @@ ra_status launch(AttnArgs& a, int D, ra_dtype dt, hipStream_t stream, const char
       return ra::fail(RA_ERR_UNSUPPORTED, "%s: K/V block of %d rows (at most 2^30)", name,
                       a.blk[i].len);
   const dim3 grid((unsigned)n_wg);
+  a.lockstep = !split;
+  for (int i = 1; i < a.nblk; ++i)
+    if (a.blk[i].cls != RA_FULL) a.lockstep = 0;
   if (dt == RA_BF16) {
     // m and l are tracked only when asked for
     const bool ml = a.m_out != nullptr || a.l_out != nullptr;
