@@ -41,6 +41,7 @@
 #include <type_traits>
 
 #include "ra_internal.h"
+#include "ra_order.h"
 
 namespace {
 
@@ -181,37 +182,15 @@ __device__ __forceinline__ void tile_coords_in(const A& a, int id, int& b, int& 
   h = bh % a.H;
   b = bh / a.H;
 }
-// Lockstep order of the 8-wave ring kernel (one workgroup per CU, 32 CUs
-// per XCD).  Each XCD takes whole heads, one at a time, so the 32 resident
-// workgroups share one head's K/V stream in that XCD's L2 -- if they walk it
-// at the same time.  A head's query tiles are taken in pairs of 32-tile
-// chunks from the top.  The later chunk starts together and visits the FULL
-// blocks first and the diagonal block last: all 32 stream the full blocks in
-// step, then the diagonal block from its first tile, and tile t of the chunk
-// finishes 4 key tiles (per 256 rows) after tile t-1.  The earlier chunk is
-// dispatched in decreasing tile order, so its workgroups land on CUs as the
-// later chunk's finish, and visits the diagonal block first: a workgroup
-// that starts later has that many fewer diagonal tiles, and all of them
-// reach the full blocks at the same step (then finish together, so the next
-// head starts in step again).  The result is the ring's up to the order in
-// which the online softmax folds the blocks in.  Returns false (caller takes
-// the plain order) unless the flag is set and the grid holds whole heads
-// per XCD and whole chunk pairs per head.
+// Lockstep order (ra_order.h) for the 8-wave ring kernel.  The result is
+// the ring's up to the order in which the online softmax folds the blocks in.
 template <class A>
 __device__ __forceinline__ bool tile_coords_lockstep(const A& a, int id, int n, int& b,
                                                      int& h, int& qt, int& rot) {
-  const int Q = a.n_qtiles, BH = a.B * a.H;
-  if (!a.lockstep || (n & 7) != 0 || (Q & 63) != 0 || (BH & 7) != 0) return false;
-  const int j = (id & 7) * (n >> 3) + (id >> 3);
-  const int bh = j / Q, r = j % Q;
-  const int top = Q - 64 * (r >> 6), pos = r & 31;
-  if (r & 32) {
-    qt = top - 33 - pos;
-    rot = 0;
-  } else {
-    qt = top - 32 + pos;
-    rot = 1;
-  }
+  int bh;
+  if (!a.lockstep ||
+      !ra_order::lockstep_coords(id, n, a.n_qtiles, a.B * a.H, bh, qt, rot))
+    return false;
   h = bh % a.H;
   b = bh / a.H;
   return true;

@@ -59,6 +59,7 @@
 
 #include "ra_cdna4.h"
 #include "ra_internal.h"
+#include "ra_order.h"
 
 namespace {
 
@@ -106,6 +107,10 @@ struct BwdArgs {
   int n_ktiles;       // 128-key tiles per block (dkv grid)
   float scale;
   float scale_log2;
+  // set by the host when every key of the blocks after the first is visible
+  // to every query: the 8-wave dq kernel may then take the lockstep order of
+  // ra_order.h (the first block last for half of the query tiles)
+  int lockstep;
   int nblk;
   BwdBlock blk[RA_MAX_P];
 };
@@ -318,10 +323,17 @@ void ring_attn_bwd_dq(const BwdArgs a) {
   // Workgroups are dispatched round-robin over the 8 XCDs: remap so that
   // every XCD takes a contiguous range of heads, and the workgroups resident
   // on it (neighbouring query tiles of one head) stream the same K/V tiles
-  // through its L2; later query tiles (more causal work) first.
-  int id = blockIdx.x;
-  if ((gridDim.x & 7) == 0) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
-  const int bh = id / n_qt, qt = n_qt - 1 - id % n_qt;
+  // through its L2; later query tiles (more causal work) first.  With 8
+  // waves, the lockstep order of ra_order.h where it applies.
+  int bh, qt, rot = 0;
+  if (NW != 8 || !a.lockstep ||
+      !ra_order::lockstep_coords((int)blockIdx.x, (int)gridDim.x, n_qt, a.B * a.H, bh, qt,
+                                 rot)) {
+    int id = blockIdx.x;
+    if ((gridDim.x & 7) == 0) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
+    bh = id / n_qt;
+    qt = n_qt - 1 - id % n_qt;
+  }
   const int b = bh / a.H, h = bh % a.H;
   const int row0 = qt * ROWS;
   const long long q_hi = qpos(a, min(row0 + ROWS, a.Sq) - 1);
@@ -378,10 +390,15 @@ void ring_attn_bwd_dq(const BwdArgs a) {
   copy_offsets<D, NW>(wave, lane, HD2, voff);
   const unsigned dst0 = base + wave * DMA * 1024;
 
-  // visited tiles: all blocks in order, tiles up to the last one with a
-  // key visible to the workgroup's last query
-  auto ntiles = [&](int bi) -> int {
-    const BwdBlock& kb = a.blk[bi];
+  // visited tiles: all blocks in order from table entry rot on (wrapping
+  // around), tiles up to the last one with a key visible to the workgroup's
+  // last query; cb / nb below count blocks in that order
+  auto entry = [&](int p) -> int {
+    const int i = p + rot;
+    return i >= a.nblk ? i - a.nblk : i;
+  };
+  auto ntiles = [&](int p) -> int {
+    const BwdBlock& kb = a.blk[entry(p)];
     const int n = (kb.len + kTile - 1) / kTile;
     long long lim = a.valid_len - 1;
     if (a.causal && q_hi < lim) lim = q_hi;
@@ -389,8 +406,8 @@ void ring_attn_bwd_dq(const BwdArgs a) {
     const long long last = (lim - kb.k_pos0) / kTile + 1;
     return last < n ? (int)last : n;
   };
-  auto copy_kv = [&](int bi, int ti, unsigned dst) {
-    const BwdBlock& kb = a.blk[bi];
+  auto copy_kv = [&](int p, int ti, unsigned dst) {
+    const BwdBlock& kb = a.blk[entry(p)];
     const long long off =
         (((long long)b * a.kv_rows_b + (long long)ti * kTile) * a.Hkv + hk) * D * 2;
     const int rows = min(kTile, kb.len - ti * kTile);
@@ -422,7 +439,7 @@ void ring_attn_bwd_dq(const BwdArgs a) {
       if (nb < a.nblk) copy_kv(nb, nt, dst0 + (BO ? 0 : 2 * C::TILE));
     };
 
-    const BwdBlock& kb = a.blk[cb];
+    const BwdBlock& kb = a.blk[entry(cb)];
     const long long kp0 = kb.k_pos0 + (long long)ct * kTile;
     const bool live = wrows > 0 && !(a.causal && kp0 > wq_hi);
     // mask: key j of the tile is hidden for this lane's query when j >= the
@@ -972,6 +989,11 @@ ra_status launch_bwd(const char* name, BwdArgs& a, int D, int block_len, hipStre
   const long long n_dkv = (long long)a.nblk * a.B * a.Hkv * a.n_ktiles;
   if (n_dq > 0x7fffffffLL || n_dkv > 0x7fffffffLL)
     return ra::fail(RA_ERR_UNSUPPORTED, "%s: grid too large", name);
+  a.lockstep = 1;
+  for (int i = 1; i < a.nblk; ++i) {
+    const long long k_end = a.blk[i].k_pos0 + a.blk[i].len;  // one past its last key
+    if ((a.causal && k_end - 1 > a.q_pos0) || k_end > a.valid_len) a.lockstep = 0;
+  }
   // dq first: it writes the row statistics that the dk/dv kernels read
   const dim3 gq((unsigned)n_dq);
   if (dq8) {
