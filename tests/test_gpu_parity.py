@@ -470,6 +470,55 @@ def test_ulysses_layout_and_attention(variant):
     check_bf16(got, ref, f"{w.name} O sampled rows")
 
 
+# ------------------------------------------------------------ lockstep order
+@pytest.mark.parametrize("D,causal", [(128, True), (64, False)])
+def test_lockstep_order(D, causal):
+    """Shares with 64 query tiles of 256 rows per head and heads in eights
+    take the lockstep workgroup order in the 8-wave forward and dQ kernels:
+    half of each head's query tiles visit the full block first and the
+    diagonal block last.  Rank 1 of a P = 2 ring over L = 32768 (H = 8):
+    every row against the 4-wave kernels (plain ring order), sampled rows at
+    a stride co-prime to the tiles (and both sides of the chunk boundary at
+    row 8192) against the oracle."""
+    B, H, P, Sb = 1, 8, 2, 16384
+    S = P * Sb
+    q, k, v, do = (W.random_tensor((B, S, H, D), seed=s_, device="cuda") for s_ in (81, 82, 83, 84))
+    kb, vb = blocks_of(k, P), blocks_of(v, P)
+    r = 1
+    q_r, do_r = q[:, Sb:].contiguous(), do[:, Sb:].contiguous()
+    got = {}
+    try:
+        for wv in (4, 8):
+            ra.set_attn_waves(wv)
+            say("lockstep", D, causal, "waves", wv)
+            o, lse = ra.ring_attn_fwd(q_r, kb, vb, r, causal=causal)
+            g = ra.ring_attn_bwd(q_r, kb, vb, o, do_r, lse, r, causal=causal)
+            torch.cuda.synchronize()
+            got[wv] = (o, lse, g)
+    finally:
+        ra.set_attn_waves(0)
+    o8, l8, g8 = got[8]
+    o4, l4, g4 = got[4]
+    check_bf16(o8.cpu(), o4.cpu().double().numpy(), "lockstep o vs 4 waves")
+    assert (l8 - l4).abs().max().item() <= LSE_BF16_ATOL
+    # the backward of the 8-wave forward's outputs through both dQ forms
+    try:
+        ra.set_attn_waves(4)
+        g48 = ra.ring_attn_bwd(q_r, kb, vb, o8, do_r, l8, r, causal=causal)
+        torch.cuda.synchronize()
+    finally:
+        ra.set_attn_waves(0)
+    check_grad(g8[0].cpu(), g48[0].cpu().double().numpy(), "lockstep dq vs 4 waves")
+    for j in range(P):
+        assert torch.equal(g8[1][j], g48[1][j]) and torch.equal(g8[2][j], g48[2][j])
+    rows = np.unique(np.concatenate([np.arange(0, Sb, 127), np.arange(8192 - 3, 8192 + 3),
+                                     np.arange(Sb - 3, Sb)]))
+    ref_o, ref_lse, _, _ = oracle.attention(q_r.cpu(), k.cpu(), v.cpu(), causal=causal,
+                                            q_pos0=Sb, rows=rows)
+    check_bf16(o8[:, rows].cpu(), ref_o, "lockstep o vs oracle")
+    check_lse(l8[:, rows].cpu(), ref_lse)
+
+
 # ------------------------------------------------------------ C4 long causal
 def test_long_context_causal_rank3(variant):
     w = W.LONG_CAUSAL
@@ -844,8 +893,9 @@ def test_ring_backward_all_ranks(D, causal, pad):
 def test_ring_backward_dq_waves(D, causal, pad):
     """The dQ kernel in 4- and 8-wave workgroups (RA_OPT_ATTN_WAVES forces
     either): every row's dq is formed by one wave in the same order both
-    ways, so the two are bit-identical, and both match the oracle.  320 rows
-    per rank leave the last 8-wave workgroup with six empty waves."""
+    ways (shares this small never take the lockstep order), so the two are
+    bit-identical, and both match the oracle.  320 rows per rank leave the
+    last 8-wave workgroup with six empty waves."""
     B, H, P, Sb = 2, 3, 4, 320
     S = P * Sb
     valid = S - pad
