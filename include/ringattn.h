@@ -340,7 +340,7 @@ ra_status ra_zigzag_attn_fwd(const void* q_r, const void* const* k_shares,
 /* Backward of one round ([RA] §3.3 closing paragraph, §6.2): the gradient
  * terms of one K/V block for one query shard, the unit the ring backward
  * repeats as each block arrives.  q, o (the forward's final output), dout
- * [B,Sq,H,D] and k, v [B,Sk,H,D]: device, bf16, contiguous; lse [B,Sq,H]
+ * [B,Sq,H,D] and k, v [B,Sk,H,D]: device, all bf16 or all fp32, contiguous; lse [B,Sq,H]
  * fp32, the natural log-sum-exp of the WHOLE forward (over every block the
  * rows attend to, as ra_ring_attn_fwd returns it), so that
  * P = exp(scale * Q K^T - lse) are this block's true probabilities
@@ -352,8 +352,10 @@ ra_status ra_zigzag_attn_fwd(const void* q_r, const void* const* k_shares,
  *   dv [B,Sk,H,D] fp32 += P^T dO
  * A block with no visible pair (SKIP) returns at once without touching
  * anything.  stats_ws: fp32 scratch of 2*B*Sq*H floats the call
- * overwrites.  Two launches on `stream`.  Only bf16 inputs
- * (RA_ERR_UNSUPPORTED for fp32); D 64 or 128; tensors 16-byte aligned
+ * overwrites.  Two launches on `stream`.  bf16 inputs round P and dS to
+ * bf16 before their products (as the forward rounds P); fp32 inputs round
+ * nothing (a plain kernel pair, the fp32 tier).  D 64 or 128; tensors
+ * 16-byte aligned
  * (RA_ERR_SHAPE); NULL pointers with non-empty sizes RA_ERR_NULL. */
 ra_status ra_block_attn_bwd(const void* q, const void* k, const void* v,
                             const void* o, const void* dout, const float* lse,
@@ -365,7 +367,7 @@ ra_status ra_block_attn_bwd(const void* q, const void* k, const void* v,
 
 /* Backward of rank `rank`'s ring ([RA] §3.3 closing paragraph, §6.2): the
  * gradients of the loss with respect to the rank's queries and to the K/V
- * blocks it visits, given the upstream gradient dO.  Inputs (device, bf16,
+ * blocks it visits, given the upstream gradient dO.  Inputs (device, bf16 or fp32,
  * [B,Sb,H,D] contiguous): q_r, o_r (the forward's output), do_r; lse_r
  * [B,Sb,H] fp32 natural log-sum-exp of the forward (ra_ring_attn_fwd's
  * lse).  k_blocks / v_blocks as in ra_ring_attn_fwd.  With P_j =
@@ -384,7 +386,7 @@ ra_status ra_block_attn_bwd(const void* q, const void* k, const void* v,
  * future) may be NULL and are not touched.  stats_ws: fp32 scratch of
  * 2*B*Sb*H floats the call overwrites (per-row base-2 lse and D, [2,B,H,Sb]).
  * Two launches on `stream` (dq and the row statistics, then dk/dv).
- * Only bf16 inputs (RA_ERR_UNSUPPORTED for fp32).  Errors as
+ * bf16 or fp32 inputs, as in ra_block_attn_bwd.  Errors as
  * ra_ring_attn_fwd. */
 ra_status ra_ring_attn_bwd(const void* q_r, const void* const* k_blocks,
                            const void* const* v_blocks, const void* o_r,
@@ -410,7 +412,7 @@ ra_status ra_ring_attn_bwd_gqa(const void* q_r, const void* const* k_blocks,
 
 /* Backward over packed samples (the form of ra_ring_attn_fwd_varlen): B =
  * 1, sample i holds global positions [cu_seqlens[i], cu_seqlens[i+1]) and
- * its rows attend only within it ([RA] §6).  q_r, o_r, do_r [1,Sb,H,D] bf16,
+ * its rows attend only within it ([RA] §6).  q_r, o_r, do_r [1,Sb,H,D] bf16 or fp32,
  * lse_r [1,Sb,H] (ra_ring_attn_fwd_varlen's lse); k_blocks / v_blocks and
  * dk_blocks / dv_blocks as in ra_ring_attn_bwd.  Accumulates (+=) dq_r and
  * the dK/dV parts of the visited blocks; rows outside every sample are not
@@ -428,15 +430,15 @@ ra_status ra_ring_attn_bwd_varlen(const void* q_r, const void* const* k_blocks,
 
 /* Backward of rank `rank`'s zigzag ring ([RA] §3.4 load balancing with
  * the backward of §3.3 closing paragraph, §6.2): as ra_ring_attn_bwd over
- * the shares of ra_zigzag_attn_fwd.  q_r, o_r, do_r [B,Sr,H,D] bf16 (chunk
+ * the shares of ra_zigzag_attn_fwd.  q_r, o_r, do_r [B,Sr,H,D] bf16 or fp32 (chunk
  * rank then chunk 2P-1-rank), lse_r [B,Sr,H] fp32 (ra_zigzag_attn_fwd's
  * lse); k_shares / v_shares HOST arrays of P device pointers to every
  * rank's [B,Sr,H,D] share.  Accumulates (+=) dq_r [B,Sr,H,D] fp32 and, into
  * dk_shares[j] / dv_shares[j] (fp32 [B,Sr,H,D], entries of shares the rank
  * skips may be NULL), the parts of share j's two chunks; summed over all
  * ranks they are the owners' gradients.  stats_ws: fp32 scratch of
- * 2*B*Sr*H floats.  Sr a multiple of 128, P at most RA_MAX_P/2, only bf16
- * inputs; other errors as ra_ring_attn_bwd.  Two launches on `stream`. */
+ * 2*B*Sr*H floats.  Sr a multiple of 128, P at most RA_MAX_P/2, bf16 or
+ * fp32 inputs; other errors as ra_ring_attn_bwd.  Two launches on `stream`. */
 ra_status ra_zigzag_attn_bwd(const void* q_r, const void* const* k_shares,
                              const void* const* v_shares, const void* o_r,
                              const void* do_r, const float* lse_r, int B, int Sr,

@@ -959,6 +959,228 @@ void ring_attn_bwd_dkv_pair(const BwdArgs a) {
   else pair_body<D, 1>(a, smem, wave, lane);
 }
 
+// ---------------------------------------------------------------------------
+// fp32 inputs: the same gradients with no rounding of P or dS (the fp32
+// tier of the checks).  Plain LDS-tiled vector arithmetic over 32 x 32
+// (query, key) tiles, 8 threads per query or key row; not tuned for speed.
+// Same launches as the bf16 path: the dq kernel also writes the row
+// statistics, which the dk/dv kernel then reads.
+// ---------------------------------------------------------------------------
+constexpr int kF32T = 32;         // rows of a query or key tile
+constexpr int kF32Threads = 256;  // 8 threads per row of a tile
+
+template <int D>
+struct F32Bwd {
+  static constexpr int LD = D + 1;  // padded LDS row (floats): rows on distinct banks
+  static constexpr int FPT = D / 8;  // features each thread owns (d = part + 8 m)
+};
+
+// Key row kr of block kb seen by a query at global position qp.
+__device__ __forceinline__ bool f32_visible(const BwdArgs& a, const BwdBlock& kb, int kr,
+                                            long long qp) {
+  const long long kp = kb.k_pos0 + kr;
+  return kr < kb.len && kp < a.valid_len && (!a.causal || kp <= qp);
+}
+
+// Rows row0 .. row0+31 of head h (zero past Sq) into t[32][LD].
+template <int D>
+__device__ __forceinline__ void f32_load_rows(float (*t)[F32Bwd<D>::LD], const float* base,
+                                              long long row_stride, int rows_total, int row0,
+                                              int tid) {
+  for (int e = tid; e < kF32T * D; e += kF32Threads) {
+    const int i = e / D, d = e % D, r = row0 + i;
+    t[i][d] = r < rows_total ? base[(long long)r * row_stride + d] : 0.0f;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kF32Threads) void ring_attn_bwd_dq_f32(const BwdArgs a) {
+  using C = F32Bwd<D>;
+  __shared__ float sq[kF32T][C::LD], sdo[kF32T][C::LD], sk[kF32T][C::LD], sv[kF32T][C::LD];
+  __shared__ float sds[kF32T][kF32T + 1];
+  __shared__ float slse[kF32T], sdsum[kF32T];
+  __shared__ long long sqp[kF32T];
+  const int tid = threadIdx.x;
+  const int n_qt = (a.Sq + kF32T - 1) / kF32T;
+  const int qt = blockIdx.x % n_qt, bh = blockIdx.x / n_qt;
+  const int b = bh / a.H, h = bh % a.H, hk = h / (a.H / a.Hkv);
+  const int row0 = qt * kF32T;
+  const long long HD = (long long)a.H * D, HDkv = (long long)a.Hkv * D;
+  const float* q = (const float*)a.q + (long long)b * a.Sq * HD + (long long)h * D;
+  const float* dout = (const float*)a.dout + (long long)b * a.Sq * HD + (long long)h * D;
+  const float* o = (const float*)a.o + (long long)b * a.Sq * HD + (long long)h * D;
+  f32_load_rows<D>(sq, q, HD, a.Sq, row0, tid);
+  f32_load_rows<D>(sdo, dout, HD, a.Sq, row0, tid);
+  const int ti = tid >> 3, part = tid & 7;  // this thread's query row and part
+  {
+    // row statistics, as the bf16 kernel forms them: base-2 lse (+inf for
+    // a row that saw no key and for a padding query) and D = rowsum(dO O)
+    // (0 for a padding query)
+    const int r = row0 + ti;
+    float dsum = 0.0f;
+    if (r < a.Sq)
+      for (int d = part; d < D; d += 8) dsum += dout[(long long)r * HD + d] * o[(long long)r * HD + d];
+    dsum += __shfl_xor(dsum, 1);
+    dsum += __shfl_xor(dsum, 2);
+    dsum += __shfl_xor(dsum, 4);
+    if (part == 0) {
+      float lse2 = INFINITY;
+      long long qp = LLONG_MAX;
+      if (r < a.Sq) {
+        qp = qpos(a, r);
+        const bool real = qp < a.valid_len;
+        const float l = a.lse[((long long)b * a.Sq + r) * a.H + h];
+        lse2 = l == -INFINITY || !real ? INFINITY : l * kLog2e;
+        if (!real) dsum = 0.0f;
+        const long long so = ((long long)b * a.H + h) * a.Sq + r;
+        a.stats[so] = lse2;
+        a.stats[(long long)a.B * a.H * a.Sq + so] = dsum;
+      }
+      slse[ti] = lse2;
+      sdsum[ti] = dsum;
+      sqp[ti] = qp;
+    }
+  }
+  const long long q_hi = qpos(a, min(row0 + kF32T, a.Sq) - 1);
+  float acc[C::FPT];
+#pragma unroll
+  for (int m = 0; m < C::FPT; ++m) acc[m] = 0.0f;
+  for (int bi = 0; bi < a.nblk; ++bi) {
+    const BwdBlock& kb = a.blk[bi];
+    const float* kp = (const float*)kb.k + (long long)b * a.kv_rows_b * HDkv + (long long)hk * D;
+    const float* vp = (const float*)kb.v + (long long)b * a.kv_rows_b * HDkv + (long long)hk * D;
+    for (int k0 = 0; k0 < kb.len; k0 += kF32T) {
+      // tiles wholly in the future of the tile's last query, or wholly
+      // padding, hold no visible key (and neither do the later ones)
+      if ((a.causal && kb.k_pos0 + k0 > q_hi) || kb.k_pos0 + k0 >= a.valid_len) break;
+      __syncthreads();  // the previous tile's readers are done
+      f32_load_rows<D>(sk, kp, HDkv, kb.len, k0, tid);
+      f32_load_rows<D>(sv, vp, HDkv, kb.len, k0, tid);
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = part + 8 * e;
+        float sc = 0.0f, dp = 0.0f;
+        for (int d = 0; d < D; ++d) {
+          sc += sq[ti][d] * sk[j][d];
+          dp += sdo[ti][d] * sv[j][d];
+        }
+        float ds = 0.0f;
+        if (f32_visible(a, kb, k0 + j, sqp[ti])) {
+          const float pr = exp2f(sc * a.scale_log2 - slse[ti]);
+          ds = pr * (dp - sdsum[ti]);
+        }
+        sds[ti][j] = ds;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < C::FPT; ++m) {
+        const int d = part + 8 * m;
+        float x = 0.0f;
+        for (int j = 0; j < kF32T; ++j) x += sds[ti][j] * sk[j][d];
+        acc[m] += x;
+      }
+    }
+  }
+  const int r = row0 + ti;
+  if (r < a.Sq) {
+    float* dq = a.dq + ((long long)b * a.Sq + r) * HD + (long long)h * D;
+#pragma unroll
+    for (int m = 0; m < C::FPT; ++m) dq[part + 8 * m] += a.scale * acc[m];
+  }
+}
+
+// One workgroup per (visited block, batch, K/V head, 32 keys): walks every
+// query tile of every query head of the group (those wholly before its keys
+// skipped when causal) and accumulates dK and dV of its keys.
+template <int D>
+__global__ __launch_bounds__(kF32Threads) void ring_attn_bwd_dkv_f32(const BwdArgs a) {
+  using C = F32Bwd<D>;
+  __shared__ float sk[kF32T][C::LD], sv[kF32T][C::LD], sq[kF32T][C::LD], sdo[kF32T][C::LD];
+  __shared__ float sp[kF32T][kF32T + 1], sds[kF32T][kF32T + 1];
+  __shared__ float slse[kF32T], sdsum[kF32T];
+  __shared__ long long sqp[kF32T];
+  const int tid = threadIdx.x;
+  int id = blockIdx.x;
+  const int kt = id % a.n_ktiles;
+  id /= a.n_ktiles;
+  const int bi = id % a.nblk;
+  id /= a.nblk;
+  const int hk = id % a.Hkv, b = id / a.Hkv;
+  const int G = a.H / a.Hkv;
+  const BwdBlock& kb = a.blk[bi];
+  const int k0 = kt * kF32T;
+  if (k0 >= kb.len) return;  // a shorter block (uniform)
+  const long long HD = (long long)a.H * D, HDkv = (long long)a.Hkv * D;
+  const long long kvoff = (long long)b * a.kv_rows_b * HDkv + (long long)hk * D;
+  f32_load_rows<D>(sk, (const float*)kb.k + kvoff, HDkv, kb.len, k0, tid);
+  f32_load_rows<D>(sv, (const float*)kb.v + kvoff, HDkv, kb.len, k0, tid);
+  const int tj = tid >> 3, part = tid & 7;  // this thread's key row and part
+  const long long k_lo = kb.k_pos0 + k0;
+  float dk[C::FPT], dv[C::FPT];
+#pragma unroll
+  for (int m = 0; m < C::FPT; ++m) dk[m] = dv[m] = 0.0f;
+  const int n_qt = (a.Sq + kF32T - 1) / kF32T;
+  const long long nst = (long long)a.B * a.H * a.Sq;
+  for (int g = 0; g < G; ++g) {
+    const int h = hk * G + g;
+    const float* q = (const float*)a.q + (long long)b * a.Sq * HD + (long long)h * D;
+    const float* dout = (const float*)a.dout + (long long)b * a.Sq * HD + (long long)h * D;
+    for (int qt = 0; qt < n_qt; ++qt) {
+      const int row0 = qt * kF32T;
+      if (a.causal && qpos(a, min(row0 + kF32T, a.Sq) - 1) < k_lo) continue;
+      __syncthreads();  // the previous tile's readers are done
+      f32_load_rows<D>(sq, q, HD, a.Sq, row0, tid);
+      f32_load_rows<D>(sdo, dout, HD, a.Sq, row0, tid);
+      if (tid < kF32T) {
+        const int r = row0 + tid;
+        const long long so = ((long long)b * a.H + h) * a.Sq + r;
+        slse[tid] = r < a.Sq ? a.stats[so] : INFINITY;
+        sdsum[tid] = r < a.Sq ? a.stats[nst + so] : 0.0f;
+        sqp[tid] = r < a.Sq ? qpos(a, r) : LLONG_MAX;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = part + 8 * e;
+        float sc = 0.0f, dp = 0.0f;
+        for (int d = 0; d < D; ++d) {
+          sc += sk[tj][d] * sq[i][d];
+          dp += sv[tj][d] * sdo[i][d];
+        }
+        float pr = 0.0f, ds = 0.0f;
+        if (f32_visible(a, kb, k0 + tj, sqp[i])) {
+          pr = exp2f(sc * a.scale_log2 - slse[i]);
+          ds = pr * (dp - sdsum[i]);
+        }
+        sp[tj][i] = pr;
+        sds[tj][i] = ds;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < C::FPT; ++m) {
+        const int d = part + 8 * m;
+        float xv = 0.0f, xk = 0.0f;
+        for (int i = 0; i < kF32T; ++i) {
+          xv += sp[tj][i] * sdo[i][d];
+          xk += sds[tj][i] * sq[i][d];
+        }
+        dv[m] += xv;
+        dk[m] += xk;
+      }
+    }
+  }
+  const int kr = k0 + tj;
+  if (kr < kb.len) {
+    const long long off = ((long long)b * a.kv_rows_b + kr) * HDkv + (long long)hk * D;
+#pragma unroll
+    for (int m = 0; m < C::FPT; ++m) {
+      kb.dk[off + part + 8 * m] += a.scale * dk[m];
+      kb.dv[off + part + 8 * m] += dv[m];
+    }
+  }
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // Checks shared by both entry points (errors before any launch).
@@ -966,7 +1188,6 @@ ra_status check_common(const char* name, int B, int Sq, int H, int D, ra_dtype d
   if (B < 0 || Sq < 0 || H < 0)
     return ra::fail(RA_ERR_SHAPE, "%s: negative size (B=%d Sq=%d H=%d)", name, B, Sq, H);
   if (dt != RA_BF16 && dt != RA_FP32) return ra::fail(RA_ERR_DTYPE, "%s: unknown dtype %d", name, (int)dt);
-  if (dt != RA_BF16) return ra::fail(RA_ERR_UNSUPPORTED, "%s: only bf16 inputs are supported", name);
   if (D != 64 && D != 128)
     return ra::fail(RA_ERR_UNSUPPORTED, "%s: head dimension %d not supported (64 or 128)", name, D);
   return RA_OK;
@@ -979,7 +1200,26 @@ void set_scale(BwdArgs& a, float scale, int D) {
 }
 
 // The three launches over a.nblk visited blocks of block_len rows each.
-ra_status launch_bwd(const char* name, BwdArgs& a, int D, int block_len, hipStream_t s) {
+ra_status launch_bwd(const char* name, BwdArgs& a, int D, ra_dtype dt, int block_len,
+                     hipStream_t s) {
+  if (dt == RA_FP32) {
+    const long long n_dq = (long long)a.B * a.H * ((a.Sq + kF32T - 1) / kF32T);
+    a.n_ktiles = (block_len + kF32T - 1) / kF32T;
+    const long long n_dkv = (long long)a.nblk * a.B * a.Hkv * a.n_ktiles;
+    if (n_dq > 0x7fffffffLL || n_dkv > 0x7fffffffLL)
+      return ra::fail(RA_ERR_UNSUPPORTED, "%s: grid too large", name);
+    const dim3 gq((unsigned)n_dq), gk((unsigned)n_dkv);
+    if (D == 128) hipLaunchKernelGGL(ring_attn_bwd_dq_f32<128>, gq, dim3(kF32Threads), 0, s, a);
+    else hipLaunchKernelGGL(ring_attn_bwd_dq_f32<64>, gq, dim3(kF32Threads), 0, s, a);
+    if (n_dkv > 0) {
+      if (D == 128) hipLaunchKernelGGL(ring_attn_bwd_dkv_f32<128>, gk, dim3(kF32Threads), 0, s, a);
+      else hipLaunchKernelGGL(ring_attn_bwd_dkv_f32<64>, gk, dim3(kF32Threads), 0, s, a);
+    }
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+      return ra::fail(RA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(err));
+    return RA_OK;
+  }
   // RA_OPT_ATTN_WAVES (4 or 8) forces the dQ workgroup size as it does the
   // forward's
   const int forced = ra::option(RA_OPT_ATTN_WAVES);
@@ -1057,7 +1297,7 @@ extern "C" ra_status ra_block_attn_bwd(const void* q, const void* k, const void*
   if (ra::block_class(q_pos0, q_pos0 + Sq, k_pos0, k_pos0 + Sk, causal != 0, valid_len) != RA_SKIP)
     a.blk[a.nblk++] = BwdBlock{k, v, dk, dv, k_pos0, Sk, 0};
   if (a.nblk == 0) return RA_OK;
-  return launch_bwd(name, a, D, Sk, (hipStream_t)stream);
+  return launch_bwd(name, a, D, dt, Sk, (hipStream_t)stream);
 }
 
 namespace {
@@ -1120,7 +1360,7 @@ ra_status ring_bwd(const char* name, const void* q_r, const void* const* k_block
     a.blk[a.nblk++] = BwdBlock{k_blocks[j], v_blocks[j], dk_blocks[j], dv_blocks[j],
                                (long long)j * Sb, Sb, 0};
   }
-  return launch_bwd(name, a, D, Sb, (hipStream_t)stream);
+  return launch_bwd(name, a, D, dt, Sb, (hipStream_t)stream);
 }
 }  // namespace
 
@@ -1202,7 +1442,7 @@ extern "C" ra_status ra_zigzag_attn_bwd(const void* q_r, const void* const* k_sh
   st = ra_zigzag_schedule(P, rank, c, causal, valid_len, src, cls);
   if (st != RA_OK) return st;
   a.nblk = 0;
-  const size_t in_row = (size_t)H * D * 2, g_row = (size_t)H * D;
+  const size_t in_row = (size_t)H * D * (dt == RA_FP32 ? 4 : 2), g_row = (size_t)H * D;
   for (int t = 0; t < P; ++t) {
     const int j = src[t];
     for (int half = 0; half < 2; ++half) {
@@ -1219,7 +1459,7 @@ extern "C" ra_status ra_zigzag_attn_bwd(const void* q_r, const void* const* k_sh
                                  dv_shares[j] + r0 * g_row, (long long)chunk * c, c, 0};
     }
   }
-  return launch_bwd(name, a, D, c, (hipStream_t)stream);
+  return launch_bwd(name, a, D, dt, c, (hipStream_t)stream);
 }
 
 extern "C" ra_status ra_ring_attn_bwd_varlen(const void* q_r, const void* const* k_blocks,
@@ -1256,7 +1496,7 @@ extern "C" ra_status ra_ring_attn_bwd_varlen(const void* q_r, const void* const*
   int src[RA_MAX_P], cls[RA_MAX_P];
   st = ra_ring_schedule(P, rank, Sb, causal, S, src, cls);
   if (st != RA_OK) return st;
-  const size_t in_row = (size_t)H * D * 2, g_row = (size_t)H * D;
+  const size_t in_row = (size_t)H * D * (dt == RA_FP32 ? 4 : 2), g_row = (size_t)H * D;
   // one launch pair per sample that meets the rank's rows: its rows of the
   // share against the parts of the visited blocks inside that sample, in
   // ring order (the forward's split, so each sample's gradients use only
@@ -1305,7 +1545,7 @@ extern "C" ra_status ra_ring_attn_bwd_varlen(const void* q_r, const void* const*
       if (k1 - k0 > max_len) max_len = (int)(k1 - k0);
     }
     if (a.nblk == 0) continue;
-    st = launch_bwd(name, a, D, max_len, (hipStream_t)stream);
+    st = launch_bwd(name, a, D, dt, max_len, (hipStream_t)stream);
     if (st != RA_OK) return st;
   }
   return RA_OK;

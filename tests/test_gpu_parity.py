@@ -1095,6 +1095,148 @@ def test_varlen_backward_all_ranks(causal):
         assert not x[:, tail].any()
 
 
+# ------------------------------------------------------------ fp32 backward
+def check_grad_fp32(got, ref, what):
+    """fp32 inputs: the fp32 tier (1e-5 absolute, fused-operator precision
+    page §3.4), relative to the gradient's scale where it exceeds 1."""
+    c = oracle.compare(got, ref)
+    scale = max(1.0, float(np.max(np.abs(ref))))
+    say(what, {k: f"{v:.3e}" for k, v in c.items()}, f"max|ref| {scale:.3e}")
+    assert np.all(np.isfinite(_f64(got)))
+    assert c["max_abs_err"] <= FP32_ATOL * scale, (what, c)
+
+
+def f32_tensors(shapes_seeds, valid=None):
+    out = [W.random_tensor(shp, dtype=torch.float32, seed=s_, device="cuda")
+           for shp, s_ in shapes_seeds]
+    return out
+
+
+@pytest.mark.parametrize("D,causal,pad,Hkv", [(64, False, 0, 2), (128, True, 37, 2),
+                                              (64, True, 0, 1)])
+def test_fp32_ring_backward(D, causal, pad, Hkv):
+    """fp32 ring backward (grouped-query when Hkv < H), B = 2, every rank,
+    96 rows per rank (ragged 32-row tiles): dq of all ranks and the dK/dV
+    parts accumulated into the owners' buffers against the full-sequence
+    gradients of the plain definition at the fp32 tier."""
+    B, H, P, Sb = 2, 2, 4, 96
+    S, G = P * Sb, H // Hkv
+    valid = S - pad
+    q, do = f32_tensors([((B, S, H, D), 101), ((B, S, H, D), 104)])
+    k, v = f32_tensors([((B, S, Hkv, D), 102), ((B, S, Hkv, D), 103)])
+    if pad:
+        # padding rows of the inputs are zero; dO stays random there
+        for x in (q, k, v):
+            x[:, valid:] = 0
+    kb, vb = blocks_of(k, P), blocks_of(v, P)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dk_all = [torch.zeros((B, Sb, Hkv, D), **f32) for _ in range(P)]
+    dv_all = [torch.zeros((B, Sb, Hkv, D), **f32) for _ in range(P)]
+    fq, fk, fv = oracle.attention_grad(q.cpu(), oracle.gqa_expand(k.cpu(), H),
+                                       oracle.gqa_expand(v.cpu(), H), do.cpu(), causal=causal,
+                                       valid_len=valid)
+    fk = fk.reshape(B, S, Hkv, G, D).sum(axis=3)
+    fv = fv.reshape(B, S, Hkv, G, D).sum(axis=3)
+    dqs = []
+    for r in range(P):
+        say("fp32 ring bwd", D, causal, pad, Hkv, "rank", r)
+        sl = slice(r * Sb, (r + 1) * Sb)
+        q_r, do_r = q[:, sl].contiguous(), do[:, sl].contiguous()
+        o, lse = ra.ring_attn_fwd(q_r, kb, vb, r, causal=causal, valid_len=valid)
+        dq, _, _ = ra.ring_attn_bwd(q_r, kb, vb, o, do_r, lse, r, causal=causal, valid_len=valid,
+                                    dk_blocks=dk_all, dv_blocks=dv_all)
+        torch.cuda.synchronize()
+        dqs.append(dq.cpu())
+    real = np.arange(valid)
+    check_grad_fp32(torch.cat(dqs, 1)[:, real], fq[:, real], "fp32 dq all ranks")
+    check_grad_fp32(torch.cat([x.cpu() for x in dk_all], 1)[:, real], fk[:, real], "fp32 dk owners")
+    check_grad_fp32(torch.cat([x.cpu() for x in dv_all], 1)[:, real], fv[:, real], "fp32 dv owners")
+    pad_rows = np.arange(valid, S)
+    assert not torch.cat(dqs, 1)[:, pad_rows].any()
+
+
+def test_fp32_zigzag_block_and_varlen_backward():
+    """The other fp32 backward forms against the plain definition at the
+    fp32 tier: zigzag shares (chunks of 128 rows, causal, 29 padding
+    tokens), one round at a time (ra_block_attn_bwd over every block, the
+    rank's lse from the whole forward), and packed samples."""
+    B, H, D, P = 1, 2, 64, 4
+    S = 1024
+    c = S // (2 * P)
+    valid = S - 29
+    q, k, v, do = f32_tensors([((B, S, H, D), s_) for s_ in (111, 112, 113, 114)])
+    for x in (q, k, v):
+        x[:, valid:] = 0
+    fq, fk, fv = oracle.attention_grad(q.cpu(), k.cpu(), v.cpu(), do.cpu(), causal=True,
+                                       valid_len=valid)
+    qs, ks, vs, dos = (zigzag_shares(x, P) for x in (q, k, v, do))
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dk_all = [torch.zeros(x.shape, **f32) for x in ks]
+    dv_all = [torch.zeros(x.shape, **f32) for x in ks]
+    for r in range(P):
+        say("fp32 zigzag bwd rank", r)
+        o, lse = ra.zigzag_attn_fwd(qs[r], ks, vs, r, causal=True, valid_len=valid)
+        dq, _, _ = ra.zigzag_attn_bwd(qs[r], ks, vs, o, dos[r], lse, r, causal=True,
+                                      valid_len=valid, dk_shares=dk_all, dv_shares=dv_all)
+        torch.cuda.synchronize()
+        pos = np.asarray(oracle.zigzag_positions(P, r, c))
+        real = pos < valid
+        check_grad_fp32(dq.cpu()[:, real], fq[:, pos[real]], f"fp32 zigzag dq r{r}")
+    for j in range(P):
+        pos = np.asarray(oracle.zigzag_positions(P, j, c))
+        real = pos < valid
+        check_grad_fp32(dk_all[j].cpu()[:, real], fk[:, pos[real]], f"fp32 zigzag dk share {j}")
+        check_grad_fp32(dv_all[j].cpu()[:, real], fv[:, pos[real]], f"fp32 zigzag dv share {j}")
+
+    # one round at a time: rank 2 of a contiguous P = 4 ring (blocks 2, 1, 0)
+    Sb, r = S // P, 2
+    sl = slice(r * Sb, (r + 1) * Sb)
+    q_r, do_r = q[:, sl].contiguous(), do[:, sl].contiguous()
+    kb, vb = blocks_of(k, P), blocks_of(v, P)
+    o, lse = ra.ring_attn_fwd(q_r, kb, vb, r, causal=True, valid_len=valid)
+    dq = torch.zeros(q_r.shape, **f32)
+    for j in (2, 1, 0):
+        say("fp32 block bwd block", j)
+        _, dk, dv = ra.block_attn_bwd(q_r, kb[j], vb[j], o, do_r, lse, q_pos0=r * Sb,
+                                      k_pos0=j * Sb, causal=True, valid_len=valid, dq=dq)
+        torch.cuda.synchronize()
+        # block j's keys get the terms of rank r's queries only
+        rq, rk, rv = oracle.ring_attention_bwd_rank(q_r.cpu(), [x.cpu() for x in kb],
+                                                    [x.cpu() for x in vb], do_r.cpu(), r,
+                                                    o_r=o.cpu(), lse_r=lse.cpu(), causal=True,
+                                                    valid_len=valid)
+        check_grad_fp32(dk.cpu(), rk[j], f"fp32 block dk {j}")
+        check_grad_fp32(dv.cpu(), rv[j], f"fp32 block dv {j}")
+    check_grad_fp32(dq.cpu(), rq, "fp32 block dq (three rounds)")
+
+    # packed samples
+    cu = [0, 300, 700, 1000]
+    q1, k1, v1, do1 = (x[:1] for x in (q, k, v, do))
+    kb1, vb1 = blocks_of(k1, P), blocks_of(v1, P)
+    dk_p = [torch.zeros((1, Sb, H, D), **f32) for _ in range(P)]
+    dv_p = [torch.zeros((1, Sb, H, D), **f32) for _ in range(P)]
+    gq, gk, gv = (np.zeros((1, S, H, D)) for _ in range(3))
+    qc, kc, vc, dc = q1.cpu(), k1.cpu(), v1.cpu(), do1.cpu()
+    for s0, s1 in zip(cu[:-1], cu[1:]):
+        g = oracle.attention_grad(qc[:, s0:s1], kc[:, s0:s1], vc[:, s0:s1], dc[:, s0:s1],
+                                  causal=True)
+        gq[:, s0:s1], gk[:, s0:s1], gv[:, s0:s1] = g
+    dqs = []
+    for r in range(P):
+        say("fp32 varlen bwd rank", r)
+        sl = slice(r * Sb, (r + 1) * Sb)
+        q_r, do_r = q1[:, sl].contiguous(), do1[:, sl].contiguous()
+        o, lse = ra.ring_attn_fwd_varlen(q_r, kb1, vb1, r, cu, causal=True)
+        dq, _, _ = ra.ring_attn_bwd_varlen(q_r, kb1, vb1, o, do_r, lse, r, cu, causal=True,
+                                           dk_blocks=dk_p, dv_blocks=dv_p)
+        torch.cuda.synchronize()
+        dqs.append(dq.cpu())
+    real = np.arange(cu[-1])
+    check_grad_fp32(torch.cat(dqs, 1)[:, real], gq[:, real], "fp32 varlen dq")
+    check_grad_fp32(torch.cat([x.cpu() for x in dk_p], 1)[:, real], gk[:, real], "fp32 varlen dk")
+    check_grad_fp32(torch.cat([x.cpu() for x in dv_p], 1)[:, real], gv[:, real], "fp32 varlen dv")
+
+
 def test_random_shapes_forward_and_backward():
     """Seeded random small shares (B, P, rows per rank from 1 to 300, heads
     and grouped K/V heads, D, causal, padding, rank): the ring forward (the

@@ -246,10 +246,13 @@ def test_device_entry_points_validate_before_launch(lib):
     st = lib.ra_ring_attn_fwd_gqa(null, arr, arr, 1, 16, 6, 0, 64, 2, 0, ra.RA_BF16, 0.0, 0,
                                   -1, null, null, null)
     assert st == 2
-    # ring backward: fp32 inputs unsupported, D, rank, NULL buffers
+    # ring backward: unknown dtype, fp32 validated like bf16, D, rank, NULL buffers
+    st = lib.ra_ring_attn_bwd(null, arr, arr, null, null, null, 1, 16, 1, 64, 2, 0, 7,
+                              0.0, 0, -1, null, arr, arr, null, null)
+    assert st == 3 and b"dtype" in lib.ra_last_error()
     st = lib.ra_ring_attn_bwd(null, arr, arr, null, null, null, 1, 16, 1, 64, 2, 0, ra.RA_FP32,
                               0.0, 0, -1, null, arr, arr, null, null)
-    assert st == 5 and b"bf16" in lib.ra_last_error()
+    assert st == 1
     st = lib.ra_ring_attn_bwd(null, arr, arr, null, null, null, 1, 16, 1, 80, 2, 0, ra.RA_BF16,
                               0.0, 0, -1, null, arr, arr, null, null)
     assert st == 5
@@ -263,10 +266,10 @@ def test_device_entry_points_validate_before_launch(lib):
     st = lib.ra_ring_attn_fwd_split(null, arr, arr, 1, 128, 1, 1, 64, 2, 0, ra.RA_BF16, 0.0, 0,
                                     -1, 0, null, 0, null, null, null)
     assert st == ra.RA_ERR_RANGE and b"nsplit" in lib.ra_last_error()
-    # one-round backward: fp32 unsupported, D, NULL, empty
+    # one-round backward: fp32 validated like bf16 (NULL), D, NULL, empty
     st = lib.ra_block_attn_bwd(null, null, null, null, null, null, 1, 16, 16, 1, 64, ra.RA_FP32,
                                0.0, 0, 0, 0, -1, null, null, null, null, null)
-    assert st == 5 and b"bf16" in lib.ra_last_error()
+    assert st == 1
     st = lib.ra_block_attn_bwd(null, null, null, null, null, null, 1, 16, 16, 1, 96, ra.RA_BF16,
                                0.0, 0, 0, 0, -1, null, null, null, null, null)
     assert st == 5 and b"96" in lib.ra_last_error()
@@ -282,7 +285,7 @@ def test_device_entry_points_validate_before_launch(lib):
     assert st == 2 and b"ra_zigzag_padded_len" in lib.ra_last_error()
     st = lib.ra_zigzag_attn_bwd(null, arr, arr, null, null, null, 1, 128, 1, 64, 2, 0, ra.RA_FP32,
                                 0.0, 1, -1, null, arr, arr, null, null)
-    assert st == 5
+    assert st == 1  # fp32 accepted; the NULL buffers are refused
     st = lib.ra_zigzag_attn_bwd(null, arr, arr, null, null, null, 1, 128, 1, 64, 2, 0, ra.RA_BF16,
                                 0.0, 1, -1, null, arr, arr, null, null)
     assert st == 1
