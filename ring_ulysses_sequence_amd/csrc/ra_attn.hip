@@ -98,9 +98,11 @@ struct AttnHead {
   // only lse back
   int acc;
   void* o_final;
-  // set by the host when every visited block after the first is FULL: the
-  // 8-wave kernel may then visit the blocks of a query tile starting from
-  // the second (the first, diagonal one last) -- see tile_coords_lockstep
+  // rotation of the block table for the later query tiles of the lockstep
+  // order (ra_order.h), 0 for none: 1 for a ring share whose visited blocks
+  // after the first are FULL, 2 for a causal zigzag share (its own two
+  // chunks first); the 8-wave kernel then visits their blocks from that
+  // table entry on, wrapping around
   int lockstep;
   int nblk;
 };
@@ -188,8 +190,9 @@ template <class A>
 __device__ __forceinline__ bool tile_coords_lockstep(const A& a, int id, int n, int& b,
                                                      int& h, int& qt, int& rot) {
   int bh;
-  if (!a.lockstep ||
-      !ra_order::lockstep_coords(id, n, a.n_qtiles, a.B * a.H, bh, qt, rot))
+  if (!a.lockstep || a.nblk <= 0 ||
+      !ra_order::lockstep_coords(id, n, a.n_qtiles, a.B * a.H, a.lockstep % a.nblk, bh, qt,
+                                 rot))
     return false;
   h = bh % a.H;
   b = bh / a.H;
@@ -1480,9 +1483,13 @@ ra_status launch(AttnArgs& a, int D, ra_dtype dt, hipStream_t stream, const char
       return ra::fail(RA_ERR_UNSUPPORTED, "%s: K/V block of %d rows (at most 2^30)", name,
                       a.blk[i].len);
   const dim3 grid((unsigned)n_wg);
-  a.lockstep = !split;
-  for (int i = 1; i < a.nblk; ++i)
-    if (a.blk[i].cls != RA_FULL) a.lockstep = 0;
+  if (split) {
+    a.lockstep = 0;
+  } else if (a.lockstep == 0) {  // not preset by the caller (the zigzag share)
+    a.lockstep = 1;
+    for (int i = 1; i < a.nblk; ++i)
+      if (a.blk[i].cls != RA_FULL) a.lockstep = 0;
+  }
   if (dt == RA_BF16) {
     // m and l are tracked only when asked for
     const bool ml = a.m_out != nullptr || a.l_out != nullptr;
@@ -2108,5 +2115,9 @@ extern "C" ra_status ra_zigzag_attn_fwd(const void* q_r, const void* const* k_sh
                                 (long long)chunk * c, c, cls[2 * t + half]};
     }
   }
+  // causal: the table starts with the share's own two chunks (each diagonal
+  // for one half of the rows, never skipped), so the later query tiles of
+  // the lockstep order start from the third entry
+  if (causal && a.nblk >= 2 && cls[0] != RA_SKIP && cls[1] != RA_SKIP) a.lockstep = 2;
   return launch(a, D, dt, (hipStream_t)stream, name);
 }

@@ -107,9 +107,10 @@ struct BwdArgs {
   int n_ktiles;       // 128-key tiles per block (dkv grid)
   float scale;
   float scale_log2;
-  // set by the host when every key of the blocks after the first is visible
-  // to every query: the 8-wave dq kernel may then take the lockstep order of
-  // ra_order.h (the first block last for half of the query tiles)
+  // rotation of the block table for the later query tiles of the lockstep
+  // order of ra_order.h, 0 for none: 1 when every key of the blocks after
+  // the first is visible to every query, 2 for a causal zigzag share (its
+  // own two chunks first); used by the 8-wave dq kernel
   int lockstep;
   int nblk;
   BwdBlock blk[RA_MAX_P];
@@ -326,9 +327,9 @@ void ring_attn_bwd_dq(const BwdArgs a) {
   // through its L2; later query tiles (more causal work) first.  With 8
   // waves, the lockstep order of ra_order.h where it applies.
   int bh, qt, rot = 0;
-  if (NW != 8 || !a.lockstep ||
-      !ra_order::lockstep_coords((int)blockIdx.x, (int)gridDim.x, n_qt, a.B * a.H, bh, qt,
-                                 rot)) {
+  if (NW != 8 || !a.lockstep || a.nblk <= 0 ||
+      !ra_order::lockstep_coords((int)blockIdx.x, (int)gridDim.x, n_qt, a.B * a.H,
+                                 a.lockstep % a.nblk, bh, qt, rot)) {
     int id = blockIdx.x;
     if ((gridDim.x & 7) == 0) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
     bh = id / n_qt;
@@ -1229,10 +1230,12 @@ ra_status launch_bwd(const char* name, BwdArgs& a, int D, ra_dtype dt, int block
   const long long n_dkv = (long long)a.nblk * a.B * a.Hkv * a.n_ktiles;
   if (n_dq > 0x7fffffffLL || n_dkv > 0x7fffffffLL)
     return ra::fail(RA_ERR_UNSUPPORTED, "%s: grid too large", name);
-  a.lockstep = 1;
-  for (int i = 1; i < a.nblk; ++i) {
-    const long long k_end = a.blk[i].k_pos0 + a.blk[i].len;  // one past its last key
-    if ((a.causal && k_end - 1 > a.q_pos0) || k_end > a.valid_len) a.lockstep = 0;
+  if (a.lockstep == 0) {  // not preset by the caller (the zigzag share)
+    a.lockstep = 1;
+    for (int i = 1; i < a.nblk; ++i) {
+      const long long k_end = a.blk[i].k_pos0 + a.blk[i].len;  // one past its last key
+      if ((a.causal && k_end - 1 > a.q_pos0) || k_end > a.valid_len) a.lockstep = 0;
+    }
   }
   // dq first: it writes the row statistics that the dk/dv kernels read
   const dim3 gq((unsigned)n_dq);
@@ -1459,6 +1462,9 @@ extern "C" ra_status ra_zigzag_attn_bwd(const void* q_r, const void* const* k_sh
                                  dv_shares[j] + r0 * g_row, (long long)chunk * c, c, 0};
     }
   }
+  // causal: the table starts with the share's own two chunks, so the later
+  // query tiles of the lockstep order start from the third entry
+  if (causal && a.nblk >= 2 && cls[0] != RA_SKIP && cls[1] != RA_SKIP) a.lockstep = 2;
   return launch_bwd(name, a, D, dt, c, (hipStream_t)stream);
 }
 

@@ -519,6 +519,48 @@ def test_lockstep_order(D, causal):
     check_lse(l8[:, rows].cpu(), ref_lse)
 
 
+def test_lockstep_order_zigzag():
+    """Causal zigzag shares of two 8192-row chunks (P = 2, L = 32768, H = 8,
+    D = 64) take the lockstep order with the later query tiles starting from
+    the third block-table entry: every row of both ranks (forward, and dq
+    through both dQ forms) against the 4-wave kernels, sampled rows of both
+    chunks at a stride co-prime to the tiles against the oracle."""
+    B, H, P, c, D = 1, 8, 2, 8192, 64
+    S = 2 * P * c
+    q, k, v, do = (W.random_tensor((B, S, H, D), seed=s_, device="cuda") for s_ in (85, 86, 87, 88))
+    qs, ks, vs, dos = (zigzag_shares(x, P) for x in (q, k, v, do))
+    for r in range(P):
+        got = {}
+        try:
+            for wv in (4, 8):
+                ra.set_attn_waves(wv)
+                say("lockstep zigzag rank", r, "waves", wv)
+                o, lse = ra.zigzag_attn_fwd(qs[r], ks, vs, r, causal=True)
+                torch.cuda.synchronize()
+                got[wv] = (o, lse)
+            o8, l8 = got[8]
+            g = {}
+            for wv in (4, 8):
+                ra.set_attn_waves(wv)
+                g[wv] = ra.zigzag_attn_bwd(qs[r], ks, vs, o8, dos[r], l8, r, causal=True)
+                torch.cuda.synchronize()
+        finally:
+            ra.set_attn_waves(0)
+        check_bf16(o8.cpu(), got[4][0].cpu().double().numpy(), f"lockstep zigzag r{r} o vs 4 waves")
+        assert (l8 - got[4][1]).abs().max().item() <= LSE_BF16_ATOL
+        check_grad(g[8][0].cpu(), g[4][0].cpu().double().numpy(), f"lockstep zigzag r{r} dq")
+        for j in range(P):
+            assert torch.equal(g[8][1][j], g[4][1][j]) and torch.equal(g[8][2][j], g[4][2][j])
+        rows = np.unique(np.concatenate([np.arange(0, c, 127), np.arange(c - 3, c)]))
+        for half, chunk in enumerate(oracle.zigzag_chunks(P, r)):
+            klim = (chunk + 1) * c
+            ref_o, ref_l, _, _ = oracle.attention(q[:, chunk * c:(chunk + 1) * c].cpu(),
+                                                  k[:, :klim].cpu(), v[:, :klim].cpu(),
+                                                  causal=True, q_pos0=chunk * c, rows=rows)
+            check_bf16(o8[:, half * c + rows].cpu(), ref_o, f"lockstep zigzag r{r} chunk {chunk}")
+            check_lse(l8[:, half * c + rows].cpu(), ref_l)
+
+
 # ------------------------------------------------------------ C4 long causal
 def test_long_context_causal_rank3(variant):
     w = W.LONG_CAUSAL
