@@ -287,6 +287,25 @@ ra_status ra_ring_attn_fwd_split_noalloc(const void* q_r, const void* const* k_b
                                          float scale, int causal, long long valid_len,
                                          int nsplit, void* o, float* lse_opt, void* stream);
 
+/* Host-only: the lockstep workgroup order that the 8-wave forward and dQ
+ * kernels take for a launch of n = Q * BH workgroups (Q query tiles of 256
+ * rows per (batch, head), BH of them), for callers that inspect a schedule
+ * and for tests; not needed to call any kernel.  Workgroups are dispatched
+ * round-robin over the 8 XCDs (32 CUs each); dispatch index id lands on XCD
+ * id % 8.  Each XCD takes whole (batch, head) problems in turn and a head's
+ * query tiles in pairs of 32-tile chunks from the top: the later chunk with
+ * block-table rotation later_rot (its blocks seen whole first, the diagonal
+ * block last), the earlier chunk in decreasing tile order with rotation 0,
+ * so that the 32 workgroups of an XCD read each K/V tile at the same step
+ * ([RA] §3.3 ring order with §3.4's causal classes; the order of the blocks
+ * inside one launch changes only the rounding).  Fills bh[id], qt[id] and
+ * rot[id] (HOST arrays of n) and returns 1 when the order applies (n and BH
+ * multiples of 8, Q a multiple of 64); returns 0 (arrays partly written) when
+ * the kernels keep their plain order for this shape; -1 with RA_ERR_SHAPE
+ * when n != Q * BH or a size is not positive, RA_ERR_NULL for a NULL array
+ * (message in ra_last_error). */
+int ra_lockstep_order(int n, int Q, int BH, int later_rot, int* bh, int* qt, int* rot);
+
 /* Host-only plan of the split ring for this share.  nsplit = 0 chooses:
  * as many runs per query tile as keep the B*H*ceil(Sb/128)*nsplit
  * workgroups within the device's 512 workgroup slots (two 128-row

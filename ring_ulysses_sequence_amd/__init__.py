@@ -44,6 +44,7 @@ EXPORTED = (
     "ra_ring_attn_fwd_gqa", "ra_ring_attn_fwd_varlen", "ra_block_attn_bwd",
     "ra_ring_attn_fwd_split", "ra_ring_split_plan", "ra_zigzag_attn_bwd", "ra_ring_attn_bwd_gqa",
     "ra_ring_attn_bwd_varlen", "ra_ring_attn_fwd_split_noalloc", "ra_block_attn_fwd_acc",
+    "ra_lockstep_order",
 )
 
 _lib = None
@@ -125,6 +126,8 @@ def _load():
                                                    c_int, c_ll, c_int, c_vp, c_vp, c_vp]),
         "ra_ring_split_plan": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_ll,
                                        c_int, ctypes.POINTER(c_ll)]),
+        "ra_lockstep_order": (c_int, [c_int, c_int, c_int, c_int, ctypes.POINTER(c_int),
+                                      ctypes.POINTER(c_int), ctypes.POINTER(c_int)]),
         "ra_block_attn_bwd": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int,
                                       c_int, c_int, c_int, c_float, c_ll, c_ll, c_int, c_ll,
                                       c_vp, c_vp, c_vp, c_vp, c_vp]),
@@ -383,6 +386,20 @@ def ring_split_plan(B: int, Sb: int, H: int, D: int, P: int, rank: int, causal: 
     if n < 0:
         raise ValueError(_load().ra_last_error().decode())
     return n, ws.value
+
+
+def lockstep_order(Q: int, BH: int, later_rot: int = 1):
+    """The lockstep workgroup order of the 8-wave kernels for Q query tiles
+    of 256 rows times BH (batch, head) problems (see ra_lockstep_order):
+    (applies, bh[id], qt[id], rot[id]) over the dispatch index id, the lists
+    meaningful only when it applies."""
+    n = Q * BH
+    arr = ctypes.c_int * max(n, 1)
+    bh, qt, rot = arr(), arr(), arr()
+    st = _load().ra_lockstep_order(n, Q, BH, later_rot, bh, qt, rot)
+    if st < 0:
+        raise ValueError(_load().ra_last_error().decode())
+    return st == 1, list(bh)[:n], list(qt)[:n], list(rot)[:n]
 
 
 def ring_attn_fwd(q_r, k_blocks: Sequence, v_blocks: Sequence, rank: int, *,

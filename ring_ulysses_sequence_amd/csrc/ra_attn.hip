@@ -1949,6 +1949,22 @@ extern "C" ra_status ra_ring_attn_fwd_split(const void* q_r, const void* const* 
                   dt, scale, causal, valid_len, o, lse_opt, stream, nsplit, ws, ws_floats);
 }
 
+extern "C" int ra_lockstep_order(int n, int Q, int BH, int later_rot, int* bh, int* qt,
+                                 int* rot) {
+  ra::clear_error();
+  if (n < 0 || Q <= 0 || BH <= 0 || later_rot < 0 || (long long)Q * BH != n) {
+    ra::fail(RA_ERR_SHAPE, "ra_lockstep_order: n=%d is not Q=%d times BH=%d", n, Q, BH);
+    return -1;
+  }
+  if (n > 0 && (!bh || !qt || !rot)) {
+    ra::fail(RA_ERR_NULL, "ra_lockstep_order: NULL output");
+    return -1;
+  }
+  for (int id = 0; id < n; ++id)
+    if (!ra_order::lockstep_coords(id, n, Q, BH, later_rot, bh[id], qt[id], rot[id])) return 0;
+  return 1;
+}
+
 extern "C" int ra_ring_split_plan(int B, int Sb, int H, int D, int P, int rank, int causal,
                                   long long valid_len, int nsplit, long long* ws_floats) {
   static const char* name = "ra_ring_split_plan";

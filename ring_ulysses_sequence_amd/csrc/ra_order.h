@@ -27,8 +27,9 @@ namespace ra_order {
 // id: the workgroup's dispatch index of n (n % 8 == 0, BH % 8 == 0).
 // Returns false, and the caller takes its plain order, when the grid does not
 // hold whole heads per XCD and whole chunk pairs per head.
-__device__ __forceinline__ bool lockstep_coords(int id, int n, int Q, int BH, int later_rot,
-                                                int& bh, int& qt, int& rot) {
+__host__ __device__ __forceinline__ bool lockstep_coords(int id, int n, int Q, int BH,
+                                                         int later_rot, int& bh, int& qt,
+                                                         int& rot) {
   if ((n & 7) != 0 || (Q & 63) != 0 || (BH & 7) != 0) return false;
   const int j = (id & 7) * (n >> 3) + (id >> 3);
   bh = j / Q;

@@ -355,3 +355,90 @@ def test_binding_checks_output_buffers_before_the_library(lib):
     # a host buffer
     with pytest.raises(ValueError, match="GPU"):
         ra._out(good, "out", like.shape, like.dtype, like)
+
+
+# ------------------------------------------------------------ lockstep order
+def _simulate(order, work, n_cu=32):
+    """Dispatch one XCD's workgroups in order, each onto the first CU to
+    become free, in units of key-tile steps (every step the same time).
+    work(bh, qt, rot) -> (first part, second part, index of the full part).
+    Returns per workgroup (start of its full-block part, end)."""
+    import heapq
+    free = [(0, c) for c in range(n_cu)]
+    heapq.heapify(free)
+    out = {}
+    for key in order:
+        t, c = heapq.heappop(free)
+        a, b, full_first = work(*key)
+        full_start = t if full_first else t + a
+        end = t + a + b
+        out[key] = (full_start, end)
+        heapq.heappush(free, (end, c))
+    return out
+
+
+@pytest.mark.parametrize("Q,BH,later_rot,case", [
+    (64, 16, 1, "ring"),         # 256-row tiles of a 16384-row share, 16 heads
+    (128, 8, 1, "ring"),         # two chunk pairs per head
+    (64, 8, 2, "zigzag0"),       # zigzag rank 0 of P = 8 (later half sees 15 whole chunks)
+    (64, 8, 2, "zigzag7"),       # zigzag rank 7 (8 whole chunks for the later half, 7 for the earlier)
+])
+def test_lockstep_order_walks_in_step(lib, Q, BH, later_rot, case):
+    """The lockstep order (ra_lockstep_order): a bijection onto (head, tile);
+    each XCD takes whole heads; within a head the later 32-tile chunk carries
+    the rotation and the earlier chunk follows in decreasing tile order.  In a
+    model with one key tile per step and one workgroup per CU, the 32
+    workgroups of each chunk pair on an XCD all run their full-block part
+    over the same steps, and the earlier chunk's all finish together, when
+    the pair's last workgroup does ([RA] §3.4: tile qt of 256 rows sees
+    4 (qt + 1) diagonal key tiles of 64)."""
+    ok, bh, qt, rot = ra.lockstep_order(Q, BH, later_rot)
+    assert ok
+    n = Q * BH
+    assert sorted(zip(bh, qt)) == [(h, t) for h in range(BH) for t in range(Q)]
+    per = n // 8
+    for x in range(8):
+        ids = list(range(x, n, 8))
+        heads = [bh[i] for i in ids]
+        assert heads == sorted(heads)  # whole heads, one after another
+        assert set(heads) == set(range(x * per // Q, (x + 1) * per // Q))
+        for h in set(heads):
+            tiles = [(qt[i], rot[i]) for i in ids if bh[i] == h]
+            for p in range(Q // 64):
+                later, earlier = tiles[64 * p:64 * p + 32], tiles[64 * p + 32:64 * p + 64]
+                top = Q - 64 * p
+                assert sorted(t for t, _ in later) == list(range(top - 32, top))
+                assert all(r == later_rot for _, r in later)
+                assert [t for t, _ in earlier] == list(range(top - 33, top - 65, -1))
+                assert all(r == 0 for _, r in earlier)
+
+        def work(h, t, r, Q=Q):
+            if case == "ring":      # full blocks F, diagonal 4(t+1)
+                full, diag = 768, 4 * (t + 1)
+            else:                   # zigzag: the two halves of the share
+                later = t >= Q // 2
+                i = t - Q // 2 if later else t
+                wholes = {"zigzag0": (15, 0), "zigzag7": (8, 7)}[case][0 if later else 1]
+                full, diag = 128 * wholes, 4 * (i + 1)
+            return (full, diag, True) if r else (diag, full, False)
+
+        sim = _simulate([(bh[i], qt[i], rot[i]) for i in ids], work)
+        for h in set(heads):
+            keys = [(bh[i], qt[i], rot[i]) for i in ids if bh[i] == h]
+            for p in range(Q // 64):
+                pair = keys[64 * p:64 * p + 64]
+                later, earlier = pair[:32], pair[32:]
+                assert len({sim[k][0] for k in later}) == 1
+                if case != "zigzag0":  # the earlier half of rank 0 has no full part
+                    assert len({sim[k][0] for k in earlier}) == 1
+                # the earlier chunk's workgroups all end when the pair's
+                # last one does, so the next pair starts in step
+                ends = {sim[k][1] for k in earlier}
+                assert len(ends) == 1 and ends == {max(sim[k][1] for k in pair)}
+
+
+def test_lockstep_order_declines_other_shapes(lib):
+    assert not ra.lockstep_order(32, 16)[0]    # half a chunk pair per head
+    assert not ra.lockstep_order(64, 12)[0]    # heads do not split evenly over 8 XCDs
+    with pytest.raises(ValueError):
+        ra.lockstep_order(0, 8)
