@@ -1953,7 +1953,8 @@ extern "C" int ra_lockstep_order(int n, int Q, int BH, int later_rot, int* bh, i
                                  int* rot) {
   ra::clear_error();
   if (n < 0 || Q <= 0 || BH <= 0 || later_rot < 0 || (long long)Q * BH != n) {
-    ra::fail(RA_ERR_SHAPE, "ra_lockstep_order: n=%d is not Q=%d times BH=%d", n, Q, BH);
+    ra::fail(RA_ERR_SHAPE, "ra_lockstep_order: bad sizes (n=%d, Q=%d, BH=%d, later_rot=%d)", n,
+             Q, BH, later_rot);
     return -1;
   }
   if (n > 0 && (!bh || !qt || !rot)) {
@@ -2132,8 +2133,9 @@ extern "C" ra_status ra_zigzag_attn_fwd(const void* q_r, const void* const* k_sh
     }
   }
   // causal: the table starts with the share's own two chunks (each diagonal
-  // for one half of the rows, never skipped), so the later query tiles of
-  // the lockstep order start from the third entry
+  // for one half of the rows; the test leaves out a chunk that is all
+  // padding), so the later query tiles of the lockstep order start from the
+  // third entry
   if (causal && a.nblk >= 2 && cls[0] != RA_SKIP && cls[1] != RA_SKIP) a.lockstep = 2;
   return launch(a, D, dt, (hipStream_t)stream, name);
 }

@@ -21,9 +21,10 @@ namespace ra_order {
 //     t of the chunk finishes a fixed number of key tiles after tile t-1;
 //   - the earlier chunk is dispatched in decreasing tile order, so its
 //     workgroups land on the CUs as the later chunk's finish, and visits the
-//     diagonal block first (table order, rot = 0): a workgroup that starts later has that
-//     many fewer diagonal tiles, so all of them reach the full blocks at the
-//     same step and finish together, and the next head starts in step again.
+//     diagonal block first (table order, rot = 0): a workgroup that starts
+//     later has that many fewer diagonal tiles, so all of them reach the
+//     full blocks at the same step and finish together, and the next head
+//     starts in step again.
 // id: the workgroup's dispatch index of n (n % 8 == 0, BH % 8 == 0).
 // Returns false, and the caller takes its plain order, when the grid does not
 // hold whole heads per XCD and whole chunk pairs per head.
