@@ -471,18 +471,24 @@ def test_ulysses_layout_and_attention(variant):
 
 
 # ------------------------------------------------------------ lockstep order
-@pytest.mark.parametrize("D,causal", [(128, True), (64, False)])
-def test_lockstep_order(D, causal):
+@pytest.mark.parametrize("D,causal,pad,Hkv", [(128, True, 0, 8), (64, False, 0, 8),
+                                              (128, True, 100, 2)])
+def test_lockstep_order(D, causal, pad, Hkv):
     """Shares with 64 query tiles of 256 rows per head and heads in eights
     take the lockstep workgroup order in the 8-wave forward and dQ kernels:
     half of each head's query tiles visit the full block first and the
-    diagonal block last.  Rank 1 of a P = 2 ring over L = 32768 (H = 8):
-    every row against the 4-wave kernels (plain ring order), sampled rows at
-    a stride co-prime to the tiles (and both sides of the chunk boundary at
-    row 8192) against the oracle."""
+    diagonal block last.  Rank 1 of a P = 2 ring over L = 32768 (H = 8; also
+    with 100 padding tokens at the end of the rank's own block and 2 K/V
+    heads): every row against the 4-wave kernels (plain ring order), sampled
+    rows at a stride co-prime to the tiles (and both sides of the chunk
+    boundary at row 8192) against the oracle."""
     B, H, P, Sb = 1, 8, 2, 16384
     S = P * Sb
-    q, k, v, do = (W.random_tensor((B, S, H, D), seed=s_, device="cuda") for s_ in (81, 82, 83, 84))
+    valid = S - pad
+    q, do = (W.random_tensor((B, S, H, D), seed=s_, device="cuda") for s_ in (81, 84))
+    k, v = (W.random_tensor((B, S, Hkv, D), seed=s_, device="cuda") for s_ in (82, 83))
+    for x in (q, k, v):
+        x[:, valid:] = 0
     kb, vb = blocks_of(k, P), blocks_of(v, P)
     r = 1
     q_r, do_r = q[:, Sb:].contiguous(), do[:, Sb:].contiguous()
@@ -490,31 +496,34 @@ def test_lockstep_order(D, causal):
     try:
         for wv in (4, 8):
             ra.set_attn_waves(wv)
-            say("lockstep", D, causal, "waves", wv)
-            o, lse = ra.ring_attn_fwd(q_r, kb, vb, r, causal=causal)
-            g = ra.ring_attn_bwd(q_r, kb, vb, o, do_r, lse, r, causal=causal)
+            say("lockstep", D, causal, pad, Hkv, "waves", wv)
+            o, lse = ra.ring_attn_fwd(q_r, kb, vb, r, causal=causal, valid_len=valid)
+            g = ra.ring_attn_bwd(q_r, kb, vb, o, do_r, lse, r, causal=causal, valid_len=valid)
             torch.cuda.synchronize()
             got[wv] = (o, lse, g)
     finally:
         ra.set_attn_waves(0)
     o8, l8, g8 = got[8]
     o4, l4, g4 = got[4]
-    check_bf16(o8.cpu(), o4.cpu().double().numpy(), "lockstep o vs 4 waves")
-    assert (l8 - l4).abs().max().item() <= LSE_BF16_ATOL
+    n = Sb - pad  # the real rows of the share
+    check_bf16(o8[:, :n].cpu(), o4[:, :n].cpu().double().numpy(), "lockstep o vs 4 waves")
+    assert (l8[:, :n] - l4[:, :n]).abs().max().item() <= LSE_BF16_ATOL
     # the backward of the 8-wave forward's outputs through both dQ forms
     try:
         ra.set_attn_waves(4)
-        g48 = ra.ring_attn_bwd(q_r, kb, vb, o8, do_r, l8, r, causal=causal)
+        g48 = ra.ring_attn_bwd(q_r, kb, vb, o8, do_r, l8, r, causal=causal, valid_len=valid)
         torch.cuda.synchronize()
     finally:
         ra.set_attn_waves(0)
     check_grad(g8[0].cpu(), g48[0].cpu().double().numpy(), "lockstep dq vs 4 waves")
     for j in range(P):
         assert torch.equal(g8[1][j], g48[1][j]) and torch.equal(g8[2][j], g48[2][j])
-    rows = np.unique(np.concatenate([np.arange(0, Sb, 127), np.arange(8192 - 3, 8192 + 3),
-                                     np.arange(Sb - 3, Sb)]))
-    ref_o, ref_lse, _, _ = oracle.attention(q_r.cpu(), k.cpu(), v.cpu(), causal=causal,
-                                            q_pos0=Sb, rows=rows)
+    rows = np.unique(np.concatenate([np.arange(0, n, 127), np.arange(8192 - 3, 8192 + 3),
+                                     np.arange(n - 3, n)]))
+    kf = oracle.gqa_expand(k.cpu(), H) if Hkv != H else k.cpu()
+    vf = oracle.gqa_expand(v.cpu(), H) if Hkv != H else v.cpu()
+    ref_o, ref_lse, _, _ = oracle.attention(q_r.cpu(), kf, vf, causal=causal, q_pos0=Sb,
+                                            valid_len=valid, rows=rows)
     check_bf16(o8[:, rows].cpu(), ref_o, "lockstep o vs oracle")
     check_lse(l8[:, rows].cpu(), ref_lse)
 
