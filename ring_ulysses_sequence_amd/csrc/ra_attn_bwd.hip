@@ -585,16 +585,23 @@ __device__ __forceinline__ void step_p(PairLane<D, 0>& w, unsigned bof, unsigned
     }
   };
   // P of (query m = 32TF + 8g + 4half + i, this lane's key) for v = 4g + i,
-  // hidden when m < rel_h + 4half
-  // the mask bound with the tile's need folded in, once per step; opaque to
-  // the compiler, which would otherwise split it back into a scalar test
-  // per weight
-  int rel_m = need ? rel_h : INT_MIN;
-  asm volatile("" : "+v"(rel_m));
+  // hidden when m < rel_h + 4half.  The mask goes into the statistics: on a
+  // tile that needs it (a uniform branch, taken on diagonal, padded and
+  // dead tiles only) the base-2 lse of every hidden query of the lane is
+  // set to +inf, so its weight exp2(s - inf) is 0 and the weights themselves
+  // take no test.
+  auto mask_stats = [&]() {
+    if (need) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int g = v >> 2, i = v & 3;
+        if (32 * TF + 8 * g + i < rel_h) st[g][i] = __float_as_uint(INFINITY);
+      }
+    }
+  };
   auto p_val = [&](int v) {
     const int g = v >> 2, i = v & 3;
-    float x = sc[v] * c_scale - as_f32(st[g])[i];
-    if (32 * TF + 8 * g + i < rel_m) x = -INFINITY;
+    const float x = sc[v] * c_scale - as_f32(st[g])[i];
     pf[v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(x);
   };
 #pragma unroll
@@ -617,6 +624,7 @@ __device__ __forceinline__ void step_p(PairLane<D, 0>& w, unsigned bof, unsigned
         claim_lds_n(n, st[1]);
         claim_lds_n(n, st[2]);
         claim_lds_n(n, st[3]);
+        mask_stats();
       }
       w.acc[j % C::NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           join(lo[i % NB], hi[i % NB]), pb[j / C::NDT], w.acc[j % C::NDT], 0, 0, 0);
@@ -632,6 +640,7 @@ __device__ __forceinline__ void step_p(PairLane<D, 0>& w, unsigned bof, unsigned
       claim_lds<0>(st[1]);
       claim_lds<0>(st[2]);
       claim_lds<0>(st[3]);
+      mask_stats();
 #pragma unroll
       for (int v = 0; v < 16; ++v) p_val(v);
     }
