@@ -403,7 +403,7 @@ ra_status ra_block_attn_bwd(const void* q, const void* k, const void* v,
  * gradients, as the ring returns them).  dk_blocks / dv_blocks are HOST
  * arrays of P device pointers; entries of blocks the rank skips (causal
  * future) may be NULL and are not touched.  stats_ws: fp32 scratch of
- * 2*B*Sb*H floats the call overwrites (per-row base-2 lse and D, [2,B,H,Sb]).
+ * 2*B*Sb*H floats the call overwrites (per-row base-2 lse and -D, [2,B,H,Sb]).
  * Two launches on `stream` (dq and the row statistics, then dk/dv).
  * bf16 or fp32 inputs, as in ra_block_attn_bwd.  Errors as
  * ra_ring_attn_fwd. */

@@ -90,7 +90,7 @@ struct BwdArgs {
   const void* dout;   // [B, Sq, H, D] bf16
   const float* lse;   // [B, Sq, H] natural log-sum-exp of the forward
   float* dq;          // [B, Sq, H, D] fp32, accumulated (+=)
-  float* stats;       // [2, B, H, Sq] fp32: base-2 lse, then rowsum(dO * O);
+  float* stats;       // [2, B, H, Sq] fp32: base-2 lse, then -rowsum(dO * O);
                       // written by the dq kernel, read by the dk/dv kernel
   long long q_pos0;   // global position of query row 0
   // query row r sits at q_pos0 + r below q_split, at q_pos1 + (r - q_split)
@@ -380,7 +380,7 @@ void ring_attn_bwd_dq(const BwdArgs a) {
     if (half == 0) {
       const long long so = ((long long)b * a.H + h) * a.Sq + r;
       a.stats[so] = lse2;
-      a.stats[(long long)a.B * a.H * a.Sq + so] = dsum;
+      a.stats[(long long)a.B * a.H * a.Sq + so] = -dsum;
     }
   }
 #pragma unroll
@@ -680,7 +680,6 @@ __device__ __forceinline__ void step_ds(PairLane<D, 1>& w, unsigned bof, unsigne
     stf[1] = lds_read_b128<SO + 32>(sa);
     stf[2] = lds_read_b128<SO + 64>(sa);
     stf[3] = lds_read_b128<SO + 96>(sa);
-    scf = f32x16{};
   }
   auto issue = [&](int i) {
     if (i < N1) {
@@ -691,18 +690,16 @@ __device__ __forceinline__ void step_ds(PairLane<D, 1>& w, unsigned bof, unsigne
       hi[i % NB] = read_tr_g<D, TO>(j / C::NDT, w.ad.hi[j % C::NDT] + bob);
     }
   };
+  // scb already holds dP - D: the dP products of its half accumulated onto
+  // that half's -D (the statistics row holds -D)
   auto ds_val = [&](int v) {
     const bf16x8 p8 = as_bf16(v < 8 ? x0 : x1);
     const float p = (float)p8[v & 7];
-    ds[v >> 3][v & 7] = (__bf16)(p * (scb[v] - as_f32(stb[v >> 2])[v & 3]));
+    ds[v >> 3][v & 7] = (__bf16)(p * scb[v]);
   };
   auto claim_b = [&](int n) {
     claim_lds_n(n, x0);
     claim_lds_n(n, x1);
-    claim_lds_n(n, stb[0]);
-    claim_lds_n(n, stb[1]);
-    claim_lds_n(n, stb[2]);
-    claim_lds_n(n, stb[3]);
   };
   if constexpr (B && !F) {
     claim_b(0);
@@ -718,8 +715,16 @@ __device__ __forceinline__ void step_ds(PairLane<D, 1>& w, unsigned bof, unsigne
     const int n = S::after(i);
     if (i < N1) {
       claim_lds_n(n, ra[i % NB]);
-      // the exchange and the previous statistics were read before every operand
+      // the exchange and the statistics were read before every operand
       if (B && i == 0) claim_b(n);
+      if (i == 0) {
+        // dP^T accumulates onto -D of its queries (in the MFMA output layout)
+        claim_lds_n(n, stf[0]);
+        claim_lds_n(n, stf[1]);
+        claim_lds_n(n, stf[2]);
+        claim_lds_n(n, stf[3]);
+        scf = __builtin_bit_cast(f32x16, stf);
+      }
       scf = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(ra[i % NB]), w.f[i], scf, 0, 0, 0);
       if constexpr (B) {
 #pragma unroll
@@ -1044,7 +1049,7 @@ __global__ __launch_bounds__(kF32Threads) void ring_attn_bwd_dq_f32(const BwdArg
         if (!real) dsum = 0.0f;
         const long long so = ((long long)b * a.H + h) * a.Sq + r;
         a.stats[so] = lse2;
-        a.stats[(long long)a.B * a.H * a.Sq + so] = dsum;
+        a.stats[(long long)a.B * a.H * a.Sq + so] = -dsum;
       }
       slse[ti] = lse2;
       sdsum[ti] = dsum;
@@ -1146,7 +1151,7 @@ __global__ __launch_bounds__(kF32Threads) void ring_attn_bwd_dkv_f32(const BwdAr
         const int r = row0 + tid;
         const long long so = ((long long)b * a.H + h) * a.Sq + r;
         slse[tid] = r < a.Sq ? a.stats[so] : INFINITY;
-        sdsum[tid] = r < a.Sq ? a.stats[nst + so] : 0.0f;
+        sdsum[tid] = r < a.Sq ? -a.stats[nst + so] : 0.0f;
         sqp[tid] = r < a.Sq ? qpos(a, r) : LLONG_MAX;
       }
       __syncthreads();
