@@ -227,6 +227,9 @@ struct DqLane {
   using C = Cfg<D>;
   bf16x8 qf[C::NC], df[C::NC];  // this lane's query row of Q and dO (B operands)
   f32x16 acc[C::NDT];           // dQ^T
+  f32x16 negd;                  // -D of this lane's query in every element: the
+                                // dP^T accumulators start from it, so they end
+                                // holding dP - D
   LaneAddr<D> ad;
 };
 
@@ -245,7 +248,7 @@ __device__ __forceinline__ void dq_half(DqLane<D>& w, float dsum, float lse2, fl
   using C = Cfg<D>;
   constexpr int RO = BO + T * 32 * C::ROWB;
   constexpr int NB = kPF + 1;
-  f32x16 sc = f32x16{}, dpt = f32x16{};
+  f32x16 sc = f32x16{}, dpt = w.negd;
   {
     u32x4 ka[NB], va[NB];
 #pragma unroll
@@ -287,7 +290,7 @@ __device__ __forceinline__ void dq_half(DqLane<D>& w, float dsum, float lse2, fl
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const float p = __builtin_amdgcn_exp2f(sc[v] * c_scale - lse2);
-    dsb[v >> 3][v & 7] = (__bf16)(p * (dpt[v] - dsum));
+    dsb[v >> 3][v & 7] = (__bf16)(p * dpt[v]);
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -385,6 +388,8 @@ void ring_attn_bwd_dq(const BwdArgs a) {
   }
 #pragma unroll
   for (int i = 0; i < C::NDT; ++i) w.acc[i] = f32x16{};
+#pragma unroll
+  for (int v = 0; v < 16; ++v) w.negd[v] = -dsum;
   const unsigned base = lds_addr(smem);
   w.ad.init(base, lane);
   int voff[DMA];
